@@ -1,0 +1,210 @@
+/*
+ * pagedattn.h -- C ABI of libpagedattn: paged-attention decode (v1 and the
+ * partitioned v2) for AMD Instinct MI355X (gfx950).
+ *
+ * What is computed.  For every sequence s of a decode batch (one query token
+ * per sequence) and every query head h, attention over the sequence's cached
+ * keys and values, which live in fixed-size blocks of a shared pool reached
+ * through a per-sequence block table (page "BI-V100 PagedAttention V2
+ * implementation" -- the commit page of paged_attention_v2_pytorch.py --
+ * argument list of paged_attention_v2_pytorch and its per-block gather loop):
+ *
+ *   s[h,t]  = scale * k_scale * sum_d q[s,h,d] K[t,kv(h),d]  +  alibi[h] * t
+ *   out[s,h] = sum_t softmax_t(s[h,:]) * v_scale * V[t,kv(h),:]
+ *
+ * with kv(h) = h / (num_heads / num_kv_heads) (same page, GQA expansion by
+ * repeat_interleave) and t the absolute 0-based key position (same page,
+ * "Alibi bias" step of Phase 1).
+ *
+ * v2 (same page, "Phase 1: Per-partition attention" and "Phase 2: Reduce
+ * across partitions") splits each sequence into partitions of
+ * PA_PARTITION_SIZE = 512 tokens; partition p covers tokens
+ * [512p, min(512p + 512, L)).  Phase 1 stores, per (s, h, p),
+ *   max_logits[s,h,p] = m_p = max over the partition of s[h,t]
+ *   exp_sums[s,h,p]   = S_p = sum over the partition of exp(s[h,t] - m_p)
+ *   tmp_out[s,h,p,:]  = O_p = sum exp(s[h,t] - m_p) v_scale V[t] / S_p
+ * (O_p is normalised: the page's prose and its merge formula need that; its
+ * printed code omits the division, which double counts S_p), and Phase 2
+ * merges them with the log-sum-exp rescale
+ *   M = max_p m_p,  r_p = exp(m_p - M) S_p,  out = sum_p (r_p / sum_q r_q) O_p.
+ * v1 (same page, commit message and "Performance vs V1") processes the whole
+ * sequence in one workgroup and writes only out.  Natural-log units
+ * throughout.
+ *
+ * Layouts (all row-major, contiguous, device memory):
+ *   query, out    [num_seqs, num_heads, head_size]                 dtype
+ *   key_cache     [num_blocks, num_kv_heads, head_size/x, block_size, x]
+ *   value_cache   [num_blocks, num_kv_heads, head_size, block_size]
+ *                 x = 16 / sizeof(KV element): 4 (f32), 8 (f16, bf16),
+ *                 16 (fp8); head dim d = c * x + j for K index [.., c, t, j].
+ *                 KV elements have type dtype, or are OCP FP8 E4M3FN bytes
+ *                 when kv_cache_dtype == PA_KV_FP8_E4M3.
+ *   block_tables  int32 [num_seqs, max_num_blocks_per_seq]; token t of
+ *                 sequence s is slot t % block_size of physical block
+ *                 block_tables[s, t / block_size].  Entries at and after
+ *                 ceil(seq_lens[s] / block_size) are never read.
+ *   seq_lens      int32 [num_seqs]
+ *   alibi_slopes  float [num_heads], or NULL for no ALiBi
+ *   exp_sums, max_logits  float [num_seqs, num_heads, max_num_partitions]
+ *   tmp_out       float [num_seqs, num_heads, max_num_partitions, head_size]
+ *
+ * Ownership.  Every buffer belongs to the caller.  The library allocates and
+ * frees nothing and keeps no pointer after a call returns.  Its only global
+ * state is a per-device cache of the compute-unit count, filled on first use
+ * under a lock.
+ *
+ * Streams.  Work is enqueued on `stream` (a hipStream_t; NULL is the null
+ * stream) and runs asynchronously; no call synchronises or copies device
+ * memory to the host (that is why max_seq_len is a host integer).
+ *
+ * Errors.  Every call returns a pa_status.  All argument checks run on the
+ * host before any HIP call, so an error leaves every buffer untouched.  A
+ * failed kernel launch returns PA_ERR_HIP.  Device data the host cannot see
+ * is guarded in the kernels: a sequence whose seq_lens entry is negative or
+ * above max_seq_len, or that reaches a block-table entry outside
+ * [0, num_blocks), reads no memory through it and gets NaN in its outputs.
+ *
+ * Supported: dtype f32 / f16 / bf16; kv_cache_dtype AUTO (KV in dtype) or
+ * FP8_E4M3 (dtype f16 or bf16); head_size 64 or 128; block_size 16 or 32;
+ * num_heads a multiple of num_kv_heads with at most 16 query heads per KV
+ * head for 16-bit / fp8 caches (any group size for f32).
+ */
+#ifndef PAGEDATTN_H
+#define PAGEDATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PA_PARTITION_SIZE 512
+
+typedef enum pa_status {
+  PA_OK = 0,
+  PA_ERR_NULL_POINTER = 1, /* a required pointer is NULL                   */
+  PA_ERR_BAD_SHAPE = 2,    /* sizes inconsistent or out of the valid range */
+  PA_ERR_MISALIGNED = 3,   /* a cache / query / out pointer not 16-byte aligned */
+  PA_ERR_UNSUPPORTED = 4,  /* valid but not built: head_size, block_size, dtype */
+  PA_ERR_HIP = 5,          /* the HIP runtime reported an error            */
+  PA_ERR_BAD_ARGUMENT = 6  /* non-finite scale, unknown enum value         */
+} pa_status;
+
+/* Element type of query and out (and of the KV cache when kv_cache_dtype is
+ * PA_KV_AUTO). */
+typedef enum pa_dtype { PA_DTYPE_F32 = 0, PA_DTYPE_F16 = 1, PA_DTYPE_BF16 = 2 } pa_dtype;
+
+/* "auto" = the cache holds dtype (V2 page, kv_cache_dtype argument);
+ * FP8_E4M3 = the cache holds OCP FP8 E4M3FN bytes, dequantised as
+ * value = decode(byte) * k_scale (keys) or * v_scale (values). */
+typedef enum pa_kv_cache_dtype { PA_KV_AUTO = 0, PA_KV_FP8_E4M3 = 1 } pa_kv_cache_dtype;
+
+/* Which algorithm a sequence takes.  AUTO chooses per sequence, on the
+ * device, with the rule of pa_should_use_v2. */
+typedef enum pa_mode { PA_MODE_V1 = 0, PA_MODE_V2 = 1, PA_MODE_AUTO = 2 } pa_mode;
+
+/* ---------------------------------------------------------------------- */
+/* Full calls                                                             */
+/* ---------------------------------------------------------------------- */
+
+/* v1: one workgroup per (sequence, KV head) walks the whole sequence and
+ * writes out only (V2 page, commit message: v1 processes the entire KV
+ * sequence in one kernel).  Unlike the page's v1 it has no shared-memory
+ * ceiling on seq_len: it keeps a running max and sum. */
+pa_status paged_attention_v1(
+    void *out, const void *query, const void *key_cache, const void *value_cache,
+    int num_seqs, int num_heads, int num_kv_heads, int head_size, float scale,
+    const int32_t *block_tables, int max_num_blocks_per_seq, const int32_t *seq_lens,
+    int num_blocks, int block_size, int max_seq_len, const float *alibi_slopes,
+    pa_dtype dtype, pa_kv_cache_dtype kv_cache_dtype, float k_scale, float v_scale,
+    void *stream);
+
+/* v2: Phase 1 (one workgroup per (partition, KV head, sequence)) then
+ * Phase 2 (one workgroup per (query head, sequence)); V2 page, "Phase 1" and
+ * "Phase 2".  Writes out; max_logits / exp_sums for every partition slot
+ * (slots p >= ceil(L/512) get -inf / 0, as the page's padding step); tmp_out
+ * for p < ceil(L/512) only (later slots are untouched scratch).  A sequence
+ * of length 0 gets out = 0 and padding statistics. */
+pa_status paged_attention_v2(
+    void *out, float *exp_sums, float *max_logits, float *tmp_out,
+    const void *query, const void *key_cache, const void *value_cache,
+    int num_seqs, int num_heads, int num_kv_heads, int head_size, float scale,
+    const int32_t *block_tables, int max_num_blocks_per_seq, const int32_t *seq_lens,
+    int num_blocks, int block_size, int max_seq_len, int max_num_partitions,
+    const float *alibi_slopes, pa_dtype dtype, pa_kv_cache_dtype kv_cache_dtype,
+    float k_scale, float v_scale, void *stream);
+
+/* Per-sequence choice between v1 and v2 (pa_should_use_v2, decided on the
+ * device from seq_lens), same arguments as paged_attention_v2.  Sequences
+ * sent down the v1 path get out only; their exp_sums / max_logits / tmp_out
+ * rows are left as they were. */
+pa_status paged_attention_auto(
+    void *out, float *exp_sums, float *max_logits, float *tmp_out,
+    const void *query, const void *key_cache, const void *value_cache,
+    int num_seqs, int num_heads, int num_kv_heads, int head_size, float scale,
+    const int32_t *block_tables, int max_num_blocks_per_seq, const int32_t *seq_lens,
+    int num_blocks, int block_size, int max_seq_len, int max_num_partitions,
+    const float *alibi_slopes, pa_dtype dtype, pa_kv_cache_dtype kv_cache_dtype,
+    float k_scale, float v_scale, void *stream);
+
+/* ---------------------------------------------------------------------- */
+/* The two phases on their own (same arguments as paged_attention_v2 plus  */
+/* the mode).  paged_attention_v2 == partition(V2) then reduce(V2), and    */
+/* paged_attention_auto == partition(AUTO) then reduce(AUTO).  With        */
+/* PA_MODE_V1 the partition phase is the whole of v1 (exp_sums, max_logits */
+/* and tmp_out may then be NULL) and the reduce phase does nothing.        */
+/* ---------------------------------------------------------------------- */
+
+/* Phase 1 (V2 page, "Phase 1: Per-partition attention"). */
+pa_status paged_attention_partition(
+    pa_mode mode, void *out, float *exp_sums, float *max_logits, float *tmp_out,
+    const void *query, const void *key_cache, const void *value_cache,
+    int num_seqs, int num_heads, int num_kv_heads, int head_size, float scale,
+    const int32_t *block_tables, int max_num_blocks_per_seq, const int32_t *seq_lens,
+    int num_blocks, int block_size, int max_seq_len, int max_num_partitions,
+    const float *alibi_slopes, pa_dtype dtype, pa_kv_cache_dtype kv_cache_dtype,
+    float k_scale, float v_scale, void *stream);
+
+/* Phase 2 (V2 page, "Phase 2: Reduce across partitions (log-sum-exp)"):
+ * reads exp_sums, max_logits and tmp_out of every sequence with more than
+ * one partition on the v2 path and writes its out rows.  The cache pointers
+ * and block_tables are not read and may be NULL. */
+pa_status paged_attention_reduce(
+    pa_mode mode, void *out, const float *exp_sums, const float *max_logits,
+    const float *tmp_out, int num_seqs, int num_heads, int num_kv_heads, int head_size,
+    const int32_t *seq_lens, int max_seq_len, int max_num_partitions, pa_dtype dtype,
+    void *stream);
+
+/* ---------------------------------------------------------------------- */
+/* Helpers                                                                */
+/* ---------------------------------------------------------------------- */
+
+/* 512 (V2 page, module constant _PARTITION_SIZE). */
+int pa_partition_size(void);
+
+/* ceil(max_seq_len / 512): the smallest valid max_num_partitions (0 -> 1). */
+int pa_num_partitions(int max_seq_len);
+
+/* The per-sequence v1/v2 rule of PA_MODE_AUTO, on the host.  It is the
+ * dispatch page's should_use_paged_v2 ("ex_engine/factors/attn_dispatch.py":
+ * tiles = num_kv_heads * ceil(seq_len / 512), v2 iff tiles > 2 * SM count)
+ * re-sized to the GPU's compute units, plus one clause of ours for small
+ * batches: v2 whenever num_seqs * num_kv_heads < 4 * cu_count, because v1
+ * would then leave compute units idle.  Returns 1 for v2, 0 for v1. */
+int pa_should_use_v2(int num_seqs, int num_kv_heads, int seq_len, int cu_count);
+
+/* Compute units of the current HIP device (cached per device); <= 0 and
+ * PA_ERR_HIP if the runtime cannot tell. */
+pa_status pa_device_cu_count(int *cu_count);
+
+/* Static description of a status code. */
+const char *pa_status_string(pa_status status);
+
+/* Library version, "major.minor.patch". */
+const char *pa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDATTN_H */

@@ -1,0 +1,261 @@
+"""Thin Python binding of libpagedattn (ctypes).
+
+Argument marshalling only: shapes are read off the torch tensors, checked,
+and passed with ``data_ptr()`` and the current HIP stream to the C ABI in
+``include/pagedattn.h``; every step of the computation runs in the library's
+HIP kernels.  The argument order follows the paged-attention op of the page
+"BI-V100 PagedAttention V2 implementation" (out, exp_sums, max_logits,
+tmp_out, query, key_cache, value_cache, num_kv_heads, scale, block_tables,
+seq_lens, block_size, max_seq_len, alibi_slopes, kv_cache_dtype, k_scale,
+v_scale).  There is no fallback: without the built library every call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedattn.so")
+
+PA_OK = 0
+STATUS_NAMES = {0: "PA_OK", 1: "PA_ERR_NULL_POINTER", 2: "PA_ERR_BAD_SHAPE",
+                3: "PA_ERR_MISALIGNED", 4: "PA_ERR_UNSUPPORTED", 5: "PA_ERR_HIP",
+                6: "PA_ERR_BAD_ARGUMENT"}
+DTYPE_CODE = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
+KV_CODE = {"auto": 0, "fp8": 1, "fp8_e4m3": 1}
+MODE_CODE = {"v1": 0, "v2": 1, "auto": 2}
+
+#: Every symbol include/pagedattn.h declares.
+EXPORTED_SYMBOLS = (
+    "paged_attention_v1", "paged_attention_v2", "paged_attention_auto",
+    "paged_attention_partition", "paged_attention_reduce", "pa_partition_size",
+    "pa_num_partitions", "pa_should_use_v2", "pa_device_cu_count", "pa_status_string",
+    "pa_version",
+)
+
+
+class PagedAttentionError(RuntimeError):
+    """A libpagedattn call returned a status other than PA_OK."""
+
+    def __init__(self, status: int, func: str, message: str):
+        super().__init__(f"{func}: {STATUS_NAMES.get(status, status)} ({message})")
+        self.status = status
+
+
+_lib = None
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_F = ctypes.c_float
+_PARTITION_ARGS = [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _P, _I, _P, _I, _I, _I, _I,
+                   _P, _I, _I, _F, _F, _P]
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libpagedattn and declare its signatures (raises if it is not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"libpagedattn is not built ({path} missing); run "
+            "`python -m paged_kv_cache_297_amd._build` or __graft_entry__.build()")
+    lib = ctypes.CDLL(path)
+    lib.paged_attention_v1.argtypes = [_P, _P, _P, _P, _I, _I, _I, _I, _F, _P, _I, _P, _I, _I, _I,
+                                       _P, _I, _I, _F, _F, _P]
+    lib.paged_attention_v1.restype = _I
+    for name in ("paged_attention_v2", "paged_attention_auto"):
+        fn = getattr(lib, name)
+        fn.argtypes = _PARTITION_ARGS[:]
+        fn.restype = _I
+    lib.paged_attention_partition.argtypes = [_I] + _PARTITION_ARGS
+    lib.paged_attention_partition.restype = _I
+    lib.paged_attention_reduce.argtypes = [_I, _P, _P, _P, _P, _I, _I, _I, _I, _P, _I, _I, _I, _P]
+    lib.paged_attention_reduce.restype = _I
+    lib.pa_partition_size.argtypes = []
+    lib.pa_partition_size.restype = _I
+    lib.pa_num_partitions.argtypes = [_I]
+    lib.pa_num_partitions.restype = _I
+    lib.pa_should_use_v2.argtypes = [_I, _I, _I, _I]
+    lib.pa_should_use_v2.restype = _I
+    lib.pa_device_cu_count.argtypes = [ctypes.POINTER(ctypes.c_int)]
+    lib.pa_device_cu_count.restype = _I
+    lib.pa_status_string.argtypes = [_I]
+    lib.pa_status_string.restype = ctypes.c_char_p
+    lib.pa_version.argtypes = []
+    lib.pa_version.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _check(status: int, func: str) -> None:
+    if status != PA_OK:
+        msg = load_library().pa_status_string(status).decode()
+        raise PagedAttentionError(status, func, msg)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+
+
+def _kv_code(kv_cache_dtype: str) -> int:
+    if kv_cache_dtype not in KV_CODE:
+        raise ValueError(f"kv_cache_dtype must be one of {sorted(KV_CODE)}")
+    return KV_CODE[kv_cache_dtype]
+
+
+def _geometry(query, key_cache, value_cache, block_tables, seq_lens, kv_cache_dtype):
+    """Checks layouts and returns (num_seqs, num_heads, head_size, num_blocks, max_blocks)."""
+    for name, t in (("query", query), ("key_cache", key_cache), ("value_cache", value_cache),
+                    ("block_tables", block_tables), ("seq_lens", seq_lens)):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if query.dtype not in DTYPE_CODE:
+        raise TypeError("query must be float32, float16 or bfloat16")
+    if block_tables.dtype != torch.int32 or seq_lens.dtype != torch.int32:
+        raise TypeError("block_tables and seq_lens must be int32")
+    num_seqs, num_heads, head_size = query.shape
+    if _kv_code(kv_cache_dtype) == 1:
+        if key_cache.element_size() != 1 or value_cache.element_size() != 1:
+            raise TypeError("an fp8 cache must be a 1-byte tensor (uint8 or float8_e4m3fn)")
+        elem = 1
+    else:
+        if key_cache.dtype != query.dtype or value_cache.dtype != query.dtype:
+            raise TypeError("with kv_cache_dtype='auto' the caches must have the query dtype")
+        elem = query.element_size()
+    x = 16 // elem
+    nb, hkv, dx, bs, xx = key_cache.shape
+    if xx != x or dx * x != head_size:
+        raise ValueError(f"key_cache must be [num_blocks, Hkv, {head_size}/{x}, block_size, {x}]")
+    if tuple(value_cache.shape) != (nb, hkv, head_size, bs):
+        raise ValueError("value_cache must be [num_blocks, Hkv, head_size, block_size]")
+    if block_tables.dim() != 2 or block_tables.shape[0] != num_seqs or seq_lens.shape != (num_seqs,):
+        raise ValueError("block_tables must be [num_seqs, max_blocks] and seq_lens [num_seqs]")
+    return num_seqs, num_heads, head_size, nb, hkv, bs, block_tables.shape[1]
+
+
+def paged_attention_v1(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor,
+                       value_cache: torch.Tensor, num_kv_heads: int, scale: float,
+                       block_tables: torch.Tensor, seq_lens: torch.Tensor, block_size: int,
+                       max_seq_len: int, alibi_slopes: Optional[torch.Tensor] = None,
+                       kv_cache_dtype: str = "auto", k_scale: float = 1.0, v_scale: float = 1.0,
+                       stream=None) -> None:
+    """Whole-sequence paged attention; writes ``out`` in place."""
+    lib = load_library()
+    b, h, d, nb, hkv, bs, mbps = _geometry(query, key_cache, value_cache, block_tables, seq_lens,
+                                           kv_cache_dtype)
+    if hkv != num_kv_heads or bs != block_size:
+        raise ValueError("num_kv_heads / block_size disagree with the cache shape")
+    if out.shape != query.shape or out.dtype != query.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor like query")
+    st = lib.paged_attention_v1(out.data_ptr(), query.data_ptr(), key_cache.data_ptr(),
+                                value_cache.data_ptr(), b, h, num_kv_heads, d, float(scale),
+                                block_tables.data_ptr(), mbps, seq_lens.data_ptr(), nb, block_size,
+                                int(max_seq_len), _ptr(alibi_slopes), DTYPE_CODE[query.dtype],
+                                _kv_code(kv_cache_dtype), float(k_scale), float(v_scale),
+                                _stream(stream))
+    _check(st, "paged_attention_v1")
+
+
+def _v2_args(out, exp_sums, max_logits, tmp_out, query, key_cache, value_cache, num_kv_heads,
+             scale, block_tables, seq_lens, block_size, max_seq_len, alibi_slopes,
+             kv_cache_dtype, k_scale, v_scale, stream):
+    b, h, d, nb, hkv, bs, mbps = _geometry(query, key_cache, value_cache, block_tables, seq_lens,
+                                           kv_cache_dtype)
+    if hkv != num_kv_heads or bs != block_size:
+        raise ValueError("num_kv_heads / block_size disagree with the cache shape")
+    if out.shape != query.shape or out.dtype != query.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor like query")
+    for name, t in (("exp_sums", exp_sums), ("max_logits", max_logits), ("tmp_out", tmp_out)):
+        if t.dtype != torch.float32 or not t.is_contiguous():
+            raise TypeError(f"{name} must be a contiguous float32 tensor")
+    p = exp_sums.shape[2]
+    if exp_sums.shape != (b, h, p) or max_logits.shape != (b, h, p) or tmp_out.shape != (b, h, p, d):
+        raise ValueError("exp_sums/max_logits must be [B, H, P] and tmp_out [B, H, P, D]")
+    if alibi_slopes is not None and (alibi_slopes.dtype != torch.float32 or alibi_slopes.numel() != h):
+        raise ValueError("alibi_slopes must be float32 [num_heads]")
+    return [out.data_ptr(), exp_sums.data_ptr(), max_logits.data_ptr(), tmp_out.data_ptr(),
+            query.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(), b, h, num_kv_heads, d,
+            float(scale), block_tables.data_ptr(), mbps, seq_lens.data_ptr(), nb, block_size,
+            int(max_seq_len), p, _ptr(alibi_slopes), DTYPE_CODE[query.dtype],
+            _kv_code(kv_cache_dtype), float(k_scale), float(v_scale), _stream(stream)]
+
+
+def paged_attention_v2(out, exp_sums, max_logits, tmp_out, query, key_cache, value_cache,
+                       num_kv_heads, scale, block_tables, seq_lens, block_size, max_seq_len,
+                       alibi_slopes=None, kv_cache_dtype="auto", k_scale=1.0, v_scale=1.0,
+                       stream=None) -> None:
+    """Partitioned paged attention (Phase 1 + Phase 2); writes all four outputs in place."""
+    lib = load_library()
+    args = _v2_args(out, exp_sums, max_logits, tmp_out, query, key_cache, value_cache,
+                    num_kv_heads, scale, block_tables, seq_lens, block_size, max_seq_len,
+                    alibi_slopes, kv_cache_dtype, k_scale, v_scale, stream)
+    _check(lib.paged_attention_v2(*args), "paged_attention_v2")
+
+
+def paged_attention_auto(out, exp_sums, max_logits, tmp_out, query, key_cache, value_cache,
+                         num_kv_heads, scale, block_tables, seq_lens, block_size, max_seq_len,
+                         alibi_slopes=None, kv_cache_dtype="auto", k_scale=1.0, v_scale=1.0,
+                         stream=None) -> None:
+    """Per-sequence v1/v2 choice on the device (pa_should_use_v2 rule)."""
+    lib = load_library()
+    args = _v2_args(out, exp_sums, max_logits, tmp_out, query, key_cache, value_cache,
+                    num_kv_heads, scale, block_tables, seq_lens, block_size, max_seq_len,
+                    alibi_slopes, kv_cache_dtype, k_scale, v_scale, stream)
+    _check(lib.paged_attention_auto(*args), "paged_attention_auto")
+
+
+def paged_attention_partition(mode, out, exp_sums, max_logits, tmp_out, query, key_cache,
+                              value_cache, num_kv_heads, scale, block_tables, seq_lens,
+                              block_size, max_seq_len, alibi_slopes=None, kv_cache_dtype="auto",
+                              k_scale=1.0, v_scale=1.0, stream=None) -> None:
+    """Phase 1 only (mode 'v1', 'v2' or 'auto')."""
+    lib = load_library()
+    args = _v2_args(out, exp_sums, max_logits, tmp_out, query, key_cache, value_cache,
+                    num_kv_heads, scale, block_tables, seq_lens, block_size, max_seq_len,
+                    alibi_slopes, kv_cache_dtype, k_scale, v_scale, stream)
+    _check(lib.paged_attention_partition(MODE_CODE[mode], *args), "paged_attention_partition")
+
+
+def paged_attention_reduce(mode, out, exp_sums, max_logits, tmp_out, seq_lens, num_kv_heads,
+                           max_seq_len, stream=None) -> None:
+    """Phase 2 only (mode 'v2' or 'auto'; 'v1' does nothing)."""
+    lib = load_library()
+    b, h, d = out.shape
+    p = exp_sums.shape[2]
+    st = lib.paged_attention_reduce(MODE_CODE[mode], out.data_ptr(), exp_sums.data_ptr(),
+                                    max_logits.data_ptr(), tmp_out.data_ptr(), b, h, num_kv_heads,
+                                    d, seq_lens.data_ptr(), int(max_seq_len), p,
+                                    DTYPE_CODE[out.dtype], _stream(stream))
+    _check(st, "paged_attention_reduce")
+
+
+def partition_size() -> int:
+    return load_library().pa_partition_size()
+
+
+def num_partitions(max_seq_len: int) -> int:
+    return load_library().pa_num_partitions(int(max_seq_len))
+
+
+def should_use_v2(num_seqs: int, num_kv_heads: int, seq_len: int, cu_count: int) -> bool:
+    return bool(load_library().pa_should_use_v2(num_seqs, num_kv_heads, seq_len, cu_count))
+
+
+def device_cu_count() -> int:
+    n = ctypes.c_int(0)
+    _check(load_library().pa_device_cu_count(ctypes.byref(n)), "pa_device_cu_count")
+    return n.value
+
+
+def version() -> str:
+    return load_library().pa_version().decode()

@@ -1,0 +1,415 @@
+// C ABI of libpagedattn: argument validation, the v1/v2 dispatch rule, kernel
+// selection and launches.  Every check runs on the host before any HIP call.
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+
+#include <mutex>
+
+#include "../../include/pagedattn.h"
+#include "pa_launch.h"
+#include "pa_params.h"
+
+namespace {
+
+using pa::Params;
+
+// ---------------------------------------------------------------------------
+// Tunables.  Defaults are the shipped dispatch; the environment variables
+// exist for tuning sweeps only.
+// ---------------------------------------------------------------------------
+struct Tunables {
+  int mfma_min_group = 5;     // query heads per KV head from which the MFMA kernel is used
+  int small_batch_factor = 4; // AUTO: v2 for all if B * Hkv < factor * CUs
+  int tile_factor = 2;        // AUTO: v2 iff Hkv * ceil(L/512) > factor * CUs
+};
+
+int env_int(const char *name, int fallback, int lo, int hi) {
+  const char *s = getenv(name);
+  if (!s || !*s) return fallback;
+  char *end = nullptr;
+  const long v = strtol(s, &end, 10);
+  if (*end != '\0' || v < lo || v > hi) return fallback;
+  return (int)v;
+}
+
+const Tunables &tunables() {
+  static const Tunables t = [] {
+    Tunables x;
+    x.mfma_min_group = env_int("PA_MFMA_MIN_GROUP", x.mfma_min_group, 1, 1 << 20);
+    x.small_batch_factor = env_int("PA_AUTO_SMALL_BATCH_FACTOR", x.small_batch_factor, 0, 1 << 20);
+    x.tile_factor = env_int("PA_AUTO_TILE_FACTOR", x.tile_factor, 0, 1 << 20);
+    return x;
+  }();
+  return t;
+}
+
+// ---------------------------------------------------------------------------
+// Per-device compute-unit count, cached.
+// ---------------------------------------------------------------------------
+constexpr int kMaxDevices = 64;
+std::mutex g_cu_mutex;
+int g_cu_count[kMaxDevices] = {0};
+
+pa_status cu_count_current(int *cu) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return PA_ERR_HIP;
+  if (dev >= 0 && dev < kMaxDevices) {
+    std::lock_guard<std::mutex> lock(g_cu_mutex);
+    if (g_cu_count[dev] > 0) {
+      *cu = g_cu_count[dev];
+      return PA_OK;
+    }
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    return PA_ERR_HIP;
+  if (dev >= 0 && dev < kMaxDevices) {
+    std::lock_guard<std::mutex> lock(g_cu_mutex);
+    g_cu_count[dev] = n;
+  }
+  *cu = n;
+  return PA_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Validation
+// ---------------------------------------------------------------------------
+struct Call {
+  pa_mode mode;
+  void *out;
+  float *exp_sums, *max_logits, *tmp_out;
+  const void *query, *key_cache, *value_cache;
+  int num_seqs, num_heads, num_kv_heads, head_size;
+  float scale;
+  const int32_t *block_tables;
+  int max_num_blocks_per_seq;
+  const int32_t *seq_lens;
+  int num_blocks, block_size, max_seq_len, max_num_partitions;
+  const float *alibi_slopes;
+  pa_dtype dtype;
+  pa_kv_cache_dtype kv_cache_dtype;
+  float k_scale, v_scale;
+  hipStream_t stream;
+};
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
+
+constexpr int kMaxGridYZ = 65535;
+
+pa_status validate_common(const Call &c, bool partition_phase) {
+  if (c.mode != PA_MODE_V1 && c.mode != PA_MODE_V2 && c.mode != PA_MODE_AUTO)
+    return PA_ERR_BAD_ARGUMENT;
+  if (c.dtype != PA_DTYPE_F32 && c.dtype != PA_DTYPE_F16 && c.dtype != PA_DTYPE_BF16)
+    return PA_ERR_BAD_ARGUMENT;
+  if (c.num_seqs < 0 || c.num_heads <= 0 || c.num_kv_heads <= 0 || c.max_seq_len < 0)
+    return PA_ERR_BAD_SHAPE;
+  if (c.num_heads % c.num_kv_heads != 0) return PA_ERR_BAD_SHAPE;
+  if (c.head_size != 64 && c.head_size != 128) return PA_ERR_UNSUPPORTED;
+  if (c.num_seqs > kMaxGridYZ) return PA_ERR_BAD_SHAPE;
+  if (!c.out || !c.seq_lens) return PA_ERR_NULL_POINTER;
+  if (!aligned16(c.out)) return PA_ERR_MISALIGNED;
+  const bool partials = c.mode != PA_MODE_V1;
+  if (partials) {
+    if (!c.exp_sums || !c.max_logits || !c.tmp_out) return PA_ERR_NULL_POINTER;
+    if (!aligned16(c.tmp_out)) return PA_ERR_MISALIGNED;
+    if (c.max_num_partitions < 1 || c.max_num_partitions < pa_num_partitions(c.max_seq_len))
+      return PA_ERR_BAD_SHAPE;
+  }
+  if (!partition_phase) return PA_OK;
+
+  if (c.kv_cache_dtype != PA_KV_AUTO && c.kv_cache_dtype != PA_KV_FP8_E4M3)
+    return PA_ERR_BAD_ARGUMENT;
+  if (c.kv_cache_dtype == PA_KV_FP8_E4M3 && c.dtype == PA_DTYPE_F32) return PA_ERR_UNSUPPORTED;
+  if (c.block_size != 16 && c.block_size != 32) return PA_ERR_UNSUPPORTED;
+  if (pa::kPartitionSize % c.block_size != 0) return PA_ERR_UNSUPPORTED;
+  if (!isfinite(c.scale) || !isfinite(c.k_scale) || !isfinite(c.v_scale))
+    return PA_ERR_BAD_ARGUMENT;
+  if (!c.query || !c.key_cache || !c.value_cache || !c.block_tables) return PA_ERR_NULL_POINTER;
+  if (!aligned16(c.query) || !aligned16(c.key_cache) || !aligned16(c.value_cache))
+    return PA_ERR_MISALIGNED;
+  if (c.max_num_blocks_per_seq < 0 || c.num_blocks < 0) return PA_ERR_BAD_SHAPE;
+  if ((long long)c.max_num_blocks_per_seq * c.block_size < c.max_seq_len) return PA_ERR_BAD_SHAPE;
+  if (c.max_seq_len > 0 && c.num_blocks < 1) return PA_ERR_BAD_SHAPE;
+  return PA_OK;
+}
+
+// Kernel choice for the partition phase.
+struct Plan {
+  bool mfma;
+  int gp;           // query-head slots per workgroup (VALU) / 16 (MFMA)
+  int head_groups;  // workgroups per KV head along grid.y
+};
+
+Plan make_plan(const Call &c) {
+  const int group = c.num_heads / c.num_kv_heads;
+  Plan pl{};
+  pl.mfma = c.dtype != PA_DTYPE_F32 && group >= tunables().mfma_min_group;
+  if (pl.mfma) {
+    pl.gp = 16;
+  } else {
+    const int kv_bytes = c.kv_cache_dtype == PA_KV_FP8_E4M3 ? 1 : (c.dtype == PA_DTYPE_F32 ? 4 : 2);
+    const int gmax = pa::valu_max_group(kv_bytes, c.head_size, c.block_size);
+    int p2 = 1;
+    while (p2 < group && p2 < gmax) p2 *= 2;
+    pl.gp = p2;
+  }
+  pl.head_groups = ceil_div(group, pl.gp);
+  return pl;
+}
+
+Params make_params(const Call &c, int cu, int head_groups) {
+  Params p{};
+  p.out = c.out;
+  p.exp_sums = c.exp_sums;
+  p.max_logits = c.max_logits;
+  p.tmp_out = c.tmp_out;
+  p.query = c.query;
+  p.key_cache = c.key_cache;
+  p.value_cache = c.value_cache;
+  p.block_tables = c.block_tables;
+  p.seq_lens = c.seq_lens;
+  p.alibi_slopes = c.alibi_slopes;
+  p.num_seqs = c.num_seqs;
+  p.num_heads = c.num_heads;
+  p.num_kv_heads = c.num_kv_heads;
+  p.group = c.num_heads / c.num_kv_heads;
+  p.max_num_blocks_per_seq = c.max_num_blocks_per_seq;
+  p.num_blocks = c.num_blocks;
+  p.max_seq_len = c.max_seq_len;
+  p.max_num_partitions = c.max_num_partitions;
+  p.head_groups = head_groups;
+  p.mode = (int)c.mode;
+  const long long b_hkv = (long long)c.num_seqs * c.num_kv_heads;
+  p.auto_all_v2 = b_hkv < (long long)tunables().small_batch_factor * cu ? 1 : 0;
+  p.auto_tile_limit = tunables().tile_factor * cu;
+  p.scale_log2 = c.scale * c.k_scale * 1.4426950408889634f;
+  p.v_scale = c.v_scale;
+  return p;
+}
+
+pa_status run_partition(const Call &c) {
+  pa_status st = validate_common(c, true);
+  if (st != PA_OK) return st;
+  const Plan pl = make_plan(c);
+  const long long grid_y = (long long)c.num_kv_heads * pl.head_groups;
+  if (grid_y > kMaxGridYZ) return PA_ERR_BAD_SHAPE;
+  if (c.num_seqs == 0) return PA_OK;
+  int cu = 0;
+  if (c.mode == PA_MODE_AUTO) {
+    st = cu_count_current(&cu);
+    if (st != PA_OK) return st;
+  }
+  const Params p = make_params(c, cu, pl.head_groups);
+  const int gx = c.mode == PA_MODE_V1 ? 1 : pa_num_partitions(c.max_seq_len);
+  const dim3 grid(gx, (unsigned)grid_y, c.num_seqs);
+  const bool fp8 = c.kv_cache_dtype == PA_KV_FP8_E4M3;
+  hipError_t e;
+  if (pl.mfma) {
+    e = pa::launch_partition_mfma(p, (int)c.dtype, fp8, c.head_size, c.block_size, grid, c.stream);
+  } else if (fp8) {
+    e = pa::launch_partition_valu_fp8(p, (int)c.dtype, c.head_size, c.block_size, pl.gp, grid,
+                                      c.stream);
+  } else if (c.dtype == PA_DTYPE_F32) {
+    e = pa::launch_partition_valu_f32(p, c.head_size, c.block_size, pl.gp, grid, c.stream);
+  } else if (c.dtype == PA_DTYPE_F16) {
+    e = pa::launch_partition_valu_f16(p, c.head_size, c.block_size, pl.gp, grid, c.stream);
+  } else {
+    e = pa::launch_partition_valu_bf16(p, c.head_size, c.block_size, pl.gp, grid, c.stream);
+  }
+  return e == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+pa_status run_reduce(const Call &c) {
+  pa_status st = validate_common(c, false);
+  if (st != PA_OK) return st;
+  if (c.mode == PA_MODE_V1 || c.num_seqs == 0) return PA_OK;
+  if ((long long)c.num_heads > 0x7fffffffLL) return PA_ERR_BAD_SHAPE;
+  int cu = 0;
+  if (c.mode == PA_MODE_AUTO) {
+    st = cu_count_current(&cu);
+    if (st != PA_OK) return st;
+  }
+  const Params p = make_params(c, cu, 1);
+  const hipError_t e = pa::launch_reduce(p, (int)c.dtype, c.head_size, c.stream);
+  return e == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+Call make_call(pa_mode mode, void *out, float *exp_sums, float *max_logits, float *tmp_out,
+               const void *query, const void *key_cache, const void *value_cache, int num_seqs,
+               int num_heads, int num_kv_heads, int head_size, float scale,
+               const int32_t *block_tables, int max_num_blocks_per_seq, const int32_t *seq_lens,
+               int num_blocks, int block_size, int max_seq_len, int max_num_partitions,
+               const float *alibi_slopes, pa_dtype dtype, pa_kv_cache_dtype kv_cache_dtype,
+               float k_scale, float v_scale, void *stream) {
+  Call c;
+  c.mode = mode;
+  c.out = out;
+  c.exp_sums = exp_sums;
+  c.max_logits = max_logits;
+  c.tmp_out = tmp_out;
+  c.query = query;
+  c.key_cache = key_cache;
+  c.value_cache = value_cache;
+  c.num_seqs = num_seqs;
+  c.num_heads = num_heads;
+  c.num_kv_heads = num_kv_heads;
+  c.head_size = head_size;
+  c.scale = scale;
+  c.block_tables = block_tables;
+  c.max_num_blocks_per_seq = max_num_blocks_per_seq;
+  c.seq_lens = seq_lens;
+  c.num_blocks = num_blocks;
+  c.block_size = block_size;
+  c.max_seq_len = max_seq_len;
+  c.max_num_partitions = max_num_partitions;
+  c.alibi_slopes = alibi_slopes;
+  c.dtype = dtype;
+  c.kv_cache_dtype = kv_cache_dtype;
+  c.k_scale = k_scale;
+  c.v_scale = v_scale;
+  c.stream = reinterpret_cast<hipStream_t>(stream);
+  return c;
+}
+
+}  // namespace
+
+extern "C" {
+
+pa_status paged_attention_partition(pa_mode mode, void *out, float *exp_sums, float *max_logits,
+                                    float *tmp_out, const void *query, const void *key_cache,
+                                    const void *value_cache, int num_seqs, int num_heads,
+                                    int num_kv_heads, int head_size, float scale,
+                                    const int32_t *block_tables, int max_num_blocks_per_seq,
+                                    const int32_t *seq_lens, int num_blocks, int block_size,
+                                    int max_seq_len, int max_num_partitions,
+                                    const float *alibi_slopes, pa_dtype dtype,
+                                    pa_kv_cache_dtype kv_cache_dtype, float k_scale,
+                                    float v_scale, void *stream) {
+  return run_partition(make_call(mode, out, exp_sums, max_logits, tmp_out, query, key_cache,
+                                 value_cache, num_seqs, num_heads, num_kv_heads, head_size, scale,
+                                 block_tables, max_num_blocks_per_seq, seq_lens, num_blocks,
+                                 block_size, max_seq_len, max_num_partitions, alibi_slopes, dtype,
+                                 kv_cache_dtype, k_scale, v_scale, stream));
+}
+
+pa_status paged_attention_reduce(pa_mode mode, void *out, const float *exp_sums,
+                                 const float *max_logits, const float *tmp_out, int num_seqs,
+                                 int num_heads, int num_kv_heads, int head_size,
+                                 const int32_t *seq_lens, int max_seq_len, int max_num_partitions,
+                                 pa_dtype dtype, void *stream) {
+  return run_reduce(make_call(mode, out, const_cast<float *>(exp_sums),
+                              const_cast<float *>(max_logits), const_cast<float *>(tmp_out),
+                              nullptr, nullptr, nullptr, num_seqs, num_heads, num_kv_heads,
+                              head_size, 1.0f, nullptr, 0, seq_lens, 0, 16, max_seq_len,
+                              max_num_partitions, nullptr, dtype, PA_KV_AUTO, 1.0f, 1.0f, stream));
+}
+
+static pa_status two_phase(pa_mode mode, void *out, float *exp_sums, float *max_logits,
+                           float *tmp_out, const void *query, const void *key_cache,
+                           const void *value_cache, int num_seqs, int num_heads, int num_kv_heads,
+                           int head_size, float scale, const int32_t *block_tables,
+                           int max_num_blocks_per_seq, const int32_t *seq_lens, int num_blocks,
+                           int block_size, int max_seq_len, int max_num_partitions,
+                           const float *alibi_slopes, pa_dtype dtype,
+                           pa_kv_cache_dtype kv_cache_dtype, float k_scale, float v_scale,
+                           void *stream) {
+  const Call c = make_call(mode, out, exp_sums, max_logits, tmp_out, query, key_cache, value_cache,
+                           num_seqs, num_heads, num_kv_heads, head_size, scale, block_tables,
+                           max_num_blocks_per_seq, seq_lens, num_blocks, block_size, max_seq_len,
+                           max_num_partitions, alibi_slopes, dtype, kv_cache_dtype, k_scale,
+                           v_scale, stream);
+  // Validate both phases before launching either.
+  pa_status st = validate_common(c, true);
+  if (st != PA_OK) return st;
+  st = run_partition(c);
+  if (st != PA_OK) return st;
+  return run_reduce(c);
+}
+
+pa_status paged_attention_v1(void *out, const void *query, const void *key_cache,
+                             const void *value_cache, int num_seqs, int num_heads,
+                             int num_kv_heads, int head_size, float scale,
+                             const int32_t *block_tables, int max_num_blocks_per_seq,
+                             const int32_t *seq_lens, int num_blocks, int block_size,
+                             int max_seq_len, const float *alibi_slopes, pa_dtype dtype,
+                             pa_kv_cache_dtype kv_cache_dtype, float k_scale, float v_scale,
+                             void *stream) {
+  return run_partition(make_call(PA_MODE_V1, out, nullptr, nullptr, nullptr, query, key_cache,
+                                 value_cache, num_seqs, num_heads, num_kv_heads, head_size, scale,
+                                 block_tables, max_num_blocks_per_seq, seq_lens, num_blocks,
+                                 block_size, max_seq_len, 1, alibi_slopes, dtype, kv_cache_dtype,
+                                 k_scale, v_scale, stream));
+}
+
+pa_status paged_attention_v2(void *out, float *exp_sums, float *max_logits, float *tmp_out,
+                             const void *query, const void *key_cache, const void *value_cache,
+                             int num_seqs, int num_heads, int num_kv_heads, int head_size,
+                             float scale, const int32_t *block_tables, int max_num_blocks_per_seq,
+                             const int32_t *seq_lens, int num_blocks, int block_size,
+                             int max_seq_len, int max_num_partitions, const float *alibi_slopes,
+                             pa_dtype dtype, pa_kv_cache_dtype kv_cache_dtype, float k_scale,
+                             float v_scale, void *stream) {
+  return two_phase(PA_MODE_V2, out, exp_sums, max_logits, tmp_out, query, key_cache, value_cache,
+                   num_seqs, num_heads, num_kv_heads, head_size, scale, block_tables,
+                   max_num_blocks_per_seq, seq_lens, num_blocks, block_size, max_seq_len,
+                   max_num_partitions, alibi_slopes, dtype, kv_cache_dtype, k_scale, v_scale,
+                   stream);
+}
+
+pa_status paged_attention_auto(void *out, float *exp_sums, float *max_logits, float *tmp_out,
+                               const void *query, const void *key_cache, const void *value_cache,
+                               int num_seqs, int num_heads, int num_kv_heads, int head_size,
+                               float scale, const int32_t *block_tables,
+                               int max_num_blocks_per_seq, const int32_t *seq_lens,
+                               int num_blocks, int block_size, int max_seq_len,
+                               int max_num_partitions, const float *alibi_slopes, pa_dtype dtype,
+                               pa_kv_cache_dtype kv_cache_dtype, float k_scale, float v_scale,
+                               void *stream) {
+  return two_phase(PA_MODE_AUTO, out, exp_sums, max_logits, tmp_out, query, key_cache,
+                   value_cache, num_seqs, num_heads, num_kv_heads, head_size, scale, block_tables,
+                   max_num_blocks_per_seq, seq_lens, num_blocks, block_size, max_seq_len,
+                   max_num_partitions, alibi_slopes, dtype, kv_cache_dtype, k_scale, v_scale,
+                   stream);
+}
+
+int pa_partition_size(void) { return pa::kPartitionSize; }
+
+int pa_num_partitions(int max_seq_len) {
+  if (max_seq_len <= 0) return 1;
+  return ceil_div(max_seq_len, pa::kPartitionSize);
+}
+
+int pa_should_use_v2(int num_seqs, int num_kv_heads, int seq_len, int cu_count) {
+  const Tunables &t = tunables();
+  if ((long long)num_seqs * num_kv_heads < (long long)t.small_batch_factor * cu_count) return 1;
+  const long long tiles = (long long)num_kv_heads * (seq_len <= 0 ? 0 : ceil_div(seq_len, pa::kPartitionSize));
+  return tiles > (long long)t.tile_factor * cu_count ? 1 : 0;
+}
+
+pa_status pa_device_cu_count(int *cu_count) {
+  if (!cu_count) return PA_ERR_NULL_POINTER;
+  *cu_count = 0;
+  return cu_count_current(cu_count);
+}
+
+const char *pa_status_string(pa_status status) {
+  switch (status) {
+    case PA_OK: return "ok";
+    case PA_ERR_NULL_POINTER: return "a required pointer is NULL";
+    case PA_ERR_BAD_SHAPE: return "sizes are inconsistent or out of range";
+    case PA_ERR_MISALIGNED: return "a cache, query, out or tmp_out pointer is not 16-byte aligned";
+    case PA_ERR_UNSUPPORTED: return "unsupported head_size, block_size or dtype combination";
+    case PA_ERR_HIP: return "the HIP runtime reported an error";
+    case PA_ERR_BAD_ARGUMENT: return "non-finite scale or unknown enum value";
+  }
+  return "unknown status";
+}
+
+const char *pa_version(void) { return "0.1.0"; }
+
+}  // extern "C"

@@ -1,0 +1,171 @@
+// Device helpers for the gfx950 paged-attention kernels: element types and
+// conversions, 16-byte loads, dot products and wave64 cross-lane reductions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pa_params.h"
+
+namespace pa {
+
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// One byte of OCP FP8 E4M3FN storage.
+struct fp8e4m3 {
+  uint8_t bits;
+};
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ float bits_f(unsigned u) { return __builtin_bit_cast(float, u); }
+__device__ __forceinline__ unsigned f_bits(float f) { return __builtin_bit_cast(unsigned, f); }
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ---------------------------------------------------------------------------
+// 16-byte loads.  KV tiles are streamed once, so they bypass reuse-oriented
+// caching with the nontemporal hint.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ u32x4 load16_stream(const void *p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+}
+__device__ __forceinline__ u32x2 load8_stream(const void *p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(p));
+}
+__device__ __forceinline__ unsigned load4_stream(const void *p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const unsigned *>(p));
+}
+__device__ __forceinline__ u32x4 load16(const void *p) {
+  return *reinterpret_cast<const u32x4 *>(p);
+}
+
+// ---------------------------------------------------------------------------
+// Packed dot products with fp32 accumulation.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float dot2(float acc, unsigned a, unsigned b, __bf16) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
+                                         __builtin_bit_cast(bf16x2, b), acc, false);
+}
+__device__ __forceinline__ float dot2(float acc, unsigned a, unsigned b, _Float16) {
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a), __builtin_bit_cast(f16x2, b), acc,
+                                false);
+}
+
+// fp8 E4M3FN pair (bytes 0,1 or 2,3 of a word) -> packed 16-bit pair, exact.
+template <bool HI>
+__device__ __forceinline__ unsigned fp8x2_to(unsigned w, __bf16) {
+  return __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+}
+template <bool HI>
+__device__ __forceinline__ unsigned fp8x2_to(unsigned w, _Float16) {
+  return __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI));
+}
+
+// fp32 pair -> packed 16-bit pair (round to nearest even).
+__device__ __forceinline__ unsigned pack2(float a, float b, __bf16) {
+  bf16x2 v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(unsigned, v);
+}
+__device__ __forceinline__ unsigned pack2(float a, float b, _Float16) {
+  f16x2 v = {(_Float16)a, (_Float16)b};
+  return __builtin_bit_cast(unsigned, v);
+}
+
+template <typename T>
+__device__ __forceinline__ float to_f32(T v) {
+  return (float)v;
+}
+template <typename T>
+__device__ __forceinline__ T from_f32(float v) {
+  return (T)v;
+}
+
+// ---------------------------------------------------------------------------
+// Cross-lane operations (wave64).
+// ---------------------------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return bits_f(__builtin_amdgcn_mov_dpp((int)f_bits(v), CTRL, 0xF, 0xF, false));
+}
+
+// All lanes of each 16-lane row get the row's max / sum.
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp<0xB1>(v));   // quad_perm [1,0,3,2]
+  v = fmaxf(v, dpp<0x4E>(v));   // quad_perm [2,3,0,1]
+  v = fmaxf(v, dpp<0x124>(v));  // row_ror:4
+  v = fmaxf(v, dpp<0x128>(v));  // row_ror:8
+  return v;
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp<0xB1>(v);
+  v += dpp<0x4E>(v);
+  v += dpp<0x124>(v);
+  v += dpp<0x128>(v);
+  return v;
+}
+
+// v_permlane16_swap swaps the odd rows of its first operand with the even
+// rows of its second; v_permlane32_swap swaps the upper half of the first
+// with the lower half of the second.  Called as swap(lo, hi) and summed, a
+// lane whose bit (16 or 32) is clear ends with lo(self) + lo(partner) and a
+// lane whose bit is set ends with hi(self) + hi(partner): one instruction per
+// pair performs a "transpose-reduce" step.
+template <int M>
+__device__ __forceinline__ void swap_pair(float lo, float hi, float &a, float &b) {
+  static_assert(M == 16 || M == 32, "permlane swap distance");
+  if constexpr (M == 16) {
+    auto r = __builtin_amdgcn_permlane16_swap(f_bits(lo), f_bits(hi), false, false);
+    a = bits_f(r[0]);
+    b = bits_f(r[1]);
+  } else {
+    auto r = __builtin_amdgcn_permlane32_swap(f_bits(lo), f_bits(hi), false, false);
+    a = bits_f(r[0]);
+    b = bits_f(r[1]);
+  }
+}
+template <int M>
+__device__ __forceinline__ float xor_sum(float v) {
+  float a, b;
+  swap_pair<M>(v, v, a, b);
+  return a + b;
+}
+template <int M>
+__device__ __forceinline__ float xor_max(float v) {
+  float a, b;
+  swap_pair<M>(v, v, a, b);
+  return fmaxf(a, b);
+}
+
+__device__ __forceinline__ float readlane(float v, int lane) {
+  return bits_f(__builtin_amdgcn_readlane(f_bits(v), lane));
+}
+
+// Orders LDS traffic of one wave (no workgroup barrier needed: the data is
+// produced and consumed by the same wave).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// ---------------------------------------------------------------------------
+// Per-sequence path choice (host mirror: pa_should_use_v2).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ bool seq_uses_v2(const Params &p, int seq_len) {
+  if (p.mode == kModeV1) return false;
+  if (p.mode == kModeV2 || p.auto_all_v2) return true;
+  const int parts = (seq_len + kPartitionSize - 1) / kPartitionSize;
+  return (long long)p.num_kv_heads * parts > (long long)p.auto_tile_limit;
+}
+
+}  // namespace pa

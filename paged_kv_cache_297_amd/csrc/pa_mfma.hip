@@ -1,0 +1,35 @@
+// MFMA partition kernels: 16-bit query with a 16-bit or fp8 E4M3FN cache.
+#include "pa_launch.h"
+#include "pa_partition_mfma.h"
+
+namespace pa {
+
+template <typename QT, typename KVT>
+static hipError_t launch_mfma_t(const Params &p, int head_size, int block_size, dim3 grid,
+                                hipStream_t stream) {
+#define PA_MFMA_CASE(D, BS)                                                                 \
+  if (head_size == D && block_size == BS) {                                                 \
+    hipLaunchKernelGGL((pa_partition_mfma<QT, KVT, D, BS>), grid, dim3(kThreads), 0, stream, \
+                       p);                                                                  \
+    return hipGetLastError();                                                               \
+  }
+  PA_MFMA_CASE(64, 16)
+  PA_MFMA_CASE(64, 32)
+  PA_MFMA_CASE(128, 16)
+  PA_MFMA_CASE(128, 32)
+#undef PA_MFMA_CASE
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_partition_mfma(const Params &p, int q_dtype, bool kv_fp8, int head_size,
+                                 int block_size, dim3 grid, hipStream_t stream) {
+  if (q_dtype == kDtF16)
+    return kv_fp8 ? launch_mfma_t<_Float16, fp8e4m3>(p, head_size, block_size, grid, stream)
+                  : launch_mfma_t<_Float16, _Float16>(p, head_size, block_size, grid, stream);
+  if (q_dtype == kDtBF16)
+    return kv_fp8 ? launch_mfma_t<__bf16, fp8e4m3>(p, head_size, block_size, grid, stream)
+                  : launch_mfma_t<__bf16, __bf16>(p, head_size, block_size, grid, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace pa

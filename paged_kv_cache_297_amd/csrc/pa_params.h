@@ -1,0 +1,39 @@
+// Launch parameters shared by the host library and the gfx950 kernels.
+#pragma once
+
+#include <stdint.h>
+
+namespace pa {
+
+// Tokens per partition (page "BI-V100 PagedAttention V2 implementation",
+// module constant _PARTITION_SIZE).
+constexpr int kPartitionSize = 512;
+// Every partition-phase workgroup is 4 wave64s; wave w takes logical blocks
+// w, w+4, w+8, ... of its token range.
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+
+enum Mode : int { kModeV1 = 0, kModeV2 = 1, kModeAuto = 2 };
+
+struct Params {
+  void *out;            // [B, H, D] dtype
+  float *exp_sums;      // [B, H, P]
+  float *max_logits;    // [B, H, P]
+  float *tmp_out;       // [B, H, P, D]
+  const void *query;    // [B, H, D] dtype
+  const void *key_cache;    // [NB, Hkv, D/x, bs, x]
+  const void *value_cache;  // [NB, Hkv, D, bs]
+  const int32_t *block_tables;  // [B, max_num_blocks_per_seq]
+  const int32_t *seq_lens;      // [B]
+  const float *alibi_slopes;    // [H] or nullptr
+  int num_seqs, num_heads, num_kv_heads, group;  // group = H / Hkv
+  int max_num_blocks_per_seq, num_blocks, max_seq_len, max_num_partitions;
+  int head_groups;      // query-head groups per KV head; grid.y = Hkv * head_groups
+  int mode;             // Mode
+  int auto_all_v2;      // AUTO: every sequence takes v2 (small batch clause)
+  int auto_tile_limit;  // AUTO: v2 iff Hkv * ceil(L / 512) > auto_tile_limit
+  float scale_log2;     // scale * k_scale * log2(e): logits are kept in log2 units
+  float v_scale;
+};
+
+}  // namespace pa

@@ -1,0 +1,145 @@
+// Work decoding and the cross-wave merge / store epilogue shared by the two
+// partition-phase kernels (VALU and MFMA).
+//
+// Grid: x = partition (v2) or 0 (v1), y = KV head * head_groups + head group,
+// z = sequence.  Each workgroup owns one (sequence, KV head, query-head group)
+// and either one 512-token partition (v2) or the whole sequence (v1).
+#pragma once
+
+#include "pa_device.h"
+
+namespace pa {
+
+struct Work {
+  int seq, kvh, head0, nh;  // sequence, KV head, first query head, query heads in the group
+  int L, n_part, part;      // sequence length, its partitions, this workgroup's partition
+  int blk_begin, blk_end;   // logical blocks [blk_begin, blk_end) of this workgroup
+  int t_ref;                // last token of this workgroup's range (ALiBi reference)
+  bool v2;                  // partials are stored (v2) or out is written directly (v1)
+};
+
+template <typename QT, int D>
+__device__ __forceinline__ void store_out_row(const Params &p, int seq, int head, int d, float v) {
+  QT *out = reinterpret_cast<QT *>(p.out);
+  out[((size_t)seq * p.num_heads + head) * D + d] = from_f32<QT>(v);
+}
+
+// Partition slots a sequence does not use hold max_logit = -inf and
+// exp_sum = 0 (page "BI-V100 PagedAttention V2 implementation", the step
+// that zeroes out unused partitions).  tmp_out of those slots is not written.
+__device__ __forceinline__ void write_stat_padding(const Params &p, const Work &w, int first) {
+  const int count = p.max_num_partitions - first;
+  for (int idx = threadIdx.x; idx < w.nh * count; idx += kThreads) {
+    const int h = idx / count, slot = first + (idx - h * count);
+    const size_t row = ((size_t)w.seq * p.num_heads + w.head0 + h) * p.max_num_partitions + slot;
+    p.max_logits[row] = -__builtin_inff();
+    p.exp_sums[row] = 0.0f;
+  }
+}
+
+// Decodes blockIdx into a Work item.  Returns false when this workgroup has
+// nothing (more) to do; sequences of length 0 (out = 0) and with an invalid
+// length (out = NaN) are finished here by the partition-0 workgroup.
+template <typename QT, int D>
+__device__ __forceinline__ bool begin_work(const Params &p, int block_size, int group_slots,
+                                          Work &w) {
+  w.seq = blockIdx.z;
+  w.kvh = blockIdx.y / p.head_groups;
+  const int hg = blockIdx.y - w.kvh * p.head_groups;
+  w.head0 = w.kvh * p.group + hg * group_slots;
+  w.nh = min(group_slots, p.group - hg * group_slots);
+  w.L = p.seq_lens[w.seq];
+  const bool bad = (w.L < 0) || (w.L > p.max_seq_len);
+  w.v2 = seq_uses_v2(p, bad ? 0 : w.L);
+  w.n_part = bad ? 0 : (w.L + kPartitionSize - 1) / kPartitionSize;
+  w.part = blockIdx.x;
+  if (bad || w.L == 0) {
+    if (w.part != 0) return false;
+    const float fill = bad ? __builtin_nanf("") : 0.0f;
+    for (int idx = threadIdx.x; idx < w.nh * D; idx += kThreads)
+      store_out_row<QT, D>(p, w.seq, w.head0 + idx / D, idx % D, fill);
+    if (w.v2) {
+      write_stat_padding(p, w, bad ? 1 : 0);
+      if (bad && threadIdx.x < w.nh) {
+        const size_t row =
+            ((size_t)w.seq * p.num_heads + w.head0 + threadIdx.x) * p.max_num_partitions;
+        p.max_logits[row] = __builtin_nanf("");
+        p.exp_sums[row] = __builtin_nanf("");
+      }
+    }
+    return false;
+  }
+  const int n_logical = (w.L + block_size - 1) / block_size;
+  if (w.v2) {
+    if (w.part >= w.n_part) return false;
+    if (w.part == 0) write_stat_padding(p, w, w.n_part);
+    const int bpp = kPartitionSize / block_size;
+    w.blk_begin = w.part * bpp;
+    w.blk_end = min(w.blk_begin + bpp, n_logical);
+    w.t_ref = min((w.part + 1) * kPartitionSize, w.L) - 1;
+  } else {
+    if (w.part != 0) return false;
+    w.blk_begin = 0;
+    w.blk_end = n_logical;
+    w.t_ref = w.L - 1;
+  }
+  return true;
+}
+
+// Cross-wave merge and stores.  Wave wv left, for query head h of the group:
+//   sm_m[wv][h]  its running max (log2 units; -inf if it saw no token)
+//   sm_l[wv][h]  sum of exp2(s - m) over its tokens
+//   sm_o[wv][h][d] sum of exp2(s - m) * V[d] over its tokens
+// The workgroup result is the log-sum-exp combination of the four waves
+// (the same rescale as the V2 page's Phase 2, applied inside one partition).
+// A NaN in sm_l (an out-of-range block-table entry) makes every output of
+// the head NaN.  Must be called after a __syncthreads() that follows the LDS
+// writes.
+template <typename QT, int D, int GS, int OSTRIDE>
+__device__ __forceinline__ void finish_partition(const Params &p, const Work &w,
+                                                 const float (*sm_o)[GS][OSTRIDE],
+                                                 const float (*sm_m)[GS],
+                                                 const float (*sm_l)[GS]) {
+  const float nanv = __builtin_nanf("");
+  for (int idx = threadIdx.x; idx < w.nh * D; idx += kThreads) {
+    const int h = idx / D, d = idx - h * D;
+    float big_m = -__builtin_inff();
+#pragma unroll
+    for (int wv = 0; wv < kWaves; ++wv) big_m = fmaxf(big_m, sm_m[wv][h]);
+    float sum = 0.0f, acc = 0.0f;
+#pragma unroll
+    for (int wv = 0; wv < kWaves; ++wv) {
+      const float mw = sm_m[wv][h];
+      const float c = (mw == -__builtin_inff()) ? 0.0f : fast_exp2(mw - big_m);
+      sum += c * sm_l[wv][h];
+      acc += c * sm_o[wv][h][d];
+    }
+    float o = acc / sum * p.v_scale;
+    const int head = w.head0 + h;
+    // The kernels add ALiBi as slope * (t - t_ref), t_ref the last token of the
+    // workgroup's range (softmax inside the range is unchanged by the shift,
+    // and the tokens that carry weight keep small, precise logits); the stored
+    // max logit is in the absolute-position convention slope * t.
+    // One rounding: the product slope * t_ref is exact inside the fma.
+    float ml = p.alibi_slopes ? fmaf(p.alibi_slopes[head], (float)w.t_ref, big_m * kLn2)
+                              : big_m * kLn2;
+    // A wave that met an out-of-range block-table entry reports a NaN sum.
+    if (sum != sum) {
+      o = nanv;
+      ml = nanv;
+    }
+    if (w.v2) {
+      const size_t row = ((size_t)w.seq * p.num_heads + head) * p.max_num_partitions + w.part;
+      p.tmp_out[row * D + d] = o;
+      if (d == 0) {
+        p.exp_sums[row] = sum;
+        p.max_logits[row] = ml;
+      }
+      if (w.n_part == 1) store_out_row<QT, D>(p, w.seq, head, d, o);
+    } else {
+      store_out_row<QT, D>(p, w.seq, head, d, o);
+    }
+  }
+}
+
+}  // namespace pa

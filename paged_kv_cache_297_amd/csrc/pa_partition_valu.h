@@ -1,0 +1,409 @@
+// Partition-phase kernel, VALU form: for narrow GQA groups (and fp32), where
+// a 16-row MFMA tile would be mostly padding.
+//
+// Per (block, KV head) tile the wave issues NL coalesced 16-byte loads per
+// lane for K and NL for V: load i of lane l reads bytes [1024 i + 16 l,
+// +16) of the tile, so every wave instruction reads 1 KB of contiguous
+// memory (the lesson of the Neuron vectorised-KV-load PR: the paged gather is
+// bound by HBM fetch, so fetch whole tiles with wide loads).  In the K layout
+// [D/x][bs][x] that hands lane l token (l % bs) and 16-byte chunk
+// (i * 64/bs + l / bs); the 64/bs lanes that share a token combine their
+// partial dot products with permlane swaps that also transpose, so that
+// afterwards each lane holds whole logits for max(1, GP*bs/64) query heads.
+// The GQA group's query slices stay in registers for the whole workgroup.
+//
+// Softmax is online per wave (running max / sum in log2 units); P is passed
+// to the V layout through a small per-wave LDS buffer, rounded to the V
+// element type as the V2 page does before its weighted sum.
+#pragma once
+
+#include "pa_partition_common.h"
+
+namespace pa {
+
+// Per (query type, KV storage type): how 16-byte K chunks meet the query and
+// how 16-byte V units meet P.
+template <typename QT, typename KVT>
+struct ValuTraits;
+
+template <>
+struct ValuTraits<float, float> {
+  static constexpr int kBytes = 4;  // storage bytes per KV element
+  static constexpr int kQW = 4;     // 32-bit query words per 16-byte K chunk
+  static constexpr int kPW = 4;     // 32-bit P words per 16-byte V unit
+  using PV = float;                 // type P is rounded to before P.V
+  __device__ static void load_q(const float *q, unsigned (&w)[kQW]) {
+    const u32x4 v = load16(q);
+    w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+  }
+  __device__ static float qk(float acc, const unsigned (&q)[kQW], const u32x4 &k) {
+    acc = fmaf(bits_f(q[0]), bits_f(k.x), acc);
+    acc = fmaf(bits_f(q[1]), bits_f(k.y), acc);
+    acc = fmaf(bits_f(q[2]), bits_f(k.z), acc);
+    acc = fmaf(bits_f(q[3]), bits_f(k.w), acc);
+    return acc;
+  }
+  __device__ static void v_words(const u32x4 &v, unsigned (&w)[kPW]) {
+    w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+  }
+  __device__ static float pv(float acc, const unsigned (&pw)[kPW], const unsigned (&vw)[kPW]) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc = fmaf(bits_f(pw[e]), bits_f(vw[e]), acc);
+    return acc;
+  }
+  // Zero the V elements of tokens >= nv (first = token of element 0).
+  __device__ static void mask_v(unsigned (&w)[kPW], int first, int nv) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (first + e >= nv) w[e] = 0u;
+  }
+};
+
+template <typename T16>
+struct ValuTraits16 {
+  static constexpr int kBytes = 2;
+  static constexpr int kQW = 4;
+  static constexpr int kPW = 4;
+  using PV = T16;
+  __device__ static void load_q(const T16 *q, unsigned (&w)[kQW]) {
+    const u32x4 v = load16(q);
+    w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+  }
+  __device__ static float qk(float acc, const unsigned (&q)[kQW], const u32x4 &k) {
+    acc = dot2(acc, q[0], k.x, T16());
+    acc = dot2(acc, q[1], k.y, T16());
+    acc = dot2(acc, q[2], k.z, T16());
+    acc = dot2(acc, q[3], k.w, T16());
+    return acc;
+  }
+  __device__ static void v_words(const u32x4 &v, unsigned (&w)[kPW]) {
+    w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+  }
+  __device__ static float pv(float acc, const unsigned (&pw)[kPW], const unsigned (&vw)[kPW]) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc = dot2(acc, pw[e], vw[e], T16());
+    return acc;
+  }
+  __device__ static void mask_v(unsigned (&w)[kPW], int first, int nv) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (first + 2 * e >= nv) w[e] = 0u;
+      else if (first + 2 * e + 1 >= nv) w[e] &= 0xFFFFu;
+    }
+  }
+};
+template <> struct ValuTraits<__bf16, __bf16> : ValuTraits16<__bf16> {};
+template <> struct ValuTraits<_Float16, _Float16> : ValuTraits16<_Float16> {};
+
+// fp8 E4M3FN cache: K is widened exactly to the query's 16-bit type for the
+// dot products, V to fp16 (exact for every E4M3 value) with P in fp16.
+template <typename T16>
+struct ValuTraitsFp8 {
+  static constexpr int kBytes = 1;
+  static constexpr int kQW = 8;   // 16 fp8 dims per chunk -> 8 packed pairs
+  static constexpr int kPW = 8;   // 16 fp8 tokens per V unit -> 8 fp16 pairs
+  using PV = _Float16;
+  __device__ static void load_q(const T16 *q, unsigned (&w)[kQW]) {
+    const u32x4 a = load16(q), b = load16(q + 8);
+    w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
+    w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
+  }
+  __device__ static float qk(float acc, const unsigned (&q)[kQW], const u32x4 &k) {
+    const unsigned kw[4] = {k.x, k.y, k.z, k.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc = dot2(acc, q[2 * e], fp8x2_to<false>(kw[e], T16()), T16());
+      acc = dot2(acc, q[2 * e + 1], fp8x2_to<true>(kw[e], T16()), T16());
+    }
+    return acc;
+  }
+  __device__ static void v_words(const u32x4 &v, unsigned (&w)[kPW]) {
+    const unsigned vw[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      w[2 * e] = fp8x2_to<false>(vw[e], _Float16());
+      w[2 * e + 1] = fp8x2_to<true>(vw[e], _Float16());
+    }
+  }
+  __device__ static float pv(float acc, const unsigned (&pw)[kPW], const unsigned (&vw)[kPW]) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc = dot2(acc, pw[e], vw[e], _Float16());
+    return acc;
+  }
+  // Applied to the widened words: word e holds tokens first+2e, first+2e+1.
+  __device__ static void mask_v(unsigned (&w)[kPW], int first, int nv) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      if (first + 2 * e >= nv) w[e] = 0u;
+      else if (first + 2 * e + 1 >= nv) w[e] &= 0xFFFFu;
+    }
+  }
+};
+template <> struct ValuTraits<__bf16, fp8e4m3> : ValuTraitsFp8<__bf16> {};
+template <> struct ValuTraits<_Float16, fp8e4m3> : ValuTraitsFp8<_Float16> {};
+
+// Which query heads a lane holds after the transpose-reduce over the R = 64/bs
+// lanes of a token: lane group r = lane / bs holds heads head_base(r) ..
+// head_base(r) + NF - 1.  Each reduce step over lane bit (bs << b) halves the
+// set of heads a lane carries while it is >= 2, keeping the upper half when
+// the bit is set (the permlane swap pairing above).
+template <int GP, int BS>
+struct HeadMap {
+  static constexpr int R = 64 / BS;
+  static constexpr int NF = GP >= R ? GP / R : 1;
+  static constexpr int head_base(int r) {
+    int h = 0, n = GP, b = 0;
+    for (int m = BS; m < 64; m *= 2, ++b) {
+      if (n >= 2) {
+        h += ((r >> b) & 1) * (n / 2);
+        n /= 2;
+      }
+    }
+    return h;
+  }
+  static constexpr int src_group(int h) {
+    for (int r = 0; r < R; ++r)
+      if (head_base(r) <= h && h < head_base(r) + NF) return r;
+    return 0;
+  }
+};
+
+template <int M, int N>
+__device__ __forceinline__ void xreduce_step(float *v) {
+  if constexpr (N >= 2) {
+#pragma unroll
+    for (int j = 0; j < N / 2; ++j) {
+      float a, b;
+      swap_pair<M>(v[j], v[N / 2 + j], a, b);
+      v[j] = a + b;
+    }
+  } else {
+    v[0] = xor_sum<M>(v[0]);
+  }
+}
+
+template <int GP, int BS>
+__device__ __forceinline__ void transpose_reduce(float (&v)[GP]) {
+  if constexpr (BS == 16) {
+    xreduce_step<16, GP>(v);
+    xreduce_step<32, (GP >= 2 ? GP / 2 : 1)>(v);
+  } else {
+    xreduce_step<32, GP>(v);
+  }
+}
+
+template <int BS>
+__device__ __forceinline__ float token_group_max(float v) {
+  v = row16_max(v);
+  if constexpr (BS == 32) v = xor_max<16>(v);
+  return v;
+}
+template <int BS>
+__device__ __forceinline__ float token_group_sum(float v) {
+  v = row16_sum(v);
+  if constexpr (BS == 32) v = xor_sum<16>(v);
+  return v;
+}
+
+// Sum over the VPD lanes that hold the same V dim (adjacent lanes).
+template <int VPD>
+__device__ __forceinline__ float dim_group_sum(float v) {
+  if constexpr (VPD >= 2) v += dpp<0xB1>(v);  // xor 1
+  if constexpr (VPD >= 4) v += dpp<0x4E>(v);  // xor 2
+  if constexpr (VPD >= 8) v += __shfl_xor(v, 4);
+  static_assert(VPD <= 8, "V unit layout");
+  return v;
+}
+
+template <typename QT, typename KVT, int D, int BS, int GP>
+__global__ void __launch_bounds__(kThreads) pa_partition_valu(const Params p) {
+  using T = ValuTraits<QT, KVT>;
+  using HM = HeadMap<GP, BS>;
+  using PV = typename T::PV;
+  constexpr int ESZ = T::kBytes;
+  constexpr int X = 16 / ESZ;               // elements per 16-byte chunk / unit
+  constexpr int R = 64 / BS;                // lanes per token in the K layout
+  constexpr int TILE = D * BS * ESZ;        // bytes of one (block, KV head) K or V tile
+  constexpr int NL = TILE / 1024;           // 16-byte loads per lane per tile
+  constexpr int VPD = BS * ESZ / 16;        // 16-byte units per V dim row
+  constexpr int NF = HM::NF;
+  static_assert(NL * 1024 == TILE, "tile must be a multiple of 1 KB");
+  static_assert(GP * NL * T::kQW <= 64, "query slice must fit in 64 VGPRs");
+
+  __shared__ float sm_o[kWaves][GP][D];
+  __shared__ float sm_m[kWaves][GP];
+  __shared__ float sm_l[kWaves][GP];
+  __shared__ __attribute__((aligned(16))) PV sm_p[kWaves][2][GP][BS];
+
+  Work w;
+  if (!begin_work<QT, D>(p, BS, GP, w)) return;
+
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int tok = lane % BS;
+  const int r = lane / BS;
+  const int tg = lane % VPD;
+
+  // Query slices of the group's heads for this lane's K chunks.
+  unsigned qw[GP][NL][T::kQW];
+  {
+    const QT *qbase = reinterpret_cast<const QT *>(p.query) +
+                      ((size_t)w.seq * p.num_heads + w.head0) * D;
+#pragma unroll
+    for (int h = 0; h < GP; ++h)
+#pragma unroll
+      for (int i = 0; i < NL; ++i) {
+        if (h < w.nh) {
+          T::load_q(qbase + h * D + (i * R + r) * X, qw[h][i]);
+        } else {
+#pragma unroll
+          for (int e = 0; e < T::kQW; ++e) qw[h][i][e] = 0u;
+        }
+      }
+  }
+  // ALiBi slope (log2 units) of each head slot this lane owns after the reduce.
+  float slope2[NF];
+#pragma unroll
+  for (int j = 0; j < NF; ++j) {
+    int hb = 0;
+#pragma unroll
+    for (int rr = 0; rr < R; ++rr)
+      if (rr == r) hb = HM::head_base(rr);
+    const int h = hb + j;
+    slope2[j] = (p.alibi_slopes && h < w.nh) ? p.alibi_slopes[w.head0 + h] * kLog2e : 0.0f;
+  }
+  int my_head_base = 0;
+#pragma unroll
+  for (int rr = 0; rr < R; ++rr)
+    if (rr == r) my_head_base = HM::head_base(rr);
+
+  float m_run[NF], l_run[NF];
+#pragma unroll
+  for (int j = 0; j < NF; ++j) {
+    m_run[j] = -__builtin_inff();
+    l_run[j] = 0.0f;
+  }
+  float acc[GP][NL];
+#pragma unroll
+  for (int h = 0; h < GP; ++h)
+#pragma unroll
+    for (int i = 0; i < NL; ++i) acc[h][i] = 0.0f;
+
+  const char *kcache = reinterpret_cast<const char *>(p.key_cache);
+  const char *vcache = reinterpret_cast<const char *>(p.value_cache);
+  const int32_t *btab = p.block_tables + (size_t)w.seq * p.max_num_blocks_per_seq;
+  const size_t head_off = (size_t)w.kvh * TILE;
+  const size_t blk_stride = (size_t)p.num_kv_heads * TILE;
+  bool poisoned = false;
+
+  struct Tile {
+    u32x4 k[NL], v[NL];
+  };
+  // Out-of-range block-table entries are redirected to block 0 (always
+  // addressable) and reported through the poison flag.
+  auto load_tile = [&](int blk) {
+    int phys = btab[blk];
+    if (phys < 0 || phys >= p.num_blocks) {
+      poisoned = true;
+      phys = 0;
+    }
+    const char *kb = kcache + (size_t)phys * blk_stride + head_off + 16 * lane;
+    const char *vb = vcache + (size_t)phys * blk_stride + head_off + 16 * lane;
+    Tile t;
+#pragma unroll
+    for (int i = 0; i < NL; ++i) t.k[i] = load16_stream(kb + 1024 * i);
+#pragma unroll
+    for (int i = 0; i < NL; ++i) t.v[i] = load16_stream(vb + 1024 * i);
+    return t;
+  };
+
+  auto process = [&](int blk, int parity, const Tile &tl) {
+    // Logits: partial dots over this lane's chunks, then transpose-reduce.
+    float s[GP];
+#pragma unroll
+    for (int h = 0; h < GP; ++h) {
+      float a = 0.0f;
+#pragma unroll
+      for (int i = 0; i < NL; ++i) a = T::qk(a, qw[h][i], tl.k[i]);
+      s[h] = a;
+    }
+    transpose_reduce<GP, BS>(s);
+    const int t_abs = blk * BS + tok;
+    float alpha[NF], pj[NF];
+#pragma unroll
+    for (int j = 0; j < NF; ++j) {
+      float x = s[j] * p.scale_log2 + slope2[j] * (float)(t_abs - w.t_ref);
+      x = (t_abs < w.L) ? x : -__builtin_inff();
+      const float bm = token_group_max<BS>(x);
+      const float m_new = fmaxf(m_run[j], bm);
+      alpha[j] = (m_new == -__builtin_inff()) ? 1.0f : fast_exp2(m_run[j] - m_new);
+      pj[j] = fast_exp2(x - m_new);
+      l_run[j] = l_run[j] * alpha[j] + pj[j];
+      m_run[j] = m_new;
+    }
+    // P into the V layout through LDS.
+#pragma unroll
+    for (int j = 0; j < NF; ++j) sm_p[wv][parity][my_head_base + j][tok] = (PV)pj[j];
+    wave_lds_sync();
+    // Rescale factor of every head, from the lanes that own it.
+    float a_bc[GP];
+#pragma unroll
+    for (int h = 0; h < GP; ++h)
+      a_bc[h] = readlane(alpha[h - HM::head_base(HM::src_group(h))], HM::src_group(h) * BS);
+    const int nv = w.L - blk * BS;  // valid tokens in this block (>= 1)
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      unsigned vw[T::kPW];
+      T::v_words(tl.v[i], vw);
+      if (nv < BS) T::mask_v(vw, tg * X, nv);
+#pragma unroll
+      for (int h = 0; h < GP; ++h) {
+        const float a_h = a_bc[h];
+        const unsigned *pp = reinterpret_cast<const unsigned *>(&sm_p[wv][parity][h][tg * X]);
+        unsigned pw[T::kPW];
+#pragma unroll
+        for (int e = 0; e < T::kPW; ++e) pw[e] = pp[e];
+        acc[h][i] = T::pv(acc[h][i] * a_h, pw, vw);
+      }
+    }
+  };
+
+  // Two tiles in flight: the next block's loads are issued before the
+  // current block is consumed (ping-pong, no register copies).
+  int blk = w.blk_begin + wv;
+  Tile ta, tb;
+  if (blk < w.blk_end) ta = load_tile(blk);
+  while (blk < w.blk_end) {
+    if (blk + kWaves < w.blk_end) tb = load_tile(blk + kWaves);
+    process(blk, 0, ta);
+    blk += kWaves;
+    if (blk >= w.blk_end) break;
+    if (blk + kWaves < w.blk_end) ta = load_tile(blk + kWaves);
+    process(blk, 1, tb);
+    blk += kWaves;
+  }
+
+  // Wave totals per head, then the cross-wave merge.
+#pragma unroll
+  for (int j = 0; j < NF; ++j) l_run[j] = token_group_sum<BS>(l_run[j]);
+#pragma unroll
+  for (int h = 0; h < GP; ++h) {
+    const int g = HM::src_group(h);
+    const int j = h - HM::head_base(g);
+    const float mh = readlane(m_run[j], g * BS);
+    const float lh = readlane(l_run[j], g * BS);
+    if (lane == 0) {
+      sm_m[wv][h] = mh;
+      sm_l[wv][h] = poisoned ? __builtin_nanf("") : lh;
+    }
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      const float v = dim_group_sum<VPD>(acc[h][i]);
+      if (tg == 0) sm_o[wv][h][(64 * i + lane) / VPD] = v;
+    }
+  }
+  __syncthreads();
+  finish_partition<QT, D, GP, D>(p, w, sm_o, sm_m, sm_l);
+}
+
+}  // namespace pa

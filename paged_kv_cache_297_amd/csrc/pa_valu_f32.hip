@@ -1,0 +1,9 @@
+// VALU partition kernels, fp32 query and cache.
+#include "pa_valu_dispatch.h"
+
+namespace pa {
+hipError_t launch_partition_valu_f32(const Params &p, int head_size, int block_size, int gp,
+                                     dim3 grid, hipStream_t stream) {
+  return launch_valu<float, float>(p, head_size, block_size, gp, grid, stream);
+}
+}  // namespace pa

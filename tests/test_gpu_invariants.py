@@ -1,0 +1,144 @@
+"""GPU invariants of the HIP path: v2 with one partition is bitwise v1,
+block-table permutation and repeated runs are bitwise stable, NaN poison in
+bytes the kernels must not read changes nothing, a sequence's result does not
+depend on the rest of the batch, q = 0 gives mean(V), and the edge cases
+(empty and invalid lengths, out-of-range block ids) behave as the header
+states."""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import pa_oracle as O
+from paged_kv_cache_297_amd import binding as B
+from paged_kv_cache_297_amd import workloads as W
+from tests import gpu_helpers as H
+
+pytestmark = pytest.mark.gpu
+
+SHAPES = {
+    "fp32": dict(number=1),
+    "gqa_bf16": dict(number=2),
+    "fp16_g4": dict(number=3),
+    "alibi_bf16": dict(number=4),
+    "fp8": dict(number=5),
+}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _require_gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    B.load_library()
+
+
+@pytest.mark.parametrize("shape", list(SHAPES))
+def test_v2_single_partition_is_bitwise_v1(shape):
+    wl = W.make_workload(SHAPES[shape]["number"], lens=[1, 17, 300, 511, 512])
+    a = H.run(wl, "v1")
+    b = H.run(wl, "v2")
+    assert np.array_equal(a["out"], b["out"])
+    assert np.array_equal(b["tmp_out"][:, :, 0, :], b["out"]) or wl.dtype != torch.float32
+
+
+@pytest.mark.parametrize("shape", list(SHAPES))
+@pytest.mark.parametrize("path", ["v2", "v1"])
+def test_block_table_permutation_is_bitwise(shape, path):
+    wl = W.make_workload(SHAPES[shape]["number"], lens=[700, 1500, 33])
+    base = H.run(wl, path)
+    g = torch.Generator(device="cpu").manual_seed(3)
+    nb = wl.key_cache.shape[0]
+    perm = torch.randperm(nb, generator=g).to(wl.key_cache.device)  # old block i -> perm[i]
+    kc = torch.empty_like(wl.key_cache); kc[perm] = wl.key_cache
+    vc = torch.empty_like(wl.value_cache); vc[perm] = wl.value_cache
+    wl.key_cache, wl.value_cache = kc, vc
+    wl.block_tables = perm.to(torch.int32)[wl.block_tables.long()].contiguous()
+    moved = H.run(wl, path)
+    for k in base:
+        assert np.array_equal(base[k], moved[k], equal_nan=True), k
+
+
+@pytest.mark.parametrize("shape", list(SHAPES))
+def test_repeat_runs_are_bitwise(shape):
+    wl = W.make_workload(SHAPES[shape]["number"], lens=[2000, 513, 64])
+    a, b = H.run(wl, "v2"), H.run(wl, "v2")
+    for k in a:
+        assert np.array_equal(a[k], b[k], equal_nan=True), k
+
+
+@pytest.mark.parametrize("shape", list(SHAPES))
+@pytest.mark.parametrize("path", ["v2", "v1"])
+def test_nan_poison_is_never_read(shape, path):
+    """NaN in unused pool blocks, past-the-end slots and unused table entries."""
+    lens = [37, 700, 1025, 16]
+    num = SHAPES[shape]["number"]
+    clean = H.run(W.make_workload(num, lens=lens), path)
+    dirty = H.run(W.make_workload(num, lens=lens, poison=True), path)
+    assert np.isfinite(dirty["out"]).all()
+    assert np.array_equal(clean["out"], dirty["out"])
+
+
+def test_batch_independence():
+    lens = [3000, 40, 1200, 517]
+    full = H.run(W.make_workload(2, lens=lens), "v2")
+    for s, L in enumerate(lens):
+        wl = W.make_workload(2, lens=lens)
+        # Same bytes, batch restricted to one sequence.
+        one = W.Workload(**{**wl.__dict__})
+        one.num_seqs = 1
+        one.query = wl.query[s:s + 1].contiguous()
+        one.block_tables = wl.block_tables[s:s + 1].contiguous()
+        one.seq_lens = wl.seq_lens[s:s + 1].contiguous()
+        one.lens = wl.lens[s:s + 1]
+        one.max_seq_len = int(L)
+        one.max_num_partitions = O.num_partitions(int(L))
+        alone = H.run(one, "v2")
+        assert np.array_equal(alone["out"][0], full["out"][s])
+
+
+@pytest.mark.parametrize("number", [1, 2, 5])
+def test_zero_query_gives_mean_value(number):
+    wl = W.make_workload(number, lens=[1000, 77])
+    wl.query.zero_()
+    res = H.run(wl, "v2")
+    ref = H.oracle(wl)
+    tol = H.TOL[wl.kv_kind]
+    # The oracle's out is the plain mean of V here; compare, and check exp_sums = counts.
+    H.check_close(res["out"], ref["out_v1"], tol, "q=0 out")
+    assert np.array_equal(res["exp_sums"][0, :, :2], np.tile([512.0, 488.0], (wl.num_heads, 1)))
+    assert np.all(res["max_logits"][:, :, 0] == 0.0)
+
+
+def test_padding_is_exact():
+    wl = W.make_workload(2, lens=[100, 1300])
+    res = H.run(wl, "v2")
+    assert np.all(np.isneginf(res["max_logits"][0, :, 1:]))
+    assert np.all(res["exp_sums"][0, :, 1:] == 0.0)
+    assert np.all(np.isneginf(res["max_logits"][1, :, 3:]))
+    assert np.all(res["exp_sums"][1, :, 3:] == 0.0)
+
+
+@pytest.mark.parametrize("path", ["v1", "v2", "auto"])
+def test_empty_and_invalid_lengths(path):
+    wl = W.make_workload(2, lens=[0, 700, 33])
+    # An invalid length (above max_seq_len) on sequence 2.
+    wl.seq_lens[2] = wl.max_seq_len + 5
+    res = H.run(wl, path)
+    assert np.all(res["out"][0] == 0.0)
+    assert np.isnan(res["out"][2]).all()
+    assert np.isfinite(res["out"][1]).all()
+    wl.seq_lens[2] = 33
+    ref = H.oracle(wl, [1])
+    H.check_close(res["out"][1], ref["out_v1"][1], H.TOL[wl.kv_kind], "valid neighbour")
+    if path == "v2":
+        assert np.all(np.isneginf(res["max_logits"][0])) and np.all(res["exp_sums"][0] == 0)
+
+
+@pytest.mark.parametrize("path", ["v1", "v2"])
+@pytest.mark.parametrize("number", [2, 3, 5])
+def test_out_of_range_block_id_gives_nan_for_that_sequence_only(path, number):
+    wl = W.make_workload(number, lens=[900, 600])
+    nb = wl.key_cache.shape[0]
+    wl.block_tables[0, 1] = nb + 1000
+    res = H.run(wl, path)
+    assert np.isnan(res["out"][0]).all()
+    assert np.isfinite(res["out"][1]).all()
