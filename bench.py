@@ -1,0 +1,283 @@
+"""Paged-attention decode benchmark on one MI355X.
+
+One step = one pass of the whole decode hot path over one batch: the
+per-sequence v1/v2 choice, Phase 1 (partition kernel) and Phase 2 (reduce
+kernel), through the library's C ABI.  The default workload is the GQA bf16
+decode batch (64 sequences, 28 query / 4 KV heads, head size 128, block size
+16, lengths uniform in [1024, 8192]).
+
+Inputs are resident in HBM before timing.  By default the step rotates over
+``--copies`` independent copies of the KV pool (4 x ~0.6 GB), so the 256 MB
+Infinity Cache cannot serve one step's KV from the previous step; ``--hot``
+times a single copy instead.  W warm-up steps, then exactly K timed steps
+between device synchronisations.  HIP events on the library's stream bracket
+each launch, giving the average partition-kernel duration used for the
+roofline.  The fp64 CPU oracle is timed on a bounded sample of the same
+workload for the CPU baseline.
+
+Prints one JSON line (stdout); progress goes to stderr.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "paged-attn decode µs/step + effective KV HBM GB/s (% of peak), 1 MI355X"
+HBM_PEAK_GBS = 8000.0
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = ("pa_partition_mfma.h", "pa_partition_valu.h", "pa_partition_common.h",
+                  "pa_device.h", "pa_params.h", "pa_reduce.hip", "pa_api.cpp")
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "paged_kv_cache_297_amd", "csrc")
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_bytes(wl, path: str, cu: int, B) -> dict:
+    """Bytes each launch must move at minimum (each KV byte once per KV head)."""
+    import numpy as np
+    lens = wl.lens.astype(np.int64)
+    esz_q = wl.query.element_size()
+    kv = wl.kv_bytes()
+    q = wl.num_seqs * wl.num_heads * wl.head_size * esz_q
+    out = q
+    blocks = int(((lens + wl.block_size - 1) // wl.block_size).sum())
+    table = blocks * 4 + wl.num_seqs * 4
+    parts = np.where(lens > 0, (lens + 511) // 512, 0)
+    if path == "v1":
+        v2 = np.zeros_like(lens, dtype=bool)
+    elif path == "v2":
+        v2 = np.ones_like(lens, dtype=bool)
+    else:
+        v2 = np.array([B.should_use_v2(wl.num_seqs, wl.num_kv_heads, int(L), cu) for L in lens])
+    h, d = wl.num_heads, wl.head_size
+    tmp = int((parts * v2).sum()) * h * d * 4
+    stats = int((v2 * wl.max_num_partitions).sum()) * h * 8   # values and padding
+    multi = v2 & (parts > 1)
+    out_p1 = int((~multi).sum()) * h * d * esz_q
+    out_p2 = int(multi.sum()) * h * d * esz_q
+    reduce_read = int((parts * multi).sum()) * h * (d * 4 + 8)
+    return {"kv": kv, "partition": kv + q + table + tmp + stats + out_p1,
+            "reduce": reduce_read + out_p2 + wl.num_seqs * 4,
+            "step": kv + q + table + tmp + stats + out + reduce_read}
+
+
+def read_traffic(workload_name: str, src_hash: str):
+    """HBM bytes per partition launch from the committed counter summary, if
+    it was measured on the current kernel sources."""
+    path = os.path.join(PROFILES, f"traffic_pa_partition_{workload_name}.md")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if line.startswith("- ") and ":" in line:
+                k, v = line[2:].split(":", 1)
+                vals[k.strip()] = v.strip().strip("`")
+    if vals.get("kernel_source_hash") != src_hash:
+        return None
+    try:
+        return int(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(wl, budget_s: float) -> dict:
+    """The fp64 oracle, single-threaded, on whole sequences of the same batch
+    until ``budget_s`` of CPU time is spent (at least one sequence)."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import pa_oracle as O
+    from paged_kv_cache_297_amd import workloads as W
+
+    alibi = None if wl.alibi_slopes is None else wl.alibi_slopes.cpu().double().numpy()
+    done, kv_done, spent = 0, 0, 0.0
+    with threadpool_limits(1):
+        for s in range(wl.num_seqs):
+            host = W.host_subset(wl, [s])
+            t0 = time.perf_counter()
+            O.paged_attention(host["query"], host["key_cache"], host["value_cache"],
+                              host["block_tables"], host["seq_lens"], wl.scale,
+                              q_kind=wl.q_kind, kv_kind=wl.kv_kind, k_scale=wl.k_scale,
+                              v_scale=wl.v_scale, alibi_slopes=alibi,
+                              max_num_partitions=wl.max_num_partitions, seqs=[s])
+            spent += time.perf_counter() - t0
+            done += 1
+            kv_done += int(wl.lens[s]) * wl.num_kv_heads * wl.head_size * 2 * wl.kv_elem_bytes
+            if spent >= budget_s:
+                break
+    gbs = kv_done / spent / 1e9
+    return {"value": round(gbs, 5), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": (f"{done} of {wl.num_seqs} sequences of the same batch "
+                       f"({kv_done / 1e6:.1f} MB of KV), v1 + v2 partials + merge in fp64, "
+                       f"1 thread, {spent:.1f} s; device-to-host copies excluded"),
+            "us_per_step_extrapolated": round(spent / kv_done * wl.kv_bytes() * 1e6, 1)}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--path", default="auto", choices=["auto", "v2", "v1"])
+    ap.add_argument("--copies", type=int, default=4)
+    ap.add_argument("--hot", action="store_true", help="one copy of the inputs (cache-hot)")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="also run a plain device copy of MIB MiB (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the decode path "
+              "has no multi-GPU part in this library.", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    from paged_kv_cache_297_amd import binding as B
+    from paged_kv_cache_297_amd import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    B.load_library()
+    torch.cuda.set_device(0)
+    copies = 1 if args.hot else max(1, args.copies)
+    log(f"building workload {args.workload} x{copies}")
+    wls = [W.make_workload(args.workload, device="cuda", seed=1000 + args.workload)]
+    base = wls[0]
+    for c in range(1, copies):
+        # Same bytes at other addresses: identical work, no cache reuse across steps.
+        w2 = W.Workload(**{**base.__dict__})
+        w2.key_cache = base.key_cache.clone()
+        w2.value_cache = base.value_cache.clone()
+        w2.query = base.query.clone()
+        w2.block_tables = base.block_tables.clone()
+        wls.append(w2)
+    outs = [wl.alloc_outputs() for wl in wls]
+    cu = B.device_cu_count()
+    stream = torch.cuda.current_stream()
+
+    def launch(i: int, ev=None):
+        wl = wls[i % copies]
+        out, es, ml, to = outs[i % copies]
+        common = (out, es, ml, to, wl.query, wl.key_cache, wl.value_cache, wl.num_kv_heads,
+                  wl.scale, wl.block_tables, wl.seq_lens, wl.block_size, wl.max_seq_len)
+        kw = dict(alibi_slopes=wl.alibi_slopes, kv_cache_dtype=wl.kv_cache_dtype,
+                  k_scale=wl.k_scale, v_scale=wl.v_scale, stream=stream)
+        if ev is not None:
+            ev[0].record(stream)
+        B.paged_attention_partition(args.path, *common, **kw)
+        if ev is not None:
+            ev[1].record(stream)
+        B.paged_attention_reduce(args.path, out, es, ml, to, wl.seq_lens, wl.num_kv_heads,
+                                 wl.max_seq_len, stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for i in range(args.warmup):
+        launch(i)
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    log(f"timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        launch(i, events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    part_ms = np.array([e[0].elapsed_time(e[1]) for e in events])
+    red_ms = np.array([e[1].elapsed_time(e[2]) for e in events])
+    step_ms = np.array([e[0].elapsed_time(e[2]) for e in events])
+
+    if args.calibrate_copy:
+        n = args.calibrate_copy * (1 << 20)
+        src = torch.empty(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"calibration copy: {n} bytes x3")
+
+    ms_per_step = wall * 1e3 / args.steps
+    ab = algorithmic_bytes(base, args.path, cu, B)
+    kv_gbs = ab["kv"] / (ms_per_step * 1e-3) / 1e9
+    part_avg = float(part_ms.mean())
+    achieved = ab["partition"] / (part_avg * 1e-3) / 1e9
+    src_hash = kernel_source_hash()
+    traffic = read_traffic(base.name, src_hash) if copies > 1 else None
+    dtype = {torch.float32: "f32", torch.float16: "f16", torch.bfloat16: "bf16"}[base.dtype]
+    if base.kv_cache_dtype == "fp8_e4m3":
+        dtype = f"{dtype} (fp8 e4m3 KV)"
+    lens = base.lens
+    result = {
+        "metric": METRIC,
+        "value": round(kv_gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "us_per_step": round(ms_per_step * 1e3, 2),
+        "pct_of_peak": round(100.0 * kv_gbs / HBM_PEAK_GBS, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": (f"{base.name}: paged-attention decode, num_seqs={base.num_seqs}, "
+                         f"num_heads={base.num_heads}, num_kv_heads={base.num_kv_heads}, "
+                         f"head_size={base.head_size}, block_size={base.block_size}, "
+                         f"seq_lens {int(lens.min())}..{int(lens.max())} "
+                         f"(sum {int(lens.sum())}), path={args.path}"),
+            "path": args.path,
+            "kv_bytes_per_step": ab["kv"],
+            "inputs": ("cache-hot single copy" if copies == 1 else
+                       f"{copies} rotating copies of the KV pool (L2/MALL-cold)"),
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "pa_partition (Phase 1)",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": ab["partition"],
+            "avg_launch_ms": round(part_avg, 5),
+            "reduce_avg_launch_ms": round(float(red_ms.mean()), 5),
+            "event_step_ms_median": round(float(np.median(step_ms)), 5),
+            "kernel_source_hash": src_hash,
+        },
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle")
+        result["cpu_baseline"] = cpu_baseline(base, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -142,7 +142,7 @@ pa_status validate_common(const Call &c, bool partition_phase) {
 struct Plan {
   bool mfma;
   int gp;           // query-head slots per workgroup (VALU) / 16 (MFMA)
-  int head_groups;  // workgroups per KV head along grid.y
+  int head_groups;  // workgroups per KV head along grid.x
 };
 
 Plan make_plan(const Call &c) {
@@ -196,8 +196,9 @@ pa_status run_partition(const Call &c) {
   pa_status st = validate_common(c, true);
   if (st != PA_OK) return st;
   const Plan pl = make_plan(c);
-  const long long grid_y = (long long)c.num_kv_heads * pl.head_groups;
-  if (grid_y > kMaxGridYZ) return PA_ERR_BAD_SHAPE;
+  const long long grid_x = (long long)c.num_kv_heads * pl.head_groups;
+  const int gz = c.mode == PA_MODE_V1 ? 1 : pa_num_partitions(c.max_seq_len);
+  if (grid_x > 0x7fffffffLL || gz > kMaxGridYZ) return PA_ERR_BAD_SHAPE;
   if (c.num_seqs == 0) return PA_OK;
   int cu = 0;
   if (c.mode == PA_MODE_AUTO) {
@@ -205,8 +206,7 @@ pa_status run_partition(const Call &c) {
     if (st != PA_OK) return st;
   }
   const Params p = make_params(c, cu, pl.head_groups);
-  const int gx = c.mode == PA_MODE_V1 ? 1 : pa_num_partitions(c.max_seq_len);
-  const dim3 grid(gx, (unsigned)grid_y, c.num_seqs);
+  const dim3 grid((unsigned)grid_x, c.num_seqs, gz);
   const bool fp8 = c.kv_cache_dtype == PA_KV_FP8_E4M3;
   hipError_t e;
   if (pl.mfma) {

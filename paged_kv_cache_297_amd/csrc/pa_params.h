@@ -28,7 +28,7 @@ struct Params {
   const float *alibi_slopes;    // [H] or nullptr
   int num_seqs, num_heads, num_kv_heads, group;  // group = H / Hkv
   int max_num_blocks_per_seq, num_blocks, max_seq_len, max_num_partitions;
-  int head_groups;      // query-head groups per KV head; grid.y = Hkv * head_groups
+  int head_groups;      // query-head groups per KV head; grid.x = Hkv * head_groups
   int mode;             // Mode
   int auto_all_v2;      // AUTO: every sequence takes v2 (small batch clause)
   int auto_tile_limit;  // AUTO: v2 iff Hkv * ceil(L / 512) > auto_tile_limit

@@ -1,9 +1,13 @@
 // Work decoding and the cross-wave merge / store epilogue shared by the two
 // partition-phase kernels (VALU and MFMA).
 //
-// Grid: x = partition (v2) or 0 (v1), y = KV head * head_groups + head group,
-// z = sequence.  Each workgroup owns one (sequence, KV head, query-head group)
-// and either one 512-token partition (v2) or the whole sequence (v1).
+// Grid: x = KV head * head_groups + head group, y = sequence, z = partition
+// (v2) or 0 (v1).  Each workgroup owns one (sequence, KV head, query-head
+// group) and either one 512-token partition (v2) or the whole sequence (v1).
+// The partition is the slowest grid dimension, so workgroups are dispatched
+// partition 0 first: the long whole-sequence workgroups of a mixed v1/v2
+// launch start early instead of queueing behind the empty partition slots of
+// their sequence.
 #pragma once
 
 #include "pa_device.h"
@@ -43,16 +47,16 @@ __device__ __forceinline__ void write_stat_padding(const Params &p, const Work &
 template <typename QT, int D>
 __device__ __forceinline__ bool begin_work(const Params &p, int block_size, int group_slots,
                                           Work &w) {
-  w.seq = blockIdx.z;
-  w.kvh = blockIdx.y / p.head_groups;
-  const int hg = blockIdx.y - w.kvh * p.head_groups;
+  w.seq = blockIdx.y;
+  w.kvh = blockIdx.x / p.head_groups;
+  const int hg = blockIdx.x - w.kvh * p.head_groups;
   w.head0 = w.kvh * p.group + hg * group_slots;
   w.nh = min(group_slots, p.group - hg * group_slots);
   w.L = p.seq_lens[w.seq];
   const bool bad = (w.L < 0) || (w.L > p.max_seq_len);
   w.v2 = seq_uses_v2(p, bad ? 0 : w.L);
   w.n_part = bad ? 0 : (w.L + kPartitionSize - 1) / kPartitionSize;
-  w.part = blockIdx.x;
+  w.part = blockIdx.z;
   if (bad || w.L == 0) {
     if (w.part != 0) return false;
     const float fill = bad ? __builtin_nanf("") : 0.0f;
