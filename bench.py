@@ -10,9 +10,10 @@ Inputs are resident in HBM before timing.  By default the step rotates over
 ``--copies`` independent copies of the KV pool (4 x ~0.6 GB), so the 256 MB
 Infinity Cache cannot serve one step's KV from the previous step; ``--hot``
 times a single copy instead.  W warm-up steps, then exactly K timed steps
-between device synchronisations.  HIP events on the library's stream bracket
-each launch, giving the average partition-kernel duration used for the
-roofline.  The fp64 CPU oracle is timed on a bounded sample of the same
+between device synchronisations.  Through the library's profiling hook
+(pa_set_timing_events) every timed launch records HIP events at the
+kernel's own start and end, giving the average partition-kernel duration
+used for the roofline.  The fp64 CPU oracle is timed on a bounded sample of the same
 workload for the CPU baseline.
 
 Prints one JSON line (stdout); progress goes to stderr.
@@ -34,8 +35,6 @@ if ROOT not in sys.path:
 METRIC = "paged-attn decode µs/step + effective KV HBM GB/s (% of peak), 1 MI355X"
 HBM_PEAK_GBS = 8000.0
 PROFILES = os.path.join(ROOT, "profiles")
-KERNEL_SOURCES = ("pa_partition_mfma.h", "pa_partition_valu.h", "pa_partition_common.h",
-                  "pa_device.h", "pa_params.h", "pa_reduce.hip", "pa_api.cpp")
 
 
 def log(msg: str) -> None:
@@ -43,11 +42,13 @@ def log(msg: str) -> None:
 
 
 def kernel_source_hash() -> str:
+    """Hash of every library source file: counter figures taken on other
+    sources are not reported."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "paged_kv_cache_297_amd", "csrc")
-    for name in KERNEL_SOURCES:
+    for name in sorted(os.listdir(csrc)):
         with open(os.path.join(csrc, name), "rb") as f:
-            h.update(f.read())
+            h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
 
 
@@ -110,9 +111,13 @@ def cpu_baseline(wl, budget_s: float) -> dict:
 
     alibi = None if wl.alibi_slopes is None else wl.alibi_slopes.cpu().double().numpy()
     done, kv_done, spent = 0, 0, 0.0
+    hosts = {}
     with threadpool_limits(1):
-        for s in range(wl.num_seqs):
-            host = W.host_subset(wl, [s])
+        while spent < budget_s and done < 50 * wl.num_seqs:
+            s = done % wl.num_seqs
+            if s not in hosts:
+                hosts[s] = W.host_subset(wl, [s])
+            host = hosts[s]
             t0 = time.perf_counter()
             O.paged_attention(host["query"], host["key_cache"], host["value_cache"],
                               host["block_tables"], host["seq_lens"], wl.scale,
@@ -122,12 +127,10 @@ def cpu_baseline(wl, budget_s: float) -> dict:
             spent += time.perf_counter() - t0
             done += 1
             kv_done += int(wl.lens[s]) * wl.num_kv_heads * wl.head_size * 2 * wl.kv_elem_bytes
-            if spent >= budget_s:
-                break
     gbs = kv_done / spent / 1e9
     return {"value": round(gbs, 5), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": (f"{done} of {wl.num_seqs} sequences of the same batch "
-                       f"({kv_done / 1e6:.1f} MB of KV), v1 + v2 partials + merge in fp64, "
+            "sample": (f"{done} sequence passes over the {wl.num_seqs} sequences of the same "
+                       f"batch ({kv_done / 1e6:.1f} MB of KV), v1 + v2 partials + merge in fp64, "
                        f"1 thread, {spent:.1f} s; device-to-host copies excluded"),
             "us_per_step_extrapolated": round(spent / kv_done * wl.kv_bytes() * 1e6, 1)}
 
@@ -187,19 +190,21 @@ def main() -> int:
         kw = dict(alibi_slopes=wl.alibi_slopes, kv_cache_dtype=wl.kv_cache_dtype,
                   k_scale=wl.k_scale, v_scale=wl.v_scale, stream=stream)
         if ev is not None:
-            ev[0].record(stream)
+            # The library records these at each kernel's own start and end.
+            B.set_timing_events(*(e.cuda_event for e in ev))
         B.paged_attention_partition(args.path, *common, **kw)
-        if ev is not None:
-            ev[1].record(stream)
         B.paged_attention_reduce(args.path, out, es, ml, to, wl.seq_lens, wl.num_kv_heads,
                                  wl.max_seq_len, stream=stream)
-        if ev is not None:
-            ev[2].record(stream)
 
     for i in range(args.warmup):
         launch(i)
     torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    # partition start/stop, reduce start/stop of every timed step; each event
+    # is recorded once here so that its handle exists.
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    for ev in events:
+        for e in ev:
+            e.record(stream)
     log(f"timing {args.steps} steps")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -207,9 +212,10 @@ def main() -> int:
         launch(i, events[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    B.set_timing_events()
     part_ms = np.array([e[0].elapsed_time(e[1]) for e in events])
-    red_ms = np.array([e[1].elapsed_time(e[2]) for e in events])
-    step_ms = np.array([e[0].elapsed_time(e[2]) for e in events])
+    red_ms = np.array([e[2].elapsed_time(e[3]) for e in events])
+    step_ms = np.array([e[0].elapsed_time(e[3]) for e in events])
 
     if args.calibrate_copy:
         n = args.calibrate_copy * (1 << 20)

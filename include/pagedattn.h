@@ -51,7 +51,7 @@
  * Ownership.  Every buffer belongs to the caller.  The library allocates and
  * frees nothing and keeps no pointer after a call returns.  Its only global
  * state is a per-device cache of the compute-unit count, filled on first use
- * under a lock.
+ * under a lock, and the per-thread profiling events of pa_set_timing_events.
  *
  * Streams.  Work is enqueued on `stream` (a hipStream_t; NULL is the null
  * stream) and runs asynchronously; no call synchronises or copies device
@@ -66,8 +66,8 @@
  *
  * Supported: dtype f32 / f16 / bf16; kv_cache_dtype AUTO (KV in dtype) or
  * FP8_E4M3 (dtype f16 or bf16); head_size 64 or 128; block_size 16 or 32;
- * num_heads a multiple of num_kv_heads with at most 16 query heads per KV
- * head for 16-bit / fp8 caches (any group size for f32).
+ * num_heads any multiple of num_kv_heads; num_seqs <= 65535; max_seq_len
+ * <= 65535 * 512 for v2 / auto.
  */
 #ifndef PAGEDATTN_H
 #define PAGEDATTN_H
@@ -196,6 +196,17 @@ int pa_should_use_v2(int num_seqs, int num_kv_heads, int seq_len, int cu_count);
 /* Compute units of the current HIP device (cached per device); <= 0 and
  * PA_ERR_HIP if the runtime cannot tell. */
 pa_status pa_device_cu_count(int *cu_count);
+
+/* Profiling hook.  For launches made afterwards from the calling thread, the
+ * partition-phase kernel records partition_start / partition_stop and the
+ * reduce-phase kernel records reduce_start / reduce_stop (hipEvent_t handles
+ * created by the caller), through hipExtLaunchKernelGGL: the events carry the
+ * kernel's own start and end times, with no queue marker in between.  A
+ * NULL pair switches its phase back to plain launches.  The events are
+ * re-recorded by every call until replaced.  A pair with one NULL member
+ * returns PA_ERR_NULL_POINTER and changes nothing. */
+pa_status pa_set_timing_events(void *partition_start, void *partition_stop, void *reduce_start,
+                               void *reduce_stop);
 
 /* Static description of a status code. */
 const char *pa_status_string(pa_status status);

@@ -32,8 +32,8 @@ MODE_CODE = {"v1": 0, "v2": 1, "auto": 2}
 EXPORTED_SYMBOLS = (
     "paged_attention_v1", "paged_attention_v2", "paged_attention_auto",
     "paged_attention_partition", "paged_attention_reduce", "pa_partition_size",
-    "pa_num_partitions", "pa_should_use_v2", "pa_device_cu_count", "pa_status_string",
-    "pa_version",
+    "pa_num_partitions", "pa_should_use_v2", "pa_device_cu_count", "pa_set_timing_events",
+    "pa_status_string", "pa_version",
 )
 
 
@@ -83,6 +83,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pa_should_use_v2.restype = _I
     lib.pa_device_cu_count.argtypes = [ctypes.POINTER(ctypes.c_int)]
     lib.pa_device_cu_count.restype = _I
+    lib.pa_set_timing_events.argtypes = [_P, _P, _P, _P]
+    lib.pa_set_timing_events.restype = _I
     lib.pa_status_string.argtypes = [_I]
     lib.pa_status_string.restype = ctypes.c_char_p
     lib.pa_version.argtypes = []
@@ -255,6 +257,14 @@ def device_cu_count() -> int:
     n = ctypes.c_int(0)
     _check(load_library().pa_device_cu_count(ctypes.byref(n)), "pa_device_cu_count")
     return n.value
+
+
+def set_timing_events(partition_start=None, partition_stop=None, reduce_start=None,
+                      reduce_stop=None) -> None:
+    """Profiling hook: hipEvent_t handles (ints) recorded at the kernels' own
+    start / end by later calls from this thread; None pairs switch it off."""
+    _check(load_library().pa_set_timing_events(partition_start, partition_stop, reduce_start,
+                                               reduce_stop), "pa_set_timing_events")
 
 
 def version() -> str:

@@ -75,6 +75,15 @@ pa_status cu_count_current(int *cu) {
 }
 
 // ---------------------------------------------------------------------------
+// Profiling hook (pa_set_timing_events): per calling thread.
+// ---------------------------------------------------------------------------
+struct TimingEvents {
+  hipEvent_t partition_start = nullptr, partition_stop = nullptr;
+  hipEvent_t reduce_start = nullptr, reduce_stop = nullptr;
+};
+thread_local TimingEvents t_events;
+
+// ---------------------------------------------------------------------------
 // Validation
 // ---------------------------------------------------------------------------
 struct Call {
@@ -206,20 +215,20 @@ pa_status run_partition(const Call &c) {
     if (st != PA_OK) return st;
   }
   const Params p = make_params(c, cu, pl.head_groups);
-  const dim3 grid((unsigned)grid_x, c.num_seqs, gz);
+  const pa::Launch l{dim3((unsigned)grid_x, c.num_seqs, gz), c.stream, t_events.partition_start,
+                     t_events.partition_stop};
   const bool fp8 = c.kv_cache_dtype == PA_KV_FP8_E4M3;
   hipError_t e;
   if (pl.mfma) {
-    e = pa::launch_partition_mfma(p, (int)c.dtype, fp8, c.head_size, c.block_size, grid, c.stream);
+    e = pa::launch_partition_mfma(p, (int)c.dtype, fp8, c.head_size, c.block_size, l);
   } else if (fp8) {
-    e = pa::launch_partition_valu_fp8(p, (int)c.dtype, c.head_size, c.block_size, pl.gp, grid,
-                                      c.stream);
+    e = pa::launch_partition_valu_fp8(p, (int)c.dtype, c.head_size, c.block_size, pl.gp, l);
   } else if (c.dtype == PA_DTYPE_F32) {
-    e = pa::launch_partition_valu_f32(p, c.head_size, c.block_size, pl.gp, grid, c.stream);
+    e = pa::launch_partition_valu_f32(p, c.head_size, c.block_size, pl.gp, l);
   } else if (c.dtype == PA_DTYPE_F16) {
-    e = pa::launch_partition_valu_f16(p, c.head_size, c.block_size, pl.gp, grid, c.stream);
+    e = pa::launch_partition_valu_f16(p, c.head_size, c.block_size, pl.gp, l);
   } else {
-    e = pa::launch_partition_valu_bf16(p, c.head_size, c.block_size, pl.gp, grid, c.stream);
+    e = pa::launch_partition_valu_bf16(p, c.head_size, c.block_size, pl.gp, l);
   }
   return e == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
@@ -235,7 +244,9 @@ pa_status run_reduce(const Call &c) {
     if (st != PA_OK) return st;
   }
   const Params p = make_params(c, cu, 1);
-  const hipError_t e = pa::launch_reduce(p, (int)c.dtype, c.head_size, c.stream);
+  const pa::Launch l{dim3(c.num_heads, c.num_seqs, 1), c.stream, t_events.reduce_start,
+                     t_events.reduce_stop};
+  const hipError_t e = pa::launch_reduce(p, (int)c.dtype, c.head_size, l);
   return e == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
@@ -375,6 +386,18 @@ pa_status paged_attention_auto(void *out, float *exp_sums, float *max_logits, fl
                    max_num_blocks_per_seq, seq_lens, num_blocks, block_size, max_seq_len,
                    max_num_partitions, alibi_slopes, dtype, kv_cache_dtype, k_scale, v_scale,
                    stream);
+}
+
+pa_status pa_set_timing_events(void *partition_start, void *partition_stop, void *reduce_start,
+                               void *reduce_stop) {
+  if ((partition_start == nullptr) != (partition_stop == nullptr) ||
+      (reduce_start == nullptr) != (reduce_stop == nullptr))
+    return PA_ERR_NULL_POINTER;
+  t_events.partition_start = reinterpret_cast<hipEvent_t>(partition_start);
+  t_events.partition_stop = reinterpret_cast<hipEvent_t>(partition_stop);
+  t_events.reduce_start = reinterpret_cast<hipEvent_t>(reduce_start);
+  t_events.reduce_stop = reinterpret_cast<hipEvent_t>(reduce_stop);
+  return PA_OK;
 }
 
 int pa_partition_size(void) { return pa::kPartitionSize; }

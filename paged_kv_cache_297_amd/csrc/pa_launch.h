@@ -2,6 +2,7 @@
 // combination, so the kernel instantiations compile in parallel).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include "pa_params.h"
@@ -9,6 +10,24 @@
 namespace pa {
 
 enum DtCode : int { kDtF32 = 0, kDtF16 = 1, kDtBF16 = 2 };
+
+// Where and how one kernel is launched.  With both events set, the launch
+// goes through hipExtLaunchKernelGGL, which records them at the kernel's own
+// start and end (the profiling hook of pa_set_timing_events).
+struct Launch {
+  dim3 grid;
+  hipStream_t stream;
+  hipEvent_t start, stop;
+};
+
+template <typename Kernel>
+hipError_t launch_kernel(Kernel kernel, const Launch &l, const Params &p) {
+  if (l.start && l.stop)
+    hipExtLaunchKernelGGL(kernel, l.grid, dim3(kThreads), 0, l.stream, l.start, l.stop, 0, p);
+  else
+    hipLaunchKernelGGL(kernel, l.grid, dim3(kThreads), 0, l.stream, p);
+  return hipGetLastError();
+}
 
 // Largest power-of-two query-head group the VALU kernel keeps in registers
 // (the query slices of one lane may use at most 64 VGPRs).
@@ -23,16 +42,16 @@ constexpr int valu_max_group(int kv_bytes, int head_size, int block_size) {
 }
 
 hipError_t launch_partition_valu_f32(const Params &p, int head_size, int block_size, int gp,
-                                     dim3 grid, hipStream_t stream);
+                                     const Launch &l);
 hipError_t launch_partition_valu_f16(const Params &p, int head_size, int block_size, int gp,
-                                     dim3 grid, hipStream_t stream);
+                                     const Launch &l);
 hipError_t launch_partition_valu_bf16(const Params &p, int head_size, int block_size, int gp,
-                                      dim3 grid, hipStream_t stream);
+                                      const Launch &l);
 // fp8 E4M3FN cache with a 16-bit query (q_dtype kDtF16 or kDtBF16).
 hipError_t launch_partition_valu_fp8(const Params &p, int q_dtype, int head_size,
-                                     int block_size, int gp, dim3 grid, hipStream_t stream);
+                                     int block_size, int gp, const Launch &l);
 hipError_t launch_partition_mfma(const Params &p, int q_dtype, bool kv_fp8, int head_size,
-                                 int block_size, dim3 grid, hipStream_t stream);
-hipError_t launch_reduce(const Params &p, int dtype, int head_size, hipStream_t stream);
+                                 int block_size, const Launch &l);
+hipError_t launch_reduce(const Params &p, int dtype, int head_size, const Launch &l);
 
 }  // namespace pa

@@ -5,14 +5,10 @@
 namespace pa {
 
 template <typename QT, typename KVT>
-static hipError_t launch_mfma_t(const Params &p, int head_size, int block_size, dim3 grid,
-                                hipStream_t stream) {
-#define PA_MFMA_CASE(D, BS)                                                                 \
-  if (head_size == D && block_size == BS) {                                                 \
-    hipLaunchKernelGGL((pa_partition_mfma<QT, KVT, D, BS>), grid, dim3(kThreads), 0, stream, \
-                       p);                                                                  \
-    return hipGetLastError();                                                               \
-  }
+static hipError_t launch_mfma_t(const Params &p, int head_size, int block_size,
+                                const Launch &l) {
+#define PA_MFMA_CASE(D, BS) \
+  if (head_size == D && block_size == BS) return launch_kernel(pa_partition_mfma<QT, KVT, D, BS>, l, p);
   PA_MFMA_CASE(64, 16)
   PA_MFMA_CASE(64, 32)
   PA_MFMA_CASE(128, 16)
@@ -22,13 +18,13 @@ static hipError_t launch_mfma_t(const Params &p, int head_size, int block_size, 
 }
 
 hipError_t launch_partition_mfma(const Params &p, int q_dtype, bool kv_fp8, int head_size,
-                                 int block_size, dim3 grid, hipStream_t stream) {
+                                 int block_size, const Launch &l) {
   if (q_dtype == kDtF16)
-    return kv_fp8 ? launch_mfma_t<_Float16, fp8e4m3>(p, head_size, block_size, grid, stream)
-                  : launch_mfma_t<_Float16, _Float16>(p, head_size, block_size, grid, stream);
+    return kv_fp8 ? launch_mfma_t<_Float16, fp8e4m3>(p, head_size, block_size, l)
+                  : launch_mfma_t<_Float16, _Float16>(p, head_size, block_size, l);
   if (q_dtype == kDtBF16)
-    return kv_fp8 ? launch_mfma_t<__bf16, fp8e4m3>(p, head_size, block_size, grid, stream)
-                  : launch_mfma_t<__bf16, __bf16>(p, head_size, block_size, grid, stream);
+    return kv_fp8 ? launch_mfma_t<__bf16, fp8e4m3>(p, head_size, block_size, l)
+                  : launch_mfma_t<__bf16, __bf16>(p, head_size, block_size, l);
   return hipErrorInvalidValue;
 }
 

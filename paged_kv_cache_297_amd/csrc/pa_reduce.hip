@@ -81,22 +81,18 @@ __global__ void __launch_bounds__(kThreads) pa_reduce_kernel(const Params p) {
 }
 
 template <typename QT>
-static hipError_t launch_reduce_t(const Params &p, int head_size, hipStream_t stream) {
-  const dim3 grid(p.num_heads, p.num_seqs, 1);
-  if (head_size == 64)
-    hipLaunchKernelGGL((pa_reduce_kernel<QT, 64>), grid, dim3(kThreads), 0, stream, p);
-  else if (head_size == 128)
-    hipLaunchKernelGGL((pa_reduce_kernel<QT, 128>), grid, dim3(kThreads), 0, stream, p);
-  else
-    return hipErrorInvalidValue;
-  return hipGetLastError();
+static hipError_t launch_reduce_t(const Params &p, int head_size, const Launch &l) {
+  if (head_size == 64) return launch_kernel(pa_reduce_kernel<QT, 64>, l, p);
+  if (head_size == 128) return launch_kernel(pa_reduce_kernel<QT, 128>, l, p);
+  return hipErrorInvalidValue;
 }
 
-hipError_t launch_reduce(const Params &p, int dtype, int head_size, hipStream_t stream) {
+// Grid: one workgroup per (query head, sequence).
+hipError_t launch_reduce(const Params &p, int dtype, int head_size, const Launch &l) {
   switch (dtype) {
-    case kDtF32: return launch_reduce_t<float>(p, head_size, stream);
-    case kDtF16: return launch_reduce_t<_Float16>(p, head_size, stream);
-    case kDtBF16: return launch_reduce_t<__bf16>(p, head_size, stream);
+    case kDtF32: return launch_reduce_t<float>(p, head_size, l);
+    case kDtF16: return launch_reduce_t<_Float16>(p, head_size, l);
+    case kDtBF16: return launch_reduce_t<__bf16>(p, head_size, l);
   }
   return hipErrorInvalidValue;
 }

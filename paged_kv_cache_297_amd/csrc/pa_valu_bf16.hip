@@ -3,7 +3,7 @@
 
 namespace pa {
 hipError_t launch_partition_valu_bf16(const Params &p, int head_size, int block_size, int gp,
-                                      dim3 grid, hipStream_t stream) {
-  return launch_valu<__bf16, __bf16>(p, head_size, block_size, gp, grid, stream);
+                                     const Launch &l) {
+  return launch_valu<__bf16, __bf16>(p, head_size, block_size, gp, l);
 }
 }  // namespace pa

@@ -14,33 +14,31 @@ constexpr int kv_bytes_of() {
 }
 
 template <typename QT, typename KVT, int D, int BS, int GP>
-hipError_t launch_valu_one(const Params &p, dim3 grid, hipStream_t stream) {
+hipError_t launch_valu_one(const Params &p, const Launch &l) {
   if constexpr (GP <= valu_max_group(kv_bytes_of<QT, KVT>(), D, BS)) {
-    hipLaunchKernelGGL((pa_partition_valu<QT, KVT, D, BS, GP>), grid, dim3(kThreads), 0, stream,
-                       p);
-    return hipGetLastError();
+    return launch_kernel(pa_partition_valu<QT, KVT, D, BS, GP>, l, p);
   } else {
     return hipErrorInvalidValue;
   }
 }
 
 template <typename QT, typename KVT, int D, int BS>
-hipError_t launch_valu_gp(const Params &p, int gp, dim3 grid, hipStream_t stream) {
+hipError_t launch_valu_gp(const Params &p, int gp, const Launch &l) {
   switch (gp) {
-    case 1: return launch_valu_one<QT, KVT, D, BS, 1>(p, grid, stream);
-    case 2: return launch_valu_one<QT, KVT, D, BS, 2>(p, grid, stream);
-    case 4: return launch_valu_one<QT, KVT, D, BS, 4>(p, grid, stream);
+    case 1: return launch_valu_one<QT, KVT, D, BS, 1>(p, l);
+    case 2: return launch_valu_one<QT, KVT, D, BS, 2>(p, l);
+    case 4: return launch_valu_one<QT, KVT, D, BS, 4>(p, l);
   }
   return hipErrorInvalidValue;
 }
 
 template <typename QT, typename KVT>
-hipError_t launch_valu(const Params &p, int head_size, int block_size, int gp, dim3 grid,
-                       hipStream_t stream) {
-  if (head_size == 64 && block_size == 16) return launch_valu_gp<QT, KVT, 64, 16>(p, gp, grid, stream);
-  if (head_size == 64 && block_size == 32) return launch_valu_gp<QT, KVT, 64, 32>(p, gp, grid, stream);
-  if (head_size == 128 && block_size == 16) return launch_valu_gp<QT, KVT, 128, 16>(p, gp, grid, stream);
-  if (head_size == 128 && block_size == 32) return launch_valu_gp<QT, KVT, 128, 32>(p, gp, grid, stream);
+hipError_t launch_valu(const Params &p, int head_size, int block_size, int gp,
+                       const Launch &l) {
+  if (head_size == 64 && block_size == 16) return launch_valu_gp<QT, KVT, 64, 16>(p, gp, l);
+  if (head_size == 64 && block_size == 32) return launch_valu_gp<QT, KVT, 64, 32>(p, gp, l);
+  if (head_size == 128 && block_size == 16) return launch_valu_gp<QT, KVT, 128, 16>(p, gp, l);
+  if (head_size == 128 && block_size == 32) return launch_valu_gp<QT, KVT, 128, 32>(p, gp, l);
   return hipErrorInvalidValue;
 }
 

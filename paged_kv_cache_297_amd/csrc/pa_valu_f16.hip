@@ -3,7 +3,7 @@
 
 namespace pa {
 hipError_t launch_partition_valu_f16(const Params &p, int head_size, int block_size, int gp,
-                                     dim3 grid, hipStream_t stream) {
-  return launch_valu<_Float16, _Float16>(p, head_size, block_size, gp, grid, stream);
+                                     const Launch &l) {
+  return launch_valu<_Float16, _Float16>(p, head_size, block_size, gp, l);
 }
 }  // namespace pa

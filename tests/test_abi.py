@@ -187,3 +187,11 @@ def test_reduce_validation():
 def test_empty_batch_is_a_no_op():
     lib = B.load_library()
     assert lib.paged_attention_v2(*v2_args(num_seqs=0)) == OK
+
+
+def test_timing_events_argument_pairs():
+    """A half-set event pair is rejected; NULL pairs switch the hook off (no GPU needed)."""
+    lib = B.load_library()
+    assert lib.pa_set_timing_events(A, None, None, None) == NULLP
+    assert lib.pa_set_timing_events(None, None, A, None) == NULLP
+    assert lib.pa_set_timing_events(None, None, None, None) == OK

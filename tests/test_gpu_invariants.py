@@ -142,3 +142,27 @@ def test_out_of_range_block_id_gives_nan_for_that_sequence_only(path, number):
     res = H.run(wl, path)
     assert np.isnan(res["out"][0]).all()
     assert np.isfinite(res["out"][1]).all()
+
+
+def test_timing_events_hook_records_kernel_times():
+    """pa_set_timing_events: the events get kernel-recorded times and the
+    results are unchanged."""
+    wl = W.make_workload(2, lens=[3000, 700])
+    plain = H.run(wl, "v2")
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    stream = torch.cuda.current_stream()
+    for e in ev:
+        e.record(stream)
+    torch.cuda.synchronize()
+    B.set_timing_events(*(e.cuda_event for e in ev))
+    try:
+        timed = H.run(wl, "v2")
+    finally:
+        B.set_timing_events()
+    for k in plain:
+        assert np.array_equal(plain[k], timed[k], equal_nan=True), k
+    part, red = ev[0].elapsed_time(ev[1]), ev[2].elapsed_time(ev[3])
+    assert 0.0 < part < 1000.0 and 0.0 < red < 1000.0
+    assert ev[1].elapsed_time(ev[2]) >= 0.0   # reduce starts after the partition kernel ends
+    with pytest.raises(B.PagedAttentionError):
+        B.set_timing_events(ev[0].cuda_event, None)
