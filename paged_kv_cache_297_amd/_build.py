@@ -41,9 +41,9 @@ def sources():
                   if f.endswith((".hip", ".cpp")))
 
 
-def _compile(src: str, verbose: bool) -> str:
-    obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *COMMON_FLAGS, "-c", src, "-o", obj]
+def _compile(src: str, verbose: bool, build_dir: str, defines) -> str:
+    obj = os.path.join(build_dir, os.path.basename(src) + ".o")
+    cmd = [hipcc(), *COMMON_FLAGS, *[f"-D{d}" for d in defines], "-c", src, "-o", obj]
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -56,21 +56,32 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False, jobs: int | None = None) -> str:
-    """Compile and link; returns the path of the shared library."""
-    os.makedirs(BUILD_DIR, exist_ok=True)
+def build(verbose: bool = False, jobs: int | None = None, defines=(), out: str = LIB_PATH) -> str:
+    """Compile and link; returns the path of the shared library.
+
+    ``defines`` (e.g. ``["PA_PREFETCH_MFMA=2"]``) override the kernels'
+    compile-time tuning constants; ``out`` places such a variant elsewhere."""
+    build_dir = BUILD_DIR if not defines else os.path.join(
+        BUILD_DIR, "_".join(d.replace("=", "") for d in defines))
+    os.makedirs(build_dir, exist_ok=True)
     srcs = sources()
     jobs = jobs or min(len(srcs), max(1, min(8, os.cpu_count() or 1)))
     with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
-    tmp = LIB_PATH + ".tmp"
+        objs = list(ex.map(lambda s: _compile(s, verbose, build_dir, defines), srcs))
+    tmp = out + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{res.stdout}{res.stderr}")
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    import argparse
+    ap = argparse.ArgumentParser(description="build libpagedattn.so for gfx950")
+    ap.add_argument("-D", dest="defines", action="append", default=[],
+                    help="tuning constant, e.g. -D PA_PREFETCH_MFMA=2")
+    ap.add_argument("-o", dest="out", default=LIB_PATH)
+    a = ap.parse_args()
+    print(build(verbose=True, defines=a.defines, out=a.out))

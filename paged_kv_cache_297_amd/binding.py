@@ -18,7 +18,9 @@ from typing import Optional
 
 import torch
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedattn.so")
+#: The in-tree build; PA_LIB_PATH selects another build of the same library.
+LIB_PATH = os.environ.get("PA_LIB_PATH") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "libpagedattn.so")
 
 PA_OK = 0
 STATUS_NAMES = {0: "PA_OK", 1: "PA_ERR_NULL_POINTER", 2: "PA_ERR_BAD_SHAPE",

@@ -36,15 +36,17 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // 16-byte loads.  KV tiles are streamed once, so they bypass reuse-oriented
 // caching with the nontemporal hint.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ u32x4 load16_stream(const void *p) {
-  return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+template <typename T>
+__device__ __forceinline__ T load_stream(const void *p) {
+#if PA_NONTEMPORAL
+  return __builtin_nontemporal_load(reinterpret_cast<const T *>(p));
+#else
+  return *reinterpret_cast<const T *>(p);
+#endif
 }
-__device__ __forceinline__ u32x2 load8_stream(const void *p) {
-  return __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(p));
-}
-__device__ __forceinline__ unsigned load4_stream(const void *p) {
-  return __builtin_nontemporal_load(reinterpret_cast<const unsigned *>(p));
-}
+__device__ __forceinline__ u32x4 load16_stream(const void *p) { return load_stream<u32x4>(p); }
+__device__ __forceinline__ u32x2 load8_stream(const void *p) { return load_stream<u32x2>(p); }
+__device__ __forceinline__ unsigned load4_stream(const void *p) { return load_stream<unsigned>(p); }
 __device__ __forceinline__ u32x4 load16(const void *p) {
   return *reinterpret_cast<const u32x4 *>(p);
 }

@@ -15,6 +15,25 @@ constexpr int kThreads = 64 * kWaves;
 
 enum Mode : int { kModeV1 = 0, kModeV2 = 1, kModeAuto = 2 };
 
+// (block, KV head) tiles a wave keeps in flight ahead of the one it consumes.
+#ifndef PA_PREFETCH_VALU
+#define PA_PREFETCH_VALU 1
+#endif
+#ifndef PA_PREFETCH_MFMA
+#define PA_PREFETCH_MFMA 1
+#endif
+// Minimum waves per SIMD the register allocator must allow (0: no bound).
+#ifndef PA_WAVES_PER_EU_MFMA
+#define PA_WAVES_PER_EU_MFMA 0
+#endif
+#ifndef PA_WAVES_PER_EU_VALU
+#define PA_WAVES_PER_EU_VALU 0
+#endif
+// KV tiles are read with the nontemporal (streaming) cache policy.
+#ifndef PA_NONTEMPORAL
+#define PA_NONTEMPORAL 1
+#endif
+
 struct Params {
   void *out;            // [B, H, D] dtype
   float *exp_sums;      // [B, H, P]

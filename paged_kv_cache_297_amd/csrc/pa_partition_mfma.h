@@ -1,19 +1,21 @@
 // Partition-phase kernel, MFMA form: for GQA groups wide enough (5..16 query
 // heads per KV head) that QK^T and PV become real dense 16-row tiles.
 //
-// A (block, KV head) tile is processed as bs/16 sub-tiles of 16 tokens.
-//   S^T = K . Q^T  with v_mfma_f32_16x16x32 (bf16/f16): A = 16 tokens x 32
-//        dims of K, B = 32 dims x 16 query heads (the group, zero padded).
-//        Lane l feeds token l%16 with the 16-byte K chunk 4i + l/16 of load i,
-//        which is exactly the coalesced 1 KB-per-instruction read of the
-//        [D/x][bs][x] layout (fp8 chunks hold 16 dims and feed two k-steps;
-//        the query slices follow the same dim order).
-//   O^T += V^T . P^T with v_mfma_f32_16x16x16: the S^T accumulator leaves
-//        lane l with head l%16 and tokens 4(l/16)..+3, which is the B operand
-//        layout of the 16x16x16 MFMA, so P never leaves registers; A = 16 dims
-//        x 16 tokens of V, read as 4 consecutive tokens of one dim per lane
-//        (8 bytes for 16-bit V, 4 for fp8) -- 512 / 256 contiguous bytes per
-//        wave instruction.
+// A wave consumes 32 tokens per step (two 16-token blocks, or one 32-token
+// block).
+//   S^T = K . Q^T with v_mfma_f32_16x16x32 (bf16/f16), one per 16-token
+//        sub-tile and 32-dim k-step: A = 16 tokens x 32 dims of K, B = 32 dims
+//        x 16 query heads (the group, zero padded).  Lane l feeds token l%16
+//        with the 16-byte K chunk 4i + l/16 of load i: the coalesced 1 KB per
+//        instruction read of the [D/x][bs][x] layout (fp8 chunks hold 16 dims
+//        and feed two k-steps; the query slices follow the same dim order).
+//   O^T += V^T . P^T with v_mfma_f32_16x16x32: lane (n, g) = (l%16, l/16)
+//        feeds head-dim row 16t + n with 8 consecutive tokens, i.e. one
+//        16-byte load of the [D][bs] V layout (8 bytes for fp8).  The S^T
+//        accumulators leave lane (n, g) with tokens 4g..4g+3 of each 16-token
+//        sub-tile; two permlane swaps (32 then 16) regroup the packed P so
+//        that lane group g holds tokens 8(g^1) .. 8(g^1)+7, the same tokens
+//        its V row covers: P never goes through LDS.
 // Each lane keeps the running max / sum of one query head (l%16), so the
 // online-softmax rescale of O needs no broadcast.  fp8 E4M3FN keys are
 // widened exactly to the query's 16-bit type, values to fp16 (P in fp16).
@@ -37,35 +39,59 @@ __device__ __forceinline__ f32x4 mfma_qk(const u32x4 &a, const u32x4 &b, const f
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
                                                 __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
 }
-__device__ __forceinline__ f32x4 mfma_pv(const u32x2 &a, const u32x2 &b, const f32x4 &c,
+__device__ __forceinline__ f32x4 mfma_pv(const u32x4 &a, const u32x4 &b, const f32x4 &c,
                                          __bf16) {
-  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a),
-                                                   __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
-__device__ __forceinline__ f32x4 mfma_pv(const u32x2 &a, const u32x2 &b, const f32x4 &c,
+__device__ __forceinline__ f32x4 mfma_pv(const u32x4 &a, const u32x4 &b, const f32x4 &c,
                                          _Float16) {
-  return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a),
-                                               __builtin_bit_cast(f16x4, b), c, 0, 0, 0);
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
 }
 
-// Zero the 16-bit elements of tokens >= nv in a 4-token V operand.
-__device__ __forceinline__ u32x2 mask_v4(u32x2 v, int first, int nv) {
-  if (first >= nv) v.x = 0u;
-  else if (first + 1 >= nv) v.x &= 0xFFFFu;
-  if (first + 2 >= nv) v.y = 0u;
-  else if (first + 3 >= nv) v.y &= 0xFFFFu;
-  return v;
+// Zero the 16-bit elements of tokens >= nv in an 8-token V operand whose
+// first element is token `first`.
+__device__ __forceinline__ u32x4 mask_v8(u32x4 v, int first, int nv) {
+  unsigned w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    if (first + 2 * e >= nv) w[e] = 0u;
+    else if (first + 2 * e + 1 >= nv) w[e] &= 0xFFFFu;
+  }
+  return u32x4{w[0], w[1], w[2], w[3]};
 }
+
+// Regroups packed P (two 4-token pieces per lane: p0 from sub-tile 0, p1
+// from sub-tile 1, tokens 4g..4g+3 each) so that lane group g holds the 8
+// tokens 8(g^1) .. 8(g^1)+7 of the 32-token step, in order.
+__device__ __forceinline__ u32x4 regroup_p(const u32x2 &p0, const u32x2 &p1) {
+  // Step 1 (lanes l <-> l^32): lower half gets P0 of groups g and g+2, upper
+  // half P1 of groups g-2 and g.
+  auto a0 = __builtin_amdgcn_permlane32_swap(p0.x, p1.x, false, false);
+  auto a1 = __builtin_amdgcn_permlane32_swap(p0.y, p1.y, false, false);
+  // Step 2 (rows 2k <-> 2k+1): even rows keep their second value and take
+  // the odd row's second value; odd rows take the even row's first value.
+  auto b0 = __builtin_amdgcn_permlane16_swap(a0[1], a0[0], false, false);
+  auto b1 = __builtin_amdgcn_permlane16_swap(a1[1], a1[0], false, false);
+  return u32x4{b0[0], b1[0], b0[1], b1[1]};
+}
+
+#if PA_WAVES_PER_EU_MFMA > 0
+#define PA_MFMA_OCCUPANCY __attribute__((amdgpu_waves_per_eu(PA_WAVES_PER_EU_MFMA)))
+#else
+#define PA_MFMA_OCCUPANCY
+#endif
 
 template <typename QT, typename KVT, int D, int BS>
-__global__ void __launch_bounds__(kThreads) pa_partition_mfma(const Params p) {
+__global__ void __launch_bounds__(kThreads) PA_MFMA_OCCUPANCY pa_partition_mfma(const Params p) {
   constexpr bool kFp8 = std::is_same<KVT, fp8e4m3>::value;
   using PT = typename std::conditional<kFp8, _Float16, KVT>::type;  // P.V operand type
   static_assert(kFp8 || std::is_same<KVT, QT>::value, "16-bit cache must match the query type");
   constexpr int ESZ = kFp8 ? 1 : 2;
-  constexpr int NSUB = BS / 16;               // 16-token sub-tiles per block
   constexpr int TILE = D * BS * ESZ;          // bytes of one K or V tile
-  constexpr int NLK = D * 16 * ESZ / 1024;    // 16-byte K loads per lane per sub-tile
+  constexpr int BPS = 32 / BS;                // blocks per 32-token step
+  constexpr int NLK = D * 16 * ESZ / 1024;    // 16-byte K loads per lane per 16-token sub-tile
   constexpr int NKS = D / 32;                 // 32-dim k-steps of QK
   constexpr int NDT = D / 16;                 // 16-dim tiles of the output
   constexpr int OSTR = D + 4;                 // padded LDS row (bank spread)
@@ -80,8 +106,9 @@ __global__ void __launch_bounds__(kThreads) pa_partition_mfma(const Params p) {
 
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int n = lane & 15;   // query head of the group (MFMA column)
+  const int n = lane & 15;   // query head of the group (MFMA column) / V dim row
   const int g = lane >> 4;   // lane group: k-slot block / row block
+  const int vtok = 8 * (g ^ 1);  // first of the 8 step tokens this lane's P / V operands hold
 
   // B operands of QK: 8 query values per lane and k-step, in the dim order
   // of the K chunks (16-bit: dims 32ks + 8g + e; fp8: chunk 4i + g of 16 dims,
@@ -108,52 +135,65 @@ __global__ void __launch_bounds__(kThreads) pa_partition_mfma(const Params p) {
   const int32_t *btab = p.block_tables + (size_t)w.seq * p.max_num_blocks_per_seq;
   const size_t head_off = (size_t)w.kvh * TILE;
   const size_t blk_stride = (size_t)p.num_kv_heads * TILE;
+  const int tok_begin = w.blk_begin * BS;
+  const int n_steps = ((w.blk_end - w.blk_begin) * BS + 31) / 32;
   bool poisoned = false;
 
-  // K: sub-tile s, load i -> chunk 4i + g, token 16s + n.
-  // V: sub-tile s, dim tile t -> dim 16t + n, tokens 16s + 4g .. +3.
+  // K: sub-tile h, load i -> chunk 4i + g, token 16h + n of the step.
+  // V: dim tile t -> dim 16t + n, tokens vtok .. vtok + 7 of the step.
+  using VOp = typename std::conditional<kFp8, u32x2, u32x4>::type;
   struct Tile {
-    u32x4 k[NSUB][NLK];
-    typename std::conditional<kFp8, unsigned, u32x2>::type v[NSUB][NDT];
+    u32x4 k[2][NLK];
+    VOp v[NDT];
   };
 
   // Out-of-range block-table entries are redirected to block 0 (always
-  // addressable) and reported through the poison flag.
-  auto load_tile = [&](int blk) {
-    int phys = btab[blk];
-    if (phys < 0 || phys >= p.num_blocks) {
-      poisoned = true;
-      phys = 0;
+  // addressable) and reported through the poison flag; the second block of
+  // a step past the range end is read from block 0 too, and all its tokens
+  // are masked.
+  auto load_tile = [&](int step) {
+    const char *kb[BPS], *vb[BPS];
+#pragma unroll
+    for (int b = 0; b < BPS; ++b) {
+      const int lb = w.blk_begin + step * BPS + b;
+      int phys = 0;
+      if (lb < w.blk_end) {
+        phys = btab[lb];
+        if (phys < 0 || phys >= p.num_blocks) {
+          poisoned = true;
+          phys = 0;
+        }
+      }
+      kb[b] = kcache + (size_t)phys * blk_stride + head_off;
+      vb[b] = vcache + (size_t)phys * blk_stride + head_off;
     }
-    const char *kb = kcache + (size_t)phys * blk_stride + head_off;
-    const char *vb = vcache + (size_t)phys * blk_stride + head_off;
     Tile tl;
 #pragma unroll
-    for (int s = 0; s < NSUB; ++s)
+    for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int i = 0; i < NLK; ++i)
-        tl.k[s][i] = load16_stream(kb + (4 * i + g) * (BS * 16) + (16 * s + n) * 16);
-#pragma unroll
-    for (int s = 0; s < NSUB; ++s)
-#pragma unroll
-      for (int t = 0; t < NDT; ++t) {
-        const char *src = vb + ((16 * t + n) * BS + 16 * s + 4 * g) * ESZ;
-        if constexpr (kFp8) tl.v[s][t] = load4_stream(src);
-        else tl.v[s][t] = load8_stream(src);
+      for (int i = 0; i < NLK; ++i) {
+        const int tok = 16 * h + n;
+        tl.k[h][i] = load16_stream(kb[tok / BS] + (4 * i + g) * (BS * 16) + (tok % BS) * 16);
       }
+#pragma unroll
+    for (int t = 0; t < NDT; ++t) {
+      const char *src = vb[vtok / BS] + ((16 * t + n) * BS + vtok % BS) * ESZ;
+      if constexpr (kFp8) tl.v[t] = load8_stream(src);
+      else tl.v[t] = load16_stream(src);
+    }
     return tl;
   };
 
-  auto process = [&](int blk, const Tile &tl) {
-    // S^T for each 16-token sub-tile: lane holds head n, tokens 16s + 4g + e.
-    f32x4 st[NSUB];
+  auto process = [&](int step, const Tile &tl) {
+    // S^T for each 16-token sub-tile: lane holds head n, tokens 16h + 4g + e.
+    f32x4 st[2];
 #pragma unroll
-    for (int s = 0; s < NSUB; ++s) {
+    for (int h = 0; h < 2; ++h) {
       f32x4 c = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int i = 0; i < NLK; ++i) {
         if constexpr (kFp8) {
-          const u32x4 kw = tl.k[s][i];
+          const u32x4 kw = tl.k[h][i];
           const u32x4 lo = {fp8x2_to<false>(kw.x, QT()), fp8x2_to<true>(kw.x, QT()),
                             fp8x2_to<false>(kw.y, QT()), fp8x2_to<true>(kw.y, QT())};
           const u32x4 hi = {fp8x2_to<false>(kw.z, QT()), fp8x2_to<true>(kw.z, QT()),
@@ -161,23 +201,23 @@ __global__ void __launch_bounds__(kThreads) pa_partition_mfma(const Params p) {
           c = mfma_qk(lo, qop[2 * i], c, QT());
           c = mfma_qk(hi, qop[2 * i + 1], c, QT());
         } else {
-          c = mfma_qk(tl.k[s][i], qop[i], c, QT());
+          c = mfma_qk(tl.k[h][i], qop[i], c, QT());
         }
       }
-      st[s] = c;
+      st[h] = c;
     }
-    // Scale, ALiBi, mask, block max over the head's tokens.
-    const int t0 = blk * BS;
-    float x[NSUB][4];
+    // Scale, ALiBi, mask, step max over the head's tokens.
+    const int t0 = tok_begin + 32 * step;
+    float x[2][4];
     float bm = -__builtin_inff();
 #pragma unroll
-    for (int s = 0; s < NSUB; ++s)
+    for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int t = t0 + 16 * s + 4 * g + e;
-        float v = st[s][e] * p.scale_log2 + slope2 * (float)(t - w.t_ref);
+        const int t = t0 + 16 * h + 4 * g + e;
+        float v = st[h][e] * p.scale_log2 + slope2 * (float)(t - w.t_ref);
         v = (t < w.L) ? v : -__builtin_inff();
-        x[s][e] = v;
+        x[h][e] = v;
         bm = fmaxf(bm, v);
       }
     bm = xor_max<32>(xor_max<16>(bm));
@@ -185,50 +225,54 @@ __global__ void __launch_bounds__(kThreads) pa_partition_mfma(const Params p) {
     const float alpha = (m_new == -__builtin_inff()) ? 1.0f : fast_exp2(m_run - m_new);
     m_run = m_new;
     float psum = 0.0f;
-    u32x2 pop[NSUB];
+    u32x2 pk[2];
 #pragma unroll
-    for (int s = 0; s < NSUB; ++s) {
+    for (int h = 0; h < 2; ++h) {
       float pe[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        pe[e] = fast_exp2(x[s][e] - m_new);
+        pe[e] = fast_exp2(x[h][e] - m_new);
         psum += pe[e];
       }
-      pop[s] = u32x2{pack2(pe[0], pe[1], PT()), pack2(pe[2], pe[3], PT())};
+      pk[h] = u32x2{pack2(pe[0], pe[1], PT()), pack2(pe[2], pe[3], PT())};
     }
     l_run = l_run * alpha + psum;
-    const int nv = w.L - t0;  // valid tokens in the block (>= 1)
+    const u32x4 pop = regroup_p(pk[0], pk[1]);
+    const int nv = w.L - (t0 + vtok);  // valid tokens among this lane's V operand
 #pragma unroll
     for (int t = 0; t < NDT; ++t) {
-      f32x4 c = oacc[t] * alpha;
-#pragma unroll
-      for (int s = 0; s < NSUB; ++s) {
-        u32x2 va;
-        if constexpr (kFp8) {
-          va = u32x2{fp8x2_to<false>(tl.v[s][t], _Float16()), fp8x2_to<true>(tl.v[s][t], _Float16())};
-        } else {
-          va = tl.v[s][t];
-        }
-        if (nv < BS) va = mask_v4(va, 16 * s + 4 * g, nv);
-        c = mfma_pv(va, pop[s], c, PT());
+      u32x4 va;
+      if constexpr (kFp8) {
+        va = u32x4{fp8x2_to<false>(tl.v[t].x, _Float16()), fp8x2_to<true>(tl.v[t].x, _Float16()),
+                   fp8x2_to<false>(tl.v[t].y, _Float16()), fp8x2_to<true>(tl.v[t].y, _Float16())};
+      } else {
+        va = tl.v[t];
       }
-      oacc[t] = c;
+      if (nv < 8) va = mask_v8(va, 0, nv);
+      oacc[t] = mfma_pv(va, pop, oacc[t] * alpha, PT());
     }
   };
 
-  // Two tiles in flight: the next block's loads are issued before the
-  // current block is consumed (ping-pong, no register copies).
-  int blk = w.blk_begin + wv;
-  Tile ta, tb;
-  if (blk < w.blk_end) ta = load_tile(blk);
-  while (blk < w.blk_end) {
-    if (blk + kWaves < w.blk_end) tb = load_tile(blk + kWaves);
-    process(blk, ta);
-    blk += kWaves;
-    if (blk >= w.blk_end) break;
-    if (blk + kWaves < w.blk_end) ta = load_tile(blk + kWaves);
-    process(blk, tb);
-    blk += kWaves;
+  // NBUF tiles rotate: the loads of step st + (NBUF-1)*4 are issued before
+  // step st is consumed, so NBUF-1 tiles per wave are always in flight.
+  constexpr int NBUF = PA_PREFETCH_MFMA + 1;
+  int st = wv;
+  Tile tb[NBUF];
+#pragma unroll
+  for (int i = 0; i < NBUF - 1; ++i)
+    if (st + i * kWaves < n_steps) tb[i] = load_tile(st + i * kWaves);
+  bool more = st < n_steps;
+  while (more) {
+#pragma unroll
+    for (int j = 0; j < NBUF; ++j) {
+      if (more) {
+        const int pre = st + (NBUF - 1) * kWaves;
+        if (pre < n_steps) tb[(j + NBUF - 1) % NBUF] = load_tile(pre);
+        process(st, tb[j]);
+        st += kWaves;
+        more = st < n_steps;
+      }
+    }
   }
 
   // Wave totals: the four lanes of head n hold partial sums over their tokens.

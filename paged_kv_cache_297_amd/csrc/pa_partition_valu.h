@@ -215,8 +215,14 @@ __device__ __forceinline__ float dim_group_sum(float v) {
   return v;
 }
 
+#if PA_WAVES_PER_EU_VALU > 0
+#define PA_VALU_OCCUPANCY __attribute__((amdgpu_waves_per_eu(PA_WAVES_PER_EU_VALU)))
+#else
+#define PA_VALU_OCCUPANCY
+#endif
+
 template <typename QT, typename KVT, int D, int BS, int GP>
-__global__ void __launch_bounds__(kThreads) pa_partition_valu(const Params p) {
+__global__ void __launch_bounds__(kThreads) PA_VALU_OCCUPANCY pa_partition_valu(const Params p) {
   using T = ValuTraits<QT, KVT>;
   using HM = HeadMap<GP, BS>;
   using PV = typename T::PV;
@@ -368,19 +374,26 @@ __global__ void __launch_bounds__(kThreads) pa_partition_valu(const Params p) {
     }
   };
 
-  // Two tiles in flight: the next block's loads are issued before the
-  // current block is consumed (ping-pong, no register copies).
+  // NBUF tiles rotate: the loads of block blk + (NBUF-1)*4 are issued before
+  // block blk is consumed, so NBUF-1 tiles per wave are always in flight.
+  constexpr int NBUF = PA_PREFETCH_VALU + 1;
   int blk = w.blk_begin + wv;
-  Tile ta, tb;
-  if (blk < w.blk_end) ta = load_tile(blk);
-  while (blk < w.blk_end) {
-    if (blk + kWaves < w.blk_end) tb = load_tile(blk + kWaves);
-    process(blk, 0, ta);
-    blk += kWaves;
-    if (blk >= w.blk_end) break;
-    if (blk + kWaves < w.blk_end) ta = load_tile(blk + kWaves);
-    process(blk, 1, tb);
-    blk += kWaves;
+  Tile tb[NBUF];
+#pragma unroll
+  for (int i = 0; i < NBUF - 1; ++i)
+    if (blk + i * kWaves < w.blk_end) tb[i] = load_tile(blk + i * kWaves);
+  bool more = blk < w.blk_end;
+  while (more) {
+#pragma unroll
+    for (int j = 0; j < NBUF; ++j) {
+      if (more) {
+        const int pre = blk + (NBUF - 1) * kWaves;
+        if (pre < w.blk_end) tb[(j + NBUF - 1) % NBUF] = load_tile(pre);
+        process(blk, ((blk - w.blk_begin) / kWaves) & 1, tb[j]);
+        blk += kWaves;
+        more = blk < w.blk_end;
+      }
+    }
   }
 
   // Wave totals per head, then the cross-wave merge.
