@@ -218,6 +218,32 @@ def paged_attention_auto(out, exp_sums, max_logits, tmp_out, query, key_cache, v
     _check(lib.paged_attention_auto(*args), "paged_attention_auto")
 
 
+class PreparedCall:
+    """A v2 / auto call whose arguments were checked and marshalled once.
+
+    ``__call__`` issues only the C call (on the stream fixed at preparation):
+    for tight loops where per-call Python argument handling would dominate,
+    e.g. timing.  The tensors must stay alive and unchanged in shape."""
+
+    def __init__(self, mode, out, exp_sums, max_logits, tmp_out, query, key_cache, value_cache,
+                 num_kv_heads, scale, block_tables, seq_lens, block_size, max_seq_len,
+                 alibi_slopes=None, kv_cache_dtype="auto", k_scale=1.0, v_scale=1.0,
+                 stream=None):
+        self.lib = load_library()
+        self.fn = {"v2": self.lib.paged_attention_v2, "auto": self.lib.paged_attention_auto}[mode]
+        self.name = f"paged_attention_{mode}"
+        self.args = _v2_args(out, exp_sums, max_logits, tmp_out, query, key_cache, value_cache,
+                             num_kv_heads, scale, block_tables, seq_lens, block_size, max_seq_len,
+                             alibi_slopes, kv_cache_dtype, k_scale, v_scale, stream)
+        self._keep = (out, exp_sums, max_logits, tmp_out, query, key_cache, value_cache,
+                      block_tables, seq_lens, alibi_slopes)
+
+    def __call__(self) -> None:
+        st = self.fn(*self.args)
+        if st != PA_OK:
+            _check(st, self.name)
+
+
 def paged_attention_partition(mode, out, exp_sums, max_logits, tmp_out, query, key_cache,
                               value_cache, num_kv_heads, scale, block_tables, seq_lens,
                               block_size, max_seq_len, alibi_slopes=None, kv_cache_dtype="auto",

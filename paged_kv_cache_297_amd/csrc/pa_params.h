@@ -22,7 +22,8 @@ enum Mode : int { kModeV1 = 0, kModeV2 = 1, kModeAuto = 2 };
 #ifndef PA_PREFETCH_MFMA
 #define PA_PREFETCH_MFMA 1
 #endif
-// Minimum waves per SIMD the register allocator must allow (0: no bound).
+// Minimum waves per SIMD the register allocator must allow (0: the kernel's
+// own choice).
 #ifndef PA_WAVES_PER_EU_MFMA
 #define PA_WAVES_PER_EU_MFMA 0
 #endif

@@ -10,73 +10,74 @@
 
 namespace pa {
 
-constexpr int kReduceChunk = 1024;  // partitions whose weights sit in LDS at once
+constexpr int kReduceBatch = 8;  // partitions whose loads one thread issues together
 
-__device__ __forceinline__ float block_max(float v, float *sm) {
-  v = xor_max<32>(xor_max<16>(row16_max(v)));
-  if ((threadIdx.x & 63) == 0) sm[threadIdx.x >> 6] = v;
-  __syncthreads();
-  float r = sm[0];
-#pragma unroll
-  for (int i = 1; i < kWaves; ++i) r = fmaxf(r, sm[i]);
-  __syncthreads();
-  return r;
-}
-
+// Thread (pg, d) folds partitions pg, pg + DG, ... of the row into a running
+// (max m, sum s = sum exp(m_p - m) S_p, acc = sum exp(m_p - m) S_p O_p[d]),
+// loading kReduceBatch partitions at a time so that the loads of max_logits,
+// exp_sums and tmp_out are in flight together; the DG partial states of a
+// dim are then combined with the same rescale.  The result is the merge above
+// with M the global max.
 template <typename QT, int D>
 __global__ void __launch_bounds__(kThreads) pa_reduce_kernel(const Params p) {
-  constexpr int DG = kThreads / D;  // partition lanes per dim
+  constexpr int DG = kThreads / D;  // partition groups per dim
   const int head = blockIdx.x, seq = blockIdx.y;
   const int L = p.seq_lens[seq];
   if (L < 0 || L > p.max_seq_len || !seq_uses_v2(p, L)) return;
   const int n_part = (L + kPartitionSize - 1) / kPartitionSize;
   if (n_part <= 1) return;
 
-  __shared__ float sm_red[kWaves];
-  __shared__ float sm_w[kReduceChunk];
-  __shared__ float sm_acc[DG][D];
+  __shared__ float sm_m[DG][D], sm_s[DG][D], sm_a[DG][D];
 
   const size_t row = ((size_t)seq * p.num_heads + head) * p.max_num_partitions;
   const float *ml = p.max_logits + row;
   const float *es = p.exp_sums + row;
   const float *to = p.tmp_out + row * D;
-  const int tid = threadIdx.x;
+  const int d = threadIdx.x % D, pg = threadIdx.x / D;
+  const float ninf = -__builtin_inff();
 
-  float m = -__builtin_inff();
-  for (int i = tid; i < n_part; i += kThreads) m = fmaxf(m, ml[i]);
-  const float big_m = block_max(m, sm_red);
-
-  const int d = tid % D, pg = tid / D;
-  float acc = 0.0f, wsum = 0.0f;
-  for (int c0 = 0; c0 < n_part; c0 += kReduceChunk) {
-    const int cnt = min(kReduceChunk, n_part - c0);
-    for (int i = tid; i < cnt; i += kThreads) {
-      const float r = fast_exp2((ml[c0 + i] - big_m) * kLog2e) * es[c0 + i];
-      sm_w[i] = r;
-    }
-    __syncthreads();
-    const float *src = to + (size_t)c0 * D + d;
-    int i = pg;
-    for (; i + 3 * DG < cnt; i += 4 * DG) {
-      const float v0 = src[(size_t)i * D], v1 = src[(size_t)(i + DG) * D];
-      const float v2 = src[(size_t)(i + 2 * DG) * D], v3 = src[(size_t)(i + 3 * DG) * D];
-      acc = fmaf(sm_w[i], v0, acc);
-      acc = fmaf(sm_w[i + DG], v1, acc);
-      acc = fmaf(sm_w[i + 2 * DG], v2, acc);
-      acc = fmaf(sm_w[i + 3 * DG], v3, acc);
-    }
-    for (; i < cnt; i += DG) acc = fmaf(sm_w[i], src[(size_t)i * D], acc);
-    for (int j = 0; j < cnt; ++j) wsum += sm_w[j];
-    __syncthreads();
-  }
-  sm_acc[pg][d] = acc;
-  __syncthreads();
-  if (tid < D) {
-    float o = 0.0f;
+  float m_run = ninf, s_run = 0.0f, a_run = 0.0f;
+  for (int base = pg; base < n_part; base += kReduceBatch * DG) {
+    float mv[kReduceBatch], ev[kReduceBatch], ov[kReduceBatch];
 #pragma unroll
-    for (int k = 0; k < DG; ++k) o += sm_acc[k][tid];
+    for (int j = 0; j < kReduceBatch; ++j) {
+      const int q = base + j * DG;
+      const bool ok = q < n_part;
+      mv[j] = ok ? ml[q] : ninf;
+      ev[j] = ok ? es[q] : 0.0f;
+      ov[j] = ok ? to[(size_t)q * D + d] : 0.0f;
+    }
+    float bm = m_run;
+#pragma unroll
+    for (int j = 0; j < kReduceBatch; ++j) bm = fmaxf(bm, mv[j]);
+    const float keep = (m_run == ninf) ? 0.0f : fast_exp2((m_run - bm) * kLog2e);
+    s_run *= keep;
+    a_run *= keep;
+#pragma unroll
+    for (int j = 0; j < kReduceBatch; ++j) {
+      const float r = (mv[j] == ninf) ? 0.0f : fast_exp2((mv[j] - bm) * kLog2e) * ev[j];
+      s_run += r;
+      a_run = fmaf(r, ov[j], a_run);
+    }
+    m_run = bm;
+  }
+  sm_m[pg][d] = m_run;
+  sm_s[pg][d] = s_run;
+  sm_a[pg][d] = a_run;
+  __syncthreads();
+  if (pg == 0) {
+    float big_m = ninf;
+#pragma unroll
+    for (int k = 0; k < DG; ++k) big_m = fmaxf(big_m, sm_m[k][d]);
+    float s = 0.0f, a = 0.0f;
+#pragma unroll
+    for (int k = 0; k < DG; ++k) {
+      const float c = (sm_m[k][d] == ninf) ? 0.0f : fast_exp2((sm_m[k][d] - big_m) * kLog2e);
+      s += c * sm_s[k][d];
+      a += c * sm_a[k][d];
+    }
     QT *out = reinterpret_cast<QT *>(p.out);
-    out[((size_t)seq * p.num_heads + head) * D + tid] = from_f32<QT>(o / wsum);
+    out[((size_t)seq * p.num_heads + head) * D + d] = from_f32<QT>(a / s);
   }
 }
 
