@@ -73,12 +73,12 @@ def algorithmic_bytes(wl, path: str, cu: int, B) -> dict:
     else:
         v2 = np.array([B.should_use_v2(wl.num_seqs, wl.num_kv_heads, int(L), cu) for L in lens])
     h, d = wl.num_heads, wl.head_size
-    tmp = int((parts * v2).sum()) * h * d * 4
+    tmp = int((parts * v2).sum()) * h * d * esz_q   # partial outputs in the query dtype
     stats = int((v2 * wl.max_num_partitions).sum()) * h * 8   # values and padding
     multi = v2 & (parts > 1)
     out_p1 = int((~multi).sum()) * h * d * esz_q
     out_p2 = int(multi.sum()) * h * d * esz_q
-    reduce_read = int((parts * multi).sum()) * h * (d * 4 + 8)
+    reduce_read = int((parts * multi).sum()) * h * (d * esz_q + 8)
     return {"kv": kv, "partition": kv + q + table + tmp + stats + out_p1,
             "reduce": reduce_read + out_p2 + wl.num_seqs * 4,
             "step": kv + q + table + tmp + stats + out + reduce_read}

@@ -46,7 +46,10 @@
  *   seq_lens      int32 [num_seqs]
  *   alibi_slopes  float [num_heads], or NULL for no ALiBi
  *   exp_sums, max_logits  float [num_seqs, num_heads, max_num_partitions]
- *   tmp_out       float [num_seqs, num_heads, max_num_partitions, head_size]
+ *   tmp_out       [num_seqs, num_heads, max_num_partitions, head_size]  dtype
+ *                 (the partial outputs are rounded to the query / output
+ *                 type, as the V2 page's Phase 1 casts each partition's
+ *                 output to the type of its tmp_output buffer)
  *
  * Ownership.  Every buffer belongs to the caller.  The library allocates and
  * frees nothing and keeps no pointer after a call returns.  Its only global
@@ -126,7 +129,7 @@ pa_status paged_attention_v1(
  * for p < ceil(L/512) only (later slots are untouched scratch).  A sequence
  * of length 0 gets out = 0 and padding statistics. */
 pa_status paged_attention_v2(
-    void *out, float *exp_sums, float *max_logits, float *tmp_out,
+    void *out, float *exp_sums, float *max_logits, void *tmp_out,
     const void *query, const void *key_cache, const void *value_cache,
     int num_seqs, int num_heads, int num_kv_heads, int head_size, float scale,
     const int32_t *block_tables, int max_num_blocks_per_seq, const int32_t *seq_lens,
@@ -139,7 +142,7 @@ pa_status paged_attention_v2(
  * sent down the v1 path get out only; their exp_sums / max_logits / tmp_out
  * rows are left as they were. */
 pa_status paged_attention_auto(
-    void *out, float *exp_sums, float *max_logits, float *tmp_out,
+    void *out, float *exp_sums, float *max_logits, void *tmp_out,
     const void *query, const void *key_cache, const void *value_cache,
     int num_seqs, int num_heads, int num_kv_heads, int head_size, float scale,
     const int32_t *block_tables, int max_num_blocks_per_seq, const int32_t *seq_lens,
@@ -157,7 +160,7 @@ pa_status paged_attention_auto(
 
 /* Phase 1 (V2 page, "Phase 1: Per-partition attention"). */
 pa_status paged_attention_partition(
-    pa_mode mode, void *out, float *exp_sums, float *max_logits, float *tmp_out,
+    pa_mode mode, void *out, float *exp_sums, float *max_logits, void *tmp_out,
     const void *query, const void *key_cache, const void *value_cache,
     int num_seqs, int num_heads, int num_kv_heads, int head_size, float scale,
     const int32_t *block_tables, int max_num_blocks_per_seq, const int32_t *seq_lens,
@@ -171,7 +174,7 @@ pa_status paged_attention_partition(
  * and block_tables are not read and may be NULL. */
 pa_status paged_attention_reduce(
     pa_mode mode, void *out, const float *exp_sums, const float *max_logits,
-    const float *tmp_out, int num_seqs, int num_heads, int num_kv_heads, int head_size,
+    const void *tmp_out, int num_seqs, int num_heads, int num_kv_heads, int head_size,
     const int32_t *seq_lens, int max_seq_len, int max_num_partitions, pa_dtype dtype,
     void *stream);
 

@@ -179,9 +179,11 @@ def _v2_args(out, exp_sums, max_logits, tmp_out, query, key_cache, value_cache, 
         raise ValueError("num_kv_heads / block_size disagree with the cache shape")
     if out.shape != query.shape or out.dtype != query.dtype or not out.is_contiguous():
         raise ValueError("out must be a contiguous tensor like query")
-    for name, t in (("exp_sums", exp_sums), ("max_logits", max_logits), ("tmp_out", tmp_out)):
+    for name, t in (("exp_sums", exp_sums), ("max_logits", max_logits)):
         if t.dtype != torch.float32 or not t.is_contiguous():
             raise TypeError(f"{name} must be a contiguous float32 tensor")
+    if tmp_out.dtype != query.dtype or not tmp_out.is_contiguous():
+        raise TypeError("tmp_out must be a contiguous tensor of the query's dtype")
     p = exp_sums.shape[2]
     if exp_sums.shape != (b, h, p) or max_logits.shape != (b, h, p) or tmp_out.shape != (b, h, p, d):
         raise ValueError("exp_sums/max_logits must be [B, H, P] and tmp_out [B, H, P, D]")

@@ -89,7 +89,8 @@ thread_local TimingEvents t_events;
 struct Call {
   pa_mode mode;
   void *out;
-  float *exp_sums, *max_logits, *tmp_out;
+  float *exp_sums, *max_logits;
+  void *tmp_out;
   const void *query, *key_cache, *value_cache;
   int num_seqs, num_heads, num_kv_heads, head_size;
   float scale;
@@ -250,7 +251,7 @@ pa_status run_reduce(const Call &c) {
   return e == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
-Call make_call(pa_mode mode, void *out, float *exp_sums, float *max_logits, float *tmp_out,
+Call make_call(pa_mode mode, void *out, float *exp_sums, float *max_logits, void *tmp_out,
                const void *query, const void *key_cache, const void *value_cache, int num_seqs,
                int num_heads, int num_kv_heads, int head_size, float scale,
                const int32_t *block_tables, int max_num_blocks_per_seq, const int32_t *seq_lens,
@@ -292,7 +293,7 @@ Call make_call(pa_mode mode, void *out, float *exp_sums, float *max_logits, floa
 extern "C" {
 
 pa_status paged_attention_partition(pa_mode mode, void *out, float *exp_sums, float *max_logits,
-                                    float *tmp_out, const void *query, const void *key_cache,
+                                    void *tmp_out, const void *query, const void *key_cache,
                                     const void *value_cache, int num_seqs, int num_heads,
                                     int num_kv_heads, int head_size, float scale,
                                     const int32_t *block_tables, int max_num_blocks_per_seq,
@@ -309,19 +310,19 @@ pa_status paged_attention_partition(pa_mode mode, void *out, float *exp_sums, fl
 }
 
 pa_status paged_attention_reduce(pa_mode mode, void *out, const float *exp_sums,
-                                 const float *max_logits, const float *tmp_out, int num_seqs,
+                                 const float *max_logits, const void *tmp_out, int num_seqs,
                                  int num_heads, int num_kv_heads, int head_size,
                                  const int32_t *seq_lens, int max_seq_len, int max_num_partitions,
                                  pa_dtype dtype, void *stream) {
   return run_reduce(make_call(mode, out, const_cast<float *>(exp_sums),
-                              const_cast<float *>(max_logits), const_cast<float *>(tmp_out),
+                              const_cast<float *>(max_logits), const_cast<void *>(tmp_out),
                               nullptr, nullptr, nullptr, num_seqs, num_heads, num_kv_heads,
                               head_size, 1.0f, nullptr, 0, seq_lens, 0, 16, max_seq_len,
                               max_num_partitions, nullptr, dtype, PA_KV_AUTO, 1.0f, 1.0f, stream));
 }
 
 static pa_status two_phase(pa_mode mode, void *out, float *exp_sums, float *max_logits,
-                           float *tmp_out, const void *query, const void *key_cache,
+                           void *tmp_out, const void *query, const void *key_cache,
                            const void *value_cache, int num_seqs, int num_heads, int num_kv_heads,
                            int head_size, float scale, const int32_t *block_tables,
                            int max_num_blocks_per_seq, const int32_t *seq_lens, int num_blocks,
@@ -357,7 +358,7 @@ pa_status paged_attention_v1(void *out, const void *query, const void *key_cache
                                  k_scale, v_scale, stream));
 }
 
-pa_status paged_attention_v2(void *out, float *exp_sums, float *max_logits, float *tmp_out,
+pa_status paged_attention_v2(void *out, float *exp_sums, float *max_logits, void *tmp_out,
                              const void *query, const void *key_cache, const void *value_cache,
                              int num_seqs, int num_heads, int num_kv_heads, int head_size,
                              float scale, const int32_t *block_tables, int max_num_blocks_per_seq,
@@ -372,7 +373,7 @@ pa_status paged_attention_v2(void *out, float *exp_sums, float *max_logits, floa
                    stream);
 }
 
-pa_status paged_attention_auto(void *out, float *exp_sums, float *max_logits, float *tmp_out,
+pa_status paged_attention_auto(void *out, float *exp_sums, float *max_logits, void *tmp_out,
                                const void *query, const void *key_cache, const void *value_cache,
                                int num_seqs, int num_heads, int num_kv_heads, int head_size,
                                float scale, const int32_t *block_tables,

@@ -51,6 +51,14 @@ __device__ __forceinline__ u32x4 load16(const void *p) {
   return *reinterpret_cast<const u32x4 *>(p);
 }
 
+// Read-only tables (block tables) are read through the constant address
+// space: a wave-uniform index then compiles to a scalar load, which waits on
+// its own counter instead of behind the KV tile loads in flight.
+typedef const int32_t __attribute__((address_space(4))) *const_i32_ptr;
+__device__ __forceinline__ const_i32_ptr as_const_table(const int32_t *p) {
+  return (const_i32_ptr)(uintptr_t)p;
+}
+
 // ---------------------------------------------------------------------------
 // Packed dot products with fp32 accumulation.
 // ---------------------------------------------------------------------------
@@ -81,6 +89,13 @@ __device__ __forceinline__ unsigned pack2(float a, float b, __bf16) {
 __device__ __forceinline__ unsigned pack2(float a, float b, _Float16) {
   f16x2 v = {(_Float16)a, (_Float16)b};
   return __builtin_bit_cast(unsigned, v);
+}
+
+// Keep-mask of a 32-bit word holding two 16-bit elements of tokens t, t + 1:
+// the half of a token >= nv is cleared.  Straight-line selects, so the tail
+// mask can be applied on every step without a divergent branch.
+__device__ __forceinline__ unsigned keep_pair_mask(int t, int nv) {
+  return (t < nv ? 0x0000FFFFu : 0u) | (t + 1 < nv ? 0xFFFF0000u : 0u);
 }
 
 template <typename T>

@@ -15,13 +15,6 @@ constexpr int kThreads = 64 * kWaves;
 
 enum Mode : int { kModeV1 = 0, kModeV2 = 1, kModeAuto = 2 };
 
-// (block, KV head) tiles a wave keeps in flight ahead of the one it consumes.
-#ifndef PA_PREFETCH_VALU
-#define PA_PREFETCH_VALU 1
-#endif
-#ifndef PA_PREFETCH_MFMA
-#define PA_PREFETCH_MFMA 1
-#endif
 // Minimum waves per SIMD the register allocator must allow (0: the kernel's
 // own choice).
 #ifndef PA_WAVES_PER_EU_MFMA
@@ -39,7 +32,7 @@ struct Params {
   void *out;            // [B, H, D] dtype
   float *exp_sums;      // [B, H, P]
   float *max_logits;    // [B, H, P]
-  float *tmp_out;       // [B, H, P, D]
+  void *tmp_out;        // [B, H, P, D] dtype
   const void *query;    // [B, H, D] dtype
   const void *key_cache;    // [NB, Hkv, D/x, bs, x]
   const void *value_cache;  // [NB, Hkv, D, bs]

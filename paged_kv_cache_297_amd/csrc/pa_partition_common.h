@@ -134,7 +134,7 @@ __device__ __forceinline__ void finish_partition(const Params &p, const Work &w,
     }
     if (w.v2) {
       const size_t row = ((size_t)w.seq * p.num_heads + head) * p.max_num_partitions + w.part;
-      p.tmp_out[row * D + d] = o;
+      reinterpret_cast<QT *>(p.tmp_out)[row * D + d] = from_f32<QT>(o);
       if (d == 0) {
         p.exp_sums[row] = sum;
         p.max_logits[row] = ml;

@@ -51,15 +51,10 @@ __device__ __forceinline__ f32x4 mfma_pv(const u32x4 &a, const u32x4 &b, const f
 }
 
 // Zero the 16-bit elements of tokens >= nv in an 8-token V operand whose
-// first element is token `first`.
-__device__ __forceinline__ u32x4 mask_v8(u32x4 v, int first, int nv) {
-  unsigned w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    if (first + 2 * e >= nv) w[e] = 0u;
-    else if (first + 2 * e + 1 >= nv) w[e] &= 0xFFFFu;
-  }
-  return u32x4{w[0], w[1], w[2], w[3]};
+// first element is token 0.
+__device__ __forceinline__ u32x4 mask_v8(u32x4 v, int nv) {
+  return u32x4{v.x & keep_pair_mask(0, nv), v.y & keep_pair_mask(2, nv),
+               v.z & keep_pair_mask(4, nv), v.w & keep_pair_mask(6, nv)};
 }
 
 // Regroups packed P (two 4-token pieces per lane: p0 from sub-tile 0, p1
@@ -78,12 +73,12 @@ __device__ __forceinline__ u32x4 regroup_p(const u32x2 &p0, const u32x2 &p1) {
 }
 
 // Waves per SIMD the register allocator must leave room for.  fp8 caches
-// halve the tile registers, so three waves fit without spilling (measured
-// 421 -> 400 us on the fp8 decode workload); the 16-bit kernels would spill.
+// halve the tile registers, so three waves fit without spilling; the 16-bit
+// kernels fit two.
 template <typename KVT>
 constexpr int mfma_waves_per_eu() {
   if constexpr (PA_WAVES_PER_EU_MFMA > 0) return PA_WAVES_PER_EU_MFMA;
-  else return std::is_same<KVT, fp8e4m3>::value ? 3 : 1;
+  else return std::is_same<KVT, fp8e4m3>::value ? 3 : 2;
 }
 
 template <typename QT, typename KVT, int D, int BS>
@@ -137,7 +132,7 @@ __global__ void __launch_bounds__(kThreads)
 
   const char *kcache = reinterpret_cast<const char *>(p.key_cache);
   const char *vcache = reinterpret_cast<const char *>(p.value_cache);
-  const int32_t *btab = p.block_tables + (size_t)w.seq * p.max_num_blocks_per_seq;
+  const const_i32_ptr btab = as_const_table(p.block_tables + (size_t)w.seq * p.max_num_blocks_per_seq);
   const size_t head_off = (size_t)w.kvh * TILE;
   const size_t blk_stride = (size_t)p.num_kv_heads * TILE;
   const int tok_begin = w.blk_begin * BS;
@@ -156,22 +151,28 @@ __global__ void __launch_bounds__(kThreads)
   // addressable) and reported through the poison flag; the second block of
   // a step past the range end is read from block 0 too, and all its tokens
   // are masked.
+  // The V operand's block differs between lane groups when two blocks make
+  // a step; it is selected as an index and addressed from the cache base, so
+  // the loads stay global (a per-lane select between two pointers compiles to
+  // flat loads, whose completion order forces full waits on every step).
   auto load_tile = [&](int step) {
-    const char *kb[BPS], *vb[BPS];
+    int phys[BPS];
+    const char *kb[BPS];
 #pragma unroll
     for (int b = 0; b < BPS; ++b) {
       const int lb = w.blk_begin + step * BPS + b;
-      int phys = 0;
+      phys[b] = 0;
       if (lb < w.blk_end) {
-        phys = btab[lb];
-        if (phys < 0 || phys >= p.num_blocks) {
+        phys[b] = btab[lb];
+        if (phys[b] < 0 || phys[b] >= p.num_blocks) {
           poisoned = true;
-          phys = 0;
+          phys[b] = 0;
         }
       }
-      kb[b] = kcache + (size_t)phys * blk_stride + head_off;
-      vb[b] = vcache + (size_t)phys * blk_stride + head_off;
+      kb[b] = kcache + (size_t)phys[b] * blk_stride + head_off;
     }
+    const int vphys = (BPS == 1 || vtok < BS) ? phys[0] : phys[BPS - 1];
+    const char *vb = vcache + (size_t)vphys * blk_stride + head_off;
     Tile tl;
 #pragma unroll
     for (int h = 0; h < 2; ++h)
@@ -182,7 +183,7 @@ __global__ void __launch_bounds__(kThreads)
       }
 #pragma unroll
     for (int t = 0; t < NDT; ++t) {
-      const char *src = vb[vtok / BS] + ((16 * t + n) * BS + vtok % BS) * ESZ;
+      const char *src = vb + ((16 * t + n) * BS + vtok % BS) * ESZ;
       if constexpr (kFp8) tl.v[t] = load8_stream(src);
       else tl.v[t] = load16_stream(src);
     }
@@ -253,31 +254,38 @@ __global__ void __launch_bounds__(kThreads)
       } else {
         va = tl.v[t];
       }
-      if (nv < 8) va = mask_v8(va, 0, nv);
+      va = mask_v8(va, nv);
       oacc[t] = mfma_pv(va, pop, oacc[t] * alpha, PT());
     }
   };
 
-  // NBUF tiles rotate: the loads of step st + (NBUF-1)*4 are issued before
-  // step st is consumed, so NBUF-1 tiles per wave are always in flight.
-  constexpr int NBUF = PA_PREFETCH_MFMA + 1;
+  // Two tiles ping-pong: while step st is consumed, the loads of the wave's
+  // next step (st + 4) are in flight.  The loop runs whole pairs and has no
+  // exit between them, and every load in it is always issued, so the wait
+  // before a step covers only that step's tile (a mid-pair exit would merge
+  // a path with the other tile still in flight into the back edge).  The
+  // scheduling barriers keep each prefetch ahead of the step's compute.
   int st = wv;
-  Tile tb[NBUF];
-#pragma unroll
-  for (int i = 0; i < NBUF - 1; ++i)
-    if (st + i * kWaves < n_steps) tb[i] = load_tile(st + i * kWaves);
-  bool more = st < n_steps;
-  while (more) {
-#pragma unroll
-    for (int j = 0; j < NBUF; ++j) {
-      if (more) {
-        const int pre = st + (NBUF - 1) * kWaves;
-        if (pre < n_steps) tb[(j + NBUF - 1) % NBUF] = load_tile(pre);
-        process(st, tb[j]);
-        st += kWaves;
-        more = st < n_steps;
-      }
-    }
+  int left = st < n_steps ? (n_steps - st + kWaves - 1) / kWaves : 0;  // this wave's steps
+  Tile ta, tb;
+  if (left > 0) ta = load_tile(st);
+  while (left >= 3) {
+    tb = load_tile(st + kWaves);
+    __builtin_amdgcn_sched_barrier(0);
+    process(st, ta);
+    ta = load_tile(st + 2 * kWaves);
+    __builtin_amdgcn_sched_barrier(0);
+    process(st + kWaves, tb);
+    st += 2 * kWaves;
+    left -= 2;
+  }
+  if (left == 2) {
+    tb = load_tile(st + kWaves);
+    __builtin_amdgcn_sched_barrier(0);
+    process(st, ta);
+    process(st + kWaves, tb);
+  } else if (left == 1) {
+    process(st, ta);
   }
 
   // Wave totals: the four lanes of head n hold partial sums over their tokens.

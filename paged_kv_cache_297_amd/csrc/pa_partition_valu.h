@@ -54,8 +54,7 @@ struct ValuTraits<float, float> {
   // Zero the V elements of tokens >= nv (first = token of element 0).
   __device__ static void mask_v(unsigned (&w)[kPW], int first, int nv) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      if (first + e >= nv) w[e] = 0u;
+    for (int e = 0; e < 4; ++e) w[e] &= (first + e < nv) ? ~0u : 0u;
   }
 };
 
@@ -86,10 +85,7 @@ struct ValuTraits16 {
   }
   __device__ static void mask_v(unsigned (&w)[kPW], int first, int nv) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      if (first + 2 * e >= nv) w[e] = 0u;
-      else if (first + 2 * e + 1 >= nv) w[e] &= 0xFFFFu;
-    }
+    for (int e = 0; e < 4; ++e) w[e] &= keep_pair_mask(first + 2 * e, nv);
   }
 };
 template <> struct ValuTraits<__bf16, __bf16> : ValuTraits16<__bf16> {};
@@ -133,10 +129,7 @@ struct ValuTraitsFp8 {
   // Applied to the widened words: word e holds tokens first+2e, first+2e+1.
   __device__ static void mask_v(unsigned (&w)[kPW], int first, int nv) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      if (first + 2 * e >= nv) w[e] = 0u;
-      else if (first + 2 * e + 1 >= nv) w[e] &= 0xFFFFu;
-    }
+    for (int e = 0; e < 8; ++e) w[e] &= keep_pair_mask(first + 2 * e, nv);
   }
 };
 template <> struct ValuTraits<__bf16, fp8e4m3> : ValuTraitsFp8<__bf16> {};
@@ -297,7 +290,7 @@ __global__ void __launch_bounds__(kThreads) PA_VALU_OCCUPANCY pa_partition_valu(
 
   const char *kcache = reinterpret_cast<const char *>(p.key_cache);
   const char *vcache = reinterpret_cast<const char *>(p.value_cache);
-  const int32_t *btab = p.block_tables + (size_t)w.seq * p.max_num_blocks_per_seq;
+  const const_i32_ptr btab = as_const_table(p.block_tables + (size_t)w.seq * p.max_num_blocks_per_seq);
   const size_t head_off = (size_t)w.kvh * TILE;
   const size_t blk_stride = (size_t)p.num_kv_heads * TILE;
   bool poisoned = false;
@@ -361,7 +354,7 @@ __global__ void __launch_bounds__(kThreads) PA_VALU_OCCUPANCY pa_partition_valu(
     for (int i = 0; i < NL; ++i) {
       unsigned vw[T::kPW];
       T::v_words(tl.v[i], vw);
-      if (nv < BS) T::mask_v(vw, tg * X, nv);
+      T::mask_v(vw, tg * X, nv);
 #pragma unroll
       for (int h = 0; h < GP; ++h) {
         const float a_h = a_bc[h];
@@ -374,26 +367,33 @@ __global__ void __launch_bounds__(kThreads) PA_VALU_OCCUPANCY pa_partition_valu(
     }
   };
 
-  // NBUF tiles rotate: the loads of block blk + (NBUF-1)*4 are issued before
-  // block blk is consumed, so NBUF-1 tiles per wave are always in flight.
-  constexpr int NBUF = PA_PREFETCH_VALU + 1;
+  // Two tiles ping-pong: while block blk is consumed, the loads of the
+  // wave's next block (blk + 4) are in flight.  The loop runs whole pairs
+  // with no exit between them and always issues its loads, so the wait
+  // before a block covers only that block's tile; the scheduling barriers
+  // keep each prefetch ahead of the block's compute.
+  auto parity = [&](int b) { return ((b - w.blk_begin) / kWaves) & 1; };
   int blk = w.blk_begin + wv;
-  Tile tb[NBUF];
-#pragma unroll
-  for (int i = 0; i < NBUF - 1; ++i)
-    if (blk + i * kWaves < w.blk_end) tb[i] = load_tile(blk + i * kWaves);
-  bool more = blk < w.blk_end;
-  while (more) {
-#pragma unroll
-    for (int j = 0; j < NBUF; ++j) {
-      if (more) {
-        const int pre = blk + (NBUF - 1) * kWaves;
-        if (pre < w.blk_end) tb[(j + NBUF - 1) % NBUF] = load_tile(pre);
-        process(blk, ((blk - w.blk_begin) / kWaves) & 1, tb[j]);
-        blk += kWaves;
-        more = blk < w.blk_end;
-      }
-    }
+  int left = blk < w.blk_end ? (w.blk_end - blk + kWaves - 1) / kWaves : 0;  // this wave's blocks
+  Tile ta, tb;
+  if (left > 0) ta = load_tile(blk);
+  while (left >= 3) {
+    tb = load_tile(blk + kWaves);
+    __builtin_amdgcn_sched_barrier(0);
+    process(blk, parity(blk), ta);
+    ta = load_tile(blk + 2 * kWaves);
+    __builtin_amdgcn_sched_barrier(0);
+    process(blk + kWaves, parity(blk + kWaves), tb);
+    blk += 2 * kWaves;
+    left -= 2;
+  }
+  if (left == 2) {
+    tb = load_tile(blk + kWaves);
+    __builtin_amdgcn_sched_barrier(0);
+    process(blk, parity(blk), ta);
+    process(blk + kWaves, parity(blk + kWaves), tb);
+  } else if (left == 1) {
+    process(blk, parity(blk), ta);
   }
 
   // Wave totals per head, then the cross-wave merge.

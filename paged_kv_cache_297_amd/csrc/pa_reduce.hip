@@ -10,71 +10,104 @@
 
 namespace pa {
 
-constexpr int kReduceBatch = 8;  // partitions whose loads one thread issues together
+constexpr int kReduceBatch = 4;  // partitions whose loads one thread issues together
 
-// Thread (pg, d) folds partitions pg, pg + DG, ... of the row into a running
-// (max m, sum s = sum exp(m_p - m) S_p, acc = sum exp(m_p - m) S_p O_p[d]),
-// loading kReduceBatch partitions at a time so that the loads of max_logits,
-// exp_sums and tmp_out are in flight together; the DG partial states of a
-// dim are then combined with the same rescale.  The result is the merge above
-// with M the global max.
+// The 16-byte chunk of a partial row as fp32 values.
+template <typename QT>
+__device__ __forceinline__ void chunk_to_f32(const u32x4 &v, float (&f)[16 / sizeof(QT)]) {
+  const unsigned w[4] = {v.x, v.y, v.z, v.w};
+  if constexpr (sizeof(QT) == 4) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) f[e] = bits_f(w[e]);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const unsigned short h = (unsigned short)(w[e / 2] >> (16 * (e % 2)));
+      f[e] = to_f32(__builtin_bit_cast(QT, h));
+    }
+  }
+}
+
+// Thread (pg, c) reads the 16-byte chunk c of the partial rows of partitions
+// pg, pg + PG, ... (TPR threads cover a row, PG = 256 / TPR partitions are
+// read per instruction), kReduceBatch partitions at a time so that their
+// max_logits, exp_sums and tmp_out loads are in flight together, and folds
+// them into a running (max m, sum s = sum exp(m_p - m) S_p, acc = sum
+// exp(m_p - m) S_p O_p).  The PG running states of each dim are then merged
+// with the same rescale: the result is the merge above with M the global max.
 template <typename QT, int D>
 __global__ void __launch_bounds__(kThreads) pa_reduce_kernel(const Params p) {
-  constexpr int DG = kThreads / D;  // partition groups per dim
+  constexpr int EPT = 16 / sizeof(QT);  // elements per 16-byte chunk
+  constexpr int TPR = D / EPT;          // threads per partial row
+  constexpr int PG = kThreads / TPR;    // partition groups
+  static_assert(kThreads % TPR == 0 && D % EPT == 0, "reduce geometry");
   const int head = blockIdx.x, seq = blockIdx.y;
   const int L = p.seq_lens[seq];
   if (L < 0 || L > p.max_seq_len || !seq_uses_v2(p, L)) return;
   const int n_part = (L + kPartitionSize - 1) / kPartitionSize;
   if (n_part <= 1) return;
 
-  __shared__ float sm_m[DG][D], sm_s[DG][D], sm_a[DG][D];
+  __shared__ float sm_m[PG], sm_s[PG];
+  __shared__ float sm_a[PG][D];
 
   const size_t row = ((size_t)seq * p.num_heads + head) * p.max_num_partitions;
   const float *ml = p.max_logits + row;
   const float *es = p.exp_sums + row;
-  const float *to = p.tmp_out + row * D;
-  const int d = threadIdx.x % D, pg = threadIdx.x / D;
+  const char *to = reinterpret_cast<const char *>(p.tmp_out) + row * D * sizeof(QT);
+  const int c = threadIdx.x % TPR, pg = threadIdx.x / TPR;
   const float ninf = -__builtin_inff();
 
-  float m_run = ninf, s_run = 0.0f, a_run = 0.0f;
-  for (int base = pg; base < n_part; base += kReduceBatch * DG) {
-    float mv[kReduceBatch], ev[kReduceBatch], ov[kReduceBatch];
+  float m_run = ninf, s_run = 0.0f, a_run[EPT];
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) a_run[e] = 0.0f;
+  for (int base = pg; base < n_part; base += kReduceBatch * PG) {
+    float mv[kReduceBatch], ev[kReduceBatch];
+    u32x4 ov[kReduceBatch];
 #pragma unroll
     for (int j = 0; j < kReduceBatch; ++j) {
-      const int q = base + j * DG;
+      const int q = base + j * PG;
       const bool ok = q < n_part;
       mv[j] = ok ? ml[q] : ninf;
       ev[j] = ok ? es[q] : 0.0f;
-      ov[j] = ok ? to[(size_t)q * D + d] : 0.0f;
+      ov[j] = ok ? load16(to + ((size_t)q * D + c * EPT) * sizeof(QT)) : u32x4{0u, 0u, 0u, 0u};
     }
     float bm = m_run;
 #pragma unroll
     for (int j = 0; j < kReduceBatch; ++j) bm = fmaxf(bm, mv[j]);
     const float keep = (m_run == ninf) ? 0.0f : fast_exp2((m_run - bm) * kLog2e);
     s_run *= keep;
-    a_run *= keep;
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) a_run[e] *= keep;
 #pragma unroll
     for (int j = 0; j < kReduceBatch; ++j) {
       const float r = (mv[j] == ninf) ? 0.0f : fast_exp2((mv[j] - bm) * kLog2e) * ev[j];
+      float f[EPT];
+      chunk_to_f32<QT>(ov[j], f);
       s_run += r;
-      a_run = fmaf(r, ov[j], a_run);
+#pragma unroll
+      for (int e = 0; e < EPT; ++e) a_run[e] = fmaf(r, f[e], a_run[e]);
     }
     m_run = bm;
   }
-  sm_m[pg][d] = m_run;
-  sm_s[pg][d] = s_run;
-  sm_a[pg][d] = a_run;
+  // Every thread of a partition group holds the same m and s.
+  if (c == 0) {
+    sm_m[pg] = m_run;
+    sm_s[pg] = s_run;
+  }
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) sm_a[pg][c * EPT + e] = a_run[e];
   __syncthreads();
-  if (pg == 0) {
+  if (threadIdx.x < D) {
+    const int d = threadIdx.x;
     float big_m = ninf;
 #pragma unroll
-    for (int k = 0; k < DG; ++k) big_m = fmaxf(big_m, sm_m[k][d]);
+    for (int k = 0; k < PG; ++k) big_m = fmaxf(big_m, sm_m[k]);
     float s = 0.0f, a = 0.0f;
 #pragma unroll
-    for (int k = 0; k < DG; ++k) {
-      const float c = (sm_m[k][d] == ninf) ? 0.0f : fast_exp2((sm_m[k][d] - big_m) * kLog2e);
-      s += c * sm_s[k][d];
-      a += c * sm_a[k][d];
+    for (int k = 0; k < PG; ++k) {
+      const float cf = (sm_m[k] == ninf) ? 0.0f : fast_exp2((sm_m[k] - big_m) * kLog2e);
+      s += cf * sm_s[k];
+      a += cf * sm_a[k][d];
     }
     QT *out = reinterpret_cast<QT *>(p.out);
     out[((size_t)seq * p.num_heads + head) * D + d] = from_f32<QT>(a / s);

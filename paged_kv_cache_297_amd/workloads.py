@@ -108,7 +108,7 @@ class Workload:
         out = torch.empty((b, h, d), dtype=self.dtype, device=dev)
         exp_sums = torch.empty((b, h, p), dtype=torch.float32, device=dev)
         max_logits = torch.empty((b, h, p), dtype=torch.float32, device=dev)
-        tmp_out = torch.empty((b, h, p, d), dtype=torch.float32, device=dev)
+        tmp_out = torch.empty((b, h, p, d), dtype=self.dtype, device=dev)
         return out, exp_sums, max_logits, tmp_out
 
 

@@ -46,7 +46,7 @@ def run(wl: W.Workload, path: str, poison_outputs: bool = True):
     if path != "v1":
         res["exp_sums"] = es.cpu().numpy().astype(np.float64)
         res["max_logits"] = ml.cpu().numpy().astype(np.float64)
-        res["tmp_out"] = to.cpu().numpy().astype(np.float64)
+        res["tmp_out"] = to.float().cpu().numpy().astype(np.float64)
     return res
 
 

@@ -37,7 +37,8 @@ def test_v2_single_partition_is_bitwise_v1(shape):
     a = H.run(wl, "v1")
     b = H.run(wl, "v2")
     assert np.array_equal(a["out"], b["out"])
-    assert np.array_equal(b["tmp_out"][:, :, 0, :], b["out"]) or wl.dtype != torch.float32
+    # tmp_out has the output dtype, so a single partition stores the same rounded row twice.
+    assert np.array_equal(b["tmp_out"][:, :, 0, :], b["out"])
 
 
 @pytest.mark.parametrize("shape", list(SHAPES))
