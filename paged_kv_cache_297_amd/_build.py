@@ -59,7 +59,7 @@ def _compile(src: str, verbose: bool, build_dir: str, defines) -> str:
 def build(verbose: bool = False, jobs: int | None = None, defines=(), out: str = LIB_PATH) -> str:
     """Compile and link; returns the path of the shared library.
 
-    ``defines`` (e.g. ``["PA_PREFETCH_MFMA=2"]``) override the kernels'
+    ``defines`` (e.g. ``["PA_NONTEMPORAL=0"]``) override the kernels'
     compile-time tuning constants; ``out`` places such a variant elsewhere."""
     build_dir = BUILD_DIR if not defines else os.path.join(
         BUILD_DIR, "_".join(d.replace("=", "") for d in defines))
@@ -81,7 +81,7 @@ if __name__ == "__main__":
     import argparse
     ap = argparse.ArgumentParser(description="build libpagedattn.so for gfx950")
     ap.add_argument("-D", dest="defines", action="append", default=[],
-                    help="tuning constant, e.g. -D PA_PREFETCH_MFMA=2")
+                    help="tuning constant, e.g. -D PA_NONTEMPORAL=0")
     ap.add_argument("-o", dest="out", default=LIB_PATH)
     a = ap.parse_args()
     print(build(verbose=True, defines=a.defines, out=a.out))

@@ -41,22 +41,23 @@ __device__ __forceinline__ void write_stat_padding(const Params &p, const Work &
   }
 }
 
-// Decodes blockIdx into a Work item.  Returns false when this workgroup has
-// nothing (more) to do; sequences of length 0 (out = 0) and with an invalid
-// length (out = NaN) are finished here by the partition-0 workgroup.
+// Decodes one work item (sequence, grid-x slot = KV head x head group,
+// partition) into a Work.  Returns false when there is nothing (more) to
+// compute; sequences of length 0 (out = 0) and with an invalid length
+// (out = NaN) are finished here by their partition-0 item.
 template <typename QT, int D>
-__device__ __forceinline__ bool begin_work(const Params &p, int block_size, int group_slots,
-                                          Work &w) {
-  w.seq = blockIdx.y;
-  w.kvh = blockIdx.x / p.head_groups;
-  const int hg = blockIdx.x - w.kvh * p.head_groups;
+__device__ __forceinline__ bool decode_work(const Params &p, int seq, int xslot, int part,
+                                           int block_size, int group_slots, Work &w) {
+  w.seq = seq;
+  w.kvh = xslot / p.head_groups;
+  const int hg = xslot - w.kvh * p.head_groups;
   w.head0 = w.kvh * p.group + hg * group_slots;
   w.nh = min(group_slots, p.group - hg * group_slots);
   w.L = p.seq_lens[w.seq];
   const bool bad = (w.L < 0) || (w.L > p.max_seq_len);
   w.v2 = seq_uses_v2(p, bad ? 0 : w.L);
   w.n_part = bad ? 0 : (w.L + kPartitionSize - 1) / kPartitionSize;
-  w.part = blockIdx.z;
+  w.part = part;
   if (bad || w.L == 0) {
     if (w.part != 0) return false;
     const float fill = bad ? __builtin_nanf("") : 0.0f;
@@ -88,6 +89,13 @@ __device__ __forceinline__ bool begin_work(const Params &p, int block_size, int 
     w.t_ref = w.L - 1;
   }
   return true;
+}
+
+// Grid form: one item per workgroup, (x, y, z) = (slot, sequence, partition).
+template <typename QT, int D>
+__device__ __forceinline__ bool begin_work(const Params &p, int block_size, int group_slots,
+                                          Work &w) {
+  return decode_work<QT, D>(p, blockIdx.y, blockIdx.x, blockIdx.z, block_size, group_slots, w);
 }
 
 // Cross-wave merge and stores.  Wave wv left, for query head h of the group:

@@ -72,13 +72,21 @@ __device__ __forceinline__ u32x4 regroup_p(const u32x2 &p0, const u32x2 &p1) {
   return u32x4{b0[0], b1[0], b0[1], b1[1]};
 }
 
-// Waves per SIMD the register allocator must leave room for.  fp8 caches
-// halve the tile registers, so three waves fit without spilling; the 16-bit
-// kernels fit two.
+// Waves per SIMD the register allocator must leave room for: two, with
+// both ping-pong tiles in registers.  (fp8 tiles are half the size, but three
+// waves make the allocator spill and measured slower than two.)
 template <typename KVT>
 constexpr int mfma_waves_per_eu() {
   if constexpr (PA_WAVES_PER_EU_MFMA > 0) return PA_WAVES_PER_EU_MFMA;
-  else return std::is_same<KVT, fp8e4m3>::value ? 3 : 2;
+  else return 2;
+}
+
+// Barrier over LDS only: orders the workgroup's LDS traffic without waiting
+// for its global stores.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
 template <typename QT, typename KVT, int D, int BS>
@@ -101,20 +109,40 @@ __global__ void __launch_bounds__(kThreads)
   __shared__ float sm_m[kWaves][16];
   __shared__ float sm_l[kWaves][16];
 
-  Work w;
-  if (!begin_work<QT, D>(p, BS, 16, w)) return;
-
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15;   // query head of the group (MFMA column) / V dim row
   const int g = lane >> 4;   // lane group: k-slot block / row block
   const int vtok = 8 * (g ^ 1);  // first of the 8 step tokens this lane's P / V operands hold
 
+  const char *kcache = reinterpret_cast<const char *>(p.key_cache);
+  const char *vcache = reinterpret_cast<const char *>(p.value_cache);
+  const size_t blk_stride = (size_t)p.num_kv_heads * TILE;
+
+  // One work item (a partition, or a whole v1 sequence, of one (sequence, KV
+  // head)) with the addressing its tile loads need.
+  struct Item {
+    Work w;
+    const_i32_ptr btab;
+    size_t head_off;
+    int tok_begin, n_steps;
+  };
+  auto make_item = [&](const Work &w) {
+    Item it;
+    it.w = w;
+    it.btab = as_const_table(p.block_tables + (size_t)w.seq * p.max_num_blocks_per_seq);
+    it.head_off = (size_t)w.kvh * TILE;
+    it.tok_begin = w.blk_begin * BS;
+    it.n_steps = ((w.blk_end - w.blk_begin) * BS + 31) / 32;
+    return it;
+  };
+
   // B operands of QK: 8 query values per lane and k-step, in the dim order
   // of the K chunks (16-bit: dims 32ks + 8g + e; fp8: chunk 4i + g of 16 dims,
   // halves ks = 2i and 2i + 1).
   u32x4 qop[NKS];
-  {
+  float slope2 = 0.0f;
+  auto load_query = [&](const Work &w) {
     const QT *q = reinterpret_cast<const QT *>(p.query) +
                   ((size_t)w.seq * p.num_heads + w.head0 + n) * D;
 #pragma unroll
@@ -122,58 +150,59 @@ __global__ void __launch_bounds__(kThreads)
       const int dim0 = kFp8 ? (16 * (4 * (ks / 2) + g) + 8 * (ks % 2)) : (32 * ks + 8 * g);
       qop[ks] = (n < w.nh) ? load16(q + dim0) : u32x4{0u, 0u, 0u, 0u};
     }
-  }
-  const float slope2 = (p.alibi_slopes && n < w.nh) ? p.alibi_slopes[w.head0 + n] * kLog2e : 0.0f;
+    slope2 = (p.alibi_slopes && n < w.nh) ? p.alibi_slopes[w.head0 + n] * kLog2e : 0.0f;
+  };
 
-  float m_run = -__builtin_inff(), l_run = 0.0f;
+  // Online-softmax state of the wave for the current item.
+  float m_run, l_run;
   f32x4 oacc[NDT];
+  bool poisoned;
+  auto reset_state = [&] {
+    m_run = -__builtin_inff();
+    l_run = 0.0f;
 #pragma unroll
-  for (int t = 0; t < NDT; ++t) oacc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-
-  const char *kcache = reinterpret_cast<const char *>(p.key_cache);
-  const char *vcache = reinterpret_cast<const char *>(p.value_cache);
-  const const_i32_ptr btab = as_const_table(p.block_tables + (size_t)w.seq * p.max_num_blocks_per_seq);
-  const size_t head_off = (size_t)w.kvh * TILE;
-  const size_t blk_stride = (size_t)p.num_kv_heads * TILE;
-  const int tok_begin = w.blk_begin * BS;
-  const int n_steps = ((w.blk_end - w.blk_begin) * BS + 31) / 32;
-  bool poisoned = false;
+    for (int t = 0; t < NDT; ++t) oacc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    poisoned = false;
+  };
 
   // K: sub-tile h, load i -> chunk 4i + g, token 16h + n of the step.
   // V: dim tile t -> dim 16t + n, tokens vtok .. vtok + 7 of the step.
+  // bad: a block-table entry of the step was out of range.
   using VOp = typename std::conditional<kFp8, u32x2, u32x4>::type;
   struct Tile {
     u32x4 k[2][NLK];
     VOp v[NDT];
+    bool bad;
   };
 
   // Out-of-range block-table entries are redirected to block 0 (always
-  // addressable) and reported through the poison flag; the second block of
-  // a step past the range end is read from block 0 too, and all its tokens
+  // addressable) and reported through the tile's bad flag; the second block
+  // of a step past the range end is read from block 0 too, and all its tokens
   // are masked.
   // The V operand's block differs between lane groups when two blocks make
   // a step; it is selected as an index and addressed from the cache base, so
   // the loads stay global (a per-lane select between two pointers compiles to
   // flat loads, whose completion order forces full waits on every step).
-  auto load_tile = [&](int step) {
+  auto load_tile = [&](const Item &it, int step) {
+    Tile tl;
+    tl.bad = false;
     int phys[BPS];
     const char *kb[BPS];
 #pragma unroll
     for (int b = 0; b < BPS; ++b) {
-      const int lb = w.blk_begin + step * BPS + b;
+      const int lb = it.w.blk_begin + step * BPS + b;
       phys[b] = 0;
-      if (lb < w.blk_end) {
-        phys[b] = btab[lb];
+      if (lb < it.w.blk_end) {
+        phys[b] = it.btab[lb];
         if (phys[b] < 0 || phys[b] >= p.num_blocks) {
-          poisoned = true;
+          tl.bad = true;
           phys[b] = 0;
         }
       }
-      kb[b] = kcache + (size_t)phys[b] * blk_stride + head_off;
+      kb[b] = kcache + (size_t)phys[b] * blk_stride + it.head_off;
     }
     const int vphys = (BPS == 1 || vtok < BS) ? phys[0] : phys[BPS - 1];
-    const char *vb = vcache + (size_t)vphys * blk_stride + head_off;
-    Tile tl;
+    const char *vb = vcache + (size_t)vphys * blk_stride + it.head_off;
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
@@ -190,7 +219,8 @@ __global__ void __launch_bounds__(kThreads)
     return tl;
   };
 
-  auto process = [&](int step, const Tile &tl) {
+  auto process = [&](const Item &it, int step, const Tile &tl) {
+    poisoned |= tl.bad;
     // S^T for each 16-token sub-tile: lane holds head n, tokens 16h + 4g + e.
     f32x4 st[2];
 #pragma unroll
@@ -213,7 +243,7 @@ __global__ void __launch_bounds__(kThreads)
       st[h] = c;
     }
     // Scale, ALiBi, mask, step max over the head's tokens.
-    const int t0 = tok_begin + 32 * step;
+    const int t0 = it.tok_begin + 32 * step;
     float x[2][4];
     float bm = -__builtin_inff();
 #pragma unroll
@@ -221,8 +251,8 @@ __global__ void __launch_bounds__(kThreads)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int t = t0 + 16 * h + 4 * g + e;
-        float v = st[h][e] * p.scale_log2 + slope2 * (float)(t - w.t_ref);
-        v = (t < w.L) ? v : -__builtin_inff();
+        float v = st[h][e] * p.scale_log2 + slope2 * (float)(t - it.w.t_ref);
+        v = (t < it.w.L) ? v : -__builtin_inff();
         x[h][e] = v;
         bm = fmaxf(bm, v);
       }
@@ -244,7 +274,7 @@ __global__ void __launch_bounds__(kThreads)
     }
     l_run = l_run * alpha + psum;
     const u32x4 pop = regroup_p(pk[0], pk[1]);
-    const int nv = w.L - (t0 + vtok);  // valid tokens among this lane's V operand
+    const int nv = it.w.L - (t0 + vtok);  // valid tokens among this lane's V operand
 #pragma unroll
     for (int t = 0; t < NDT; ++t) {
       u32x4 va;
@@ -259,47 +289,62 @@ __global__ void __launch_bounds__(kThreads)
     }
   };
 
-  // Two tiles ping-pong: while step st is consumed, the loads of the wave's
-  // next step (st + 4) are in flight.  The loop runs whole pairs and has no
-  // exit between them, and every load in it is always issued, so the wait
-  // before a step covers only that step's tile (a mid-pair exit would merge
-  // a path with the other tile still in flight into the back edge).  The
-  // scheduling barriers keep each prefetch ahead of the step's compute.
-  int st = wv;
-  int left = st < n_steps ? (n_steps - st + kWaves - 1) / kWaves : 0;  // this wave's steps
+  // The wave's steps of the item (wv, wv + 4, ...): two tiles ping-pong,
+  // and while step st is consumed the loads of the wave's next step are in
+  // flight.  The loop runs whole pairs and has no exit between them, and
+  // every load in it is always issued, so the wait before a step covers only
+  // that step's tile (a mid-pair exit would merge a path with the other tile
+  // still in flight into the back edge).  The scheduling barriers keep each
+  // prefetch ahead of the step's compute.  On entry ta is loading the wave's
+  // first step.
   Tile ta, tb;
-  if (left > 0) ta = load_tile(st);
-  while (left >= 3) {
-    tb = load_tile(st + kWaves);
-    __builtin_amdgcn_sched_barrier(0);
-    process(st, ta);
-    ta = load_tile(st + 2 * kWaves);
-    __builtin_amdgcn_sched_barrier(0);
-    process(st + kWaves, tb);
-    st += 2 * kWaves;
-    left -= 2;
-  }
-  if (left == 2) {
-    tb = load_tile(st + kWaves);
-    __builtin_amdgcn_sched_barrier(0);
-    process(st, ta);
-    process(st + kWaves, tb);
-  } else if (left == 1) {
-    process(st, ta);
-  }
+  auto run_steps = [&](const Item &it) {
+    int st = wv;
+    int left = st < it.n_steps ? (it.n_steps - st + kWaves - 1) / kWaves : 0;
+    while (left >= 3) {
+      tb = load_tile(it, st + kWaves);
+      __builtin_amdgcn_sched_barrier(0);
+      process(it, st, ta);
+      ta = load_tile(it, st + 2 * kWaves);
+      __builtin_amdgcn_sched_barrier(0);
+      process(it, st + kWaves, tb);
+      st += 2 * kWaves;
+      left -= 2;
+    }
+    if (left == 2) {
+      tb = load_tile(it, st + kWaves);
+      __builtin_amdgcn_sched_barrier(0);
+      process(it, st, ta);
+      process(it, st + kWaves, tb);
+    } else if (left == 1) {
+      process(it, st, ta);
+    }
+  };
 
-  // Wave totals: the four lanes of head n hold partial sums over their tokens.
-  const float l_tot = xor_sum<32>(xor_sum<16>(l_run));
+  // Cross-wave merge and stores of one item.  Wave totals: the four lanes of
+  // head n hold partial sums over their tokens.
+  auto finish_item = [&](const Item &it) {
+    const float l_tot = xor_sum<32>(xor_sum<16>(l_run));
 #pragma unroll
-  for (int t = 0; t < NDT; ++t)
+    for (int t = 0; t < NDT; ++t)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) sm_o[wv][n][16 * t + 4 * g + e] = oacc[t][e];
-  if (g == 0) {
-    sm_m[wv][n] = m_run;
-    sm_l[wv][n] = poisoned ? __builtin_nanf("") : l_tot;
-  }
-  __syncthreads();
-  finish_partition<QT, D, 16, OSTR>(p, w, sm_o, sm_m, sm_l);
+      for (int e = 0; e < 4; ++e) sm_o[wv][n][16 * t + 4 * g + e] = oacc[t][e];
+    if (g == 0) {
+      sm_m[wv][n] = m_run;
+      sm_l[wv][n] = poisoned ? __builtin_nanf("") : l_tot;
+    }
+    lds_barrier();
+    finish_partition<QT, D, 16, OSTR>(p, it.w, sm_o, sm_m, sm_l);
+  };
+
+  Work w;
+  if (!begin_work<QT, D>(p, BS, 16, w)) return;
+  const Item it = make_item(w);
+  load_query(w);
+  reset_state();
+  if (wv < it.n_steps) ta = load_tile(it, wv);
+  run_steps(it);
+  finish_item(it);
 }
 
 }  // namespace pa
