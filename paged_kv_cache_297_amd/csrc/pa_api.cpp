@@ -24,6 +24,7 @@ struct Tunables {
   int mfma_min_group = 5;     // query heads per KV head from which the MFMA kernel is used
   int small_batch_factor = 4; // AUTO: v2 for all if B * Hkv < factor * CUs
   int tile_factor = 2;        // AUTO: v2 iff Hkv * ceil(L/512) > factor * CUs
+  int parts_reversed = 1;     // all-v2 launches dispatch the last partition first
 };
 
 int env_int(const char *name, int fallback, int lo, int hi) {
@@ -41,6 +42,7 @@ const Tunables &tunables() {
     x.mfma_min_group = env_int("PA_MFMA_MIN_GROUP", x.mfma_min_group, 1, 1 << 20);
     x.small_batch_factor = env_int("PA_AUTO_SMALL_BATCH_FACTOR", x.small_batch_factor, 0, 1 << 20);
     x.tile_factor = env_int("PA_AUTO_TILE_FACTOR", x.tile_factor, 0, 1 << 20);
+    x.parts_reversed = env_int("PA_PARTS_REVERSED", x.parts_reversed, 0, 1);
     return x;
   }();
   return t;
@@ -197,6 +199,8 @@ Params make_params(const Call &c, int cu, int head_groups) {
   const long long b_hkv = (long long)c.num_seqs * c.num_kv_heads;
   p.auto_all_v2 = b_hkv < (long long)tunables().small_batch_factor * cu ? 1 : 0;
   p.auto_tile_limit = tunables().tile_factor * cu;
+  p.parts_reversed = tunables().parts_reversed &&
+                     (c.mode == PA_MODE_V2 || (c.mode == PA_MODE_AUTO && p.auto_all_v2)) ? 1 : 0;
   p.scale_log2 = c.scale * c.k_scale * 1.4426950408889634f;
   p.v_scale = c.v_scale;
   return p;

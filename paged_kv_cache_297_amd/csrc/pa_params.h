@@ -45,6 +45,7 @@ struct Params {
   int mode;             // Mode
   int auto_all_v2;      // AUTO: every sequence takes v2 (small batch clause)
   int auto_tile_limit;  // AUTO: v2 iff Hkv * ceil(L / 512) > auto_tile_limit
+  int parts_reversed;   // grid z walks the partitions from the last to the first
   float scale_log2;     // scale * k_scale * log2(e): logits are kept in log2 units
   float v_scale;
 };

@@ -4,10 +4,14 @@
 // Grid: x = KV head * head_groups + head group, y = sequence, z = partition
 // (v2) or 0 (v1).  Each workgroup owns one (sequence, KV head, query-head
 // group) and either one 512-token partition (v2) or the whole sequence (v1).
-// The partition is the slowest grid dimension, so workgroups are dispatched
-// partition 0 first: the long whole-sequence workgroups of a mixed v1/v2
-// launch start early instead of queueing behind the empty partition slots of
-// their sequence.
+// The partition is the slowest grid dimension.  A launch that mixes v1 and v2
+// dispatches partition 0 first, so its long whole-sequence workgroups start
+// early instead of queueing behind the empty partition slots of their
+// sequence.  A launch whose sequences all take v2 dispatches the last
+// partition first: the grid slices of high partitions, mostly empty slots of
+// the shorter sequences, pass while the device fills, and the launch ends on
+// partition 0, full for every sequence, instead of on a few long-sequence
+// workgroups that cannot keep HBM busy.
 #pragma once
 
 #include "pa_device.h"
@@ -91,11 +95,13 @@ __device__ __forceinline__ bool decode_work(const Params &p, int seq, int xslot,
   return true;
 }
 
-// Grid form: one item per workgroup, (x, y, z) = (slot, sequence, partition).
+// One item per workgroup: (x, y, z) = (slot, sequence, partition), the
+// partition counted from the last one when parts_reversed is set.
 template <typename QT, int D>
 __device__ __forceinline__ bool begin_work(const Params &p, int block_size, int group_slots,
                                           Work &w) {
-  return decode_work<QT, D>(p, blockIdx.y, blockIdx.x, blockIdx.z, block_size, group_slots, w);
+  const int part = p.parts_reversed ? (int)(gridDim.z - 1 - blockIdx.z) : (int)blockIdx.z;
+  return decode_work<QT, D>(p, blockIdx.y, blockIdx.x, part, block_size, group_slots, w);
 }
 
 // Cross-wave merge and stores.  Wave wv left, for query head h of the group:
