@@ -140,7 +140,9 @@ pa_status paged_attention_v2(
 /* Per-sequence choice between v1 and v2 (pa_should_use_v2, decided on the
  * device from seq_lens), same arguments as paged_attention_v2.  Sequences
  * sent down the v1 path get out only; their exp_sums / max_logits / tmp_out
- * rows are left as they were. */
+ * rows are left as they were.  When the rule sends every sequence to v1
+ * (it does at max_seq_len, and it is monotone in the length), the call runs
+ * as plain v1: one workgroup per (sequence, KV head), no reduce phase. */
 pa_status paged_attention_auto(
     void *out, float *exp_sums, float *max_logits, void *tmp_out,
     const void *query, const void *key_cache, const void *value_cache,
@@ -192,8 +194,8 @@ int pa_num_partitions(int max_seq_len);
  * dispatch page's should_use_paged_v2 ("ex_engine/factors/attn_dispatch.py":
  * tiles = num_kv_heads * ceil(seq_len / 512), v2 iff tiles > 2 * SM count)
  * re-sized to the GPU's compute units, plus one clause of ours for small
- * batches: v2 whenever num_seqs * num_kv_heads < 4 * cu_count, because v1
- * would then leave compute units idle.  Returns 1 for v2, 0 for v1. */
+ * batches: v2 whenever num_seqs * num_kv_heads < cu_count, because v1 would
+ * then leave compute units without a workgroup.  Returns 1 for v2, 0 for v1. */
 int pa_should_use_v2(int num_seqs, int num_kv_heads, int seq_len, int cu_count);
 
 /* Compute units of the current HIP device (cached per device); <= 0 and
@@ -205,8 +207,9 @@ pa_status pa_device_cu_count(int *cu_count);
  * reduce-phase kernel records reduce_start / reduce_stop (hipEvent_t handles
  * created by the caller), through hipExtLaunchKernelGGL: the events carry the
  * kernel's own start and end times, with no queue marker in between.  A
- * NULL pair switches its phase back to plain launches.  The events are
- * re-recorded by every call until replaced.  A pair with one NULL member
+ * NULL pair switches its phase back to plain launches.  A reduce phase with
+ * nothing to merge (an all-v1 auto call) records its pair back to back.  The
+ * events are re-recorded by every call until replaced.  A pair with one NULL member
  * returns PA_ERR_NULL_POINTER and changes nothing. */
 pa_status pa_set_timing_events(void *partition_start, void *partition_stop, void *reduce_start,
                                void *reduce_stop);

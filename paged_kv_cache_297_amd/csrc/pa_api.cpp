@@ -22,7 +22,7 @@ using pa::Params;
 // ---------------------------------------------------------------------------
 struct Tunables {
   int mfma_min_group = 5;     // query heads per KV head from which the MFMA kernel is used
-  int small_batch_factor = 4; // AUTO: v2 for all if B * Hkv < factor * CUs
+  int small_batch_factor = 1; // AUTO: v2 for all if B * Hkv < factor * CUs
   int tile_factor = 2;        // AUTO: v2 iff Hkv * ceil(L/512) > factor * CUs
   int parts_reversed = 1;     // all-v2 launches dispatch the last partition first
 };
@@ -206,19 +206,31 @@ Params make_params(const Call &c, int cu, int head_groups) {
   return p;
 }
 
+// AUTO launches in which every sequence takes v1: the rule is monotone in the
+// length, so v1 at max_seq_len means v1 for every valid length (an invalid
+// length also takes the v1 path).  Such a launch runs as plain v1: one grid
+// slice instead of one per partition, and no reduce.
+bool auto_all_v1(const Call &c, int cu) {
+  if (c.mode != PA_MODE_AUTO) return false;
+  const Tunables &t = tunables();
+  if ((long long)c.num_seqs * c.num_kv_heads < (long long)t.small_batch_factor * cu) return false;
+  return (long long)c.num_kv_heads * pa_num_partitions(c.max_seq_len) <= (long long)t.tile_factor * cu;
+}
+
 pa_status run_partition(const Call &c) {
   pa_status st = validate_common(c, true);
   if (st != PA_OK) return st;
   const Plan pl = make_plan(c);
   const long long grid_x = (long long)c.num_kv_heads * pl.head_groups;
-  const int gz = c.mode == PA_MODE_V1 ? 1 : pa_num_partitions(c.max_seq_len);
-  if (grid_x > 0x7fffffffLL || gz > kMaxGridYZ) return PA_ERR_BAD_SHAPE;
+  if (grid_x > 0x7fffffffLL || pa_num_partitions(c.max_seq_len) > kMaxGridYZ)
+    return PA_ERR_BAD_SHAPE;
   if (c.num_seqs == 0) return PA_OK;
   int cu = 0;
   if (c.mode == PA_MODE_AUTO) {
     st = cu_count_current(&cu);
     if (st != PA_OK) return st;
   }
+  const int gz = (c.mode == PA_MODE_V1 || auto_all_v1(c, cu)) ? 1 : pa_num_partitions(c.max_seq_len);
   const Params p = make_params(c, cu, pl.head_groups);
   const pa::Launch l{dim3((unsigned)grid_x, c.num_seqs, gz), c.stream, t_events.partition_start,
                      t_events.partition_stop};
@@ -247,6 +259,14 @@ pa_status run_reduce(const Call &c) {
   if (c.mode == PA_MODE_AUTO) {
     st = cu_count_current(&cu);
     if (st != PA_OK) return st;
+  }
+  if (auto_all_v1(c, cu)) {
+    // Nothing to merge.  The profiling events still mark an (empty) phase.
+    if (t_events.reduce_start && t_events.reduce_stop &&
+        (hipEventRecord(t_events.reduce_start, c.stream) != hipSuccess ||
+         hipEventRecord(t_events.reduce_stop, c.stream) != hipSuccess))
+      return PA_ERR_HIP;
+    return PA_OK;
   }
   const Params p = make_params(c, cu, 1);
   const pa::Launch l{dim3(c.num_heads, c.num_seqs, 1), c.stream, t_events.reduce_start,

@@ -59,7 +59,7 @@ def test_helpers():
 
 
 def test_dispatch_rule_matches_page_rule_when_batch_is_large():
-    """With the small-batch clause off (B * Hkv >= 4 * CUs), the host rule is
+    """With the small-batch clause off (B * Hkv >= CUs), the host rule is
     the dispatch page's should_use_paged_v2 with SMs -> compute units."""
     lib = B.load_library()
     for cu in (16, 80, 256):
@@ -72,7 +72,11 @@ def test_dispatch_rule_matches_page_rule_when_batch_is_large():
 
 def test_dispatch_small_batch_clause():
     lib = B.load_library()
-    assert lib.pa_should_use_v2(4, 8, 1, 256) == 1          # 32 < 1024: always v2
+    assert lib.pa_should_use_v2(4, 8, 1, 256) == 1          # 32 < 256: always v2
+    assert lib.pa_should_use_v2(31, 8, 1, 256) == 1         # 248 < 256 (boundary)
+    assert lib.pa_should_use_v2(32, 8, 1, 256) == 0         # 256 workgroups fill the CUs
+    assert lib.pa_should_use_v2(32, 8, 32768, 256) == 0     # 8 * 64 = 512 tiles: not > 512
+    assert lib.pa_should_use_v2(32, 8, 32769, 256) == 1     # 8 * 65 > 512
     assert lib.pa_should_use_v2(256, 32, 2048, 256) == 0    # large batch, short: v1
     assert lib.pa_should_use_v2(256, 32, 16385, 256) == 1   # 32 * 33 > 512
 

@@ -167,3 +167,23 @@ def test_timing_events_hook_records_kernel_times():
     assert ev[1].elapsed_time(ev[2]) >= 0.0   # reduce starts after the partition kernel ends
     with pytest.raises(B.PagedAttentionError):
         B.set_timing_events(ev[0].cuda_event, None)
+
+
+def test_auto_all_v1_runs_as_plain_v1():
+    """An auto call whose rule gives v1 for every sequence (B * Hkv >= CUs,
+    short sequences) is bitwise the v1 result and leaves the partial buffers
+    as they were (the NaN the helper fills them with)."""
+    cu = B.device_cu_count()
+    hkv = 4
+    n = (cu + hkv - 1) // hkv
+    lens = [300 + 97 * s for s in range(n)]
+    wl = W.make_workload(2, lens=lens)
+    assert not any(H.uses_v2(wl, s) for s in range(n))
+    a = H.run(wl, "auto")
+    b = H.run(wl, "v1")
+    assert np.array_equal(a["out"], b["out"])
+    for k in ("exp_sums", "max_logits", "tmp_out"):
+        assert np.isnan(a[k]).all(), k
+    some = [0, n // 2, n - 1]
+    ref = H.oracle(wl, some)
+    H.check_close(a["out"][some], ref["out_v1"][some], H.TOL[wl.kv_kind], "auto all-v1")
