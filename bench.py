@@ -85,14 +85,17 @@ def algorithmic_bytes(wl, path: str, cu: int, B) -> dict:
             "any_v2": bool(v2.any())}
 
 
-def read_traffic(workload_name: str, src_hash: str):
+def read_traffic(workload_name: str, src_hash: str, call_path: str):
     """HBM bytes per partition launch from the committed counter summary, if
-    it was measured on the current kernel sources."""
+    it was measured on the current kernel sources with the same path."""
     path = os.path.join(PROFILES, f"traffic_pa_partition_{workload_name}.md")
     if not os.path.exists(path):
         return None
     vals = {}
     with open(path) as f:
+        header = f.readline()
+        if f"path={call_path}" not in header:
+            return None
         for line in f:
             if line.startswith("- ") and ":" in line:
                 k, v = line[2:].split(":", 1)
@@ -258,7 +261,7 @@ def main() -> int:
     part_avg = float(part_ms.mean())
     achieved = ab["partition"] / (part_avg * 1e-3) / 1e9
     src_hash = kernel_source_hash()
-    traffic = read_traffic(base.name, src_hash) if copies > 1 else None
+    traffic = read_traffic(base.name, src_hash, args.path) if copies > 1 else None
     dtype = {torch.float32: "f32", torch.float16: "f16", torch.bfloat16: "bf16"}[base.dtype]
     if base.kv_cache_dtype == "fp8_e4m3":
         dtype = f"{dtype} (fp8 e4m3 KV)"
@@ -301,6 +304,8 @@ def main() -> int:
             "avg_launch_ms": round(part_avg, 5),
             "reduce_avg_launch_ms": round(float(red_ms.mean()), 5),
             "event_step_ms_median": round(float(np.median(step_ms)), 5),
+            "event_step_us_p10_p50_p90": [round(float(np.percentile(step_ms, q)) * 1e3, 2)
+                                          for q in (10, 50, 90)],
             "kernel_source_hash": src_hash,
         },
     }
