@@ -44,6 +44,15 @@ Readings where the pages are silent, ambiguous or contradict themselves
 * The attention weights are NOT rounded to the V dtype before the weighted
   sum (the page's ``.to(v_part.dtype)``): this oracle is exact fp64; the GPU's
   rounding of P is covered by the stated tolerances.
+* Sliding window and logit soft cap (the dispatch page's decode configuration
+  fields ``window_left`` / ``softcap``, which the pages pass on but do not
+  define; the Neuron page hands the same pair to ``flash_attn_varlen_func`` as
+  ``window_size`` / ``softcap``, whose meaning is taken): with window_left
+  W >= 0 the decode query (position L - 1) sees the keys t >= L - 1 - W only
+  (W = -1: no window; a right window is moot for the last token); with
+  soft cap c > 0 each scaled logit s becomes c * tanh(s / c), before the ALiBi
+  bias is added.  Partitions with no visible key hold -inf, 0, 0 like the
+  padding partitions.
 
 Every function works on NumPy arrays; floating point is float64 throughout.
 """
@@ -154,13 +163,18 @@ def gather_sequence(key_cache: np.ndarray, value_cache: np.ndarray,
 # --------------------------------------------------------------------------
 
 def sequence_logits(q: np.ndarray, k: np.ndarray, scale: float,
-                    alibi_slopes: Optional[np.ndarray]) -> np.ndarray:
+                    alibi_slopes: Optional[np.ndarray], window_left: int = -1,
+                    soft_cap: float = 0.0) -> np.ndarray:
     """Scaled logits s[h, t] for one sequence.
 
     q [H, D] float64, k [L, Hkv, D] float64.  Query head h reads KV head
     h // (H / Hkv) (V2 page, GQA expansion by repeat_interleave).
     s[h, t] = scale * sum_d q[h, d] k[t, kv(h), d]  +  slope[h] * t
     (V2 page, Phase 1: scores, then the ALiBi bias with absolute positions).
+    With soft_cap c > 0 the scaled dot product is replaced by c * tanh(. / c)
+    before the bias; with window_left W >= 0 the keys t < L - 1 - W get -inf
+    (the decode configuration fields of the dispatch page, read as described
+    in the module docstring).
     """
     num_heads = q.shape[0]
     seq_len, hkv, _ = k.shape
@@ -168,9 +182,13 @@ def sequence_logits(q: np.ndarray, k: np.ndarray, scale: float,
     s = np.empty((num_heads, seq_len))
     for h in range(num_heads):
         s[h] = (k[:, h // group, :] @ q[h]) * scale
+    if soft_cap > 0.0:
+        s = soft_cap * np.tanh(s / soft_cap)
     if alibi_slopes is not None:
         positions = np.arange(seq_len, dtype=np.float64)
         s = s + np.asarray(alibi_slopes, dtype=np.float64)[:, None] * positions[None, :]
+    if window_left >= 0:
+        s[:, :max(0, seq_len - 1 - window_left)] = -np.inf
     return s
 
 
@@ -199,7 +217,9 @@ def partition_partials(s: np.ndarray, v: np.ndarray, max_num_partitions: int,
       m_p = max_{t in T_p} s[h, t]                      (max_logits)
       S_p = sum_{t in T_p} exp(s[h, t] - m_p)           (exp_sums)
       O_p = sum_{t in T_p} exp(s[h, t] - m_p) v_t / S_p  (tmp_output, normalised)
-    Partitions P_s <= p < max_num_partitions are padding: -inf, 0, 0.
+    Partitions P_s <= p < max_num_partitions are padding: -inf, 0, 0; so is a
+    partition in which no key is visible (all its logits -inf: before a
+    sliding window).
     Returns (max_logits [H, P], exp_sums [H, P], tmp_out [H, P, D]).
     """
     num_heads, seq_len = s.shape
@@ -214,6 +234,8 @@ def partition_partials(s: np.ndarray, v: np.ndarray, max_num_partitions: int,
         end = min(start + partition_size, seq_len)
         sp = s[:, start:end]
         m_p = sp.max(axis=1)
+        if np.all(np.isneginf(m_p)):
+            continue
         e = np.exp(sp - m_p[:, None])
         s_p = e.sum(axis=1)
         max_logits[:, p] = m_p
@@ -249,13 +271,14 @@ def paged_attention(query_raw: np.ndarray, key_cache_raw: np.ndarray,
                     max_num_partitions: Optional[int] = None,
                     partition_size: int = PARTITION_SIZE,
                     seqs: Optional[list] = None,
-                    check_merge: bool = True) -> Dict[str, np.ndarray]:
+                    check_merge: bool = True, window_left: int = -1,
+                    soft_cap: float = 0.0) -> Dict[str, np.ndarray]:
     """Reference v1 output and v2 partials/merged output for a decode batch.
 
     query_raw [B, H, D] and the caches are raw storage (see decode_storage);
     block_tables int32 [B, max_blocks_per_seq]; seq_lens int [B].
     ``seqs`` restricts the work to those batch rows (others stay zero /
-    padding).  Returns a dict of float64 arrays:
+    padding).  ``window_left`` / ``soft_cap``: see sequence_logits.  Returns a dict of float64 arrays:
       out_v1 [B, H, D], out_v2 [B, H, D], max_logits [B, H, P],
       exp_sums [B, H, P], tmp_out [B, H, P, D].
     With ``check_merge`` the merged v2 output is asserted equal to the
@@ -283,7 +306,7 @@ def paged_attention(query_raw: np.ndarray, key_cache_raw: np.ndarray,
         k_pool = decode_storage(key_cache_raw[phys], kv_kind) * k_scale
         v_pool = decode_storage(value_cache_raw[phys], kv_kind) * v_scale
         k, v = gather_sequence(k_pool, v_pool, np.arange(n_logical), seq_len, block_size)
-        s = sequence_logits(q_all[b], k, scale, alibi_slopes)
+        s = sequence_logits(q_all[b], k, scale, alibi_slopes, window_left, soft_cap)
         out_v1[b] = softmax_output(s, v)
         ml, es, to = partition_partials(s, v, max_num_partitions, partition_size)
         max_logits[b], exp_sums[b], tmp_out[b] = ml, es, to

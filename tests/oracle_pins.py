@@ -87,13 +87,17 @@ def pack_paged(k_dense_raw, v_dense_raw, lens, block_size, x, pool_blocks, rng,
     return kc, vc, tables
 
 
-def dense_attention(q, k, v, scale, slopes=None):
-    """softmax(scale * q K^T + slope * t) V on contiguous K/V [L, Hkv, D]."""
+def dense_attention(q, k, v, scale, slopes=None, cap=0.0):
+    """softmax(scale * q K^T + slope * t) V on contiguous K/V [L, Hkv, D];
+    with cap > 0 the scaled dot products pass through cap * tanh(. / cap)
+    first (that formula itself is pinned by pin_soft_cap_forms)."""
     num_heads = q.shape[0]
     group = num_heads // k.shape[1]
     out = np.empty((num_heads, v.shape[2]))
     for h in range(num_heads):
         logits = scale * (k[:, h // group, :] @ q[h])
+        if cap > 0.0:
+            logits = cap * np.tanh(logits / cap)
         if slopes is not None:
             logits = logits + slopes[h] * np.arange(k.shape[0])
         out[h] = scipy.special.softmax(logits) @ v[:, h // group, :]
@@ -393,6 +397,102 @@ def pin_partition_count_golden():
         assert O.num_partitions(int(seq_len)) == int(parts), (seq_len, parts)
 
 
+def pin_sliding_window(lens=(1, 16, 17, 600, 1100), hkv=2, group=3, head_size=64,
+                       block_size=16, kv_kind="bf16", alibi=True, cap=0.0, seed=11):
+    """Sliding window W: the oracle on the paged layout equals dense attention
+    over the last W + 1 keys of the contiguous K/V (a window is a contiguous
+    key range; ALiBi's absolute offset cancels in the softmax); W = 0 returns
+    the last value row; W >= L - 1 and W = -1 give exactly the unwindowed
+    result; partitions with no visible key are padding (-inf, 0, 0) and the
+    visible ones hold the log-sum-exp statistics of their visible keys."""
+    case = build_case(list(lens), hkv, group, head_size, block_size, kv_kind, seed=seed)
+    num_heads = hkv * group
+    scale = 1.0 / math.sqrt(head_size)
+    slopes = (np.array([2.0 ** (-8.0 * (h + 1) / num_heads) for h in range(num_heads)])
+              if alibi else None)
+    full = run_oracle(case, scale, slopes, soft_cap=cap)
+    for w in (0, 1, 15, 16, 17, 100, 511, 512, 513, 1099, 5000):
+        res = run_oracle(case, scale, slopes, window_left=w, soft_cap=cap)
+        for b, L in enumerate(lens):
+            lo = max(0, L - 1 - w)
+            q = case["q"][b]
+            ref = dense_attention(q, case["k"][b][lo:], case["v"][b][lo:], scale,
+                                  None if slopes is None else slopes, cap=cap)
+            _close(res["out_v1"][b], ref, 1e-12, f"window {w} L {L} v1")
+            _close(res["out_v2"][b], ref, 1e-12, f"window {w} L {L} v2")
+            if w == 0:
+                group_of = np.arange(num_heads) // group
+                _close(res["out_v1"][b], case["v"][b][L - 1][group_of], 1e-12, "window 0")
+            if w >= L - 1:
+                for key in ("out_v1", "out_v2", "max_logits", "exp_sums", "tmp_out"):
+                    assert np.array_equal(res[key][b], full[key][b]), (key, w, L)
+            # statistics per partition over the visible keys only
+            logits = dense_logits(q, case["k"][b], scale, slopes)
+            if cap > 0.0:
+                raw = dense_logits(q, case["k"][b], scale, None)
+                logits = logits - raw + cap * np.tanh(raw / cap)
+            for p in range(O.num_partitions(L)):
+                a, e = p * 512, min((p + 1) * 512, L)
+                vis = logits[:, max(a, lo):e]
+                if vis.shape[1] == 0:
+                    assert np.all(np.isneginf(res["max_logits"][b, :, p]))
+                    assert np.all(res["exp_sums"][b, :, p] == 0.0)
+                    assert np.all(res["tmp_out"][b, :, p] == 0.0)
+                else:
+                    _close(res["max_logits"][b, :, p], vis.max(axis=1), 1e-12, "window max")
+                    _close(np.log(res["exp_sums"][b, :, p]) + res["max_logits"][b, :, p],
+                           scipy.special.logsumexp(vis, axis=1), 1e-12, "window logsumexp")
+    # W = -1 is no window at all
+    none = run_oracle(case, scale, slopes, window_left=-1, soft_cap=cap)
+    for key in ("out_v1", "max_logits", "exp_sums"):
+        assert np.array_equal(none[key], full[key]), key
+
+
+def pin_soft_cap_forms():
+    """The soft cap c * tanh(s / c) on the scaled logits, before ALiBi:
+    small logits follow the series s - s^3 / (3 c^2) (placement of c and of
+    the scale); large logits stay inside (-c, c) with their order kept; the
+    ALiBi bias is added after the cap (logits minus the bias lie in (-c, c)
+    even with steep slopes); a huge cap changes nothing; q = 0 still gives
+    the plain mean of V."""
+    case = build_case([40], 1, 2, 64, 16, "f32", seed=21)
+    q, k = case["q"][0], case["k"][0]
+    scale = 1.0 / 8.0
+    # series regime: scale the query down so |s| <= ~2e-3
+    small = O.sequence_logits(q * 1e-3, k, scale, None, -1, 0.5)
+    s = dense_logits(q * 1e-3, k, scale)
+    assert np.abs(s).max() < 5e-3
+    _close(small, s - s ** 3 / (3 * 0.5 ** 2), 1e-11, "soft cap series")
+    # saturation regime
+    big = O.sequence_logits(q * 50.0, k, scale, None, -1, 2.0)
+    sb = dense_logits(q * 50.0, k, scale)
+    assert np.all(np.abs(big) <= 2.0)      # tanh saturates to exactly 1 in fp64
+    assert np.abs(sb).max() > 20.0 and np.abs(big).max() > 1.99
+    for h in range(big.shape[0]):
+        assert np.all(np.diff(big[h][np.argsort(sb[h])]) >= 0.0), "the cap must keep the order"
+    # ALiBi after the cap
+    slopes = np.array([3.0, 5.0])
+    with_bias = O.sequence_logits(q, k, scale, slopes, -1, 1.0)
+    unbiased = with_bias - slopes[:, None] * np.arange(k.shape[0])[None, :]
+    assert np.all(np.abs(unbiased) <= 1.0)
+    # a huge cap is no cap
+    _close(O.sequence_logits(q, k, scale, slopes, -1, 1e9), O.sequence_logits(q, k, scale, slopes),
+           1e-12, "huge cap")
+    # q = 0: every logit is 0 -> the mean of V
+    case0 = build_case([300], 1, 1, 64, 16, "f32", seed=22)
+    case0["q_raw"] = np.zeros_like(case0["q_raw"])
+    res = run_oracle(case0, 0.125, soft_cap=3.0)
+    _close(res["out_v1"][0, 0], case0["v"][0][:, 0, :].mean(axis=0), 1e-12, "cap q=0 mean")
+
+
+def pin_window_and_cap_brute_force():
+    """Window and soft cap together on every storage kind: paged oracle ==
+    dense attention over the visible keys."""
+    for kind, bs, group in (("fp8_e4m3", 32, 8), ("f16", 16, 4), ("f32", 16, 1)):
+        pin_sliding_window(lens=(33, 700), hkv=1, group=group, head_size=128 if kind == "fp8_e4m3" else 64,
+                           block_size=bs, kv_kind=kind, alibi=kind != "f16", cap=20.0, seed=31)
+
+
 BRUTE_FORCE_SMALL = [
     # lens, hkv, group, D, bs, kind, alibi, k_scale, v_scale
     ([1, 15, 16, 17], 1, 1, 64, 16, "f32", False, 1.0, 1.0),
@@ -418,5 +518,8 @@ def run_all_pins():
     pin_block_table_permutation()
     pin_convexity_and_dominant_key()
     pin_empty_sequence()
+    pin_sliding_window()
+    pin_sliding_window(lens=(513, 1100), alibi=False, cap=5.0)
+    pin_soft_cap_forms()
     pin_dispatch_golden()
     pin_partition_count_golden()

@@ -40,37 +40,97 @@ def _gather_slot_off_by_one(key_cache, value_cache, row, seq_len, bs):
     return np.roll(k, -1, axis=0), np.roll(v, -1, axis=0)
 
 
-def _logits_gqa_modulo(q, k, scale, slopes):
-    nh = q.shape[0]
-    hkv = k.shape[1]
-    s = np.stack([(k[:, h % hkv, :] @ q[h]) * scale for h in range(nh)])
-    if slopes is not None:
-        s = s + np.asarray(slopes)[:, None] * np.arange(k.shape[0])[None, :]
+def _window(s, window_left):
+    if window_left >= 0:
+        s[:, :max(0, s.shape[1] - 1 - window_left)] = -np.inf
     return s
 
 
-def _logits_alibi_relative(q, k, scale, slopes):
-    s = O.__dict__["_orig_logits"](q, k, scale, None)
+def _logits_gqa_modulo(q, k, scale, slopes, window_left=-1, soft_cap=0.0):
+    nh = q.shape[0]
+    hkv = k.shape[1]
+    s = np.stack([(k[:, h % hkv, :] @ q[h]) * scale for h in range(nh)])
+    if soft_cap > 0.0:
+        s = soft_cap * np.tanh(s / soft_cap)
+    if slopes is not None:
+        s = s + np.asarray(slopes)[:, None] * np.arange(k.shape[0])[None, :]
+    return _window(s, window_left)
+
+
+def _logits_alibi_relative(q, k, scale, slopes, window_left=-1, soft_cap=0.0):
+    s = O.__dict__["_orig_logits"](q, k, scale, None, window_left, soft_cap)
     if slopes is not None:
         L = k.shape[0]
         s = s + np.asarray(slopes)[:, None] * (np.arange(L) - (L - 1))[None, :]
     return s
 
 
-def _logits_alibi_scaled(q, k, scale, slopes):
-    s = O.__dict__["_orig_logits"](q, k, 1.0, slopes)
+def _logits_alibi_scaled(q, k, scale, slopes, window_left=-1, soft_cap=0.0):
+    s = O.__dict__["_orig_logits"](q, k, 1.0, slopes, window_left, soft_cap)
     return s * scale
 
 
-def _logits_no_scale(q, k, scale, slopes):
-    return O.__dict__["_orig_logits"](q, k, 1.0, slopes)
+def _logits_no_scale(q, k, scale, slopes, window_left=-1, soft_cap=0.0):
+    return O.__dict__["_orig_logits"](q, k, 1.0, slopes, window_left, soft_cap)
 
 
-def _logits_alibi_sign(q, k, scale, slopes):
-    s = O.__dict__["_orig_logits"](q, k, scale, None)
+def _logits_alibi_sign(q, k, scale, slopes, window_left=-1, soft_cap=0.0):
+    s = O.__dict__["_orig_logits"](q, k, scale, None, window_left, soft_cap)
     if slopes is not None:
         s = s - np.asarray(slopes)[:, None] * np.arange(k.shape[0])[None, :]
     return s
+
+
+def _logits_window_off_by_one(q, k, scale, slopes, window_left=-1, soft_cap=0.0):
+    # one key fewer: t >= L - W instead of t >= L - 1 - W
+    s = O.__dict__["_orig_logits"](q, k, scale, slopes, -1, soft_cap)
+    if window_left >= 0:
+        s[:, :max(0, k.shape[0] - window_left)] = -np.inf
+    return s
+
+
+def _logits_window_from_start(q, k, scale, slopes, window_left=-1, soft_cap=0.0):
+    # window anchored at the first key instead of the query position
+    s = O.__dict__["_orig_logits"](q, k, scale, slopes, -1, soft_cap)
+    if window_left >= 0:
+        s[:, window_left + 1:] = -np.inf
+    return s
+
+
+def _logits_cap_after_alibi(q, k, scale, slopes, window_left=-1, soft_cap=0.0):
+    s = O.__dict__["_orig_logits"](q, k, scale, slopes, -1, 0.0)
+    if soft_cap > 0.0:
+        s = soft_cap * np.tanh(s / soft_cap)
+    return _window(s, window_left)
+
+
+def _logits_cap_inside_unscaled(q, k, scale, slopes, window_left=-1, soft_cap=0.0):
+    # c * tanh(s) instead of c * tanh(s / c)
+    s = O.__dict__["_orig_logits"](q, k, scale, None, -1, 0.0)
+    if soft_cap > 0.0:
+        s = soft_cap * np.tanh(s)
+    if slopes is not None:
+        s = s + np.asarray(slopes)[:, None] * np.arange(k.shape[0])[None, :]
+    return _window(s, window_left)
+
+
+def _logits_cap_ignored(q, k, scale, slopes, window_left=-1, soft_cap=0.0):
+    return O.__dict__["_orig_logits"](q, k, scale, slopes, window_left, 0.0)
+
+
+def _logits_window_ignored(q, k, scale, slopes, window_left=-1, soft_cap=0.0):
+    return O.__dict__["_orig_logits"](q, k, scale, slopes, -1, soft_cap)
+
+
+def _partials_masked_partition_zero_max(s, v, max_p, ps=O.PARTITION_SIZE):
+    # a partition with no visible key reported with max 0 / sum 1 (as if it held one token)
+    ml, es, to = O.__dict__["_orig_partials"](s, v, max_p, ps)
+    L = s.shape[1]
+    n = O.num_partitions(L, ps)
+    dead = np.isneginf(ml[:, :n]) & (es[:, :n] == 0)
+    ml[:, :n] = np.where(dead, 0.0, ml[:, :n])
+    es[:, :n] = np.where(dead, 1.0, es[:, :n])
+    return ml, es, to
 
 
 def _partials_unnormalised(s, v, max_p, ps=O.PARTITION_SIZE):
@@ -140,6 +200,13 @@ MUTATIONS = {
     "softmax_max_over_heads": ("softmax_output", _softmax_wrong_axis_max),
     "partition_count_floor": ("num_partitions", _num_partitions_floor),
     "bf16_decode_low_half": ("decode_storage", _decode_bf16_low),
+    "window_off_by_one": ("sequence_logits", _logits_window_off_by_one),
+    "window_from_first_key": ("sequence_logits", _logits_window_from_start),
+    "window_ignored": ("sequence_logits", _logits_window_ignored),
+    "soft_cap_after_alibi": ("sequence_logits", _logits_cap_after_alibi),
+    "soft_cap_without_inner_division": ("sequence_logits", _logits_cap_inside_unscaled),
+    "soft_cap_ignored": ("sequence_logits", _logits_cap_ignored),
+    "masked_partition_not_padding": ("partition_partials", _partials_masked_partition_zero_max),
 }
 
 

@@ -84,3 +84,19 @@ def test_dispatch_golden():
 
 def test_partition_count_golden():
     P.pin_partition_count_golden()
+
+
+def test_sliding_window():
+    P.pin_sliding_window()
+
+
+def test_sliding_window_with_soft_cap():
+    P.pin_sliding_window(lens=(513, 1100), alibi=False, cap=5.0)
+
+
+def test_soft_cap_forms():
+    P.pin_soft_cap_forms()
+
+
+def test_window_and_cap_every_kind():
+    P.pin_window_and_cap_brute_force()
