@@ -106,6 +106,32 @@ typedef enum pa_kv_cache_dtype { PA_KV_AUTO = 0, PA_KV_FP8_E4M3 = 1 } pa_kv_cach
  * device, with the rule of pa_should_use_v2. */
 typedef enum pa_mode { PA_MODE_V1 = 0, PA_MODE_V2 = 1, PA_MODE_AUTO = 2 } pa_mode;
 
+/* Decode options of the *_ex entry points: the sliding window and the logit
+ * soft cap of the dispatch page's decode configuration (AttnDispatchConfig
+ * fields window_left and softcap, -1 and 0 meaning off), which the Neuron
+ * page hands to a flash-attention call as window_size / softcap.  The pages
+ * pass them on without defining them; the meaning taken is that call's:
+ *
+ *   window_left = W >= 0: the decode query, at position L - 1, attends to
+ *     the keys t with L - 1 - W <= t <= L - 1 only (the last W + 1 tokens;
+ *     W = 0 keeps the last token alone).  W = -1: every key.  A right window
+ *     is moot for the last token and has no field.
+ *   logits_soft_cap = c > 0: each scaled logit scale * k_scale * q.K becomes
+ *     c * tanh(logit / c) before the ALiBi bias is added.  c = 0: off.
+ *
+ * Keys outside the window are neither weighted nor read when their whole
+ * block lies outside it (their block-table entries may be stale).  In v2, a
+ * partition with no key inside the window gets max_logits = -inf and
+ * exp_sums = 0 (as the V2 page's unused partitions) and no tmp_out row;
+ * the auto rule (pa_should_use_v2) is applied to the window-clipped length
+ * min(L, W + 1).  A NULL options pointer means both off: the *_ex call is then
+ * the plain call.  window_left < -1, or a cap that is negative, infinite or
+ * NaN, returns PA_ERR_BAD_ARGUMENT. */
+typedef struct pa_decode_options {
+  int window_left;
+  float logits_soft_cap;
+} pa_decode_options;
+
 /* ---------------------------------------------------------------------- */
 /* Full calls                                                             */
 /* ---------------------------------------------------------------------- */
@@ -181,6 +207,56 @@ pa_status paged_attention_reduce(
     void *stream);
 
 /* ---------------------------------------------------------------------- */
+/* The same calls with decode options (sliding window, logit soft cap; see */
+/* pa_decode_options).  Every other argument and every error is that of   */
+/* the call without the suffix, which equals the *_ex call with NULL.     */
+/* The two phases of one v2 / auto computation must be given the same     */
+/* options: the reduce skips the partitions before the window.           */
+/* ---------------------------------------------------------------------- */
+
+pa_status paged_attention_v1_ex(
+    void *out, const void *query, const void *key_cache, const void *value_cache,
+    int num_seqs, int num_heads, int num_kv_heads, int head_size, float scale,
+    const int32_t *block_tables, int max_num_blocks_per_seq, const int32_t *seq_lens,
+    int num_blocks, int block_size, int max_seq_len, const float *alibi_slopes,
+    pa_dtype dtype, pa_kv_cache_dtype kv_cache_dtype, float k_scale, float v_scale,
+    const pa_decode_options *options, void *stream);
+
+pa_status paged_attention_v2_ex(
+    void *out, float *exp_sums, float *max_logits, void *tmp_out,
+    const void *query, const void *key_cache, const void *value_cache,
+    int num_seqs, int num_heads, int num_kv_heads, int head_size, float scale,
+    const int32_t *block_tables, int max_num_blocks_per_seq, const int32_t *seq_lens,
+    int num_blocks, int block_size, int max_seq_len, int max_num_partitions,
+    const float *alibi_slopes, pa_dtype dtype, pa_kv_cache_dtype kv_cache_dtype,
+    float k_scale, float v_scale, const pa_decode_options *options, void *stream);
+
+pa_status paged_attention_auto_ex(
+    void *out, float *exp_sums, float *max_logits, void *tmp_out,
+    const void *query, const void *key_cache, const void *value_cache,
+    int num_seqs, int num_heads, int num_kv_heads, int head_size, float scale,
+    const int32_t *block_tables, int max_num_blocks_per_seq, const int32_t *seq_lens,
+    int num_blocks, int block_size, int max_seq_len, int max_num_partitions,
+    const float *alibi_slopes, pa_dtype dtype, pa_kv_cache_dtype kv_cache_dtype,
+    float k_scale, float v_scale, const pa_decode_options *options, void *stream);
+
+pa_status paged_attention_partition_ex(
+    pa_mode mode, void *out, float *exp_sums, float *max_logits, void *tmp_out,
+    const void *query, const void *key_cache, const void *value_cache,
+    int num_seqs, int num_heads, int num_kv_heads, int head_size, float scale,
+    const int32_t *block_tables, int max_num_blocks_per_seq, const int32_t *seq_lens,
+    int num_blocks, int block_size, int max_seq_len, int max_num_partitions,
+    const float *alibi_slopes, pa_dtype dtype, pa_kv_cache_dtype kv_cache_dtype,
+    float k_scale, float v_scale, const pa_decode_options *options, void *stream);
+
+/* Only options->window_left is used here (the soft cap acts in Phase 1). */
+pa_status paged_attention_reduce_ex(
+    pa_mode mode, void *out, const float *exp_sums, const float *max_logits,
+    const void *tmp_out, int num_seqs, int num_heads, int num_kv_heads, int head_size,
+    const int32_t *seq_lens, int max_seq_len, int max_num_partitions, pa_dtype dtype,
+    const pa_decode_options *options, void *stream);
+
+/* ---------------------------------------------------------------------- */
 /* Helpers                                                                */
 /* ---------------------------------------------------------------------- */
 
@@ -195,7 +271,8 @@ int pa_num_partitions(int max_seq_len);
  * tiles = num_kv_heads * ceil(seq_len / 512), v2 iff tiles > 2 * SM count)
  * re-sized to the GPU's compute units, plus one clause of ours for small
  * batches: v2 whenever num_seqs * num_kv_heads < cu_count, because v1 would
- * then leave compute units without a workgroup.  Returns 1 for v2, 0 for v1. */
+ * then leave compute units without a workgroup.  Returns 1 for v2, 0 for v1.
+ * Under a sliding window of W >= 0 the auto call passes min(L, W + 1). */
 int pa_should_use_v2(int num_seqs, int num_kv_heads, int seq_len, int cu_count);
 
 /* Compute units of the current HIP device (cached per device); <= 0 and

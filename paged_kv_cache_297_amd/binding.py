@@ -33,10 +33,17 @@ MODE_CODE = {"v1": 0, "v2": 1, "auto": 2}
 #: Every symbol include/pagedattn.h declares.
 EXPORTED_SYMBOLS = (
     "paged_attention_v1", "paged_attention_v2", "paged_attention_auto",
-    "paged_attention_partition", "paged_attention_reduce", "pa_partition_size",
+    "paged_attention_partition", "paged_attention_reduce",
+    "paged_attention_v1_ex", "paged_attention_v2_ex", "paged_attention_auto_ex",
+    "paged_attention_partition_ex", "paged_attention_reduce_ex", "pa_partition_size",
     "pa_num_partitions", "pa_should_use_v2", "pa_device_cu_count", "pa_set_timing_events",
     "pa_status_string", "pa_version",
 )
+
+
+class DecodeOptions(ctypes.Structure):
+    """pa_decode_options: sliding window (-1: none) and logit soft cap (0: none)."""
+    _fields_ = [("window_left", ctypes.c_int), ("logits_soft_cap", ctypes.c_float)]
 
 
 class PagedAttentionError(RuntimeError):
@@ -77,6 +84,14 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.paged_attention_partition.restype = _I
     lib.paged_attention_reduce.argtypes = [_I, _P, _P, _P, _P, _I, _I, _I, _I, _P, _I, _I, _I, _P]
     lib.paged_attention_reduce.restype = _I
+    # The *_ex forms: the same arguments with a pa_decode_options pointer
+    # before the stream.
+    for name in ("paged_attention_v1", "paged_attention_v2", "paged_attention_auto",
+                 "paged_attention_partition", "paged_attention_reduce"):
+        plain = getattr(lib, name).argtypes
+        ex = getattr(lib, name + "_ex")
+        ex.argtypes = plain[:-1] + [_P, _P]
+        ex.restype = _I
     lib.pa_partition_size.argtypes = []
     lib.pa_partition_size.restype = _I
     lib.pa_num_partitions.argtypes = [_I]
@@ -117,6 +132,22 @@ def _kv_code(kv_cache_dtype: str) -> int:
     return KV_CODE[kv_cache_dtype]
 
 
+def _options(window_left: int, logits_soft_cap: float) -> Optional[DecodeOptions]:
+    """None when both options are off (the plain entry point is called)."""
+    if int(window_left) == -1 and float(logits_soft_cap) == 0.0:
+        return None
+    return DecodeOptions(int(window_left), float(logits_soft_cap))
+
+
+def _call(lib, name: str, args, opts: Optional[DecodeOptions]) -> None:
+    """Calls ``name`` (opts None) or ``name``_ex with a pointer to opts."""
+    if opts is None:
+        _check(getattr(lib, name)(*args), name)
+    else:
+        _check(getattr(lib, name + "_ex")(*args[:-1], ctypes.addressof(opts), args[-1]),
+               name + "_ex")
+
+
 def _geometry(query, key_cache, value_cache, block_tables, seq_lens, kv_cache_dtype):
     """Checks layouts and returns (num_seqs, num_heads, head_size, num_blocks, max_blocks)."""
     for name, t in (("query", query), ("key_cache", key_cache), ("value_cache", value_cache),
@@ -152,8 +183,9 @@ def paged_attention_v1(out: torch.Tensor, query: torch.Tensor, key_cache: torch.
                        block_tables: torch.Tensor, seq_lens: torch.Tensor, block_size: int,
                        max_seq_len: int, alibi_slopes: Optional[torch.Tensor] = None,
                        kv_cache_dtype: str = "auto", k_scale: float = 1.0, v_scale: float = 1.0,
-                       stream=None) -> None:
-    """Whole-sequence paged attention; writes ``out`` in place."""
+                       stream=None, window_left: int = -1, logits_soft_cap: float = 0.0) -> None:
+    """Whole-sequence paged attention; writes ``out`` in place.  ``window_left`` /
+    ``logits_soft_cap`` are the decode options (-1 / 0: off)."""
     lib = load_library()
     b, h, d, nb, hkv, bs, mbps = _geometry(query, key_cache, value_cache, block_tables, seq_lens,
                                            kv_cache_dtype)
@@ -161,13 +193,11 @@ def paged_attention_v1(out: torch.Tensor, query: torch.Tensor, key_cache: torch.
         raise ValueError("num_kv_heads / block_size disagree with the cache shape")
     if out.shape != query.shape or out.dtype != query.dtype or not out.is_contiguous():
         raise ValueError("out must be a contiguous tensor like query")
-    st = lib.paged_attention_v1(out.data_ptr(), query.data_ptr(), key_cache.data_ptr(),
-                                value_cache.data_ptr(), b, h, num_kv_heads, d, float(scale),
-                                block_tables.data_ptr(), mbps, seq_lens.data_ptr(), nb, block_size,
-                                int(max_seq_len), _ptr(alibi_slopes), DTYPE_CODE[query.dtype],
-                                _kv_code(kv_cache_dtype), float(k_scale), float(v_scale),
-                                _stream(stream))
-    _check(st, "paged_attention_v1")
+    args = [out.data_ptr(), query.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(), b, h,
+            num_kv_heads, d, float(scale), block_tables.data_ptr(), mbps, seq_lens.data_ptr(), nb,
+            block_size, int(max_seq_len), _ptr(alibi_slopes), DTYPE_CODE[query.dtype],
+            _kv_code(kv_cache_dtype), float(k_scale), float(v_scale), _stream(stream)]
+    _call(lib, "paged_attention_v1", args, _options(window_left, logits_soft_cap))
 
 
 def _v2_args(out, exp_sums, max_logits, tmp_out, query, key_cache, value_cache, num_kv_heads,
@@ -199,25 +229,25 @@ def _v2_args(out, exp_sums, max_logits, tmp_out, query, key_cache, value_cache, 
 def paged_attention_v2(out, exp_sums, max_logits, tmp_out, query, key_cache, value_cache,
                        num_kv_heads, scale, block_tables, seq_lens, block_size, max_seq_len,
                        alibi_slopes=None, kv_cache_dtype="auto", k_scale=1.0, v_scale=1.0,
-                       stream=None) -> None:
+                       stream=None, window_left=-1, logits_soft_cap=0.0) -> None:
     """Partitioned paged attention (Phase 1 + Phase 2); writes all four outputs in place."""
     lib = load_library()
     args = _v2_args(out, exp_sums, max_logits, tmp_out, query, key_cache, value_cache,
                     num_kv_heads, scale, block_tables, seq_lens, block_size, max_seq_len,
                     alibi_slopes, kv_cache_dtype, k_scale, v_scale, stream)
-    _check(lib.paged_attention_v2(*args), "paged_attention_v2")
+    _call(lib, "paged_attention_v2", args, _options(window_left, logits_soft_cap))
 
 
 def paged_attention_auto(out, exp_sums, max_logits, tmp_out, query, key_cache, value_cache,
                          num_kv_heads, scale, block_tables, seq_lens, block_size, max_seq_len,
                          alibi_slopes=None, kv_cache_dtype="auto", k_scale=1.0, v_scale=1.0,
-                         stream=None) -> None:
+                         stream=None, window_left=-1, logits_soft_cap=0.0) -> None:
     """Per-sequence v1/v2 choice on the device (pa_should_use_v2 rule)."""
     lib = load_library()
     args = _v2_args(out, exp_sums, max_logits, tmp_out, query, key_cache, value_cache,
                     num_kv_heads, scale, block_tables, seq_lens, block_size, max_seq_len,
                     alibi_slopes, kv_cache_dtype, k_scale, v_scale, stream)
-    _check(lib.paged_attention_auto(*args), "paged_attention_auto")
+    _call(lib, "paged_attention_auto", args, _options(window_left, logits_soft_cap))
 
 
 class PreparedCall:
@@ -230,13 +260,21 @@ class PreparedCall:
     def __init__(self, mode, out, exp_sums, max_logits, tmp_out, query, key_cache, value_cache,
                  num_kv_heads, scale, block_tables, seq_lens, block_size, max_seq_len,
                  alibi_slopes=None, kv_cache_dtype="auto", k_scale=1.0, v_scale=1.0,
-                 stream=None):
+                 stream=None, window_left=-1, logits_soft_cap=0.0):
         self.lib = load_library()
-        self.fn = {"v2": self.lib.paged_attention_v2, "auto": self.lib.paged_attention_auto}[mode]
         self.name = f"paged_attention_{mode}"
+        if mode not in ("v2", "auto"):
+            raise ValueError("mode must be 'v2' or 'auto'")
         self.args = _v2_args(out, exp_sums, max_logits, tmp_out, query, key_cache, value_cache,
                              num_kv_heads, scale, block_tables, seq_lens, block_size, max_seq_len,
                              alibi_slopes, kv_cache_dtype, k_scale, v_scale, stream)
+        self.opts = _options(window_left, logits_soft_cap)
+        if self.opts is None:
+            self.fn = getattr(self.lib, self.name)
+        else:
+            self.name += "_ex"
+            self.fn = getattr(self.lib, self.name)
+            self.args = self.args[:-1] + [ctypes.addressof(self.opts), self.args[-1]]
         self._keep = (out, exp_sums, max_logits, tmp_out, query, key_cache, value_cache,
                       block_tables, seq_lens, alibi_slopes)
 
@@ -249,26 +287,28 @@ class PreparedCall:
 def paged_attention_partition(mode, out, exp_sums, max_logits, tmp_out, query, key_cache,
                               value_cache, num_kv_heads, scale, block_tables, seq_lens,
                               block_size, max_seq_len, alibi_slopes=None, kv_cache_dtype="auto",
-                              k_scale=1.0, v_scale=1.0, stream=None) -> None:
+                              k_scale=1.0, v_scale=1.0, stream=None, window_left=-1,
+                              logits_soft_cap=0.0) -> None:
     """Phase 1 only (mode 'v1', 'v2' or 'auto')."""
     lib = load_library()
     args = _v2_args(out, exp_sums, max_logits, tmp_out, query, key_cache, value_cache,
                     num_kv_heads, scale, block_tables, seq_lens, block_size, max_seq_len,
                     alibi_slopes, kv_cache_dtype, k_scale, v_scale, stream)
-    _check(lib.paged_attention_partition(MODE_CODE[mode], *args), "paged_attention_partition")
+    _call(lib, "paged_attention_partition", [MODE_CODE[mode]] + args,
+          _options(window_left, logits_soft_cap))
 
 
 def paged_attention_reduce(mode, out, exp_sums, max_logits, tmp_out, seq_lens, num_kv_heads,
-                           max_seq_len, stream=None) -> None:
-    """Phase 2 only (mode 'v2' or 'auto'; 'v1' does nothing)."""
+                           max_seq_len, stream=None, window_left=-1) -> None:
+    """Phase 2 only (mode 'v2' or 'auto'; 'v1' does nothing).  ``window_left``
+    must be the one the partition phase was given."""
     lib = load_library()
     b, h, d = out.shape
     p = exp_sums.shape[2]
-    st = lib.paged_attention_reduce(MODE_CODE[mode], out.data_ptr(), exp_sums.data_ptr(),
-                                    max_logits.data_ptr(), tmp_out.data_ptr(), b, h, num_kv_heads,
-                                    d, seq_lens.data_ptr(), int(max_seq_len), p,
-                                    DTYPE_CODE[out.dtype], _stream(stream))
-    _check(st, "paged_attention_reduce")
+    args = [MODE_CODE[mode], out.data_ptr(), exp_sums.data_ptr(), max_logits.data_ptr(),
+            tmp_out.data_ptr(), b, h, num_kv_heads, d, seq_lens.data_ptr(), int(max_seq_len), p,
+            DTYPE_CODE[out.dtype], _stream(stream)]
+    _call(lib, "paged_attention_reduce", args, _options(window_left, 0.0))
 
 
 def partition_size() -> int:

@@ -104,8 +104,29 @@ struct Call {
   pa_dtype dtype;
   pa_kv_cache_dtype kv_cache_dtype;
   float k_scale, v_scale;
+  int window_left;        // pa_decode_options (-1: no window)
+  float logits_soft_cap;  // (0: no soft cap)
   hipStream_t stream;
 };
+
+// Copies the decode options into the call (NULL: both off).
+pa_status apply_options(const pa_decode_options *o, Call &c) {
+  c.window_left = -1;
+  c.logits_soft_cap = 0.0f;
+  if (!o) return PA_OK;
+  if (o->window_left < -1) return PA_ERR_BAD_ARGUMENT;
+  if (!isfinite(o->logits_soft_cap) || o->logits_soft_cap < 0.0f) return PA_ERR_BAD_ARGUMENT;
+  c.window_left = o->window_left;
+  c.logits_soft_cap = o->logits_soft_cap;
+  return PA_OK;
+}
+
+// The length the auto rule sees for a sequence of length L: the
+// window-clipped min(L, W + 1).
+long long rule_length(const Call &c, long long L) {
+  if (c.window_left >= 0 && L > (long long)c.window_left + 1) return (long long)c.window_left + 1;
+  return L;
+}
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -140,6 +161,10 @@ pa_status validate_common(const Call &c, bool partition_phase) {
   if (c.block_size != 16 && c.block_size != 32) return PA_ERR_UNSUPPORTED;
   if (pa::kPartitionSize % c.block_size != 0) return PA_ERR_UNSUPPORTED;
   if (!isfinite(c.scale) || !isfinite(c.k_scale) || !isfinite(c.v_scale))
+    return PA_ERR_BAD_ARGUMENT;
+  // A soft cap so small that scale * k_scale / cap leaves the float range.
+  if (c.logits_soft_cap > 0.0f &&
+      !isfinite((float)((double)c.scale * (double)c.k_scale / (double)c.logits_soft_cap)))
     return PA_ERR_BAD_ARGUMENT;
   if (!c.query || !c.key_cache || !c.value_cache || !c.block_tables) return PA_ERR_NULL_POINTER;
   if (!aligned16(c.query) || !aligned16(c.key_cache) || !aligned16(c.value_cache))
@@ -203,18 +228,26 @@ Params make_params(const Call &c, int cu, int head_groups) {
                      (c.mode == PA_MODE_V2 || (c.mode == PA_MODE_AUTO && p.auto_all_v2)) ? 1 : 0;
   p.scale_log2 = c.scale * c.k_scale * 1.4426950408889634f;
   p.v_scale = c.v_scale;
+  p.window_left = c.window_left;
+  p.cap_on = c.logits_soft_cap > 0.0f ? 1 : 0;
+  if (p.cap_on) {
+    p.cap_in = (float)(2.0 * 1.4426950408889634 * (double)c.scale * (double)c.k_scale /
+                       (double)c.logits_soft_cap);
+    p.cap_out = (float)((double)c.logits_soft_cap * 1.4426950408889634);
+  }
   return p;
 }
 
 // AUTO launches in which every sequence takes v1: the rule is monotone in the
-// length, so v1 at max_seq_len means v1 for every valid length (an invalid
-// length also takes the v1 path).  Such a launch runs as plain v1: one grid
-// slice instead of one per partition, and no reduce.
+// length, so v1 at max_seq_len (window-clipped) means v1 for every valid
+// length (an invalid length also takes the v1 path).  Such a launch runs as
+// plain v1: one grid slice instead of one per partition, and no reduce.
 bool auto_all_v1(const Call &c, int cu) {
   if (c.mode != PA_MODE_AUTO) return false;
   const Tunables &t = tunables();
   if ((long long)c.num_seqs * c.num_kv_heads < (long long)t.small_batch_factor * cu) return false;
-  return (long long)c.num_kv_heads * pa_num_partitions(c.max_seq_len) <= (long long)t.tile_factor * cu;
+  const int len = (int)rule_length(c, c.max_seq_len);
+  return (long long)c.num_kv_heads * pa_num_partitions(len) <= (long long)t.tile_factor * cu;
 }
 
 pa_status run_partition(const Call &c) {
@@ -308,6 +341,8 @@ Call make_call(pa_mode mode, void *out, float *exp_sums, float *max_logits, void
   c.kv_cache_dtype = kv_cache_dtype;
   c.k_scale = k_scale;
   c.v_scale = v_scale;
+  c.window_left = -1;
+  c.logits_soft_cap = 0.0f;
   c.stream = reinterpret_cast<hipStream_t>(stream);
   return c;
 }
@@ -315,6 +350,27 @@ Call make_call(pa_mode mode, void *out, float *exp_sums, float *max_logits, void
 }  // namespace
 
 extern "C" {
+
+pa_status paged_attention_partition_ex(pa_mode mode, void *out, float *exp_sums,
+                                       float *max_logits, void *tmp_out, const void *query,
+                                       const void *key_cache, const void *value_cache,
+                                       int num_seqs, int num_heads, int num_kv_heads,
+                                       int head_size, float scale, const int32_t *block_tables,
+                                       int max_num_blocks_per_seq, const int32_t *seq_lens,
+                                       int num_blocks, int block_size, int max_seq_len,
+                                       int max_num_partitions, const float *alibi_slopes,
+                                       pa_dtype dtype, pa_kv_cache_dtype kv_cache_dtype,
+                                       float k_scale, float v_scale,
+                                       const pa_decode_options *options, void *stream) {
+  Call c = make_call(mode, out, exp_sums, max_logits, tmp_out, query, key_cache, value_cache,
+                     num_seqs, num_heads, num_kv_heads, head_size, scale, block_tables,
+                     max_num_blocks_per_seq, seq_lens, num_blocks, block_size, max_seq_len,
+                     max_num_partitions, alibi_slopes, dtype, kv_cache_dtype, k_scale, v_scale,
+                     stream);
+  const pa_status st = apply_options(options, c);
+  if (st != PA_OK) return st;
+  return run_partition(c);
+}
 
 pa_status paged_attention_partition(pa_mode mode, void *out, float *exp_sums, float *max_logits,
                                     void *tmp_out, const void *query, const void *key_cache,
@@ -326,11 +382,27 @@ pa_status paged_attention_partition(pa_mode mode, void *out, float *exp_sums, fl
                                     const float *alibi_slopes, pa_dtype dtype,
                                     pa_kv_cache_dtype kv_cache_dtype, float k_scale,
                                     float v_scale, void *stream) {
-  return run_partition(make_call(mode, out, exp_sums, max_logits, tmp_out, query, key_cache,
-                                 value_cache, num_seqs, num_heads, num_kv_heads, head_size, scale,
-                                 block_tables, max_num_blocks_per_seq, seq_lens, num_blocks,
-                                 block_size, max_seq_len, max_num_partitions, alibi_slopes, dtype,
-                                 kv_cache_dtype, k_scale, v_scale, stream));
+  return paged_attention_partition_ex(mode, out, exp_sums, max_logits, tmp_out, query, key_cache,
+                                      value_cache, num_seqs, num_heads, num_kv_heads, head_size,
+                                      scale, block_tables, max_num_blocks_per_seq, seq_lens,
+                                      num_blocks, block_size, max_seq_len, max_num_partitions,
+                                      alibi_slopes, dtype, kv_cache_dtype, k_scale, v_scale,
+                                      nullptr, stream);
+}
+
+pa_status paged_attention_reduce_ex(pa_mode mode, void *out, const float *exp_sums,
+                                    const float *max_logits, const void *tmp_out, int num_seqs,
+                                    int num_heads, int num_kv_heads, int head_size,
+                                    const int32_t *seq_lens, int max_seq_len,
+                                    int max_num_partitions, pa_dtype dtype,
+                                    const pa_decode_options *options, void *stream) {
+  Call c = make_call(mode, out, const_cast<float *>(exp_sums), const_cast<float *>(max_logits),
+                     const_cast<void *>(tmp_out), nullptr, nullptr, nullptr, num_seqs, num_heads,
+                     num_kv_heads, head_size, 1.0f, nullptr, 0, seq_lens, 0, 16, max_seq_len,
+                     max_num_partitions, nullptr, dtype, PA_KV_AUTO, 1.0f, 1.0f, stream);
+  const pa_status st = apply_options(options, c);
+  if (st != PA_OK) return st;
+  return run_reduce(c);
 }
 
 pa_status paged_attention_reduce(pa_mode mode, void *out, const float *exp_sums,
@@ -338,11 +410,9 @@ pa_status paged_attention_reduce(pa_mode mode, void *out, const float *exp_sums,
                                  int num_heads, int num_kv_heads, int head_size,
                                  const int32_t *seq_lens, int max_seq_len, int max_num_partitions,
                                  pa_dtype dtype, void *stream) {
-  return run_reduce(make_call(mode, out, const_cast<float *>(exp_sums),
-                              const_cast<float *>(max_logits), const_cast<void *>(tmp_out),
-                              nullptr, nullptr, nullptr, num_seqs, num_heads, num_kv_heads,
-                              head_size, 1.0f, nullptr, 0, seq_lens, 0, 16, max_seq_len,
-                              max_num_partitions, nullptr, dtype, PA_KV_AUTO, 1.0f, 1.0f, stream));
+  return paged_attention_reduce_ex(mode, out, exp_sums, max_logits, tmp_out, num_seqs, num_heads,
+                                   num_kv_heads, head_size, seq_lens, max_seq_len,
+                                   max_num_partitions, dtype, nullptr, stream);
 }
 
 static pa_status two_phase(pa_mode mode, void *out, float *exp_sums, float *max_logits,
@@ -353,18 +423,37 @@ static pa_status two_phase(pa_mode mode, void *out, float *exp_sums, float *max_
                            int block_size, int max_seq_len, int max_num_partitions,
                            const float *alibi_slopes, pa_dtype dtype,
                            pa_kv_cache_dtype kv_cache_dtype, float k_scale, float v_scale,
-                           void *stream) {
-  const Call c = make_call(mode, out, exp_sums, max_logits, tmp_out, query, key_cache, value_cache,
-                           num_seqs, num_heads, num_kv_heads, head_size, scale, block_tables,
-                           max_num_blocks_per_seq, seq_lens, num_blocks, block_size, max_seq_len,
-                           max_num_partitions, alibi_slopes, dtype, kv_cache_dtype, k_scale,
-                           v_scale, stream);
+                           const pa_decode_options *options, void *stream) {
+  Call c = make_call(mode, out, exp_sums, max_logits, tmp_out, query, key_cache, value_cache,
+                     num_seqs, num_heads, num_kv_heads, head_size, scale, block_tables,
+                     max_num_blocks_per_seq, seq_lens, num_blocks, block_size, max_seq_len,
+                     max_num_partitions, alibi_slopes, dtype, kv_cache_dtype, k_scale, v_scale,
+                     stream);
   // Validate both phases before launching either.
-  pa_status st = validate_common(c, true);
+  pa_status st = apply_options(options, c);
+  if (st != PA_OK) return st;
+  st = validate_common(c, true);
   if (st != PA_OK) return st;
   st = run_partition(c);
   if (st != PA_OK) return st;
   return run_reduce(c);
+}
+
+pa_status paged_attention_v1_ex(void *out, const void *query, const void *key_cache,
+                                const void *value_cache, int num_seqs, int num_heads,
+                                int num_kv_heads, int head_size, float scale,
+                                const int32_t *block_tables, int max_num_blocks_per_seq,
+                                const int32_t *seq_lens, int num_blocks, int block_size,
+                                int max_seq_len, const float *alibi_slopes, pa_dtype dtype,
+                                pa_kv_cache_dtype kv_cache_dtype, float k_scale, float v_scale,
+                                const pa_decode_options *options, void *stream) {
+  Call c = make_call(PA_MODE_V1, out, nullptr, nullptr, nullptr, query, key_cache, value_cache,
+                     num_seqs, num_heads, num_kv_heads, head_size, scale, block_tables,
+                     max_num_blocks_per_seq, seq_lens, num_blocks, block_size, max_seq_len, 1,
+                     alibi_slopes, dtype, kv_cache_dtype, k_scale, v_scale, stream);
+  const pa_status st = apply_options(options, c);
+  if (st != PA_OK) return st;
+  return run_partition(c);
 }
 
 pa_status paged_attention_v1(void *out, const void *query, const void *key_cache,
@@ -375,11 +464,28 @@ pa_status paged_attention_v1(void *out, const void *query, const void *key_cache
                              int max_seq_len, const float *alibi_slopes, pa_dtype dtype,
                              pa_kv_cache_dtype kv_cache_dtype, float k_scale, float v_scale,
                              void *stream) {
-  return run_partition(make_call(PA_MODE_V1, out, nullptr, nullptr, nullptr, query, key_cache,
-                                 value_cache, num_seqs, num_heads, num_kv_heads, head_size, scale,
-                                 block_tables, max_num_blocks_per_seq, seq_lens, num_blocks,
-                                 block_size, max_seq_len, 1, alibi_slopes, dtype, kv_cache_dtype,
-                                 k_scale, v_scale, stream));
+  return paged_attention_v1_ex(out, query, key_cache, value_cache, num_seqs, num_heads,
+                               num_kv_heads, head_size, scale, block_tables,
+                               max_num_blocks_per_seq, seq_lens, num_blocks, block_size,
+                               max_seq_len, alibi_slopes, dtype, kv_cache_dtype, k_scale, v_scale,
+                               nullptr, stream);
+}
+
+pa_status paged_attention_v2_ex(void *out, float *exp_sums, float *max_logits, void *tmp_out,
+                                const void *query, const void *key_cache,
+                                const void *value_cache, int num_seqs, int num_heads,
+                                int num_kv_heads, int head_size, float scale,
+                                const int32_t *block_tables, int max_num_blocks_per_seq,
+                                const int32_t *seq_lens, int num_blocks, int block_size,
+                                int max_seq_len, int max_num_partitions,
+                                const float *alibi_slopes, pa_dtype dtype,
+                                pa_kv_cache_dtype kv_cache_dtype, float k_scale, float v_scale,
+                                const pa_decode_options *options, void *stream) {
+  return two_phase(PA_MODE_V2, out, exp_sums, max_logits, tmp_out, query, key_cache, value_cache,
+                   num_seqs, num_heads, num_kv_heads, head_size, scale, block_tables,
+                   max_num_blocks_per_seq, seq_lens, num_blocks, block_size, max_seq_len,
+                   max_num_partitions, alibi_slopes, dtype, kv_cache_dtype, k_scale, v_scale,
+                   options, stream);
 }
 
 pa_status paged_attention_v2(void *out, float *exp_sums, float *max_logits, void *tmp_out,
@@ -394,7 +500,24 @@ pa_status paged_attention_v2(void *out, float *exp_sums, float *max_logits, void
                    num_seqs, num_heads, num_kv_heads, head_size, scale, block_tables,
                    max_num_blocks_per_seq, seq_lens, num_blocks, block_size, max_seq_len,
                    max_num_partitions, alibi_slopes, dtype, kv_cache_dtype, k_scale, v_scale,
-                   stream);
+                   nullptr, stream);
+}
+
+pa_status paged_attention_auto_ex(void *out, float *exp_sums, float *max_logits, void *tmp_out,
+                                  const void *query, const void *key_cache,
+                                  const void *value_cache, int num_seqs, int num_heads,
+                                  int num_kv_heads, int head_size, float scale,
+                                  const int32_t *block_tables, int max_num_blocks_per_seq,
+                                  const int32_t *seq_lens, int num_blocks, int block_size,
+                                  int max_seq_len, int max_num_partitions,
+                                  const float *alibi_slopes, pa_dtype dtype,
+                                  pa_kv_cache_dtype kv_cache_dtype, float k_scale, float v_scale,
+                                  const pa_decode_options *options, void *stream) {
+  return two_phase(PA_MODE_AUTO, out, exp_sums, max_logits, tmp_out, query, key_cache,
+                   value_cache, num_seqs, num_heads, num_kv_heads, head_size, scale, block_tables,
+                   max_num_blocks_per_seq, seq_lens, num_blocks, block_size, max_seq_len,
+                   max_num_partitions, alibi_slopes, dtype, kv_cache_dtype, k_scale, v_scale,
+                   options, stream);
 }
 
 pa_status paged_attention_auto(void *out, float *exp_sums, float *max_logits, void *tmp_out,
@@ -410,7 +533,7 @@ pa_status paged_attention_auto(void *out, float *exp_sums, float *max_logits, vo
                    value_cache, num_seqs, num_heads, num_kv_heads, head_size, scale, block_tables,
                    max_num_blocks_per_seq, seq_lens, num_blocks, block_size, max_seq_len,
                    max_num_partitions, alibi_slopes, dtype, kv_cache_dtype, k_scale, v_scale,
-                   stream);
+                   nullptr, stream);
 }
 
 pa_status pa_set_timing_events(void *partition_start, void *partition_stop, void *reduce_start,

@@ -91,11 +91,30 @@ __device__ __forceinline__ unsigned pack2(float a, float b, _Float16) {
   return __builtin_bit_cast(unsigned, v);
 }
 
+// Whether token t lies in [lo, lo + span) (span >= 1): one unsigned compare.
+__device__ __forceinline__ bool in_span(int t, int lo, int span) {
+  return (unsigned)(t - lo) < (unsigned)span;
+}
+
 // Keep-mask of a 32-bit word holding two 16-bit elements of tokens t, t + 1:
-// the half of a token >= nv is cleared.  Straight-line selects, so the tail
-// mask can be applied on every step without a divergent branch.
-__device__ __forceinline__ unsigned keep_pair_mask(int t, int nv) {
-  return (t < nv ? 0x0000FFFFu : 0u) | (t + 1 < nv ? 0xFFFF0000u : 0u);
+// the half of a token outside [lo, lo + span) is cleared.  Straight-line
+// selects, so the window and tail masks can be applied on every step without
+// a divergent branch.
+__device__ __forceinline__ unsigned keep_pair_mask(int t, int lo, int span) {
+  return (in_span(t, lo, span) ? 0x0000FFFFu : 0u) | (in_span(t + 1, lo, span) ? 0xFFFF0000u : 0u);
+}
+
+// A key's logit in log2 units, before the ALiBi term, from its dot product
+// with the query: scale * k_scale * q.K, or under a soft cap c
+// c * tanh(scale * k_scale * q.K / c), with tanh(y) = 1 - 2 / (exp(2y) + 1)
+// (an exp that overflows to +inf gives 1, one that underflows to 0 gives -1).
+// cap_on is uniform, so the branch is a scalar one.
+__device__ __forceinline__ float scaled_logit(const Params &p, float dot) {
+  if (p.cap_on) {
+    const float e = fast_exp2(dot * p.cap_in);
+    return fmaf(-2.0f * p.cap_out, __builtin_amdgcn_rcpf(e + 1.0f), p.cap_out);
+  }
+  return dot * p.scale_log2;
 }
 
 template <typename T>
@@ -176,7 +195,8 @@ __device__ __forceinline__ void wave_lds_sync() {
 }
 
 // ---------------------------------------------------------------------------
-// Per-sequence path choice (host mirror: pa_should_use_v2).
+// Per-sequence path choice (host mirror: pa_should_use_v2).  seq_len is the
+// length the rule sees: the window-clipped min(L, W + 1) under a window.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ bool seq_uses_v2(const Params &p, int seq_len) {
   if (p.mode == kModeV1) return false;

@@ -1,6 +1,7 @@
 // Launch parameters shared by the host library and the gfx950 kernels.
 #pragma once
 
+#include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace pa {
@@ -48,6 +49,16 @@ struct Params {
   int parts_reversed;   // grid z walks the partitions from the last to the first
   float scale_log2;     // scale * k_scale * log2(e): logits are kept in log2 units
   float v_scale;
+  int window_left;      // -1: every key; W >= 0: keys t >= L - 1 - W only
+  int cap_on;           // logit soft cap c > 0 in use
+  float cap_in;         // 2 * log2(e) * scale * k_scale / c: exponent of exp(2 s / c)
+  float cap_out;        // c * log2(e): the capped logit in log2 units
 };
+
+// First key position inside the sliding window of a sequence of length
+// L >= 1 (0 without a window).
+__host__ __device__ inline int window_first_token(int window_left, int L) {
+  return (window_left >= 0 && L - 1 - window_left > 0) ? L - 1 - window_left : 0;
+}
 
 }  // namespace pa

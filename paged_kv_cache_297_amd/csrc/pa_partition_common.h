@@ -23,7 +23,9 @@ struct Work {
   int L, n_part, part;      // sequence length, its partitions, this workgroup's partition
   int blk_begin, blk_end;   // logical blocks [blk_begin, blk_end) of this workgroup
   int t_ref;                // last token of this workgroup's range (ALiBi reference)
+  int t_lo, span;           // keys weighed: [t_lo, t_lo + span) = window start .. t_ref
   bool v2;                  // partials are stored (v2) or out is written directly (v1)
+  bool single;              // v2 with one partition in the window: out is written too
 };
 
 template <typename QT, int D>
@@ -45,10 +47,23 @@ __device__ __forceinline__ void write_stat_padding(const Params &p, const Work &
   }
 }
 
+// The statistics of one partition slot with no key in the window: the
+// padding values, no tmp_out row.
+__device__ __forceinline__ void write_stat_empty(const Params &p, const Work &w, int slot) {
+  if (threadIdx.x < w.nh) {
+    const size_t row =
+        ((size_t)w.seq * p.num_heads + w.head0 + threadIdx.x) * p.max_num_partitions + slot;
+    p.max_logits[row] = -__builtin_inff();
+    p.exp_sums[row] = 0.0f;
+  }
+}
+
 // Decodes one work item (sequence, grid-x slot = KV head x head group,
 // partition) into a Work.  Returns false when there is nothing (more) to
 // compute; sequences of length 0 (out = 0) and with an invalid length
-// (out = NaN) are finished here by their partition-0 item.
+// (out = NaN) are finished here by their partition-0 item.  Under a sliding
+// window the range starts at the block holding the first key of the window;
+// v2 partitions before it only store padding statistics.
 template <typename QT, int D>
 __device__ __forceinline__ bool decode_work(const Params &p, int seq, int xslot, int part,
                                            int block_size, int group_slots, Work &w) {
@@ -59,7 +74,9 @@ __device__ __forceinline__ bool decode_work(const Params &p, int seq, int xslot,
   w.nh = min(group_slots, p.group - hg * group_slots);
   w.L = p.seq_lens[w.seq];
   const bool bad = (w.L < 0) || (w.L > p.max_seq_len);
-  w.v2 = seq_uses_v2(p, bad ? 0 : w.L);
+  w.t_lo = bad ? 0 : window_first_token(p.window_left, w.L);
+  w.v2 = seq_uses_v2(p, bad ? 0 : w.L - w.t_lo);
+  w.single = false;
   w.n_part = bad ? 0 : (w.L + kPartitionSize - 1) / kPartitionSize;
   w.part = part;
   if (bad || w.L == 0) {
@@ -82,16 +99,25 @@ __device__ __forceinline__ bool decode_work(const Params &p, int seq, int xslot,
   if (w.v2) {
     if (w.part >= w.n_part) return false;
     if (w.part == 0) write_stat_padding(p, w, w.n_part);
+    const int part_lo = w.t_lo / kPartitionSize;  // first partition with a key in the window
+    if (w.part < part_lo) {
+      write_stat_empty(p, w, w.part);
+      return false;
+    }
+    w.single = w.n_part - part_lo == 1;
     const int bpp = kPartitionSize / block_size;
-    w.blk_begin = w.part * bpp;
-    w.blk_end = min(w.blk_begin + bpp, n_logical);
+    w.blk_begin = max(w.part * bpp, w.t_lo / block_size);
+    w.blk_end = min(w.part * bpp + bpp, n_logical);
     w.t_ref = min((w.part + 1) * kPartitionSize, w.L) - 1;
   } else {
     if (w.part != 0) return false;
-    w.blk_begin = 0;
+    w.blk_begin = w.t_lo / block_size;
     w.blk_end = n_logical;
     w.t_ref = w.L - 1;
   }
+  // The upper bound matters where a 32-token MFMA step that starts inside
+  // the window's first block runs past the end of a v2 partition.
+  w.span = w.t_ref + 1 - w.t_lo;
   return true;
 }
 
@@ -153,7 +179,7 @@ __device__ __forceinline__ void finish_partition(const Params &p, const Work &w,
         p.exp_sums[row] = sum;
         p.max_logits[row] = ml;
       }
-      if (w.n_part == 1) store_out_row<QT, D>(p, w.seq, head, d, o);
+      if (w.single) store_out_row<QT, D>(p, w.seq, head, d, o);
     } else {
       store_out_row<QT, D>(p, w.seq, head, d, o);
     }

@@ -50,11 +50,11 @@ __device__ __forceinline__ f32x4 mfma_pv(const u32x4 &a, const u32x4 &b, const f
                                                 __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
 }
 
-// Zero the 16-bit elements of tokens >= nv in an 8-token V operand whose
-// first element is token 0.
-__device__ __forceinline__ u32x4 mask_v8(u32x4 v, int nv) {
-  return u32x4{v.x & keep_pair_mask(0, nv), v.y & keep_pair_mask(2, nv),
-               v.z & keep_pair_mask(4, nv), v.w & keep_pair_mask(6, nv)};
+// Zero the 16-bit elements of tokens outside [lo, lo + span) in an 8-token V
+// operand whose first element is token 0.
+__device__ __forceinline__ u32x4 mask_v8(u32x4 v, int lo, int span) {
+  return u32x4{v.x & keep_pair_mask(0, lo, span), v.y & keep_pair_mask(2, lo, span),
+               v.z & keep_pair_mask(4, lo, span), v.w & keep_pair_mask(6, lo, span)};
 }
 
 // Regroups packed P (two 4-token pieces per lane: p0 from sub-tile 0, p1
@@ -242,7 +242,8 @@ __global__ void __launch_bounds__(kThreads)
       }
       st[h] = c;
     }
-    // Scale, ALiBi, mask, step max over the head's tokens.
+    // Scale (and soft cap), ALiBi, window / tail mask, step max over the
+    // head's tokens.
     const int t0 = it.tok_begin + 32 * step;
     float x[2][4];
     float bm = -__builtin_inff();
@@ -251,8 +252,8 @@ __global__ void __launch_bounds__(kThreads)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int t = t0 + 16 * h + 4 * g + e;
-        float v = st[h][e] * p.scale_log2 + slope2 * (float)(t - it.w.t_ref);
-        v = (t < it.w.L) ? v : -__builtin_inff();
+        float v = scaled_logit(p, st[h][e]) + slope2 * (float)(t - it.w.t_ref);
+        v = in_span(t, it.w.t_lo, it.w.span) ? v : -__builtin_inff();
         x[h][e] = v;
         bm = fmaxf(bm, v);
       }
@@ -274,7 +275,7 @@ __global__ void __launch_bounds__(kThreads)
     }
     l_run = l_run * alpha + psum;
     const u32x4 pop = regroup_p(pk[0], pk[1]);
-    const int nv = it.w.L - (t0 + vtok);  // valid tokens among this lane's V operand
+    const int vlo = it.w.t_lo - (t0 + vtok);  // window start relative to this lane's V operand
 #pragma unroll
     for (int t = 0; t < NDT; ++t) {
       u32x4 va;
@@ -284,7 +285,7 @@ __global__ void __launch_bounds__(kThreads)
       } else {
         va = tl.v[t];
       }
-      va = mask_v8(va, nv);
+      va = mask_v8(va, vlo, it.w.span);
       oacc[t] = mfma_pv(va, pop, oacc[t] * alpha, PT());
     }
   };

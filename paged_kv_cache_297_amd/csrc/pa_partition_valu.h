@@ -51,10 +51,11 @@ struct ValuTraits<float, float> {
     for (int e = 0; e < 4; ++e) acc = fmaf(bits_f(pw[e]), bits_f(vw[e]), acc);
     return acc;
   }
-  // Zero the V elements of tokens >= nv (first = token of element 0).
-  __device__ static void mask_v(unsigned (&w)[kPW], int first, int nv) {
+  // Zero the V elements of tokens outside [lo, lo + span) (first = token of
+  // element 0).
+  __device__ static void mask_v(unsigned (&w)[kPW], int first, int lo, int span) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) w[e] &= (first + e < nv) ? ~0u : 0u;
+    for (int e = 0; e < 4; ++e) w[e] &= in_span(first + e, lo, span) ? ~0u : 0u;
   }
 };
 
@@ -83,9 +84,9 @@ struct ValuTraits16 {
     for (int e = 0; e < 4; ++e) acc = dot2(acc, pw[e], vw[e], T16());
     return acc;
   }
-  __device__ static void mask_v(unsigned (&w)[kPW], int first, int nv) {
+  __device__ static void mask_v(unsigned (&w)[kPW], int first, int lo, int span) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) w[e] &= keep_pair_mask(first + 2 * e, nv);
+    for (int e = 0; e < 4; ++e) w[e] &= keep_pair_mask(first + 2 * e, lo, span);
   }
 };
 template <> struct ValuTraits<__bf16, __bf16> : ValuTraits16<__bf16> {};
@@ -127,9 +128,9 @@ struct ValuTraitsFp8 {
     return acc;
   }
   // Applied to the widened words: word e holds tokens first+2e, first+2e+1.
-  __device__ static void mask_v(unsigned (&w)[kPW], int first, int nv) {
+  __device__ static void mask_v(unsigned (&w)[kPW], int first, int lo, int span) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) w[e] &= keep_pair_mask(first + 2 * e, nv);
+    for (int e = 0; e < 8; ++e) w[e] &= keep_pair_mask(first + 2 * e, lo, span);
   }
 };
 template <> struct ValuTraits<__bf16, fp8e4m3> : ValuTraitsFp8<__bf16> {};
@@ -331,8 +332,8 @@ __global__ void __launch_bounds__(kThreads) PA_VALU_OCCUPANCY pa_partition_valu(
     float alpha[NF], pj[NF];
 #pragma unroll
     for (int j = 0; j < NF; ++j) {
-      float x = s[j] * p.scale_log2 + slope2[j] * (float)(t_abs - w.t_ref);
-      x = (t_abs < w.L) ? x : -__builtin_inff();
+      float x = scaled_logit(p, s[j]) + slope2[j] * (float)(t_abs - w.t_ref);
+      x = in_span(t_abs, w.t_lo, w.span) ? x : -__builtin_inff();
       const float bm = token_group_max<BS>(x);
       const float m_new = fmaxf(m_run[j], bm);
       alpha[j] = (m_new == -__builtin_inff()) ? 1.0f : fast_exp2(m_run[j] - m_new);
@@ -349,12 +350,12 @@ __global__ void __launch_bounds__(kThreads) PA_VALU_OCCUPANCY pa_partition_valu(
 #pragma unroll
     for (int h = 0; h < GP; ++h)
       a_bc[h] = readlane(alpha[h - HM::head_base(HM::src_group(h))], HM::src_group(h) * BS);
-    const int nv = w.L - blk * BS;  // valid tokens in this block (>= 1)
+    const int vlo = w.t_lo - blk * BS;  // window start relative to the block
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
       unsigned vw[T::kPW];
       T::v_words(tl.v[i], vw);
-      T::mask_v(vw, tg * X, nv);
+      T::mask_v(vw, tg * X, vlo, w.span);
 #pragma unroll
       for (int h = 0; h < GP; ++h) {
         const float a_h = a_bc[h];

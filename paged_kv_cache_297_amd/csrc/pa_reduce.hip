@@ -3,8 +3,11 @@
 // across partitions"):
 //   M = max_p m_p,  r_p = exp(m_p - M) * S_p,  out = sum_p r_p O_p / sum_p r_p.
 // One 256-thread workgroup per (query head, sequence); sequences with a single
-// partition (out already written by Phase 1), on the v1 path, or with an
-// invalid length are skipped.
+// partition in the window (out already written by Phase 1), on the v1 path,
+// or with an invalid length are skipped.  Under a sliding window the merge
+// starts at the first partition holding a key of the window; a partition
+// with max_logit = -inf adds nothing, and its tmp_out row (never written) is
+// not used.
 #include "pa_device.h"
 #include "pa_launch.h"
 
@@ -43,9 +46,12 @@ __global__ void __launch_bounds__(kThreads) pa_reduce_kernel(const Params p) {
   static_assert(kThreads % TPR == 0 && D % EPT == 0, "reduce geometry");
   const int head = blockIdx.x, seq = blockIdx.y;
   const int L = p.seq_lens[seq];
-  if (L < 0 || L > p.max_seq_len || !seq_uses_v2(p, L)) return;
+  if (L < 0 || L > p.max_seq_len) return;
+  const int t_lo = window_first_token(p.window_left, L);
+  if (!seq_uses_v2(p, L - t_lo)) return;
   const int n_part = (L + kPartitionSize - 1) / kPartitionSize;
-  if (n_part <= 1) return;
+  const int part_lo = t_lo / kPartitionSize;
+  if (n_part - part_lo <= 1) return;
 
   __shared__ float sm_m[PG], sm_s[PG];
   __shared__ float sm_a[PG][D];
@@ -60,7 +66,7 @@ __global__ void __launch_bounds__(kThreads) pa_reduce_kernel(const Params p) {
   float m_run = ninf, s_run = 0.0f, a_run[EPT];
 #pragma unroll
   for (int e = 0; e < EPT; ++e) a_run[e] = 0.0f;
-  for (int base = pg; base < n_part; base += kReduceBatch * PG) {
+  for (int base = part_lo + pg; base < n_part; base += kReduceBatch * PG) {
     float mv[kReduceBatch], ev[kReduceBatch];
     u32x4 ov[kReduceBatch];
 #pragma unroll
@@ -84,8 +90,9 @@ __global__ void __launch_bounds__(kThreads) pa_reduce_kernel(const Params p) {
       float f[EPT];
       chunk_to_f32<QT>(ov[j], f);
       s_run += r;
+      const bool live = mv[j] != ninf;
 #pragma unroll
-      for (int e = 0; e < EPT; ++e) a_run[e] = fmaf(r, f[e], a_run[e]);
+      for (int e = 0; e < EPT; ++e) a_run[e] = live ? fmaf(r, f[e], a_run[e]) : a_run[e];
     }
     m_run = bm;
   }

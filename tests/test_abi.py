@@ -199,3 +199,75 @@ def test_timing_events_argument_pairs():
     assert lib.pa_set_timing_events(A, None, None, None) == NULLP
     assert lib.pa_set_timing_events(None, None, A, None) == NULLP
     assert lib.pa_set_timing_events(None, None, None, None) == OK
+
+
+# --------------------------------------------------------------------------
+# Decode options (sliding window, logit soft cap): the *_ex entry points
+# --------------------------------------------------------------------------
+
+def opts(window_left=-1, cap=0.0):
+    return ctypes.byref(B.DecodeOptions(window_left, cap))
+
+
+BAD_OPTIONS = [(-2, 0.0), (-100, 0.0), (-1, -1.0), (-1, float("nan")), (-1, float("inf")),
+               (5, -0.5)]
+
+
+def ex_args(fn, options, **kw):
+    """Arguments of the *_ex form of ``fn`` (options before the stream)."""
+    a = v2_args(**kw)
+    if fn == "paged_attention_v1_ex":
+        a = a[0:1] + a[4:18] + a[19:]
+    elif fn == "paged_attention_partition_ex":
+        a = [V2] + a
+    return a[:-1] + [options, a[-1]]
+
+
+EX_FUNCS = ["paged_attention_v1_ex", "paged_attention_v2_ex", "paged_attention_auto_ex",
+            "paged_attention_partition_ex"]
+
+
+@pytest.mark.parametrize("fn", EX_FUNCS)
+@pytest.mark.parametrize("w,cap", BAD_OPTIONS)
+def test_ex_rejects_bad_options(fn, w, cap):
+    lib = B.load_library()
+    assert getattr(lib, fn)(*ex_args(fn, opts(w, cap))) == BADARG
+    # Checked before the batch is looked at.
+    assert getattr(lib, fn)(*ex_args(fn, opts(w, cap), num_seqs=0)) == BADARG
+
+
+@pytest.mark.parametrize("fn", EX_FUNCS)
+def test_ex_rejects_a_cap_that_overflows_the_logit_scale(fn):
+    """scale * k_scale / cap beyond the float range (a subnormal cap)."""
+    lib = B.load_library()
+    assert getattr(lib, fn)(*ex_args(fn, opts(-1, 1e-45))) == BADARG
+    assert getattr(lib, fn)(*ex_args(fn, opts(-1, 1e-45), scale=0.0, num_seqs=0)) == OK
+
+
+@pytest.mark.parametrize("fn", EX_FUNCS)
+@pytest.mark.parametrize("kw,status", CASES[::3])
+def test_ex_with_null_options_validates_as_the_plain_call(fn, kw, status):
+    lib = B.load_library()
+    if fn == "paged_attention_v1_ex" and any(k in kw for k in ("exp_sums", "tmp_out", "max_parts")):
+        pytest.skip("v1 has no partial buffers")
+    assert getattr(lib, fn)(*ex_args(fn, None, **kw)) == status
+
+
+@pytest.mark.parametrize("fn", EX_FUNCS)
+@pytest.mark.parametrize("w,cap", [(-1, 0.0), (0, 0.0), (4095, 0.0), (2 ** 31 - 1, 50.0),
+                                   (-1, 1e-3), (17, 30.0)])
+def test_ex_accepts_valid_options(fn, w, cap):
+    lib = B.load_library()
+    assert getattr(lib, fn)(*ex_args(fn, opts(w, cap), num_seqs=0)) == OK
+    assert getattr(lib, fn)(*ex_args(fn, opts(w, cap), head_size=96)) == UNSUP
+
+
+def test_reduce_ex_options():
+    lib = B.load_library()
+    base = [V2, A, A, A, A, 0, 4, 2, 64, A, 700, 2, F32]
+    assert lib.paged_attention_reduce_ex(*base, None, None) == OK
+    assert lib.paged_attention_reduce_ex(*base, opts(100, 0.0), None) == OK
+    for w, cap in BAD_OPTIONS:
+        assert lib.paged_attention_reduce_ex(*base, opts(w, cap), None) == BADARG
+    bad = list(base); bad[8] = 80
+    assert lib.paged_attention_reduce_ex(*bad, opts(3, 0.0), None) == UNSUP
