@@ -17,7 +17,9 @@ steps are then run again with the library's profiling hook
 start and end, giving the average partition-kernel duration used for the
 roofline (the recording adds a few microseconds per step, so it is not part
 of the wall-clock region).  The fp64 CPU oracle is timed on a bounded sample of the same
-workload for the CPU baseline.
+workload for the CPU baseline.  ``--window W`` / ``--softcap C`` turn on the
+decode options (sliding window over the last W + 1 keys, logit soft cap);
+the KV bytes then count the keys inside the window only.
 
 Prints one JSON line (stdout); progress goes to stderr.
 """
@@ -55,23 +57,27 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def algorithmic_bytes(wl, path: str, cu: int, B) -> dict:
-    """Bytes each launch must move at minimum (each KV byte once per KV head)."""
+def algorithmic_bytes(wl, path: str, cu: int, B, window_left: int = -1) -> dict:
+    """Bytes each launch must move at minimum (each KV byte inside the window
+    once per KV head)."""
     import numpy as np
     lens = wl.lens.astype(np.int64)
+    t_lo = np.maximum(0, lens - 1 - window_left) if window_left >= 0 else np.zeros_like(lens)
+    eff = lens - t_lo                                 # keys inside the window
     esz_q = wl.query.element_size()
-    kv = wl.kv_bytes()
+    kv = int(eff.sum()) * wl.num_kv_heads * wl.head_size * 2 * wl.kv_elem_bytes
     q = wl.num_seqs * wl.num_heads * wl.head_size * esz_q
     out = q
-    blocks = int(((lens + wl.block_size - 1) // wl.block_size).sum())
+    blocks = int(((lens + wl.block_size - 1) // wl.block_size - t_lo // wl.block_size).sum())
     table = blocks * 4 + wl.num_seqs * 4
-    parts = np.where(lens > 0, (lens + 511) // 512, 0)
+    # Partitions holding a key of the window.
+    parts = np.where(lens > 0, (lens + 511) // 512 - t_lo // 512, 0)
     if path == "v1":
         v2 = np.zeros_like(lens, dtype=bool)
     elif path == "v2":
         v2 = np.ones_like(lens, dtype=bool)
     else:
-        v2 = np.array([B.should_use_v2(wl.num_seqs, wl.num_kv_heads, int(L), cu) for L in lens])
+        v2 = np.array([B.should_use_v2(wl.num_seqs, wl.num_kv_heads, int(n), cu) for n in eff])
     h, d = wl.num_heads, wl.head_size
     tmp = int((parts * v2).sum()) * h * d * esz_q   # partial outputs in the query dtype
     stats = int((v2 * wl.max_num_partitions).sum()) * h * 8   # values and padding
@@ -108,7 +114,7 @@ def read_traffic(workload_name: str, src_hash: str, call_path: str):
         return None
 
 
-def cpu_baseline(wl, budget_s: float) -> dict:
+def cpu_baseline(wl, budget_s: float, window_left: int = -1, soft_cap: float = 0.0) -> dict:
     """The fp64 oracle, single-threaded, on whole sequences of the same batch
     until ``budget_s`` of CPU time is spent (at least one sequence)."""
     from threadpoolctl import threadpool_limits
@@ -117,6 +123,8 @@ def cpu_baseline(wl, budget_s: float) -> dict:
     from paged_kv_cache_297_amd import workloads as W
 
     alibi = None if wl.alibi_slopes is None else wl.alibi_slopes.cpu().double().numpy()
+    eff_all = [min(int(L), window_left + 1) if window_left >= 0 else int(L) for L in wl.lens]
+    kv_step = sum(eff_all) * wl.num_kv_heads * wl.head_size * 2 * wl.kv_elem_bytes
     done, kv_done, spent = 0, 0, 0.0
     hosts = {}
     with threadpool_limits(1):
@@ -130,16 +138,19 @@ def cpu_baseline(wl, budget_s: float) -> dict:
                               host["block_tables"], host["seq_lens"], wl.scale,
                               q_kind=wl.q_kind, kv_kind=wl.kv_kind, k_scale=wl.k_scale,
                               v_scale=wl.v_scale, alibi_slopes=alibi,
-                              max_num_partitions=wl.max_num_partitions, seqs=[s])
+                              max_num_partitions=wl.max_num_partitions, seqs=[s],
+                              window_left=window_left, soft_cap=soft_cap)
             spent += time.perf_counter() - t0
             done += 1
-            kv_done += int(wl.lens[s]) * wl.num_kv_heads * wl.head_size * 2 * wl.kv_elem_bytes
+            L = int(wl.lens[s])
+            eff = min(L, window_left + 1) if window_left >= 0 else L
+            kv_done += eff * wl.num_kv_heads * wl.head_size * 2 * wl.kv_elem_bytes
     gbs = kv_done / spent / 1e9
     return {"value": round(gbs, 5), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": (f"{done} sequence passes over the {wl.num_seqs} sequences of the same "
                        f"batch ({kv_done / 1e6:.1f} MB of KV), v1 + v2 partials + merge in fp64, "
                        f"1 thread, {spent:.1f} s; device-to-host copies excluded"),
-            "us_per_step_extrapolated": round(spent / kv_done * wl.kv_bytes() * 1e6, 1)}
+            "us_per_step_extrapolated": round(spent / kv_done * kv_step * 1e6, 1)}
 
 
 def main() -> int:
@@ -155,6 +166,10 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="also run a plain device copy of MIB MiB (counter calibration)")
+    ap.add_argument("--window", type=int, default=-1, metavar="W",
+                    help="sliding window: attend to the last W + 1 keys (-1: off)")
+    ap.add_argument("--softcap", type=float, default=0.0, metavar="C",
+                    help="logit soft cap C * tanh(s / C) (0: off)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -187,7 +202,7 @@ def main() -> int:
         wls.append(w2)
     outs = [wl.alloc_outputs() for wl in wls]
     cu = B.device_cu_count()
-    ab = algorithmic_bytes(base, args.path, cu, B)
+    ab = algorithmic_bytes(base, args.path, cu, B, args.window)
     stream = torch.cuda.current_stream()
 
     # Arguments are checked and marshalled once per input copy; a timed step is
@@ -198,7 +213,8 @@ def main() -> int:
         common = (out, es, ml, to, wl.query, wl.key_cache, wl.value_cache, wl.num_kv_heads,
                   wl.scale, wl.block_tables, wl.seq_lens, wl.block_size, wl.max_seq_len)
         kw = dict(alibi_slopes=wl.alibi_slopes, kv_cache_dtype=wl.kv_cache_dtype,
-                  k_scale=wl.k_scale, v_scale=wl.v_scale, stream=stream)
+                  k_scale=wl.k_scale, v_scale=wl.v_scale, stream=stream,
+                  window_left=args.window, logits_soft_cap=args.softcap)
         if args.path == "v1":
             calls.append(lambda out=out, wl=wl, kw=kw: B.paged_attention_v1(
                 out, wl.query, wl.key_cache, wl.value_cache, wl.num_kv_heads, wl.scale,
@@ -261,7 +277,9 @@ def main() -> int:
     part_avg = float(part_ms.mean())
     achieved = ab["partition"] / (part_avg * 1e-3) / 1e9
     src_hash = kernel_source_hash()
-    traffic = read_traffic(base.name, src_hash, args.path) if copies > 1 else None
+    options = args.window != -1 or args.softcap != 0.0
+    traffic = (read_traffic(base.name, src_hash, args.path)
+               if copies > 1 and not options else None)
     dtype = {torch.float32: "f32", torch.float16: "f16", torch.bfloat16: "bf16"}[base.dtype]
     if base.kv_cache_dtype == "fp8_e4m3":
         dtype = f"{dtype} (fp8 e4m3 KV)"
@@ -286,8 +304,12 @@ def main() -> int:
                          f"num_heads={base.num_heads}, num_kv_heads={base.num_kv_heads}, "
                          f"head_size={base.head_size}, block_size={base.block_size}, "
                          f"seq_lens {int(lens.min())}..{int(lens.max())} "
-                         f"(sum {int(lens.sum())}), path={args.path}"),
+                         f"(sum {int(lens.sum())}), path={args.path}"
+                         + (f", window_left={args.window}, soft_cap={args.softcap:g}"
+                            if options else "")),
             "path": args.path,
+            "window_left": args.window,
+            "logits_soft_cap": args.softcap,
             "kv_bytes_per_step": ab["kv"],
             "inputs": ("cache-hot single copy" if copies == 1 else
                        f"{copies} rotating copies of the KV pool (L2/MALL-cold)"),
@@ -311,7 +333,7 @@ def main() -> int:
     }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle")
-        result["cpu_baseline"] = cpu_baseline(base, args.cpu_budget)
+        result["cpu_baseline"] = cpu_baseline(base, args.cpu_budget, args.window, args.softcap)
     print(json.dumps(result), flush=True)
     return 0
 

@@ -228,7 +228,9 @@ Params make_params(const Call &c, int cu, int head_groups) {
                      (c.mode == PA_MODE_V2 || (c.mode == PA_MODE_AUTO && p.auto_all_v2)) ? 1 : 0;
   p.scale_log2 = c.scale * c.k_scale * 1.4426950408889634f;
   p.v_scale = c.v_scale;
-  p.window_left = c.window_left;
+  // A window no sequence outgrows (W >= max_seq_len - 1) clips nothing: the
+  // kernels then run their window-free form.
+  p.window_left = (c.window_left >= 0 && c.window_left < c.max_seq_len - 1) ? c.window_left : -1;
   p.cap_on = c.logits_soft_cap > 0.0f ? 1 : 0;
   if (p.cap_on) {
     p.cap_in = (float)(2.0 * 1.4426950408889634 * (double)c.scale * (double)c.k_scale /

@@ -91,30 +91,40 @@ __device__ __forceinline__ unsigned pack2(float a, float b, _Float16) {
   return __builtin_bit_cast(unsigned, v);
 }
 
-// Whether token t lies in [lo, lo + span) (span >= 1): one unsigned compare.
+// Whether token t lies in [lo, lo + span) (span >= 1).  Without a sliding
+// window (WIN false) lo is at or before the first token a workgroup loads,
+// so only the upper bound is tested: one compare against a per-block scalar
+// instead of a subtraction and a compare per element.
+template <bool WIN>
 __device__ __forceinline__ bool in_span(int t, int lo, int span) {
-  return (unsigned)(t - lo) < (unsigned)span;
+  if constexpr (WIN) return (unsigned)(t - lo) < (unsigned)span;
+  else return t < lo + span;
 }
 
 // Keep-mask of a 32-bit word holding two 16-bit elements of tokens t, t + 1:
 // the half of a token outside [lo, lo + span) is cleared.  Straight-line
 // selects, so the window and tail masks can be applied on every step without
 // a divergent branch.
+template <bool WIN>
 __device__ __forceinline__ unsigned keep_pair_mask(int t, int lo, int span) {
-  return (in_span(t, lo, span) ? 0x0000FFFFu : 0u) | (in_span(t + 1, lo, span) ? 0xFFFF0000u : 0u);
+  return (in_span<WIN>(t, lo, span) ? 0x0000FFFFu : 0u) |
+         (in_span<WIN>(t + 1, lo, span) ? 0xFFFF0000u : 0u);
 }
 
 // A key's logit in log2 units, before the ALiBi term, from its dot product
-// with the query: scale * k_scale * q.K, or under a soft cap c
+// with the query: scale * k_scale * q.K, or under a soft cap c (CAP)
 // c * tanh(scale * k_scale * q.K / c), with tanh(y) = 1 - 2 / (exp(2y) + 1)
 // (an exp that overflows to +inf gives 1, one that underflows to 0 gives -1).
-// cap_on is uniform, so the branch is a scalar one.
+// The cap is a compile-time choice: a run-time branch here, even a uniform
+// one, splits the tile loop and costs the loads their overlap.
+template <bool CAP>
 __device__ __forceinline__ float scaled_logit(const Params &p, float dot) {
-  if (p.cap_on) {
+  if constexpr (CAP) {
     const float e = fast_exp2(dot * p.cap_in);
     return fmaf(-2.0f * p.cap_out, __builtin_amdgcn_rcpf(e + 1.0f), p.cap_out);
+  } else {
+    return dot * p.scale_log2;
   }
-  return dot * p.scale_log2;
 }
 
 template <typename T>

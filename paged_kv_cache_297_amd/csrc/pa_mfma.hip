@@ -4,11 +4,22 @@
 
 namespace pa {
 
+// The soft cap and the sliding window are compile-time variants.
+template <typename QT, typename KVT, int D, int BS>
+static hipError_t launch_opts(const Params &p, const Launch &l) {
+  const bool win = p.window_left >= 0;
+  if (p.cap_on)
+    return win ? launch_kernel(pa_partition_mfma<QT, KVT, D, BS, true, true>, l, p)
+               : launch_kernel(pa_partition_mfma<QT, KVT, D, BS, true, false>, l, p);
+  return win ? launch_kernel(pa_partition_mfma<QT, KVT, D, BS, false, true>, l, p)
+             : launch_kernel(pa_partition_mfma<QT, KVT, D, BS, false, false>, l, p);
+}
+
 template <typename QT, typename KVT>
 static hipError_t launch_mfma_t(const Params &p, int head_size, int block_size,
                                 const Launch &l) {
-#define PA_MFMA_CASE(D, BS) \
-  if (head_size == D && block_size == BS) return launch_kernel(pa_partition_mfma<QT, KVT, D, BS>, l, p);
+#define PA_MFMA_CASE(D, BS)                                                   \
+  if (head_size == D && block_size == BS) return launch_opts<QT, KVT, D, BS>(p, l);
   PA_MFMA_CASE(64, 16)
   PA_MFMA_CASE(64, 32)
   PA_MFMA_CASE(128, 16)

@@ -52,9 +52,10 @@ __device__ __forceinline__ f32x4 mfma_pv(const u32x4 &a, const u32x4 &b, const f
 
 // Zero the 16-bit elements of tokens outside [lo, lo + span) in an 8-token V
 // operand whose first element is token 0.
+template <bool WIN>
 __device__ __forceinline__ u32x4 mask_v8(u32x4 v, int lo, int span) {
-  return u32x4{v.x & keep_pair_mask(0, lo, span), v.y & keep_pair_mask(2, lo, span),
-               v.z & keep_pair_mask(4, lo, span), v.w & keep_pair_mask(6, lo, span)};
+  return u32x4{v.x & keep_pair_mask<WIN>(0, lo, span), v.y & keep_pair_mask<WIN>(2, lo, span),
+               v.z & keep_pair_mask<WIN>(4, lo, span), v.w & keep_pair_mask<WIN>(6, lo, span)};
 }
 
 // Regroups packed P (two 4-token pieces per lane: p0 from sub-tile 0, p1
@@ -89,7 +90,7 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-template <typename QT, typename KVT, int D, int BS>
+template <typename QT, typename KVT, int D, int BS, bool CAP, bool WIN>
 __global__ void __launch_bounds__(kThreads)
     __attribute__((amdgpu_waves_per_eu(mfma_waves_per_eu<KVT>())))
     pa_partition_mfma(const Params p) {
@@ -252,8 +253,8 @@ __global__ void __launch_bounds__(kThreads)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int t = t0 + 16 * h + 4 * g + e;
-        float v = scaled_logit(p, st[h][e]) + slope2 * (float)(t - it.w.t_ref);
-        v = in_span(t, it.w.t_lo, it.w.span) ? v : -__builtin_inff();
+        float v = scaled_logit<CAP>(p, st[h][e]) + slope2 * (float)(t - it.w.t_ref);
+        v = in_span<WIN>(t, it.w.t_lo, it.w.span) ? v : -__builtin_inff();
         x[h][e] = v;
         bm = fmaxf(bm, v);
       }
@@ -285,7 +286,7 @@ __global__ void __launch_bounds__(kThreads)
       } else {
         va = tl.v[t];
       }
-      va = mask_v8(va, vlo, it.w.span);
+      va = mask_v8<WIN>(va, vlo, it.w.span);
       oacc[t] = mfma_pv(va, pop, oacc[t] * alpha, PT());
     }
   };

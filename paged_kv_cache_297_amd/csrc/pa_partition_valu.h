@@ -53,9 +53,10 @@ struct ValuTraits<float, float> {
   }
   // Zero the V elements of tokens outside [lo, lo + span) (first = token of
   // element 0).
+  template <bool WIN>
   __device__ static void mask_v(unsigned (&w)[kPW], int first, int lo, int span) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) w[e] &= in_span(first + e, lo, span) ? ~0u : 0u;
+    for (int e = 0; e < 4; ++e) w[e] &= in_span<WIN>(first + e, lo, span) ? ~0u : 0u;
   }
 };
 
@@ -84,9 +85,10 @@ struct ValuTraits16 {
     for (int e = 0; e < 4; ++e) acc = dot2(acc, pw[e], vw[e], T16());
     return acc;
   }
+  template <bool WIN>
   __device__ static void mask_v(unsigned (&w)[kPW], int first, int lo, int span) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) w[e] &= keep_pair_mask(first + 2 * e, lo, span);
+    for (int e = 0; e < 4; ++e) w[e] &= keep_pair_mask<WIN>(first + 2 * e, lo, span);
   }
 };
 template <> struct ValuTraits<__bf16, __bf16> : ValuTraits16<__bf16> {};
@@ -128,9 +130,10 @@ struct ValuTraitsFp8 {
     return acc;
   }
   // Applied to the widened words: word e holds tokens first+2e, first+2e+1.
+  template <bool WIN>
   __device__ static void mask_v(unsigned (&w)[kPW], int first, int lo, int span) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) w[e] &= keep_pair_mask(first + 2 * e, lo, span);
+    for (int e = 0; e < 8; ++e) w[e] &= keep_pair_mask<WIN>(first + 2 * e, lo, span);
   }
 };
 template <> struct ValuTraits<__bf16, fp8e4m3> : ValuTraitsFp8<__bf16> {};
@@ -215,7 +218,7 @@ __device__ __forceinline__ float dim_group_sum(float v) {
 #define PA_VALU_OCCUPANCY
 #endif
 
-template <typename QT, typename KVT, int D, int BS, int GP>
+template <typename QT, typename KVT, int D, int BS, int GP, bool CAP, bool WIN>
 __global__ void __launch_bounds__(kThreads) PA_VALU_OCCUPANCY pa_partition_valu(const Params p) {
   using T = ValuTraits<QT, KVT>;
   using HM = HeadMap<GP, BS>;
@@ -332,8 +335,8 @@ __global__ void __launch_bounds__(kThreads) PA_VALU_OCCUPANCY pa_partition_valu(
     float alpha[NF], pj[NF];
 #pragma unroll
     for (int j = 0; j < NF; ++j) {
-      float x = scaled_logit(p, s[j]) + slope2[j] * (float)(t_abs - w.t_ref);
-      x = in_span(t_abs, w.t_lo, w.span) ? x : -__builtin_inff();
+      float x = scaled_logit<CAP>(p, s[j]) + slope2[j] * (float)(t_abs - w.t_ref);
+      x = in_span<WIN>(t_abs, w.t_lo, w.span) ? x : -__builtin_inff();
       const float bm = token_group_max<BS>(x);
       const float m_new = fmaxf(m_run[j], bm);
       alpha[j] = (m_new == -__builtin_inff()) ? 1.0f : fast_exp2(m_run[j] - m_new);
@@ -355,7 +358,7 @@ __global__ void __launch_bounds__(kThreads) PA_VALU_OCCUPANCY pa_partition_valu(
     for (int i = 0; i < NL; ++i) {
       unsigned vw[T::kPW];
       T::v_words(tl.v[i], vw);
-      T::mask_v(vw, tg * X, vlo, w.span);
+      T::template mask_v<WIN>(vw, tg * X, vlo, w.span);
 #pragma unroll
       for (int h = 0; h < GP; ++h) {
         const float a_h = a_bc[h];

@@ -16,7 +16,12 @@ constexpr int kv_bytes_of() {
 template <typename QT, typename KVT, int D, int BS, int GP>
 hipError_t launch_valu_one(const Params &p, const Launch &l) {
   if constexpr (GP <= valu_max_group(kv_bytes_of<QT, KVT>(), D, BS)) {
-    return launch_kernel(pa_partition_valu<QT, KVT, D, BS, GP>, l, p);
+    const bool win = p.window_left >= 0;
+    if (p.cap_on)
+      return win ? launch_kernel(pa_partition_valu<QT, KVT, D, BS, GP, true, true>, l, p)
+                 : launch_kernel(pa_partition_valu<QT, KVT, D, BS, GP, true, false>, l, p);
+    return win ? launch_kernel(pa_partition_valu<QT, KVT, D, BS, GP, false, true>, l, p)
+               : launch_kernel(pa_partition_valu<QT, KVT, D, BS, GP, false, false>, l, p);
   } else {
     return hipErrorInvalidValue;
   }
