@@ -72,7 +72,9 @@ def algorithmic_bytes(wl, path: str, cu: int, B, window_left: int = -1) -> dict:
     table = blocks * 4 + wl.num_seqs * 4
     # Partitions holding a key of the window.
     parts = np.where(lens > 0, (lens + 511) // 512 - t_lo // 512, 0)
-    if path == "v1":
+    if path in ("v1", "split"):
+        # split: the pieces' partials are scratch inside one launch, not part
+        # of the result; the minimum is that of v1.
         v2 = np.zeros_like(lens, dtype=bool)
     elif path == "v2":
         v2 = np.ones_like(lens, dtype=bool)
@@ -159,7 +161,7 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
-    ap.add_argument("--path", default="auto", choices=["auto", "v2", "v1"])
+    ap.add_argument("--path", default="auto", choices=["auto", "v2", "v1", "split"])
     ap.add_argument("--copies", type=int, default=4)
     ap.add_argument("--hot", action="store_true", help="one copy of the inputs (cache-hot)")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
@@ -219,6 +221,9 @@ def main() -> int:
             calls.append(lambda out=out, wl=wl, kw=kw: B.paged_attention_v1(
                 out, wl.query, wl.key_cache, wl.value_cache, wl.num_kv_heads, wl.scale,
                 wl.block_tables, wl.seq_lens, wl.block_size, wl.max_seq_len, **kw))
+        elif args.path == "split":
+            calls.append(B.PreparedCall("split", *common, **kw,
+                                        counters=B.split_counters(wl.num_seqs, wl.num_heads)))
         else:
             calls.append(B.PreparedCall(args.path, *common, **kw))
 
@@ -254,7 +259,7 @@ def main() -> int:
     torch.cuda.synchronize()
     B.set_timing_events()
     part_ms = np.array([e[0].elapsed_time(e[1]) for e in events])
-    if args.path == "v1" or not ab["any_v2"]:
+    if args.path in ("v1", "split") or not ab["any_v2"]:
         # No reduce kernel runs (an all-v1 auto call records its reduce events
         # back to back; their gap is event overhead, not work).
         red_ms = np.zeros(len(events))

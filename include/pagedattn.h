@@ -75,6 +75,7 @@
 #ifndef PAGEDATTN_H
 #define PAGEDATTN_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -255,6 +256,47 @@ pa_status paged_attention_reduce_ex(
     const void *tmp_out, int num_seqs, int num_heads, int num_kv_heads, int head_size,
     const int32_t *seq_lens, int max_seq_len, int max_num_partitions, pa_dtype dtype,
     const pa_decode_options *options, void *stream);
+
+/* ---------------------------------------------------------------------- */
+/* Balanced split (work decomposition for ragged batches)                 */
+/* ---------------------------------------------------------------------- */
+
+/* The decode of paged_attention_v2_ex with the work cut differently: each
+ * sequence's window is split into k <= 64 equal pieces of at least 512 keys
+ * (k = 1 for short sequences).  The piece size comes from the batch's shape
+ * (num_seqs, KV heads, the window-clipped max_seq_len, the device's compute
+ * units): a batch with at least two (sequence, KV head) items per compute
+ * unit has its longest sequences cut in about four; a smaller one is cut so
+ * that a full-length sequence gives about one piece per compute unit.  The
+ * piece that finishes last merges the k partial results with the V2 page's
+ * Phase 2 log-sum-exp rescale, inside the same kernel: one launch, no
+ * reduce phase.  Compared with paged_attention_auto it pays off on long or
+ * ragged batches (no tail of long single-workgroup sequences, no empty
+ * partition slots); on a batch whose sequences already fill the device
+ * once, the partial stores and merges cost more than they save.  The result equals the v1
+ * / v2 result up to rounding (each partial is rounded to the output type,
+ * as tmp_out is).
+ *
+ * exp_sums, max_logits and tmp_out (shapes as for v2) serve as scratch for
+ * the pieces: their contents after the call are unspecified.  counters is
+ * int32 [num_seqs, num_heads] (pa_split_counters_size bytes, 4-byte
+ * aligned) that must be all zero before the first call; every call leaves
+ * it all zero again.  Calls that share a counters buffer must not run
+ * concurrently.  Errors are those of paged_attention_v2_ex, plus
+ * PA_ERR_NULL_POINTER for counters == NULL and PA_ERR_MISALIGNED for a
+ * counters pointer that is not 4-byte aligned. */
+pa_status paged_attention_split(
+    void *out, float *exp_sums, float *max_logits, void *tmp_out, int32_t *counters,
+    const void *query, const void *key_cache, const void *value_cache,
+    int num_seqs, int num_heads, int num_kv_heads, int head_size, float scale,
+    const int32_t *block_tables, int max_num_blocks_per_seq, const int32_t *seq_lens,
+    int num_blocks, int block_size, int max_seq_len, int max_num_partitions,
+    const float *alibi_slopes, pa_dtype dtype, pa_kv_cache_dtype kv_cache_dtype,
+    float k_scale, float v_scale, const pa_decode_options *options, void *stream);
+
+/* Bytes of the counters buffer of paged_attention_split (0 for non-positive
+ * sizes). */
+size_t pa_split_counters_size(int num_seqs, int num_heads);
 
 /* ---------------------------------------------------------------------- */
 /* Helpers                                                                */

@@ -35,7 +35,8 @@ EXPORTED_SYMBOLS = (
     "paged_attention_v1", "paged_attention_v2", "paged_attention_auto",
     "paged_attention_partition", "paged_attention_reduce",
     "paged_attention_v1_ex", "paged_attention_v2_ex", "paged_attention_auto_ex",
-    "paged_attention_partition_ex", "paged_attention_reduce_ex", "pa_partition_size",
+    "paged_attention_partition_ex", "paged_attention_reduce_ex", "paged_attention_split",
+    "pa_split_counters_size", "pa_partition_size",
     "pa_num_partitions", "pa_should_use_v2", "pa_device_cu_count", "pa_set_timing_events",
     "pa_status_string", "pa_version",
 )
@@ -92,6 +93,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         ex = getattr(lib, name + "_ex")
         ex.argtypes = plain[:-1] + [_P, _P]
         ex.restype = _I
+    lib.paged_attention_split.argtypes = _PARTITION_ARGS[:4] + [_P] + _PARTITION_ARGS[4:-1] + [_P, _P]
+    lib.paged_attention_split.restype = _I
+    lib.pa_split_counters_size.argtypes = [_I, _I]
+    lib.pa_split_counters_size.restype = ctypes.c_size_t
     lib.pa_partition_size.argtypes = []
     lib.pa_partition_size.restype = _I
     lib.pa_num_partitions.argtypes = [_I]
@@ -250,6 +255,35 @@ def paged_attention_auto(out, exp_sums, max_logits, tmp_out, query, key_cache, v
     _call(lib, "paged_attention_auto", args, _options(window_left, logits_soft_cap))
 
 
+def split_counters(num_seqs: int, num_heads: int, device="cuda") -> torch.Tensor:
+    """A zeroed counters buffer for paged_attention_split (int32 [B, H])."""
+    return torch.zeros((num_seqs, num_heads), dtype=torch.int32, device=device)
+
+
+def _split_args(out, exp_sums, max_logits, tmp_out, counters, query, *rest, opts):
+    args = _v2_args(out, exp_sums, max_logits, tmp_out, query, *rest)
+    b, h = query.shape[0], query.shape[1]
+    if counters.dtype != torch.int32 or not counters.is_contiguous() or counters.numel() < b * h:
+        raise TypeError("counters must be a contiguous int32 tensor of num_seqs * num_heads")
+    ptr = None if opts is None else ctypes.addressof(opts)
+    return args[:4] + [counters.data_ptr()] + args[4:-1] + [ptr, args[-1]]
+
+
+def paged_attention_split(out, exp_sums, max_logits, tmp_out, counters, query, key_cache,
+                          value_cache, num_kv_heads, scale, block_tables, seq_lens, block_size,
+                          max_seq_len, alibi_slopes=None, kv_cache_dtype="auto", k_scale=1.0,
+                          v_scale=1.0, stream=None, window_left=-1, logits_soft_cap=0.0) -> None:
+    """Balanced split decode: writes ``out``; the partial buffers are scratch and
+    ``counters`` (split_counters) must be zero on entry (it is left zero)."""
+    lib = load_library()
+    opts = _options(window_left, logits_soft_cap)
+    args = _split_args(out, exp_sums, max_logits, tmp_out, counters, query, key_cache,
+                       value_cache, num_kv_heads, scale, block_tables, seq_lens, block_size,
+                       max_seq_len, alibi_slopes, kv_cache_dtype, k_scale, v_scale, stream,
+                       opts=opts)
+    _check(lib.paged_attention_split(*args), "paged_attention_split")
+
+
 class PreparedCall:
     """A v2 / auto call whose arguments were checked and marshalled once.
 
@@ -260,15 +294,27 @@ class PreparedCall:
     def __init__(self, mode, out, exp_sums, max_logits, tmp_out, query, key_cache, value_cache,
                  num_kv_heads, scale, block_tables, seq_lens, block_size, max_seq_len,
                  alibi_slopes=None, kv_cache_dtype="auto", k_scale=1.0, v_scale=1.0,
-                 stream=None, window_left=-1, logits_soft_cap=0.0):
+                 stream=None, window_left=-1, logits_soft_cap=0.0, counters=None):
         self.lib = load_library()
         self.name = f"paged_attention_{mode}"
-        if mode not in ("v2", "auto"):
-            raise ValueError("mode must be 'v2' or 'auto'")
+        if mode not in ("v2", "auto", "split"):
+            raise ValueError("mode must be 'v2', 'auto' or 'split'")
+        self.opts = _options(window_left, logits_soft_cap)
+        self.counters = counters
+        if mode == "split":
+            if counters is None:
+                raise ValueError("the split mode needs a counters buffer (split_counters)")
+            self.args = _split_args(out, exp_sums, max_logits, tmp_out, counters, query,
+                                    key_cache, value_cache, num_kv_heads, scale, block_tables,
+                                    seq_lens, block_size, max_seq_len, alibi_slopes,
+                                    kv_cache_dtype, k_scale, v_scale, stream, opts=self.opts)
+            self.fn = self.lib.paged_attention_split
+            self._keep = (out, exp_sums, max_logits, tmp_out, counters, query, key_cache,
+                          value_cache, block_tables, seq_lens, alibi_slopes)
+            return
         self.args = _v2_args(out, exp_sums, max_logits, tmp_out, query, key_cache, value_cache,
                              num_kv_heads, scale, block_tables, seq_lens, block_size, max_seq_len,
                              alibi_slopes, kv_cache_dtype, k_scale, v_scale, stream)
-        self.opts = _options(window_left, logits_soft_cap)
         if self.opts is None:
             self.fn = getattr(self.lib, self.name)
         else:

@@ -25,6 +25,8 @@ struct Tunables {
   int small_batch_factor = 1; // AUTO: v2 for all if B * Hkv < factor * CUs
   int tile_factor = 2;        // AUTO: v2 iff Hkv * ceil(L/512) > factor * CUs
   int parts_reversed = 1;     // all-v2 launches dispatch the last partition first
+  int split_reversed = 0;     // split launches dispatch the last piece slice first
+  int split_target = 0;       // split: fixed piece target in keys (0: the size rule)
 };
 
 int env_int(const char *name, int fallback, int lo, int hi) {
@@ -43,6 +45,8 @@ const Tunables &tunables() {
     x.small_batch_factor = env_int("PA_AUTO_SMALL_BATCH_FACTOR", x.small_batch_factor, 0, 1 << 20);
     x.tile_factor = env_int("PA_AUTO_TILE_FACTOR", x.tile_factor, 0, 1 << 20);
     x.parts_reversed = env_int("PA_PARTS_REVERSED", x.parts_reversed, 0, 1);
+    x.split_reversed = env_int("PA_SPLIT_REVERSED", x.split_reversed, 0, 1);
+    x.split_target = env_int("PA_SPLIT_TARGET", x.split_target, 0, 1 << 30);
     return x;
   }();
   return t;
@@ -106,6 +110,8 @@ struct Call {
   float k_scale, v_scale;
   int window_left;        // pa_decode_options (-1: no window)
   float logits_soft_cap;  // (0: no soft cap)
+  int32_t *counters;      // paged_attention_split only (mode is then V2 for validation)
+  bool split;
   hipStream_t stream;
 };
 
@@ -126,6 +132,40 @@ pa_status apply_options(const pa_decode_options *o, Call &c) {
 long long rule_length(const Call &c, long long L) {
   if (c.window_left >= 0 && L > (long long)c.window_left + 1) return (long long)c.window_left + 1;
   return L;
+}
+
+// Split mode: the piece target in keys, from host-known sizes only (the
+// lengths live on the device; L = the window-clipped max_seq_len).  A large
+// batch (B * gx >= 2 CUs: every CU already has two (sequence, head group)
+// items) only needs its long poles cut: target L / 4.  A smaller batch is
+// cut so that sequences of length L give about one piece per CU: target
+// B * L * gx / CUs (no cut when the items already fill the CUs once).  At
+// least kSplitMinPiece, rounded up to 512.  Measured on MI355X: cutting a
+// batch that already fills the CUs once (the GQA and fp8 workloads) costs
+// more in partial stores and merges than it gains in balance.
+int split_target(const Call &c, long long grid_x, int cu) {
+  if (tunables().split_target > 0)
+    return (tunables().split_target + 511) / 512 * 512 > pa::kSplitMinPiece
+               ? (tunables().split_target + 511) / 512 * 512
+               : pa::kSplitMinPiece;
+  const long long len = rule_length(c, c.max_seq_len);
+  const long long items = (long long)c.num_seqs * grid_x;
+  long long t = items >= 2LL * cu ? (len + 3) / 4 : (items * len + cu - 1) / cu;
+  t = t > pa::kSplitMinPiece ? t : pa::kSplitMinPiece;
+  t = (t + 511) / 512 * 512;
+  return (int)(t < (1LL << 30) ? t : (1LL << 30));
+}
+
+// Split mode: grid slices per sequence, enough for the pieces of the
+// longest window (its aligned start adds up to 31 keys); the kernel clamps
+// its piece count to the grid's depth.
+int split_grid_z(const Call &c, long long grid_x, int cu) {
+  const long long len = rule_length(c, c.max_seq_len) + 31;
+  const long long t = split_target(c, grid_x, cu);
+  long long z = (len + t - 1) / t;
+  if (z < 1) z = 1;
+  if (z > pa::kSplitMaxPieces) z = pa::kSplitMaxPieces;
+  return (int)z;
 }
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
@@ -152,6 +192,10 @@ pa_status validate_common(const Call &c, bool partition_phase) {
     if (!aligned16(c.tmp_out)) return PA_ERR_MISALIGNED;
     if (c.max_num_partitions < 1 || c.max_num_partitions < pa_num_partitions(c.max_seq_len))
       return PA_ERR_BAD_SHAPE;
+  }
+  if (c.split) {
+    if (!c.counters) return PA_ERR_NULL_POINTER;
+    if (((uintptr_t)c.counters & 3u) != 0) return PA_ERR_MISALIGNED;
   }
   if (!partition_phase) return PA_OK;
 
@@ -220,12 +264,18 @@ Params make_params(const Call &c, int cu, int head_groups) {
   p.max_seq_len = c.max_seq_len;
   p.max_num_partitions = c.max_num_partitions;
   p.head_groups = head_groups;
-  p.mode = (int)c.mode;
+  p.mode = c.split ? pa::kModeSplit : (int)c.mode;
+  p.counters = c.counters;
+  p.split_target = c.split ? split_target(c, (long long)c.num_kv_heads * head_groups, cu) : 0;
   const long long b_hkv = (long long)c.num_seqs * c.num_kv_heads;
   p.auto_all_v2 = b_hkv < (long long)tunables().small_batch_factor * cu ? 1 : 0;
   p.auto_tile_limit = tunables().tile_factor * cu;
-  p.parts_reversed = tunables().parts_reversed &&
-                     (c.mode == PA_MODE_V2 || (c.mode == PA_MODE_AUTO && p.auto_all_v2)) ? 1 : 0;
+  p.parts_reversed = c.split ? tunables().split_reversed
+                             : tunables().parts_reversed &&
+                                       (c.mode == PA_MODE_V2 ||
+                                        (c.mode == PA_MODE_AUTO && p.auto_all_v2))
+                                   ? 1
+                                   : 0;
   p.scale_log2 = c.scale * c.k_scale * 1.4426950408889634f;
   p.v_scale = c.v_scale;
   // A window no sequence outgrows (W >= max_seq_len - 1) clips nothing: the
@@ -261,11 +311,13 @@ pa_status run_partition(const Call &c) {
     return PA_ERR_BAD_SHAPE;
   if (c.num_seqs == 0) return PA_OK;
   int cu = 0;
-  if (c.mode == PA_MODE_AUTO) {
+  if (c.mode == PA_MODE_AUTO || c.split) {
     st = cu_count_current(&cu);
     if (st != PA_OK) return st;
   }
-  const int gz = (c.mode == PA_MODE_V1 || auto_all_v1(c, cu)) ? 1 : pa_num_partitions(c.max_seq_len);
+  const int gz = c.split ? split_grid_z(c, grid_x, cu)
+                 : (c.mode == PA_MODE_V1 || auto_all_v1(c, cu)) ? 1
+                                                                : pa_num_partitions(c.max_seq_len);
   const Params p = make_params(c, cu, pl.head_groups);
   const pa::Launch l{dim3((unsigned)grid_x, c.num_seqs, gz), c.stream, t_events.partition_start,
                      t_events.partition_stop};
@@ -345,6 +397,8 @@ Call make_call(pa_mode mode, void *out, float *exp_sums, float *max_logits, void
   c.v_scale = v_scale;
   c.window_left = -1;
   c.logits_soft_cap = 0.0f;
+  c.counters = nullptr;
+  c.split = false;
   c.stream = reinterpret_cast<hipStream_t>(stream);
   return c;
 }
@@ -536,6 +590,33 @@ pa_status paged_attention_auto(void *out, float *exp_sums, float *max_logits, vo
                    max_num_blocks_per_seq, seq_lens, num_blocks, block_size, max_seq_len,
                    max_num_partitions, alibi_slopes, dtype, kv_cache_dtype, k_scale, v_scale,
                    nullptr, stream);
+}
+
+pa_status paged_attention_split(void *out, float *exp_sums, float *max_logits, void *tmp_out,
+                                int32_t *counters, const void *query, const void *key_cache,
+                                const void *value_cache, int num_seqs, int num_heads,
+                                int num_kv_heads, int head_size, float scale,
+                                const int32_t *block_tables, int max_num_blocks_per_seq,
+                                const int32_t *seq_lens, int num_blocks, int block_size,
+                                int max_seq_len, int max_num_partitions,
+                                const float *alibi_slopes, pa_dtype dtype,
+                                pa_kv_cache_dtype kv_cache_dtype, float k_scale, float v_scale,
+                                const pa_decode_options *options, void *stream) {
+  Call c = make_call(PA_MODE_V2, out, exp_sums, max_logits, tmp_out, query, key_cache,
+                     value_cache, num_seqs, num_heads, num_kv_heads, head_size, scale,
+                     block_tables, max_num_blocks_per_seq, seq_lens, num_blocks, block_size,
+                     max_seq_len, max_num_partitions, alibi_slopes, dtype, kv_cache_dtype,
+                     k_scale, v_scale, stream);
+  c.split = true;
+  c.counters = counters;
+  const pa_status st = apply_options(options, c);
+  if (st != PA_OK) return st;
+  return run_partition(c);
+}
+
+size_t pa_split_counters_size(int num_seqs, int num_heads) {
+  if (num_seqs <= 0 || num_heads <= 0) return 0;
+  return (size_t)num_seqs * (size_t)num_heads * sizeof(int32_t);
 }
 
 pa_status pa_set_timing_events(void *partition_start, void *partition_stop, void *reduce_start,

@@ -14,7 +14,17 @@ constexpr int kPartitionSize = 512;
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 
-enum Mode : int { kModeV1 = 0, kModeV2 = 1, kModeAuto = 2 };
+// kModeSplit: balanced split of each sequence into equal pieces sized from
+// the batch's total length, merged in the partition kernel by the piece that
+// finishes last (paged_attention_split).
+enum Mode : int { kModeV1 = 0, kModeV2 = 1, kModeAuto = 2, kModeSplit = 3 };
+
+// Split mode: the piece target is at least this many keys, so every piece
+// but a sequence's only one spans at least 512 keys.
+constexpr int kSplitMinPiece = 1024;
+// Split mode: at most this many pieces per sequence (the merge keeps their
+// statistics in LDS).
+constexpr int kSplitMaxPieces = 64;
 
 // Minimum waves per SIMD the register allocator must allow (0: the kernel's
 // own choice).
@@ -53,6 +63,8 @@ struct Params {
   int cap_on;           // logit soft cap c > 0 in use
   float cap_in;         // 2 * log2(e) * scale * k_scale / c: exponent of exp(2 s / c)
   float cap_out;        // c * log2(e): the capped logit in log2 units
+  int *counters;        // split mode: [B, H] arrival counters, zero between calls
+  int split_target;     // split mode: keys per piece before equalising (multiple of 512)
 };
 
 // First key position inside the sliding window of a sequence of length

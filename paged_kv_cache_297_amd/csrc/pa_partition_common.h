@@ -20,6 +20,7 @@ namespace pa {
 
 struct Work {
   int seq, kvh, head0, nh;  // sequence, KV head, first query head, query heads in the group
+  int xslot;                // grid-x slot (KV head x head group)
   int L, n_part, part;      // sequence length, its partitions, this workgroup's partition
   int blk_begin, blk_end;   // logical blocks [blk_begin, blk_end) of this workgroup
   int t_ref;                // last token of this workgroup's range (ALiBi reference)
@@ -58,6 +59,16 @@ __device__ __forceinline__ void write_stat_empty(const Params &p, const Work &w,
   }
 }
 
+// Split mode: keys per piece for a sequence with `len` keys from its
+// 32-aligned start: k = ceil(len / split_target) pieces (at most max_pieces,
+// the grid's depth) of equal length rounded up to 32 keys.
+__device__ __forceinline__ int split_piece_len(const Params &p, int len, int max_pieces) {
+  int k = (len + p.split_target - 1) / p.split_target;
+  k = k < max_pieces ? k : max_pieces;
+  k = k > 1 ? k : 1;
+  return ((len + k - 1) / k + 31) / 32 * 32;
+}
+
 // Decodes one work item (sequence, grid-x slot = KV head x head group,
 // partition) into a Work.  Returns false when there is nothing (more) to
 // compute; sequences of length 0 (out = 0) and with an invalid length
@@ -68,6 +79,7 @@ template <typename QT, int D>
 __device__ __forceinline__ bool decode_work(const Params &p, int seq, int xslot, int part,
                                            int block_size, int group_slots, Work &w) {
   w.seq = seq;
+  w.xslot = xslot;
   w.kvh = xslot / p.head_groups;
   const int hg = xslot - w.kvh * p.head_groups;
   w.head0 = w.kvh * p.group + hg * group_slots;
@@ -75,7 +87,8 @@ __device__ __forceinline__ bool decode_work(const Params &p, int seq, int xslot,
   w.L = p.seq_lens[w.seq];
   const bool bad = (w.L < 0) || (w.L > p.max_seq_len);
   w.t_lo = bad ? 0 : window_first_token(p.window_left, w.L);
-  w.v2 = seq_uses_v2(p, bad ? 0 : w.L - w.t_lo);
+  const bool split = p.mode == kModeSplit;
+  w.v2 = !split && seq_uses_v2(p, bad ? 0 : w.L - w.t_lo);
   w.single = false;
   w.n_part = bad ? 0 : (w.L + kPartitionSize - 1) / kPartitionSize;
   w.part = part;
@@ -96,7 +109,23 @@ __device__ __forceinline__ bool decode_work(const Params &p, int seq, int xslot,
     return false;
   }
   const int n_logical = (w.L + block_size - 1) / block_size;
-  if (w.v2) {
+  if (split) {
+    // Pieces start on 32-key boundaries from the window's first aligned key;
+    // every piece but a sequence's only one spans at least 512 keys, so
+    // grid slices past len / 512 are empty without further work.
+    const int base = w.t_lo / 32 * 32;
+    const int len = w.L - base;
+    if (w.part * 512 >= len) return false;
+    const int piece = split_piece_len(p, len, (int)gridDim.z);
+    const int k = (len + piece - 1) / piece;
+    if (w.part >= k) return false;
+    w.n_part = k;
+    w.v2 = k > 1;  // partials, merged by the last piece to finish
+    const int t0 = base + w.part * piece, t1 = min(t0 + piece, w.L);
+    w.blk_begin = max(t0, w.t_lo) / block_size;
+    w.blk_end = (t1 + block_size - 1) / block_size;
+    w.t_ref = t1 - 1;
+  } else if (w.v2) {
     if (w.part >= w.n_part) return false;
     if (w.part == 0) write_stat_padding(p, w, w.n_part);
     const int part_lo = w.t_lo / kPartitionSize;  // first partition with a key in the window
@@ -130,49 +159,163 @@ __device__ __forceinline__ bool begin_work(const Params &p, int block_size, int 
   return decode_work<QT, D>(p, blockIdx.y, blockIdx.x, part, block_size, group_slots, w);
 }
 
-// Cross-wave merge and stores.  Wave wv left, for query head h of the group:
+// ---------------------------------------------------------------------------
+// Split mode: the pieces of one (sequence, grid-x slot) exchange their
+// partials through memory and an arrival counter.  The partials are stored
+// and loaded with device-scope relaxed atomics, which write through and read
+// past the non-coherent state of the per-XCD L2 caches, so no cache-wide
+// writeback or invalidate is needed (a device-scope fence costs one of
+// each, per wave); ordering comes from waiting for the stores to complete
+// before the workgroup barrier that precedes the arrival.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void coherent_store(void *ptr, unsigned v) {
+  __hip_atomic_store(reinterpret_cast<unsigned *>(ptr), v, __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ unsigned coherent_load(const void *ptr) {
+  return __hip_atomic_load(reinterpret_cast<const unsigned *>(ptr), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// One element of a partial row, rounded to QT, stored / loaded past the L2.
+template <typename QT>
+__device__ __forceinline__ void coherent_store_elem(QT *ptr, float v) {
+  if constexpr (sizeof(QT) == 4) {
+    coherent_store(ptr, f_bits(v));
+  } else {
+    __hip_atomic_store(reinterpret_cast<unsigned short *>(ptr),
+                       __builtin_bit_cast(unsigned short, from_f32<QT>(v)), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+template <typename QT>
+__device__ __forceinline__ float coherent_load_elem(const QT *ptr) {
+  if constexpr (sizeof(QT) == 4) {
+    return bits_f(coherent_load(ptr));
+  } else {
+    return to_f32(__builtin_bit_cast(
+        QT, __hip_atomic_load(reinterpret_cast<const unsigned short *>(ptr), __ATOMIC_RELAXED,
+                              __HIP_MEMORY_SCOPE_AGENT)));
+  }
+}
+
+// After a piece's partials are stored (slot = piece): the piece that
+// arrives last at the (sequence, grid-x slot) counter merges the k pieces
+// with the log-sum-exp rescale of the V2 page's Phase 2, writes out, and
+// resets the counter to zero for the next call.
+template <typename QT, int D>
+__device__ __forceinline__ void split_merge(const Params &p, const Work &w) {
+  __shared__ int sm_last;
+  __shared__ float sm_pm[16][kSplitMaxPieces], sm_ps[16][kSplitMaxPieces];
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's partial stores are done
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int *ctr = p.counters + (size_t)w.seq * p.num_heads + w.xslot;
+    const int last =
+        __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+        w.n_part - 1;
+    if (last) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    sm_last = last;
+  }
+  __syncthreads();
+  if (!sm_last) return;
+  const size_t row0 = ((size_t)w.seq * p.num_heads + w.head0) * p.max_num_partitions;
+  for (int idx = threadIdx.x; idx < w.nh * w.n_part; idx += kThreads) {
+    const int h = idx / w.n_part, c = idx - h * w.n_part;
+    const size_t r = row0 + (size_t)h * p.max_num_partitions + c;
+    sm_pm[h][c] = bits_f(coherent_load(p.max_logits + r));
+    sm_ps[h][c] = bits_f(coherent_load(p.exp_sums + r));
+  }
+  __syncthreads();
+  const QT *to = reinterpret_cast<const QT *>(p.tmp_out);
+  const float ninf = -__builtin_inff();
+  for (int idx = threadIdx.x; idx < w.nh * D; idx += kThreads) {
+    const int h = idx / D, d = idx - h * D;
+    float big_m = ninf;
+    bool nan_seen = false;
+    for (int c = 0; c < w.n_part; ++c) {
+      nan_seen |= sm_pm[h][c] != sm_pm[h][c];
+      big_m = fmaxf(big_m, sm_pm[h][c]);
+    }
+    const QT *col = to + (row0 + (size_t)h * p.max_num_partitions) * D + d;
+    float s = 0.0f, a = 0.0f;
+#pragma unroll 4
+    for (int c = 0; c < w.n_part; ++c) {
+      const float m = sm_pm[h][c];
+      const float r = m == ninf ? 0.0f : fast_exp2((m - big_m) * kLog2e) * sm_ps[h][c];
+      const float o = coherent_load_elem<QT>(col + (size_t)c * D);
+      s += r;
+      a = m == ninf ? a : fmaf(r, o, a);
+    }
+    store_out_row<QT, D>(p, w.seq, w.head0 + h, d, nan_seen ? __builtin_nanf("") : a / s);
+  }
+}
+
+// One element of a workgroup's result.  Wave wv left, for query head h of
+// the group:
 //   sm_m[wv][h]  its running max (log2 units; -inf if it saw no token)
 //   sm_l[wv][h]  sum of exp2(s - m) over its tokens
 //   sm_o[wv][h][d] sum of exp2(s - m) * V[d] over its tokens
 // The workgroup result is the log-sum-exp combination of the four waves
-// (the same rescale as the V2 page's Phase 2, applied inside one partition).
-// A NaN in sm_l (an out-of-range block-table entry) makes every output of
-// the head NaN.  Must be called after a __syncthreads() that follows the LDS
-// writes.
+// (the same rescale as the V2 page's Phase 2, applied inside one partition):
+// the normalised output o, the sum and the max logit ml (natural log units).
+// A NaN in sm_l (an out-of-range block-table entry) makes o and ml NaN.
+template <int GS, int OSTRIDE>
+__device__ __forceinline__ float wave_merge(const Params &p, const Work &w,
+                                            const float (*sm_o)[GS][OSTRIDE],
+                                            const float (*sm_m)[GS], const float (*sm_l)[GS],
+                                            int h, int d, float &sum, float &ml) {
+  float big_m = -__builtin_inff();
+#pragma unroll
+  for (int wv = 0; wv < kWaves; ++wv) big_m = fmaxf(big_m, sm_m[wv][h]);
+  sum = 0.0f;
+  float acc = 0.0f;
+#pragma unroll
+  for (int wv = 0; wv < kWaves; ++wv) {
+    const float mw = sm_m[wv][h];
+    const float c = (mw == -__builtin_inff()) ? 0.0f : fast_exp2(mw - big_m);
+    sum += c * sm_l[wv][h];
+    acc += c * sm_o[wv][h][d];
+  }
+  float o = acc / sum * p.v_scale;
+  const int head = w.head0 + h;
+  // The kernels add ALiBi as slope * (t - t_ref), t_ref the last token of the
+  // workgroup's range (softmax inside the range is unchanged by the shift,
+  // and the tokens that carry weight keep small, precise logits); the stored
+  // max logit is in the absolute-position convention slope * t.
+  // One rounding: the product slope * t_ref is exact inside the fma.
+  ml = p.alibi_slopes ? fmaf(p.alibi_slopes[head], (float)w.t_ref, big_m * kLn2) : big_m * kLn2;
+  // A wave that met an out-of-range block-table entry reports a NaN sum.
+  if (sum != sum) {
+    o = __builtin_nanf("");
+    ml = __builtin_nanf("");
+  }
+  return o;
+}
+
+// Cross-wave merge and stores of a workgroup's result: out directly (v1, a
+// single partition or piece), the partials of a v2 partition, or a split
+// piece's partials followed by the arrival at its counter.  Must be called
+// after a __syncthreads() that follows the LDS writes.
 template <typename QT, int D, int GS, int OSTRIDE>
 __device__ __forceinline__ void finish_partition(const Params &p, const Work &w,
                                                  const float (*sm_o)[GS][OSTRIDE],
                                                  const float (*sm_m)[GS],
                                                  const float (*sm_l)[GS]) {
-  const float nanv = __builtin_nanf("");
+  const bool split = p.mode == kModeSplit;
   for (int idx = threadIdx.x; idx < w.nh * D; idx += kThreads) {
     const int h = idx / D, d = idx - h * D;
-    float big_m = -__builtin_inff();
-#pragma unroll
-    for (int wv = 0; wv < kWaves; ++wv) big_m = fmaxf(big_m, sm_m[wv][h]);
-    float sum = 0.0f, acc = 0.0f;
-#pragma unroll
-    for (int wv = 0; wv < kWaves; ++wv) {
-      const float mw = sm_m[wv][h];
-      const float c = (mw == -__builtin_inff()) ? 0.0f : fast_exp2(mw - big_m);
-      sum += c * sm_l[wv][h];
-      acc += c * sm_o[wv][h][d];
-    }
-    float o = acc / sum * p.v_scale;
+    float sum, ml;
+    const float o = wave_merge<GS, OSTRIDE>(p, w, sm_o, sm_m, sm_l, h, d, sum, ml);
     const int head = w.head0 + h;
-    // The kernels add ALiBi as slope * (t - t_ref), t_ref the last token of the
-    // workgroup's range (softmax inside the range is unchanged by the shift,
-    // and the tokens that carry weight keep small, precise logits); the stored
-    // max logit is in the absolute-position convention slope * t.
-    // One rounding: the product slope * t_ref is exact inside the fma.
-    float ml = p.alibi_slopes ? fmaf(p.alibi_slopes[head], (float)w.t_ref, big_m * kLn2)
-                              : big_m * kLn2;
-    // A wave that met an out-of-range block-table entry reports a NaN sum.
-    if (sum != sum) {
-      o = nanv;
-      ml = nanv;
-    }
-    if (w.v2) {
+    if (w.v2 && split) {
+      const size_t row = ((size_t)w.seq * p.num_heads + head) * p.max_num_partitions + w.part;
+      coherent_store_elem<QT>(reinterpret_cast<QT *>(p.tmp_out) + row * D + d, o);
+      if (d == 0) {
+        coherent_store(p.exp_sums + row, f_bits(sum));
+        coherent_store(p.max_logits + row, f_bits(ml));
+      }
+    } else if (w.v2) {
       const size_t row = ((size_t)w.seq * p.num_heads + head) * p.max_num_partitions + w.part;
       reinterpret_cast<QT *>(p.tmp_out)[row * D + d] = from_f32<QT>(o);
       if (d == 0) {
@@ -184,6 +327,7 @@ __device__ __forceinline__ void finish_partition(const Params &p, const Work &w,
       store_out_row<QT, D>(p, w.seq, head, d, o);
     }
   }
+  if (split && w.v2) split_merge<QT, D>(p, w);
 }
 
 }  // namespace pa

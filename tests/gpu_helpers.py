@@ -40,6 +40,11 @@ def run(wl: W.Workload, path: str, poison_outputs: bool = True, window_left: int
               logits_soft_cap=soft_cap)
     if path == "v1":
         B.paged_attention_v1(out, *args, **kw)
+    elif path == "split":
+        counters = B.split_counters(wl.num_seqs, wl.num_heads, device=out.device)
+        B.paged_attention_split(out, es, ml, to, counters, *args, **kw)
+        torch.cuda.synchronize()
+        assert int(counters.abs().sum().item()) == 0, "split counters not left at zero"
     elif path == "v2":
         B.paged_attention_v2(out, es, ml, to, *args, **kw)
     elif path == "auto":
@@ -48,7 +53,7 @@ def run(wl: W.Workload, path: str, poison_outputs: bool = True, window_left: int
         raise ValueError(path)
     torch.cuda.synchronize()
     res = {"out": out.float().cpu().numpy().astype(np.float64)}
-    if path != "v1":
+    if path not in ("v1", "split"):
         res["exp_sums"] = es.cpu().numpy().astype(np.float64)
         res["max_logits"] = ml.cpu().numpy().astype(np.float64)
         res["tmp_out"] = to.float().cpu().numpy().astype(np.float64)
@@ -107,7 +112,9 @@ def check_close(got, ref, tol, what, extra_atol=0.0):
 
 
 def merge_bound(wl: W.Workload, ref: dict, s: int) -> float:
-    """Extra error of the merged output that the max_logits contract implies.
+    """Extra error of the merged output that the max_logits contract implies
+    (also for the split path's longer pieces: the largest stored max logit
+    is no larger, the spread of the piece outputs no wider).
 
     max_logits hold absolute-position ALiBi logits in fp32, so each stored
     m_p is off by up to half an ulp of |m_p| (about slope * L); the weights
@@ -151,8 +158,8 @@ def check_against_oracle(wl: W.Workload, res: dict, ref: dict, seqs, path: str,
         for s, e in zip(seqs, extra):
             check_close(res["out"][s], ref["out_v1"][s], tol, f"{wl.name}/{path} out seq {s}",
                         extra_atol=e)
-    if path == "v1":
-        return
+    if path in ("v1", "split"):
+        return   # no partials (split: they are scratch)
     # Partials of sequences on the v2 path.
     v2 = [s for s in seqs if path == "v2" or uses_v2(wl, s, window_left)]
     if not v2:

@@ -271,3 +271,35 @@ def test_reduce_ex_options():
         assert lib.paged_attention_reduce_ex(*base, opts(w, cap), None) == BADARG
     bad = list(base); bad[8] = 80
     assert lib.paged_attention_reduce_ex(*bad, opts(3, 0.0), None) == UNSUP
+
+
+# --------------------------------------------------------------------------
+# Balanced split entry point
+# --------------------------------------------------------------------------
+
+def split_args(counters=A, options=None, **kw):
+    a = v2_args(**kw)
+    return a[:4] + [counters] + a[4:-1] + [options, a[-1]]
+
+
+@pytest.mark.parametrize("kw,status", CASES)
+def test_split_validation_follows_v2(kw, status):
+    lib = B.load_library()
+    assert lib.paged_attention_split(*split_args(**kw)) == status
+
+
+def test_split_counters_checks():
+    lib = B.load_library()
+    assert lib.paged_attention_split(*split_args(counters=None)) == NULLP
+    assert lib.paged_attention_split(*split_args(counters=A + 2)) == MISAL
+    assert lib.paged_attention_split(*split_args(counters=A + 4, num_seqs=0)) == OK
+    assert lib.paged_attention_split(*split_args(options=opts(-5, 0.0))) == BADARG
+    assert lib.paged_attention_split(*split_args(options=opts(100, 30.0), num_seqs=0)) == OK
+
+
+def test_split_counters_size():
+    lib = B.load_library()
+    assert lib.pa_split_counters_size(3, 4) == 48
+    assert lib.pa_split_counters_size(0, 4) == 0
+    assert lib.pa_split_counters_size(5, -1) == 0
+    assert lib.pa_split_counters_size(65535, 128) == 65535 * 128 * 4
