@@ -299,6 +299,50 @@ pa_status paged_attention_split(
 size_t pa_split_counters_size(int num_seqs, int num_heads);
 
 /* ---------------------------------------------------------------------- */
+/* Paged prefill                                                          */
+/* ---------------------------------------------------------------------- */
+
+/* Options of paged_prefill (the dispatch page's AttnDispatchConfig fields
+ * is_causal, window_left, window_right, softcap; NULL = causal, no window,
+ * no cap, the page's defaults). */
+typedef struct pa_prefill_options {
+  int causal;             /* nonzero: a query sees no key after its position */
+  int window_left;        /* -1: unbounded; W >= 0: keys t >= p - W only     */
+  int window_right;       /* -1: unbounded; W >= 0: keys t <= p + W only     */
+  float logits_soft_cap;  /* 0: off; c > 0: logit -> c * tanh(logit / c)    */
+} pa_prefill_options;
+
+/* Prefill attention over a paged cache (dispatch page, dispatch_prefill:
+ * flash attention with block tables and cumulative sequence offsets).
+ * Sequence b owns the query rows cu_seq_q[b] .. cu_seq_q[b+1] - 1 (nq_b rows)
+ * and nk_b = cu_seq_k[b+1] - cu_seq_k[b] keys, key t in slot t % block_size
+ * of block block_tables[b, t / block_size].  The queries are the last nq_b
+ * positions of the sequence: query i sits at p = nk_b - nq_b + i, and sees key
+ * t iff (!causal || t <= p) and the window bounds hold.  Logits are
+ * scale * q . k (soft-capped when asked); the output row is the softmax-
+ * weighted sum of the visible values, or zero when no key is visible.
+ * Query head h reads KV head h / (num_heads / num_kv_heads).
+ *
+ * Layouts (contiguous, device memory): query, out [total_q, num_heads,
+ * head_size] dtype; key_cache, value_cache [num_blocks, num_kv_heads,
+ * block_size, head_size] dtype (the page's prefill layout, different from
+ * the decode layout); block_tables int32 [num_seqs, max_num_blocks_per_seq];
+ * cu_seq_q, cu_seq_k int32 [num_seqs + 1].  max_seq_q / max_seq_k bound the
+ * per-sequence query / key counts (host integers).
+ *
+ * Supported: dtype f16 / bf16 (f32: PA_ERR_UNSUPPORTED); head_size 64 or 128;
+ * block_size 16 or 32; num_heads / num_kv_heads <= 64.  Errors as for the
+ * decode calls; cu_seq_* entries that break max_seq_q / max_seq_k / total_q,
+ * and block-table entries outside [0, num_blocks), give NaN rows for that
+ * sequence (rows past max_seq_q are not written).  Accumulation is fp32. */
+pa_status paged_prefill(
+    void *out, const void *query, const void *key_cache, const void *value_cache,
+    int total_q, int num_seqs, int num_heads, int num_kv_heads, int head_size, float scale,
+    const int32_t *block_tables, int max_num_blocks_per_seq, const int32_t *cu_seq_q,
+    const int32_t *cu_seq_k, int max_seq_q, int max_seq_k, int num_blocks, int block_size,
+    pa_dtype dtype, const pa_prefill_options *options, void *stream);
+
+/* ---------------------------------------------------------------------- */
 /* Helpers                                                                */
 /* ---------------------------------------------------------------------- */
 

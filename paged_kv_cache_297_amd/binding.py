@@ -36,10 +36,16 @@ EXPORTED_SYMBOLS = (
     "paged_attention_partition", "paged_attention_reduce",
     "paged_attention_v1_ex", "paged_attention_v2_ex", "paged_attention_auto_ex",
     "paged_attention_partition_ex", "paged_attention_reduce_ex", "paged_attention_split",
-    "pa_split_counters_size", "pa_partition_size",
+    "pa_split_counters_size", "paged_prefill", "pa_partition_size",
     "pa_num_partitions", "pa_should_use_v2", "pa_device_cu_count", "pa_set_timing_events",
     "pa_status_string", "pa_version",
 )
+
+
+class PrefillOptions(ctypes.Structure):
+    """pa_prefill_options: causal flag, left / right window (-1: none), soft cap (0: none)."""
+    _fields_ = [("causal", ctypes.c_int), ("window_left", ctypes.c_int),
+                ("window_right", ctypes.c_int), ("logits_soft_cap", ctypes.c_float)]
 
 
 class DecodeOptions(ctypes.Structure):
@@ -95,6 +101,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         ex.restype = _I
     lib.paged_attention_split.argtypes = _PARTITION_ARGS[:4] + [_P] + _PARTITION_ARGS[4:-1] + [_P, _P]
     lib.paged_attention_split.restype = _I
+    lib.paged_prefill.argtypes = [_P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P, _I, _P, _P, _I, _I,
+                                  _I, _I, _I, _P, _P]
+    lib.paged_prefill.restype = _I
     lib.pa_split_counters_size.argtypes = [_I, _I]
     lib.pa_split_counters_size.restype = ctypes.c_size_t
     lib.pa_partition_size.argtypes = []
@@ -355,6 +364,69 @@ def paged_attention_reduce(mode, out, exp_sums, max_logits, tmp_out, seq_lens, n
             tmp_out.data_ptr(), b, h, num_kv_heads, d, seq_lens.data_ptr(), int(max_seq_len), p,
             DTYPE_CODE[out.dtype], _stream(stream)]
     _call(lib, "paged_attention_reduce", args, _options(window_left, 0.0))
+
+
+def _prefill_args(out, query, key_cache, value_cache, num_kv_heads, scale, block_tables,
+                  cu_seq_q, cu_seq_k, max_seq_q, max_seq_k, stream, opts):
+    for name, t in (("out", out), ("query", query), ("key_cache", key_cache),
+                    ("value_cache", value_cache), ("block_tables", block_tables),
+                    ("cu_seq_q", cu_seq_q), ("cu_seq_k", cu_seq_k)):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if query.dtype not in DTYPE_CODE:
+        raise TypeError("query must be float16 or bfloat16")
+    if key_cache.dtype != query.dtype or value_cache.dtype != query.dtype or out.dtype != query.dtype:
+        raise TypeError("out and the caches must have the query dtype")
+    for name, t in (("block_tables", block_tables), ("cu_seq_q", cu_seq_q), ("cu_seq_k", cu_seq_k)):
+        if t.dtype != torch.int32:
+            raise TypeError(f"{name} must be int32")
+    total_q, h, d = query.shape
+    nb, hkv, bs, dk = key_cache.shape
+    if hkv != num_kv_heads or dk != d or tuple(value_cache.shape) != tuple(key_cache.shape):
+        raise ValueError("caches must be [num_blocks, num_kv_heads, block_size, head_size]")
+    if out.shape != query.shape:
+        raise ValueError("out must be shaped like query")
+    b = block_tables.shape[0]
+    if cu_seq_q.shape != (b + 1,) or cu_seq_k.shape != (b + 1,):
+        raise ValueError("cu_seq_q / cu_seq_k must be [num_seqs + 1]")
+    ptr = None if opts is None else ctypes.addressof(opts)
+    return [out.data_ptr(), query.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(),
+            total_q, b, h, num_kv_heads, d, float(scale), block_tables.data_ptr(),
+            block_tables.shape[1], cu_seq_q.data_ptr(), cu_seq_k.data_ptr(), int(max_seq_q),
+            int(max_seq_k), nb, bs, DTYPE_CODE[query.dtype], ptr, _stream(stream)]
+
+
+def paged_prefill(out, query, key_cache, value_cache, num_kv_heads, scale, block_tables,
+                  cu_seq_q, cu_seq_k, max_seq_q, max_seq_k, causal=True, window_left=-1,
+                  window_right=-1, logits_soft_cap=0.0, stream=None) -> None:
+    """Paged prefill attention (pa_prefill_options from the keyword arguments);
+    writes ``out`` in place."""
+    lib = load_library()
+    opts = PrefillOptions(1 if causal else 0, int(window_left), int(window_right),
+                          float(logits_soft_cap))
+    args = _prefill_args(out, query, key_cache, value_cache, num_kv_heads, scale, block_tables,
+                         cu_seq_q, cu_seq_k, max_seq_q, max_seq_k, stream, opts)
+    _check(lib.paged_prefill(*args), "paged_prefill")
+
+
+class PreparedPrefill:
+    """A paged_prefill call marshalled once (see PreparedCall)."""
+
+    def __init__(self, out, query, key_cache, value_cache, num_kv_heads, scale, block_tables,
+                 cu_seq_q, cu_seq_k, max_seq_q, max_seq_k, causal=True, window_left=-1,
+                 window_right=-1, logits_soft_cap=0.0, stream=None):
+        self.lib = load_library()
+        self.opts = PrefillOptions(1 if causal else 0, int(window_left), int(window_right),
+                                   float(logits_soft_cap))
+        self.args = _prefill_args(out, query, key_cache, value_cache, num_kv_heads, scale,
+                                  block_tables, cu_seq_q, cu_seq_k, max_seq_q, max_seq_k, stream,
+                                  self.opts)
+        self._keep = (out, query, key_cache, value_cache, block_tables, cu_seq_q, cu_seq_k)
+
+    def __call__(self) -> None:
+        st = self.lib.paged_prefill(*self.args)
+        if st != PA_OK:
+            _check(st, "paged_prefill")
 
 
 def partition_size() -> int:

@@ -11,6 +11,7 @@
 #include "../../include/pagedattn.h"
 #include "pa_launch.h"
 #include "pa_params.h"
+#include "pa_prefill.h"
 
 namespace {
 
@@ -612,6 +613,77 @@ pa_status paged_attention_split(void *out, float *exp_sums, float *max_logits, v
   const pa_status st = apply_options(options, c);
   if (st != PA_OK) return st;
   return run_partition(c);
+}
+
+pa_status paged_prefill(void *out, const void *query, const void *key_cache,
+                        const void *value_cache, int total_q, int num_seqs, int num_heads,
+                        int num_kv_heads, int head_size, float scale, const int32_t *block_tables,
+                        int max_num_blocks_per_seq, const int32_t *cu_seq_q,
+                        const int32_t *cu_seq_k, int max_seq_q, int max_seq_k, int num_blocks,
+                        int block_size, pa_dtype dtype, const pa_prefill_options *options,
+                        void *stream) {
+  pa_prefill_options o{1, -1, -1, 0.0f};
+  if (options) o = *options;
+  if (dtype != PA_DTYPE_F32 && dtype != PA_DTYPE_F16 && dtype != PA_DTYPE_BF16)
+    return PA_ERR_BAD_ARGUMENT;
+  if (o.window_left < -1 || o.window_right < -1 || !isfinite(o.logits_soft_cap) ||
+      o.logits_soft_cap < 0.0f || !isfinite(scale))
+    return PA_ERR_BAD_ARGUMENT;
+  if (o.logits_soft_cap > 0.0f &&
+      !isfinite((float)((double)scale / (double)o.logits_soft_cap)))
+    return PA_ERR_BAD_ARGUMENT;
+  if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || total_q < 0 || max_seq_q < 0 ||
+      max_seq_k < 0 || max_num_blocks_per_seq < 0 || num_blocks < 0)
+    return PA_ERR_BAD_SHAPE;
+  if (num_heads % num_kv_heads != 0) return PA_ERR_BAD_SHAPE;
+  const int group = num_heads / num_kv_heads;
+  if (group > pa::kPrefillCols) return PA_ERR_UNSUPPORTED;
+  if (num_seqs > kMaxGridYZ || num_kv_heads > kMaxGridYZ) return PA_ERR_BAD_SHAPE;
+  if (dtype == PA_DTYPE_F32) return PA_ERR_UNSUPPORTED;
+  if (head_size != 64 && head_size != 128) return PA_ERR_UNSUPPORTED;
+  if (block_size != 16 && block_size != 32) return PA_ERR_UNSUPPORTED;
+  if (!out || !query || !key_cache || !value_cache || !block_tables || !cu_seq_q || !cu_seq_k)
+    return PA_ERR_NULL_POINTER;
+  if (!aligned16(out) || !aligned16(query) || !aligned16(key_cache) || !aligned16(value_cache))
+    return PA_ERR_MISALIGNED;
+  if ((long long)max_num_blocks_per_seq * block_size < max_seq_k) return PA_ERR_BAD_SHAPE;
+  if (max_seq_k > 0 && num_blocks < 1) return PA_ERR_BAD_SHAPE;
+  if (num_seqs == 0 || total_q == 0 || max_seq_q == 0) return PA_OK;
+  pa::PrefillParams p{};
+  p.out = out;
+  p.query = query;
+  p.key_cache = key_cache;
+  p.value_cache = value_cache;
+  p.block_tables = block_tables;
+  p.cu_seq_q = cu_seq_q;
+  p.cu_seq_k = cu_seq_k;
+  p.total_q = total_q;
+  p.num_seqs = num_seqs;
+  p.num_heads = num_heads;
+  p.num_kv_heads = num_kv_heads;
+  p.group = group;
+  p.max_num_blocks_per_seq = max_num_blocks_per_seq;
+  p.num_blocks = num_blocks;
+  p.max_seq_q = max_seq_q;
+  p.max_seq_k = max_seq_k;
+  p.q_tile = pa::kPrefillCols / group;
+  const long long tiles = ((long long)max_seq_q + p.q_tile - 1) / p.q_tile;
+  if (tiles > 0x7fffffffLL) return PA_ERR_BAD_SHAPE;
+  p.num_q_tiles = (int)tiles;
+  p.causal = o.causal ? 1 : 0;
+  p.window_left = o.window_left;
+  p.window_right = o.window_right;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  const bool cap = o.logits_soft_cap > 0.0f;
+  if (cap) {
+    p.cap_in = (float)(2.0 * 1.4426950408889634 * (double)scale / (double)o.logits_soft_cap);
+    p.cap_out = (float)((double)o.logits_soft_cap * 1.4426950408889634);
+  }
+  const pa::Launch l{dim3((unsigned)tiles, num_kv_heads, num_seqs),
+                     reinterpret_cast<hipStream_t>(stream), t_events.partition_start,
+                     t_events.partition_stop};
+  const hipError_t e = pa::launch_prefill(p, (int)dtype, head_size, block_size, cap, l);
+  return e == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
 size_t pa_split_counters_size(int num_seqs, int num_heads) {

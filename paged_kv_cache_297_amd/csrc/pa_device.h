@@ -117,8 +117,8 @@ __device__ __forceinline__ unsigned keep_pair_mask(int t, int lo, int span) {
 // (an exp that overflows to +inf gives 1, one that underflows to 0 gives -1).
 // The cap is a compile-time choice: a run-time branch here, even a uniform
 // one, splits the tile loop and costs the loads their overlap.
-template <bool CAP>
-__device__ __forceinline__ float scaled_logit(const Params &p, float dot) {
+template <bool CAP, typename P>
+__device__ __forceinline__ float scaled_logit(const P &p, float dot) {
   if constexpr (CAP) {
     const float e = fast_exp2(dot * p.cap_in);
     return fmaf(-2.0f * p.cap_out, __builtin_amdgcn_rcpf(e + 1.0f), p.cap_out);

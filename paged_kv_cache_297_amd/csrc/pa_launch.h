@@ -20,8 +20,8 @@ struct Launch {
   hipEvent_t start, stop;
 };
 
-template <typename Kernel>
-hipError_t launch_kernel(Kernel kernel, const Launch &l, const Params &p) {
+template <typename Kernel, typename P>
+hipError_t launch_kernel(Kernel kernel, const Launch &l, const P &p) {
   if (l.start && l.stop)
     hipExtLaunchKernelGGL(kernel, l.grid, dim3(kThreads), 0, l.stream, l.start, l.stop, 0, p);
   else

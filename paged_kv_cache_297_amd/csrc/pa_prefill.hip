@@ -1,0 +1,268 @@
+// Paged prefill attention (page "Layer 3: Attention prefill/decode dispatch",
+// dispatch_prefill: flash attention over variable-length sequences whose keys
+// and values are read through block tables from a [num_blocks, Hkv, bs, D]
+// cache, with cumulative query / key offsets, a causal flag, a left / right
+// window and a logit soft cap).  The queries of a sequence are its last nq
+// positions: query token i sits at position nk - nq + i.
+//
+// A workgroup owns 64 query columns -- (query token, query head) pairs of one
+// KV head, 16 per wave -- and walks the keys its columns can see in steps of
+// 32.  Each step's K and V tiles are loaded once per workgroup (the next
+// step's loads are in flight while the current step is computed) and staged
+// in LDS: K as rows, V transposed, so that both MFMA operands are 16-byte
+// LDS reads.  Per wave and step, with v_mfma_f32_16x16x32:
+//   S^T = K . Q^T   (A = 16 keys x 32 dims of K, B = 32 dims x 16 columns of
+//                    Q held in registers), two 16-key sub-tiles;
+//   masks, soft cap, online softmax per column (max / sum across the four
+//   lanes of a column);
+//   O^T += V^T . P^T (A = 16 dims x 8 keys of the transposed V, B = P regrouped
+//                    by two permlane swaps, as in the decode kernel).
+#include "pa_partition_mfma.h"
+#include "pa_prefill.h"
+
+namespace pa {
+
+template <typename QT, int D, int BS, bool CAP>
+__global__ void __launch_bounds__(kThreads) pa_prefill_kernel(const PrefillParams p) {
+  constexpr int NKS = D / 32;                  // 32-dim k-steps of QK^T
+  constexpr int NDT = D / 16;                  // 16-dim output tiles
+  constexpr int KP = D + 8;                    // padded K row in LDS (elements)
+  constexpr int VP = kPrefillStep + 8;         // padded V^T row in LDS (keys)
+  constexpr int CPR = D / 8;                   // 16-byte chunks per key row
+  constexpr int NLK = kPrefillStep * CPR / kThreads;  // K chunks per thread per step
+  constexpr int VTHREADS = (kPrefillStep / 2) * CPR;  // threads loading V key pairs
+  static_assert(NLK >= 1 && NLK * kThreads == kPrefillStep * CPR, "K tile geometry");
+  static_assert(VTHREADS <= kThreads, "V tile geometry");
+  static_assert(kPrefillStep % BS == 0, "a step covers whole blocks");
+
+  __shared__ __attribute__((aligned(16))) QT sk[kPrefillStep][KP];
+  __shared__ __attribute__((aligned(16))) QT sv[D][VP];
+  __shared__ int sm_bad;
+
+  const int tile = p.num_q_tiles - 1 - (int)blockIdx.x;  // latest (heaviest) tiles first
+  const int kvh = blockIdx.y, seq = blockIdx.z;
+  const int q_begin = p.cu_seq_q[seq], q_end = p.cu_seq_q[seq + 1];
+  const int nq = q_end - q_begin, nk = p.cu_seq_k[seq + 1] - p.cu_seq_k[seq];
+  const int t0 = tile * p.q_tile;
+  if (t0 >= nq) return;
+  const int t1 = min(t0 + p.q_tile, nq);
+
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n = lane & 15, g = lane >> 4;
+  const int col = 16 * wv + n;
+  const int tok = t0 + col / p.group;
+  const int head = kvh * p.group + col % p.group;
+  const bool col_ok = col < p.q_tile * p.group && tok < t1;
+  QT *out = reinterpret_cast<QT *>(p.out);
+
+  // Lengths or offsets the host could not check: the tile's rows become NaN.
+  const bool bad = nk < 0 || nk > p.max_seq_k || nq > p.max_seq_q || q_begin < 0 ||
+                   q_end > p.total_q;
+  if (bad) {
+    if (col_ok && q_begin >= 0 && q_begin + tok < p.total_q) {
+      QT *row = out + ((size_t)(q_begin + tok) * p.num_heads + head) * D;
+      for (int d = 4 * g; d < D; d += 16)
+        for (int e = 0; e < 4; ++e) row[d + e] = from_f32<QT>(__builtin_nanf(""));
+    }
+    return;
+  }
+
+  // Keys the tile's queries can see, and this column's own range [vlo, vhi).
+  const long long pos0 = (long long)nk - nq;
+  long long lo = 0, hi = nk;
+  if (p.causal) hi = min(hi, pos0 + t1);
+  if (p.window_right >= 0) hi = min(hi, pos0 + t1 + p.window_right);
+  if (p.window_left >= 0) lo = max(lo, pos0 + t0 - p.window_left);
+  int vlo = 0, vhi = 0;
+  if (col_ok) {
+    const long long qpos = pos0 + tok;
+    long long a = 0, b = nk;
+    if (p.causal) b = min(b, qpos + 1);
+    if (p.window_right >= 0) b = min(b, qpos + 1 + p.window_right);
+    if (p.window_left >= 0) a = max(a, qpos - p.window_left);
+    vlo = (int)max(a, 0LL);
+    vhi = (int)max(min(b, (long long)nk), 0LL);
+  }
+
+  // B operands of QK^T: 8 query values per lane and k-step (dims 32ks + 8g).
+  u32x4 qop[NKS];
+  {
+    const QT *q = reinterpret_cast<const QT *>(p.query) +
+                  ((size_t)(q_begin + (col_ok ? tok : t0)) * p.num_heads + head) * D;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+      qop[ks] = col_ok ? load16(q + 32 * ks + 8 * g) : u32x4{0u, 0u, 0u, 0u};
+  }
+
+  const char *kcache = reinterpret_cast<const char *>(p.key_cache);
+  const char *vcache = reinterpret_cast<const char *>(p.value_cache);
+  const const_i32_ptr btab =
+      as_const_table(p.block_tables + (size_t)seq * p.max_num_blocks_per_seq);
+  // Byte offset of key t's row; an out-of-range table entry reads block 0
+  // and poisons the workgroup's result.
+  bool poisoned = false;
+  auto key_row = [&](int t) -> size_t {
+    int phys = btab[t / BS];
+    if (phys < 0 || phys >= p.num_blocks) {
+      poisoned = true;
+      phys = 0;
+    }
+    return (((size_t)phys * p.num_kv_heads + kvh) * BS + t % BS) * D * sizeof(QT);
+  };
+
+  // One step's tiles in registers: K chunks (row-major) and two keys' chunks
+  // of V; keys at or past nk are zero.
+  struct Stage {
+    u32x4 k[NLK];
+    u32x4 v[2];
+  };
+  auto load_stage = [&](int base) {
+    Stage st;
+#pragma unroll
+    for (int i = 0; i < NLK; ++i) {
+      const int c = threadIdx.x + kThreads * i, key = c / CPR, ch = c % CPR;
+      const int t = base + key;
+      st.k[i] = t < nk ? load16(kcache + key_row(t) + ch * 16) : u32x4{0u, 0u, 0u, 0u};
+    }
+    st.v[0] = st.v[1] = u32x4{0u, 0u, 0u, 0u};
+    if (threadIdx.x < VTHREADS) {
+      const int kp = threadIdx.x % (kPrefillStep / 2), ch = threadIdx.x / (kPrefillStep / 2);
+      const int t = base + 2 * kp;
+      if (t < nk) st.v[0] = load16(vcache + key_row(t) + ch * 16);
+      if (t + 1 < nk) st.v[1] = load16(vcache + key_row(t + 1) + ch * 16);
+    }
+    return st;
+  };
+  auto store_stage = [&](const Stage &st) {
+#pragma unroll
+    for (int i = 0; i < NLK; ++i) {
+      const int c = threadIdx.x + kThreads * i, key = c / CPR, ch = c % CPR;
+      *reinterpret_cast<u32x4 *>(&sk[key][ch * 8]) = st.k[i];
+    }
+    if (threadIdx.x < VTHREADS) {
+      const int kp = threadIdx.x % (kPrefillStep / 2), ch = threadIdx.x / (kPrefillStep / 2);
+      const unsigned a[4] = {st.v[0].x, st.v[0].y, st.v[0].z, st.v[0].w};
+      const unsigned b[4] = {st.v[1].x, st.v[1].y, st.v[1].z, st.v[1].w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const unsigned lo16 = (a[e / 2] >> (16 * (e % 2))) & 0xffffu;
+        const unsigned hi16 = (b[e / 2] >> (16 * (e % 2))) & 0xffffu;
+        *reinterpret_cast<unsigned *>(&sv[ch * 8 + e][2 * kp]) = lo16 | (hi16 << 16);
+      }
+    }
+  };
+
+  float m_run = -__builtin_inff(), l_run = 0.0f;
+  f32x4 oacc[NDT];
+#pragma unroll
+  for (int t = 0; t < NDT; ++t) oacc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+  auto compute = [&](int base) {
+    f32x4 s[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      f32x4 c = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        const u32x4 a = *reinterpret_cast<const u32x4 *>(&sk[16 * h + n][32 * ks + 8 * g]);
+        c = mfma_qk(a, qop[ks], c, QT());
+      }
+      s[h] = c;
+    }
+    float x[2][4];
+    float bm = -__builtin_inff();
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int t = base + 16 * h + 4 * g + e;
+        const float v = scaled_logit<CAP>(p, s[h][e]);
+        x[h][e] = (t >= vlo && t < vhi) ? v : -__builtin_inff();
+        bm = fmaxf(bm, x[h][e]);
+      }
+    bm = xor_max<32>(xor_max<16>(bm));
+    const float m_new = fmaxf(m_run, bm);
+    const float alpha = (m_new == -__builtin_inff()) ? 1.0f : fast_exp2(m_run - m_new);
+    m_run = m_new;
+    float psum = 0.0f;
+    u32x2 pk[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      float pe[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        pe[e] = x[h][e] == -__builtin_inff() ? 0.0f : fast_exp2(x[h][e] - m_new);
+        psum += pe[e];
+      }
+      pk[h] = u32x2{pack2(pe[0], pe[1], QT()), pack2(pe[2], pe[3], QT())};
+    }
+    l_run = l_run * alpha + psum;
+    const u32x4 pop = regroup_p(pk[0], pk[1]);
+#pragma unroll
+    for (int t = 0; t < NDT; ++t) {
+      const u32x4 va = *reinterpret_cast<const u32x4 *>(&sv[16 * t + n][8 * (g ^ 1)]);
+      oacc[t] = mfma_pv(va, pop, oacc[t] * alpha, QT());
+    }
+  };
+
+  if (threadIdx.x == 0) sm_bad = 0;
+  __syncthreads();
+  int base = (int)(lo & ~(long long)(kPrefillStep - 1));
+  if (base < hi) {
+    Stage st = load_stage(base);
+    store_stage(st);
+    __syncthreads();
+    for (; base < hi; base += kPrefillStep) {
+      const bool more = base + kPrefillStep < hi;
+      if (more) st = load_stage(base + kPrefillStep);
+      compute(base);
+      __syncthreads();
+      if (more) {
+        store_stage(st);
+        __syncthreads();
+      }
+    }
+  }
+  if (poisoned) sm_bad = 1;
+  __syncthreads();
+
+  const float l_tot = xor_sum<32>(xor_sum<16>(l_run));
+  if (!col_ok) return;
+  const bool nan_out = sm_bad != 0;
+  QT *row = out + ((size_t)(q_begin + tok) * p.num_heads + head) * D;
+#pragma unroll
+  for (int t = 0; t < NDT; ++t) {
+    float o[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      o[e] = nan_out ? __builtin_nanf("") : (l_tot > 0.0f ? oacc[t][e] / l_tot : 0.0f);
+    *reinterpret_cast<u32x2 *>(row + 16 * t + 4 * g) =
+        u32x2{pack2(o[0], o[1], QT()), pack2(o[2], o[3], QT())};
+  }
+}
+
+template <typename QT, int D, int BS>
+static hipError_t launch_prefill_bs(const PrefillParams &p, bool cap, const Launch &l) {
+  return cap ? launch_kernel(pa_prefill_kernel<QT, D, BS, true>, l, p)
+             : launch_kernel(pa_prefill_kernel<QT, D, BS, false>, l, p);
+}
+
+template <typename QT>
+static hipError_t launch_prefill_t(const PrefillParams &p, int head_size, int block_size,
+                                   bool cap, const Launch &l) {
+  if (head_size == 64 && block_size == 16) return launch_prefill_bs<QT, 64, 16>(p, cap, l);
+  if (head_size == 64 && block_size == 32) return launch_prefill_bs<QT, 64, 32>(p, cap, l);
+  if (head_size == 128 && block_size == 16) return launch_prefill_bs<QT, 128, 16>(p, cap, l);
+  if (head_size == 128 && block_size == 32) return launch_prefill_bs<QT, 128, 32>(p, cap, l);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_prefill(const PrefillParams &p, int dtype, int head_size, int block_size,
+                          bool cap, const Launch &l) {
+  if (dtype == kDtF16) return launch_prefill_t<_Float16>(p, head_size, block_size, cap, l);
+  if (dtype == kDtBF16) return launch_prefill_t<__bf16>(p, head_size, block_size, cap, l);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace pa

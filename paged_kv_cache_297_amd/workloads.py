@@ -289,3 +289,118 @@ def host_subset(wl: Workload, seqs) -> dict:
     return dict(query=raw_storage(wl.query), key_cache=raw_storage(wl.key_cache[idx]),
                 value_cache=raw_storage(wl.value_cache[idx]), block_tables=new_tables,
                 seq_lens=wl.lens.copy())
+
+
+# --------------------------------------------------------------------------
+# Prefill batches (inputs only)
+# --------------------------------------------------------------------------
+
+#: Prefill workloads: query / key counts per sequence and the model shape.
+#:   prefill_bf16   8 prompts of 2048 tokens (nq = nk = 2048), H=32, Hkv=8,
+#:                  D=128, bs=16, bf16, causal: a fresh prefill
+#:   chunked_bf16   16 sequences, 512 new tokens over 8192-token contexts
+#:                  (nq = 512, nk = 8192), same model shape: chunked prefill
+PREFILL_WORKLOADS = {
+    "prefill_bf16": dict(qlens=(2048,) * 8, klens=(2048,) * 8, H=32, Hkv=8, D=128, bs=16,
+                         dtype=torch.bfloat16),
+    "chunked_bf16": dict(qlens=(512,) * 16, klens=(8192,) * 16, H=32, Hkv=8, D=128, bs=16,
+                         dtype=torch.bfloat16),
+}
+
+
+@dataclass
+class PrefillWorkload:
+    name: str
+    num_seqs: int
+    num_heads: int
+    num_kv_heads: int
+    head_size: int
+    block_size: int
+    dtype: torch.dtype
+    query: torch.Tensor          # [total_q, H, D]
+    key_cache: torch.Tensor      # [NB, Hkv, bs, D]
+    value_cache: torch.Tensor    # [NB, Hkv, bs, D]
+    block_tables: torch.Tensor   # int32 [B, max_blocks]
+    cu_seq_q: torch.Tensor       # int32 [B + 1]
+    cu_seq_k: torch.Tensor       # int32 [B + 1]
+    qlens: np.ndarray
+    klens: np.ndarray
+    scale: float
+
+    @property
+    def max_seq_q(self) -> int:
+        return int(self.qlens.max(initial=0))
+
+    @property
+    def max_seq_k(self) -> int:
+        return int(self.klens.max(initial=0))
+
+    @property
+    def kind(self) -> str:
+        return STORAGE_KIND[self.dtype]
+
+
+def make_prefill_workload(name: str = "prefill_bf16", device="cuda", *, qlens=None, klens=None,
+                          seed: int = 2000, **overrides) -> PrefillWorkload:
+    """Seeded prefill batch: N(0, 1) query / key / value values rounded to the
+    dtype (torch generator on ``device``), a shuffled block pool holding
+    exactly the blocks the sequences need (NumPy PCG64)."""
+    spec = dict(PREFILL_WORKLOADS[name])
+    if qlens is not None:
+        spec["qlens"] = tuple(qlens)
+    if klens is not None:
+        spec["klens"] = tuple(klens)
+    spec.update(overrides)
+    ql = np.asarray(spec["qlens"], dtype=np.int64)
+    kl = np.asarray(spec["klens"], dtype=np.int64)
+    b, h, hkv, d, bs, dtype = len(ql), spec["H"], spec["Hkv"], spec["D"], spec["bs"], spec["dtype"]
+    rng = np.random.Generator(np.random.PCG64(seed))
+    need = (kl + bs - 1) // bs
+    pool = max(int(need.sum()), 1)
+    perm = rng.permutation(pool)
+    tables = np.zeros((b, max(1, int(need.max(initial=0)))), dtype=np.int32)
+    off = 0
+    for s in range(b):
+        tables[s, :need[s]] = perm[off:off + need[s]]
+        off += need[s]
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    query = torch.empty((int(ql.sum()), h, d), dtype=dtype, device=device)
+    key_cache = torch.empty((pool, hkv, bs, d), dtype=dtype, device=device)
+    value_cache = torch.empty((pool, hkv, bs, d), dtype=dtype, device=device)
+    for t in (query, key_cache, value_cache):
+        _fill_random(t, gen, 1.0)
+    cu_q = np.concatenate([[0], np.cumsum(ql)]).astype(np.int32)
+    cu_k = np.concatenate([[0], np.cumsum(kl)]).astype(np.int32)
+    return PrefillWorkload(
+        name=name, num_seqs=b, num_heads=h, num_kv_heads=hkv, head_size=d, block_size=bs,
+        dtype=dtype, query=query, key_cache=key_cache, value_cache=value_cache,
+        block_tables=torch.from_numpy(tables).to(device),
+        cu_seq_q=torch.from_numpy(cu_q).to(device), cu_seq_k=torch.from_numpy(cu_k).to(device),
+        qlens=ql, klens=kl, scale=1.0 / math.sqrt(d))
+
+
+def prefill_host_subset(wl: PrefillWorkload, seqs) -> dict:
+    """Raw host storage of the listed sequences (queries and a compacted pool)
+    for the CPU oracle: dict(query, key_cache, value_cache, block_tables,
+    cu_seq_q, cu_seq_k, rows) with ``rows`` the global query rows kept."""
+    bs = wl.block_size
+    tables = wl.block_tables.cpu().numpy()
+    cu_q = np.concatenate([[0], np.cumsum(wl.qlens)])
+    blocks, rows = [], []
+    new_tables = np.zeros((len(seqs), tables.shape[1]), dtype=np.int32)
+    qlens, klens = [], []
+    for i, s in enumerate(seqs):
+        n = (int(wl.klens[s]) + bs - 1) // bs
+        new_tables[i, :n] = np.arange(len(blocks), len(blocks) + n)
+        blocks.extend(int(v) for v in tables[s, :n])
+        rows.extend(range(int(cu_q[s]), int(cu_q[s + 1])))
+        qlens.append(int(wl.qlens[s]))
+        klens.append(int(wl.klens[s]))
+    idx = torch.tensor(blocks if blocks else [0], dtype=torch.long, device=wl.key_cache.device)
+    ridx = torch.tensor(rows if rows else [0], dtype=torch.long, device=wl.query.device)
+    return dict(query=raw_storage(wl.query[ridx]), key_cache=raw_storage(wl.key_cache[idx]),
+                value_cache=raw_storage(wl.value_cache[idx]), block_tables=new_tables,
+                cu_seq_q=np.concatenate([[0], np.cumsum(qlens)]).astype(np.int32),
+                cu_seq_k=np.concatenate([[0], np.cumsum(klens)]).astype(np.int32),
+                rows=np.asarray(rows, dtype=np.int64))

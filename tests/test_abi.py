@@ -303,3 +303,48 @@ def test_split_counters_size():
     assert lib.pa_split_counters_size(0, 4) == 0
     assert lib.pa_split_counters_size(5, -1) == 0
     assert lib.pa_split_counters_size(65535, 128) == 65535 * 128 * 4
+
+
+# --------------------------------------------------------------------------
+# Paged prefill
+# --------------------------------------------------------------------------
+
+def prefill_args(options=None, **kw):
+    a = dict(out=A, query=A, key_cache=A, value_cache=A, total_q=10, num_seqs=2, num_heads=8,
+             num_kv_heads=2, head_size=128, scale=0.1, block_tables=A, max_blocks=8,
+             cu_q=A, cu_k=A, max_q=6, max_k=100, num_blocks=16, block_size=16, dtype=BF16)
+    a.update(kw)
+    return [a["out"], a["query"], a["key_cache"], a["value_cache"], a["total_q"], a["num_seqs"],
+            a["num_heads"], a["num_kv_heads"], a["head_size"], a["scale"], a["block_tables"],
+            a["max_blocks"], a["cu_q"], a["cu_k"], a["max_q"], a["max_k"], a["num_blocks"],
+            a["block_size"], a["dtype"], options, None]
+
+
+def popts(causal=1, wl=-1, wr=-1, cap=0.0):
+    return ctypes.byref(B.PrefillOptions(causal, wl, wr, cap))
+
+
+PREFILL_CASES = [
+    (dict(out=None), NULLP), (dict(cu_q=None), NULLP), (dict(block_tables=None), NULLP),
+    (dict(query=A + 8), MISAL), (dict(value_cache=A + 2), MISAL),
+    (dict(num_heads=7), SHAPE), (dict(num_seqs=-1), SHAPE), (dict(total_q=-1), SHAPE),
+    (dict(max_blocks=6), SHAPE), (dict(num_blocks=0), SHAPE), (dict(num_seqs=70000), SHAPE),
+    (dict(head_size=96), UNSUP), (dict(block_size=8), UNSUP), (dict(dtype=F32), UNSUP),
+    (dict(num_heads=130, num_kv_heads=2), UNSUP),   # group 65 > 64
+    (dict(dtype=9), BADARG), (dict(scale=float("inf")), BADARG),
+    (dict(num_seqs=0), OK), (dict(total_q=0), OK), (dict(max_q=0), OK),
+]
+
+
+@pytest.mark.parametrize("kw,status", PREFILL_CASES)
+def test_prefill_validation(kw, status):
+    lib = B.load_library()
+    assert lib.paged_prefill(*prefill_args(**kw)) == status
+
+
+def test_prefill_options_validation():
+    lib = B.load_library()
+    for o in (popts(wl=-2), popts(wr=-5), popts(cap=-1.0), popts(cap=float("nan")),
+              popts(cap=1e-45)):
+        assert lib.paged_prefill(*prefill_args(options=o)) == BADARG
+    assert lib.paged_prefill(*prefill_args(options=popts(0, 5, 9, 30.0), num_seqs=0)) == OK
