@@ -155,6 +155,87 @@ def cpu_baseline(wl, budget_s: float, window_left: int = -1, soft_cap: float = 0
             "us_per_step_extrapolated": round(spent / kv_done * kv_step * 1e6, 1)}
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 / fp16 matrix peak
+
+
+def prefill_flops(qlens, klens, num_heads: int, head_size: int) -> int:
+    """Useful flops of a causal prefill batch: 2 * D multiply-adds for QK^T and
+    2 * D for PV per visible (query, key) pair and head.  Query i of a
+    sequence sits at position nk - nq + i and sees keys 0 .. that position."""
+    pairs = 0
+    for nq, nk in zip(qlens, klens):
+        nq, nk = int(nq), int(nk)
+        lo = nk - nq  # keys visible to query 0, minus one
+        for_all = sum(max(0, min(nk, lo + i + 1)) for i in range(nq))
+        pairs += for_all
+    return 4 * head_size * num_heads * pairs
+
+
+def bench_prefill(args) -> int:
+    """Times paged_prefill on a prefill workload; prints the JSON line."""
+    import numpy as np
+    import torch
+
+    from paged_kv_cache_297_amd import binding as B
+    from paged_kv_cache_297_amd import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    B.load_library()
+    wl = W.make_prefill_workload(args.prefill, device="cuda")
+    stream = torch.cuda.current_stream()
+    out = torch.empty_like(wl.query)
+    call = B.PreparedPrefill(out, wl.query, wl.key_cache, wl.value_cache, wl.num_kv_heads,
+                             wl.scale, wl.block_tables, wl.cu_seq_q, wl.cu_seq_k, wl.max_seq_q,
+                             wl.max_seq_k, causal=True, stream=stream)
+    lib = B.load_library()
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for ev in events:
+        for e in ev:
+            e.record(stream)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        call()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    for ev in events:
+        lib.pa_set_timing_events(ev[0].cuda_event, ev[1].cuda_event, None, None)
+        call()
+    torch.cuda.synchronize()
+    B.set_timing_events()
+    kern_ms = np.array([e[0].elapsed_time(e[1]) for e in events])
+    flops = prefill_flops(wl.qlens, wl.klens, wl.num_heads, wl.head_size)
+    ms = wall * 1e3 / args.steps
+    tflops = flops / (ms * 1e-3) / 1e12
+    kavg = float(kern_ms.mean())
+    achieved = flops / (kavg * 1e-3) / 1e12
+    result = {
+        "metric": "paged prefill attention TFLOP/s (causal), 1 MI355X",
+        "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None,
+        "dtype": {torch.float16: "f16", torch.bfloat16: "bf16"}[wl.dtype], "data": "synthetic",
+        "config": {"workload": (f"{wl.name}: paged prefill, num_seqs={wl.num_seqs}, "
+                                f"query tokens {int(wl.qlens.min())}..{int(wl.qlens.max())}, "
+                                f"keys {int(wl.klens.min())}..{int(wl.klens.max())}, "
+                                f"num_heads={wl.num_heads}, num_kv_heads={wl.num_kv_heads}, "
+                                f"head_size={wl.head_size}, block_size={wl.block_size}, causal"),
+                   "flops_per_step": flops},
+        "roofline": {"bound": "mfma", "kernel": "pa_prefill_kernel", "achieved": round(achieved, 2),
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "algorithmic_flops_per_launch": flops, "avg_launch_ms": round(kavg, 5),
+                     "kernel_source_hash": kernel_source_hash()},
+    }
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -172,12 +253,17 @@ def main() -> int:
                     help="sliding window: attend to the last W + 1 keys (-1: off)")
     ap.add_argument("--softcap", type=float, default=0.0, metavar="C",
                     help="logit soft cap C * tanh(s / C) (0: off)")
+    ap.add_argument("--prefill", default=None, choices=["prefill_bf16", "chunked_bf16"],
+                    help="time paged prefill on this workload instead of decode")
     args = ap.parse_args()
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the decode path "
               "has no multi-GPU part in this library.", file=sys.stderr)
         return 2
+
+    if args.prefill:
+        return bench_prefill(args)
 
     import numpy as np
     import torch

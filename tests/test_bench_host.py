@@ -50,3 +50,11 @@ def test_window_shrinks_tables_and_partials(wl):
     multi = live > 1
     assert win["reduce"] == int((live * multi).sum()) * h * (d * esz + 8) \
         + int(multi.sum()) * h * d * esz + wl.num_seqs * 4
+
+
+def test_prefill_flops_counts_the_causal_pairs():
+    """Against the oracle's own visibility mask (nq <= nk, nq > nk, square)."""
+    from oracle import prefill_oracle as P
+    qlens, klens = [1, 7, 40, 9, 64], [1, 30, 40, 4, 64]
+    pairs = sum(int(P.visible_keys(q, k, True, -1, -1).sum()) for q, k in zip(qlens, klens))
+    assert bench.prefill_flops(qlens, klens, 3, 128) == 4 * 128 * 3 * pairs
