@@ -331,7 +331,7 @@ typedef struct pa_prefill_options {
  * per-sequence query / key counts (host integers).
  *
  * Supported: dtype f16 / bf16 (f32: PA_ERR_UNSUPPORTED); head_size 64 or 128;
- * block_size 16 or 32; num_heads / num_kv_heads <= 64.  Errors as for the
+ * block_size 16 or 32; num_heads / num_kv_heads <= 128.  Errors as for the
  * decode calls; cu_seq_* entries that break max_seq_q / max_seq_k / total_q,
  * and block-table entries outside [0, num_blocks), give NaN rows for that
  * sequence (rows past max_seq_q are not written).  Accumulation is fp32. */

@@ -637,7 +637,7 @@ pa_status paged_prefill(void *out, const void *query, const void *key_cache,
     return PA_ERR_BAD_SHAPE;
   if (num_heads % num_kv_heads != 0) return PA_ERR_BAD_SHAPE;
   const int group = num_heads / num_kv_heads;
-  if (group > pa::kPrefillCols) return PA_ERR_UNSUPPORTED;
+  if (group > pa::kPrefillMaxCols) return PA_ERR_UNSUPPORTED;
   if (num_seqs > kMaxGridYZ || num_kv_heads > kMaxGridYZ) return PA_ERR_BAD_SHAPE;
   if (dtype == PA_DTYPE_F32) return PA_ERR_UNSUPPORTED;
   if (head_size != 64 && head_size != 128) return PA_ERR_UNSUPPORTED;
@@ -666,7 +666,12 @@ pa_status paged_prefill(void *out, const void *query, const void *key_cache,
   p.num_blocks = num_blocks;
   p.max_seq_q = max_seq_q;
   p.max_seq_k = max_seq_k;
-  p.q_tile = pa::kPrefillCols / group;
+  // Two column tiles per wave when each query sees many keys (long context
+  // over few new tokens: chunked prefill), one otherwise (fresh prompts:
+  // more, shorter workgroups balance the causal triangle).  A group wider
+  // than one tile's worth of columns needs two.
+  p.tiles_per_wave = (max_seq_k >= 2LL * max_seq_q || group > 16 * pa::kWaves) ? 2 : 1;
+  p.q_tile = 16 * p.tiles_per_wave * pa::kWaves / group;
   const long long tiles = ((long long)max_seq_q + p.q_tile - 1) / p.q_tile;
   if (tiles > 0x7fffffffLL) return PA_ERR_BAD_SHAPE;
   p.num_q_tiles = (int)tiles;

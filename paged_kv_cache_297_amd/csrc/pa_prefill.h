@@ -7,8 +7,8 @@
 namespace pa {
 
 // Query columns of one workgroup: (query token, query head) pairs of one KV
-// head, 16 per wave.
-constexpr int kPrefillCols = 16 * kWaves;
+// head, one or two 16-column MFMA tiles per wave (tiles_per_wave).
+constexpr int kPrefillMaxCols = 16 * 2 * kWaves;
 // Keys per step of the prefill loop (two 16-key MFMA sub-tiles).
 constexpr int kPrefillStep = 32;
 
@@ -22,7 +22,8 @@ struct PrefillParams {
   const int32_t *cu_seq_k;      // [B + 1]
   int total_q, num_seqs, num_heads, num_kv_heads, group;
   int max_num_blocks_per_seq, num_blocks, max_seq_q, max_seq_k;
-  int q_tile;        // query tokens per workgroup: kPrefillCols / group
+  int tiles_per_wave;  // 1 or 2 column tiles per wave
+  int q_tile;        // query tokens per workgroup: 16 * tiles_per_wave * waves / group
   int num_q_tiles;   // ceil(max_seq_q / q_tile) = grid.x
   int causal, window_left, window_right;
   float scale_log2;  // scale * log2(e)

@@ -5,12 +5,13 @@
 // window and a logit soft cap).  The queries of a sequence are its last nq
 // positions: query token i sits at position nk - nq + i.
 //
-// A workgroup owns 64 query columns -- (query token, query head) pairs of one
-// KV head, 16 per wave -- and walks the keys its columns can see in steps of
-// 32.  Each step's K and V tiles are loaded once per workgroup (the next
+// A workgroup owns 64 or 128 query columns -- (query token, query head) pairs
+// of one KV head, one or two 16-column MFMA tiles per wave -- and walks the
+// keys its columns can see in steps of 32.  Each step's K and V tiles are loaded once per workgroup (the next
 // step's loads are in flight while the current step is computed) and staged
 // in LDS: K as rows, V transposed, so that both MFMA operands are 16-byte
-// LDS reads.  Per wave and step, with v_mfma_f32_16x16x32:
+// LDS reads, each feeding the wave's column tiles.  Per wave, column
+// tile and step, with v_mfma_f32_16x16x32:
 //   S^T = K . Q^T   (A = 16 keys x 32 dims of K, B = 32 dims x 16 columns of
 //                    Q held in registers), two 16-key sub-tiles;
 //   masks, soft cap, online softmax per column (max / sum across the four
@@ -22,8 +23,9 @@
 
 namespace pa {
 
-template <typename QT, int D, int BS, bool CAP>
+template <typename QT, int D, int BS, int NT, bool CAP>
 __global__ void __launch_bounds__(kThreads) pa_prefill_kernel(const PrefillParams p) {
+  // NT: 16-column MFMA tiles per wave
   constexpr int NKS = D / 32;                  // 32-dim k-steps of QK^T
   constexpr int NDT = D / 16;                  // 16-dim output tiles
   constexpr int KP = D + 8;                    // padded K row in LDS (elements)
@@ -50,49 +52,58 @@ __global__ void __launch_bounds__(kThreads) pa_prefill_kernel(const PrefillParam
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15, g = lane >> 4;
-  const int col = 16 * wv + n;
-  const int tok = t0 + col / p.group;
-  const int head = kvh * p.group + col % p.group;
-  const bool col_ok = col < p.q_tile * p.group && tok < t1;
   QT *out = reinterpret_cast<QT *>(p.out);
+
+  // Column j of the wave: (query token, query head) pair 64 wv + 16 j + n.
+  int tok[NT], head[NT], vlo[NT], vhi[NT];
+  bool col_ok[NT];
+  const long long pos0 = (long long)nk - nq;  // position of query token 0
+#pragma unroll
+  for (int j = 0; j < NT; ++j) {
+    const int col = 16 * (NT * wv + j) + n;
+    tok[j] = t0 + col / p.group;
+    head[j] = kvh * p.group + col % p.group;
+    col_ok[j] = col < p.q_tile * p.group && tok[j] < t1;
+    // The keys this column sees: [vlo, vhi).
+    const long long qpos = pos0 + tok[j];
+    long long a = 0, b = nk;
+    if (p.causal) b = min(b, qpos + 1);
+    if (p.window_right >= 0) b = min(b, qpos + 1 + p.window_right);
+    if (p.window_left >= 0) a = max(a, qpos - p.window_left);
+    vlo[j] = col_ok[j] ? (int)max(a, 0LL) : 0;
+    vhi[j] = col_ok[j] ? (int)max(min(b, (long long)nk), 0LL) : 0;
+  }
 
   // Lengths or offsets the host could not check: the tile's rows become NaN.
   const bool bad = nk < 0 || nk > p.max_seq_k || nq > p.max_seq_q || q_begin < 0 ||
                    q_end > p.total_q;
   if (bad) {
-    if (col_ok && q_begin >= 0 && q_begin + tok < p.total_q) {
-      QT *row = out + ((size_t)(q_begin + tok) * p.num_heads + head) * D;
-      for (int d = 4 * g; d < D; d += 16)
-        for (int e = 0; e < 4; ++e) row[d + e] = from_f32<QT>(__builtin_nanf(""));
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      if (col_ok[j] && q_begin >= 0 && q_begin + tok[j] < p.total_q) {
+        QT *row = out + ((size_t)(q_begin + tok[j]) * p.num_heads + head[j]) * D;
+        for (int d = 4 * g; d < D; d += 16)
+          for (int e = 0; e < 4; ++e) row[d + e] = from_f32<QT>(__builtin_nanf(""));
+      }
     }
     return;
   }
 
-  // Keys the tile's queries can see, and this column's own range [vlo, vhi).
-  const long long pos0 = (long long)nk - nq;
+  // Keys any column of the workgroup sees.
   long long lo = 0, hi = nk;
   if (p.causal) hi = min(hi, pos0 + t1);
   if (p.window_right >= 0) hi = min(hi, pos0 + t1 + p.window_right);
   if (p.window_left >= 0) lo = max(lo, pos0 + t0 - p.window_left);
-  int vlo = 0, vhi = 0;
-  if (col_ok) {
-    const long long qpos = pos0 + tok;
-    long long a = 0, b = nk;
-    if (p.causal) b = min(b, qpos + 1);
-    if (p.window_right >= 0) b = min(b, qpos + 1 + p.window_right);
-    if (p.window_left >= 0) a = max(a, qpos - p.window_left);
-    vlo = (int)max(a, 0LL);
-    vhi = (int)max(min(b, (long long)nk), 0LL);
-  }
 
-  // B operands of QK^T: 8 query values per lane and k-step (dims 32ks + 8g).
-  u32x4 qop[NKS];
-  {
+  // B operands of QK^T: 8 query values per lane, column tile and k-step.
+  u32x4 qop[NT][NKS];
+#pragma unroll
+  for (int j = 0; j < NT; ++j) {
     const QT *q = reinterpret_cast<const QT *>(p.query) +
-                  ((size_t)(q_begin + (col_ok ? tok : t0)) * p.num_heads + head) * D;
+                  ((size_t)(q_begin + (col_ok[j] ? tok[j] : t0)) * p.num_heads + head[j]) * D;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks)
-      qop[ks] = col_ok ? load16(q + 32 * ks + 8 * g) : u32x4{0u, 0u, 0u, 0u};
+      qop[j][ks] = col_ok[j] ? load16(q + 32 * ks + 8 * g) : u32x4{0u, 0u, 0u, 0u};
   }
 
   const char *kcache = reinterpret_cast<const char *>(p.key_cache);
@@ -153,61 +164,79 @@ __global__ void __launch_bounds__(kThreads) pa_prefill_kernel(const PrefillParam
     }
   };
 
-  float m_run = -__builtin_inff(), l_run = 0.0f;
-  f32x4 oacc[NDT];
+  float m_run[NT], l_run[NT];
+  f32x4 oacc[NT][NDT];
 #pragma unroll
-  for (int t = 0; t < NDT; ++t) oacc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int j = 0; j < NT; ++j) {
+    m_run[j] = -__builtin_inff();
+    l_run[j] = 0.0f;
+#pragma unroll
+    for (int t = 0; t < NDT; ++t) oacc[j][t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  }
 
   auto compute = [&](int base) {
-    f32x4 s[2];
+    // S^T of every column tile; each K fragment read from LDS feeds NT MFMAs.
+    f32x4 s[NT][2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      f32x4 c = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int j = 0; j < NT; ++j) s[j][h] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
         const u32x4 a = *reinterpret_cast<const u32x4 *>(&sk[16 * h + n][32 * ks + 8 * g]);
-        c = mfma_qk(a, qop[ks], c, QT());
+#pragma unroll
+        for (int j = 0; j < NT; ++j) s[j][h] = mfma_qk(a, qop[j][ks], s[j][h], QT());
       }
-      s[h] = c;
     }
-    float x[2][4];
-    float bm = -__builtin_inff();
+    u32x4 pop[NT];
+    float alpha[NT];
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+    for (int j = 0; j < NT; ++j) {
+      float x[2][4];
+      float bm = -__builtin_inff();
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int t = base + 16 * h + 4 * g + e;
-        const float v = scaled_logit<CAP>(p, s[h][e]);
-        x[h][e] = (t >= vlo && t < vhi) ? v : -__builtin_inff();
-        bm = fmaxf(bm, x[h][e]);
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int t = base + 16 * h + 4 * g + e;
+          const float v = scaled_logit<CAP>(p, s[j][h][e]);
+          x[h][e] = (t >= vlo[j] && t < vhi[j]) ? v : -__builtin_inff();
+          bm = fmaxf(bm, x[h][e]);
+        }
+      bm = xor_max<32>(xor_max<16>(bm));
+      const float m_new = fmaxf(m_run[j], bm);
+      alpha[j] = (m_new == -__builtin_inff()) ? 1.0f : fast_exp2(m_run[j] - m_new);
+      m_run[j] = m_new;
+      float psum = 0.0f;
+      u32x2 pk[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        float pe[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          pe[e] = x[h][e] == -__builtin_inff() ? 0.0f : fast_exp2(x[h][e] - m_new);
+          psum += pe[e];
+        }
+        pk[h] = u32x2{pack2(pe[0], pe[1], QT()), pack2(pe[2], pe[3], QT())};
       }
-    bm = xor_max<32>(xor_max<16>(bm));
-    const float m_new = fmaxf(m_run, bm);
-    const float alpha = (m_new == -__builtin_inff()) ? 1.0f : fast_exp2(m_run - m_new);
-    m_run = m_new;
-    float psum = 0.0f;
-    u32x2 pk[2];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      float pe[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        pe[e] = x[h][e] == -__builtin_inff() ? 0.0f : fast_exp2(x[h][e] - m_new);
-        psum += pe[e];
-      }
-      pk[h] = u32x2{pack2(pe[0], pe[1], QT()), pack2(pe[2], pe[3], QT())};
+      l_run[j] = l_run[j] * alpha[j] + psum;
+      pop[j] = regroup_p(pk[0], pk[1]);
     }
-    l_run = l_run * alpha + psum;
-    const u32x4 pop = regroup_p(pk[0], pk[1]);
+    // O^T += V^T . P^T; each V fragment read from LDS feeds NT MFMAs.
 #pragma unroll
     for (int t = 0; t < NDT; ++t) {
       const u32x4 va = *reinterpret_cast<const u32x4 *>(&sv[16 * t + n][8 * (g ^ 1)]);
-      oacc[t] = mfma_pv(va, pop, oacc[t] * alpha, QT());
+#pragma unroll
+      for (int j = 0; j < NT; ++j) oacc[j][t] = mfma_pv(va, pop[j], oacc[j][t] * alpha[j], QT());
     }
   };
 
   if (threadIdx.x == 0) sm_bad = 0;
   __syncthreads();
+  // One LDS buffer: the next step's tiles load into registers while the
+  // current step is computed, then replace it between two barriers.  (A
+  // two-buffer, one-barrier pipeline measured slower: the second buffer
+  // cost occupancy.)
   int base = (int)(lo & ~(long long)(kPrefillStep - 1));
   if (base < hi) {
     Stage st = load_stage(base);
@@ -227,25 +256,31 @@ __global__ void __launch_bounds__(kThreads) pa_prefill_kernel(const PrefillParam
   if (poisoned) sm_bad = 1;
   __syncthreads();
 
-  const float l_tot = xor_sum<32>(xor_sum<16>(l_run));
-  if (!col_ok) return;
   const bool nan_out = sm_bad != 0;
-  QT *row = out + ((size_t)(q_begin + tok) * p.num_heads + head) * D;
 #pragma unroll
-  for (int t = 0; t < NDT; ++t) {
-    float o[4];
+  for (int j = 0; j < NT; ++j) {
+    const float l_tot = xor_sum<32>(xor_sum<16>(l_run[j]));
+    if (!col_ok[j]) continue;
+    QT *row = out + ((size_t)(q_begin + tok[j]) * p.num_heads + head[j]) * D;
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      o[e] = nan_out ? __builtin_nanf("") : (l_tot > 0.0f ? oacc[t][e] / l_tot : 0.0f);
-    *reinterpret_cast<u32x2 *>(row + 16 * t + 4 * g) =
-        u32x2{pack2(o[0], o[1], QT()), pack2(o[2], o[3], QT())};
+    for (int t = 0; t < NDT; ++t) {
+      float o[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        o[e] = nan_out ? __builtin_nanf("") : (l_tot > 0.0f ? oacc[j][t][e] / l_tot : 0.0f);
+      *reinterpret_cast<u32x2 *>(row + 16 * t + 4 * g) =
+          u32x2{pack2(o[0], o[1], QT()), pack2(o[2], o[3], QT())};
+    }
   }
 }
 
 template <typename QT, int D, int BS>
 static hipError_t launch_prefill_bs(const PrefillParams &p, bool cap, const Launch &l) {
-  return cap ? launch_kernel(pa_prefill_kernel<QT, D, BS, true>, l, p)
-             : launch_kernel(pa_prefill_kernel<QT, D, BS, false>, l, p);
+  if (p.tiles_per_wave == 2)
+    return cap ? launch_kernel(pa_prefill_kernel<QT, D, BS, 2, true>, l, p)
+               : launch_kernel(pa_prefill_kernel<QT, D, BS, 2, false>, l, p);
+  return cap ? launch_kernel(pa_prefill_kernel<QT, D, BS, 1, true>, l, p)
+             : launch_kernel(pa_prefill_kernel<QT, D, BS, 1, false>, l, p);
 }
 
 template <typename QT>

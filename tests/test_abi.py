@@ -330,7 +330,7 @@ PREFILL_CASES = [
     (dict(num_heads=7), SHAPE), (dict(num_seqs=-1), SHAPE), (dict(total_q=-1), SHAPE),
     (dict(max_blocks=6), SHAPE), (dict(num_blocks=0), SHAPE), (dict(num_seqs=70000), SHAPE),
     (dict(head_size=96), UNSUP), (dict(block_size=8), UNSUP), (dict(dtype=F32), UNSUP),
-    (dict(num_heads=130, num_kv_heads=2), UNSUP),   # group 65 > 64
+    (dict(num_heads=258, num_kv_heads=2), UNSUP),   # group 129 > 128
     (dict(dtype=9), BADARG), (dict(scale=float("inf")), BADARG),
     (dict(num_seqs=0), OK), (dict(total_q=0), OK), (dict(max_q=0), OK),
 ]

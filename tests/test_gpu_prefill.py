@@ -28,7 +28,13 @@ OPTIONS = [dict(causal=True), dict(causal=False), dict(causal=True, window_left=
            dict(causal=False, window_right=0)]
 
 FAMILIES = [(torch.bfloat16, 128, 16, 4), (torch.bfloat16, 64, 32, 1), (torch.float16, 128, 32, 7),
-            (torch.float16, 64, 16, 16), (torch.bfloat16, 128, 16, 64)]
+            (torch.bfloat16, 128, 32, 128), (torch.float16, 64, 16, 16),
+            (torch.bfloat16, 128, 16, 64)]
+
+#: Pairs whose key counts stay below twice the query counts: the kernel then
+#: runs one column tile per wave (the PAIRS above select two).
+PAIRS_SQUARE = [(1, 1), (17, 17), (64, 64), (65, 65), (5, 3), (130, 131), (200, 250), (0, 5),
+                (3, 0), (90, 40)]
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -76,6 +82,21 @@ def test_prefill_matrix(fam):
         got = run(wl, **o)
         ref, rows = oracle(wl, **o)
         H.check_close(got[rows], ref, TOL, f"prefill {_fam_id(fam)} {o}")
+
+
+@pytest.mark.parametrize("fam", FAMILIES[:3] + FAMILIES[4:], ids=_fam_id)
+def test_prefill_matrix_one_tile_per_wave(fam):
+    dt, d, bs, group = fam
+    hkv = 2 if group < 64 else 1
+    wl = W.make_prefill_workload(qlens=[q for q, _ in PAIRS_SQUARE],
+                                 klens=[k for _, k in PAIRS_SQUARE], H=hkv * group, Hkv=hkv, D=d,
+                                 bs=bs, dtype=dt, seed=9500 + FAMILIES.index(fam))
+    assert wl.max_seq_k < 2 * wl.max_seq_q
+    for o in OPTIONS:
+        H.say(f"  prefill square {_fam_id(fam)} {o}")
+        got = run(wl, **o)
+        ref, rows = oracle(wl, **o)
+        H.check_close(got[rows], ref, TOL, f"prefill square {_fam_id(fam)} {o}")
 
 
 @pytest.mark.parametrize("name,seq", [("prefill_bf16", 5), ("chunked_bf16", 11)])
