@@ -9,7 +9,7 @@ namespace pa {
 // Query columns of one workgroup: (query token, query head) pairs of one KV
 // head, one or two 16-column MFMA tiles per wave (tiles_per_wave).
 constexpr int kPrefillMaxCols = 16 * 2 * kWaves;
-// Keys per step of the prefill loop (two 16-key MFMA sub-tiles).
+// Keys per step of the prefill loop (16-key MFMA sub-tiles; a multiple of 32).
 constexpr int kPrefillStep = 32;
 
 struct PrefillParams {

@@ -32,9 +32,12 @@ __global__ void __launch_bounds__(kThreads) pa_prefill_kernel(const PrefillParam
   constexpr int VP = kPrefillStep + 8;         // padded V^T row in LDS (keys)
   constexpr int CPR = D / 8;                   // 16-byte chunks per key row
   constexpr int NLK = kPrefillStep * CPR / kThreads;  // K chunks per thread per step
-  constexpr int VTHREADS = (kPrefillStep / 2) * CPR;  // threads loading V key pairs
+  constexpr int VTASKS = (kPrefillStep / 2) * CPR;    // (key pair, chunk) V tasks per step
+  constexpr int NLV = (VTASKS + kThreads - 1) / kThreads;  // V tasks per thread
+  constexpr int NSUB = kPrefillStep / 16;      // 16-key sub-tiles per step
+  constexpr int NHALF = kPrefillStep / 32;     // 32-key P.V slices per step
   static_assert(NLK >= 1 && NLK * kThreads == kPrefillStep * CPR, "K tile geometry");
-  static_assert(VTHREADS <= kThreads, "V tile geometry");
+  static_assert(VTASKS % kThreads == 0 || VTASKS < kThreads, "V tile geometry");
   static_assert(kPrefillStep % BS == 0, "a step covers whole blocks");
 
   __shared__ __attribute__((aligned(16))) QT sk[kPrefillStep][KP];
@@ -126,7 +129,7 @@ __global__ void __launch_bounds__(kThreads) pa_prefill_kernel(const PrefillParam
   // of V; keys at or past nk are zero.
   struct Stage {
     u32x4 k[NLK];
-    u32x4 v[2];
+    u32x4 v[NLV][2];
   };
   auto load_stage = [&](int base) {
     Stage st;
@@ -136,12 +139,16 @@ __global__ void __launch_bounds__(kThreads) pa_prefill_kernel(const PrefillParam
       const int t = base + key;
       st.k[i] = t < nk ? load16(kcache + key_row(t) + ch * 16) : u32x4{0u, 0u, 0u, 0u};
     }
-    st.v[0] = st.v[1] = u32x4{0u, 0u, 0u, 0u};
-    if (threadIdx.x < VTHREADS) {
-      const int kp = threadIdx.x % (kPrefillStep / 2), ch = threadIdx.x / (kPrefillStep / 2);
+#pragma unroll
+    for (int i = 0; i < NLV; ++i) {
+      const int c = threadIdx.x + kThreads * i;
+      const int kp = c % (kPrefillStep / 2), ch = c / (kPrefillStep / 2);
       const int t = base + 2 * kp;
-      if (t < nk) st.v[0] = load16(vcache + key_row(t) + ch * 16);
-      if (t + 1 < nk) st.v[1] = load16(vcache + key_row(t + 1) + ch * 16);
+      st.v[i][0] = st.v[i][1] = u32x4{0u, 0u, 0u, 0u};
+      if (c < VTASKS) {
+        if (t < nk) st.v[i][0] = load16(vcache + key_row(t) + ch * 16);
+        if (t + 1 < nk) st.v[i][1] = load16(vcache + key_row(t + 1) + ch * 16);
+      }
     }
     return st;
   };
@@ -151,15 +158,19 @@ __global__ void __launch_bounds__(kThreads) pa_prefill_kernel(const PrefillParam
       const int c = threadIdx.x + kThreads * i, key = c / CPR, ch = c % CPR;
       *reinterpret_cast<u32x4 *>(&sk[key][ch * 8]) = st.k[i];
     }
-    if (threadIdx.x < VTHREADS) {
-      const int kp = threadIdx.x % (kPrefillStep / 2), ch = threadIdx.x / (kPrefillStep / 2);
-      const unsigned a[4] = {st.v[0].x, st.v[0].y, st.v[0].z, st.v[0].w};
-      const unsigned b[4] = {st.v[1].x, st.v[1].y, st.v[1].z, st.v[1].w};
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const unsigned lo16 = (a[e / 2] >> (16 * (e % 2))) & 0xffffu;
-        const unsigned hi16 = (b[e / 2] >> (16 * (e % 2))) & 0xffffu;
-        *reinterpret_cast<unsigned *>(&sv[ch * 8 + e][2 * kp]) = lo16 | (hi16 << 16);
+    for (int i = 0; i < NLV; ++i) {
+      const int c = threadIdx.x + kThreads * i;
+      const int kp = c % (kPrefillStep / 2), ch = c / (kPrefillStep / 2);
+      if (c < VTASKS) {
+        const unsigned a[4] = {st.v[i][0].x, st.v[i][0].y, st.v[i][0].z, st.v[i][0].w};
+        const unsigned b[4] = {st.v[i][1].x, st.v[i][1].y, st.v[i][1].z, st.v[i][1].w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const unsigned lo16 = (a[e / 2] >> (16 * (e % 2))) & 0xffffu;
+          const unsigned hi16 = (b[e / 2] >> (16 * (e % 2))) & 0xffffu;
+          *reinterpret_cast<unsigned *>(&sv[ch * 8 + e][2 * kp]) = lo16 | (hi16 << 16);
+        }
       }
     }
   };
@@ -176,30 +187,30 @@ __global__ void __launch_bounds__(kThreads) pa_prefill_kernel(const PrefillParam
 
   auto compute = [&](int base) {
     // S^T of every column tile; each K fragment read from LDS feeds NT MFMAs.
-    f32x4 s[NT][2];
+    f32x4 sc[NT][NSUB];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
+    for (int h = 0; h < NSUB; ++h) {
 #pragma unroll
-      for (int j = 0; j < NT; ++j) s[j][h] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      for (int j = 0; j < NT; ++j) sc[j][h] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
         const u32x4 a = *reinterpret_cast<const u32x4 *>(&sk[16 * h + n][32 * ks + 8 * g]);
 #pragma unroll
-        for (int j = 0; j < NT; ++j) s[j][h] = mfma_qk(a, qop[j][ks], s[j][h], QT());
+        for (int j = 0; j < NT; ++j) sc[j][h] = mfma_qk(a, qop[j][ks], sc[j][h], QT());
       }
     }
-    u32x4 pop[NT];
+    u32x4 pop[NT][NHALF];
     float alpha[NT];
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
-      float x[2][4];
+      float x[NSUB][4];
       float bm = -__builtin_inff();
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
+      for (int h = 0; h < NSUB; ++h)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int t = base + 16 * h + 4 * g + e;
-          const float v = scaled_logit<CAP>(p, s[j][h][e]);
+          const float v = scaled_logit<CAP>(p, sc[j][h][e]);
           x[h][e] = (t >= vlo[j] && t < vhi[j]) ? v : -__builtin_inff();
           bm = fmaxf(bm, x[h][e]);
         }
@@ -208,9 +219,9 @@ __global__ void __launch_bounds__(kThreads) pa_prefill_kernel(const PrefillParam
       alpha[j] = (m_new == -__builtin_inff()) ? 1.0f : fast_exp2(m_run[j] - m_new);
       m_run[j] = m_new;
       float psum = 0.0f;
-      u32x2 pk[2];
+      u32x2 pk[NSUB];
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
+      for (int h = 0; h < NSUB; ++h) {
         float pe[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -220,14 +231,21 @@ __global__ void __launch_bounds__(kThreads) pa_prefill_kernel(const PrefillParam
         pk[h] = u32x2{pack2(pe[0], pe[1], QT()), pack2(pe[2], pe[3], QT())};
       }
       l_run[j] = l_run[j] * alpha[j] + psum;
-      pop[j] = regroup_p(pk[0], pk[1]);
+#pragma unroll
+      for (int hf = 0; hf < NHALF; ++hf) pop[j][hf] = regroup_p(pk[2 * hf], pk[2 * hf + 1]);
     }
-    // O^T += V^T . P^T; each V fragment read from LDS feeds NT MFMAs.
+    // O^T += V^T . P^T per 32-key slice; each V fragment read from LDS feeds
+    // NT MFMAs.
 #pragma unroll
     for (int t = 0; t < NDT; ++t) {
-      const u32x4 va = *reinterpret_cast<const u32x4 *>(&sv[16 * t + n][8 * (g ^ 1)]);
 #pragma unroll
-      for (int j = 0; j < NT; ++j) oacc[j][t] = mfma_pv(va, pop[j], oacc[j][t] * alpha[j], QT());
+      for (int hf = 0; hf < NHALF; ++hf) {
+        const u32x4 va =
+            *reinterpret_cast<const u32x4 *>(&sv[16 * t + n][32 * hf + 8 * (g ^ 1)]);
+#pragma unroll
+        for (int j = 0; j < NT; ++j)
+          oacc[j][t] = mfma_pv(va, pop[j][hf], hf == 0 ? oacc[j][t] * alpha[j] : oacc[j][t], QT());
+      }
     }
   };
 
@@ -237,7 +255,7 @@ __global__ void __launch_bounds__(kThreads) pa_prefill_kernel(const PrefillParam
   // current step is computed, then replace it between two barriers.  (A
   // two-buffer, one-barrier pipeline measured slower: the second buffer
   // cost occupancy.)
-  int base = (int)(lo & ~(long long)(kPrefillStep - 1));
+  int base = (int)(lo - lo % BS);  // steps start on a block boundary: earlier blocks are never read
   if (base < hi) {
     Stage st = load_stage(base);
     store_stage(st);
