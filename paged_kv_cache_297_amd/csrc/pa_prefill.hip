@@ -23,8 +23,17 @@
 
 namespace pa {
 
+// Waves per SIMD the register allocator must leave room for: three with one
+// column tile per wave, two with two.
+template <int NT>
+constexpr int prefill_waves_per_eu() {
+  return NT == 1 ? 3 : 2;
+}
+
 template <typename QT, int D, int BS, int NT, bool CAP>
-__global__ void __launch_bounds__(kThreads) pa_prefill_kernel(const PrefillParams p) {
+__global__ void __launch_bounds__(kThreads)
+    __attribute__((amdgpu_waves_per_eu(prefill_waves_per_eu<NT>())))
+    pa_prefill_kernel(const PrefillParams p) {
   // NT: 16-column MFMA tiles per wave
   constexpr int NKS = D / 32;                  // 32-dim k-steps of QK^T
   constexpr int NDT = D / 16;                  // 16-dim output tiles
@@ -256,18 +265,46 @@ __global__ void __launch_bounds__(kThreads) pa_prefill_kernel(const PrefillParam
   // two-buffer, one-barrier pipeline measured slower: the second buffer
   // cost occupancy.)
   int base = (int)(lo - lo % BS);  // steps start on a block boundary: earlier blocks are never read
-  if (base < hi) {
-    Stage st = load_stage(base);
-    store_stage(st);
-    __syncthreads();
-    for (; base < hi; base += kPrefillStep) {
-      const bool more = base + kPrefillStep < hi;
-      if (more) st = load_stage(base + kPrefillStep);
-      compute(base);
+  if constexpr (NT == 1) {
+    // With one column tile the registers allow a second stage: loads run
+    // two steps ahead (the last step's loads repeat it, so every load is
+    // issued and each wait covers only the stage it needs).
+    const int n_steps = base < hi ? (int)((hi - base + kPrefillStep - 1) / kPrefillStep) : 0;
+    if (n_steps > 0) {
+      auto step_base = [&](int s) { return base + kPrefillStep * min(s, n_steps - 1); };
+      Stage sa = load_stage(step_base(0));
+      Stage sb = load_stage(step_base(1));
+      store_stage(sa);
       __syncthreads();
-      if (more) {
-        store_stage(st);
+      for (int s = 0;; s += 2) {
+        sa = load_stage(step_base(s + 2));
+        compute(base + kPrefillStep * s);
         __syncthreads();
+        if (s + 1 >= n_steps) break;
+        store_stage(sb);  // step s + 1
+        __syncthreads();
+        sb = load_stage(step_base(s + 3));
+        compute(base + kPrefillStep * (s + 1));
+        __syncthreads();
+        if (s + 2 >= n_steps) break;
+        store_stage(sa);  // step s + 2
+        __syncthreads();
+      }
+    }
+  } else {
+    if (base < hi) {
+      Stage st = load_stage(base);
+      store_stage(st);
+      __syncthreads();
+      for (; base < hi; base += kPrefillStep) {
+        const bool more = base + kPrefillStep < hi;
+        if (more) st = load_stage(base + kPrefillStep);
+        compute(base);
+        __syncthreads();
+        if (more) {
+          store_stage(st);
+          __syncthreads();
+        }
       }
     }
   }
