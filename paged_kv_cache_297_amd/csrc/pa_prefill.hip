@@ -122,16 +122,26 @@ __global__ void __launch_bounds__(kThreads)
   const char *vcache = reinterpret_cast<const char *>(p.value_cache);
   const const_i32_ptr btab =
       as_const_table(p.block_tables + (size_t)seq * p.max_num_blocks_per_seq);
-  // Byte offset of key t's row; an out-of-range table entry reads block 0
-  // and poisons the workgroup's result.
+  // A step covers NB whole blocks (it starts on a block boundary); their
+  // table entries are uniform, read once per step.  An out-of-range entry
+  // reads block 0 and poisons the workgroup's result.
+  constexpr int NB = kPrefillStep / BS;
+  const size_t head_off = (size_t)kvh * BS * D * sizeof(QT);
+  const size_t blk_stride = (size_t)p.num_kv_heads * BS * D * sizeof(QT);
   bool poisoned = false;
-  auto key_row = [&](int t) -> size_t {
-    int phys = btab[t / BS];
-    if (phys < 0 || phys >= p.num_blocks) {
-      poisoned = true;
-      phys = 0;
+  auto step_blocks = [&](int base, size_t (&boff)[NB]) {
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      int phys = 0;
+      if (base + b * BS < nk) {
+        phys = btab[base / BS + b];
+        if (phys < 0 || phys >= p.num_blocks) {
+          poisoned = true;
+          phys = 0;
+        }
+      }
+      boff[b] = (size_t)phys * blk_stride + head_off;
     }
-    return (((size_t)phys * p.num_kv_heads + kvh) * BS + t % BS) * D * sizeof(QT);
   };
 
   // One step's tiles in registers: K chunks (row-major) and two keys' chunks
@@ -141,22 +151,25 @@ __global__ void __launch_bounds__(kThreads)
     u32x4 v[NLV][2];
   };
   auto load_stage = [&](int base) {
+    size_t boff[NB];
+    step_blocks(base, boff);
     Stage st;
 #pragma unroll
     for (int i = 0; i < NLK; ++i) {
       const int c = threadIdx.x + kThreads * i, key = c / CPR, ch = c % CPR;
-      const int t = base + key;
-      st.k[i] = t < nk ? load16(kcache + key_row(t) + ch * 16) : u32x4{0u, 0u, 0u, 0u};
+      const size_t off = boff[key / BS] + ((key % BS) * D + ch * 8) * sizeof(QT);
+      st.k[i] = base + key < nk ? load16(kcache + off) : u32x4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
     for (int i = 0; i < NLV; ++i) {
       const int c = threadIdx.x + kThreads * i;
       const int kp = c % (kPrefillStep / 2), ch = c / (kPrefillStep / 2);
-      const int t = base + 2 * kp;
+      const int key = 2 * kp;  // keys key, key + 1: one block (block sizes are even)
+      const size_t off = boff[key / BS] + ((key % BS) * D + ch * 8) * sizeof(QT);
       st.v[i][0] = st.v[i][1] = u32x4{0u, 0u, 0u, 0u};
       if (c < VTASKS) {
-        if (t < nk) st.v[i][0] = load16(vcache + key_row(t) + ch * 16);
-        if (t + 1 < nk) st.v[i][1] = load16(vcache + key_row(t + 1) + ch * 16);
+        if (base + key < nk) st.v[i][0] = load16(vcache + off);
+        if (base + key + 1 < nk) st.v[i][1] = load16(vcache + off + D * sizeof(QT));
       }
     }
     return st;
@@ -174,12 +187,12 @@ __global__ void __launch_bounds__(kThreads)
       if (c < VTASKS) {
         const unsigned a[4] = {st.v[i][0].x, st.v[i][0].y, st.v[i][0].z, st.v[i][0].w};
         const unsigned b[4] = {st.v[i][1].x, st.v[i][1].y, st.v[i][1].z, st.v[i][1].w};
+        // Dim e of the two keys as one dword: the 16-bit halves e % 2 of
+        // word e / 2 of each key (byte permute: bytes 0-3 from a, 4-7 from b).
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const unsigned lo16 = (a[e / 2] >> (16 * (e % 2))) & 0xffffu;
-          const unsigned hi16 = (b[e / 2] >> (16 * (e % 2))) & 0xffffu;
-          *reinterpret_cast<unsigned *>(&sv[ch * 8 + e][2 * kp]) = lo16 | (hi16 << 16);
-        }
+        for (int e = 0; e < 8; ++e)
+          *reinterpret_cast<unsigned *>(&sv[ch * 8 + e][2 * kp]) =
+              __builtin_amdgcn_perm(b[e / 2], a[e / 2], (e % 2) ? 0x07060302u : 0x05040100u);
       }
     }
   };
@@ -195,6 +208,12 @@ __global__ void __launch_bounds__(kThreads)
   }
 
   auto compute = [&](int base) {
+    // Every valid column of the wave sees the whole step: no masks needed.
+    bool inside = true;
+#pragma unroll
+    for (int j = 0; j < NT; ++j)
+      inside &= !col_ok[j] || (base >= vlo[j] && base + kPrefillStep <= vhi[j]);
+    const bool full = __all(inside);
     // S^T of every column tile; each K fragment read from LDS feeds NT MFMAs.
     f32x4 sc[NT][NSUB];
 #pragma unroll
@@ -220,7 +239,7 @@ __global__ void __launch_bounds__(kThreads)
         for (int e = 0; e < 4; ++e) {
           const int t = base + 16 * h + 4 * g + e;
           const float v = scaled_logit<CAP>(p, sc[j][h][e]);
-          x[h][e] = (t >= vlo[j] && t < vhi[j]) ? v : -__builtin_inff();
+          x[h][e] = (full || (t >= vlo[j] && t < vhi[j])) ? v : -__builtin_inff();
           bm = fmaxf(bm, x[h][e]);
         }
       bm = xor_max<32>(xor_max<16>(bm));
@@ -243,6 +262,16 @@ __global__ void __launch_bounds__(kThreads)
 #pragma unroll
       for (int hf = 0; hf < NHALF; ++hf) pop[j][hf] = regroup_p(pk[2 * hf], pk[2 * hf + 1]);
     }
+    // Rescale the accumulators only when some column's max moved.
+    bool same = true;
+#pragma unroll
+    for (int j = 0; j < NT; ++j) same &= alpha[j] == 1.0f;
+    if (!__all(same)) {
+#pragma unroll
+      for (int j = 0; j < NT; ++j)
+#pragma unroll
+        for (int t = 0; t < NDT; ++t) oacc[j][t] = oacc[j][t] * alpha[j];
+    }
     // O^T += V^T . P^T per 32-key slice; each V fragment read from LDS feeds
     // NT MFMAs.
 #pragma unroll
@@ -252,8 +281,7 @@ __global__ void __launch_bounds__(kThreads)
         const u32x4 va =
             *reinterpret_cast<const u32x4 *>(&sv[16 * t + n][32 * hf + 8 * (g ^ 1)]);
 #pragma unroll
-        for (int j = 0; j < NT; ++j)
-          oacc[j][t] = mfma_pv(va, pop[j][hf], hf == 0 ? oacc[j][t] * alpha[j] : oacc[j][t], QT());
+        for (int j = 0; j < NT; ++j) oacc[j][t] = mfma_pv(va, pop[j][hf], oacc[j][t], QT());
       }
     }
   };
