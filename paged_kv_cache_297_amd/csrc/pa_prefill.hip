@@ -231,32 +231,56 @@ __global__ void __launch_bounds__(kThreads)
     float alpha[NT];
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
-      float x[NSUB][4];
-      float bm = -__builtin_inff();
-#pragma unroll
-      for (int h = 0; h < NSUB; ++h)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int t = base + 16 * h + 4 * g + e;
-          const float v = scaled_logit<CAP>(p, sc[j][h][e]);
-          x[h][e] = (full || (t >= vlo[j] && t < vhi[j])) ? v : -__builtin_inff();
-          bm = fmaxf(bm, x[h][e]);
-        }
-      bm = xor_max<32>(xor_max<16>(bm));
-      const float m_new = fmaxf(m_run[j], bm);
-      alpha[j] = (m_new == -__builtin_inff()) ? 1.0f : fast_exp2(m_run[j] - m_new);
-      m_run[j] = m_new;
       float psum = 0.0f;
       u32x2 pk[NSUB];
+      if (!CAP && full) {
+        // Every key visible and no cap: the max of the raw dot products
+        // scaled once, and each weight one fma and one exp2.
+        float bm = -__builtin_inff();
 #pragma unroll
-      for (int h = 0; h < NSUB; ++h) {
-        float pe[4];
+        for (int h = 0; h < NSUB; ++h)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          pe[e] = x[h][e] == -__builtin_inff() ? 0.0f : fast_exp2(x[h][e] - m_new);
-          psum += pe[e];
+          for (int e = 0; e < 4; ++e) bm = fmaxf(bm, sc[j][h][e]);
+        bm = xor_max<32>(xor_max<16>(bm)) * p.scale_log2;
+        const float m_new = fmaxf(m_run[j], bm);
+        alpha[j] = fast_exp2(m_run[j] - m_new);  // m_run = -inf: 0, l_run and oacc are 0
+        m_run[j] = m_new;
+#pragma unroll
+        for (int h = 0; h < NSUB; ++h) {
+          float pe[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            pe[e] = fast_exp2(fmaf(sc[j][h][e], p.scale_log2, -m_new));
+            psum += pe[e];
+          }
+          pk[h] = u32x2{pack2(pe[0], pe[1], QT()), pack2(pe[2], pe[3], QT())};
         }
-        pk[h] = u32x2{pack2(pe[0], pe[1], QT()), pack2(pe[2], pe[3], QT())};
+      } else {
+        float x[NSUB][4];
+        float bm = -__builtin_inff();
+#pragma unroll
+        for (int h = 0; h < NSUB; ++h)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int t = base + 16 * h + 4 * g + e;
+            const float v = scaled_logit<CAP>(p, sc[j][h][e]);
+            x[h][e] = (full || (t >= vlo[j] && t < vhi[j])) ? v : -__builtin_inff();
+            bm = fmaxf(bm, x[h][e]);
+          }
+        bm = xor_max<32>(xor_max<16>(bm));
+        const float m_new = fmaxf(m_run[j], bm);
+        alpha[j] = (m_new == -__builtin_inff()) ? 1.0f : fast_exp2(m_run[j] - m_new);
+        m_run[j] = m_new;
+#pragma unroll
+        for (int h = 0; h < NSUB; ++h) {
+          float pe[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            pe[e] = x[h][e] == -__builtin_inff() ? 0.0f : fast_exp2(x[h][e] - m_new);
+            psum += pe[e];
+          }
+          pk[h] = u32x2{pack2(pe[0], pe[1], QT()), pack2(pe[2], pe[3], QT())};
+        }
       }
       l_run[j] = l_run[j] * alpha[j] + psum;
 #pragma unroll
