@@ -46,12 +46,15 @@ def log(msg: str) -> None:
     print(msg, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash() -> str:
-    """Hash of every library source file: counter figures taken on other
-    sources are not reported."""
+def kernel_source_hash(prefill: bool = False) -> str:
+    """Hash of the library sources a measurement depends on (the decode path:
+    every source but the prefill kernel's own files; prefill: every source):
+    counter figures taken on other sources are not reported."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "paged_kv_cache_297_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
+        if not prefill and name.startswith("pa_prefill"):
+            continue
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
@@ -230,7 +233,7 @@ def bench_prefill(args) -> int:
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
                      "algorithmic_flops_per_launch": flops, "avg_launch_ms": round(kavg, 5),
-                     "kernel_source_hash": kernel_source_hash()},
+                     "kernel_source_hash": kernel_source_hash(prefill=True)},
     }
     print(json.dumps(result), flush=True)
     return 0
