@@ -19,7 +19,9 @@ roofline (the recording adds a few microseconds per step, so it is not part
 of the wall-clock region).  The fp64 CPU oracle is timed on a bounded sample of the same
 workload for the CPU baseline.  ``--window W`` / ``--softcap C`` turn on the
 decode options (sliding window over the last W + 1 keys, logit soft cap);
-the KV bytes then count the keys inside the window only.
+the KV bytes then count the keys inside the window only.  ``--layout
+block_rows`` repacks the same caches into the [num_blocks, num_kv_heads,
+block_size, head_size] layout and times the kernels for that layout.
 
 Prints one JSON line (stdout); progress goes to stderr.
 """
@@ -256,6 +258,8 @@ def main() -> int:
                     help="sliding window: attend to the last W + 1 keys (-1: off)")
     ap.add_argument("--softcap", type=float, default=0.0, metavar="C",
                     help="logit soft cap C * tanh(s / C) (0: off)")
+    ap.add_argument("--layout", default="decode", choices=["decode", "block_rows"],
+                    help="KV cache layout of the decode call (16-bit caches for block_rows)")
     ap.add_argument("--prefill", default=None, choices=["prefill_bf16", "chunked_bf16"],
                     help="time paged prefill on this workload instead of decode")
     args = ap.parse_args()
@@ -283,6 +287,9 @@ def main() -> int:
     log(f"building workload {args.workload} x{copies}")
     wls = [W.make_workload(args.workload, device="cuda", seed=1000 + args.workload)]
     base = wls[0]
+    if args.layout == "block_rows":
+        base.key_cache, base.value_cache = W.to_block_rows(base.key_cache, base.value_cache)
+        torch.cuda.empty_cache()
     for c in range(1, copies):
         # Same bytes at other addresses: identical work, no cache reuse across steps.
         w2 = W.Workload(**{**base.__dict__})
@@ -305,7 +312,8 @@ def main() -> int:
                   wl.scale, wl.block_tables, wl.seq_lens, wl.block_size, wl.max_seq_len)
         kw = dict(alibi_slopes=wl.alibi_slopes, kv_cache_dtype=wl.kv_cache_dtype,
                   k_scale=wl.k_scale, v_scale=wl.v_scale, stream=stream,
-                  window_left=args.window, logits_soft_cap=args.softcap)
+                  window_left=args.window, logits_soft_cap=args.softcap,
+                  kv_layout=args.layout)
         if args.path == "v1":
             calls.append(lambda out=out, wl=wl, kw=kw: B.paged_attention_v1(
                 out, wl.query, wl.key_cache, wl.value_cache, wl.num_kv_heads, wl.scale,
@@ -373,7 +381,7 @@ def main() -> int:
     src_hash = kernel_source_hash()
     options = args.window != -1 or args.softcap != 0.0
     traffic = (read_traffic(base.name, src_hash, args.path)
-               if copies > 1 and not options else None)
+               if copies > 1 and not options and args.layout == "decode" else None)
     dtype = {torch.float32: "f32", torch.float16: "f16", torch.bfloat16: "bf16"}[base.dtype]
     if base.kv_cache_dtype == "fp8_e4m3":
         dtype = f"{dtype} (fp8 e4m3 KV)"
@@ -399,18 +407,21 @@ def main() -> int:
                          f"head_size={base.head_size}, block_size={base.block_size}, "
                          f"seq_lens {int(lens.min())}..{int(lens.max())} "
                          f"(sum {int(lens.sum())}), path={args.path}"
+                         + (f", kv_layout={args.layout}" if args.layout != "decode" else "")
                          + (f", window_left={args.window}, soft_cap={args.softcap:g}"
                             if options else "")),
             "path": args.path,
             "window_left": args.window,
             "logits_soft_cap": args.softcap,
+            "kv_layout": args.layout,
             "kv_bytes_per_step": ab["kv"],
             "inputs": ("cache-hot single copy" if copies == 1 else
                        f"{copies} rotating copies of the KV pool (L2/MALL-cold)"),
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "pa_partition (Phase 1)",
+            "kernel": ("pa_partition (Phase 1)" if args.layout == "decode"
+                       else "pa_partition_nhd (Phase 1, block-rows layout)"),
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",

@@ -107,6 +107,14 @@ typedef enum pa_kv_cache_dtype { PA_KV_AUTO = 0, PA_KV_FP8_E4M3 = 1 } pa_kv_cach
  * device, with the rule of pa_should_use_v2. */
 typedef enum pa_mode { PA_MODE_V1 = 0, PA_MODE_V2 = 1, PA_MODE_AUTO = 2 } pa_mode;
 
+/* Cache layouts a decode call reads.  DECODE is the V2 page's layout (K
+ * [num_blocks, num_kv_heads, head_size/x, block_size, x], V [num_blocks,
+ * num_kv_heads, head_size, block_size]).  BLOCK_ROWS is the dispatch page's
+ * decode signature: K and V both [num_blocks, num_kv_heads, block_size,
+ * head_size] (each token's head_size values contiguous); dtype f16 or bf16
+ * and kv_cache_dtype AUTO only (others: PA_ERR_UNSUPPORTED). */
+typedef enum pa_kv_layout { PA_KV_LAYOUT_DECODE = 0, PA_KV_LAYOUT_BLOCK_ROWS = 1 } pa_kv_layout;
+
 /* Decode options of the *_ex entry points: the sliding window and the logit
  * soft cap of the dispatch page's decode configuration (AttnDispatchConfig
  * fields window_left and softcap, -1 and 0 meaning off), which the Neuron
@@ -125,12 +133,14 @@ typedef enum pa_mode { PA_MODE_V1 = 0, PA_MODE_V2 = 1, PA_MODE_AUTO = 2 } pa_mod
  * partition with no key inside the window gets max_logits = -inf and
  * exp_sums = 0 (as the V2 page's unused partitions) and no tmp_out row;
  * the auto rule (pa_should_use_v2) is applied to the window-clipped length
- * min(L, W + 1).  A NULL options pointer means both off: the *_ex call is then
- * the plain call.  window_left < -1, or a cap that is negative, infinite or
- * NaN, returns PA_ERR_BAD_ARGUMENT. */
+ * min(L, W + 1).  kv_layout selects the cache layout (pa_kv_layout).  A NULL
+ * options pointer means no window, no cap and the DECODE layout: the *_ex
+ * call is then the plain call.  window_left < -1, a cap that is negative,
+ * infinite or NaN, or an unknown layout returns PA_ERR_BAD_ARGUMENT. */
 typedef struct pa_decode_options {
   int window_left;
   float logits_soft_cap;
+  int kv_layout;  /* pa_kv_layout of key_cache / value_cache */
 } pa_decode_options;
 
 /* ---------------------------------------------------------------------- */

@@ -29,6 +29,9 @@ STATUS_NAMES = {0: "PA_OK", 1: "PA_ERR_NULL_POINTER", 2: "PA_ERR_BAD_SHAPE",
 DTYPE_CODE = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
 KV_CODE = {"auto": 0, "fp8": 1, "fp8_e4m3": 1}
 MODE_CODE = {"v1": 0, "v2": 1, "auto": 2}
+#: pa_kv_layout: "decode" (K [NB, Hkv, D/x, bs, x], V [NB, Hkv, D, bs]) or
+#: "block_rows" (K and V [NB, Hkv, bs, D]).
+LAYOUT_CODE = {"decode": 0, "block_rows": 1}
 
 #: Every symbol include/pagedattn.h declares.
 EXPORTED_SYMBOLS = (
@@ -49,8 +52,10 @@ class PrefillOptions(ctypes.Structure):
 
 
 class DecodeOptions(ctypes.Structure):
-    """pa_decode_options: sliding window (-1: none) and logit soft cap (0: none)."""
-    _fields_ = [("window_left", ctypes.c_int), ("logits_soft_cap", ctypes.c_float)]
+    """pa_decode_options: sliding window (-1: none), logit soft cap (0: none) and
+    the cache layout (LAYOUT_CODE)."""
+    _fields_ = [("window_left", ctypes.c_int), ("logits_soft_cap", ctypes.c_float),
+                ("kv_layout", ctypes.c_int)]
 
 
 class PagedAttentionError(RuntimeError):
@@ -146,11 +151,19 @@ def _kv_code(kv_cache_dtype: str) -> int:
     return KV_CODE[kv_cache_dtype]
 
 
-def _options(window_left: int, logits_soft_cap: float) -> Optional[DecodeOptions]:
-    """None when both options are off (the plain entry point is called)."""
-    if int(window_left) == -1 and float(logits_soft_cap) == 0.0:
+def _layout_code(kv_layout: str) -> int:
+    if kv_layout not in LAYOUT_CODE:
+        raise ValueError(f"kv_layout must be one of {sorted(LAYOUT_CODE)}")
+    return LAYOUT_CODE[kv_layout]
+
+
+def _options(window_left: int, logits_soft_cap: float,
+             kv_layout: str = "decode") -> Optional[DecodeOptions]:
+    """None when every option is off (the plain entry point is called)."""
+    code = _layout_code(kv_layout)
+    if int(window_left) == -1 and float(logits_soft_cap) == 0.0 and code == 0:
         return None
-    return DecodeOptions(int(window_left), float(logits_soft_cap))
+    return DecodeOptions(int(window_left), float(logits_soft_cap), code)
 
 
 def _call(lib, name: str, args, opts: Optional[DecodeOptions]) -> None:
@@ -162,8 +175,10 @@ def _call(lib, name: str, args, opts: Optional[DecodeOptions]) -> None:
                name + "_ex")
 
 
-def _geometry(query, key_cache, value_cache, block_tables, seq_lens, kv_cache_dtype):
-    """Checks layouts and returns (num_seqs, num_heads, head_size, num_blocks, max_blocks)."""
+def _geometry(query, key_cache, value_cache, block_tables, seq_lens, kv_cache_dtype,
+              kv_layout="decode"):
+    """Checks layouts and returns (num_seqs, num_heads, head_size, num_blocks, Hkv,
+    block_size, max_blocks)."""
     for name, t in (("query", query), ("key_cache", key_cache), ("value_cache", value_cache),
                     ("block_tables", block_tables), ("seq_lens", seq_lens)):
         if not t.is_contiguous():
@@ -182,11 +197,19 @@ def _geometry(query, key_cache, value_cache, block_tables, seq_lens, kv_cache_dt
             raise TypeError("with kv_cache_dtype='auto' the caches must have the query dtype")
         elem = query.element_size()
     x = 16 // elem
-    nb, hkv, dx, bs, xx = key_cache.shape
-    if xx != x or dx * x != head_size:
-        raise ValueError(f"key_cache must be [num_blocks, Hkv, {head_size}/{x}, block_size, {x}]")
-    if tuple(value_cache.shape) != (nb, hkv, head_size, bs):
-        raise ValueError("value_cache must be [num_blocks, Hkv, head_size, block_size]")
+    if _layout_code(kv_layout) == 1:
+        if key_cache.dim() != 4 or key_cache.shape[3] != head_size:
+            raise ValueError("key_cache must be [num_blocks, Hkv, block_size, head_size]")
+        nb, hkv, bs, _ = key_cache.shape
+        if tuple(value_cache.shape) != tuple(key_cache.shape):
+            raise ValueError("value_cache must be [num_blocks, Hkv, block_size, head_size]")
+    else:
+        nb, hkv, dx, bs, xx = key_cache.shape
+        if xx != x or dx * x != head_size:
+            raise ValueError(
+                f"key_cache must be [num_blocks, Hkv, {head_size}/{x}, block_size, {x}]")
+        if tuple(value_cache.shape) != (nb, hkv, head_size, bs):
+            raise ValueError("value_cache must be [num_blocks, Hkv, head_size, block_size]")
     if block_tables.dim() != 2 or block_tables.shape[0] != num_seqs or seq_lens.shape != (num_seqs,):
         raise ValueError("block_tables must be [num_seqs, max_blocks] and seq_lens [num_seqs]")
     return num_seqs, num_heads, head_size, nb, hkv, bs, block_tables.shape[1]
@@ -197,12 +220,14 @@ def paged_attention_v1(out: torch.Tensor, query: torch.Tensor, key_cache: torch.
                        block_tables: torch.Tensor, seq_lens: torch.Tensor, block_size: int,
                        max_seq_len: int, alibi_slopes: Optional[torch.Tensor] = None,
                        kv_cache_dtype: str = "auto", k_scale: float = 1.0, v_scale: float = 1.0,
-                       stream=None, window_left: int = -1, logits_soft_cap: float = 0.0) -> None:
+                       stream=None, window_left: int = -1, logits_soft_cap: float = 0.0,
+                       kv_layout: str = "decode") -> None:
     """Whole-sequence paged attention; writes ``out`` in place.  ``window_left`` /
-    ``logits_soft_cap`` are the decode options (-1 / 0: off)."""
+    ``logits_soft_cap`` / ``kv_layout`` are the decode options (-1 / 0 / "decode":
+    off)."""
     lib = load_library()
     b, h, d, nb, hkv, bs, mbps = _geometry(query, key_cache, value_cache, block_tables, seq_lens,
-                                           kv_cache_dtype)
+                                           kv_cache_dtype, kv_layout)
     if hkv != num_kv_heads or bs != block_size:
         raise ValueError("num_kv_heads / block_size disagree with the cache shape")
     if out.shape != query.shape or out.dtype != query.dtype or not out.is_contiguous():
@@ -211,14 +236,14 @@ def paged_attention_v1(out: torch.Tensor, query: torch.Tensor, key_cache: torch.
             num_kv_heads, d, float(scale), block_tables.data_ptr(), mbps, seq_lens.data_ptr(), nb,
             block_size, int(max_seq_len), _ptr(alibi_slopes), DTYPE_CODE[query.dtype],
             _kv_code(kv_cache_dtype), float(k_scale), float(v_scale), _stream(stream)]
-    _call(lib, "paged_attention_v1", args, _options(window_left, logits_soft_cap))
+    _call(lib, "paged_attention_v1", args, _options(window_left, logits_soft_cap, kv_layout))
 
 
 def _v2_args(out, exp_sums, max_logits, tmp_out, query, key_cache, value_cache, num_kv_heads,
              scale, block_tables, seq_lens, block_size, max_seq_len, alibi_slopes,
-             kv_cache_dtype, k_scale, v_scale, stream):
+             kv_cache_dtype, k_scale, v_scale, stream, kv_layout="decode"):
     b, h, d, nb, hkv, bs, mbps = _geometry(query, key_cache, value_cache, block_tables, seq_lens,
-                                           kv_cache_dtype)
+                                           kv_cache_dtype, kv_layout)
     if hkv != num_kv_heads or bs != block_size:
         raise ValueError("num_kv_heads / block_size disagree with the cache shape")
     if out.shape != query.shape or out.dtype != query.dtype or not out.is_contiguous():
@@ -243,25 +268,27 @@ def _v2_args(out, exp_sums, max_logits, tmp_out, query, key_cache, value_cache, 
 def paged_attention_v2(out, exp_sums, max_logits, tmp_out, query, key_cache, value_cache,
                        num_kv_heads, scale, block_tables, seq_lens, block_size, max_seq_len,
                        alibi_slopes=None, kv_cache_dtype="auto", k_scale=1.0, v_scale=1.0,
-                       stream=None, window_left=-1, logits_soft_cap=0.0) -> None:
+                       stream=None, window_left=-1, logits_soft_cap=0.0,
+                       kv_layout="decode") -> None:
     """Partitioned paged attention (Phase 1 + Phase 2); writes all four outputs in place."""
     lib = load_library()
     args = _v2_args(out, exp_sums, max_logits, tmp_out, query, key_cache, value_cache,
                     num_kv_heads, scale, block_tables, seq_lens, block_size, max_seq_len,
-                    alibi_slopes, kv_cache_dtype, k_scale, v_scale, stream)
-    _call(lib, "paged_attention_v2", args, _options(window_left, logits_soft_cap))
+                    alibi_slopes, kv_cache_dtype, k_scale, v_scale, stream, kv_layout)
+    _call(lib, "paged_attention_v2", args, _options(window_left, logits_soft_cap, kv_layout))
 
 
 def paged_attention_auto(out, exp_sums, max_logits, tmp_out, query, key_cache, value_cache,
                          num_kv_heads, scale, block_tables, seq_lens, block_size, max_seq_len,
                          alibi_slopes=None, kv_cache_dtype="auto", k_scale=1.0, v_scale=1.0,
-                         stream=None, window_left=-1, logits_soft_cap=0.0) -> None:
+                         stream=None, window_left=-1, logits_soft_cap=0.0,
+                         kv_layout="decode") -> None:
     """Per-sequence v1/v2 choice on the device (pa_should_use_v2 rule)."""
     lib = load_library()
     args = _v2_args(out, exp_sums, max_logits, tmp_out, query, key_cache, value_cache,
                     num_kv_heads, scale, block_tables, seq_lens, block_size, max_seq_len,
-                    alibi_slopes, kv_cache_dtype, k_scale, v_scale, stream)
-    _call(lib, "paged_attention_auto", args, _options(window_left, logits_soft_cap))
+                    alibi_slopes, kv_cache_dtype, k_scale, v_scale, stream, kv_layout)
+    _call(lib, "paged_attention_auto", args, _options(window_left, logits_soft_cap, kv_layout))
 
 
 def split_counters(num_seqs: int, num_heads: int, device="cuda") -> torch.Tensor:
@@ -270,7 +297,8 @@ def split_counters(num_seqs: int, num_heads: int, device="cuda") -> torch.Tensor
 
 
 def _split_args(out, exp_sums, max_logits, tmp_out, counters, query, *rest, opts):
-    args = _v2_args(out, exp_sums, max_logits, tmp_out, query, *rest)
+    layout = "block_rows" if opts is not None and opts.kv_layout == 1 else "decode"
+    args = _v2_args(out, exp_sums, max_logits, tmp_out, query, *rest, kv_layout=layout)
     b, h = query.shape[0], query.shape[1]
     if counters.dtype != torch.int32 or not counters.is_contiguous() or counters.numel() < b * h:
         raise TypeError("counters must be a contiguous int32 tensor of num_seqs * num_heads")
@@ -281,11 +309,12 @@ def _split_args(out, exp_sums, max_logits, tmp_out, counters, query, *rest, opts
 def paged_attention_split(out, exp_sums, max_logits, tmp_out, counters, query, key_cache,
                           value_cache, num_kv_heads, scale, block_tables, seq_lens, block_size,
                           max_seq_len, alibi_slopes=None, kv_cache_dtype="auto", k_scale=1.0,
-                          v_scale=1.0, stream=None, window_left=-1, logits_soft_cap=0.0) -> None:
+                          v_scale=1.0, stream=None, window_left=-1, logits_soft_cap=0.0,
+                          kv_layout="decode") -> None:
     """Balanced split decode: writes ``out``; the partial buffers are scratch and
     ``counters`` (split_counters) must be zero on entry (it is left zero)."""
     lib = load_library()
-    opts = _options(window_left, logits_soft_cap)
+    opts = _options(window_left, logits_soft_cap, kv_layout)
     args = _split_args(out, exp_sums, max_logits, tmp_out, counters, query, key_cache,
                        value_cache, num_kv_heads, scale, block_tables, seq_lens, block_size,
                        max_seq_len, alibi_slopes, kv_cache_dtype, k_scale, v_scale, stream,
@@ -303,12 +332,13 @@ class PreparedCall:
     def __init__(self, mode, out, exp_sums, max_logits, tmp_out, query, key_cache, value_cache,
                  num_kv_heads, scale, block_tables, seq_lens, block_size, max_seq_len,
                  alibi_slopes=None, kv_cache_dtype="auto", k_scale=1.0, v_scale=1.0,
-                 stream=None, window_left=-1, logits_soft_cap=0.0, counters=None):
+                 stream=None, window_left=-1, logits_soft_cap=0.0, counters=None,
+                 kv_layout="decode"):
         self.lib = load_library()
         self.name = f"paged_attention_{mode}"
         if mode not in ("v2", "auto", "split"):
             raise ValueError("mode must be 'v2', 'auto' or 'split'")
-        self.opts = _options(window_left, logits_soft_cap)
+        self.opts = _options(window_left, logits_soft_cap, kv_layout)
         self.counters = counters
         if mode == "split":
             if counters is None:
@@ -323,7 +353,7 @@ class PreparedCall:
             return
         self.args = _v2_args(out, exp_sums, max_logits, tmp_out, query, key_cache, value_cache,
                              num_kv_heads, scale, block_tables, seq_lens, block_size, max_seq_len,
-                             alibi_slopes, kv_cache_dtype, k_scale, v_scale, stream)
+                             alibi_slopes, kv_cache_dtype, k_scale, v_scale, stream, kv_layout)
         if self.opts is None:
             self.fn = getattr(self.lib, self.name)
         else:
@@ -343,14 +373,14 @@ def paged_attention_partition(mode, out, exp_sums, max_logits, tmp_out, query, k
                               value_cache, num_kv_heads, scale, block_tables, seq_lens,
                               block_size, max_seq_len, alibi_slopes=None, kv_cache_dtype="auto",
                               k_scale=1.0, v_scale=1.0, stream=None, window_left=-1,
-                              logits_soft_cap=0.0) -> None:
+                              logits_soft_cap=0.0, kv_layout="decode") -> None:
     """Phase 1 only (mode 'v1', 'v2' or 'auto')."""
     lib = load_library()
     args = _v2_args(out, exp_sums, max_logits, tmp_out, query, key_cache, value_cache,
                     num_kv_heads, scale, block_tables, seq_lens, block_size, max_seq_len,
-                    alibi_slopes, kv_cache_dtype, k_scale, v_scale, stream)
+                    alibi_slopes, kv_cache_dtype, k_scale, v_scale, stream, kv_layout)
     _call(lib, "paged_attention_partition", [MODE_CODE[mode]] + args,
-          _options(window_left, logits_soft_cap))
+          _options(window_left, logits_soft_cap, kv_layout))
 
 
 def paged_attention_reduce(mode, out, exp_sums, max_logits, tmp_out, seq_lens, num_kv_heads,

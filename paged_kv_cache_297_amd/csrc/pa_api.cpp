@@ -111,6 +111,7 @@ struct Call {
   float k_scale, v_scale;
   int window_left;        // pa_decode_options (-1: no window)
   float logits_soft_cap;  // (0: no soft cap)
+  int kv_layout;          // pa_kv_layout
   int32_t *counters;      // paged_attention_split only (mode is then V2 for validation)
   bool split;
   hipStream_t stream;
@@ -120,11 +121,15 @@ struct Call {
 pa_status apply_options(const pa_decode_options *o, Call &c) {
   c.window_left = -1;
   c.logits_soft_cap = 0.0f;
+  c.kv_layout = PA_KV_LAYOUT_DECODE;
   if (!o) return PA_OK;
   if (o->window_left < -1) return PA_ERR_BAD_ARGUMENT;
   if (!isfinite(o->logits_soft_cap) || o->logits_soft_cap < 0.0f) return PA_ERR_BAD_ARGUMENT;
+  if (o->kv_layout != PA_KV_LAYOUT_DECODE && o->kv_layout != PA_KV_LAYOUT_BLOCK_ROWS)
+    return PA_ERR_BAD_ARGUMENT;
   c.window_left = o->window_left;
   c.logits_soft_cap = o->logits_soft_cap;
+  c.kv_layout = o->kv_layout;
   return PA_OK;
 }
 
@@ -203,6 +208,9 @@ pa_status validate_common(const Call &c, bool partition_phase) {
   if (c.kv_cache_dtype != PA_KV_AUTO && c.kv_cache_dtype != PA_KV_FP8_E4M3)
     return PA_ERR_BAD_ARGUMENT;
   if (c.kv_cache_dtype == PA_KV_FP8_E4M3 && c.dtype == PA_DTYPE_F32) return PA_ERR_UNSUPPORTED;
+  if (c.kv_layout == PA_KV_LAYOUT_BLOCK_ROWS &&
+      (c.dtype == PA_DTYPE_F32 || c.kv_cache_dtype != PA_KV_AUTO))
+    return PA_ERR_UNSUPPORTED;
   if (c.block_size != 16 && c.block_size != 32) return PA_ERR_UNSUPPORTED;
   if (pa::kPartitionSize % c.block_size != 0) return PA_ERR_UNSUPPORTED;
   if (!isfinite(c.scale) || !isfinite(c.k_scale) || !isfinite(c.v_scale))
@@ -230,8 +238,14 @@ struct Plan {
 Plan make_plan(const Call &c) {
   const int group = c.num_heads / c.num_kv_heads;
   Plan pl{};
-  pl.mfma = c.dtype != PA_DTYPE_F32 && group >= tunables().mfma_min_group;
-  if (pl.mfma) {
+  pl.mfma = c.kv_layout == PA_KV_LAYOUT_DECODE && c.dtype != PA_DTYPE_F32 &&
+            group >= tunables().mfma_min_group;
+  if (c.kv_layout == PA_KV_LAYOUT_BLOCK_ROWS) {
+    const int gmax = pa::nhd_max_group(c.head_size, c.block_size);
+    int p2 = 1;
+    while (p2 < group && p2 < gmax) p2 *= 2;
+    pl.gp = p2;
+  } else if (pl.mfma) {
     pl.gp = 16;
   } else {
     const int kv_bytes = c.kv_cache_dtype == PA_KV_FP8_E4M3 ? 1 : (c.dtype == PA_DTYPE_F32 ? 4 : 2);
@@ -324,7 +338,9 @@ pa_status run_partition(const Call &c) {
                      t_events.partition_stop};
   const bool fp8 = c.kv_cache_dtype == PA_KV_FP8_E4M3;
   hipError_t e;
-  if (pl.mfma) {
+  if (c.kv_layout == PA_KV_LAYOUT_BLOCK_ROWS) {
+    e = pa::launch_partition_nhd(p, (int)c.dtype, c.head_size, c.block_size, pl.gp, l);
+  } else if (pl.mfma) {
     e = pa::launch_partition_mfma(p, (int)c.dtype, fp8, c.head_size, c.block_size, l);
   } else if (fp8) {
     e = pa::launch_partition_valu_fp8(p, (int)c.dtype, c.head_size, c.block_size, pl.gp, l);
@@ -398,6 +414,7 @@ Call make_call(pa_mode mode, void *out, float *exp_sums, float *max_logits, void
   c.v_scale = v_scale;
   c.window_left = -1;
   c.logits_soft_cap = 0.0f;
+  c.kv_layout = PA_KV_LAYOUT_DECODE;
   c.counters = nullptr;
   c.split = false;
   c.stream = reinterpret_cast<hipStream_t>(stream);

@@ -41,6 +41,15 @@ constexpr int valu_max_group(int kv_bytes, int head_size, int block_size) {
   return p2;
 }
 
+// Largest power-of-two head group one workgroup holds for this layout: the
+// ping-pong tiles take 16 VGPRs per 1 KB load, each head 8 accumulators, 4
+// query words and NL logits; wider groups are split over grid.x (their
+// workgroups read the same tiles, adjacent in the grid, mostly from L2).
+// Two waves per SIMD at least.
+constexpr int nhd_max_group(int head_size, int block_size) {
+  return head_size * block_size * 2 / 1024 >= 8 ? 2 : 4;
+}
+
 hipError_t launch_partition_valu_f32(const Params &p, int head_size, int block_size, int gp,
                                      const Launch &l);
 hipError_t launch_partition_valu_f16(const Params &p, int head_size, int block_size, int gp,
@@ -53,5 +62,10 @@ hipError_t launch_partition_valu_fp8(const Params &p, int q_dtype, int head_size
 hipError_t launch_partition_mfma(const Params &p, int q_dtype, bool kv_fp8, int head_size,
                                  int block_size, const Launch &l);
 hipError_t launch_reduce(const Params &p, int dtype, int head_size, const Launch &l);
+
+// [num_blocks, Hkv, block_size, head_size] caches, 16-bit (q_dtype kDtF16 or
+// kDtBF16); gp = 1, 2 or 4 query heads per workgroup (nhd_max_group).
+hipError_t launch_partition_nhd(const Params &p, int q_dtype, int head_size, int block_size,
+                                int gp, const Launch &l);
 
 }  // namespace pa

@@ -1,0 +1,49 @@
+// Partition kernels for the [num_blocks, Hkv, block_size, head_size] cache
+// layout, 16-bit caches.
+#include "pa_launch.h"
+#include "pa_partition_nhd.h"
+
+namespace pa {
+
+template <typename QT, int D, int BS, int GP>
+static hipError_t launch_nhd_opts(const Params &p, const Launch &l) {
+  if constexpr (GP <= nhd_max_group(D, BS)) {
+    const bool win = p.window_left >= 0;
+    if (p.cap_on)
+      return win ? launch_kernel(pa_partition_nhd<QT, D, BS, GP, true, true>, l, p)
+                 : launch_kernel(pa_partition_nhd<QT, D, BS, GP, true, false>, l, p);
+    return win ? launch_kernel(pa_partition_nhd<QT, D, BS, GP, false, true>, l, p)
+               : launch_kernel(pa_partition_nhd<QT, D, BS, GP, false, false>, l, p);
+  } else {
+    return hipErrorInvalidValue;
+  }
+}
+
+template <typename QT, int D, int BS>
+static hipError_t launch_nhd_gp(const Params &p, int gp, const Launch &l) {
+  switch (gp) {
+    case 1: return launch_nhd_opts<QT, D, BS, 1>(p, l);
+    case 2: return launch_nhd_opts<QT, D, BS, 2>(p, l);
+    case 4: return launch_nhd_opts<QT, D, BS, 4>(p, l);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <typename QT>
+static hipError_t launch_nhd_t(const Params &p, int head_size, int block_size, int gp,
+                               const Launch &l) {
+  if (head_size == 64 && block_size == 16) return launch_nhd_gp<QT, 64, 16>(p, gp, l);
+  if (head_size == 64 && block_size == 32) return launch_nhd_gp<QT, 64, 32>(p, gp, l);
+  if (head_size == 128 && block_size == 16) return launch_nhd_gp<QT, 128, 16>(p, gp, l);
+  if (head_size == 128 && block_size == 32) return launch_nhd_gp<QT, 128, 32>(p, gp, l);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_partition_nhd(const Params &p, int q_dtype, int head_size, int block_size,
+                                int gp, const Launch &l) {
+  if (q_dtype == kDtF16) return launch_nhd_t<_Float16>(p, head_size, block_size, gp, l);
+  if (q_dtype == kDtBF16) return launch_nhd_t<__bf16>(p, head_size, block_size, gp, l);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace pa

@@ -258,6 +258,16 @@ def _poison(key_cache, value_cache, tables, seq_lens, bs, pool, fp8):
             value_cache[last, :, :, L % bs:] = nan_k
 
 
+def to_block_rows(key_cache: torch.Tensor, value_cache: torch.Tensor):
+    """The same 16-bit caches repacked from the decode layout (K [NB, Hkv, D/x,
+    bs, x], V [NB, Hkv, D, bs]) into the [NB, Hkv, bs, D] block-rows layout
+    (a copy; values unchanged)."""
+    nb, hkv, dx, bs, x = key_cache.shape
+    k = key_cache.permute(0, 1, 3, 2, 4).reshape(nb, hkv, bs, dx * x).contiguous()
+    v = value_cache.permute(0, 1, 3, 2).contiguous()
+    return k, v
+
+
 def raw_storage(t: torch.Tensor) -> np.ndarray:
     """Host copy of a tensor's storage words as the oracle reads them."""
     t = t.detach().contiguous().cpu()

@@ -23,21 +23,23 @@ def say(msg: str) -> None:
 
 
 def run(wl: W.Workload, path: str, poison_outputs: bool = True, window_left: int = -1,
-        soft_cap: float = 0.0, block_tables=None):
-    """Runs ``path`` ('v1', 'v2', 'auto') and returns host float64 copies of
-    out, exp_sums, max_logits, tmp_out (the last three None for v1).
-    ``window_left`` / ``soft_cap``: the decode options (-1 / 0: off);
-    ``block_tables`` replaces the workload's table."""
+        soft_cap: float = 0.0, block_tables=None, caches=None, kv_layout: str = "decode"):
+    """Runs ``path`` ('v1', 'v2', 'auto', 'split') and returns host float64
+    copies of out, exp_sums, max_logits, tmp_out (the last three None for v1
+    and split).  ``window_left`` / ``soft_cap``: the decode options (-1 / 0:
+    off); ``block_tables`` replaces the workload's table; ``caches`` = (K, V)
+    replaces its caches, which are then in ``kv_layout``."""
     out, es, ml, to = wl.alloc_outputs()
     if poison_outputs:
         for t in (out, es, ml, to):
             t.fill_(float("nan"))
     tables = wl.block_tables if block_tables is None else block_tables
-    args = (wl.query, wl.key_cache, wl.value_cache, wl.num_kv_heads, wl.scale,
+    kc, vc = (wl.key_cache, wl.value_cache) if caches is None else caches
+    args = (wl.query, kc, vc, wl.num_kv_heads, wl.scale,
             tables, wl.seq_lens, wl.block_size, wl.max_seq_len)
     kw = dict(alibi_slopes=wl.alibi_slopes, kv_cache_dtype=wl.kv_cache_dtype,
               k_scale=wl.k_scale, v_scale=wl.v_scale, window_left=window_left,
-              logits_soft_cap=soft_cap)
+              logits_soft_cap=soft_cap, kv_layout=kv_layout)
     if path == "v1":
         B.paged_attention_v1(out, *args, **kw)
     elif path == "split":

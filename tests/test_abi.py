@@ -262,6 +262,28 @@ def test_ex_accepts_valid_options(fn, w, cap):
     assert getattr(lib, fn)(*ex_args(fn, opts(w, cap), head_size=96)) == UNSUP
 
 
+def layout_opts(layout, window_left=-1, cap=0.0):
+    return ctypes.byref(B.DecodeOptions(window_left, cap, layout))
+
+
+@pytest.mark.parametrize("fn", EX_FUNCS)
+def test_ex_cache_layout_option(fn):
+    """kv_layout: 0 / 1 accepted, anything else rejected; the block-rows
+    layout has 16-bit kernels only (f32 query or fp8 cache: unsupported)."""
+    lib = B.load_library()
+    for bad in (2, -1, 100):
+        assert getattr(lib, fn)(*ex_args(fn, layout_opts(bad))) == BADARG
+    rows = B.LAYOUT_CODE["block_rows"]
+    assert getattr(lib, fn)(*ex_args(fn, layout_opts(rows), dtype=BF16, num_seqs=0)) == OK
+    assert getattr(lib, fn)(*ex_args(fn, layout_opts(rows))) == UNSUP          # f32
+    assert getattr(lib, fn)(*ex_args(fn, layout_opts(rows), dtype=BF16, kv=FP8)) == UNSUP
+    assert getattr(lib, fn)(*ex_args(fn, layout_opts(rows, 40, 5.0), dtype=F16,
+                                     num_seqs=0)) == OK
+    lib_split = lib.paged_attention_split
+    assert lib_split(*split_args(options=layout_opts(rows), dtype=BF16, kv=FP8)) == UNSUP
+    assert lib_split(*split_args(options=layout_opts(3), dtype=BF16)) == BADARG
+
+
 def test_reduce_ex_options():
     lib = B.load_library()
     base = [V2, A, A, A, A, 0, 4, 2, 64, A, 700, 2, F32]
