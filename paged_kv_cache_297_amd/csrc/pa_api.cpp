@@ -238,15 +238,14 @@ struct Plan {
 Plan make_plan(const Call &c) {
   const int group = c.num_heads / c.num_kv_heads;
   Plan pl{};
-  pl.mfma = c.kv_layout == PA_KV_LAYOUT_DECODE && c.dtype != PA_DTYPE_F32 &&
-            group >= tunables().mfma_min_group;
-  if (c.kv_layout == PA_KV_LAYOUT_BLOCK_ROWS) {
+  pl.mfma = c.dtype != PA_DTYPE_F32 && group >= tunables().mfma_min_group;
+  if (pl.mfma) {
+    pl.gp = 16;
+  } else if (c.kv_layout == PA_KV_LAYOUT_BLOCK_ROWS) {
     const int gmax = pa::nhd_max_group(c.head_size, c.block_size);
     int p2 = 1;
     while (p2 < group && p2 < gmax) p2 *= 2;
     pl.gp = p2;
-  } else if (pl.mfma) {
-    pl.gp = 16;
   } else {
     const int kv_bytes = c.kv_cache_dtype == PA_KV_FP8_E4M3 ? 1 : (c.dtype == PA_DTYPE_F32 ? 4 : 2);
     const int gmax = pa::valu_max_group(kv_bytes, c.head_size, c.block_size);
@@ -339,7 +338,8 @@ pa_status run_partition(const Call &c) {
   const bool fp8 = c.kv_cache_dtype == PA_KV_FP8_E4M3;
   hipError_t e;
   if (c.kv_layout == PA_KV_LAYOUT_BLOCK_ROWS) {
-    e = pa::launch_partition_nhd(p, (int)c.dtype, c.head_size, c.block_size, pl.gp, l);
+    e = pl.mfma ? pa::launch_partition_mfma_rows(p, (int)c.dtype, c.head_size, c.block_size, l)
+                : pa::launch_partition_nhd(p, (int)c.dtype, c.head_size, c.block_size, pl.gp, l);
   } else if (pl.mfma) {
     e = pa::launch_partition_mfma(p, (int)c.dtype, fp8, c.head_size, c.block_size, l);
   } else if (fp8) {

@@ -67,5 +67,8 @@ hipError_t launch_reduce(const Params &p, int dtype, int head_size, const Launch
 // kDtBF16); gp = 1, 2 or 4 query heads per workgroup (nhd_max_group).
 hipError_t launch_partition_nhd(const Params &p, int q_dtype, int head_size, int block_size,
                                 int gp, const Launch &l);
+// MFMA partition kernel (16 query-head slots) on the same layout.
+hipError_t launch_partition_mfma_rows(const Params &p, int q_dtype, int head_size,
+                                      int block_size, const Launch &l);
 
 }  // namespace pa

@@ -1,6 +1,8 @@
 // Partition kernels for the [num_blocks, Hkv, block_size, head_size] cache
-// layout, 16-bit caches.
+// layout, 16-bit caches: the VALU form for one to four query heads per KV
+// head, the MFMA form (block-rows variant) for wider groups.
 #include "pa_launch.h"
+#include "pa_partition_mfma.h"
 #include "pa_partition_nhd.h"
 
 namespace pa {
@@ -43,6 +45,33 @@ hipError_t launch_partition_nhd(const Params &p, int q_dtype, int head_size, int
                                 int gp, const Launch &l) {
   if (q_dtype == kDtF16) return launch_nhd_t<_Float16>(p, head_size, block_size, gp, l);
   if (q_dtype == kDtBF16) return launch_nhd_t<__bf16>(p, head_size, block_size, gp, l);
+  return hipErrorInvalidValue;
+}
+
+template <typename QT, int D, int BS>
+static hipError_t launch_rows_mfma_opts(const Params &p, const Launch &l) {
+  const bool win = p.window_left >= 0;
+  if (p.cap_on)
+    return win ? launch_kernel(pa_partition_mfma<QT, QT, D, BS, true, true, true>, l, p)
+               : launch_kernel(pa_partition_mfma<QT, QT, D, BS, true, false, true>, l, p);
+  return win ? launch_kernel(pa_partition_mfma<QT, QT, D, BS, false, true, true>, l, p)
+             : launch_kernel(pa_partition_mfma<QT, QT, D, BS, false, false, true>, l, p);
+}
+
+template <typename QT>
+static hipError_t launch_rows_mfma_t(const Params &p, int head_size, int block_size,
+                                     const Launch &l) {
+  if (head_size == 64 && block_size == 16) return launch_rows_mfma_opts<QT, 64, 16>(p, l);
+  if (head_size == 64 && block_size == 32) return launch_rows_mfma_opts<QT, 64, 32>(p, l);
+  if (head_size == 128 && block_size == 16) return launch_rows_mfma_opts<QT, 128, 16>(p, l);
+  if (head_size == 128 && block_size == 32) return launch_rows_mfma_opts<QT, 128, 32>(p, l);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_partition_mfma_rows(const Params &p, int q_dtype, int head_size,
+                                      int block_size, const Launch &l) {
+  if (q_dtype == kDtF16) return launch_rows_mfma_t<_Float16>(p, head_size, block_size, l);
+  if (q_dtype == kDtBF16) return launch_rows_mfma_t<__bf16>(p, head_size, block_size, l);
   return hipErrorInvalidValue;
 }
 

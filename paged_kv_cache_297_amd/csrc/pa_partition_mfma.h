@@ -19,6 +19,17 @@
 // Each lane keeps the running max / sum of one query head (l%16), so the
 // online-softmax rescale of O needs no broadcast.  fp8 E4M3FN keys are
 // widened exactly to the query's 16-bit type, values to fp16 (P in fp16).
+//
+// ROWS: the [num_blocks, Hkv, block_size, head_size] layout (16-bit only).
+// K feeds the same operands from token rows (lane (n, g), k-step ks: the 16
+// bytes of dims 32 ks + 8 g of token n).  V rows are loaded as whole 1 KB
+// runs of consecutive tokens, stored as rows in a per-wave LDS slab, and
+// read back column-wise with the gfx950 transposing LDS read
+// (ds_read_b64_tr_b16): within each 16-lane group, lane 4 j + q names 4
+// consecutive values of one row and lane i receives value i % 4 of the
+// rows named by lanes i / 4, 4 + i / 4, 8 + i / 4, 12 + i / 4 -- so lanes
+// naming (row t0 + j, dims d0 + 4 q ..) hand lane n the values of dim d0 + n
+// at tokens t0 .. t0 + 3: half a V^T operand per read.
 #pragma once
 
 #include <type_traits>
@@ -90,7 +101,16 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-template <typename QT, typename KVT, int D, int BS, bool CAP, bool WIN>
+// Transposing LDS read of four 16-bit values (lane layout above).
+__device__ __forceinline__ u32x2 lds_read_tr16(const char *lds_ptr) {
+  typedef __attribute__((__vector_size__(4 * sizeof(__fp16)))) __fp16 h4;
+  typedef __attribute__((address_space(3))) h4 lds_h4;
+  const h4 v = __builtin_amdgcn_ds_read_tr16_b64_v4f16(
+      (lds_h4 *)((__attribute__((address_space(3))) char *)lds_ptr));
+  return __builtin_bit_cast(u32x2, v);
+}
+
+template <typename QT, typename KVT, int D, int BS, bool CAP, bool WIN, bool ROWS = false>
 __global__ void __launch_bounds__(kThreads)
     __attribute__((amdgpu_waves_per_eu(mfma_waves_per_eu<KVT>())))
     pa_partition_mfma(const Params p) {
@@ -105,10 +125,18 @@ __global__ void __launch_bounds__(kThreads)
   constexpr int NDT = D / 16;                 // 16-dim tiles of the output
   constexpr int OSTR = D + 4;                 // padded LDS row (bank spread)
   static_assert(NLK >= 1 && NLK * (kFp8 ? 2 : 1) == NKS, "K sub-tile geometry");
+  static_assert(!ROWS || !kFp8, "the block-rows layout has 16-bit caches only");
+  // ROWS: V slab rows (one per step token, 32 bytes of padding spread the
+  // four rows a transposing read touches over distinct banks), tokens per
+  // 1 KB V load, lanes per token row.
+  constexpr int VSTR = 2 * D + 32;
+  constexpr int VTPL = 512 / D;
+  constexpr int VR = D / 8;
 
   __shared__ float sm_o[kWaves][16][OSTR];
   __shared__ float sm_m[kWaves][16];
   __shared__ float sm_l[kWaves][16];
+  __shared__ __attribute__((aligned(16))) char sm_v[ROWS ? kWaves * 32 * VSTR : 16];
 
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -202,6 +230,23 @@ __global__ void __launch_bounds__(kThreads)
       }
       kb[b] = kcache + (size_t)phys[b] * blk_stride + it.head_off;
     }
+    if constexpr (ROWS) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int i = 0; i < NLK; ++i) {
+          const int tok = 16 * h + n;
+          tl.k[h][i] = load16_stream(kb[tok / BS] + (tok % BS) * (2 * D) + 64 * i + 16 * g);
+        }
+      // V load i: tokens VTPL i .. VTPL i + VTPL - 1 (one block), 1 KB.
+#pragma unroll
+      for (int i = 0; i < NDT; ++i) {
+        const int tok = VTPL * i + lane / VR;
+        const char *vb = vcache + (size_t)phys[(VTPL * i) / BS] * blk_stride + it.head_off;
+        tl.v[i] = load16_stream(vb + (tok % BS) * (2 * D) + 16 * (lane % VR));
+      }
+      return tl;
+    }
     const int vphys = (BPS == 1 || vtok < BS) ? phys[0] : phys[BPS - 1];
     const char *vb = vcache + (size_t)vphys * blk_stride + it.head_off;
 #pragma unroll
@@ -220,8 +265,27 @@ __global__ void __launch_bounds__(kThreads)
     return tl;
   };
 
+  char *const vslab = sm_v + (ROWS ? wv * 32 * VSTR : 0);
   auto process = [&](const Item &it, int step, const Tile &tl) {
     poisoned |= tl.bad;
+    // ROWS: V rows into the wave's slab, then the transposed operands out
+    // (the wave's LDS accesses execute in order; the previous step's reads
+    // were consumed by its PV products before these writes).
+    u32x4 vrows[ROWS ? NDT : 1];
+    if constexpr (ROWS) {
+#pragma unroll
+      for (int i = 0; i < NDT; ++i)
+        *reinterpret_cast<u32x4 *>(vslab + (VTPL * i + lane / VR) * VSTR + 16 * (lane % VR)) =
+            tl.v[i];
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+      const char *rd = vslab + (vtok + (n >> 2)) * VSTR + 8 * (n & 3);
+#pragma unroll
+      for (int t = 0; t < NDT; ++t) {
+        const u32x2 lo = lds_read_tr16(rd + 32 * t);
+        const u32x2 hi = lds_read_tr16(rd + 4 * VSTR + 32 * t);
+        vrows[t] = u32x4{lo.x, lo.y, hi.x, hi.y};
+      }
+    }
     // S^T for each 16-token sub-tile: lane holds head n, tokens 16h + 4g + e.
     f32x4 st[2];
 #pragma unroll
@@ -283,6 +347,8 @@ __global__ void __launch_bounds__(kThreads)
       if constexpr (kFp8) {
         va = u32x4{fp8x2_to<false>(tl.v[t].x, _Float16()), fp8x2_to<true>(tl.v[t].x, _Float16()),
                    fp8x2_to<false>(tl.v[t].y, _Float16()), fp8x2_to<true>(tl.v[t].y, _Float16())};
+      } else if constexpr (ROWS) {
+        va = vrows[t];
       } else {
         va = tl.v[t];
       }

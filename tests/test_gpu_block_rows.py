@@ -3,8 +3,8 @@ num_kv_heads, block_size, head_size] for K and V, the dispatch page's decode
 signature) against the fp64 oracle: the caches are the decode workloads'
 own, repacked on the device (values unchanged), so the oracle reads the same
 numbers.  Every instance family (f16 / bf16, head sizes 64 / 128, block sizes
-16 / 32, one to four query heads per workgroup) on every path (v1, v2, auto,
-split) with and without window, soft cap and ALiBi; the full-size 16-bit
+16 / 32; the VALU kernel with one to four query heads per workgroup, the MFMA
+kernel for wider groups) on every path (v1, v2, auto, split) with and without window, soft cap and ALiBi; the full-size 16-bit
 decode workloads; NaN-poisoned pools; stale block ids."""
 
 import numpy as np
@@ -42,13 +42,14 @@ def _check(wl, paths, window_left=-1, soft_cap=0.0, seqs=None):
                                soft_cap=soft_cap)
 
 
-#: (dtype, query heads per KV head, head size, block size).  Groups 1..8
-#: cover workgroups of one, two and four query heads, a ragged last head
-#: group (3, 5) and several head groups per KV head (8 at D 128 / bs 32).
+#: (dtype, query heads per KV head, head size, block size).  Groups 1..4 run
+#: the VALU kernel (workgroups of one, two and four query heads, a ragged
+#: last head group at 3); 5..16 the MFMA kernel (16-head tiles, padded).
 FAMILIES = [
     (torch.bfloat16, 1, 128, 16), (torch.float16, 2, 128, 16), (torch.bfloat16, 7, 128, 16),
     (torch.float16, 3, 64, 16), (torch.bfloat16, 4, 64, 16), (torch.bfloat16, 5, 64, 32),
     (torch.float16, 8, 128, 32), (torch.bfloat16, 2, 128, 32), (torch.float16, 1, 64, 32),
+    (torch.float16, 16, 64, 16), (torch.bfloat16, 12, 128, 32),
 ]
 
 LENS = [0, 1, 15, 16, 17, 100, 511, 512, 513, 700, 1100, 2100, 5000]
