@@ -21,10 +21,12 @@
 // widened exactly to the query's 16-bit type, values to fp16 (P in fp16).
 //
 // ROWS: the [num_blocks, Hkv, block_size, head_size] layout (16-bit only).
-// K feeds the same operands from token rows (lane (n, g), k-step ks: the 16
-// bytes of dims 32 ks + 8 g of token n).  V rows are loaded as whole 1 KB
-// runs of consecutive tokens, stored as rows in a per-wave LDS slab, and
-// read back column-wise with the gfx950 transposing LDS read
+// K and V rows are both loaded as whole 1 KB runs of consecutive tokens and
+// pass through a per-wave LDS slab.  K rows are read back as the same QK
+// operands (lane (n, g), k-step ks: the 16 bytes of dims 32 ks + 8 g of
+// token n), with a row stride that spreads the 16 rows of one read over all
+// banks.  V rows are read back column-wise with the gfx950 transposing LDS
+// read
 // (ds_read_b64_tr_b16): within each 16-lane group, lane 4 j + q names 4
 // consecutive values of one row and lane i receives value i % 4 of the
 // rows named by lanes i / 4, 4 + i / 4, 8 + i / 4, 12 + i / 4 -- so lanes
@@ -127,9 +129,11 @@ __global__ void __launch_bounds__(kThreads)
   static_assert(NLK >= 1 && NLK * (kFp8 ? 2 : 1) == NKS, "K sub-tile geometry");
   static_assert(!ROWS || !kFp8, "the block-rows layout has 16-bit caches only");
   // ROWS: V slab rows (one per step token, 32 bytes of padding spread the
-  // four rows a transposing read touches over distinct banks), tokens per
-  // 1 KB V load, lanes per token row.
+  // four rows a transposing read touches over distinct banks), K slab rows
+  // (16 bytes of padding: the 16 token rows of a K operand read start on
+  // distinct 4-bank groups), tokens per 1 KB load, lanes per token row.
   constexpr int VSTR = 2 * D + 32;
+  constexpr int KSTR = 2 * D + 16;
   constexpr int VTPL = 512 / D;
   constexpr int VR = D / 8;
 
@@ -231,19 +235,15 @@ __global__ void __launch_bounds__(kThreads)
       kb[b] = kcache + (size_t)phys[b] * blk_stride + it.head_off;
     }
     if constexpr (ROWS) {
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int i = 0; i < NLK; ++i) {
-          const int tok = 16 * h + n;
-          tl.k[h][i] = load16_stream(kb[tok / BS] + (tok % BS) * (2 * D) + 64 * i + 16 * g);
-        }
-      // V load i: tokens VTPL i .. VTPL i + VTPL - 1 (one block), 1 KB.
+      // K and V load i: tokens VTPL i .. VTPL i + VTPL - 1 (one block), 1 KB
+      // each; the K loads fill tl.k in order (2 NLK == NDT of them).
 #pragma unroll
       for (int i = 0; i < NDT; ++i) {
         const int tok = VTPL * i + lane / VR;
-        const char *vb = vcache + (size_t)phys[(VTPL * i) / BS] * blk_stride + it.head_off;
-        tl.v[i] = load16_stream(vb + (tok % BS) * (2 * D) + 16 * (lane % VR));
+        const size_t row = (size_t)phys[(VTPL * i) / BS] * blk_stride + it.head_off +
+                           (tok % BS) * (2 * D) + 16 * (lane % VR);
+        tl.k[i / NLK][i % NLK] = load16_stream(kcache + row);
+        tl.v[i] = load16_stream(vcache + row);
       }
       return tl;
     }
@@ -272,7 +272,21 @@ __global__ void __launch_bounds__(kThreads)
     // (the wave's LDS accesses execute in order; the previous step's reads
     // were consumed by its PV products before these writes).
     u32x4 vrows[ROWS ? NDT : 1];
+    u32x4 krows[2][NLK];
     if constexpr (ROWS) {
+      // K rows in, the QK operands out; then the V rows over them (the
+      // wave's LDS accesses execute in order).
+#pragma unroll
+      for (int i = 0; i < NDT; ++i)
+        *reinterpret_cast<u32x4 *>(vslab + (VTPL * i + lane / VR) * KSTR + 16 * (lane % VR)) =
+            tl.k[i / NLK][i % NLK];
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int i = 0; i < NLK; ++i)
+          krows[h][i] =
+              *reinterpret_cast<const u32x4 *>(vslab + (16 * h + n) * KSTR + 64 * i + 16 * g);
 #pragma unroll
       for (int i = 0; i < NDT; ++i)
         *reinterpret_cast<u32x4 *>(vslab + (VTPL * i + lane / VR) * VSTR + 16 * (lane % VR)) =
@@ -301,6 +315,8 @@ __global__ void __launch_bounds__(kThreads)
                             fp8x2_to<false>(kw.w, QT()), fp8x2_to<true>(kw.w, QT())};
           c = mfma_qk(lo, qop[2 * i], c, QT());
           c = mfma_qk(hi, qop[2 * i + 1], c, QT());
+        } else if constexpr (ROWS) {
+          c = mfma_qk(krows[h][i], qop[i], c, QT());
         } else {
           c = mfma_qk(tl.k[h][i], qop[i], c, QT());
         }
