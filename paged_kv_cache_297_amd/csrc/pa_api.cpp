@@ -23,6 +23,11 @@ using pa::Params;
 // ---------------------------------------------------------------------------
 struct Tunables {
   int mfma_min_group = 5;     // query heads per KV head from which the MFMA kernel is used
+  // The same on the block-rows layout.  Measured on MI355X (long-context
+  // batch, 4 x 100000 keys, 8 KV heads): the MFMA form ties the VALU form at
+  // 2 heads per KV head (272 us each) and beats it from 3 (277 vs 321 us;
+  // at 4: 274 vs 305 us); at 1 it loses (ragged batch: 2325 vs 2238 us).
+  int rows_mfma_min_group = 3;
   int small_batch_factor = 1; // AUTO: v2 for all if B * Hkv < factor * CUs
   int tile_factor = 2;        // AUTO: v2 iff Hkv * ceil(L/512) > factor * CUs
   int parts_reversed = 1;     // all-v2 launches dispatch the last partition first
@@ -43,6 +48,8 @@ const Tunables &tunables() {
   static const Tunables t = [] {
     Tunables x;
     x.mfma_min_group = env_int("PA_MFMA_MIN_GROUP", x.mfma_min_group, 1, 1 << 20);
+    x.rows_mfma_min_group =
+        env_int("PA_ROWS_MFMA_MIN_GROUP", x.rows_mfma_min_group, 1, 1 << 20);
     x.small_batch_factor = env_int("PA_AUTO_SMALL_BATCH_FACTOR", x.small_batch_factor, 0, 1 << 20);
     x.tile_factor = env_int("PA_AUTO_TILE_FACTOR", x.tile_factor, 0, 1 << 20);
     x.parts_reversed = env_int("PA_PARTS_REVERSED", x.parts_reversed, 0, 1);
@@ -238,7 +245,9 @@ struct Plan {
 Plan make_plan(const Call &c) {
   const int group = c.num_heads / c.num_kv_heads;
   Plan pl{};
-  pl.mfma = c.dtype != PA_DTYPE_F32 && group >= tunables().mfma_min_group;
+  const int min_group = c.kv_layout == PA_KV_LAYOUT_BLOCK_ROWS ? tunables().rows_mfma_min_group
+                                                               : tunables().mfma_min_group;
+  pl.mfma = c.dtype != PA_DTYPE_F32 && group >= min_group;
   if (pl.mfma) {
     pl.gp = 16;
   } else if (c.kv_layout == PA_KV_LAYOUT_BLOCK_ROWS) {

@@ -3,7 +3,7 @@ num_kv_heads, block_size, head_size] for K and V, the dispatch page's decode
 signature) against the fp64 oracle: the caches are the decode workloads'
 own, repacked on the device (values unchanged), so the oracle reads the same
 numbers.  Every instance family (f16 / bf16, head sizes 64 / 128, block sizes
-16 / 32; the VALU kernel with one to four query heads per workgroup, the MFMA
+16 / 32; the VALU kernel for one or two query heads per KV head, the MFMA
 kernel for wider groups) on every path (v1, v2, auto, split) with and without window, soft cap and ALiBi; the full-size 16-bit
 decode workloads; NaN-poisoned pools; stale block ids."""
 
@@ -42,9 +42,9 @@ def _check(wl, paths, window_left=-1, soft_cap=0.0, seqs=None):
                                soft_cap=soft_cap)
 
 
-#: (dtype, query heads per KV head, head size, block size).  Groups 1..4 run
-#: the VALU kernel (workgroups of one, two and four query heads, a ragged
-#: last head group at 3); 5..16 the MFMA kernel (16-head tiles, padded).
+#: (dtype, query heads per KV head, head size, block size).  Groups 1 and 2
+#: run the VALU kernel (workgroups of one and two query heads); 3..16 the
+#: MFMA kernel (16-head tiles, padded).
 FAMILIES = [
     (torch.bfloat16, 1, 128, 16), (torch.float16, 2, 128, 16), (torch.bfloat16, 7, 128, 16),
     (torch.float16, 3, 64, 16), (torch.bfloat16, 4, 64, 16), (torch.bfloat16, 5, 64, 32),
