@@ -50,12 +50,13 @@ def log(msg: str) -> None:
 
 def kernel_source_hash(prefill: bool = False) -> str:
     """Hash of the library sources a measurement depends on (the decode path:
-    every source but the prefill kernel's own files; prefill: every source):
-    counter figures taken on other sources are not reported."""
+    every source but the prefill kernel's own files and the stream-read
+    hook's; prefill: every source but the hook's): counter figures taken on
+    other sources are not reported."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "paged_kv_cache_297_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
-        if not prefill and name.startswith("pa_prefill"):
+        if name == "pa_stream.hip" or (not prefill and name.startswith("pa_prefill")):
             continue
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + b"\0" + f.read())
@@ -119,6 +120,35 @@ def read_traffic(workload_name: str, src_hash: str, call_path: str):
         return int(vals["hbm_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
+
+
+def stream_read_ceiling(B, gib: int, reps: int = 10) -> float:
+    """GB/s of the library's plain streaming read (pa_stream_read) over a
+    gib-GiB device buffer: 16-byte loads, one workgroup per CU (measured on
+    MI355X: 7.17 TB/s; 2-32 workgroups per CU read 6.95-7.04 TB/s), median of
+    ``reps`` reads after two warm-ups.  The buffer is far larger
+    than the 256 MB Infinity Cache, so every read comes from HBM."""
+    import numpy as np
+    import torch
+
+    n = gib << 30
+    buf = torch.ones(n // 4, dtype=torch.int32, device="cuda")
+    sink = torch.empty(B.device_cu_count(), dtype=torch.int32, device="cuda")
+    for _ in range(2):
+        B.stream_read(buf, sink)
+    ts = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        B.stream_read(buf, sink)
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    del buf
+    torch.cuda.empty_cache()
+    gbs = n / (float(np.median(ts)) * 1e-3) / 1e9
+    log(f"stream read ceiling: {gbs:.1f} GB/s over {gib} GiB")
+    return round(gbs, 1)
 
 
 def cpu_baseline(wl, budget_s: float, window_left: int = -1, soft_cap: float = 0.0) -> dict:
@@ -260,6 +290,9 @@ def main() -> int:
                     help="logit soft cap C * tanh(s / C) (0: off)")
     ap.add_argument("--layout", default="decode", choices=["decode", "block_rows"],
                     help="KV cache layout of the decode call (16-bit caches for block_rows)")
+    ap.add_argument("--stream-gib", type=int, default=4, metavar="GIB",
+                    help="also time the library's streaming read of GIB GiB: the practical HBM "
+                         "read ceiling (0: skip)")
     ap.add_argument("--prefill", default=None, choices=["prefill_bf16", "chunked_bf16"],
                     help="time paged prefill on this workload instead of decode")
     args = ap.parse_args()
@@ -374,6 +407,8 @@ def main() -> int:
         torch.cuda.synchronize()
         log(f"calibration copy: {n} bytes x3")
 
+    stream_gbs = stream_read_ceiling(B, args.stream_gib) if args.stream_gib > 0 else None
+
     ms_per_step = wall * 1e3 / args.steps
     kv_gbs = ab["kv"] / (ms_per_step * 1e-3) / 1e9
     part_avg = float(part_ms.mean())
@@ -434,6 +469,8 @@ def main() -> int:
             "event_step_us_p10_p50_p90": [round(float(np.percentile(step_ms, q)) * 1e3, 2)
                                           for q in (10, 50, 90)],
             "kernel_source_hash": src_hash,
+            "stream_read_gbs": stream_gbs,
+            "frac_of_stream_read": (round(achieved / stream_gbs, 4) if stream_gbs else None),
         },
     }
     if not args.no_cpu_baseline:

@@ -387,6 +387,22 @@ pa_status pa_device_cu_count(int *cu_count);
 pa_status pa_set_timing_events(void *partition_start, void *partition_stop, void *reduce_start,
                                void *reduce_stop);
 
+/* Measurement hook, not part of attention: the practical HBM read ceiling
+ * that the decode kernels' bandwidth is reported against.  Reads `bytes`
+ * bytes at `buf` with 16-byte nontemporal loads: num_workgroups workgroups
+ * of 256 threads, workgroup w streaming the w-th contiguous share (the same
+ * access shape as a partition workgroup's run of tiles), and writes the XOR
+ * of the 32-bit words workgroup w read to sink[w].
+ *   buf   device memory, 16-byte aligned, caller-owned; bytes a multiple of
+ *         16 (0 is allowed: every sink word becomes 0)
+ *   sink  device memory, num_workgroups uint32 words, caller-owned
+ *   num_workgroups  1 .. 2^31 - 1
+ * Errors: PA_ERR_NULL_POINTER (buf or sink NULL), PA_ERR_MISALIGNED (buf not
+ * 16-byte aligned or bytes not a multiple of 16), PA_ERR_BAD_SHAPE
+ * (num_workgroups < 1), PA_ERR_HIP (launch failure). */
+pa_status pa_stream_read(const void *buf, size_t bytes, uint32_t *sink, int num_workgroups,
+                         void *stream);
+
 /* Static description of a status code. */
 const char *pa_status_string(pa_status status);
 

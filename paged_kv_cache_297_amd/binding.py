@@ -41,7 +41,7 @@ EXPORTED_SYMBOLS = (
     "paged_attention_partition_ex", "paged_attention_reduce_ex", "paged_attention_split",
     "pa_split_counters_size", "paged_prefill", "pa_partition_size",
     "pa_num_partitions", "pa_should_use_v2", "pa_device_cu_count", "pa_set_timing_events",
-    "pa_status_string", "pa_version",
+    "pa_status_string", "pa_version", "pa_stream_read",
 )
 
 
@@ -121,6 +121,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pa_device_cu_count.restype = _I
     lib.pa_set_timing_events.argtypes = [_P, _P, _P, _P]
     lib.pa_set_timing_events.restype = _I
+    lib.pa_stream_read.argtypes = [_P, ctypes.c_size_t, _P, _I, _P]
+    lib.pa_stream_read.restype = _I
     lib.pa_status_string.argtypes = [_I]
     lib.pa_status_string.restype = ctypes.c_char_p
     lib.pa_version.argtypes = []
@@ -483,6 +485,17 @@ def set_timing_events(partition_start=None, partition_stop=None, reduce_start=No
     start / end by later calls from this thread; None pairs switch it off."""
     _check(load_library().pa_set_timing_events(partition_start, partition_stop, reduce_start,
                                                reduce_stop), "pa_set_timing_events")
+
+
+def stream_read(buf: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
+    """Measurement hook: streams every byte of ``buf`` (contiguous device
+    tensor) once; sink (int32, one word per workgroup) gets each workgroup's
+    XOR of the words it read."""
+    if not (buf.is_contiguous() and sink.is_contiguous() and sink.dtype == torch.int32):
+        raise ValueError("stream_read: contiguous buffer and int32 sink required")
+    _check(load_library().pa_stream_read(buf.data_ptr(), buf.numel() * buf.element_size(),
+                                         sink.data_ptr(), sink.numel(), _stream(stream)),
+           "pa_stream_read")
 
 
 def version() -> str:

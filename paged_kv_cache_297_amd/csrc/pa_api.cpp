@@ -754,6 +754,16 @@ pa_status pa_device_cu_count(int *cu_count) {
   return cu_count_current(cu_count);
 }
 
+pa_status pa_stream_read(const void *buf, size_t bytes, uint32_t *sink, int num_workgroups,
+                         void *stream) {
+  if (!buf || !sink) return PA_ERR_NULL_POINTER;
+  if (!aligned16(buf) || bytes % 16 != 0) return PA_ERR_MISALIGNED;
+  if (num_workgroups < 1) return PA_ERR_BAD_SHAPE;
+  const hipError_t e = pa::launch_stream_read(buf, bytes, sink, num_workgroups,
+                                              static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
 const char *pa_status_string(pa_status status) {
   switch (status) {
     case PA_OK: return "ok";

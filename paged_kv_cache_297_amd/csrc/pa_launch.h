@@ -62,6 +62,9 @@ hipError_t launch_partition_valu_fp8(const Params &p, int q_dtype, int head_size
 hipError_t launch_partition_mfma(const Params &p, int q_dtype, bool kv_fp8, int head_size,
                                  int block_size, const Launch &l);
 hipError_t launch_reduce(const Params &p, int dtype, int head_size, const Launch &l);
+// Streaming read of bytes (a multiple of 16) at buf, one share per workgroup.
+hipError_t launch_stream_read(const void *buf, size_t bytes, unsigned *sink, int workgroups,
+                              hipStream_t stream);
 
 // [num_blocks, Hkv, block_size, head_size] caches, 16-bit (q_dtype kDtF16 or
 // kDtBF16); gp = 1, 2 or 4 query heads per workgroup (nhd_max_group).

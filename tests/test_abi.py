@@ -70,6 +70,19 @@ def test_dispatch_rule_matches_page_rule_when_batch_is_large():
                 assert bool(lib.pa_should_use_v2(b, hkv, L, cu)) == want, (cu, hkv, L)
 
 
+def test_stream_read_validation():
+    """The measurement hook checks its arguments before any HIP call (fake,
+    never dereferenced device addresses)."""
+    lib = B.load_library()
+    f = lib.pa_stream_read
+    assert f(None, 1024, 0x10000, 4, None) == NULLP
+    assert f(0x10000, 1024, None, 4, None) == NULLP
+    assert f(0x10008, 1024, 0x10000, 4, None) == MISAL   # buffer not 16-byte aligned
+    assert f(0x10000, 1000, 0x10000, 4, None) == MISAL   # bytes not a multiple of 16
+    assert f(0x10000, 1024, 0x10000, 0, None) == SHAPE
+    assert f(0x10000, 1024, 0x10000, -3, None) == SHAPE
+
+
 def test_dispatch_small_batch_clause():
     lib = B.load_library()
     assert lib.pa_should_use_v2(4, 8, 1, 256) == 1          # 32 < 256: always v2

@@ -187,3 +187,29 @@ def test_auto_all_v1_runs_as_plain_v1():
     some = [0, n // 2, n - 1]
     ref = H.oracle(wl, some)
     H.check_close(a["out"][some], ref["out_v1"][some], H.TOL[wl.kv_kind], "auto all-v1")
+
+
+@pytest.mark.parametrize("nbytes,wgs", [(0, 3), (16, 1), (4096 * 16 + 48, 7), (1 << 24, 512)])
+def test_stream_read_reads_every_word_once(nbytes, wgs):
+    """The bandwidth-ceiling hook: each workgroup reads its contiguous share
+    exactly once, so the XOR of the sink words is the XOR of all the
+    buffer's 32-bit words (ragged shares and a 0-byte buffer included)."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(nbytes + wgs)
+    base = torch.randint(-2 ** 31, 2 ** 31 - 1, (max(4, nbytes // 4),), dtype=torch.int32,
+                         device="cuda", generator=g)
+    words = base[:nbytes // 4]
+    sink = torch.full((wgs,), 12345, dtype=torch.int32, device="cuda")
+    if nbytes:
+        B.stream_read(words, sink)
+    else:
+        # Through the C ABI with a valid address and 0 bytes (torch gives an
+        # empty tensor a NULL data pointer).
+        st = B.load_library().pa_stream_read(base.data_ptr(), 0, sink.data_ptr(), wgs,
+                                             torch.cuda.current_stream().cuda_stream)
+        assert st == B.PA_OK
+    torch.cuda.synchronize()
+    host = words.cpu().numpy().view(np.uint32)
+    want = int(np.bitwise_xor.reduce(host)) if host.size else 0
+    got = int(np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32)))
+    assert got == want
