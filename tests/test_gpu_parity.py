@@ -99,3 +99,17 @@ def test_auto_mixed_dispatch_small():
     wl = W.make_workload(4, lens=lens)
     assert H.uses_v2(wl, 0) and not H.uses_v2(wl, 1)
     _run_and_check(wl, ["auto"], seqs=[0, 1, 2, 8, n - 1])
+
+
+@pytest.mark.parametrize("number,group,alibi", [(4, 1, True), (2, 8, False)],
+                         ids=["valu-alibi", "mfma"])
+def test_many_partitions(number, group, alibi):
+    """A 262221-key sequence (513 partitions: the reduce merges them over
+    several rounds; the split path caps it at 64 pieces) next to a short one,
+    on the VALU and the MFMA kernel, with ALiBi slopes on positions up to
+    2.6e5 for the first."""
+    lens = [262221, 1000]
+    wl = W.make_workload(number, lens=lens, H=group, Hkv=1, D=128, bs=16, alibi=alibi,
+                         seed=9100 + group)
+    assert wl.max_num_partitions == 513
+    _run_and_check(wl, ["v2", "auto", "split"])
