@@ -363,6 +363,9 @@ def main() -> int:
             lib.pa_set_timing_events(*ev)
         calls[i % copies]()
 
+    # The stream-read ceiling, on the same warm device just before the timed
+    # steps (taken after them it read up to 11% lower on one box).
+    stream_gbs = stream_read_ceiling(B, args.stream_gib) if args.stream_gib > 0 else None
     for i in range(args.warmup):
         launch(i)
     torch.cuda.synchronize()
@@ -406,8 +409,6 @@ def main() -> int:
             dst.copy_(src)
         torch.cuda.synchronize()
         log(f"calibration copy: {n} bytes x3")
-
-    stream_gbs = stream_read_ceiling(B, args.stream_gib) if args.stream_gib > 0 else None
 
     ms_per_step = wall * 1e3 / args.steps
     kv_gbs = ab["kv"] / (ms_per_step * 1e-3) / 1e9
