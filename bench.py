@@ -363,8 +363,9 @@ def main() -> int:
             lib.pa_set_timing_events(*ev)
         calls[i % copies]()
 
-    # The stream-read ceiling, on the same warm device just before the timed
-    # steps (taken after them it read up to 11% lower on one box).
+    # The stream-read ceiling, once the inputs are built and before the
+    # warm-up and timed steps (taken after them it read up to 11% lower on one
+    # box).
     stream_gbs = stream_read_ceiling(B, args.stream_gib) if args.stream_gib > 0 else None
     for i in range(args.warmup):
         launch(i)
