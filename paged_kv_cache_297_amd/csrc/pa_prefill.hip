@@ -23,6 +23,36 @@
 
 namespace pa {
 
+// Workgroups are handed to the 8 XCDs (each with its own L2) round-robin in
+// launch order.  With PA_PREFILL_XCD_MAP the launch index is remapped so that
+// XCD k runs the k-th eighth of the (query tile, KV head, sequence) items in
+// grid order: the query tiles of one (sequence, KV head), which all read the
+// same keys and values, share one L2.
+#ifndef PA_PREFILL_XCD_MAP
+#define PA_PREFILL_XCD_MAP 1
+#endif
+constexpr int kXcds = 8;
+
+__device__ __forceinline__ void prefill_item(int &bx, int &by, int &bz) {
+  bx = blockIdx.x;
+  by = blockIdx.y;
+  bz = blockIdx.z;
+#if PA_PREFILL_XCD_MAP
+  // A bijection on [0, whole): launch lin = 8 s + k (XCD k, round s) runs
+  // item k * whole / 8 + s.
+  const unsigned long long gx = gridDim.x, gy = gridDim.y;
+  const unsigned long long total = gx * gy * gridDim.z;
+  const unsigned long long lin = bx + gx * (by + gy * bz);
+  const unsigned long long whole = total - total % kXcds;  // the rest keep their place
+  if (lin < whole) {
+    const unsigned long long item = (lin % kXcds) * (whole / kXcds) + lin / kXcds;
+    bx = (int)(item % gx);
+    by = (int)((item / gx) % gy);
+    bz = (int)(item / (gx * gy));
+  }
+#endif
+}
+
 // Waves per SIMD the register allocator must leave room for: three with one
 // column tile per wave, two with two.
 template <int NT>
@@ -53,8 +83,10 @@ __global__ void __launch_bounds__(kThreads)
   __shared__ __attribute__((aligned(16))) QT sv[D][VP];
   __shared__ int sm_bad;
 
-  const int tile = p.num_q_tiles - 1 - (int)blockIdx.x;  // latest (heaviest) tiles first
-  const int kvh = blockIdx.y, seq = blockIdx.z;
+  int bx, by, bz;
+  prefill_item(bx, by, bz);
+  const int tile = p.num_q_tiles - 1 - bx;  // latest (heaviest) tiles first
+  const int kvh = by, seq = bz;
   const int q_begin = p.cu_seq_q[seq], q_end = p.cu_seq_q[seq + 1];
   const int nq = q_end - q_begin, nk = p.cu_seq_k[seq + 1] - p.cu_seq_k[seq];
   const int t0 = tile * p.q_tile;
