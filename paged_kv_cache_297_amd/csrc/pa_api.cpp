@@ -28,6 +28,7 @@ struct Tunables {
   // 2 heads per KV head (272 us each) and beats it from 3 (277 vs 321 us;
   // at 4: 274 vs 305 us); at 1 it loses (ragged batch: 2325 vs 2238 us).
   int rows_mfma_min_group = 3;
+  int prefill_tiles = 0;      // prefill column tiles per wave: 0 = by shape, else 1 or 2
   int small_batch_factor = 1; // AUTO: v2 for all if B * Hkv < factor * CUs
   int tile_factor = 2;        // AUTO: v2 iff Hkv * ceil(L/512) > factor * CUs
   int parts_reversed = 1;     // all-v2 launches dispatch the last partition first
@@ -50,6 +51,7 @@ const Tunables &tunables() {
     x.mfma_min_group = env_int("PA_MFMA_MIN_GROUP", x.mfma_min_group, 1, 1 << 20);
     x.rows_mfma_min_group =
         env_int("PA_ROWS_MFMA_MIN_GROUP", x.rows_mfma_min_group, 1, 1 << 20);
+    x.prefill_tiles = env_int("PA_PREFILL_TILES", x.prefill_tiles, 0, 2);
     x.small_batch_factor = env_int("PA_AUTO_SMALL_BATCH_FACTOR", x.small_batch_factor, 0, 1 << 20);
     x.tile_factor = env_int("PA_AUTO_TILE_FACTOR", x.tile_factor, 0, 1 << 20);
     x.parts_reversed = env_int("PA_PARTS_REVERSED", x.parts_reversed, 0, 1);
@@ -692,11 +694,22 @@ pa_status paged_prefill(void *out, const void *query, const void *key_cache,
   p.num_blocks = num_blocks;
   p.max_seq_q = max_seq_q;
   p.max_seq_k = max_seq_k;
-  // Two column tiles per wave when each query sees many keys (long context
-  // over few new tokens: chunked prefill), one otherwise (fresh prompts:
-  // more, shorter workgroups balance the causal triangle).  A group wider
-  // than one tile's worth of columns needs two.
-  p.tiles_per_wave = (max_seq_k >= 2LL * max_seq_q || group > 16 * pa::kWaves) ? 2 : 1;
+  // Two column tiles per wave (each K / V fragment read from LDS feeds
+  // both) when each query sees many keys (chunked prefill), or when the
+  // two-tile grid still gives every CU two workgroups; one otherwise (small
+  // fresh batches: more, shorter workgroups fill the CUs).  A group wider
+  // than one tile's worth of columns needs two.  Measured on MI355X with the
+  // XCD mapping: 8 fresh 2048-token prompts 0.495 ms with two tiles vs 0.543
+  // with one; 16 chunks of 512 over 8192 keys 1.62 vs 1.86 ms.
+  int cu = 0;
+  const pa_status cst = cu_count_current(&cu);
+  if (cst != PA_OK) return cst;
+  const int q_tile2 = 16 * 2 * pa::kWaves / group;
+  const long long grid2 = ((long long)max_seq_q + q_tile2 - 1) / q_tile2 * num_kv_heads * num_seqs;
+  p.tiles_per_wave =
+      (max_seq_k >= 2LL * max_seq_q || group > 16 * pa::kWaves || grid2 >= 2LL * cu) ? 2 : 1;
+  if (tunables().prefill_tiles > 0 && group <= 16 * pa::kWaves)
+    p.tiles_per_wave = tunables().prefill_tiles;
   p.q_tile = 16 * p.tiles_per_wave * pa::kWaves / group;
   const long long tiles = ((long long)max_seq_q + p.q_tile - 1) / p.q_tile;
   if (tiles > 0x7fffffffLL) return PA_ERR_BAD_SHAPE;

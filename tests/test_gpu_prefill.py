@@ -31,7 +31,8 @@ FAMILIES = [(torch.bfloat16, 128, 16, 4), (torch.bfloat16, 64, 32, 1), (torch.fl
             (torch.bfloat16, 128, 32, 128), (torch.float16, 64, 16, 16),
             (torch.bfloat16, 128, 16, 64)]
 
-#: Pairs whose key counts stay below twice the query counts: the kernel then
+#: Pairs whose key counts stay below twice the query counts, in a batch too
+#: small to give every CU two workgroups of two column tiles: the kernel then
 #: runs one column tile per wave (the PAIRS above select two).
 PAIRS_SQUARE = [(1, 1), (17, 17), (64, 64), (65, 65), (5, 3), (130, 131), (200, 250), (0, 5),
                 (3, 0), (90, 40)]
