@@ -124,10 +124,12 @@ def read_traffic(workload_name: str, src_hash: str, call_path: str):
 
 def stream_read_ceiling(B, gib: int, reps: int = 10) -> float:
     """GB/s of the library's plain streaming read (pa_stream_read) over a
-    gib-GiB device buffer: 16-byte loads, one workgroup per CU (measured on
-    MI355X: 7.17 TB/s; 2-32 workgroups per CU read 6.95-7.04 TB/s), median of
-    ``reps`` reads after two warm-ups.  The buffer is far larger
-    than the 256 MB Infinity Cache, so every read comes from HBM."""
+    fresh gib-GiB device buffer, one launch per pass: 16-byte loads, one
+    workgroup per CU (measured on MI355X: 7.17 TB/s; 2-32 workgroups per CU
+    read 6.95-7.04 TB/s), median of ``reps`` passes after two warm-ups.  The
+    buffer is far larger than the 256 MB Infinity Cache, so every read comes
+    from HBM.  (Reading the workload's own pools instead, a few hundred MB
+    per launch, read 6.3-6.9 TB/s: launch ramps weigh more there.)"""
     import numpy as np
     import torch
 
@@ -363,10 +365,6 @@ def main() -> int:
             lib.pa_set_timing_events(*ev)
         calls[i % copies]()
 
-    # The stream-read ceiling, once the inputs are built and before the
-    # warm-up and timed steps (taken after them it read up to 11% lower on one
-    # box).
-    stream_gbs = stream_read_ceiling(B, args.stream_gib) if args.stream_gib > 0 else None
     for i in range(args.warmup):
         launch(i)
     torch.cuda.synchronize()
@@ -410,6 +408,10 @@ def main() -> int:
             dst.copy_(src)
         torch.cuda.synchronize()
         log(f"calibration copy: {n} bytes x3")
+
+    # The stream-read ceiling, after the timed steps (allocating its buffer
+    # before them slowed the steps by 6%).
+    stream_gbs = stream_read_ceiling(B, args.stream_gib) if args.stream_gib > 0 else None
 
     ms_per_step = wall * 1e3 / args.steps
     kv_gbs = ab["kv"] / (ms_per_step * 1e-3) / 1e9
