@@ -53,6 +53,15 @@ __device__ __forceinline__ void prefill_item(int &bx, int &by, int &bz) {
 #endif
 }
 
+// Lazy rescaling of the running softmax state: a column keeps its reference
+// max until the running max rises by more than this (log2 units), so its
+// weights exp2(s - m_ref) stay at most 2^8 (exact in the 16-bit P operands
+// and far from overflow in the fp32 sums), and the accumulators are rescaled
+// only on those rare steps instead of on nearly every one.  The output, the
+// weighted sum over the sum of weights, is the same in exact arithmetic for
+// any reference.
+constexpr float kLazyRescale = 8.0f;
+
 // Waves per SIMD the register allocator must leave room for: three with one
 // column tile per wave, two with two.
 template <int NT>
@@ -274,15 +283,18 @@ __global__ void __launch_bounds__(kThreads)
 #pragma unroll
           for (int e = 0; e < 4; ++e) bm = fmaxf(bm, sc[j][h][e]);
         bm = xor_max<32>(xor_max<16>(bm)) * p.scale_log2;
-        const float m_new = fmaxf(m_run[j], bm);
-        alpha[j] = fast_exp2(m_run[j] - m_new);  // m_run = -inf: 0, l_run and oacc are 0
-        m_run[j] = m_new;
+        // Every key is visible, so bm is finite; m_run = -inf always moves
+        // (alpha 0: l_run and oacc are 0).
+        const bool move = bm > m_run[j] + kLazyRescale;
+        const float m_ref = move ? bm : m_run[j];
+        alpha[j] = move ? fast_exp2(m_run[j] - bm) : 1.0f;
+        m_run[j] = m_ref;
 #pragma unroll
         for (int h = 0; h < NSUB; ++h) {
           float pe[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            pe[e] = fast_exp2(fmaf(sc[j][h][e], p.scale_log2, -m_new));
+            pe[e] = fast_exp2(fmaf(sc[j][h][e], p.scale_log2, -m_ref));
             psum += pe[e];
           }
           pk[h] = u32x2{pack2(pe[0], pe[1], QT()), pack2(pe[2], pe[3], QT())};
@@ -300,15 +312,18 @@ __global__ void __launch_bounds__(kThreads)
             bm = fmaxf(bm, x[h][e]);
           }
         bm = xor_max<32>(xor_max<16>(bm));
-        const float m_new = fmaxf(m_run[j], bm);
-        alpha[j] = (m_new == -__builtin_inff()) ? 1.0f : fast_exp2(m_run[j] - m_new);
-        m_run[j] = m_new;
+        // bm = -inf (nothing visible yet) never moves the reference; a finite
+        // bm over m_run = -inf always does.
+        const bool move = bm > m_run[j] + kLazyRescale;
+        const float m_ref = move ? bm : m_run[j];
+        alpha[j] = move ? fast_exp2(m_run[j] - bm) : 1.0f;
+        m_run[j] = m_ref;
 #pragma unroll
         for (int h = 0; h < NSUB; ++h) {
           float pe[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            pe[e] = x[h][e] == -__builtin_inff() ? 0.0f : fast_exp2(x[h][e] - m_new);
+            pe[e] = x[h][e] == -__builtin_inff() ? 0.0f : fast_exp2(x[h][e] - m_ref);
             psum += pe[e];
           }
           pk[h] = u32x2{pack2(pe[0], pe[1], QT()), pack2(pe[2], pe[3], QT())};
