@@ -58,3 +58,17 @@ def test_prefill_flops_counts_the_causal_pairs():
     qlens, klens = [1, 7, 40, 9, 64], [1, 30, 40, 4, 64]
     pairs = sum(int(P.visible_keys(q, k, True, -1, -1).sum()) for q, k in zip(qlens, klens))
     assert bench.prefill_flops(qlens, klens, 3, 128) == 4 * 128 * 3 * pairs
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU: --gpus above 1 exits with status 2 and says
+    so (before touching a device)."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    res = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                         capture_output=True, text=True, timeout=120)
+    assert res.returncode == 2
+    assert "one GPU" in res.stderr
+    assert res.stdout == ""
