@@ -157,3 +157,45 @@ def test_prefill_blocks_outside_the_window_are_not_read():
     got = run(wl, window_left=50, tables=tables)
     ref, rows = oracle(wl, window_left=50)
     H.check_close(got[rows], ref, TOL, "window skips stale blocks")
+
+
+def _random_prefill(case: int) -> dict:
+    rng = np.random.default_rng(30000 + case)
+    n = int(rng.integers(1, 7))
+    qlens, klens = [], []
+    for _ in range(n):
+        q = int(rng.choice([0, 1, int(rng.integers(2, 40)), int(rng.integers(40, 400))]))
+        k = q + int(rng.choice([0, 0, int(rng.integers(0, 64)), int(rng.integers(64, 1500))]))
+        if rng.random() < 0.1:
+            k = int(rng.integers(0, max(1, q)))   # fewer keys than queries
+        qlens.append(q)
+        klens.append(k)
+    if max(qlens) == 0:
+        qlens[0], klens[0] = 9, 30
+    opts = dict(causal=bool(rng.random() < 0.7))
+    if rng.random() < 0.3:
+        opts["window_left"] = int(rng.integers(0, 300))
+    if rng.random() < 0.2:
+        opts["window_right"] = int(rng.integers(0, 50))
+    if rng.random() < 0.25:
+        opts["soft_cap"] = float(rng.choice([5.0, 30.0]))
+    return dict(qlens=qlens, klens=klens, opts=opts,
+                dtype=[torch.bfloat16, torch.float16][int(rng.integers(0, 2))],
+                d=int(rng.choice([64, 128])), bs=int(rng.choice([16, 32])),
+                group=int(rng.choice([1, 2, 4, 5, 8, 16])), hkv=int(rng.choice([1, 2, 3])))
+
+
+@pytest.mark.parametrize("case", range(32))
+def test_prefill_random(case):
+    """Seeded random batches (query / key counts with empty sides and
+    nk < nq, groups, head / block sizes, masks, soft cap): grid sizes that
+    leave a remainder after the last full XCD round, and both column-tile
+    forms."""
+    c = _random_prefill(case)
+    wl = W.make_prefill_workload(qlens=c["qlens"], klens=c["klens"], H=c["hkv"] * c["group"],
+                                 Hkv=c["hkv"], D=c["d"], bs=c["bs"], dtype=c["dtype"],
+                                 seed=31000 + case)
+    H.say(f"  prefill random {case}: q={c['qlens']} k={c['klens']} {c['opts']}")
+    got = run(wl, **c["opts"])
+    ref, rows = oracle(wl, **c["opts"])
+    H.check_close(got[rows], ref, TOL, f"prefill random {case} {c['opts']}")
