@@ -144,7 +144,8 @@ def cap_bound(wl: W.Workload, soft_cap: float) -> float:
     visible at fp32 tolerances (1e-5)."""
     if soft_cap <= 0.0 or wl.kv_kind != "f32":
         return 0.0
-    vmax = float(wl.value_cache.abs().max().item()) * wl.v_scale
+    # NaN poison in unread slots is not a value any output weighs.
+    vmax = float(torch.nan_to_num(wl.value_cache, nan=0.0).abs().max().item()) * wl.v_scale
     return 8.0 * 2.0 ** -24 * soft_cap * 2.0 * vmax
 
 

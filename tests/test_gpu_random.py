@@ -5,7 +5,9 @@ fp16 query), query heads per KV head, KV heads, head size, block size, a
 ragged batch of lengths (empty sequences, partition edges, short and long
 ones), ALiBi, a sliding window, a logit soft cap, the cache layout and the
 path (v1, v2, auto, split), and checks every output the path defines against
-the oracle on the same bytes.  The draws are seeded, so every case is the
+the oracle on the same bytes.  Odd cases are NaN-poisoned: unused block-table
+entries point at an all-NaN block and the slots past each sequence's end hold
+NaN, which no output may see.  The draws are seeded, so every case is the
 same on every run."""
 
 import numpy as np
@@ -65,6 +67,7 @@ def _draw(case: int) -> dict:
         cap=float(rng.choice([0.0, 0.0, 0.0, 5.0, 30.0])),
         layout="block_rows" if sixteen and rng.random() < 0.35 else "decode",
         path=str(rng.choice(["v1", "v2", "auto", "split"])),
+        poison=bool(case % 2),
     )
 
 
@@ -79,7 +82,8 @@ def test_random_config(case):
     c = _draw(case)
     dtype, kv = KINDS[c["kind"]]
     wl = W.make_workload(2, lens=c["lens"], H=c["hkv"] * c["group"], Hkv=c["hkv"], D=c["d"],
-                         bs=c["bs"], dtype=dtype, kv=kv, alibi=c["alibi"], seed=21000 + case)
+                         bs=c["bs"], dtype=dtype, kv=kv, alibi=c["alibi"], seed=21000 + case,
+                         poison=c["poison"])
     caches = W.to_block_rows(wl.key_cache, wl.value_cache) if c["layout"] == "block_rows" else None
     H.say(f"  random case {_case_id(case)} lens={c['lens']} W={c['window']} cap={c['cap']} "
           f"alibi={c['alibi']}")
