@@ -62,16 +62,25 @@ __device__ __forceinline__ void prefill_item(int &bx, int &by, int &bz) {
 // any reference.
 constexpr float kLazyRescale = 8.0f;
 
+// Two-tile form: the query tile lives in LDS (read per step) instead of in
+// registers, which frees the 32 VGPRs that keep it at two waves per SIMD.
+#ifndef PA_PREFILL_Q_LDS
+#define PA_PREFILL_Q_LDS 1
+#endif
+
 // Waves per SIMD the register allocator must leave room for: three with one
-// column tile per wave, two with two.
-template <int NT>
+// column tile per wave; with two, three when the query tile is in LDS (two
+// for head size 128 with 32-token blocks, which would spill at three), else
+// two.
+template <int NT, int D, int BS>
 constexpr int prefill_waves_per_eu() {
-  return NT == 1 ? 3 : 2;
+  if constexpr (NT == 1) return 3;
+  else return (PA_PREFILL_Q_LDS && !(D == 128 && BS == 32)) ? 3 : 2;
 }
 
 template <typename QT, int D, int BS, int NT, bool CAP>
 __global__ void __launch_bounds__(kThreads)
-    __attribute__((amdgpu_waves_per_eu(prefill_waves_per_eu<NT>())))
+    __attribute__((amdgpu_waves_per_eu(prefill_waves_per_eu<NT, D, BS>())))
     pa_prefill_kernel(const PrefillParams p) {
   // NT: 16-column MFMA tiles per wave
   constexpr int NKS = D / 32;                  // 32-dim k-steps of QK^T
@@ -91,6 +100,14 @@ __global__ void __launch_bounds__(kThreads)
   __shared__ __attribute__((aligned(16))) QT sk[kPrefillStep][KP];
   __shared__ __attribute__((aligned(16))) QT sv[D][VP];
   __shared__ int sm_bad;
+  // Query tile of the two-tile form: row = column of the workgroup, D / 8
+  // 16-byte chunks per row, chunk c stored at c ^ qswz(row) so that the 16
+  // rows one operand read touches fall on distinct bank groups.
+  constexpr bool kQLds = PA_PREFILL_Q_LDS && NT == 2;
+  constexpr int QCOLS = 16 * NT * kWaves;
+  constexpr int QCH = D / 8;
+  __shared__ __attribute__((aligned(16))) QT sq[kQLds ? QCOLS : 1][kQLds ? D : 8];
+  auto qswz = [](int row) { return QCH == 16 ? (row & 15) : ((row >> 1) & 7); };
 
   int bx, by, bz;
   prefill_item(bx, by, bz);
@@ -149,14 +166,27 @@ __global__ void __launch_bounds__(kThreads)
   if (p.window_left >= 0) lo = max(lo, pos0 + t0 - p.window_left);
 
   // B operands of QK^T: 8 query values per lane, column tile and k-step.
-  u32x4 qop[NT][NKS];
+  u32x4 qop[kQLds ? 1 : NT][NKS];
+  if constexpr (kQLds) {
+    // Published by the barrier after the first K / V stage.
+    for (int ci = threadIdx.x; ci < QCOLS * QCH; ci += kThreads) {
+      const int col = ci / QCH, c = ci % QCH;
+      const int tk = t0 + col / p.group, hd = kvh * p.group + col % p.group;
+      const bool ok = col < p.q_tile * p.group && tk < t1;
+      const QT *q = reinterpret_cast<const QT *>(p.query) +
+                    ((size_t)(q_begin + (ok ? tk : t0)) * p.num_heads + hd) * D + 8 * c;
+      *reinterpret_cast<u32x4 *>(&sq[col][(c ^ qswz(col)) * 8]) =
+          ok ? load16(q) : u32x4{0u, 0u, 0u, 0u};
+    }
+  } else {
 #pragma unroll
-  for (int j = 0; j < NT; ++j) {
-    const QT *q = reinterpret_cast<const QT *>(p.query) +
-                  ((size_t)(q_begin + (col_ok[j] ? tok[j] : t0)) * p.num_heads + head[j]) * D;
+    for (int j = 0; j < NT; ++j) {
+      const QT *q = reinterpret_cast<const QT *>(p.query) +
+                    ((size_t)(q_begin + (col_ok[j] ? tok[j] : t0)) * p.num_heads + head[j]) * D;
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks)
-      qop[j][ks] = col_ok[j] ? load16(q + 32 * ks + 8 * g) : u32x4{0u, 0u, 0u, 0u};
+      for (int ks = 0; ks < NKS; ++ks)
+        qop[j][ks] = col_ok[j] ? load16(q + 32 * ks + 8 * g) : u32x4{0u, 0u, 0u, 0u};
+    }
   }
 
   const char *kcache = reinterpret_cast<const char *>(p.key_cache);
@@ -258,14 +288,26 @@ __global__ void __launch_bounds__(kThreads)
     // S^T of every column tile; each K fragment read from LDS feeds NT MFMAs.
     f32x4 sc[NT][NSUB];
 #pragma unroll
-    for (int h = 0; h < NSUB; ++h) {
+    for (int h = 0; h < NSUB; ++h)
 #pragma unroll
       for (int j = 0; j < NT; ++j) sc[j][h] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
+    for (int ks = 0; ks < NKS; ++ks) {
+      u32x4 qv[NT];
+#pragma unroll
+      for (int j = 0; j < NT; ++j) {
+        if constexpr (kQLds) {
+          const int row = 16 * (NT * wv + j) + n;
+          qv[j] = *reinterpret_cast<const u32x4 *>(&sq[row][((4 * ks + g) ^ qswz(row)) * 8]);
+        } else {
+          qv[j] = qop[j][ks];
+        }
+      }
+#pragma unroll
+      for (int h = 0; h < NSUB; ++h) {
         const u32x4 a = *reinterpret_cast<const u32x4 *>(&sk[16 * h + n][32 * ks + 8 * g]);
 #pragma unroll
-        for (int j = 0; j < NT; ++j) sc[j][h] = mfma_qk(a, qop[j][ks], sc[j][h], QT());
+        for (int j = 0; j < NT; ++j) sc[j][h] = mfma_qk(a, qv[j], sc[j][h], QT());
       }
     }
     u32x4 pop[NT][NHALF];
