@@ -3,20 +3,26 @@
 One step = one pass of the whole decode hot path over one batch: the
 per-sequence v1/v2 choice, Phase 1 (partition kernel) and Phase 2 (reduce
 kernel), one call of the library's C ABI (arguments marshalled once, before
-timing).  The default workload is the GQA bf16
-decode batch (64 sequences, 28 query / 4 KV heads, head size 128, block size
-16, lengths uniform in [1024, 8192]).
+timing).  The headline workload is the largest that fits one GPU: the ragged
+MHA ALiBi bf16 batch (256 sequences, 32 query / 32 KV heads, head size 128,
+block size 16, lognormal lengths of median 2048 clipped to [16, 32768], about
+14 GB of KV; the auto path mixes v1 and v2 there, so both kernels are timed).
+The two other long-context workloads (4 x 100000 fp16 tokens; fp8 KV, 32 x
+32768) are timed in the same process and reported inside the line
+(``also_timed``; ``--also none`` skips them).  tmp_out is float32 by default
+(``--partials out``: the query dtype).
 
 Inputs are resident in HBM before timing.  By default the step rotates over
-``--copies`` independent copies of the KV pool (4 x ~0.6 GB), so the 256 MB
-Infinity Cache cannot serve one step's KV from the previous step; ``--hot``
-times a single copy instead.  W warm-up steps, then exactly K timed steps
+``--copies`` independent copies of the KV pool (4 x 14 GB for the headline),
+so the 256 MB Infinity Cache cannot serve one step's KV from the previous
+step; ``--hot`` times a single copy instead.  W warm-up steps, then exactly K timed steps
 between device synchronisations give ms_per_step and value.  The same K
 steps are then run again with the library's profiling hook
 (pa_set_timing_events): every launch records HIP events at the kernel's own
 start and end, giving the average partition-kernel duration used for the
-roofline (the recording adds a few microseconds per step, so it is not part
-of the wall-clock region).  The fp64 CPU oracle is timed on a bounded sample of the same
+roofline of the dominant kernel (``frac``) and the partition-start to
+reduce-end time of the whole step (``step_frac``); the recording adds a few
+microseconds per step, so it is not part of the wall-clock region.  The fp64 CPU oracle is timed on a bounded sample of the same
 workload for the CPU baseline.  ``--window W`` / ``--softcap C`` turn on the
 decode options (sliding window over the last W + 1 keys, logit soft cap);
 the KV bytes then count the keys inside the window only.  ``--layout
@@ -63,9 +69,10 @@ def kernel_source_hash(prefill: bool = False) -> str:
     return h.hexdigest()[:16]
 
 
-def algorithmic_bytes(wl, path: str, cu: int, B, window_left: int = -1) -> dict:
+def algorithmic_bytes(wl, path: str, cu: int, B, window_left: int = -1,
+                      partials: str = "f32") -> dict:
     """Bytes each launch must move at minimum (each KV byte inside the window
-    once per KV head)."""
+    once per KV head; partial rows in the partial dtype)."""
     import numpy as np
     lens = wl.lens.astype(np.int64)
     t_lo = np.maximum(0, lens - 1 - window_left) if window_left >= 0 else np.zeros_like(lens)
@@ -87,28 +94,30 @@ def algorithmic_bytes(wl, path: str, cu: int, B, window_left: int = -1) -> dict:
     else:
         v2 = np.array([B.should_use_v2(wl.num_seqs, wl.num_kv_heads, int(n), cu) for n in eff])
     h, d = wl.num_heads, wl.head_size
-    tmp = int((parts * v2).sum()) * h * d * esz_q   # partial outputs in the query dtype
+    esz_t = 4 if partials == "f32" else esz_q
+    tmp = int((parts * v2).sum()) * h * d * esz_t   # partial outputs
     stats = int((v2 * wl.max_num_partitions).sum()) * h * 8   # values and padding
     multi = v2 & (parts > 1)
     out_p1 = int((~multi).sum()) * h * d * esz_q
     out_p2 = int(multi.sum()) * h * d * esz_q
-    reduce_read = int((parts * multi).sum()) * h * (d * esz_q + 8)
+    reduce_read = int((parts * multi).sum()) * h * (d * esz_t + 8)
     return {"kv": kv, "partition": kv + q + table + tmp + stats + out_p1,
             "reduce": reduce_read + out_p2 + wl.num_seqs * 4,
             "step": kv + q + table + tmp + stats + out + reduce_read,
             "any_v2": bool(v2.any())}
 
 
-def read_traffic(workload_name: str, src_hash: str, call_path: str):
+def read_traffic(workload_name: str, src_hash: str, call_path: str, partials: str):
     """HBM bytes per partition launch from the committed counter summary, if
-    it was measured on the current kernel sources with the same path."""
+    it was measured on the current kernel sources with the same path and
+    partial dtype."""
     path = os.path.join(PROFILES, f"traffic_pa_partition_{workload_name}.md")
     if not os.path.exists(path):
         return None
     vals = {}
     with open(path) as f:
         header = f.readline()
-        if f"path={call_path}" not in header:
+        if f"path={call_path}" not in header or f"partials={partials}" not in header:
             return None
         for line in f:
             if line.startswith("- ") and ":" in line:
@@ -151,6 +160,18 @@ def stream_read_ceiling(B, gib: int, reps: int = 10) -> float:
     gbs = n / (float(np.median(ts)) * 1e-3) / 1e9
     log(f"stream read ceiling: {gbs:.1f} GB/s over {gib} GiB")
     return round(gbs, 1)
+
+
+def cpu_model() -> str:
+    """The host CPU's model name (/proc/cpuinfo), or 'unknown'."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def cpu_baseline(wl, budget_s: float, window_left: int = -1, soft_cap: float = 0.0) -> dict:
@@ -198,6 +219,7 @@ def cpu_baseline(wl, budget_s: float, window_left: int = -1, soft_cap: float = 0
                 break
     gbs = kv_done / spent / 1e9
     return {"value": round(gbs, 5), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": (f"{passes} passes over the first {len(sample)} of the batch's "
                        f"{wl.num_seqs} sequences ({kv_done / 1e6:.1f} MB of KV), v1 + v2 "
                        f"partials + merge in fp64, {threads} threads (one sequence per task, one "
@@ -286,13 +308,172 @@ def bench_prefill(args) -> int:
     return 0
 
 
+def prepare(number: int, args, B, W):
+    """Builds workload ``number`` with ``--copies`` rotating copies (same bytes at
+    other addresses) and its marshalled calls; returns (base, calls, extra)."""
+    import torch
+
+    copies = 1 if args.hot else max(1, args.copies)
+    log(f"building workload {number} x{copies}")
+    base = W.make_workload(number, device="cuda", seed=1000 + number)
+    if args.layout == "block_rows":
+        base.key_cache, base.value_cache = W.to_block_rows(base.key_cache, base.value_cache)
+        torch.cuda.empty_cache()
+    wls = [base]
+    for _ in range(1, copies):
+        # Same bytes at other addresses: identical work, no cache reuse across steps.
+        w2 = W.Workload(**{**base.__dict__})
+        w2.key_cache = base.key_cache.clone()
+        w2.value_cache = base.value_cache.clone()
+        w2.query = base.query.clone()
+        w2.block_tables = base.block_tables.clone()
+        wls.append(w2)
+    stream = torch.cuda.current_stream()
+    calls, keep = [], []
+    for wl in wls:
+        out, es, ml, to = wl.alloc_outputs(args.partials)
+        keep.append((out, es, ml, to))
+        common = (out, es, ml, to, wl.query, wl.key_cache, wl.value_cache, wl.num_kv_heads,
+                  wl.scale, wl.block_tables, wl.seq_lens, wl.block_size, wl.max_seq_len)
+        kw = dict(alibi_slopes=wl.alibi_slopes, kv_cache_dtype=wl.kv_cache_dtype,
+                  k_scale=wl.k_scale, v_scale=wl.v_scale, stream=stream,
+                  window_left=args.window, logits_soft_cap=args.softcap,
+                  kv_layout=args.layout)
+        # Arguments are checked and marshalled once per input copy; a timed step
+        # is one C call (v1 = partition kernel only; v2 / auto = partition +
+        # reduce; split = one launch).
+        if args.path == "v1":
+            calls.append(lambda out=out, wl=wl, kw=kw: B.paged_attention_v1(
+                out, wl.query, wl.key_cache, wl.value_cache, wl.num_kv_heads, wl.scale,
+                wl.block_tables, wl.seq_lens, wl.block_size, wl.max_seq_len, **kw))
+        elif args.path == "split":
+            calls.append(B.PreparedCall("split", *common, **kw,
+                                        counters=B.split_counters(wl.num_seqs, wl.num_heads)))
+        else:
+            calls.append(B.PreparedCall(args.path, *common, **kw))
+    return base, calls, (wls, keep)
+
+
+def time_steps(calls, steps: int, warmup: int, B):
+    """W warm-up steps, K timed steps between device synchronisations (wall
+    clock), then the same K steps again with the library's profiling hook
+    recording each kernel's own start / end.  Returns (wall_s, partition_ms,
+    reduce_ms, step_ms) with the event arrays per step."""
+    import numpy as np
+    import torch
+
+    lib = B.load_library()
+    stream = torch.cuda.current_stream()
+    n = len(calls)
+
+    def launch(i: int, ev=None):
+        if ev is not None:
+            # The library records these at each kernel's own start and end.
+            lib.pa_set_timing_events(*ev)
+        calls[i % n]()
+
+    for i in range(warmup):
+        launch(i)
+    torch.cuda.synchronize()
+    # partition start/stop, reduce start/stop of every timed step; each event
+    # is recorded once here so that its handle exists.
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    for ev in events:
+        for e in ev:
+            e.record(stream)
+    handles = [tuple(e.cuda_event for e in ev) for ev in events]
+    log(f"timing {steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        launch(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    # The same K steps again with the kernels recording their own start / end
+    # (the recording adds a few microseconds per step, so it is kept out of
+    # the wall-clock region above).
+    log(f"timing {steps} steps per kernel")
+    for i in range(steps):
+        launch(i, handles[i])
+    torch.cuda.synchronize()
+    B.set_timing_events()
+    part = np.array([e[0].elapsed_time(e[1]) for e in events])
+    red = np.array([e[2].elapsed_time(e[3]) for e in events])
+    step = np.array([e[0].elapsed_time(e[3]) for e in events])
+    return wall, part, red, step
+
+
+def measure(number: int, args, B, W, cu: int, keep_base: bool = False) -> dict:
+    """Times workload ``number`` on the chosen path; the figures of one bench
+    line (the step, the dominant kernel's roofline, the whole step's).  With
+    ``keep_base`` the first copy of the inputs is returned too (for the CPU
+    baseline); the others are freed."""
+    import numpy as np
+    import torch
+
+    base, calls, hold = prepare(number, args, B, W)
+    ab = algorithmic_bytes(base, args.path, cu, B, args.window, args.partials)
+    wall, part_ms, red_ms, step_ms = time_steps(calls, args.steps, args.warmup, B)
+    if args.path in ("v1", "split") or not ab["any_v2"]:
+        # No reduce kernel runs (an all-v1 auto call records its reduce events
+        # back to back; their gap is event overhead, not work).
+        red_ms = np.zeros(len(part_ms))
+        step_ms = part_ms
+    ms = wall * 1e3 / args.steps
+    part_avg = float(part_ms.mean())
+    step_avg = float(step_ms.mean())
+    achieved = ab["partition"] / (part_avg * 1e-3) / 1e9
+    step_achieved = ab["step"] / (step_avg * 1e-3) / 1e9
+    options = args.window != -1 or args.softcap != 0.0
+    lens = base.lens
+    dtype = {torch.float32: "f32", torch.float16: "f16", torch.bfloat16: "bf16"}[base.dtype]
+    if base.kv_cache_dtype == "fp8_e4m3":
+        dtype = f"{dtype} (fp8 e4m3 KV)"
+    copies = len(calls)
+    res = {
+        "name": base.name,
+        "dtype": dtype,
+        "workload": (f"{base.name}: paged-attention decode, num_seqs={base.num_seqs}, "
+                     f"num_heads={base.num_heads}, num_kv_heads={base.num_kv_heads}, "
+                     f"head_size={base.head_size}, block_size={base.block_size}, "
+                     f"seq_lens {int(lens.min())}..{int(lens.max())} "
+                     f"(sum {int(lens.sum())}), path={args.path}, partials={args.partials}"
+                     + (f", kv_layout={args.layout}" if args.layout != "decode" else "")
+                     + (f", window_left={args.window}, soft_cap={args.softcap:g}"
+                        if options else "")),
+        "ms_per_step": ms,
+        "kv_gbs": ab["kv"] / (ms * 1e-3) / 1e9,
+        "ab": ab,
+        "part_avg": part_avg,
+        "red_avg": float(red_ms.mean()),
+        "step_avg": step_avg,
+        "step_p": [float(np.percentile(step_ms, q)) * 1e3 for q in (10, 50, 90)],
+        "achieved": achieved,
+        "step_achieved": step_achieved,
+        "copies": copies,
+        "options": options,
+        "base": base if keep_base else None,
+    }
+    del calls, hold, base
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--workload", type=int, default=4, choices=[1, 2, 3, 4, 5],
+                    help="the headline workload (default 4: ragged MHA ALiBi bf16, the "
+                         "largest that fits one GPU)")
+    ap.add_argument("--also", default="3,5",
+                    help="other workloads timed in the same process, reported inside the line "
+                         "(comma list, or 'none')")
     ap.add_argument("--path", default="auto", choices=["auto", "v2", "v1", "split"])
+    ap.add_argument("--partials", default="f32", choices=["f32", "out"],
+                    help="dtype of tmp_out: float32 (the default contract) or the query dtype")
     ap.add_argument("--copies", type=int, default=4)
     ap.add_argument("--hot", action="store_true", help="one copy of the inputs (cache-hot)")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
@@ -320,7 +501,6 @@ def main() -> int:
     if args.prefill:
         return bench_prefill(args)
 
-    import numpy as np
     import torch
 
     from paged_kv_cache_297_amd import binding as B
@@ -331,87 +511,12 @@ def main() -> int:
         return 2
     B.load_library()
     torch.cuda.set_device(0)
-    copies = 1 if args.hot else max(1, args.copies)
-    log(f"building workload {args.workload} x{copies}")
-    wls = [W.make_workload(args.workload, device="cuda", seed=1000 + args.workload)]
-    base = wls[0]
-    if args.layout == "block_rows":
-        base.key_cache, base.value_cache = W.to_block_rows(base.key_cache, base.value_cache)
-        torch.cuda.empty_cache()
-    for c in range(1, copies):
-        # Same bytes at other addresses: identical work, no cache reuse across steps.
-        w2 = W.Workload(**{**base.__dict__})
-        w2.key_cache = base.key_cache.clone()
-        w2.value_cache = base.value_cache.clone()
-        w2.query = base.query.clone()
-        w2.block_tables = base.block_tables.clone()
-        wls.append(w2)
-    outs = [wl.alloc_outputs() for wl in wls]
     cu = B.device_cu_count()
-    ab = algorithmic_bytes(base, args.path, cu, B, args.window)
-    stream = torch.cuda.current_stream()
+    also = [] if args.also.strip().lower() in ("", "none") else [
+        int(x) for x in args.also.split(",") if int(x) != args.workload]
 
-    # Arguments are checked and marshalled once per input copy; a timed step is
-    # one C call (v1 = partition kernel only; v2 / auto = partition + reduce).
-    lib = B.load_library()
-    calls = []
-    for wl, (out, es, ml, to) in zip(wls, outs):
-        common = (out, es, ml, to, wl.query, wl.key_cache, wl.value_cache, wl.num_kv_heads,
-                  wl.scale, wl.block_tables, wl.seq_lens, wl.block_size, wl.max_seq_len)
-        kw = dict(alibi_slopes=wl.alibi_slopes, kv_cache_dtype=wl.kv_cache_dtype,
-                  k_scale=wl.k_scale, v_scale=wl.v_scale, stream=stream,
-                  window_left=args.window, logits_soft_cap=args.softcap,
-                  kv_layout=args.layout)
-        if args.path == "v1":
-            calls.append(lambda out=out, wl=wl, kw=kw: B.paged_attention_v1(
-                out, wl.query, wl.key_cache, wl.value_cache, wl.num_kv_heads, wl.scale,
-                wl.block_tables, wl.seq_lens, wl.block_size, wl.max_seq_len, **kw))
-        elif args.path == "split":
-            calls.append(B.PreparedCall("split", *common, **kw,
-                                        counters=B.split_counters(wl.num_seqs, wl.num_heads)))
-        else:
-            calls.append(B.PreparedCall(args.path, *common, **kw))
-
-    def launch(i: int, ev=None):
-        if ev is not None:
-            # The library records these at each kernel's own start and end.
-            lib.pa_set_timing_events(*ev)
-        calls[i % copies]()
-
-    for i in range(args.warmup):
-        launch(i)
-    torch.cuda.synchronize()
-    # partition start/stop, reduce start/stop of every timed step; each event
-    # is recorded once here so that its handle exists.
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    for ev in events:
-        for e in ev:
-            e.record(stream)
-    handles = [tuple(e.cuda_event for e in ev) for ev in events]
-    log(f"timing {args.steps} steps")
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        launch(i)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    # The same K steps again with the kernels recording their own start / end
-    # (the recording adds a few microseconds per step, so it is kept out of
-    # the wall-clock region above).
-    log(f"timing {args.steps} steps per kernel")
-    for i in range(args.steps):
-        launch(i, handles[i])
-    torch.cuda.synchronize()
-    B.set_timing_events()
-    part_ms = np.array([e[0].elapsed_time(e[1]) for e in events])
-    if args.path in ("v1", "split") or not ab["any_v2"]:
-        # No reduce kernel runs (an all-v1 auto call records its reduce events
-        # back to back; their gap is event overhead, not work).
-        red_ms = np.zeros(len(events))
-        step_ms = part_ms
-    else:
-        red_ms = np.array([e[2].elapsed_time(e[3]) for e in events])
-        step_ms = np.array([e[0].elapsed_time(e[3]) for e in events])
+    head = measure(args.workload, args, B, W, cu, keep_base=not args.no_cpu_baseline)
+    others = [measure(n, args, B, W, cu) for n in also]
 
     if args.calibrate_copy:
         n = args.calibrate_copy * (1 << 20)
@@ -420,79 +525,83 @@ def main() -> int:
         for _ in range(3):
             dst.copy_(src)
         torch.cuda.synchronize()
+        del src, dst
         log(f"calibration copy: {n} bytes x3")
 
     # The stream-read ceiling, after the timed steps (allocating its buffer
     # before them slowed the steps by 6%).
     stream_gbs = stream_read_ceiling(B, args.stream_gib) if args.stream_gib > 0 else None
 
-    ms_per_step = wall * 1e3 / args.steps
-    kv_gbs = ab["kv"] / (ms_per_step * 1e-3) / 1e9
-    part_avg = float(part_ms.mean())
-    achieved = ab["partition"] / (part_avg * 1e-3) / 1e9
     src_hash = kernel_source_hash()
-    options = args.window != -1 or args.softcap != 0.0
-    traffic = (read_traffic(base.name, src_hash, args.path)
-               if copies > 1 and not options and args.layout == "decode" else None)
-    dtype = {torch.float32: "f32", torch.float16: "f16", torch.bfloat16: "bf16"}[base.dtype]
-    if base.kv_cache_dtype == "fp8_e4m3":
-        dtype = f"{dtype} (fp8 e4m3 KV)"
-    lens = base.lens
+    ab = head["ab"]
+    traffic = (read_traffic(head["name"], src_hash, args.path, args.partials)
+               if head["copies"] > 1 and not head["options"] and args.layout == "decode"
+               else None)
+    ms = head["ms_per_step"]
     result = {
         "metric": METRIC,
-        "value": round(kv_gbs, 1),
+        "value": round(head["kv_gbs"], 1),
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5),
-        "us_per_step": round(ms_per_step * 1e3, 2),
-        "pct_of_peak": round(100.0 * kv_gbs / HBM_PEAK_GBS, 2),
+        "ms_per_step": round(ms, 5),
+        "us_per_step": round(ms * 1e3, 2),
+        "pct_of_peak": round(100.0 * head["kv_gbs"] / HBM_PEAK_GBS, 2),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": dtype,
+        "dtype": head["dtype"],
         "data": "synthetic",
         "config": {
-            "workload": (f"{base.name}: paged-attention decode, num_seqs={base.num_seqs}, "
-                         f"num_heads={base.num_heads}, num_kv_heads={base.num_kv_heads}, "
-                         f"head_size={base.head_size}, block_size={base.block_size}, "
-                         f"seq_lens {int(lens.min())}..{int(lens.max())} "
-                         f"(sum {int(lens.sum())}), path={args.path}"
-                         + (f", kv_layout={args.layout}" if args.layout != "decode" else "")
-                         + (f", window_left={args.window}, soft_cap={args.softcap:g}"
-                            if options else "")),
+            "workload": head["workload"],
             "path": args.path,
+            "partials": args.partials,
             "window_left": args.window,
             "logits_soft_cap": args.softcap,
             "kv_layout": args.layout,
             "kv_bytes_per_step": ab["kv"],
-            "inputs": ("cache-hot single copy" if copies == 1 else
-                       f"{copies} rotating copies of the KV pool (L2/MALL-cold)"),
+            "inputs": ("cache-hot single copy" if head["copies"] == 1 else
+                       f"{head['copies']} rotating copies of the KV pool (L2/MALL-cold)"),
         },
         "roofline": {
             "bound": "hbm",
             "kernel": ("pa_partition (Phase 1)" if args.layout == "decode"
                        else "pa_partition_nhd (Phase 1, block-rows layout)"),
-            "achieved": round(achieved, 1),
+            "achieved": round(head["achieved"], 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "frac": round(head["achieved"] / HBM_PEAK_GBS, 4),
             "traffic": traffic,
             "algorithmic_bytes_per_launch": ab["partition"],
-            "avg_launch_ms": round(part_avg, 5),
-            "reduce_avg_launch_ms": round(float(red_ms.mean()), 5),
-            "event_step_ms_median": round(float(np.median(step_ms)), 5),
-            "event_step_us_p10_p50_p90": [round(float(np.percentile(step_ms, q)) * 1e3, 2)
-                                          for q in (10, 50, 90)],
+            "avg_launch_ms": round(head["part_avg"], 5),
+            "reduce_avg_launch_ms": round(head["red_avg"], 5),
+            "step_algorithmic_bytes": ab["step"],
+            "step_avg_ms": round(head["step_avg"], 5),
+            "step_achieved": round(head["step_achieved"], 1),
+            "step_frac": round(head["step_achieved"] / HBM_PEAK_GBS, 4),
+            "event_step_us_p10_p50_p90": [round(x, 2) for x in head["step_p"]],
             "kernel_source_hash": src_hash,
             "stream_read_gbs": stream_gbs,
-            "frac_of_stream_read": (round(achieved / stream_gbs, 4) if stream_gbs else None),
+            "frac_of_stream_read": (round(head["achieved"] / stream_gbs, 4)
+                                    if stream_gbs else None),
         },
+        "also_timed": [{
+            "workload": o["workload"], "dtype": o["dtype"],
+            "us_per_step": round(o["ms_per_step"] * 1e3, 2),
+            "kv_gbs": round(o["kv_gbs"], 1),
+            "pct_of_peak": round(100.0 * o["kv_gbs"] / HBM_PEAK_GBS, 2),
+            "kernel_avg_ms": round(o["part_avg"], 5),
+            "kernel_frac": round(o["achieved"] / HBM_PEAK_GBS, 4),
+            "reduce_avg_ms": round(o["red_avg"], 5),
+            "step_frac": round(o["step_achieved"] / HBM_PEAK_GBS, 4),
+            "event_step_us_p10_p50_p90": [round(x, 2) for x in o["step_p"]],
+        } for o in others],
     }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle")
-        result["cpu_baseline"] = cpu_baseline(base, args.cpu_budget, args.window, args.softcap)
+        result["cpu_baseline"] = cpu_baseline(head["base"], args.cpu_budget, args.window,
+                                              args.softcap)
     print(json.dumps(result), flush=True)
     return 0
 

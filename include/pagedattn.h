@@ -46,10 +46,12 @@
  *   seq_lens      int32 [num_seqs]
  *   alibi_slopes  float [num_heads], or NULL for no ALiBi
  *   exp_sums, max_logits  float [num_seqs, num_heads, max_num_partitions]
- *   tmp_out       [num_seqs, num_heads, max_num_partitions, head_size]  dtype
- *                 (the partial outputs are rounded to the query / output
- *                 type, as the V2 page's Phase 1 casts each partition's
- *                 output to the type of its tmp_output buffer)
+ *   tmp_out       [num_seqs, num_heads, max_num_partitions, head_size]
+ *                 float by default; the caller may choose the query /
+ *                 output dtype instead (pa_decode_options.partial_dtype):
+ *                 the V2 page's Phase 1 casts each partition's output to
+ *                 the type of the caller's tmp_output buffer.  Partials are
+ *                 accumulated in fp32 and rounded once to that type.
  *
  * Ownership.  Every buffer belongs to the caller.  The library allocates and
  * frees nothing and keeps no pointer after a call returns.  Its only global
@@ -84,7 +86,17 @@ extern "C" {
 
 #define PA_PARTITION_SIZE 512
 
-typedef enum pa_status {
+/* The enums below are int-sized in C and C++ alike.  A C caller may pass any
+ * int where one is expected; in C++ the fixed base type makes every int value
+ * a valid value of the enum, so the library can reject unknown values
+ * (PA_ERR_BAD_ARGUMENT) without undefined behaviour. */
+#ifdef __cplusplus
+#define PA_ENUM_BASE : int
+#else
+#define PA_ENUM_BASE
+#endif
+
+typedef enum pa_status PA_ENUM_BASE {
   PA_OK = 0,
   PA_ERR_NULL_POINTER = 1, /* a required pointer is NULL                   */
   PA_ERR_BAD_SHAPE = 2,    /* sizes inconsistent or out of the valid range */
@@ -96,16 +108,16 @@ typedef enum pa_status {
 
 /* Element type of query and out (and of the KV cache when kv_cache_dtype is
  * PA_KV_AUTO). */
-typedef enum pa_dtype { PA_DTYPE_F32 = 0, PA_DTYPE_F16 = 1, PA_DTYPE_BF16 = 2 } pa_dtype;
+typedef enum pa_dtype PA_ENUM_BASE { PA_DTYPE_F32 = 0, PA_DTYPE_F16 = 1, PA_DTYPE_BF16 = 2 } pa_dtype;
 
 /* "auto" = the cache holds dtype (V2 page, kv_cache_dtype argument);
  * FP8_E4M3 = the cache holds OCP FP8 E4M3FN bytes, dequantised as
  * value = decode(byte) * k_scale (keys) or * v_scale (values). */
-typedef enum pa_kv_cache_dtype { PA_KV_AUTO = 0, PA_KV_FP8_E4M3 = 1 } pa_kv_cache_dtype;
+typedef enum pa_kv_cache_dtype PA_ENUM_BASE { PA_KV_AUTO = 0, PA_KV_FP8_E4M3 = 1 } pa_kv_cache_dtype;
 
 /* Which algorithm a sequence takes.  AUTO chooses per sequence, on the
  * device, with the rule of pa_should_use_v2. */
-typedef enum pa_mode { PA_MODE_V1 = 0, PA_MODE_V2 = 1, PA_MODE_AUTO = 2 } pa_mode;
+typedef enum pa_mode PA_ENUM_BASE { PA_MODE_V1 = 0, PA_MODE_V2 = 1, PA_MODE_AUTO = 2 } pa_mode;
 
 /* Cache layouts a decode call reads.  DECODE is the V2 page's layout (K
  * [num_blocks, num_kv_heads, head_size/x, block_size, x], V [num_blocks,
@@ -113,7 +125,14 @@ typedef enum pa_mode { PA_MODE_V1 = 0, PA_MODE_V2 = 1, PA_MODE_AUTO = 2 } pa_mod
  * decode signature: K and V both [num_blocks, num_kv_heads, block_size,
  * head_size] (each token's head_size values contiguous); dtype f16 or bf16
  * and kv_cache_dtype AUTO only (others: PA_ERR_UNSUPPORTED). */
-typedef enum pa_kv_layout { PA_KV_LAYOUT_DECODE = 0, PA_KV_LAYOUT_BLOCK_ROWS = 1 } pa_kv_layout;
+typedef enum pa_kv_layout PA_ENUM_BASE { PA_KV_LAYOUT_DECODE = 0, PA_KV_LAYOUT_BLOCK_ROWS = 1 } pa_kv_layout;
+
+/* Element type of the v2 partial outputs in tmp_out (V2 page, "Phase 1:
+ * Per-partition attention": each partition's output is cast to the dtype of
+ * the caller's tmp_output buffer).  F32 is the default; OUT = the query /
+ * output dtype (half the partial-row bytes for 16-bit queries; for f32
+ * queries both are f32). */
+typedef enum pa_partial_dtype PA_ENUM_BASE { PA_PARTIAL_F32 = 0, PA_PARTIAL_OUT = 1 } pa_partial_dtype;
 
 /* Decode options of the *_ex entry points: the sliding window and the logit
  * soft cap of the dispatch page's decode configuration (AttnDispatchConfig
@@ -133,14 +152,17 @@ typedef enum pa_kv_layout { PA_KV_LAYOUT_DECODE = 0, PA_KV_LAYOUT_BLOCK_ROWS = 1
  * partition with no key inside the window gets max_logits = -inf and
  * exp_sums = 0 (as the V2 page's unused partitions) and no tmp_out row;
  * the auto rule (pa_should_use_v2) is applied to the window-clipped length
- * min(L, W + 1).  kv_layout selects the cache layout (pa_kv_layout).  A NULL
- * options pointer means no window, no cap and the DECODE layout: the *_ex
- * call is then the plain call.  window_left < -1, a cap that is negative,
- * infinite or NaN, or an unknown layout returns PA_ERR_BAD_ARGUMENT. */
+ * min(L, W + 1).  kv_layout selects the cache layout (pa_kv_layout) and
+ * partial_dtype the element type of tmp_out (pa_partial_dtype).  A NULL
+ * options pointer means no window, no cap, the DECODE layout and fp32
+ * partials (all fields zero but window_left = -1): the *_ex call is then the
+ * plain call.  window_left < -1, a cap that is negative, infinite or NaN, or
+ * an unknown layout or partial dtype returns PA_ERR_BAD_ARGUMENT. */
 typedef struct pa_decode_options {
   int window_left;
   float logits_soft_cap;
-  int kv_layout;  /* pa_kv_layout of key_cache / value_cache */
+  int kv_layout;      /* pa_kv_layout of key_cache / value_cache */
+  int partial_dtype;  /* pa_partial_dtype of tmp_out */
 } pa_decode_options;
 
 /* ---------------------------------------------------------------------- */
@@ -260,7 +282,8 @@ pa_status paged_attention_partition_ex(
     const float *alibi_slopes, pa_dtype dtype, pa_kv_cache_dtype kv_cache_dtype,
     float k_scale, float v_scale, const pa_decode_options *options, void *stream);
 
-/* Only options->window_left is used here (the soft cap acts in Phase 1). */
+/* Only options->window_left and options->partial_dtype are used here (the
+ * soft cap acts in Phase 1); both must be those the partition phase got. */
 pa_status paged_attention_reduce_ex(
     pa_mode mode, void *out, const float *exp_sums, const float *max_logits,
     const void *tmp_out, int num_seqs, int num_heads, int num_kv_heads, int head_size,
@@ -284,8 +307,8 @@ pa_status paged_attention_reduce_ex(
  * ragged batches (no tail of long single-workgroup sequences, no empty
  * partition slots); on a batch whose sequences already fill the device
  * once, the partial stores and merges cost more than they save.  The result equals the v1
- * / v2 result up to rounding (each partial is rounded to the output type,
- * as tmp_out is).
+ * / v2 result up to rounding (each partial is rounded to the partial dtype
+ * of the options, fp32 by default, as tmp_out is).
  *
  * exp_sums, max_logits and tmp_out (shapes as for v2) serve as scratch for
  * the pieces: their contents after the call are unspecified.  counters is
@@ -341,8 +364,9 @@ typedef struct pa_prefill_options {
  * per-sequence query / key counts (host integers).
  *
  * Supported: dtype f16 / bf16 (f32: PA_ERR_UNSUPPORTED); head_size 64 or 128;
- * block_size 16 or 32; num_heads / num_kv_heads <= 128.  Errors as for the
- * decode calls; cu_seq_* entries that break max_seq_q / max_seq_k / total_q,
+ * block_size 16 or 32; num_heads / num_kv_heads <= 128; scale finite and
+ * >= 0 (a negative or non-finite scale: PA_ERR_BAD_ARGUMENT).  Errors as for
+ * the decode calls; cu_seq_* entries that break max_seq_q / max_seq_k / total_q,
  * and block-table entries outside [0, num_blocks), give NaN rows for that
  * sequence (rows past max_seq_q are not written).  Accumulation is fp32. */
 pa_status paged_prefill(

@@ -32,6 +32,8 @@ MODE_CODE = {"v1": 0, "v2": 1, "auto": 2}
 #: pa_kv_layout: "decode" (K [NB, Hkv, D/x, bs, x], V [NB, Hkv, D, bs]) or
 #: "block_rows" (K and V [NB, Hkv, bs, D]).
 LAYOUT_CODE = {"decode": 0, "block_rows": 1}
+#: pa_partial_dtype: tmp_out in float32 (the default) or in the query dtype.
+PARTIAL_F32, PARTIAL_OUT = 0, 1
 
 #: Every symbol include/pagedattn.h declares.
 EXPORTED_SYMBOLS = (
@@ -52,10 +54,11 @@ class PrefillOptions(ctypes.Structure):
 
 
 class DecodeOptions(ctypes.Structure):
-    """pa_decode_options: sliding window (-1: none), logit soft cap (0: none) and
-    the cache layout (LAYOUT_CODE)."""
+    """pa_decode_options: sliding window (-1: none), logit soft cap (0: none),
+    the cache layout (LAYOUT_CODE) and the partial dtype of tmp_out
+    (PARTIAL_F32 / PARTIAL_OUT)."""
     _fields_ = [("window_left", ctypes.c_int), ("logits_soft_cap", ctypes.c_float),
-                ("kv_layout", ctypes.c_int)]
+                ("kv_layout", ctypes.c_int), ("partial_dtype", ctypes.c_int)]
 
 
 class PagedAttentionError(RuntimeError):
@@ -159,13 +162,23 @@ def _layout_code(kv_layout: str) -> int:
     return LAYOUT_CODE[kv_layout]
 
 
-def _options(window_left: int, logits_soft_cap: float,
-             kv_layout: str = "decode") -> Optional[DecodeOptions]:
+def _options(window_left: int, logits_soft_cap: float, kv_layout: str = "decode",
+             partial: int = PARTIAL_F32) -> Optional[DecodeOptions]:
     """None when every option is off (the plain entry point is called)."""
     code = _layout_code(kv_layout)
-    if int(window_left) == -1 and float(logits_soft_cap) == 0.0 and code == 0:
+    if int(window_left) == -1 and float(logits_soft_cap) == 0.0 and code == 0 and partial == 0:
         return None
-    return DecodeOptions(int(window_left), float(logits_soft_cap), code)
+    return DecodeOptions(int(window_left), float(logits_soft_cap), code, int(partial))
+
+
+def _partial_code(tmp_out: torch.Tensor, query: torch.Tensor) -> int:
+    """pa_partial_dtype from the dtype of the caller's tmp_out: float32, or the
+    query dtype (the V2 page casts each partial to the tmp_output dtype)."""
+    if tmp_out.dtype == torch.float32:
+        return PARTIAL_F32
+    if tmp_out.dtype == query.dtype:
+        return PARTIAL_OUT
+    raise TypeError("tmp_out must be float32 or have the query's dtype")
 
 
 def _call(lib, name: str, args, opts: Optional[DecodeOptions]) -> None:
@@ -253,8 +266,9 @@ def _v2_args(out, exp_sums, max_logits, tmp_out, query, key_cache, value_cache, 
     for name, t in (("exp_sums", exp_sums), ("max_logits", max_logits)):
         if t.dtype != torch.float32 or not t.is_contiguous():
             raise TypeError(f"{name} must be a contiguous float32 tensor")
-    if tmp_out.dtype != query.dtype or not tmp_out.is_contiguous():
-        raise TypeError("tmp_out must be a contiguous tensor of the query's dtype")
+    _partial_code(tmp_out, query)
+    if not tmp_out.is_contiguous():
+        raise TypeError("tmp_out must be contiguous")
     p = exp_sums.shape[2]
     if exp_sums.shape != (b, h, p) or max_logits.shape != (b, h, p) or tmp_out.shape != (b, h, p, d):
         raise ValueError("exp_sums/max_logits must be [B, H, P] and tmp_out [B, H, P, D]")
@@ -277,7 +291,8 @@ def paged_attention_v2(out, exp_sums, max_logits, tmp_out, query, key_cache, val
     args = _v2_args(out, exp_sums, max_logits, tmp_out, query, key_cache, value_cache,
                     num_kv_heads, scale, block_tables, seq_lens, block_size, max_seq_len,
                     alibi_slopes, kv_cache_dtype, k_scale, v_scale, stream, kv_layout)
-    _call(lib, "paged_attention_v2", args, _options(window_left, logits_soft_cap, kv_layout))
+    _call(lib, "paged_attention_v2", args, _options(window_left, logits_soft_cap, kv_layout,
+                                                    _partial_code(tmp_out, query)))
 
 
 def paged_attention_auto(out, exp_sums, max_logits, tmp_out, query, key_cache, value_cache,
@@ -290,7 +305,8 @@ def paged_attention_auto(out, exp_sums, max_logits, tmp_out, query, key_cache, v
     args = _v2_args(out, exp_sums, max_logits, tmp_out, query, key_cache, value_cache,
                     num_kv_heads, scale, block_tables, seq_lens, block_size, max_seq_len,
                     alibi_slopes, kv_cache_dtype, k_scale, v_scale, stream, kv_layout)
-    _call(lib, "paged_attention_auto", args, _options(window_left, logits_soft_cap, kv_layout))
+    _call(lib, "paged_attention_auto", args, _options(window_left, logits_soft_cap, kv_layout,
+                                                      _partial_code(tmp_out, query)))
 
 
 def split_counters(num_seqs: int, num_heads: int, device="cuda") -> torch.Tensor:
@@ -316,7 +332,7 @@ def paged_attention_split(out, exp_sums, max_logits, tmp_out, counters, query, k
     """Balanced split decode: writes ``out``; the partial buffers are scratch and
     ``counters`` (split_counters) must be zero on entry (it is left zero)."""
     lib = load_library()
-    opts = _options(window_left, logits_soft_cap, kv_layout)
+    opts = _options(window_left, logits_soft_cap, kv_layout, _partial_code(tmp_out, query))
     args = _split_args(out, exp_sums, max_logits, tmp_out, counters, query, key_cache,
                        value_cache, num_kv_heads, scale, block_tables, seq_lens, block_size,
                        max_seq_len, alibi_slopes, kv_cache_dtype, k_scale, v_scale, stream,
@@ -340,7 +356,8 @@ class PreparedCall:
         self.name = f"paged_attention_{mode}"
         if mode not in ("v2", "auto", "split"):
             raise ValueError("mode must be 'v2', 'auto' or 'split'")
-        self.opts = _options(window_left, logits_soft_cap, kv_layout)
+        self.opts = _options(window_left, logits_soft_cap, kv_layout,
+                             _partial_code(tmp_out, query))
         self.counters = counters
         if mode == "split":
             if counters is None:
@@ -382,7 +399,7 @@ def paged_attention_partition(mode, out, exp_sums, max_logits, tmp_out, query, k
                     num_kv_heads, scale, block_tables, seq_lens, block_size, max_seq_len,
                     alibi_slopes, kv_cache_dtype, k_scale, v_scale, stream, kv_layout)
     _call(lib, "paged_attention_partition", [MODE_CODE[mode]] + args,
-          _options(window_left, logits_soft_cap, kv_layout))
+          _options(window_left, logits_soft_cap, kv_layout, _partial_code(tmp_out, query)))
 
 
 def paged_attention_reduce(mode, out, exp_sums, max_logits, tmp_out, seq_lens, num_kv_heads,
@@ -395,7 +412,8 @@ def paged_attention_reduce(mode, out, exp_sums, max_logits, tmp_out, seq_lens, n
     args = [MODE_CODE[mode], out.data_ptr(), exp_sums.data_ptr(), max_logits.data_ptr(),
             tmp_out.data_ptr(), b, h, num_kv_heads, d, seq_lens.data_ptr(), int(max_seq_len), p,
             DTYPE_CODE[out.dtype], _stream(stream)]
-    _call(lib, "paged_attention_reduce", args, _options(window_left, 0.0))
+    _call(lib, "paged_attention_reduce", args,
+          _options(window_left, 0.0, partial=_partial_code(tmp_out, out)))
 
 
 def _prefill_args(out, query, key_cache, value_cache, num_kv_heads, scale, block_tables,

@@ -121,24 +121,30 @@ struct Call {
   int window_left;        // pa_decode_options (-1: no window)
   float logits_soft_cap;  // (0: no soft cap)
   int kv_layout;          // pa_kv_layout
+  int partial_dtype;      // pa_partial_dtype of tmp_out
   int32_t *counters;      // paged_attention_split only (mode is then V2 for validation)
   bool split;
   hipStream_t stream;
 };
 
-// Copies the decode options into the call (NULL: both off).
+// Copies the decode options into the call (NULL: every option off, fp32
+// partials).
 pa_status apply_options(const pa_decode_options *o, Call &c) {
   c.window_left = -1;
   c.logits_soft_cap = 0.0f;
   c.kv_layout = PA_KV_LAYOUT_DECODE;
+  c.partial_dtype = PA_PARTIAL_F32;
   if (!o) return PA_OK;
   if (o->window_left < -1) return PA_ERR_BAD_ARGUMENT;
   if (!isfinite(o->logits_soft_cap) || o->logits_soft_cap < 0.0f) return PA_ERR_BAD_ARGUMENT;
   if (o->kv_layout != PA_KV_LAYOUT_DECODE && o->kv_layout != PA_KV_LAYOUT_BLOCK_ROWS)
     return PA_ERR_BAD_ARGUMENT;
+  if (o->partial_dtype != PA_PARTIAL_F32 && o->partial_dtype != PA_PARTIAL_OUT)
+    return PA_ERR_BAD_ARGUMENT;
   c.window_left = o->window_left;
   c.logits_soft_cap = o->logits_soft_cap;
   c.kv_layout = o->kv_layout;
+  c.partial_dtype = o->partial_dtype;
   return PA_OK;
 }
 
@@ -301,6 +307,7 @@ Params make_params(const Call &c, int cu, int head_groups) {
                                         (c.mode == PA_MODE_AUTO && p.auto_all_v2))
                                    ? 1
                                    : 0;
+  p.tmp_f32 = (c.dtype == PA_DTYPE_F32 || c.partial_dtype == PA_PARTIAL_F32) ? 1 : 0;
   p.scale_log2 = c.scale * c.k_scale * 1.4426950408889634f;
   p.v_scale = c.v_scale;
   // A window no sequence outgrows (W >= max_seq_len - 1) clips nothing: the
@@ -311,6 +318,8 @@ Params make_params(const Call &c, int cu, int head_groups) {
     p.cap_in = (float)(2.0 * 1.4426950408889634 * (double)c.scale * (double)c.k_scale /
                        (double)c.logits_soft_cap);
     p.cap_out = (float)((double)c.logits_soft_cap * 1.4426950408889634);
+    p.cap_in_nat =
+        (float)(2.0 * (double)c.scale * (double)c.k_scale / (double)c.logits_soft_cap);
   }
   return p;
 }
@@ -426,6 +435,7 @@ Call make_call(pa_mode mode, void *out, float *exp_sums, float *max_logits, void
   c.window_left = -1;
   c.logits_soft_cap = 0.0f;
   c.kv_layout = PA_KV_LAYOUT_DECODE;
+  c.partial_dtype = PA_PARTIAL_F32;
   c.counters = nullptr;
   c.split = false;
   c.stream = reinterpret_cast<hipStream_t>(stream);
@@ -654,8 +664,10 @@ pa_status paged_prefill(void *out, const void *query, const void *key_cache,
   if (options) o = *options;
   if (dtype != PA_DTYPE_F32 && dtype != PA_DTYPE_F16 && dtype != PA_DTYPE_BF16)
     return PA_ERR_BAD_ARGUMENT;
+  // A negative scale is refused: the kernel's step max is the max of the raw
+  // dot products scaled once, the max logit only for scale >= 0.
   if (o.window_left < -1 || o.window_right < -1 || !isfinite(o.logits_soft_cap) ||
-      o.logits_soft_cap < 0.0f || !isfinite(scale))
+      o.logits_soft_cap < 0.0f || !isfinite(scale) || scale < 0.0f)
     return PA_ERR_BAD_ARGUMENT;
   if (o.logits_soft_cap > 0.0f &&
       !isfinite((float)((double)scale / (double)o.logits_soft_cap)))
@@ -790,6 +802,6 @@ const char *pa_status_string(pa_status status) {
   return "unknown status";
 }
 
-const char *pa_version(void) { return "0.1.0"; }
+const char *pa_version(void) { return "0.2.0"; }
 
 }  // extern "C"

@@ -113,13 +113,23 @@ __device__ __forceinline__ unsigned keep_pair_mask(int t, int lo, int span) {
 
 // A key's logit in log2 units, before the ALiBi term, from its dot product
 // with the query: scale * k_scale * q.K, or under a soft cap c (CAP)
-// c * tanh(scale * k_scale * q.K / c), with tanh(y) = 1 - 2 / (exp(2y) + 1)
-// (an exp that overflows to +inf gives 1, one that underflows to 0 gives -1).
+// c * tanh(scale * k_scale * q.K / c).  The 16-bit kernels take
+// tanh(y) = 1 - 2 / (exp(2y) + 1) from the hardware exp2 and reciprocal (an
+// exp that overflows to +inf gives 1, one that underflows to 0 gives -1): it
+// cancels near y = 0, a few ulps of 1 absolute, far below 16-bit tolerances.
+// ACCURATE (fp32 queries) takes tanh(y) = expm1(2y) / (expm1(2y) + 2), which
+// keeps a relative error of a few ulps at every y; 2y is clamped at 20,
+// where tanh is 1 in fp32 (a NaN passes the clamp).
 // The cap is a compile-time choice: a run-time branch here, even a uniform
 // one, splits the tile loop and costs the loads their overlap.
-template <bool CAP, typename P>
+template <bool CAP, bool ACCURATE = false, typename P>
 __device__ __forceinline__ float scaled_logit(const P &p, float dot) {
-  if constexpr (CAP) {
+  if constexpr (CAP && ACCURATE) {
+    float y2 = dot * p.cap_in_nat;
+    y2 = y2 > 20.0f ? 20.0f : y2;
+    const float em = expm1f(y2);
+    return p.cap_out * (em / (em + 2.0f));
+  } else if constexpr (CAP) {
     const float e = fast_exp2(dot * p.cap_in);
     return fmaf(-2.0f * p.cap_out, __builtin_amdgcn_rcpf(e + 1.0f), p.cap_out);
   } else {

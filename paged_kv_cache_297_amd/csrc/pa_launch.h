@@ -1,8 +1,9 @@
 // Internal launcher entry points (one translation unit per element-type
-// combination, so the kernel instantiations compile in parallel).
+// combination, so the kernel instantiations compile in parallel).  Host-side
+// declarations only: this header is also compiled by a plain C++ compiler
+// (the host library's sanitizer build).
 #pragma once
 
-#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include "pa_params.h"
@@ -11,23 +12,14 @@ namespace pa {
 
 enum DtCode : int { kDtF32 = 0, kDtF16 = 1, kDtBF16 = 2 };
 
-// Where and how one kernel is launched.  With both events set, the launch
-// goes through hipExtLaunchKernelGGL, which records them at the kernel's own
-// start and end (the profiling hook of pa_set_timing_events).
+// Where and how one kernel is launched (launch_kernel in
+// pa_launch_kernel.h): with both events set, the launch records them at the
+// kernel's own start and end (the profiling hook of pa_set_timing_events).
 struct Launch {
   dim3 grid;
   hipStream_t stream;
   hipEvent_t start, stop;
 };
-
-template <typename Kernel, typename P>
-hipError_t launch_kernel(Kernel kernel, const Launch &l, const P &p) {
-  if (l.start && l.stop)
-    hipExtLaunchKernelGGL(kernel, l.grid, dim3(kThreads), 0, l.stream, l.start, l.stop, 0, p);
-  else
-    hipLaunchKernelGGL(kernel, l.grid, dim3(kThreads), 0, l.stream, p);
-  return hipGetLastError();
-}
 
 // Largest power-of-two query-head group the VALU kernel keeps in registers
 // (the query slices of one lane may use at most 64 VGPRs).

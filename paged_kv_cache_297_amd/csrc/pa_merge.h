@@ -1,0 +1,79 @@
+// The merge of partial results and the arrival protocol of a work item cut
+// into pieces, shared by the device kernels and by a host build (plain C++,
+// no HIP headers) that exercises the same code on the CPU.
+//
+// Merge: Phase 2 of page "BI-V100 PagedAttention V2 implementation" ("Phase
+// 2: Reduce across partitions (log-sum-exp)"): partials c = 0 .. k-1 with max
+// logit m_c (natural-log units), exp-sum S_c and normalised output O_c give
+//   M = max_c m_c,  r_c = exp(m_c - M) S_c,  out = sum_c r_c O_c / sum_c r_c.
+#pragma once
+
+#if defined(__HIPCC__)
+#define PA_HD __host__ __device__
+#define PA_UNROLL4 _Pragma("unroll 4")
+#else
+#include <math.h>
+#define PA_HD
+#define PA_UNROLL4
+#endif
+
+namespace pa {
+
+constexpr float kMergeLog2e = 1.4426950408889634f;
+
+// One output element of the merge above.  A partial with m_c = -inf (no key
+// in its range) adds nothing and its O_c is not read; a NaN m_c (a piece that
+// met an invalid block-table entry) makes the result NaN.  exp2_fn(x) = 2^x;
+// load_o(c) = O_c.  The partials are taken in index order, so the result
+// does not depend on the order in which they were produced.
+template <typename Exp2, typename LoadO>
+PA_HD inline float lse_merge(const float *m, const float *s, int k, Exp2 exp2_fn, LoadO load_o) {
+  const float ninf = -__builtin_inff();
+  float big_m = ninf;
+  bool nan_seen = false;
+  for (int c = 0; c < k; ++c) {
+    nan_seen |= m[c] != m[c];
+    big_m = fmaxf(big_m, m[c]);
+  }
+  float sum = 0.0f, acc = 0.0f;
+  PA_UNROLL4
+  for (int c = 0; c < k; ++c) {
+    const float mc = m[c];
+    const float r = mc == ninf ? 0.0f : exp2_fn((mc - big_m) * kMergeLog2e) * s[c];
+    sum += r;
+    acc = mc == ninf ? acc : fmaf(r, load_o(c), acc);
+  }
+  return nan_seen ? __builtin_nanf("") : acc / sum;
+}
+
+// The arrival of one of the k pieces of an item at the item's counter (zero
+// before its first piece arrives): true for the piece that arrives last,
+// which also resets the counter to zero, so the next call finds it zero.
+// fetch_add(ctr) adds 1 and returns the value before the addition; on the
+// device it is an agent-scope release, so every piece's partial stores are
+// ordered before its increment, and the increments form one release
+// sequence.  acquire(ctr) runs in the last piece only, before it reads
+// anything: an acquire load of the counter (on the device at agent scope),
+// which reads the last increment and so synchronises with every piece's
+// release.  store(ctr, v) writes v.
+template <typename FetchAdd, typename Acquire, typename Store>
+PA_HD inline bool arrive_last(int *ctr, int k, FetchAdd fetch_add, Acquire acquire, Store store) {
+  const bool last = fetch_add(ctr) == k - 1;
+  if (last) {
+    acquire(ctr);
+    store(ctr, 0);
+  }
+  return last;
+}
+
+// Keys per piece when a range of len keys is cut into
+// k = ceil(len / target) pieces (1 .. max_pieces) of equal length, rounded up
+// to 32 keys (the MFMA step); the last piece may be shorter.
+PA_HD inline int split_piece_len(int target, int len, int max_pieces) {
+  int k = (len + target - 1) / target;
+  k = k < max_pieces ? k : max_pieces;
+  k = k > 1 ? k : 1;
+  return ((len + k - 1) / k + 31) / 32 * 32;
+}
+
+}  // namespace pa

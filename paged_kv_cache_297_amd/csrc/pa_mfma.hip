@@ -1,5 +1,5 @@
 // MFMA partition kernels: 16-bit query with a 16-bit or fp8 E4M3FN cache.
-#include "pa_launch.h"
+#include "pa_launch_kernel.h"
 #include "pa_partition_mfma.h"
 
 namespace pa {

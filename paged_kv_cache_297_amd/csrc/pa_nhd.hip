@@ -1,7 +1,7 @@
 // Partition kernels for the [num_blocks, Hkv, block_size, head_size] cache
 // layout, 16-bit caches: the VALU form for one to four query heads per KV
 // head, the MFMA form (block-rows variant) for wider groups.
-#include "pa_launch.h"
+#include "pa_launch_kernel.h"
 #include "pa_partition_mfma.h"
 #include "pa_partition_nhd.h"
 

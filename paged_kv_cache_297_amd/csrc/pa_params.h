@@ -43,7 +43,7 @@ struct Params {
   void *out;            // [B, H, D] dtype
   float *exp_sums;      // [B, H, P]
   float *max_logits;    // [B, H, P]
-  void *tmp_out;        // [B, H, P, D] dtype
+  void *tmp_out;        // [B, H, P, D] fp32 (tmp_f32) or the query dtype
   const void *query;    // [B, H, D] dtype
   const void *key_cache;    // [NB, Hkv, D/x, bs, x]
   const void *value_cache;  // [NB, Hkv, D, bs]
@@ -63,6 +63,8 @@ struct Params {
   int cap_on;           // logit soft cap c > 0 in use
   float cap_in;         // 2 * log2(e) * scale * k_scale / c: exponent of exp(2 s / c)
   float cap_out;        // c * log2(e): the capped logit in log2 units
+  float cap_in_nat;     // 2 * scale * k_scale / c: 2y of tanh(y) (fp32 kernels)
+  int tmp_f32;          // partial outputs are stored as fp32 (else in the query dtype)
   int *counters;        // split mode: [B, H] arrival counters, zero between calls
   int split_target;     // split mode: keys per piece before equalising (multiple of 512)
 };

@@ -15,6 +15,7 @@
 #pragma once
 
 #include "pa_device.h"
+#include "pa_merge.h"
 
 namespace pa {
 
@@ -57,16 +58,6 @@ __device__ __forceinline__ void write_stat_empty(const Params &p, const Work &w,
     p.max_logits[row] = -__builtin_inff();
     p.exp_sums[row] = 0.0f;
   }
-}
-
-// Split mode: keys per piece for a sequence with `len` keys from its
-// 32-aligned start: k = ceil(len / split_target) pieces (at most max_pieces,
-// the grid's depth) of equal length rounded up to 32 keys.
-__device__ __forceinline__ int split_piece_len(const Params &p, int len, int max_pieces) {
-  int k = (len + p.split_target - 1) / p.split_target;
-  k = k < max_pieces ? k : max_pieces;
-  k = k > 1 ? k : 1;
-  return ((len + k - 1) / k + 31) / 32 * 32;
 }
 
 // Decodes one work item (sequence, grid-x slot = KV head x head group,
@@ -116,7 +107,9 @@ __device__ __forceinline__ bool decode_work(const Params &p, int seq, int xslot,
     const int base = w.t_lo / 32 * 32;
     const int len = w.L - base;
     if (w.part * 512 >= len) return false;
-    const int piece = split_piece_len(p, len, (int)gridDim.z);
+    // k = ceil(len / split_target) pieces (at most the grid's depth) of
+    // equal length rounded up to 32 keys.
+    const int piece = split_piece_len(p.split_target, len, (int)gridDim.z);
     const int k = (len + piece - 1) / piece;
     if (w.part >= k) return false;
     w.n_part = k;
@@ -161,12 +154,17 @@ __device__ __forceinline__ bool begin_work(const Params &p, int block_size, int 
 
 // ---------------------------------------------------------------------------
 // Split mode: the pieces of one (sequence, grid-x slot) exchange their
-// partials through memory and an arrival counter.  The partials are stored
-// and loaded with device-scope relaxed atomics, which write through and read
-// past the non-coherent state of the per-XCD L2 caches, so no cache-wide
-// writeback or invalidate is needed (a device-scope fence costs one of
-// each, per wave); ordering comes from waiting for the stores to complete
-// before the workgroup barrier that precedes the arrival.
+// partials through memory and an arrival counter.  Ordering: every wave
+// waits for its partial stores to complete and meets the others at a
+// workgroup barrier (workgroup-scope happens-before); thread 0 then adds 1 to
+// the counter with an agent-scope release atomic, which orders the
+// workgroup's stores before the increment; in the piece that arrives last an
+// agent-scope acquire load of the counter (it reads the last increment),
+// followed by a workgroup barrier, orders the increments of every other
+// piece before the loads of the merge.  The
+// partials themselves are stored and loaded with agent-scope relaxed atomics:
+// they write through and read past the per-XCD L2 caches, so the release
+// finds no dirty lines of them to write back.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ void coherent_store(void *ptr, unsigned v) {
   __hip_atomic_store(reinterpret_cast<unsigned *>(ptr), v, __ATOMIC_RELAXED,
@@ -177,7 +175,8 @@ __device__ __forceinline__ unsigned coherent_load(const void *ptr) {
                            __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// One element of a partial row, rounded to QT, stored / loaded past the L2.
+// One element of a partial row, rounded to QT (fp32 or a 16-bit type),
+// stored / loaded past the L2.
 template <typename QT>
 __device__ __forceinline__ void coherent_store_elem(QT *ptr, float v) {
   if constexpr (sizeof(QT) == 4) {
@@ -203,7 +202,7 @@ __device__ __forceinline__ float coherent_load_elem(const QT *ptr) {
 // arrives last at the (sequence, grid-x slot) counter merges the k pieces
 // with the log-sum-exp rescale of the V2 page's Phase 2, writes out, and
 // resets the counter to zero for the next call.
-template <typename QT, int D>
+template <typename QT, typename TT, int D>
 __device__ __forceinline__ void split_merge(const Params &p, const Work &w) {
   __shared__ int sm_last;
   __shared__ float sm_pm[16][kSplitMaxPieces], sm_ps[16][kSplitMaxPieces];
@@ -211,11 +210,15 @@ __device__ __forceinline__ void split_merge(const Params &p, const Work &w) {
   __syncthreads();
   if (threadIdx.x == 0) {
     int *ctr = p.counters + (size_t)w.seq * p.num_heads + w.xslot;
-    const int last =
-        __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-        w.n_part - 1;
-    if (last) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    sm_last = last;
+    sm_last = arrive_last(
+        ctr, w.n_part,
+        [](int *c) {
+          return __hip_atomic_fetch_add(c, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        },
+        [](int *c) { (void)__hip_atomic_load(c, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT); },
+        [](int *c, int v) {
+          __hip_atomic_store(c, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        });
   }
   __syncthreads();
   if (!sm_last) return;
@@ -227,27 +230,14 @@ __device__ __forceinline__ void split_merge(const Params &p, const Work &w) {
     sm_ps[h][c] = bits_f(coherent_load(p.exp_sums + r));
   }
   __syncthreads();
-  const QT *to = reinterpret_cast<const QT *>(p.tmp_out);
-  const float ninf = -__builtin_inff();
+  const TT *to = reinterpret_cast<const TT *>(p.tmp_out);
   for (int idx = threadIdx.x; idx < w.nh * D; idx += kThreads) {
     const int h = idx / D, d = idx - h * D;
-    float big_m = ninf;
-    bool nan_seen = false;
-    for (int c = 0; c < w.n_part; ++c) {
-      nan_seen |= sm_pm[h][c] != sm_pm[h][c];
-      big_m = fmaxf(big_m, sm_pm[h][c]);
-    }
-    const QT *col = to + (row0 + (size_t)h * p.max_num_partitions) * D + d;
-    float s = 0.0f, a = 0.0f;
-#pragma unroll 4
-    for (int c = 0; c < w.n_part; ++c) {
-      const float m = sm_pm[h][c];
-      const float r = m == ninf ? 0.0f : fast_exp2((m - big_m) * kLog2e) * sm_ps[h][c];
-      const float o = coherent_load_elem<QT>(col + (size_t)c * D);
-      s += r;
-      a = m == ninf ? a : fmaf(r, o, a);
-    }
-    store_out_row<QT, D>(p, w.seq, w.head0 + h, d, nan_seen ? __builtin_nanf("") : a / s);
+    const TT *col = to + (row0 + (size_t)h * p.max_num_partitions) * D + d;
+    const float o = lse_merge(
+        sm_pm[h], sm_ps[h], w.n_part, [](float x) { return fast_exp2(x); },
+        [&](int c) { return coherent_load_elem<TT>(col + (size_t)c * D); });
+    store_out_row<QT, D>(p, w.seq, w.head0 + h, d, o);
   }
 }
 
@@ -310,14 +300,20 @@ __device__ __forceinline__ void finish_partition(const Params &p, const Work &w,
     const int head = w.head0 + h;
     if (w.v2 && split) {
       const size_t row = ((size_t)w.seq * p.num_heads + head) * p.max_num_partitions + w.part;
-      coherent_store_elem<QT>(reinterpret_cast<QT *>(p.tmp_out) + row * D + d, o);
+      if (p.tmp_f32)
+        coherent_store_elem<float>(reinterpret_cast<float *>(p.tmp_out) + row * D + d, o);
+      else
+        coherent_store_elem<QT>(reinterpret_cast<QT *>(p.tmp_out) + row * D + d, o);
       if (d == 0) {
         coherent_store(p.exp_sums + row, f_bits(sum));
         coherent_store(p.max_logits + row, f_bits(ml));
       }
     } else if (w.v2) {
       const size_t row = ((size_t)w.seq * p.num_heads + head) * p.max_num_partitions + w.part;
-      reinterpret_cast<QT *>(p.tmp_out)[row * D + d] = from_f32<QT>(o);
+      if (p.tmp_f32)
+        reinterpret_cast<float *>(p.tmp_out)[row * D + d] = o;
+      else
+        reinterpret_cast<QT *>(p.tmp_out)[row * D + d] = from_f32<QT>(o);
       if (d == 0) {
         p.exp_sums[row] = sum;
         p.max_logits[row] = ml;
@@ -327,7 +323,10 @@ __device__ __forceinline__ void finish_partition(const Params &p, const Work &w,
       store_out_row<QT, D>(p, w.seq, head, d, o);
     }
   }
-  if (split && w.v2) split_merge<QT, D>(p, w);
+  if (split && w.v2) {
+    if (p.tmp_f32) split_merge<QT, float, D>(p, w);
+    else split_merge<QT, QT, D>(p, w);
+  }
 }
 
 }  // namespace pa

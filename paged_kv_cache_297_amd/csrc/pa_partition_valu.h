@@ -17,6 +17,8 @@
 // element type as the V2 page does before its weighted sum.
 #pragma once
 
+#include <type_traits>
+
 #include "pa_partition_common.h"
 
 namespace pa {
@@ -335,7 +337,8 @@ __global__ void __launch_bounds__(kThreads) PA_VALU_OCCUPANCY pa_partition_valu(
     float alpha[NF], pj[NF];
 #pragma unroll
     for (int j = 0; j < NF; ++j) {
-      float x = scaled_logit<CAP>(p, s[j]) + slope2[j] * (float)(t_abs - w.t_ref);
+      float x = scaled_logit<CAP, std::is_same<QT, float>::value>(p, s[j]) +
+                slope2[j] * (float)(t_abs - w.t_ref);
       x = in_span<WIN>(t_abs, w.t_lo, w.span) ? x : -__builtin_inff();
       const float bm = token_group_max<BS>(x);
       const float m_new = fmaxf(m_run[j], bm);

@@ -18,6 +18,7 @@
 //   lanes of a column);
 //   O^T += V^T . P^T (A = 16 dims x 8 keys of the transposed V, B = P regrouped
 //                    by two permlane swaps, as in the decode kernel).
+#include "pa_launch_kernel.h"
 #include "pa_partition_mfma.h"
 #include "pa_prefill.h"
 

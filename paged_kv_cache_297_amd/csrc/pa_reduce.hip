@@ -9,24 +9,24 @@
 // with max_logit = -inf adds nothing, and its tmp_out row (never written) is
 // not used.
 #include "pa_device.h"
-#include "pa_launch.h"
+#include "pa_launch_kernel.h"
 
 namespace pa {
 
 constexpr int kReduceBatch = 4;  // partitions whose loads one thread issues together
 
-// The 16-byte chunk of a partial row as fp32 values.
-template <typename QT>
-__device__ __forceinline__ void chunk_to_f32(const u32x4 &v, float (&f)[16 / sizeof(QT)]) {
+// The 16-byte chunk of a partial row (element type TT) as fp32 values.
+template <typename TT>
+__device__ __forceinline__ void chunk_to_f32(const u32x4 &v, float (&f)[16 / sizeof(TT)]) {
   const unsigned w[4] = {v.x, v.y, v.z, v.w};
-  if constexpr (sizeof(QT) == 4) {
+  if constexpr (sizeof(TT) == 4) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) f[e] = bits_f(w[e]);
   } else {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const unsigned short h = (unsigned short)(w[e / 2] >> (16 * (e % 2)));
-      f[e] = to_f32(__builtin_bit_cast(QT, h));
+      f[e] = to_f32(__builtin_bit_cast(TT, h));
     }
   }
 }
@@ -38,9 +38,10 @@ __device__ __forceinline__ void chunk_to_f32(const u32x4 &v, float (&f)[16 / siz
 // them into a running (max m, sum s = sum exp(m_p - m) S_p, acc = sum
 // exp(m_p - m) S_p O_p).  The PG running states of each dim are then merged
 // with the same rescale: the result is the merge above with M the global max.
-template <typename QT, int D>
+// QT: the output type; TT: the partial type (fp32, or QT).
+template <typename QT, typename TT, int D>
 __global__ void __launch_bounds__(kThreads) pa_reduce_kernel(const Params p) {
-  constexpr int EPT = 16 / sizeof(QT);  // elements per 16-byte chunk
+  constexpr int EPT = 16 / sizeof(TT);  // elements per 16-byte chunk
   constexpr int TPR = D / EPT;          // threads per partial row
   constexpr int PG = kThreads / TPR;    // partition groups
   static_assert(kThreads % TPR == 0 && D % EPT == 0, "reduce geometry");
@@ -59,7 +60,7 @@ __global__ void __launch_bounds__(kThreads) pa_reduce_kernel(const Params p) {
   const size_t row = ((size_t)seq * p.num_heads + head) * p.max_num_partitions;
   const float *ml = p.max_logits + row;
   const float *es = p.exp_sums + row;
-  const char *to = reinterpret_cast<const char *>(p.tmp_out) + row * D * sizeof(QT);
+  const char *to = reinterpret_cast<const char *>(p.tmp_out) + row * D * sizeof(TT);
   const int c = threadIdx.x % TPR, pg = threadIdx.x / TPR;
   const float ninf = -__builtin_inff();
 
@@ -75,7 +76,7 @@ __global__ void __launch_bounds__(kThreads) pa_reduce_kernel(const Params p) {
       const bool ok = q < n_part;
       mv[j] = ok ? ml[q] : ninf;
       ev[j] = ok ? es[q] : 0.0f;
-      ov[j] = ok ? load16(to + ((size_t)q * D + c * EPT) * sizeof(QT)) : u32x4{0u, 0u, 0u, 0u};
+      ov[j] = ok ? load16(to + ((size_t)q * D + c * EPT) * sizeof(TT)) : u32x4{0u, 0u, 0u, 0u};
     }
     float bm = m_run;
 #pragma unroll
@@ -88,7 +89,7 @@ __global__ void __launch_bounds__(kThreads) pa_reduce_kernel(const Params p) {
     for (int j = 0; j < kReduceBatch; ++j) {
       const float r = (mv[j] == ninf) ? 0.0f : fast_exp2((mv[j] - bm) * kLog2e) * ev[j];
       float f[EPT];
-      chunk_to_f32<QT>(ov[j], f);
+      chunk_to_f32<TT>(ov[j], f);
       s_run += r;
       const bool live = mv[j] != ninf;
 #pragma unroll
@@ -121,19 +122,24 @@ __global__ void __launch_bounds__(kThreads) pa_reduce_kernel(const Params p) {
   }
 }
 
-template <typename QT>
+template <typename QT, typename TT>
 static hipError_t launch_reduce_t(const Params &p, int head_size, const Launch &l) {
-  if (head_size == 64) return launch_kernel(pa_reduce_kernel<QT, 64>, l, p);
-  if (head_size == 128) return launch_kernel(pa_reduce_kernel<QT, 128>, l, p);
+  if (head_size == 64) return launch_kernel(pa_reduce_kernel<QT, TT, 64>, l, p);
+  if (head_size == 128) return launch_kernel(pa_reduce_kernel<QT, TT, 128>, l, p);
   return hipErrorInvalidValue;
 }
 
-// Grid: one workgroup per (query head, sequence).
+// Grid: one workgroup per (query head, sequence).  The partial type is fp32
+// when p.tmp_f32 is set, else the output type.
 hipError_t launch_reduce(const Params &p, int dtype, int head_size, const Launch &l) {
   switch (dtype) {
-    case kDtF32: return launch_reduce_t<float>(p, head_size, l);
-    case kDtF16: return launch_reduce_t<_Float16>(p, head_size, l);
-    case kDtBF16: return launch_reduce_t<__bf16>(p, head_size, l);
+    case kDtF32: return launch_reduce_t<float, float>(p, head_size, l);
+    case kDtF16:
+      return p.tmp_f32 ? launch_reduce_t<_Float16, float>(p, head_size, l)
+                       : launch_reduce_t<_Float16, _Float16>(p, head_size, l);
+    case kDtBF16:
+      return p.tmp_f32 ? launch_reduce_t<__bf16, float>(p, head_size, l)
+                       : launch_reduce_t<__bf16, __bf16>(p, head_size, l);
   }
   return hipErrorInvalidValue;
 }

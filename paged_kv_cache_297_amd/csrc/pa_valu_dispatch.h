@@ -2,7 +2,7 @@
 // kernel instantiations that fit the register budget.
 #pragma once
 
-#include "pa_launch.h"
+#include "pa_launch_kernel.h"
 #include "pa_partition_valu.h"
 
 namespace pa {

@@ -101,14 +101,19 @@ class Workload:
         """Bytes of K and V the live tokens occupy (each read once per KV head)."""
         return int(self.lens.sum()) * self.num_kv_heads * self.head_size * 2 * self.kv_elem_bytes
 
-    def alloc_outputs(self):
-        """out, exp_sums, max_logits, tmp_out on the workload's device."""
+    def alloc_outputs(self, partials: str = "f32"):
+        """out, exp_sums, max_logits, tmp_out on the workload's device; tmp_out
+        is float32 (``partials="f32"``, the default) or in the query dtype
+        (``"out"``)."""
         dev = self.query.device
         b, h, d, p = self.num_seqs, self.num_heads, self.head_size, self.max_num_partitions
         out = torch.empty((b, h, d), dtype=self.dtype, device=dev)
         exp_sums = torch.empty((b, h, p), dtype=torch.float32, device=dev)
         max_logits = torch.empty((b, h, p), dtype=torch.float32, device=dev)
-        tmp_out = torch.empty((b, h, p, d), dtype=self.dtype, device=dev)
+        if partials not in ("f32", "out"):
+            raise ValueError("partials must be 'f32' or 'out'")
+        tdt = torch.float32 if partials == "f32" else self.dtype
+        tmp_out = torch.empty((b, h, p, d), dtype=tdt, device=dev)
         return out, exp_sums, max_logits, tmp_out
 
 

@@ -1,0 +1,87 @@
+"""Kernel choice and grid sizing of the host library, checked against the
+HIP stand-ins of tests/sanitize/hip_host_stubs.cpp (a 256-CU device; nothing
+is launched).  Run only inside the sanitizer build's process
+(tests/test_sanitize_host.py), where the library exports pa_stub_last_launch;
+fake, aligned device addresses are never dereferenced."""
+
+import ctypes
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+from paged_kv_cache_297_amd import binding as B  # noqa: E402
+
+A = 0x10000
+F32, F16, BF16 = 0, 1, 2
+
+
+@pytest.fixture(scope="module")
+def lib():
+    lib = B.load_library()
+    if not hasattr(lib, "pa_stub_last_launch"):
+        pytest.skip("needs the sanitizer build with the HIP stand-ins")
+    return lib
+
+
+def last(lib):
+    kind = ctypes.create_string_buffer(32)
+    grid = (ctypes.c_uint * 3)()
+    args = (ctypes.c_int * 2)()
+    assert lib.pa_stub_last_launch(kind, 32, grid, args) == 1
+    return kind.value.decode(), tuple(grid), tuple(args)
+
+
+def call(lib, fn, B_, H, Hkv, D, bs, L, dtype, kv=0, mode=None, counters=None):
+    P = max(1, -(-L // 512))
+    a = [A, A, A, A, A, A, A, B_, H, Hkv, D, 0.1, A, -(-L // bs), A, 1 << 20, bs, L, P, None,
+         dtype, kv, 1.0, 1.0, None]
+    if fn == "paged_attention_partition":
+        a = [mode] + a
+    elif fn == "paged_attention_split":
+        a = a[:4] + [counters or A] + a[4:-1] + [None, None]
+    assert getattr(lib, fn)(*a) == B.PA_OK
+    return last(lib)
+
+
+def test_gqa_auto_runs_as_plain_v1_on_mfma(lib):
+    # 64 x 4 (sequence, KV head) items fill 256 CUs; 4 x 16 tiles <= 2 x 256.
+    assert call(lib, "paged_attention_auto", 64, 28, 4, 128, 16, 8192, BF16) == \
+        ("mfma", (4, 64, 1), (BF16, 16))
+
+
+def test_long_context_auto_is_all_v2(lib):
+    # 4 x 8 items < 256 CUs: every sequence takes v2; the partition phase has
+    # one grid slice per partition, then the reduce covers (head, sequence).
+    assert call(lib, "paged_attention_partition", 4, 32, 8, 128, 16, 100000, F16,
+                mode=2) == ("valu_f16", (8, 4, 196), (128, 4))
+    assert call(lib, "paged_attention_auto", 4, 32, 8, 128, 16, 100000, F16) == \
+        ("reduce", (32, 4, 1), (F16, 128))
+
+
+def test_fp8_auto_is_all_v1(lib):
+    assert call(lib, "paged_attention_auto", 32, 64, 8, 128, 32, 32768, BF16, kv=1) == \
+        ("mfma_fp8", (8, 32, 1), (BF16, 16))
+
+
+def test_ragged_alibi_auto_mixes(lib):
+    kind, grid, args = call(lib, "paged_attention_partition", 256, 32, 32, 128, 16, 32768,
+                            BF16, mode=2)
+    assert (kind, grid, args) == ("valu_bf16", (32, 256, 64), (128, 1))
+
+
+def test_v1_has_one_slice_and_fp32_valu(lib):
+    a = [A, A, A, A, 2, 4, 2, 64, 0.125, A, 44, A, 64, 16, 700, None, F32, 0, 1.0, 1.0, None]
+    assert lib.paged_attention_v1(*a) == B.PA_OK
+    assert last(lib) == ("valu_f32", (2, 2, 1), (64, 2))
+
+
+def test_split_grid_depth(lib):
+    # Small batch: target B * L * gx / CUs = 4 * 100000 * 8 / 256 = 12500
+    # -> 12800 keys, ceil(100031 / 12800) = 8 slices.
+    assert call(lib, "paged_attention_split", 4, 32, 8, 128, 16, 100000, F16) == \
+        ("valu_f16", (8, 4, 8), (128, 4))

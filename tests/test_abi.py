@@ -297,6 +297,49 @@ def test_ex_cache_layout_option(fn):
     assert lib_split(*split_args(options=layout_opts(3), dtype=BF16)) == BADARG
 
 
+def partial_opts(partial, window_left=-1, cap=0.0):
+    return ctypes.byref(B.DecodeOptions(window_left, cap, 0, partial))
+
+
+@pytest.mark.parametrize("fn", EX_FUNCS)
+def test_ex_partial_dtype_option(fn):
+    """partial_dtype: 0 (fp32 tmp_out) and 1 (query dtype) accepted, anything
+    else rejected before the batch is looked at; both fine for every dtype."""
+    lib = B.load_library()
+    for bad in (2, -1, 7):
+        assert getattr(lib, fn)(*ex_args(fn, partial_opts(bad))) == BADARG
+        assert getattr(lib, fn)(*ex_args(fn, partial_opts(bad), num_seqs=0)) == BADARG
+    for good in (B.PARTIAL_F32, B.PARTIAL_OUT):
+        for dt in (F32, F16, BF16):
+            assert getattr(lib, fn)(*ex_args(fn, partial_opts(good, 40, 5.0), dtype=dt,
+                                             num_seqs=0)) == OK
+        # The other checks still apply.
+        assert getattr(lib, fn)(*ex_args(fn, partial_opts(good), head_size=96)) == UNSUP
+    if fn != "paged_attention_v1_ex":
+        assert getattr(lib, fn)(*ex_args(fn, partial_opts(B.PARTIAL_OUT), tmp_out=A + 8)) == MISAL
+    lib_split = lib.paged_attention_split
+    assert lib_split(*split_args(options=partial_opts(3))) == BADARG
+    assert lib_split(*split_args(options=partial_opts(B.PARTIAL_OUT), dtype=BF16,
+                                 num_seqs=0)) == OK
+    base = [V2, A, A, A, A, 0, 4, 2, 64, A, 700, 2, BF16]
+    assert lib.paged_attention_reduce_ex(*base, partial_opts(B.PARTIAL_OUT), None) == OK
+    assert lib.paged_attention_reduce_ex(*base, partial_opts(5), None) == BADARG
+
+
+def test_binding_partial_dtype_from_tmp_out():
+    """The binding takes the partial dtype from tmp_out's dtype: float32 or the
+    query dtype; any other dtype is refused before a call."""
+    import torch
+    q = torch.empty((2, 4, 64), dtype=torch.bfloat16)
+    assert B._partial_code(torch.empty(1, dtype=torch.float32), q) == B.PARTIAL_F32
+    assert B._partial_code(torch.empty(1, dtype=torch.bfloat16), q) == B.PARTIAL_OUT
+    with pytest.raises(TypeError):
+        B._partial_code(torch.empty(1, dtype=torch.float16), q)
+    assert B._options(-1, 0.0, "decode", B.PARTIAL_F32) is None
+    o = B._options(-1, 0.0, "decode", B.PARTIAL_OUT)
+    assert (o.window_left, o.kv_layout, o.partial_dtype) == (-1, 0, 1)
+
+
 def test_reduce_ex_options():
     lib = B.load_library()
     base = [V2, A, A, A, A, 0, 4, 2, 64, A, 700, 2, F32]
@@ -367,6 +410,9 @@ PREFILL_CASES = [
     (dict(head_size=96), UNSUP), (dict(block_size=8), UNSUP), (dict(dtype=F32), UNSUP),
     (dict(num_heads=258, num_kv_heads=2), UNSUP),   # group 129 > 128
     (dict(dtype=9), BADARG), (dict(scale=float("inf")), BADARG),
+    # A negative scale is refused (the step max is taken on the raw dots).
+    (dict(scale=-0.1), BADARG), (dict(scale=-0.1, num_seqs=0), BADARG),
+    (dict(scale=0.0, num_seqs=0), OK),
     (dict(num_seqs=0), OK), (dict(total_q=0), OK), (dict(max_q=0), OK),
 ]
 

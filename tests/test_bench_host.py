@@ -37,11 +37,12 @@ def test_window_counts_the_keys_inside_it(wl):
     assert bench.algorithmic_bytes(wl, "v2", 256, _NoRule, w)["kv"] == int(eff.sum()) * per_key
 
 
-def test_window_shrinks_tables_and_partials(wl):
-    full = bench.algorithmic_bytes(wl, "v2", 256, _NoRule)
+@pytest.mark.parametrize("partials", ["f32", "out"])
+def test_window_shrinks_tables_and_partials(wl, partials):
+    full = bench.algorithmic_bytes(wl, "v2", 256, _NoRule, partials=partials)
     w = 100
-    win = bench.algorithmic_bytes(wl, "v2", 256, _NoRule, w)
-    esz = wl.query.element_size()
+    win = bench.algorithmic_bytes(wl, "v2", 256, _NoRule, w, partials)
+    esz = 4 if partials == "f32" else wl.query.element_size()
     h, d = wl.num_heads, wl.head_size
     # Live partitions: 2100 -> t_lo 1999 -> partitions 3..4; 1100 -> 999 -> 1..2;
     # 513 -> 412 -> 0..1; the rest one each.
@@ -49,7 +50,7 @@ def test_window_shrinks_tables_and_partials(wl):
     assert win["partition"] - win["kv"] < full["partition"] - full["kv"]
     multi = live > 1
     assert win["reduce"] == int((live * multi).sum()) * h * (d * esz + 8) \
-        + int(multi.sum()) * h * d * esz + wl.num_seqs * 4
+        + int(multi.sum()) * h * d * wl.query.element_size() + wl.num_seqs * 4
 
 
 def test_prefill_flops_counts_the_causal_pairs():

@@ -31,14 +31,17 @@ def _require_gpu():
     B.load_library()
 
 
+@pytest.mark.parametrize("partials", ["f32", "out"])
 @pytest.mark.parametrize("shape", list(SHAPES))
-def test_v2_single_partition_is_bitwise_v1(shape):
+def test_v2_single_partition_is_bitwise_v1(shape, partials):
     wl = W.make_workload(SHAPES[shape]["number"], lens=[1, 17, 300, 511, 512])
     a = H.run(wl, "v1")
-    b = H.run(wl, "v2")
+    b = H.run(wl, "v2", partials=partials)
     assert np.array_equal(a["out"], b["out"])
-    # tmp_out has the output dtype, so a single partition stores the same rounded row twice.
-    assert np.array_equal(b["tmp_out"][:, :, 0, :], b["out"])
+    # A single partition stores its row twice: once as the partial (fp32 or
+    # the output dtype), once rounded to the output dtype.
+    part = torch.from_numpy(b["tmp_out"][:, :, 0, :]).to(wl.dtype).double().numpy()
+    assert np.array_equal(part, b["out"])
 
 
 @pytest.mark.parametrize("shape", list(SHAPES))
