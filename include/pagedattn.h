@@ -331,6 +331,36 @@ pa_status paged_attention_split(
  * sizes). */
 size_t pa_split_counters_size(int num_seqs, int num_heads);
 
+/* Size of the library's device array used by paged_attention_split_static. */
+#define PA_SPLIT_STATIC_SCRATCH_BYTES (64u << 20)
+
+/* paged_attention_split for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same decode, the same kernels and the same result, with no
+ * exp_sums / max_logits / tmp_out / counters arguments.  The pieces' counters
+ * and partials live in a device array the library owns,
+ * PA_SPLIT_STATIC_SCRATCH_BYTES (64 MiB) per GPU, held from the first call on
+ * that GPU until the process ends; the call allocates and frees nothing.
+ * The array holds, each region rounded up to 256 bytes, num_seqs * num_heads
+ * int32 counters and, for Z = the split's pieces per sequence at most (1 ..
+ * 64, from the batch shape as in paged_attention_split), num_seqs * num_heads
+ * * Z exp-sums and max-logits (fp32) and partial rows of head_size elements
+ * (fp32, or 2 bytes with options->partial_dtype = PA_PARTIAL_OUT and a 16-bit
+ * query).  A call needing more returns PA_ERR_BAD_SHAPE and launches
+ * nothing.  Each call first clears its counters with a fill kernel (no
+ * memset) on `stream`.  Every call on one GPU shares that GPU's array and
+ * leaves its contents behind: calls that overlap on one GPU (different
+ * streams, or host threads, without ordering between them) race and give
+ * undefined results.  Arguments, options and errors otherwise as for
+ * paged_attention_split; out is written, nothing else the caller owns. */
+pa_status paged_attention_split_static(
+    void *out, const void *query, const void *key_cache, const void *value_cache,
+    int num_seqs, int num_heads, int num_kv_heads, int head_size, float scale,
+    const int32_t *block_tables, int max_num_blocks_per_seq, const int32_t *seq_lens,
+    int num_blocks, int block_size, int max_seq_len, const float *alibi_slopes,
+    pa_dtype dtype, pa_kv_cache_dtype kv_cache_dtype, float k_scale, float v_scale,
+    const pa_decode_options *options, void *stream);
+
 /* ---------------------------------------------------------------------- */
 /* Paged prefill                                                          */
 /* ---------------------------------------------------------------------- */

@@ -41,7 +41,7 @@ EXPORTED_SYMBOLS = (
     "paged_attention_partition", "paged_attention_reduce",
     "paged_attention_v1_ex", "paged_attention_v2_ex", "paged_attention_auto_ex",
     "paged_attention_partition_ex", "paged_attention_reduce_ex", "paged_attention_split",
-    "pa_split_counters_size", "paged_prefill", "pa_partition_size",
+    "pa_split_counters_size", "paged_attention_split_static", "paged_prefill", "pa_partition_size",
     "pa_num_partitions", "pa_should_use_v2", "pa_device_cu_count", "pa_set_timing_events",
     "pa_status_string", "pa_version", "pa_stream_read",
 )
@@ -109,6 +109,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         ex.restype = _I
     lib.paged_attention_split.argtypes = _PARTITION_ARGS[:4] + [_P] + _PARTITION_ARGS[4:-1] + [_P, _P]
     lib.paged_attention_split.restype = _I
+    lib.paged_attention_split_static.argtypes = lib.paged_attention_v1.argtypes[:-1] + [_P, _P]
+    lib.paged_attention_split_static.restype = _I
     lib.paged_prefill.argtypes = [_P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P, _I, _P, _P, _I, _I,
                                   _I, _I, _I, _P, _P]
     lib.paged_prefill.restype = _I
@@ -338,6 +340,38 @@ def paged_attention_split(out, exp_sums, max_logits, tmp_out, counters, query, k
                        max_seq_len, alibi_slopes, kv_cache_dtype, k_scale, v_scale, stream,
                        opts=opts)
     _check(lib.paged_attention_split(*args), "paged_attention_split")
+
+
+#: Bytes of the library's own scratch array (paged_attention_split_static).
+SPLIT_STATIC_SCRATCH_BYTES = 64 << 20
+
+
+def paged_attention_split_static(out, query, key_cache, value_cache, num_kv_heads, scale,
+                                 block_tables, seq_lens, block_size, max_seq_len,
+                                 alibi_slopes=None, kv_cache_dtype="auto", k_scale=1.0,
+                                 v_scale=1.0, stream=None, window_left=-1, logits_soft_cap=0.0,
+                                 kv_layout="decode", partials="f32") -> None:
+    """Balanced split decode with no scratch arguments: the counters and the
+    pieces' partials live in the library's own device array (for callers
+    that cannot allocate).  Writes ``out``; ``partials`` ('f32' or 'out')
+    picks the partial dtype.  Calls that overlap on one GPU race."""
+    lib = load_library()
+    b, h, d, nb, hkv, bs, mbps = _geometry(query, key_cache, value_cache, block_tables, seq_lens,
+                                           kv_cache_dtype, kv_layout)
+    if hkv != num_kv_heads or bs != block_size:
+        raise ValueError("num_kv_heads / block_size disagree with the cache shape")
+    if out.shape != query.shape or out.dtype != query.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor like query")
+    if partials not in ("f32", "out"):
+        raise ValueError("partials must be 'f32' or 'out'")
+    opts = _options(window_left, logits_soft_cap, kv_layout,
+                    PARTIAL_F32 if partials == "f32" else PARTIAL_OUT)
+    args = [out.data_ptr(), query.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(), b, h,
+            num_kv_heads, d, float(scale), block_tables.data_ptr(), mbps, seq_lens.data_ptr(), nb,
+            block_size, int(max_seq_len), _ptr(alibi_slopes), DTYPE_CODE[query.dtype],
+            _kv_code(kv_cache_dtype), float(k_scale), float(v_scale),
+            None if opts is None else ctypes.addressof(opts), _stream(stream)]
+    _check(lib.paged_attention_split_static(*args), "paged_attention_split_static")
 
 
 class PreparedCall:

@@ -124,6 +124,7 @@ struct Call {
   int partial_dtype;      // pa_partial_dtype of tmp_out
   int32_t *counters;      // paged_attention_split only (mode is then V2 for validation)
   bool split;
+  bool static_scratch;    // the partial buffers and counters are the library's own array
   hipStream_t stream;
 };
 
@@ -207,14 +208,14 @@ pa_status validate_common(const Call &c, bool partition_phase) {
   if (c.num_seqs > kMaxGridYZ) return PA_ERR_BAD_SHAPE;
   if (!c.out || !c.seq_lens) return PA_ERR_NULL_POINTER;
   if (!aligned16(c.out)) return PA_ERR_MISALIGNED;
-  const bool partials = c.mode != PA_MODE_V1;
+  const bool partials = c.mode != PA_MODE_V1 && !c.static_scratch;
   if (partials) {
     if (!c.exp_sums || !c.max_logits || !c.tmp_out) return PA_ERR_NULL_POINTER;
     if (!aligned16(c.tmp_out)) return PA_ERR_MISALIGNED;
     if (c.max_num_partitions < 1 || c.max_num_partitions < pa_num_partitions(c.max_seq_len))
       return PA_ERR_BAD_SHAPE;
   }
-  if (c.split) {
+  if (c.split && !c.static_scratch) {
     if (!c.counters) return PA_ERR_NULL_POINTER;
     if (((uintptr_t)c.counters & 3u) != 0) return PA_ERR_MISALIGNED;
   }
@@ -438,6 +439,7 @@ Call make_call(pa_mode mode, void *out, float *exp_sums, float *max_logits, void
   c.partial_dtype = PA_PARTIAL_F32;
   c.counters = nullptr;
   c.split = false;
+  c.static_scratch = false;
   c.stream = reinterpret_cast<hipStream_t>(stream);
   return c;
 }
@@ -650,6 +652,58 @@ pa_status paged_attention_split(void *out, float *exp_sums, float *max_logits, v
   c.counters = counters;
   const pa_status st = apply_options(options, c);
   if (st != PA_OK) return st;
+  return run_partition(c);
+}
+
+pa_status paged_attention_split_static(void *out, const void *query, const void *key_cache,
+                                       const void *value_cache, int num_seqs, int num_heads,
+                                       int num_kv_heads, int head_size, float scale,
+                                       const int32_t *block_tables, int max_num_blocks_per_seq,
+                                       const int32_t *seq_lens, int num_blocks, int block_size,
+                                       int max_seq_len, const float *alibi_slopes,
+                                       pa_dtype dtype, pa_kv_cache_dtype kv_cache_dtype,
+                                       float k_scale, float v_scale,
+                                       const pa_decode_options *options, void *stream) {
+  Call c = make_call(PA_MODE_V2, out, nullptr, nullptr, nullptr, query, key_cache, value_cache,
+                     num_seqs, num_heads, num_kv_heads, head_size, scale, block_tables,
+                     max_num_blocks_per_seq, seq_lens, num_blocks, block_size, max_seq_len,
+                     pa_num_partitions(max_seq_len), alibi_slopes, dtype, kv_cache_dtype, k_scale,
+                     v_scale, stream);
+  c.split = true;
+  c.static_scratch = true;
+  pa_status st = apply_options(options, c);
+  if (st != PA_OK) return st;
+  st = validate_common(c, true);
+  if (st != PA_OK) return st;
+  if (c.num_seqs == 0) return PA_OK;
+  // The pieces' scratch, laid out in the library's array: counters
+  // [B, H] int32, then exp_sums and max_logits [B, H, Z] and tmp_out
+  // [B, H, Z, D], Z = the split grid's depth (a piece's slot is its index,
+  // below Z), each region 256-byte aligned.
+  const Plan pl = make_plan(c);
+  const long long grid_x = (long long)c.num_kv_heads * pl.head_groups;
+  int cu = 0;
+  st = cu_count_current(&cu);
+  if (st != PA_OK) return st;
+  const int gz = split_grid_z(c, grid_x, cu);
+  const size_t tsz = (c.dtype == PA_DTYPE_F32 || c.partial_dtype == PA_PARTIAL_F32) ? 4 : 2;
+  const size_t rows = (size_t)c.num_seqs * (size_t)c.num_heads;
+  auto up = [](size_t n) { return (n + 255) / 256 * 256; };
+  const size_t off_es = up(rows * 4);
+  const size_t off_ml = off_es + up(rows * gz * 4);
+  const size_t off_to = off_ml + up(rows * gz * 4);
+  const size_t need = off_to + up(rows * gz * (size_t)c.head_size * tsz);
+  if (need > (size_t)PA_SPLIT_STATIC_SCRATCH_BYTES) return PA_ERR_BAD_SHAPE;
+  char *base = nullptr;
+  st = pa::static_scratch(reinterpret_cast<void **>(&base));
+  if (st != PA_OK) return st;
+  c.counters = reinterpret_cast<int32_t *>(base);
+  c.exp_sums = reinterpret_cast<float *>(base + off_es);
+  c.max_logits = reinterpret_cast<float *>(base + off_ml);
+  c.tmp_out = base + off_to;
+  c.max_num_partitions = gz;
+  // Counters start at zero on every call (a fill kernel, no memset node).
+  if (pa::launch_fill_zero(c.counters, rows, c.stream) != hipSuccess) return PA_ERR_HIP;
   return run_partition(c);
 }
 

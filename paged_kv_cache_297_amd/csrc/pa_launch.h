@@ -6,6 +6,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include "../../include/pagedattn.h"
 #include "pa_params.h"
 
 namespace pa {
@@ -57,6 +58,13 @@ hipError_t launch_reduce(const Params &p, int dtype, int head_size, const Launch
 // Streaming read of bytes (a multiple of 16) at buf, one share per workgroup.
 hipError_t launch_stream_read(const void *buf, size_t bytes, unsigned *sink, int workgroups,
                               hipStream_t stream);
+
+// The library's own device array for paged_attention_split_static
+// (PA_SPLIT_STATIC_SCRATCH_BYTES, 256-byte aligned), on the current device:
+// its address, looked up once per device.
+pa_status static_scratch(void **ptr);
+// Zeroes n int32 words at p with a fill kernel on stream.
+hipError_t launch_fill_zero(int *p, size_t n, hipStream_t stream);
 
 // [num_blocks, Hkv, block_size, head_size] caches, 16-bit (q_dtype kDtF16 or
 // kDtBF16); gp = 1, 2 or 4 query heads per workgroup (nhd_max_group).

@@ -87,4 +87,14 @@ hipError_t launch_partition_mfma_rows(const Params &, int q, int, int, const Lau
 hipError_t launch_prefill(const PrefillParams &p, int dtype, int, int, bool, const Launch &l) {
   return record("prefill", l, dtype, p.tiles_per_wave);
 }
+// The library's device array: a fake, 256-byte aligned device address that
+// no stand-in dereferences.
+pa_status static_scratch(void **ptr) {
+  *ptr = reinterpret_cast<void *>(static_cast<uintptr_t>(0x40000000));
+  return PA_OK;
+}
+hipError_t launch_fill_zero(int *, size_t n, hipStream_t) {
+  const Launch l{dim3((unsigned)n, 1, 1), nullptr, nullptr, nullptr};
+  return record("fill_zero", l, 0, 0);
+}
 }  // namespace pa

@@ -85,3 +85,20 @@ def test_split_grid_depth(lib):
     # -> 12800 keys, ceil(100031 / 12800) = 8 slices.
     assert call(lib, "paged_attention_split", 4, 32, 8, 128, 16, 100000, F16) == \
         ("valu_f16", (8, 4, 8), (128, 4))
+
+
+def test_split_static_lays_out_its_array(lib):
+    """The allocation-free split: the same launch as split (grid depth from the
+    batch shape), after clearing its counters; a batch whose scratch exceeds
+    the 64 MiB array is refused before anything is launched."""
+    a = [A, A, A, A, 4, 32, 8, 128, 0.1, A, 6250, A, 1 << 20, 16, 100000, None, F16, 0, 1.0,
+         1.0, None, None]
+    assert lib.paged_attention_split_static(*a) == B.PA_OK
+    assert last(lib) == ("valu_f16", (8, 4, 8), (128, 4))
+    # 65535 sequences x 64 heads x Z pieces of fp32 partial rows: far beyond.
+    big = [A, A, A, A, 65535, 64, 64, 128, 0.1, A, 2048, A, 1 << 20, 16, 32768, None, F16, 0,
+           1.0, 1.0, None, None]
+    lib.paged_attention_v1(*(a[:20] + [None]))          # some other launch first
+    before = last(lib)
+    assert lib.paged_attention_split_static(*big) == 2   # PA_ERR_BAD_SHAPE
+    assert last(lib) == before

@@ -375,6 +375,31 @@ def test_split_counters_checks():
     assert lib.paged_attention_split(*split_args(options=opts(100, 30.0), num_seqs=0)) == OK
 
 
+def static_args(options=None, **kw):
+    a = v2_args(**kw)
+    # paged_attention_v1's arguments, then the options, then the stream.
+    return a[0:1] + a[4:18] + a[19:-1] + [options, a[-1]]
+
+
+@pytest.mark.parametrize("kw,status", [c for c in CASES
+                                       if not any(k in c[0] for k in
+                                                  ("exp_sums", "max_logits", "tmp_out",
+                                                   "max_parts"))])
+def test_split_static_validation_follows_split(kw, status):
+    lib = B.load_library()
+    assert lib.paged_attention_split_static(*static_args(**kw)) == status
+
+
+def test_split_static_options_and_limits():
+    lib = B.load_library()
+    st = lib.paged_attention_split_static
+    assert st(*static_args(options=opts(-5, 0.0))) == BADARG
+    assert st(*static_args(options=partial_opts(4))) == BADARG
+    assert st(*static_args(options=opts(100, 30.0), num_seqs=0)) == OK
+    # No partial buffers to pass: NULL-free signature, empty batch is a no-op.
+    assert st(*static_args(num_seqs=0)) == OK
+
+
 def test_split_counters_size():
     lib = B.load_library()
     assert lib.pa_split_counters_size(3, 4) == 48
