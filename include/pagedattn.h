@@ -327,6 +327,40 @@ pa_status paged_attention_split(
     const float *alibi_slopes, pa_dtype dtype, pa_kv_cache_dtype kv_cache_dtype,
     float k_scale, float v_scale, const pa_decode_options *options, void *stream);
 
+/* ---------------------------------------------------------------------- */
+/* Work list (persistent, cost-balanced scheduling for ragged batches)     */
+/* ---------------------------------------------------------------------- */
+
+/* The decode of paged_attention_v2_ex scheduled from a work list built on
+ * the device, in one persistent launch: as many workgroups as the GPU holds
+ * at once ("workers"), none of them without work on a batch of at least
+ * 2048 keys per worker.  The batch's items -- (sequence, KV head) -- are laid
+ * end to end by the memory-load cost model of the PoD page (FlashInfer PR
+ * #967, work estimate qo_len + 2 * page_size * kv_len: one query row and the
+ * K and V rows of every key in the window); worker w takes the w-th equal
+ * share of that line, cutting an item only on 32-key steps and at least 512
+ * keys from either end (so a cut item has at most ceil(L / 512) pieces, and
+ * at most 64).  Every worker builds its own entries of the list from
+ * seq_lens; each walks its items in order, writes out directly for an item
+ * it holds whole, and otherwise stores the piece's partials (slot = piece)
+ * and arrives at the item's counter: the last piece merges them with the V2
+ * page's Phase 2 log-sum-exp rescale.  The result equals the v1 / v2 result
+ * up to rounding (partials rounded to the options' partial dtype, fp32 by
+ * default).
+ *
+ * Buffers, counters contract and errors as for paged_attention_split
+ * (exp_sums, max_logits and tmp_out are scratch; counters int32 [num_seqs,
+ * num_heads], zero before the first call and left zero).  Decode layout only
+ * (options->kv_layout = BLOCK_ROWS: PA_ERR_UNSUPPORTED). */
+pa_status paged_attention_worklist(
+    void *out, float *exp_sums, float *max_logits, void *tmp_out, int32_t *counters,
+    const void *query, const void *key_cache, const void *value_cache,
+    int num_seqs, int num_heads, int num_kv_heads, int head_size, float scale,
+    const int32_t *block_tables, int max_num_blocks_per_seq, const int32_t *seq_lens,
+    int num_blocks, int block_size, int max_seq_len, int max_num_partitions,
+    const float *alibi_slopes, pa_dtype dtype, pa_kv_cache_dtype kv_cache_dtype,
+    float k_scale, float v_scale, const pa_decode_options *options, void *stream);
+
 /* Bytes of the counters buffer of paged_attention_split (0 for non-positive
  * sizes). */
 size_t pa_split_counters_size(int num_seqs, int num_heads);

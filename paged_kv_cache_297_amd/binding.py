@@ -41,7 +41,7 @@ EXPORTED_SYMBOLS = (
     "paged_attention_partition", "paged_attention_reduce",
     "paged_attention_v1_ex", "paged_attention_v2_ex", "paged_attention_auto_ex",
     "paged_attention_partition_ex", "paged_attention_reduce_ex", "paged_attention_split",
-    "pa_split_counters_size", "paged_attention_split_static", "paged_prefill", "pa_partition_size",
+    "pa_split_counters_size", "paged_attention_split_static", "paged_attention_worklist", "paged_prefill", "pa_partition_size",
     "pa_num_partitions", "pa_should_use_v2", "pa_device_cu_count", "pa_set_timing_events",
     "pa_status_string", "pa_version", "pa_stream_read",
 )
@@ -109,6 +109,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         ex.restype = _I
     lib.paged_attention_split.argtypes = _PARTITION_ARGS[:4] + [_P] + _PARTITION_ARGS[4:-1] + [_P, _P]
     lib.paged_attention_split.restype = _I
+    lib.paged_attention_worklist.argtypes = lib.paged_attention_split.argtypes[:]
+    lib.paged_attention_worklist.restype = _I
     lib.paged_attention_split_static.argtypes = lib.paged_attention_v1.argtypes[:-1] + [_P, _P]
     lib.paged_attention_split_static.restype = _I
     lib.paged_prefill.argtypes = [_P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P, _I, _P, _P, _I, _I,
@@ -326,6 +328,23 @@ def _split_args(out, exp_sums, max_logits, tmp_out, counters, query, *rest, opts
     return args[:4] + [counters.data_ptr()] + args[4:-1] + [ptr, args[-1]]
 
 
+def paged_attention_worklist(out, exp_sums, max_logits, tmp_out, counters, query, key_cache,
+                             value_cache, num_kv_heads, scale, block_tables, seq_lens, block_size,
+                             max_seq_len, alibi_slopes=None, kv_cache_dtype="auto", k_scale=1.0,
+                             v_scale=1.0, stream=None, window_left=-1, logits_soft_cap=0.0,
+                             kv_layout="decode") -> None:
+    """Work-list decode (one persistent launch, items balanced by memory-load
+    cost): writes ``out``; the partial buffers are scratch and ``counters``
+    (split_counters) must be zero on entry (it is left zero)."""
+    lib = load_library()
+    opts = _options(window_left, logits_soft_cap, kv_layout, _partial_code(tmp_out, query))
+    args = _split_args(out, exp_sums, max_logits, tmp_out, counters, query, key_cache,
+                       value_cache, num_kv_heads, scale, block_tables, seq_lens, block_size,
+                       max_seq_len, alibi_slopes, kv_cache_dtype, k_scale, v_scale, stream,
+                       opts=opts)
+    _check(lib.paged_attention_worklist(*args), "paged_attention_worklist")
+
+
 def paged_attention_split(out, exp_sums, max_logits, tmp_out, counters, query, key_cache,
                           value_cache, num_kv_heads, scale, block_tables, seq_lens, block_size,
                           max_seq_len, alibi_slopes=None, kv_cache_dtype="auto", k_scale=1.0,
@@ -388,19 +407,19 @@ class PreparedCall:
                  kv_layout="decode"):
         self.lib = load_library()
         self.name = f"paged_attention_{mode}"
-        if mode not in ("v2", "auto", "split"):
-            raise ValueError("mode must be 'v2', 'auto' or 'split'")
+        if mode not in ("v2", "auto", "split", "worklist"):
+            raise ValueError("mode must be 'v2', 'auto', 'split' or 'worklist'")
         self.opts = _options(window_left, logits_soft_cap, kv_layout,
                              _partial_code(tmp_out, query))
         self.counters = counters
-        if mode == "split":
+        if mode in ("split", "worklist"):
             if counters is None:
-                raise ValueError("the split mode needs a counters buffer (split_counters)")
+                raise ValueError(f"the {mode} mode needs a counters buffer (split_counters)")
             self.args = _split_args(out, exp_sums, max_logits, tmp_out, counters, query,
                                     key_cache, value_cache, num_kv_heads, scale, block_tables,
                                     seq_lens, block_size, max_seq_len, alibi_slopes,
                                     kv_cache_dtype, k_scale, v_scale, stream, opts=self.opts)
-            self.fn = self.lib.paged_attention_split
+            self.fn = getattr(self.lib, self.name)
             self._keep = (out, exp_sums, max_logits, tmp_out, counters, query, key_cache,
                           value_cache, block_tables, seq_lens, alibi_slopes)
             return

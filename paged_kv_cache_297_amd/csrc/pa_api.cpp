@@ -34,6 +34,14 @@ struct Tunables {
   int parts_reversed = 1;     // all-v2 launches dispatch the last partition first
   int split_reversed = 0;     // split launches dispatch the last piece slice first
   int split_target = 0;       // split: fixed piece target in keys (0: the size rule)
+  // List: an item's cost beyond its keys, in keys (the PoD page's qo_len
+  // term: one query row against two cache rows per key rounds to 1).
+  int list_item_cost = 1;
+  // List: workers per CU (0: as many workgroups as one CU holds at once).
+  // One per CU already streams at the device's rate (one workgroup reads up
+  // to ~48 GB/s, the device ~28 GB/s per CU); more workers only cut more
+  // items into pieces.
+  int list_per_cu = 1;
 };
 
 int env_int(const char *name, int fallback, int lo, int hi) {
@@ -57,6 +65,8 @@ const Tunables &tunables() {
     x.parts_reversed = env_int("PA_PARTS_REVERSED", x.parts_reversed, 0, 1);
     x.split_reversed = env_int("PA_SPLIT_REVERSED", x.split_reversed, 0, 1);
     x.split_target = env_int("PA_SPLIT_TARGET", x.split_target, 0, 1 << 30);
+    x.list_item_cost = env_int("PA_LIST_ITEM_COST", x.list_item_cost, 0, 511);
+    x.list_per_cu = env_int("PA_LIST_PER_CU", x.list_per_cu, 0, 16);
     return x;
   }();
   return t;
@@ -123,7 +133,8 @@ struct Call {
   int kv_layout;          // pa_kv_layout
   int partial_dtype;      // pa_partial_dtype of tmp_out
   int32_t *counters;      // paged_attention_split only (mode is then V2 for validation)
-  bool split;
+  bool split;             // a piece mode: split, or list (the work list)
+  bool list;
   bool static_scratch;    // the partial buffers and counters are the library's own array
   hipStream_t stream;
 };
@@ -225,7 +236,7 @@ pa_status validate_common(const Call &c, bool partition_phase) {
     return PA_ERR_BAD_ARGUMENT;
   if (c.kv_cache_dtype == PA_KV_FP8_E4M3 && c.dtype == PA_DTYPE_F32) return PA_ERR_UNSUPPORTED;
   if (c.kv_layout == PA_KV_LAYOUT_BLOCK_ROWS &&
-      (c.dtype == PA_DTYPE_F32 || c.kv_cache_dtype != PA_KV_AUTO))
+      (c.dtype == PA_DTYPE_F32 || c.kv_cache_dtype != PA_KV_AUTO || c.list))
     return PA_ERR_UNSUPPORTED;
   if (c.block_size != 16 && c.block_size != 32) return PA_ERR_UNSUPPORTED;
   if (pa::kPartitionSize % c.block_size != 0) return PA_ERR_UNSUPPORTED;
@@ -296,7 +307,8 @@ Params make_params(const Call &c, int cu, int head_groups) {
   p.max_seq_len = c.max_seq_len;
   p.max_num_partitions = c.max_num_partitions;
   p.head_groups = head_groups;
-  p.mode = c.split ? pa::kModeSplit : (int)c.mode;
+  p.mode = c.list ? pa::kModeList : c.split ? pa::kModeSplit : (int)c.mode;
+  p.item_cost = tunables().list_item_cost;
   p.counters = c.counters;
   p.split_target = c.split ? split_target(c, (long long)c.num_kv_heads * head_groups, cu) : 0;
   const long long b_hkv = (long long)c.num_seqs * c.num_kv_heads;
@@ -346,16 +358,21 @@ pa_status run_partition(const Call &c) {
     return PA_ERR_BAD_SHAPE;
   if (c.num_seqs == 0) return PA_OK;
   int cu = 0;
-  if (c.mode == PA_MODE_AUTO || c.split) {
+  if (c.mode == PA_MODE_AUTO || c.split) {  // also the list
     st = cu_count_current(&cu);
     if (st != PA_OK) return st;
   }
-  const int gz = c.split ? split_grid_z(c, grid_x, cu)
+  const int gz = c.list    ? 1
+                 : c.split ? split_grid_z(c, grid_x, cu)
                  : (c.mode == PA_MODE_V1 || auto_all_v1(c, cu)) ? 1
                                                                 : pa_num_partitions(c.max_seq_len);
   const Params p = make_params(c, cu, pl.head_groups);
-  const pa::Launch l{dim3((unsigned)grid_x, c.num_seqs, gz), c.stream, t_events.partition_start,
-                     t_events.partition_stop};
+  pa::Launch l{dim3((unsigned)grid_x, c.num_seqs, gz), c.stream, t_events.partition_start,
+               t_events.partition_stop};
+  if (c.list) {
+    l.list_cus = cu;
+    l.list_per_cu = tunables().list_per_cu;
+  }
   const bool fp8 = c.kv_cache_dtype == PA_KV_FP8_E4M3;
   hipError_t e;
   if (c.kv_layout == PA_KV_LAYOUT_BLOCK_ROWS) {
@@ -439,6 +456,7 @@ Call make_call(pa_mode mode, void *out, float *exp_sums, float *max_logits, void
   c.partial_dtype = PA_PARTIAL_F32;
   c.counters = nullptr;
   c.split = false;
+  c.list = false;
   c.static_scratch = false;
   c.stream = reinterpret_cast<hipStream_t>(stream);
   return c;
@@ -649,6 +667,29 @@ pa_status paged_attention_split(void *out, float *exp_sums, float *max_logits, v
                      max_seq_len, max_num_partitions, alibi_slopes, dtype, kv_cache_dtype,
                      k_scale, v_scale, stream);
   c.split = true;
+  c.counters = counters;
+  const pa_status st = apply_options(options, c);
+  if (st != PA_OK) return st;
+  return run_partition(c);
+}
+
+pa_status paged_attention_worklist(void *out, float *exp_sums, float *max_logits,
+                                   void *tmp_out, int32_t *counters, const void *query,
+                                   const void *key_cache, const void *value_cache, int num_seqs,
+                                   int num_heads, int num_kv_heads, int head_size, float scale,
+                                   const int32_t *block_tables, int max_num_blocks_per_seq,
+                                   const int32_t *seq_lens, int num_blocks, int block_size,
+                                   int max_seq_len, int max_num_partitions,
+                                   const float *alibi_slopes, pa_dtype dtype,
+                                   pa_kv_cache_dtype kv_cache_dtype, float k_scale, float v_scale,
+                                   const pa_decode_options *options, void *stream) {
+  Call c = make_call(PA_MODE_V2, out, exp_sums, max_logits, tmp_out, query, key_cache,
+                     value_cache, num_seqs, num_heads, num_kv_heads, head_size, scale,
+                     block_tables, max_num_blocks_per_seq, seq_lens, num_blocks, block_size,
+                     max_seq_len, max_num_partitions, alibi_slopes, dtype, kv_cache_dtype,
+                     k_scale, v_scale, stream);
+  c.split = true;
+  c.list = true;
   c.counters = counters;
   const pa_status st = apply_options(options, c);
   if (st != PA_OK) return st;

@@ -20,6 +20,11 @@ struct Launch {
   dim3 grid;
   hipStream_t stream;
   hipEvent_t start, stop;
+  // Persistent (list) launch: grid.x becomes list_cus x list_per_cu workers,
+  // list_per_cu = 0 meaning as many as the kernel's occupancy lets one CU
+  // hold (grid.y = grid.z = 1).
+  int list_cus = 0;
+  int list_per_cu = 0;
 };
 
 // Largest power-of-two query-head group the VALU kernel keeps in registers

@@ -4,15 +4,22 @@
 
 namespace pa {
 
-// The soft cap and the sliding window are compile-time variants.
-template <typename QT, typename KVT, int D, int BS>
-static hipError_t launch_opts(const Params &p, const Launch &l) {
+// The soft cap, the sliding window and the persistent list form are
+// compile-time variants.
+template <typename QT, typename KVT, int D, int BS, bool LIST>
+static hipError_t launch_list(const Params &p, const Launch &l) {
   const bool win = p.window_left >= 0;
   if (p.cap_on)
-    return win ? launch_kernel(pa_partition_mfma<QT, KVT, D, BS, true, true>, l, p)
-               : launch_kernel(pa_partition_mfma<QT, KVT, D, BS, true, false>, l, p);
-  return win ? launch_kernel(pa_partition_mfma<QT, KVT, D, BS, false, true>, l, p)
-             : launch_kernel(pa_partition_mfma<QT, KVT, D, BS, false, false>, l, p);
+    return win ? launch_kernel(pa_partition_mfma<QT, KVT, D, BS, true, true, false, LIST>, l, p)
+               : launch_kernel(pa_partition_mfma<QT, KVT, D, BS, true, false, false, LIST>, l, p);
+  return win ? launch_kernel(pa_partition_mfma<QT, KVT, D, BS, false, true, false, LIST>, l, p)
+             : launch_kernel(pa_partition_mfma<QT, KVT, D, BS, false, false, false, LIST>, l, p);
+}
+
+template <typename QT, typename KVT, int D, int BS>
+static hipError_t launch_opts(const Params &p, const Launch &l) {
+  return p.mode == kModeList ? launch_list<QT, KVT, D, BS, true>(p, l)
+                             : launch_list<QT, KVT, D, BS, false>(p, l);
 }
 
 template <typename QT, typename KVT>

@@ -16,8 +16,11 @@ constexpr int kThreads = 64 * kWaves;
 
 // kModeSplit: balanced split of each sequence into equal pieces sized from
 // the batch's total length, merged in the partition kernel by the piece that
-// finishes last (paged_attention_split).
-enum Mode : int { kModeV1 = 0, kModeV2 = 1, kModeAuto = 2, kModeSplit = 3 };
+// finishes last (paged_attention_split).  kModeList: persistent launch over
+// a work list balanced by memory-load cost (paged_attention_worklist); cut
+// items are merged the same way.  Both are "piece" modes: out only, the
+// partial buffers are scratch.
+enum Mode : int { kModeV1 = 0, kModeV2 = 1, kModeAuto = 2, kModeSplit = 3, kModeList = 4 };
 
 // Split mode: the piece target is at least this many keys, so every piece
 // but a sequence's only one spans at least 512 keys.
@@ -67,6 +70,7 @@ struct Params {
   int tmp_f32;          // partial outputs are stored as fp32 (else in the query dtype)
   int *counters;        // split mode: [B, H] arrival counters, zero between calls
   int split_target;     // split mode: keys per piece before equalising (multiple of 512)
+  int item_cost;        // list mode: cost of an item beyond its keys (the query row)
 };
 
 // First key position inside the sliding window of a sequence of length

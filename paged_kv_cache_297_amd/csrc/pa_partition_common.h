@@ -16,6 +16,7 @@
 
 #include "pa_device.h"
 #include "pa_merge.h"
+#include "pa_worklist.h"
 
 namespace pa {
 
@@ -29,6 +30,16 @@ struct Work {
   bool v2;                  // partials are stored (v2) or out is written directly (v1)
   bool single;              // v2 with one partition in the window: out is written too
 };
+
+// threadIdx.x for the epilogues, through an empty asm statement: in the
+// persistent list form the epilogue runs once per item, and without this the
+// compiler hoists its thread-dependent addresses out of the item loop and
+// spills them.  (No instruction is emitted; the value is the thread index.)
+__device__ __forceinline__ int epi_tid() {
+  int t = threadIdx.x;
+  asm volatile("" : "+v"(t));
+  return t;
+}
 
 template <typename QT, int D>
 __device__ __forceinline__ void store_out_row(const Params &p, int seq, int head, int d, float v) {
@@ -206,9 +217,10 @@ template <typename QT, typename TT, int D>
 __device__ __forceinline__ void split_merge(const Params &p, const Work &w) {
   __shared__ int sm_last;
   __shared__ float sm_pm[16][kSplitMaxPieces], sm_ps[16][kSplitMaxPieces];
+  const int tid = epi_tid();
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's partial stores are done
   __syncthreads();
-  if (threadIdx.x == 0) {
+  if (tid == 0) {
     int *ctr = p.counters + (size_t)w.seq * p.num_heads + w.xslot;
     sm_last = arrive_last(
         ctr, w.n_part,
@@ -222,23 +234,251 @@ __device__ __forceinline__ void split_merge(const Params &p, const Work &w) {
   }
   __syncthreads();
   if (!sm_last) return;
+  // At most kSplitMaxPieces pieces by construction (both piece modes); the
+  // bound keeps the LDS statistics in range whatever the caller's sizes.
+  const int k = min(w.n_part, kSplitMaxPieces);
   const size_t row0 = ((size_t)w.seq * p.num_heads + w.head0) * p.max_num_partitions;
-  for (int idx = threadIdx.x; idx < w.nh * w.n_part; idx += kThreads) {
-    const int h = idx / w.n_part, c = idx - h * w.n_part;
+  for (int idx = tid; idx < w.nh * k; idx += kThreads) {
+    const int h = idx / k, c = idx - h * k;
     const size_t r = row0 + (size_t)h * p.max_num_partitions + c;
     sm_pm[h][c] = bits_f(coherent_load(p.max_logits + r));
     sm_ps[h][c] = bits_f(coherent_load(p.exp_sums + r));
   }
   __syncthreads();
   const TT *to = reinterpret_cast<const TT *>(p.tmp_out);
-  for (int idx = threadIdx.x; idx < w.nh * D; idx += kThreads) {
+  for (int idx = tid; idx < w.nh * D; idx += kThreads) {
     const int h = idx / D, d = idx - h * D;
     const TT *col = to + (row0 + (size_t)h * p.max_num_partitions) * D + d;
     const float o = lse_merge(
-        sm_pm[h], sm_ps[h], w.n_part, [](float x) { return fast_exp2(x); },
+        sm_pm[h], sm_ps[h], k, [](float x) { return fast_exp2(x); },
         [&](int c) { return coherent_load_elem<TT>(col + (size_t)c * D); });
     store_out_row<QT, D>(p, w.seq, w.head0 + h, d, o);
   }
+}
+
+// ---------------------------------------------------------------------------
+// List mode (paged_attention_worklist): a persistent launch of gridDim.x
+// workgroups ("workers").  The batch's items -- (sequence, grid-x slot) --
+// lie end to end on a line by their memory-load cost (pa_worklist.h); worker
+// w takes the w-th equal share of the line, with its ends snapped so that
+// an item is cut only on 32-key steps and at least 512 keys from its ends.
+// Every worker builds its own part of the list: all four waves scan
+// seq_lens with wave-wide prefix sums (no LDS, no barrier), find the items
+// holding their two boundaries, and then walk the items in between.  A cut
+// item's pieces store partials in their slots and the last to arrive merges
+// them (split_merge); a whole item writes out directly.
+// ---------------------------------------------------------------------------
+struct ListCursor {
+  ListShares sh;     // line length T, workers with work W, the equal shares
+  int w;             // this worker
+  long long end;     // snapped end of this worker's range on the line
+  long long pos;     // line position of the current item
+  int seq, x;        // current item
+  int L, keys, base; // its length, keys on the line, first key (32-aligned window start)
+  long long cost;
+  long long start;   // offset at which this worker's piece of the current item starts
+};
+
+// Wave-uniform 64-bit value (every lane holds the same).
+__device__ __forceinline__ long long wave_uniform64(long long v) {
+  const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)(unsigned long long)v);
+  const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)((unsigned long long)v >> 32));
+  return (long long)(((unsigned long long)hi << 32) | lo);
+}
+
+__device__ __forceinline__ int uniform32(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+__device__ __forceinline__ long long wave_sum64(long long v) {
+#pragma unroll
+  for (int m = 1; m < 64; m *= 2) v += __shfl_xor(v, m);
+  return wave_uniform64(v);
+}
+
+__device__ __forceinline__ int wave_max32(int v) {
+#pragma unroll
+  for (int m = 1; m < 64; m *= 2) v = max(v, __shfl_xor(v, m));
+  return __builtin_amdgcn_readfirstlane(v);
+}
+
+// Inclusive prefix sum over the wave's lanes.
+__device__ __forceinline__ long long wave_inclusive_scan64(long long v, int lane) {
+#pragma unroll
+  for (int d = 1; d < 64; d *= 2) {
+    const long long t = __shfl_up(v, d);
+    if (lane >= d) v += t;
+  }
+  return v;
+}
+
+// The cursor and a work item hold wave-uniform values; some come out of
+// VALU arithmetic (the double quotients of the list geometry), so they are
+// moved back to scalar registers: kept in vector registers they would make
+// the block-table reads vector loads and crowd the tile registers.
+__device__ __forceinline__ void scalarize(ListCursor &c) {
+  c.sh.total = wave_uniform64(c.sh.total);
+  c.sh.q = wave_uniform64(c.sh.q);
+  c.sh.r = wave_uniform64(c.sh.r);
+  c.sh.workers = uniform32(c.sh.workers);
+  c.end = wave_uniform64(c.end);
+  c.pos = wave_uniform64(c.pos);
+  c.cost = wave_uniform64(c.cost);
+  c.start = wave_uniform64(c.start);
+  c.w = uniform32(c.w);
+  c.seq = uniform32(c.seq);
+  c.x = uniform32(c.x);
+  c.L = uniform32(c.L);
+  c.keys = uniform32(c.keys);
+  c.base = uniform32(c.base);
+}
+
+__device__ __forceinline__ void scalarize(Work &w) {
+  w.seq = uniform32(w.seq);
+  w.kvh = uniform32(w.kvh);
+  w.head0 = uniform32(w.head0);
+  w.nh = uniform32(w.nh);
+  w.xslot = uniform32(w.xslot);
+  w.L = uniform32(w.L);
+  w.n_part = uniform32(w.n_part);
+  w.part = uniform32(w.part);
+  w.blk_begin = uniform32(w.blk_begin);
+  w.blk_end = uniform32(w.blk_end);
+  w.t_ref = uniform32(w.t_ref);
+  w.t_lo = uniform32(w.t_lo);
+  w.span = uniform32(w.span);
+}
+
+// The list cost of sequence s (lane-parallel), with its keys and base.
+__device__ __forceinline__ long long list_seq_cost(const Params &p, int s, int &L, int &keys,
+                                                   int &base) {
+  L = p.seq_lens[s];
+  keys = list_keys(L, p.max_seq_len, p.window_left, &base);
+  return list_cost(keys, p.item_cost);
+}
+
+// Finds the item holding line position target (0 <= target < T): its
+// sequence, slot, line position and the target's offset in it.
+__device__ __forceinline__ void list_locate(const Params &p, int gx, long long target,
+                                            ListCursor &c, long long &offset) {
+  const int lane = threadIdx.x & 63;
+  long long run = 0;  // line position of the chunk's first sequence
+  for (int s0 = 0; s0 < p.num_seqs; s0 += 64) {
+    const int s = s0 + lane;
+    int L = 0, keys = 0, base = 0;
+    const long long cost = s < p.num_seqs ? list_seq_cost(p, s, L, keys, base) : 0;
+    const long long span = cost * gx;
+    const long long incl = wave_inclusive_scan64(span, lane);
+    const long long chunk = wave_uniform64(__shfl(incl, 63));
+    if (target < run + chunk || s0 + 64 >= p.num_seqs) {
+      const unsigned long long hit = __ballot(s < p.num_seqs && target < run + incl);
+      const int l = hit ? __builtin_ctzll(hit) : min(63, p.num_seqs - 1 - s0);
+      const long long item0 = wave_uniform64(__shfl(run + incl - span, l));  // line position of (seq, 0)
+      c.seq = s0 + l;
+      c.L = __builtin_amdgcn_readfirstlane(__shfl(L, l));
+      c.keys = __builtin_amdgcn_readfirstlane(__shfl(keys, l));
+      c.base = __builtin_amdgcn_readfirstlane(__shfl(base, l));
+      c.cost = wave_uniform64(__shfl(cost, l));
+      const long long rel = target - item0;
+      c.x = uniform32((int)list_div(rel, c.cost));
+      c.x = c.x < gx ? c.x : gx - 1;
+      c.pos = item0 + (long long)c.x * c.cost;
+      offset = wave_uniform64(target - c.pos);
+      return;
+    }
+    run += chunk;
+  }
+}
+
+// Moves the cursor to the next item on the line.
+__device__ __forceinline__ void list_advance(const Params &p, int gx, ListCursor &c) {
+  c.pos += c.cost;
+  c.start = 0;
+  if (++c.x < gx) return;
+  c.x = 0;
+  if (++c.seq >= p.num_seqs) return;
+  c.cost = list_seq_cost(p, c.seq, c.L, c.keys, c.base);
+}
+
+// Sets up worker blockIdx.x; false when it has no range (a batch too small
+// for every worker).
+__device__ __forceinline__ bool list_begin(const Params &p, ListCursor &c) {
+  const int gx = p.num_kv_heads * p.head_groups;
+  const int lane = threadIdx.x & 63;
+  long long sum = 0;
+  int kmax = 0;
+  for (int s0 = 0; s0 < p.num_seqs; s0 += 64) {
+    const int s = s0 + lane;
+    int L = 0, keys = 0, base = 0;
+    if (s < p.num_seqs) {
+      sum += list_seq_cost(p, s, L, keys, base);
+      kmax = max(kmax, keys);
+    }
+  }
+  const long long total = wave_sum64(sum) * gx;
+  c.sh = list_shares(total, uniform32(list_workers(total, (int)gridDim.x, wave_max32(kmax))));
+  c.sh.q = wave_uniform64(c.sh.q);
+  c.sh.r = wave_uniform64(c.sh.r);
+  c.w = blockIdx.x;
+  if (c.w >= c.sh.workers) return false;
+  // This worker's end: the next worker's start, snapped.
+  if (c.w + 1 >= c.sh.workers) {
+    c.end = c.sh.total;
+  } else {
+    long long off = 0;
+    list_locate(p, gx, wave_uniform64(list_boundary(c.sh, c.w + 1)), c, off);
+    c.end = wave_uniform64(c.pos + list_snap(off, c.keys, c.cost));
+  }
+  long long off = 0;
+  list_locate(p, gx, wave_uniform64(list_boundary(c.sh, c.w)), c, off);
+  c.start = list_snap(off, c.keys, c.cost);
+  if (c.start >= c.cost) list_advance(p, gx, c);
+  scalarize(c);
+  return true;
+}
+
+// The next piece of this worker's range as a Work, or false at the end.
+// Empty and invalid sequences are finished here (out = 0 / NaN) and
+// skipped.
+template <typename QT, int D>
+__device__ __forceinline__ bool list_next(const Params &p, int block_size, int group_slots,
+                                          ListCursor &c, Work &w) {
+  const int gx = p.num_kv_heads * p.head_groups;
+  while (c.pos < c.end && c.seq < p.num_seqs) {
+    w.seq = c.seq;
+    w.xslot = c.x;
+    w.kvh = c.x / p.head_groups;
+    const int hg = c.x - w.kvh * p.head_groups;
+    w.head0 = w.kvh * p.group + hg * group_slots;
+    w.nh = min(group_slots, p.group - hg * group_slots);
+    w.L = c.L;
+    const long long stop = min(c.cost, c.end - c.pos);  // end of the piece (offset)
+    const long long start = c.start;
+    const long long item_pos = c.pos;
+    const int keys = c.keys, base = c.base;
+    list_advance(p, gx, c);
+    if (keys == 0) {
+      // Empty (out = 0) or invalid length (out = NaN); the item is never cut.
+      const bool bad = w.L != 0;
+      for (int idx = epi_tid(); idx < w.nh * D; idx += kThreads)
+        store_out_row<QT, D>(p, w.seq, w.head0 + idx / D, idx % D,
+                             bad ? __builtin_nanf("") : 0.0f);
+      continue;
+    }
+    list_piece(c.sh, item_pos, keys, c.w, start, &w.n_part, &w.part);
+    if (stop <= start) continue;
+    w.t_lo = window_first_token(p.window_left, w.L);
+    w.v2 = w.n_part > 1;
+    w.single = false;
+    const int t0 = base + (int)start;
+    const int t1 = min(base + (int)min(stop, (long long)keys), w.L);
+    w.blk_begin = max(t0, w.t_lo) / block_size;
+    w.blk_end = (t1 + block_size - 1) / block_size;
+    w.t_ref = t1 - 1;
+    w.span = w.t_ref + 1 - w.t_lo;
+    scalarize(c);
+    scalarize(w);
+    return true;
+  }
+  return false;
 }
 
 // One element of a workgroup's result.  Wave wv left, for query head h of
@@ -292,8 +532,8 @@ __device__ __forceinline__ void finish_partition(const Params &p, const Work &w,
                                                  const float (*sm_o)[GS][OSTRIDE],
                                                  const float (*sm_m)[GS],
                                                  const float (*sm_l)[GS]) {
-  const bool split = p.mode == kModeSplit;
-  for (int idx = threadIdx.x; idx < w.nh * D; idx += kThreads) {
+  const bool split = p.mode >= kModeSplit;  // split or list: pieces merge in-kernel
+  for (int idx = epi_tid(); idx < w.nh * D; idx += kThreads) {
     const int h = idx / D, d = idx - h * D;
     float sum, ml;
     const float o = wave_merge<GS, OSTRIDE>(p, w, sm_o, sm_m, sm_l, h, d, sum, ml);

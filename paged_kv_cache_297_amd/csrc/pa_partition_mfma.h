@@ -112,7 +112,8 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const char *lds_ptr) {
   return __builtin_bit_cast(u32x2, v);
 }
 
-template <typename QT, typename KVT, int D, int BS, bool CAP, bool WIN, bool ROWS = false>
+template <typename QT, typename KVT, int D, int BS, bool CAP, bool WIN, bool ROWS = false,
+          bool LIST = false>
 __global__ void __launch_bounds__(kThreads)
     __attribute__((amdgpu_waves_per_eu(mfma_waves_per_eu<KVT>())))
     pa_partition_mfma(const Params p) {
@@ -381,8 +382,7 @@ __global__ void __launch_bounds__(kThreads)
   // still in flight into the back edge).  The scheduling barriers keep each
   // prefetch ahead of the step's compute.  On entry ta is loading the wave's
   // first step.
-  Tile ta, tb;
-  auto run_steps = [&](const Item &it) {
+  auto run_steps = [&](const Item &it, Tile &ta, Tile &tb) {
     int st = wv;
     int left = st < it.n_steps ? (it.n_steps - st + kWaves - 1) / kWaves : 0;
     while (left >= 3) {
@@ -409,26 +409,48 @@ __global__ void __launch_bounds__(kThreads)
   // head n hold partial sums over their tokens.
   auto finish_item = [&](const Item &it) {
     const float l_tot = xor_sum<32>(xor_sum<16>(l_run));
+    // Lane indices re-read here (see epi_tid) rather than carried in
+    // registers across the list form's item loop.
+    const int et = epi_tid(), ew = et >> 6, en = et & 15, eg = (et & 63) >> 4;
 #pragma unroll
     for (int t = 0; t < NDT; ++t)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) sm_o[wv][n][16 * t + 4 * g + e] = oacc[t][e];
-    if (g == 0) {
-      sm_m[wv][n] = m_run;
-      sm_l[wv][n] = poisoned ? __builtin_nanf("") : l_tot;
+      for (int e = 0; e < 4; ++e) sm_o[ew][en][16 * t + 4 * eg + e] = oacc[t][e];
+    if (eg == 0) {
+      sm_m[ew][en] = m_run;
+      sm_l[ew][en] = poisoned ? __builtin_nanf("") : l_tot;
     }
     lds_barrier();
     finish_partition<QT, D, 16, OSTR>(p, it.w, sm_o, sm_m, sm_l);
   };
 
-  Work w;
-  if (!begin_work<QT, D>(p, BS, 16, w)) return;
-  const Item it = make_item(w);
-  load_query(w);
-  reset_state();
-  if (wv < it.n_steps) ta = load_tile(it, wv);
-  run_steps(it);
-  finish_item(it);
+  if constexpr (LIST) {
+    // Persistent worker: the pieces of its share of the work list in order;
+    // the barrier frees the LDS of one piece's epilogue for the next.
+    ListCursor cur;
+    if (!list_begin(p, cur)) return;
+    Work w;
+    while (list_next<QT, D>(p, BS, 16, cur, w)) {
+      const Item it = make_item(w);
+      load_query(w);
+      reset_state();
+      Tile ta, tb;  // per item: nothing of one item's tiles lives into the next
+      if (wv < it.n_steps) ta = load_tile(it, wv);
+      run_steps(it, ta, tb);
+      finish_item(it);
+      __syncthreads();
+    }
+  } else {
+    Work w;
+    if (!begin_work<QT, D>(p, BS, 16, w)) return;
+    const Item it = make_item(w);
+    load_query(w);
+    reset_state();
+    Tile ta, tb;
+    if (wv < it.n_steps) ta = load_tile(it, wv);
+    run_steps(it, ta, tb);
+    finish_item(it);
+  }
 }
 
 }  // namespace pa

@@ -220,7 +220,7 @@ __device__ __forceinline__ float dim_group_sum(float v) {
 #define PA_VALU_OCCUPANCY
 #endif
 
-template <typename QT, typename KVT, int D, int BS, int GP, bool CAP, bool WIN>
+template <typename QT, typename KVT, int D, int BS, int GP, bool CAP, bool WIN, bool LIST = false>
 __global__ void __launch_bounds__(kThreads) PA_VALU_OCCUPANCY pa_partition_valu(const Params p) {
   using T = ValuTraits<QT, KVT>;
   using HM = HeadMap<GP, BS>;
@@ -240,69 +240,69 @@ __global__ void __launch_bounds__(kThreads) PA_VALU_OCCUPANCY pa_partition_valu(
   __shared__ float sm_l[kWaves][GP];
   __shared__ __attribute__((aligned(16))) PV sm_p[kWaves][2][GP][BS];
 
-  Work w;
-  if (!begin_work<QT, D>(p, BS, GP, w)) return;
+  // One work item: a partition, a whole v1 sequence, or a piece.
+  auto run_item = [&](const Work &w) {
+    const int lane = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int tok = lane % BS;
+    const int r = lane / BS;
+    const int tg = lane % VPD;
 
-  const int lane = threadIdx.x & 63;
-  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int tok = lane % BS;
-  const int r = lane / BS;
-  const int tg = lane % VPD;
+    // Query slices of the group's heads for this lane's K chunks.
+    unsigned qw[GP][NL][T::kQW];
+    {
+      const QT *qbase = reinterpret_cast<const QT *>(p.query) +
+                        ((size_t)w.seq * p.num_heads + w.head0) * D;
+#pragma unroll
+      for (int h = 0; h < GP; ++h)
+#pragma unroll
+        for (int i = 0; i < NL; ++i) {
+          if (h < w.nh) {
+            T::load_q(qbase + h * D + (i * R + r) * X, qw[h][i]);
+          } else {
+#pragma unroll
+            for (int e = 0; e < T::kQW; ++e) qw[h][i][e] = 0u;
+          }
+        }
+    }
+    // ALiBi slope (log2 units) of each head slot this lane owns after the reduce.
+    float slope2[NF];
+#pragma unroll
+    for (int j = 0; j < NF; ++j) {
+      int hb = 0;
+#pragma unroll
+      for (int rr = 0; rr < R; ++rr)
+        if (rr == r) hb = HM::head_base(rr);
+      const int h = hb + j;
+      slope2[j] = (p.alibi_slopes && h < w.nh) ? p.alibi_slopes[w.head0 + h] * kLog2e : 0.0f;
+    }
+    int my_head_base = 0;
+#pragma unroll
+    for (int rr = 0; rr < R; ++rr)
+      if (rr == r) my_head_base = HM::head_base(rr);
 
-  // Query slices of the group's heads for this lane's K chunks.
-  unsigned qw[GP][NL][T::kQW];
-  {
-    const QT *qbase = reinterpret_cast<const QT *>(p.query) +
-                      ((size_t)w.seq * p.num_heads + w.head0) * D;
+    float m_run[NF], l_run[NF];
+#pragma unroll
+    for (int j = 0; j < NF; ++j) {
+      m_run[j] = -__builtin_inff();
+      l_run[j] = 0.0f;
+    }
+    float acc[GP][NL];
 #pragma unroll
     for (int h = 0; h < GP; ++h)
 #pragma unroll
-      for (int i = 0; i < NL; ++i) {
-        if (h < w.nh) {
-          T::load_q(qbase + h * D + (i * R + r) * X, qw[h][i]);
-        } else {
-#pragma unroll
-          for (int e = 0; e < T::kQW; ++e) qw[h][i][e] = 0u;
-        }
-      }
-  }
-  // ALiBi slope (log2 units) of each head slot this lane owns after the reduce.
-  float slope2[NF];
-#pragma unroll
-  for (int j = 0; j < NF; ++j) {
-    int hb = 0;
-#pragma unroll
-    for (int rr = 0; rr < R; ++rr)
-      if (rr == r) hb = HM::head_base(rr);
-    const int h = hb + j;
-    slope2[j] = (p.alibi_slopes && h < w.nh) ? p.alibi_slopes[w.head0 + h] * kLog2e : 0.0f;
-  }
-  int my_head_base = 0;
-#pragma unroll
-  for (int rr = 0; rr < R; ++rr)
-    if (rr == r) my_head_base = HM::head_base(rr);
+      for (int i = 0; i < NL; ++i) acc[h][i] = 0.0f;
 
-  float m_run[NF], l_run[NF];
-#pragma unroll
-  for (int j = 0; j < NF; ++j) {
-    m_run[j] = -__builtin_inff();
-    l_run[j] = 0.0f;
-  }
-  float acc[GP][NL];
-#pragma unroll
-  for (int h = 0; h < GP; ++h)
-#pragma unroll
-    for (int i = 0; i < NL; ++i) acc[h][i] = 0.0f;
+    const char *kcache = reinterpret_cast<const char *>(p.key_cache);
+    const char *vcache = reinterpret_cast<const char *>(p.value_cache);
+    const const_i32_ptr btab =
+        as_const_table(p.block_tables + (size_t)w.seq * p.max_num_blocks_per_seq);
+    const size_t head_off = (size_t)w.kvh * TILE;
+    const size_t blk_stride = (size_t)p.num_kv_heads * TILE;
+    bool poisoned = false;
 
-  const char *kcache = reinterpret_cast<const char *>(p.key_cache);
-  const char *vcache = reinterpret_cast<const char *>(p.value_cache);
-  const const_i32_ptr btab = as_const_table(p.block_tables + (size_t)w.seq * p.max_num_blocks_per_seq);
-  const size_t head_off = (size_t)w.kvh * TILE;
-  const size_t blk_stride = (size_t)p.num_kv_heads * TILE;
-  bool poisoned = false;
-
-  struct Tile {
-    u32x4 k[NL], v[NL];
+    struct Tile {
+      u32x4 k[NL], v[NL];
   };
   // Out-of-range block-table entries are redirected to block 0 (always
   // addressable) and reported through the poison flag.
@@ -424,6 +424,23 @@ __global__ void __launch_bounds__(kThreads) PA_VALU_OCCUPANCY pa_partition_valu(
   }
   __syncthreads();
   finish_partition<QT, D, GP, D>(p, w, sm_o, sm_m, sm_l);
+  };
+
+  if constexpr (LIST) {
+    // Persistent worker: the pieces of its share of the work list in order;
+    // the barrier frees the LDS of one piece's epilogue for the next.
+    ListCursor cur;
+    if (!list_begin(p, cur)) return;
+    Work w;
+    while (list_next<QT, D>(p, BS, GP, cur, w)) {
+      run_item(w);
+      __syncthreads();
+    }
+  } else {
+    Work w;
+    if (!begin_work<QT, D>(p, BS, GP, w)) return;
+    run_item(w);
+  }
 }
 
 }  // namespace pa

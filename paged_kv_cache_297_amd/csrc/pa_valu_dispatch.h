@@ -13,15 +13,23 @@ constexpr int kv_bytes_of() {
   else return (int)sizeof(KVT);
 }
 
+template <typename QT, typename KVT, int D, int BS, int GP, bool LIST>
+hipError_t launch_valu_list(const Params &p, const Launch &l) {
+  const bool win = p.window_left >= 0;
+  if (p.cap_on)
+    return win ? launch_kernel(pa_partition_valu<QT, KVT, D, BS, GP, true, true, LIST>, l, p)
+               : launch_kernel(pa_partition_valu<QT, KVT, D, BS, GP, true, false, LIST>, l, p);
+  return win ? launch_kernel(pa_partition_valu<QT, KVT, D, BS, GP, false, true, LIST>, l, p)
+             : launch_kernel(pa_partition_valu<QT, KVT, D, BS, GP, false, false, LIST>, l, p);
+}
+
+// The soft cap, the sliding window and the persistent list form are
+// compile-time variants.
 template <typename QT, typename KVT, int D, int BS, int GP>
 hipError_t launch_valu_one(const Params &p, const Launch &l) {
   if constexpr (GP <= valu_max_group(kv_bytes_of<QT, KVT>(), D, BS)) {
-    const bool win = p.window_left >= 0;
-    if (p.cap_on)
-      return win ? launch_kernel(pa_partition_valu<QT, KVT, D, BS, GP, true, true>, l, p)
-                 : launch_kernel(pa_partition_valu<QT, KVT, D, BS, GP, true, false>, l, p);
-    return win ? launch_kernel(pa_partition_valu<QT, KVT, D, BS, GP, false, true>, l, p)
-               : launch_kernel(pa_partition_valu<QT, KVT, D, BS, GP, false, false>, l, p);
+    return p.mode == kModeList ? launch_valu_list<QT, KVT, D, BS, GP, true>(p, l)
+                               : launch_valu_list<QT, KVT, D, BS, GP, false>(p, l);
   } else {
     return hipErrorInvalidValue;
   }

@@ -25,9 +25,9 @@ def say(msg: str) -> None:
 def run(wl: W.Workload, path: str, poison_outputs: bool = True, window_left: int = -1,
         soft_cap: float = 0.0, block_tables=None, caches=None, kv_layout: str = "decode",
         partials: str = "f32"):
-    """Runs ``path`` ('v1', 'v2', 'auto', 'split') and returns host float64
-    copies of out, exp_sums, max_logits, tmp_out (the last three None for v1
-    and split).  ``window_left`` / ``soft_cap``: the decode options (-1 / 0:
+    """Runs ``path`` ('v1', 'v2', 'auto', 'split', 'worklist') and returns
+    host float64 copies of out, exp_sums, max_logits, tmp_out (the last three
+    None for v1, split and worklist).  ``window_left`` / ``soft_cap``: the decode options (-1 / 0:
     off); ``block_tables`` replaces the workload's table; ``caches`` = (K, V)
     replaces its caches, which are then in ``kv_layout``; ``partials``: the
     dtype of tmp_out ('f32' or 'out', the query dtype)."""
@@ -44,11 +44,12 @@ def run(wl: W.Workload, path: str, poison_outputs: bool = True, window_left: int
               logits_soft_cap=soft_cap, kv_layout=kv_layout)
     if path == "v1":
         B.paged_attention_v1(out, *args, **kw)
-    elif path == "split":
+    elif path in ("split", "worklist"):
         counters = B.split_counters(wl.num_seqs, wl.num_heads, device=out.device)
-        B.paged_attention_split(out, es, ml, to, counters, *args, **kw)
+        fn = B.paged_attention_split if path == "split" else B.paged_attention_worklist
+        fn(out, es, ml, to, counters, *args, **kw)
         torch.cuda.synchronize()
-        assert int(counters.abs().sum().item()) == 0, "split counters not left at zero"
+        assert int(counters.abs().sum().item()) == 0, f"{path} counters not left at zero"
     elif path == "v2":
         B.paged_attention_v2(out, es, ml, to, *args, **kw)
     elif path == "auto":
@@ -57,7 +58,7 @@ def run(wl: W.Workload, path: str, poison_outputs: bool = True, window_left: int
         raise ValueError(path)
     torch.cuda.synchronize()
     res = {"out": out.float().cpu().numpy().astype(np.float64)}
-    if path not in ("v1", "split"):
+    if path not in ("v1", "split", "worklist"):
         res["exp_sums"] = es.cpu().numpy().astype(np.float64)
         res["max_logits"] = ml.cpu().numpy().astype(np.float64)
         res["tmp_out"] = to.float().cpu().numpy().astype(np.float64)
@@ -148,8 +149,8 @@ def check_against_oracle(wl: W.Workload, res: dict, ref: dict, seqs, path: str,
         for s, e in zip(seqs, extra):
             check_close(res["out"][s], ref["out_v1"][s], tol, f"{wl.name}/{path} out seq {s}",
                         extra_atol=e)
-    if path in ("v1", "split"):
-        return   # no partials (split: they are scratch)
+    if path in ("v1", "split", "worklist"):
+        return   # no partials (split, worklist: they are scratch)
     # Partials of sequences on the v2 path.
     v2 = [s for s in seqs if path == "v2" or uses_v2(wl, s, window_left)]
     if not v2:

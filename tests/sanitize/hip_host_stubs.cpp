@@ -19,12 +19,20 @@ struct LastLaunch {
 };
 thread_local LastLaunch g_last = {{0}, {0, 0, 0}, 0, 0};
 
+// A persistent (list) launch reports its grid as (CUs x workers per CU, 0,
+// 0) (0 workers per CU: the kernel's occupancy, not known here).
+dim3 reported_grid(const pa::Launch &l) {
+  if (l.list_cus > 0) return dim3((unsigned)(l.list_cus * l.list_per_cu), 0, 0);
+  return l.grid;
+}
+
 hipError_t record(const char *kind, const pa::Launch &l, int a0, int a1) {
   strncpy(g_last.kind, kind, sizeof g_last.kind - 1);
   g_last.kind[sizeof g_last.kind - 1] = '\0';
-  g_last.grid[0] = l.grid.x;
-  g_last.grid[1] = l.grid.y;
-  g_last.grid[2] = l.grid.z;
+  const dim3 g = reported_grid(l);
+  g_last.grid[0] = g.x;
+  g_last.grid[1] = g.y;
+  g_last.grid[2] = g.z;
   g_last.arg0 = a0;
   g_last.arg1 = a1;
   return hipSuccess;

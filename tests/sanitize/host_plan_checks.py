@@ -42,7 +42,7 @@ def call(lib, fn, B_, H, Hkv, D, bs, L, dtype, kv=0, mode=None, counters=None):
          dtype, kv, 1.0, 1.0, None]
     if fn == "paged_attention_partition":
         a = [mode] + a
-    elif fn == "paged_attention_split":
+    elif fn in ("paged_attention_split", "paged_attention_worklist"):
         a = a[:4] + [counters or A] + a[4:-1] + [None, None]
     assert getattr(lib, fn)(*a) == B.PA_OK
     return last(lib)
@@ -102,3 +102,12 @@ def test_split_static_lays_out_its_array(lib):
     before = last(lib)
     assert lib.paged_attention_split_static(*big) == 2   # PA_ERR_BAD_SHAPE
     assert last(lib) == before
+
+
+def test_worklist_is_one_persistent_launch(lib):
+    """The work list: one launch sized from the device (256 CUs x one worker
+    per CU), the kernel family of the other paths."""
+    assert call(lib, "paged_attention_worklist", 256, 32, 32, 128, 16, 32768, BF16) == \
+        ("valu_bf16", (256, 0, 0), (128, 1))
+    assert call(lib, "paged_attention_worklist", 64, 28, 4, 128, 16, 8192, BF16) == \
+        ("mfma", (256, 0, 0), (BF16, 16))

@@ -366,6 +366,26 @@ def test_split_validation_follows_v2(kw, status):
     assert lib.paged_attention_split(*split_args(**kw)) == status
 
 
+@pytest.mark.parametrize("kw,status", CASES)
+def test_worklist_validation_follows_v2(kw, status):
+    lib = B.load_library()
+    assert lib.paged_attention_worklist(*split_args(**kw)) == status
+
+
+def test_worklist_counters_options_and_layout():
+    lib = B.load_library()
+    wl = lib.paged_attention_worklist
+    assert wl(*split_args(counters=None)) == NULLP
+    assert wl(*split_args(counters=A + 2)) == MISAL
+    assert wl(*split_args(counters=A + 4, num_seqs=0)) == OK
+    assert wl(*split_args(options=opts(-5, 0.0))) == BADARG
+    assert wl(*split_args(options=partial_opts(9))) == BADARG
+    assert wl(*split_args(options=opts(100, 30.0), num_seqs=0)) == OK
+    # Decode layout only.
+    rows = B.LAYOUT_CODE["block_rows"]
+    assert wl(*split_args(options=layout_opts(rows), dtype=BF16)) == UNSUP
+
+
 def test_split_counters_checks():
     lib = B.load_library()
     assert lib.paged_attention_split(*split_args(counters=None)) == NULLP

@@ -1,0 +1,141 @@
+"""GPU parity of the work-list path (paged_attention_worklist: one persistent
+launch over a device-built list balanced by memory-load cost): every kernel
+family and the full-size decode workloads against the fp64 oracle, with and
+without the decode options; the counters are left at zero, repeated calls
+are bitwise stable, and the edge cases (empty / invalid lengths, out-of-range
+block ids, NaN in unread bytes) behave as for v1 / v2.  It agrees with the
+split path up to rounding of the partials."""
+
+import numpy as np
+import pytest
+import torch
+
+from paged_kv_cache_297_amd import binding as B
+from paged_kv_cache_297_amd import workloads as W
+from tests import gpu_helpers as H
+from tests.test_gpu_window import FAMILIES, _family_id
+
+pytestmark = pytest.mark.gpu
+
+#: Ragged lengths with several sequences long enough to be cut.
+LENS = [0, 1, 17, 511, 513, 1100, 1600, 2100, 3000, 5000, 9000, 700, 20000, 4097]
+
+OPTIONS = [(-1, 0.0), (600, 0.0), (-1, 30.0), (100, 5.0), (2500, 0.0)]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _require_gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    B.load_library()
+
+
+def _check(wl, window_left=-1, soft_cap=0.0, seqs=None, partials="f32"):
+    ref = H.oracle(wl, seqs, window_left=window_left, soft_cap=soft_cap)
+    seqs = list(range(wl.num_seqs)) if seqs is None else seqs
+    H.say(f"  {wl.name} worklist W={window_left} cap={soft_cap} seqs={len(seqs)} {partials}")
+    res = H.run(wl, "worklist", window_left=window_left, soft_cap=soft_cap, partials=partials)
+    H.check_against_oracle(wl, res, ref, seqs, "worklist", window_left=window_left,
+                           soft_cap=soft_cap)
+    return res
+
+
+@pytest.mark.parametrize("fam", FAMILIES, ids=_family_id)
+def test_worklist_matrix(fam):
+    kv, dt, group, d, bs = fam
+    i = FAMILIES.index(fam)
+    wl = W.make_workload(2, lens=LENS, H=2 * group, Hkv=2, D=d, bs=bs, dtype=dt, kv=kv,
+                         alibi=(i % 2 == 1), seed=9000 + i)
+    for w_left, cap in OPTIONS:
+        _check(wl, w_left, cap)
+
+
+def test_worklist_tiny_fp32():
+    _check(W.make_workload(1))
+
+
+def test_worklist_gqa_bf16_full():
+    wl = W.make_workload(2)
+    _check(wl)
+    _check(wl, 1023, 50.0, partials="out")
+
+
+def test_worklist_long_fp16():
+    wl = W.make_workload(3)
+    _check(wl, seqs=[0, 3])
+    _check(wl, 4095, 0.0, seqs=[1])
+
+
+def test_worklist_ragged_alibi():
+    wl = W.make_workload(4)
+    order = np.argsort(wl.lens)
+    seqs = sorted(set(order[-3:].tolist() + order[:2].tolist() + [7, 100]))
+    _check(wl, seqs=seqs)
+
+
+def test_worklist_fp8_kv():
+    wl = W.make_workload(5)
+    _check(wl, seqs=[0, 31])
+    _check(wl, 4095, 30.0, seqs=[5])
+
+
+def test_worklist_repeated_calls_are_bitwise():
+    """One counters buffer over several calls: identical outputs, counters zero."""
+    wl = W.make_workload(4, lens=LENS + [12000, 4000], seed=9100)
+    counters = B.split_counters(wl.num_seqs, wl.num_heads)
+    outs = []
+    for _ in range(3):
+        out, es, ml, to = wl.alloc_outputs()
+        out.fill_(float("nan"))
+        B.paged_attention_worklist(out, es, ml, to, counters, wl.query, wl.key_cache,
+                                   wl.value_cache, wl.num_kv_heads, wl.scale, wl.block_tables,
+                                   wl.seq_lens, wl.block_size, wl.max_seq_len,
+                                   alibi_slopes=wl.alibi_slopes)
+        torch.cuda.synchronize()
+        assert int(counters.abs().sum().item()) == 0
+        outs.append(out.float().cpu().numpy())
+    assert np.isfinite(outs[0][1:]).all()
+    for o in outs[1:]:
+        assert np.array_equal(o, outs[0], equal_nan=True)
+
+
+def test_worklist_empty_and_invalid_lengths():
+    wl = W.make_workload(2, lens=[0, 2700, 33, 5000, 0])
+    wl.seq_lens[2] = wl.max_seq_len + 5
+    res = H.run(wl, "worklist")
+    assert np.all(res["out"][0] == 0.0) and np.all(res["out"][4] == 0.0)
+    assert np.isnan(res["out"][2]).all()
+    wl.seq_lens[2] = 33
+    ref = H.oracle(wl, [1, 3])
+    for s in (1, 3):
+        H.check_close(res["out"][s], ref["out_v1"][s], H.TOL[wl.kv_kind], f"valid seq {s}")
+
+
+@pytest.mark.parametrize("number", [2, 4, 5])
+def test_worklist_out_of_range_block_id(number):
+    """A stale entry in one sequence's table: NaN for that sequence only."""
+    wl = W.make_workload(number, lens=[6000, 600, 5000])
+    nb = wl.key_cache.shape[0]
+    wl.block_tables[0, 150] = nb + 1000
+    res = H.run(wl, "worklist")
+    assert np.isnan(res["out"][0]).all()
+    assert np.isfinite(res["out"][1:]).all()
+
+
+@pytest.mark.parametrize("number", [1, 2, 5])
+def test_worklist_nan_poison_is_never_read(number):
+    lens = [37, 700, 3025, 16, 4100]
+    clean = H.run(W.make_workload(number, lens=lens), "worklist")
+    dirty = H.run(W.make_workload(number, lens=lens, poison=True), "worklist")
+    assert np.isfinite(dirty["out"]).all()
+    assert np.array_equal(clean["out"], dirty["out"])
+
+
+def test_worklist_matches_split_up_to_rounding():
+    """Same result as the split path (pieces differ, so only up to the
+    rounding of partials and merge order)."""
+    wl = W.make_workload(4, lens=[30000, 100, 7000, 2600, 15000, 512], seed=9200)
+    a = H.run(wl, "worklist")["out"]
+    b = H.run(wl, "split")["out"]
+    assert np.allclose(a, b, rtol=2e-2, atol=2e-2)
+    rel = np.linalg.norm(a - b) / np.linalg.norm(b)
+    assert rel < 5e-3, rel
