@@ -9,8 +9,10 @@ block size 16, lognormal lengths of median 2048 clipped to [16, 32768], about
 14 GB of KV; the auto path mixes v1 and v2 there, so both kernels are timed).
 The two other long-context workloads (4 x 100000 fp16 tokens; fp8 KV, 32 x
 32768) are timed in the same process and reported inside the line
-(``also_timed``; ``--also none`` skips them).  tmp_out is float32 by default
-(``--partials out``: the query dtype).
+(``also_timed``; ``--also none`` skips them), and the other decode paths
+(balanced split, work list) on the headline workload's same inputs
+(``paths_on_this_workload``; ``--compare none`` skips them).  tmp_out is
+float32 by default (``--partials out``: the query dtype).
 
 Inputs are resident in HBM before timing.  By default the step rotates over
 ``--copies`` independent copies of the KV pool (4 x 14 GB for the headline),
@@ -308,9 +310,10 @@ def bench_prefill(args) -> int:
     return 0
 
 
-def prepare(number: int, args, B, W):
+def prepare(number: int, args, B, W, paths):
     """Builds workload ``number`` with ``--copies`` rotating copies (same bytes at
-    other addresses) and its marshalled calls; returns (base, calls, extra)."""
+    other addresses) and the marshalled calls of each path in ``paths``;
+    returns (base, {path: calls}, hold)."""
     import torch
 
     copies = 1 if args.hot else max(1, args.copies)
@@ -329,7 +332,7 @@ def prepare(number: int, args, B, W):
         w2.block_tables = base.block_tables.clone()
         wls.append(w2)
     stream = torch.cuda.current_stream()
-    calls, keep = [], []
+    calls, keep = {path: [] for path in paths}, []
     for wl in wls:
         out, es, ml, to = wl.alloc_outputs(args.partials)
         keep.append((out, es, ml, to))
@@ -341,16 +344,17 @@ def prepare(number: int, args, B, W):
                   kv_layout=args.layout)
         # Arguments are checked and marshalled once per input copy; a timed step
         # is one C call (v1 = partition kernel only; v2 / auto = partition +
-        # reduce; split = one launch).
-        if args.path == "v1":
-            calls.append(lambda out=out, wl=wl, kw=kw: B.paged_attention_v1(
-                out, wl.query, wl.key_cache, wl.value_cache, wl.num_kv_heads, wl.scale,
-                wl.block_tables, wl.seq_lens, wl.block_size, wl.max_seq_len, **kw))
-        elif args.path in ("split", "worklist"):
-            calls.append(B.PreparedCall(args.path, *common, **kw,
-                                        counters=B.split_counters(wl.num_seqs, wl.num_heads)))
-        else:
-            calls.append(B.PreparedCall(args.path, *common, **kw))
+        # reduce; split, worklist = one launch).
+        for path in paths:
+            if path == "v1":
+                calls[path].append(lambda out=out, wl=wl, kw=kw: B.paged_attention_v1(
+                    out, wl.query, wl.key_cache, wl.value_cache, wl.num_kv_heads, wl.scale,
+                    wl.block_tables, wl.seq_lens, wl.block_size, wl.max_seq_len, **kw))
+            elif path in ("split", "worklist"):
+                calls[path].append(B.PreparedCall(
+                    path, *common, **kw, counters=B.split_counters(wl.num_seqs, wl.num_heads)))
+            else:
+                calls[path].append(B.PreparedCall(path, *common, **kw))
     return base, calls, (wls, keep)
 
 
@@ -403,23 +407,33 @@ def time_steps(calls, steps: int, warmup: int, B):
     return wall, part, red, step
 
 
-def measure(number: int, args, B, W, cu: int, keep_base: bool = False) -> dict:
+def measure(number: int, args, B, W, cu: int, keep_base: bool = False,
+            other_paths=()) -> dict:
     """Times workload ``number`` on the chosen path; the figures of one bench
     line (the step, the dominant kernel's roofline, the whole step's).  With
     ``keep_base`` the first copy of the inputs is returned too (for the CPU
-    baseline); the others are freed."""
+    baseline); the others are freed.  ``other_paths`` are timed afterwards on
+    the same inputs (wall clock of the same K steps) for comparison."""
     import numpy as np
     import torch
 
-    base, calls, hold = prepare(number, args, B, W)
+    paths = [args.path] + [q for q in other_paths if q != args.path]
+    base, calls, hold = prepare(number, args, B, W, paths)
     ab = algorithmic_bytes(base, args.path, cu, B, args.window, args.partials)
-    wall, part_ms, red_ms, step_ms = time_steps(calls, args.steps, args.warmup, B)
+    wall, part_ms, red_ms, step_ms = time_steps(calls[args.path], args.steps, args.warmup, B)
     if args.path in ("v1", "split", "worklist") or not ab["any_v2"]:
         # No reduce kernel runs (an all-v1 auto call records its reduce events
         # back to back; their gap is event overhead, not work).
         red_ms = np.zeros(len(part_ms))
         step_ms = part_ms
     ms = wall * 1e3 / args.steps
+    others = {}
+    for q in paths[1:]:
+        log(f"timing {args.steps} steps of path {q}")
+        w2, pm2, _, _ = time_steps(calls[q], args.steps, args.warmup, B)
+        others[q] = {"us_per_step": round(w2 * 1e6 / args.steps, 2),
+                     "kv_gbs": round(ab["kv"] / (w2 / args.steps) / 1e9, 1),
+                     "kernel_avg_ms": round(float(pm2.mean()), 5)}
     part_avg = float(part_ms.mean())
     step_avg = float(step_ms.mean())
     achieved = ab["partition"] / (part_avg * 1e-3) / 1e9
@@ -429,7 +443,7 @@ def measure(number: int, args, B, W, cu: int, keep_base: bool = False) -> dict:
     dtype = {torch.float32: "f32", torch.float16: "f16", torch.bfloat16: "bf16"}[base.dtype]
     if base.kv_cache_dtype == "fp8_e4m3":
         dtype = f"{dtype} (fp8 e4m3 KV)"
-    copies = len(calls)
+    copies = len(calls[args.path])
     res = {
         "name": base.name,
         "dtype": dtype,
@@ -452,6 +466,7 @@ def measure(number: int, args, B, W, cu: int, keep_base: bool = False) -> dict:
         "step_achieved": step_achieved,
         "copies": copies,
         "options": options,
+        "other_paths": others,
         "base": base if keep_base else None,
     }
     del calls, hold, base
@@ -468,6 +483,9 @@ def main() -> int:
     ap.add_argument("--workload", type=int, default=4, choices=[1, 2, 3, 4, 5],
                     help="the headline workload (default 4: ragged MHA ALiBi bf16, the "
                          "largest that fits one GPU)")
+    ap.add_argument("--compare", default="split,worklist",
+                    help="other decode paths timed on the headline workload, reported inside the "
+                         "line (comma list, or 'none')")
     ap.add_argument("--also", default="3,5",
                     help="other workloads timed in the same process, reported inside the line "
                          "(comma list, or 'none')")
@@ -515,7 +533,14 @@ def main() -> int:
     also = [] if args.also.strip().lower() in ("", "none") else [
         int(x) for x in args.also.split(",") if int(x) != args.workload]
 
-    head = measure(args.workload, args, B, W, cu, keep_base=not args.no_cpu_baseline)
+    compare = [] if args.compare.strip().lower() in ("", "none") else [
+        q.strip() for q in args.compare.split(",")]
+    for q in compare:
+        if q not in ("auto", "v2", "v1", "split", "worklist"):
+            print(f"unknown path {q!r} in --compare", file=sys.stderr)
+            return 2
+    head = measure(args.workload, args, B, W, cu, keep_base=not args.no_cpu_baseline,
+                   other_paths=compare)
     others = [measure(n, args, B, W, cu) for n in also]
 
     if args.calibrate_copy:
@@ -586,6 +611,7 @@ def main() -> int:
             "frac_of_stream_read": (round(head["achieved"] / stream_gbs, 4)
                                     if stream_gbs else None),
         },
+        "paths_on_this_workload": head["other_paths"],
         "also_timed": [{
             "workload": o["workload"], "dtype": o["dtype"],
             "us_per_step": round(o["ms_per_step"] * 1e3, 2),

@@ -332,21 +332,24 @@ pa_status paged_attention_split(
 /* ---------------------------------------------------------------------- */
 
 /* The decode of paged_attention_v2_ex scheduled from a work list built on
- * the device, in one persistent launch: as many workgroups as the GPU holds
- * at once ("workers"), none of them without work on a batch of at least
- * 2048 keys per worker.  The batch's items -- (sequence, KV head) -- are laid
- * end to end by the memory-load cost model of the PoD page (FlashInfer PR
- * #967, work estimate qo_len + 2 * page_size * kv_len: one query row and the
- * K and V rows of every key in the window); worker w takes the w-th equal
- * share of that line, cutting an item only on 32-key steps and at least 512
- * keys from either end (so a cut item has at most ceil(L / 512) pieces, and
- * at most 64).  Every worker builds its own entries of the list from
- * seq_lens; each walks its items in order, writes out directly for an item
- * it holds whole, and otherwise stores the piece's partials (slot = piece)
- * and arrives at the item's counter: the last piece merges them with the V2
- * page's Phase 2 log-sum-exp rescale.  The result equals the v1 / v2 result
- * up to rounding (partials rounded to the options' partial dtype, fp32 by
- * default).
+ * the device, in one persistent launch of one workgroup per compute unit.
+ * The workers are the workgroups, or their waves when the batch has at
+ * least two (sequence, KV head) items per wave (many small items); none is
+ * without work on a batch of at least 2048 keys per worker.  The items are
+ * laid end to end by the work-cost model of the PoD page (FlashInfer PR
+ * #967, qo_len + 2 * page_size * kv_len, a model of memory load): the K and
+ * V rows of every key in the window, plus a per-item term standing for the
+ * item's fixed cost (64 keys' worth, measured); worker w takes the w-th
+ * equal share of that line, cutting an item only on 32-key steps and at
+ * least 512 keys from either end (so a cut item has at most ceil(L / 512)
+ * pieces, and at most 64).  Every worker builds its own entries of the list
+ * from seq_lens; each walks its items in order, writes out directly for an
+ * item it holds whole, and otherwise stores the piece's partials (slot =
+ * piece) and arrives at the item's counter: the last piece merges them with
+ * the V2 page's Phase 2 log-sum-exp rescale.  The result equals the v1 / v2
+ * result up to rounding (partials rounded to the options' partial dtype,
+ * fp32 by default).  Fastest on ragged batches of many short sequences;
+ * paged_attention_split is faster on a few long ones.
  *
  * Buffers, counters contract and errors as for paged_attention_split
  * (exp_sums, max_logits and tmp_out are scratch; counters int32 [num_seqs,

@@ -34,14 +34,20 @@ struct Tunables {
   int parts_reversed = 1;     // all-v2 launches dispatch the last partition first
   int split_reversed = 0;     // split launches dispatch the last piece slice first
   int split_target = 0;       // split: fixed piece target in keys (0: the size rule)
-  // List: an item's cost beyond its keys, in keys (the PoD page's qo_len
-  // term: one query row against two cache rows per key rounds to 1).
-  int list_item_cost = 1;
+  // List: an item's cost beyond its keys, in keys: the place of the PoD
+  // page's qo_len term (the per-request work that does not scale with the
+  // cache).  Here it stands for an item's fixed cost -- its epilogue and the
+  // latency of its first loads -- which measures at about 64 keys' worth of
+  // streaming: on MI355X the ragged ALiBi batch ran at 2104 / 2073 / 2085 /
+  // 2088 / 2103 us for 16 / 64 / 128 / 256 / 511.
+  int list_item_cost = 64;
   // List: workers per CU (0: as many workgroups as one CU holds at once).
   // One per CU already streams at the device's rate (one workgroup reads up
   // to ~48 GB/s, the device ~28 GB/s per CU); more workers only cut more
   // items into pieces.
   int list_per_cu = 1;
+  int list_lds = 0;           // list: dynamic LDS bytes reserved per worker
+  int list_wave = -1;         // list: 1 / 0 = one worker per wave / workgroup; -1: by shape
 };
 
 int env_int(const char *name, int fallback, int lo, int hi) {
@@ -67,6 +73,8 @@ const Tunables &tunables() {
     x.split_target = env_int("PA_SPLIT_TARGET", x.split_target, 0, 1 << 30);
     x.list_item_cost = env_int("PA_LIST_ITEM_COST", x.list_item_cost, 0, 511);
     x.list_per_cu = env_int("PA_LIST_PER_CU", x.list_per_cu, 0, 16);
+    x.list_lds = env_int("PA_LIST_LDS", x.list_lds, 0, 160 * 1024);
+    x.list_wave = env_int("PA_LIST_WAVE", x.list_wave, -1, 1);
     return x;
   }();
   return t;
@@ -309,6 +317,17 @@ Params make_params(const Call &c, int cu, int head_groups) {
   p.head_groups = head_groups;
   p.mode = c.list ? pa::kModeList : c.split ? pa::kModeSplit : (int)c.mode;
   p.item_cost = tunables().list_item_cost;
+  // List workers: one per wave when the batch has at least two items
+  // (sequence, head group) per wave worker -- many small items, where a
+  // workgroup-wide epilogue per item would idle the CU -- else one per
+  // workgroup.  (VALU kernels only; the MFMA kernels' batches have few,
+  // large items per worker.)
+  if (c.list) {
+    const long long waves = 4LL * cu * (tunables().list_per_cu > 0 ? tunables().list_per_cu : 1);
+    p.list_wave = tunables().list_wave >= 0
+                      ? tunables().list_wave
+                      : ((long long)c.num_seqs * c.num_kv_heads * head_groups >= 2 * waves ? 1 : 0);
+  }
   p.counters = c.counters;
   p.split_target = c.split ? split_target(c, (long long)c.num_kv_heads * head_groups, cu) : 0;
   const long long b_hkv = (long long)c.num_seqs * c.num_kv_heads;
@@ -372,6 +391,7 @@ pa_status run_partition(const Call &c) {
   if (c.list) {
     l.list_cus = cu;
     l.list_per_cu = tunables().list_per_cu;
+    l.list_lds = tunables().list_lds;
   }
   const bool fp8 = c.kv_cache_dtype == PA_KV_FP8_E4M3;
   hipError_t e;

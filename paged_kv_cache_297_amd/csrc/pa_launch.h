@@ -25,6 +25,9 @@ struct Launch {
   // hold (grid.y = grid.z = 1).
   int list_cus = 0;
   int list_per_cu = 0;
+  // Dynamic LDS reserved by a list launch (bytes): enough of it keeps a
+  // second worker off a CU that already holds one.
+  int list_lds = 0;
 };
 
 // Largest power-of-two query-head group the VALU kernel keeps in registers

@@ -36,14 +36,16 @@ inline int resident_per_cu(const void *kernel) {
 template <typename Kernel, typename P>
 hipError_t launch_kernel(Kernel kernel, const Launch &l, const P &p) {
   dim3 grid = l.grid;
+  size_t lds = 0;
   if (l.list_cus > 0) {
     const int per_cu = l.list_per_cu > 0 ? l.list_per_cu : resident_per_cu((const void *)kernel);
     grid = dim3((unsigned)(l.list_cus * per_cu), 1, 1);
+    lds = (size_t)l.list_lds;
   }
   if (l.start && l.stop)
-    hipExtLaunchKernelGGL(kernel, grid, dim3(kThreads), 0, l.stream, l.start, l.stop, 0, p);
+    hipExtLaunchKernelGGL(kernel, grid, dim3(kThreads), lds, l.stream, l.start, l.stop, 0, p);
   else
-    hipLaunchKernelGGL(kernel, grid, dim3(kThreads), 0, l.stream, p);
+    hipLaunchKernelGGL(kernel, grid, dim3(kThreads), lds, l.stream, p);
   return hipGetLastError();
 }
 

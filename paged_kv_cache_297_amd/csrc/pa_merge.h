@@ -21,25 +21,27 @@ namespace pa {
 
 constexpr float kMergeLog2e = 1.4426950408889634f;
 
-// One output element of the merge above.  A partial with m_c = -inf (no key
-// in its range) adds nothing and its O_c is not read; a NaN m_c (a piece that
-// met an invalid block-table entry) makes the result NaN.  exp2_fn(x) = 2^x;
-// load_o(c) = O_c.  The partials are taken in index order, so the result
-// does not depend on the order in which they were produced.
-template <typename Exp2, typename LoadO>
-PA_HD inline float lse_merge(const float *m, const float *s, int k, Exp2 exp2_fn, LoadO load_o) {
+// One output element of the merge above.  m(c) = m_c, s(c) = S_c, o(c) =
+// O_c (each called for c < k only); exp2_fn(x) = 2^x.  A partial with m_c =
+// -inf (no key in its range) adds nothing and its O_c is not read; a NaN m_c
+// (a piece that met an invalid block-table entry) makes the result NaN.  The
+// partials are taken in index order, so the result does not depend on the
+// order in which they were produced.
+template <typename M, typename S, typename Exp2, typename LoadO>
+PA_HD inline float lse_merge(M m, S s, int k, Exp2 exp2_fn, LoadO load_o) {
   const float ninf = -__builtin_inff();
   float big_m = ninf;
   bool nan_seen = false;
   for (int c = 0; c < k; ++c) {
-    nan_seen |= m[c] != m[c];
-    big_m = fmaxf(big_m, m[c]);
+    const float mc = m(c);
+    nan_seen |= mc != mc;
+    big_m = fmaxf(big_m, mc);
   }
   float sum = 0.0f, acc = 0.0f;
   PA_UNROLL4
   for (int c = 0; c < k; ++c) {
-    const float mc = m[c];
-    const float r = mc == ninf ? 0.0f : exp2_fn((mc - big_m) * kMergeLog2e) * s[c];
+    const float mc = m(c);
+    const float r = mc == ninf ? 0.0f : exp2_fn((mc - big_m) * kMergeLog2e) * s(c);
     sum += r;
     acc = mc == ninf ? acc : fmaf(r, load_o(c), acc);
   }

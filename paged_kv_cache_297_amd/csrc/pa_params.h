@@ -71,6 +71,7 @@ struct Params {
   int *counters;        // split mode: [B, H] arrival counters, zero between calls
   int split_target;     // split mode: keys per piece before equalising (multiple of 512)
   int item_cost;        // list mode: cost of an item beyond its keys (the query row)
+  int list_wave;        // list mode, VALU kernel: one worker per wave (else per workgroup)
 };
 
 // First key position inside the sliding window of a sequence of length

@@ -250,23 +250,26 @@ __device__ __forceinline__ void split_merge(const Params &p, const Work &w) {
     const int h = idx / D, d = idx - h * D;
     const TT *col = to + (row0 + (size_t)h * p.max_num_partitions) * D + d;
     const float o = lse_merge(
-        sm_pm[h], sm_ps[h], k, [](float x) { return fast_exp2(x); },
+        [&](int c) { return sm_pm[h][c]; }, [&](int c) { return sm_ps[h][c]; }, k,
+        [](float x) { return fast_exp2(x); },
         [&](int c) { return coherent_load_elem<TT>(col + (size_t)c * D); });
     store_out_row<QT, D>(p, w.seq, w.head0 + h, d, o);
   }
 }
 
 // ---------------------------------------------------------------------------
-// List mode (paged_attention_worklist): a persistent launch of gridDim.x
-// workgroups ("workers").  The batch's items -- (sequence, grid-x slot) --
-// lie end to end on a line by their memory-load cost (pa_worklist.h); worker
-// w takes the w-th equal share of the line, with its ends snapped so that
-// an item is cut only on 32-key steps and at least 512 keys from its ends.
-// Every worker builds its own part of the list: all four waves scan
-// seq_lens with wave-wide prefix sums (no LDS, no barrier), find the items
-// holding their two boundaries, and then walk the items in between.  A cut
-// item's pieces store partials in their slots and the last to arrive merges
-// them (split_merge); a whole item writes out directly.
+// List mode (paged_attention_worklist): a persistent launch in which every
+// wave is a worker.  The batch's items -- (sequence, grid-x slot) -- lie end
+// to end on a line by their memory-load cost (pa_worklist.h); worker w takes
+// the w-th equal share of the line, with its ends snapped so that an item is
+// cut only on 32-key steps and at least 512 keys from its ends.  Every
+// worker builds its own part of the list: it scans seq_lens with wave-wide
+// prefix sums, finds the items holding its two boundaries, and then walks
+// the items in between, each one whole, with its own online softmax.  Its
+// epilogue works from registers: a whole item writes out; a cut item's piece
+// stores its partials in its slot and arrives at the item's counter, and the
+// last piece to arrive merges them.  No step of it waits for the other waves
+// of the workgroup, so one wave's epilogue overlaps the others' streaming.
 // ---------------------------------------------------------------------------
 struct ListCursor {
   ListShares sh;     // line length T, workers with work W, the equal shares
@@ -398,9 +401,10 @@ __device__ __forceinline__ void list_advance(const Params &p, int gx, ListCursor
   c.cost = list_seq_cost(p, c.seq, c.L, c.keys, c.base);
 }
 
-// Sets up worker blockIdx.x; false when it has no range (a batch too small
-// for every worker).
-__device__ __forceinline__ bool list_begin(const Params &p, ListCursor &c) {
+// Sets up worker `worker` of `grid_workers`; false when it has no range (a
+// batch too small for every worker).  Wave-uniform.
+__device__ __forceinline__ bool list_begin(const Params &p, ListCursor &c, int worker,
+                                           int grid_workers) {
   const int gx = p.num_kv_heads * p.head_groups;
   const int lane = threadIdx.x & 63;
   long long sum = 0;
@@ -414,10 +418,10 @@ __device__ __forceinline__ bool list_begin(const Params &p, ListCursor &c) {
     }
   }
   const long long total = wave_sum64(sum) * gx;
-  c.sh = list_shares(total, uniform32(list_workers(total, (int)gridDim.x, wave_max32(kmax))));
+  c.sh = list_shares(total, uniform32(list_workers(total, grid_workers, wave_max32(kmax))));
   c.sh.q = wave_uniform64(c.sh.q);
   c.sh.r = wave_uniform64(c.sh.r);
-  c.w = blockIdx.x;
+  c.w = worker;
   if (c.w >= c.sh.workers) return false;
   // This worker's end: the next worker's start, snapped.
   if (c.w + 1 >= c.sh.workers) {
@@ -436,11 +440,12 @@ __device__ __forceinline__ bool list_begin(const Params &p, ListCursor &c) {
 }
 
 // The next piece of this worker's range as a Work, or false at the end.
-// Empty and invalid sequences are finished here (out = 0 / NaN) and
-// skipped.
+// Empty and invalid sequences are finished here (out = 0 / NaN, written by
+// the worker's lanes) and skipped.
 template <typename QT, int D>
 __device__ __forceinline__ bool list_next(const Params &p, int block_size, int group_slots,
                                           ListCursor &c, Work &w) {
+  const int lane = epi_tid() & 63;
   const int gx = p.num_kv_heads * p.head_groups;
   while (c.pos < c.end && c.seq < p.num_seqs) {
     w.seq = c.seq;
@@ -458,7 +463,7 @@ __device__ __forceinline__ bool list_next(const Params &p, int block_size, int g
     if (keys == 0) {
       // Empty (out = 0) or invalid length (out = NaN); the item is never cut.
       const bool bad = w.L != 0;
-      for (int idx = epi_tid(); idx < w.nh * D; idx += kThreads)
+      for (int idx = lane; idx < w.nh * D; idx += 64)
         store_out_row<QT, D>(p, w.seq, w.head0 + idx / D, idx % D,
                              bad ? __builtin_nanf("") : 0.0f);
       continue;
@@ -479,6 +484,86 @@ __device__ __forceinline__ bool list_next(const Params &p, int block_size, int g
     return true;
   }
   return false;
+}
+
+// ---------------------------------------------------------------------------
+// List mode: the epilogue of one wave's piece, from registers.
+// ---------------------------------------------------------------------------
+
+// One element of a piece's normalised output: out directly when the item is
+// whole, else the piece's partial row (slot = piece), written past the L2.
+template <typename QT, int D>
+__device__ __forceinline__ void piece_elem(const Params &p, const Work &w, int h, int d,
+                                           float o) {
+  const int head = w.head0 + h;
+  if (!w.v2) {
+    store_out_row<QT, D>(p, w.seq, head, d, o);
+    return;
+  }
+  const size_t row = ((size_t)w.seq * p.num_heads + head) * p.max_num_partitions + w.part;
+  if (p.tmp_f32)
+    coherent_store_elem<float>(reinterpret_cast<float *>(p.tmp_out) + row * D + d, o);
+  else
+    coherent_store_elem<QT>(reinterpret_cast<QT *>(p.tmp_out) + row * D + d, o);
+}
+
+// The statistics of head h of a cut item's piece: the exp-sum l (NaN after
+// an out-of-range block-table entry) and the max logit m (log2 units; stored
+// in natural-log units and the absolute ALiBi convention, as wave_merge).
+__device__ __forceinline__ void piece_stats(const Params &p, const Work &w, int h, float m,
+                                            float l) {
+  const int head = w.head0 + h;
+  const size_t row = ((size_t)w.seq * p.num_heads + head) * p.max_num_partitions + w.part;
+  float ml = p.alibi_slopes ? fmaf(p.alibi_slopes[head], (float)w.t_ref, m * kLn2) : m * kLn2;
+  ml = l != l ? __builtin_nanf("") : ml;
+  coherent_store(p.exp_sums + row, f_bits(l));
+  coherent_store(p.max_logits + row, f_bits(ml));
+}
+
+// After a wave has stored its piece's partials: its arrival at the item's
+// counter (lane 0; agent-scope release increment, acquire load in the last
+// piece, as split_merge), and in the last piece the Phase 2 merge of the k
+// partials, dims across the wave's lanes.  The wavefront-scope fences order
+// the other lanes' stores before lane 0's release and lane 0's acquire
+// before the other lanes' loads.
+template <typename QT, typename TT, int D>
+__device__ __forceinline__ void piece_arrive(const Params &p, const Work &w) {
+  const int lane = epi_tid() & 63;
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's partial stores are done
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  int last = 0;
+  if (lane == 0) {
+    int *ctr = p.counters + (size_t)w.seq * p.num_heads + w.xslot;
+    last = arrive_last(
+        ctr, w.n_part,
+        [](int *c) {
+          return __hip_atomic_fetch_add(c, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        },
+        [](int *c) { (void)__hip_atomic_load(c, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT); },
+        [](int *c, int v) {
+          __hip_atomic_store(c, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        });
+  }
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  if (!__builtin_amdgcn_readfirstlane(last)) return;
+  // Lane c < k holds piece c's statistics; the merge reads them by lane.
+  const int k = min(w.n_part, kSplitMaxPieces);
+  const TT *to = reinterpret_cast<const TT *>(p.tmp_out);
+  for (int h = 0; h < w.nh; ++h) {
+    const size_t row0 = ((size_t)w.seq * p.num_heads + w.head0 + h) * p.max_num_partitions;
+    const float mc = lane < k ? bits_f(coherent_load(p.max_logits + row0 + lane)) : 0.0f;
+    const float sc = lane < k ? bits_f(coherent_load(p.exp_sums + row0 + lane)) : 0.0f;
+    for (int d = lane; d < D; d += 64) {
+      const TT *col = to + row0 * D + d;
+      const float o = lse_merge(
+          [&](int c) { return readlane(mc, c); }, [&](int c) { return readlane(sc, c); }, k,
+          [](float x) { return fast_exp2(x); },
+          [&](int c) { return coherent_load_elem<TT>(col + (size_t)c * D); });
+      store_out_row<QT, D>(p, w.seq, w.head0 + h, d, o);
+    }
+  }
 }
 
 // One element of a workgroup's result.  Wave wv left, for query head h of

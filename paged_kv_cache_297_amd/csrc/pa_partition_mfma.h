@@ -374,32 +374,34 @@ __global__ void __launch_bounds__(kThreads)
     }
   };
 
-  // The wave's steps of the item (wv, wv + 4, ...): two tiles ping-pong,
-  // and while step st is consumed the loads of the wave's next step are in
-  // flight.  The loop runs whole pairs and has no exit between them, and
+  // The wave's steps of the item (first, first + stride, ...; stride 4 when
+  // the workgroup shares the item, 1 for a list worker): two tiles
+  // ping-pong, and while step st is consumed the loads of the wave's next
+  // step are in flight.  The loop runs whole pairs and has no exit between them, and
   // every load in it is always issued, so the wait before a step covers only
   // that step's tile (a mid-pair exit would merge a path with the other tile
   // still in flight into the back edge).  The scheduling barriers keep each
   // prefetch ahead of the step's compute.  On entry ta is loading the wave's
   // first step.
-  auto run_steps = [&](const Item &it, Tile &ta, Tile &tb) {
-    int st = wv;
-    int left = st < it.n_steps ? (it.n_steps - st + kWaves - 1) / kWaves : 0;
+  auto run_steps = [&](const Item &it, Tile &ta, Tile &tb, int first, auto stride_c) {
+    constexpr int S = decltype(stride_c)::value;
+    int st = first;
+    int left = st < it.n_steps ? (it.n_steps - st + S - 1) / S : 0;
     while (left >= 3) {
-      tb = load_tile(it, st + kWaves);
+      tb = load_tile(it, st + S);
       __builtin_amdgcn_sched_barrier(0);
       process(it, st, ta);
-      ta = load_tile(it, st + 2 * kWaves);
+      ta = load_tile(it, st + 2 * S);
       __builtin_amdgcn_sched_barrier(0);
-      process(it, st + kWaves, tb);
-      st += 2 * kWaves;
+      process(it, st + S, tb);
+      st += 2 * S;
       left -= 2;
     }
     if (left == 2) {
-      tb = load_tile(it, st + kWaves);
+      tb = load_tile(it, st + S);
       __builtin_amdgcn_sched_barrier(0);
       process(it, st, ta);
-      process(it, st + kWaves, tb);
+      process(it, st + S, tb);
     } else if (left == 1) {
       process(it, st, ta);
     }
@@ -425,20 +427,36 @@ __global__ void __launch_bounds__(kThreads)
   };
 
   if constexpr (LIST) {
-    // Persistent worker: the pieces of its share of the work list in order;
-    // the barrier frees the LDS of one piece's epilogue for the next.
+    // Persistent, one worker per workgroup: the pieces of its share of the
+    // work list in order.  The next piece's query and first tile are
+    // requested before this piece's epilogue (cross-wave merge, stores,
+    // arrival), which then overlaps their latency; the barrier frees the LDS
+    // of one piece's epilogue for the next.  (The GQA groups this kernel
+    // serves make few, large items per worker, where one worker per wave
+    // would cut every item into many pieces.)
     ListCursor cur;
-    if (!list_begin(p, cur)) return;
+    if (!list_begin(p, cur, (int)blockIdx.x, (int)gridDim.x)) return;
     Work w;
-    while (list_next<QT, D>(p, BS, 16, cur, w)) {
-      const Item it = make_item(w);
-      load_query(w);
+    if (!list_next<QT, D>(p, BS, 16, cur, w)) return;
+    Item it = make_item(w);
+    load_query(w);
+    Tile ta, tb;
+    if (wv < it.n_steps) ta = load_tile(it, wv);
+    while (true) {
       reset_state();
-      Tile ta, tb;  // per item: nothing of one item's tiles lives into the next
-      if (wv < it.n_steps) ta = load_tile(it, wv);
-      run_steps(it, ta, tb);
+      run_steps(it, ta, tb, wv, std::integral_constant<int, kWaves>{});
+      Work wn;
+      const bool more = list_next<QT, D>(p, BS, 16, cur, wn);
+      Item itn;
+      if (more) {
+        itn = make_item(wn);
+        load_query(wn);
+        if (wv < itn.n_steps) ta = load_tile(itn, wv);
+      }
       finish_item(it);
       __syncthreads();
+      if (!more) break;
+      it = itn;
     }
   } else {
     Work w;
@@ -448,7 +466,7 @@ __global__ void __launch_bounds__(kThreads)
     reset_state();
     Tile ta, tb;
     if (wv < it.n_steps) ta = load_tile(it, wv);
-    run_steps(it, ta, tb);
+    run_steps(it, ta, tb, wv, std::integral_constant<int, kWaves>{});
     finish_item(it);
   }
 }

@@ -220,7 +220,9 @@ __device__ __forceinline__ float dim_group_sum(float v) {
 #define PA_VALU_OCCUPANCY
 #endif
 
-template <typename QT, typename KVT, int D, int BS, int GP, bool CAP, bool WIN, bool LIST = false>
+// LIST: 0 = one work item per workgroup (grid decomposition); 1 = persistent
+// list, one worker per workgroup; 2 = persistent list, one worker per wave.
+template <typename QT, typename KVT, int D, int BS, int GP, bool CAP, bool WIN, int LIST = 0>
 __global__ void __launch_bounds__(kThreads) PA_VALU_OCCUPANCY pa_partition_valu(const Params p) {
   using T = ValuTraits<QT, KVT>;
   using HM = HeadMap<GP, BS>;
@@ -240,81 +242,90 @@ __global__ void __launch_bounds__(kThreads) PA_VALU_OCCUPANCY pa_partition_valu(
   __shared__ float sm_l[kWaves][GP];
   __shared__ __attribute__((aligned(16))) PV sm_p[kWaves][2][GP][BS];
 
-  // One work item: a partition, a whole v1 sequence, or a piece.
-  auto run_item = [&](const Work &w) {
-    const int lane = threadIdx.x & 63;
-    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int tok = lane % BS;
-    const int r = lane / BS;
-    const int tg = lane % VPD;
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int tok = lane % BS;
+  const int r = lane / BS;
+  const int tg = lane % VPD;
+  int my_head_base = 0;  // first head slot this lane owns after the transpose-reduce
+#pragma unroll
+  for (int rr = 0; rr < R; ++rr)
+    if (rr == r) my_head_base = HM::head_base(rr);
 
-    // Query slices of the group's heads for this lane's K chunks.
-    unsigned qw[GP][NL][T::kQW];
-    {
-      const QT *qbase = reinterpret_cast<const QT *>(p.query) +
-                        ((size_t)w.seq * p.num_heads + w.head0) * D;
+  const char *kcache = reinterpret_cast<const char *>(p.key_cache);
+  const char *vcache = reinterpret_cast<const char *>(p.value_cache);
+  const size_t blk_stride = (size_t)p.num_kv_heads * TILE;
+
+  // One work item (a partition, a whole v1 sequence, or a piece) with the
+  // addressing its tile loads need.
+  struct Item {
+    Work w;
+    const_i32_ptr btab;
+    size_t head_off;
+  };
+  auto make_item = [&](const Work &w) {
+    Item it;
+    it.w = w;
+    it.btab = as_const_table(p.block_tables + (size_t)w.seq * p.max_num_blocks_per_seq);
+    it.head_off = (size_t)w.kvh * TILE;
+    return it;
+  };
+
+  // Query slices of the group's heads for this lane's K chunks, and the
+  // ALiBi slope (log2 units) of each head slot this lane owns.
+  unsigned qw[GP][NL][T::kQW];
+  float slope2[NF];
+  auto load_query = [&](const Work &w) {
+    const QT *qbase = reinterpret_cast<const QT *>(p.query) +
+                      ((size_t)w.seq * p.num_heads + w.head0) * D;
 #pragma unroll
-      for (int h = 0; h < GP; ++h)
+    for (int h = 0; h < GP; ++h)
 #pragma unroll
-        for (int i = 0; i < NL; ++i) {
-          if (h < w.nh) {
-            T::load_q(qbase + h * D + (i * R + r) * X, qw[h][i]);
-          } else {
+      for (int i = 0; i < NL; ++i) {
+        if (h < w.nh) {
+          T::load_q(qbase + h * D + (i * R + r) * X, qw[h][i]);
+        } else {
 #pragma unroll
-            for (int e = 0; e < T::kQW; ++e) qw[h][i][e] = 0u;
-          }
+          for (int e = 0; e < T::kQW; ++e) qw[h][i][e] = 0u;
         }
-    }
-    // ALiBi slope (log2 units) of each head slot this lane owns after the reduce.
-    float slope2[NF];
+      }
 #pragma unroll
     for (int j = 0; j < NF; ++j) {
-      int hb = 0;
-#pragma unroll
-      for (int rr = 0; rr < R; ++rr)
-        if (rr == r) hb = HM::head_base(rr);
-      const int h = hb + j;
+      const int h = my_head_base + j;
       slope2[j] = (p.alibi_slopes && h < w.nh) ? p.alibi_slopes[w.head0 + h] * kLog2e : 0.0f;
     }
-    int my_head_base = 0;
-#pragma unroll
-    for (int rr = 0; rr < R; ++rr)
-      if (rr == r) my_head_base = HM::head_base(rr);
+  };
 
-    float m_run[NF], l_run[NF];
+  // Online-softmax state of the wave for the current item.
+  float m_run[NF], l_run[NF];
+  float acc[GP][NL];
+  bool poisoned;
+  auto reset_state = [&] {
 #pragma unroll
     for (int j = 0; j < NF; ++j) {
       m_run[j] = -__builtin_inff();
       l_run[j] = 0.0f;
     }
-    float acc[GP][NL];
 #pragma unroll
     for (int h = 0; h < GP; ++h)
 #pragma unroll
       for (int i = 0; i < NL; ++i) acc[h][i] = 0.0f;
+    poisoned = false;
+  };
 
-    const char *kcache = reinterpret_cast<const char *>(p.key_cache);
-    const char *vcache = reinterpret_cast<const char *>(p.value_cache);
-    const const_i32_ptr btab =
-        as_const_table(p.block_tables + (size_t)w.seq * p.max_num_blocks_per_seq);
-    const size_t head_off = (size_t)w.kvh * TILE;
-    const size_t blk_stride = (size_t)p.num_kv_heads * TILE;
-    bool poisoned = false;
-
-    struct Tile {
-      u32x4 k[NL], v[NL];
+  struct Tile {
+    u32x4 k[NL], v[NL];
+    bool bad;  // the block-table entry was out of range
   };
   // Out-of-range block-table entries are redirected to block 0 (always
-  // addressable) and reported through the poison flag.
-  auto load_tile = [&](int blk) {
-    int phys = btab[blk];
-    if (phys < 0 || phys >= p.num_blocks) {
-      poisoned = true;
-      phys = 0;
-    }
-    const char *kb = kcache + (size_t)phys * blk_stride + head_off + 16 * lane;
-    const char *vb = vcache + (size_t)phys * blk_stride + head_off + 16 * lane;
+  // addressable) and reported through the tile's bad flag.
+  auto load_tile = [&](const Item &it, int blk) {
     Tile t;
+    int phys = it.btab[blk];
+    t.bad = phys < 0 || phys >= p.num_blocks;
+    phys = t.bad ? 0 : phys;
+    const char *kb = kcache + (size_t)phys * blk_stride + it.head_off + 16 * lane;
+    const char *vb = vcache + (size_t)phys * blk_stride + it.head_off + 16 * lane;
 #pragma unroll
     for (int i = 0; i < NL; ++i) t.k[i] = load16_stream(kb + 1024 * i);
 #pragma unroll
@@ -322,7 +333,9 @@ __global__ void __launch_bounds__(kThreads) PA_VALU_OCCUPANCY pa_partition_valu(
     return t;
   };
 
-  auto process = [&](int blk, int parity, const Tile &tl) {
+  auto process = [&](const Item &it, int blk, int parity, const Tile &tl) {
+    const Work &w = it.w;
+    poisoned |= tl.bad;
     // Logits: partial dots over this lane's chunks, then transpose-reduce.
     float s[GP];
 #pragma unroll
@@ -374,72 +387,170 @@ __global__ void __launch_bounds__(kThreads) PA_VALU_OCCUPANCY pa_partition_valu(
     }
   };
 
-  // Two tiles ping-pong: while block blk is consumed, the loads of the
-  // wave's next block (blk + 4) are in flight.  The loop runs whole pairs
-  // with no exit between them and always issues its loads, so the wait
-  // before a block covers only that block's tile; the scheduling barriers
-  // keep each prefetch ahead of the block's compute.
-  auto parity = [&](int b) { return ((b - w.blk_begin) / kWaves) & 1; };
-  int blk = w.blk_begin + wv;
-  int left = blk < w.blk_end ? (w.blk_end - blk + kWaves - 1) / kWaves : 0;  // this wave's blocks
-  Tile ta, tb;
-  if (left > 0) ta = load_tile(blk);
-  while (left >= 3) {
-    tb = load_tile(blk + kWaves);
-    __builtin_amdgcn_sched_barrier(0);
-    process(blk, parity(blk), ta);
-    ta = load_tile(blk + 2 * kWaves);
-    __builtin_amdgcn_sched_barrier(0);
-    process(blk + kWaves, parity(blk + kWaves), tb);
-    blk += 2 * kWaves;
-    left -= 2;
-  }
-  if (left == 2) {
-    tb = load_tile(blk + kWaves);
-    __builtin_amdgcn_sched_barrier(0);
-    process(blk, parity(blk), ta);
-    process(blk + kWaves, parity(blk + kWaves), tb);
-  } else if (left == 1) {
-    process(blk, parity(blk), ta);
-  }
-
-  // Wave totals per head, then the cross-wave merge.
-#pragma unroll
-  for (int j = 0; j < NF; ++j) l_run[j] = token_group_sum<BS>(l_run[j]);
-#pragma unroll
-  for (int h = 0; h < GP; ++h) {
-    const int g = HM::src_group(h);
-    const int j = h - HM::head_base(g);
-    const float mh = readlane(m_run[j], g * BS);
-    const float lh = readlane(l_run[j], g * BS);
-    if (lane == 0) {
-      sm_m[wv][h] = mh;
-      sm_l[wv][h] = poisoned ? __builtin_nanf("") : lh;
+  // The wave's blocks of the item (blk_begin + first, then every stride-th;
+  // stride 4 when the workgroup shares the item, 1 for a list worker): two
+  // tiles ping-pong, and while block blk is consumed the loads of the wave's
+  // next block are in flight.  The loop runs whole pairs with no exit
+  // between them and always issues its loads, so the wait before a block
+  // covers only that block's tile; the scheduling barriers keep each
+  // prefetch ahead of the block's compute.  On entry ta holds (or is
+  // loading) the wave's first block.
+  auto run_steps = [&](const Item &it, Tile &ta, Tile &tb, int first, auto stride_c) {
+    constexpr int S = decltype(stride_c)::value;
+    const Work &w = it.w;
+    auto parity = [&](int b) { return ((b - w.blk_begin) / S) & 1; };
+    int blk = w.blk_begin + first;
+    int left = blk < w.blk_end ? (w.blk_end - blk + S - 1) / S : 0;
+    while (left >= 3) {
+      tb = load_tile(it, blk + S);
+      __builtin_amdgcn_sched_barrier(0);
+      process(it, blk, parity(blk), ta);
+      ta = load_tile(it, blk + 2 * S);
+      __builtin_amdgcn_sched_barrier(0);
+      process(it, blk + S, parity(blk + S), tb);
+      blk += 2 * S;
+      left -= 2;
     }
-#pragma unroll
-    for (int i = 0; i < NL; ++i) {
-      const float v = dim_group_sum<VPD>(acc[h][i]);
-      if (tg == 0) sm_o[wv][h][(64 * i + lane) / VPD] = v;
+    if (left == 2) {
+      tb = load_tile(it, blk + S);
+      __builtin_amdgcn_sched_barrier(0);
+      process(it, blk, parity(blk), ta);
+      process(it, blk + S, parity(blk + S), tb);
+    } else if (left == 1) {
+      process(it, blk, parity(blk), ta);
     }
-  }
-  __syncthreads();
-  finish_partition<QT, D, GP, D>(p, w, sm_o, sm_m, sm_l);
+  };
+  // The wave's first tile of an item, if it has a block.
+  auto first_tile = [&](const Item &it, Tile &ta, int first) {
+    const int b0 = it.w.blk_begin + first;
+    if (b0 < it.w.blk_end) ta = load_tile(it, b0);
   };
 
-  if constexpr (LIST) {
-    // Persistent worker: the pieces of its share of the work list in order;
+  // Wave totals per head, then the cross-wave merge and the stores.  Lane
+  // indices are re-read here (epi_tid) rather than carried across the list
+  // form's item loop.
+  auto finish_item = [&](const Item &it) {
+    const int et = epi_tid(), el = et & 63, ew = et >> 6, etg = el % VPD;
+#pragma unroll
+    for (int j = 0; j < NF; ++j) l_run[j] = token_group_sum<BS>(l_run[j]);
+#pragma unroll
+    for (int h = 0; h < GP; ++h) {
+      const int g = HM::src_group(h);
+      const int j = h - HM::head_base(g);
+      const float mh = readlane(m_run[j], g * BS);
+      const float lh = readlane(l_run[j], g * BS);
+      if (el == 0) {
+        sm_m[ew][h] = mh;
+        sm_l[ew][h] = poisoned ? __builtin_nanf("") : lh;
+      }
+#pragma unroll
+      for (int i = 0; i < NL; ++i) {
+        const float v = dim_group_sum<VPD>(acc[h][i]);
+        if (etg == 0) sm_o[ew][h][(64 * i + el) / VPD] = v;
+      }
+    }
+    __syncthreads();
+    finish_partition<QT, D, GP, D>(p, it.w, sm_o, sm_m, sm_l);
+  };
+
+  // A list worker's epilogue, from registers: every head's running max and
+  // sum come from the lanes that own it; lane l with l % VPD == 0 holds dim
+  // (64 i + l) / VPD of each head.
+  auto finish_wave = [&](const Item &it) {
+    const Work &w = it.w;
+    const int el = epi_tid() & 63, etg = el % VPD;
+#pragma unroll
+    for (int j = 0; j < NF; ++j) l_run[j] = token_group_sum<BS>(l_run[j]);
+#pragma unroll
+    for (int h = 0; h < GP; ++h) {
+      const int g = HM::src_group(h);
+      const int j = h - HM::head_base(g);
+      const float mh = readlane(m_run[j], g * BS);
+      const float lh = readlane(l_run[j], g * BS);
+      const float lsum = poisoned ? __builtin_nanf("") : lh;
+      const float scale = p.v_scale / lh;
+#pragma unroll
+      for (int i = 0; i < NL; ++i) {
+        const float v = dim_group_sum<VPD>(acc[h][i]);
+        if (h < w.nh && etg == 0)
+          piece_elem<QT, D>(p, w, h, (64 * i + el) / VPD,
+                            lsum != lsum ? __builtin_nanf("") : v * scale);
+      }
+      if (h < w.nh && w.v2 && el == 0) piece_stats(p, w, h, mh, lsum);
+    }
+    if (w.v2) {
+      if (p.tmp_f32) piece_arrive<QT, float, D>(p, w);
+      else piece_arrive<QT, QT, D>(p, w);
+    }
+  };
+
+  if constexpr (LIST == 2) {
+    // Persistent, one worker per wave: every wave walks the pieces of its
+    // share of the work list in order, on its own (many small items: a
+    // wave's epilogue then overlaps the other waves' streaming).  The next
+    // piece's query and first tile are requested before this piece's
+    // epilogue, which then overlaps their latency.
+    ListCursor cur;
+    if (!list_begin(p, cur, (int)blockIdx.x * kWaves + wv, (int)gridDim.x * kWaves)) return;
+    Work w;
+    if (!list_next<QT, D>(p, BS, GP, cur, w)) return;
+    Item it = make_item(w);
+    load_query(w);
+    Tile ta, tb;
+    first_tile(it, ta, 0);
+    while (true) {
+      reset_state();
+      run_steps(it, ta, tb, 0, std::integral_constant<int, 1>{});
+      Work wn;
+      const bool more = list_next<QT, D>(p, BS, GP, cur, wn);
+      Item itn;
+      if (more) {
+        itn = make_item(wn);
+        load_query(wn);
+        first_tile(itn, ta, 0);
+      }
+      finish_wave(it);
+      if (!more) break;
+      it = itn;
+    }
+  } else if constexpr (LIST == 1) {
+    // Persistent, one worker per workgroup (few, large items: the four
+    // waves share each piece and merge through LDS).  Prefetch as above;
     // the barrier frees the LDS of one piece's epilogue for the next.
     ListCursor cur;
-    if (!list_begin(p, cur)) return;
+    if (!list_begin(p, cur, (int)blockIdx.x, (int)gridDim.x)) return;
     Work w;
-    while (list_next<QT, D>(p, BS, GP, cur, w)) {
-      run_item(w);
+    if (!list_next<QT, D>(p, BS, GP, cur, w)) return;
+    Item it = make_item(w);
+    load_query(w);
+    Tile ta, tb;
+    first_tile(it, ta, wv);
+    while (true) {
+      reset_state();
+      run_steps(it, ta, tb, wv, std::integral_constant<int, kWaves>{});
+      Work wn;
+      const bool more = list_next<QT, D>(p, BS, GP, cur, wn);
+      Item itn;
+      if (more) {
+        itn = make_item(wn);
+        load_query(wn);
+        first_tile(itn, ta, wv);
+      }
+      finish_item(it);
       __syncthreads();
+      if (!more) break;
+      it = itn;
     }
   } else {
     Work w;
     if (!begin_work<QT, D>(p, BS, GP, w)) return;
-    run_item(w);
+    const Item it = make_item(w);
+    load_query(w);
+    reset_state();
+    Tile ta, tb;
+    first_tile(it, ta, wv);
+    run_steps(it, ta, tb, wv, std::integral_constant<int, kWaves>{});
+    finish_item(it);
   }
 }
 

@@ -13,7 +13,7 @@ constexpr int kv_bytes_of() {
   else return (int)sizeof(KVT);
 }
 
-template <typename QT, typename KVT, int D, int BS, int GP, bool LIST>
+template <typename QT, typename KVT, int D, int BS, int GP, int LIST>
 hipError_t launch_valu_list(const Params &p, const Launch &l) {
   const bool win = p.window_left >= 0;
   if (p.cap_on)
@@ -28,8 +28,9 @@ hipError_t launch_valu_list(const Params &p, const Launch &l) {
 template <typename QT, typename KVT, int D, int BS, int GP>
 hipError_t launch_valu_one(const Params &p, const Launch &l) {
   if constexpr (GP <= valu_max_group(kv_bytes_of<QT, KVT>(), D, BS)) {
-    return p.mode == kModeList ? launch_valu_list<QT, KVT, D, BS, GP, true>(p, l)
-                               : launch_valu_list<QT, KVT, D, BS, GP, false>(p, l);
+    if (p.mode != kModeList) return launch_valu_list<QT, KVT, D, BS, GP, 0>(p, l);
+    return p.list_wave ? launch_valu_list<QT, KVT, D, BS, GP, 2>(p, l)
+                       : launch_valu_list<QT, KVT, D, BS, GP, 1>(p, l);
   } else {
     return hipErrorInvalidValue;
   }

@@ -7,10 +7,11 @@
 // 32-aligned start of its window, base_s, to its length L_s.  Its cost is the
 // memory-load model of the PoD page (FlashInfer PR #967, the work estimate
 // qo_len + 2 * page_size * kv_len, which its author describes as modelling
-// memory load rather than compute): one query row plus two rows (K and V) per
-// key, i.e., in units of a key's K and V rows, cost = keys + item_cost
-// (item_cost = 1 for the query row by default; an empty or invalid sequence
-// costs 1 + item_cost, so its output still has an owner).
+// memory load rather than compute): a per-request term plus two rows (K and
+// V) per key, i.e., in units of a key's K and V rows, cost = keys + item_cost.
+// item_cost is the per-item term (the library calibrates it to an item's
+// fixed cost); an empty or invalid sequence costs 1 + item_cost, so its
+// output still has an owner.
 //
 // Line.  The items lie end to end on a line of total length T = gx * sum_s
 // cost_s, item (s, x) at C = gx * P_s + x * cost_s with P_s the cost of the

@@ -77,7 +77,8 @@ int main() {
           if (!last) return;
           ++mergers;
           for (int j = 0; j < d; ++j)
-            out[j] = pa::lse_merge(m.data(), s.data(), k, [](float x) { return exp2f(x); },
+            out[j] = pa::lse_merge([&](int cc) { return m[cc]; }, [&](int cc) { return s[cc]; },
+                                   k, [](float x) { return exp2f(x); },
                                    [&](int cc) { return o[(size_t)cc * d + j]; });
         });
       }
