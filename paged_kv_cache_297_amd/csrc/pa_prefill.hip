@@ -217,10 +217,15 @@ __global__ void __launch_bounds__(kThreads)
   };
 
   // One step's tiles in registers: K chunks (row-major) and two keys' chunks
-  // of V; keys at or past nk are zero.
+  // of V; keys at or past nk become zero.  Every load is issued (a block past
+  // the end reads block 0, always addressable), so the stage has no branches
+  // around its loads; the zeroing waits for store_stage, where the data is
+  // consumed (a select right after a load would wait for the load there and
+  // serialise the prefetch).
   struct Stage {
     u32x4 k[NLK];
     u32x4 v[NLV][2];
+    bool kok[NLK], vok[NLV][2];
   };
   auto load_stage = [&](int base) {
     size_t boff[NB];
@@ -230,7 +235,8 @@ __global__ void __launch_bounds__(kThreads)
     for (int i = 0; i < NLK; ++i) {
       const int c = threadIdx.x + kThreads * i, key = c / CPR, ch = c % CPR;
       const size_t off = boff[key / BS] + ((key % BS) * D + ch * 8) * sizeof(QT);
-      st.k[i] = base + key < nk ? load16(kcache + off) : u32x4{0u, 0u, 0u, 0u};
+      st.k[i] = load16(kcache + off);
+      st.kok[i] = base + key < nk;
     }
 #pragma unroll
     for (int i = 0; i < NLV; ++i) {
@@ -239,9 +245,11 @@ __global__ void __launch_bounds__(kThreads)
       const int key = 2 * kp;  // keys key, key + 1: one block (block sizes are even)
       const size_t off = boff[key / BS] + ((key % BS) * D + ch * 8) * sizeof(QT);
       st.v[i][0] = st.v[i][1] = u32x4{0u, 0u, 0u, 0u};
+      st.vok[i][0] = base + key < nk;
+      st.vok[i][1] = base + key + 1 < nk;
       if (c < VTASKS) {
-        if (base + key < nk) st.v[i][0] = load16(vcache + off);
-        if (base + key + 1 < nk) st.v[i][1] = load16(vcache + off + D * sizeof(QT));
+        st.v[i][0] = load16(vcache + off);
+        st.v[i][1] = load16(vcache + off + D * sizeof(QT));
       }
     }
     return st;
@@ -250,15 +258,18 @@ __global__ void __launch_bounds__(kThreads)
 #pragma unroll
     for (int i = 0; i < NLK; ++i) {
       const int c = threadIdx.x + kThreads * i, key = c / CPR, ch = c % CPR;
-      *reinterpret_cast<u32x4 *>(&sk[key][ch * 8]) = st.k[i];
+      *reinterpret_cast<u32x4 *>(&sk[key][ch * 8]) =
+          st.kok[i] ? st.k[i] : u32x4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
     for (int i = 0; i < NLV; ++i) {
       const int c = threadIdx.x + kThreads * i;
       const int kp = c % (kPrefillStep / 2), ch = c / (kPrefillStep / 2);
       if (c < VTASKS) {
-        const unsigned a[4] = {st.v[i][0].x, st.v[i][0].y, st.v[i][0].z, st.v[i][0].w};
-        const unsigned b[4] = {st.v[i][1].x, st.v[i][1].y, st.v[i][1].z, st.v[i][1].w};
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        const u32x4 va = st.vok[i][0] ? st.v[i][0] : z, vb = st.vok[i][1] ? st.v[i][1] : z;
+        const unsigned a[4] = {va.x, va.y, va.z, va.w};
+        const unsigned b[4] = {vb.x, vb.y, vb.z, vb.w};
         // Dim e of the two keys as one dword: the 16-bit halves e % 2 of
         // word e / 2 of each key (byte permute: bytes 0-3 from a, 4-7 from b).
 #pragma unroll
@@ -459,12 +470,13 @@ __global__ void __launch_bounds__(kThreads)
     const float l_tot = xor_sum<32>(xor_sum<16>(l_run[j]));
     if (!col_ok[j]) continue;
     QT *row = out + ((size_t)(q_begin + tok[j]) * p.num_heads + head[j]) * D;
+    // One reciprocal per column (the output is rounded to 16 bits).
+    const float inv = nan_out ? __builtin_nanf("") : (l_tot > 0.0f ? 1.0f / l_tot : 0.0f);
 #pragma unroll
     for (int t = 0; t < NDT; ++t) {
       float o[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        o[e] = nan_out ? __builtin_nanf("") : (l_tot > 0.0f ? oacc[j][t][e] / l_tot : 0.0f);
+      for (int e = 0; e < 4; ++e) o[e] = oacc[j][t][e] * inv;
       *reinterpret_cast<u32x2 *>(row + 16 * t + 4 * g) =
           u32x2{pack2(o[0], o[1], QT()), pack2(o[2], o[3], QT())};
     }
