@@ -73,15 +73,68 @@ constexpr float kLazyRescale = 8.0f;
 // column tile per wave; with two, three when the query tile is in LDS (two
 // for head size 128 with 32-token blocks, which would spill at three), else
 // two.
-template <int NT, int D, int BS>
+template <int NT, int D, int BS, bool RING>
 constexpr int prefill_waves_per_eu() {
-  if constexpr (NT == 1) return 3;
+  if constexpr (RING) return D == 64 ? 4 : 3;
+  else if constexpr (NT == 1) return 3;
   else return (PA_PREFILL_Q_LDS && !(D == 128 && BS == 32)) ? 3 : 2;
 }
 
-template <typename QT, int D, int BS, int NT, bool CAP>
+// Geometry of the ring form: K and V tiles loaded by direct-to-LDS loads
+// (global_load_lds_dwordx4: lane l of a wave writes its 16 bytes at
+// M0 + 16 l), three stages deep.  One load moves 1 KB, KPI whole key rows;
+// lane l fetches chunk l / KPI (8 dims) of key l % KPI, so within the load
+// the 16-byte chunks are stored chunk-major: (key j, chunk c) at
+// 16 (KPI c + j).  Loads sit IB = 1 KB + PAD apart.  With that layout
+//   - a QK operand read (16 lanes: keys n = 0..15, one chunk) touches 16
+//     distinct 16-byte bank groups (the pad shifts successive loads by a
+//     quarter or half of the banks), and
+//   - a transposing read of V (16 lanes: four keys x four 4-dim pieces)
+//     touches 16 distinct 8-byte bank pairs,
+// and both have per-lane bases with compile-time offsets for the k-step,
+// the 16-key sub-tile, the 16-dim output tile and the 4-key half.
+template <int D>
+struct PrefillRing {
+  static constexpr int ROWB = D * 2;                    // bytes of one key row
+  static constexpr int KPI = 1024 / ROWB;               // keys per load (4 or 8)
+  static constexpr int PAD = D == 128 ? 64 : 128;
+  static constexpr int IB = 1024 + PAD;                 // LDS bytes per load
+  static constexpr int NI = kPrefillStep / KPI;         // loads per tile and step
+  static constexpr int IPW = NI / kWaves;               // ... per wave
+  static constexpr int TILE = NI * IB;                  // one K (or V) tile
+  static constexpr int STAGE = 2 * TILE;                // K tile, then V tile
+  static constexpr int NSTAGE = 3;
+  static constexpr int BYTES = NSTAGE * STAGE;
+  static_assert(IPW >= 1 && IPW * kWaves == NI, "whole loads per wave");
+  static_assert(KPI == 4 || KPI == 8, "16-bit rows of 64 or 128 dims");
+};
+
+// s_waitcnt immediate that waits until at most n vector memory operations
+// of the wave are outstanding (LDS and export counts left alone).
+constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
+
+// Address of a __shared__ object in the LDS aperture.
+__device__ __forceinline__ unsigned lds_addr(const void *p) {
+  return (unsigned)(size_t)(const __attribute__((address_space(3))) char *)p;
+}
+
+// One direct-to-LDS load: 16 bytes from each lane's address to LDS address
+// lds + 16 * lane (lds uniform; M0 must hold it one wait state before the
+// load).  Issued from asm so that the compiler does not track it: given LDS
+// addresses that differ only at run time (the ring stage), it would
+// otherwise wait for every load in flight before each LDS read, the
+// prefetched stages included.  The load has no result register; the ring's
+// own s_waitcnt vmcnt waits order every read of its data.
+__device__ __forceinline__ void lds_dma16(const void *src, unsigned lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(src), "s"(lds)
+               : "memory", "m0");
+}
+
+template <typename QT, int D, int BS, int NT, bool CAP, bool RING>
 __global__ void __launch_bounds__(kThreads)
-    __attribute__((amdgpu_waves_per_eu(prefill_waves_per_eu<NT, D, BS>())))
+    __attribute__((amdgpu_waves_per_eu(prefill_waves_per_eu<NT, D, BS, RING>())))
     pa_prefill_kernel(const PrefillParams p) {
   // NT: 16-column MFMA tiles per wave
   constexpr int NKS = D / 32;                  // 32-dim k-steps of QK^T
@@ -98,13 +151,15 @@ __global__ void __launch_bounds__(kThreads)
   static_assert(VTASKS % kThreads == 0 || VTASKS < kThreads, "V tile geometry");
   static_assert(kPrefillStep % BS == 0, "a step covers whole blocks");
 
-  __shared__ __attribute__((aligned(16))) QT sk[kPrefillStep][KP];
-  __shared__ __attribute__((aligned(16))) QT sv[D][VP];
+  using RG = PrefillRing<D>;
+  __shared__ __attribute__((aligned(16))) QT sk[RING ? 1 : kPrefillStep][RING ? 8 : KP];
+  __shared__ __attribute__((aligned(16))) QT sv[RING ? 1 : D][RING ? 8 : VP];
+  __shared__ __attribute__((aligned(1024))) char ring[RING ? RG::BYTES : 16];
   __shared__ int sm_bad;
   // Query tile of the two-tile form: row = column of the workgroup, D / 8
   // 16-byte chunks per row, chunk c stored at c ^ qswz(row) so that the 16
   // rows one operand read touches fall on distinct bank groups.
-  constexpr bool kQLds = PA_PREFILL_Q_LDS && NT == 2;
+  constexpr bool kQLds = !RING && PA_PREFILL_Q_LDS && NT == 2;
   constexpr int QCOLS = 16 * NT * kWaves;
   constexpr int QCH = D / 8;
   __shared__ __attribute__((aligned(16))) QT sq[kQLds ? QCOLS : 1][kQLds ? D : 8];
@@ -290,7 +345,14 @@ __global__ void __launch_bounds__(kThreads)
     for (int t = 0; t < NDT; ++t) oacc[j][t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   }
 
-  auto compute = [&](int base) {
+  // Ring form, per lane: base of the QK operand reads (key n % 16 of a
+  // sub-tile, chunk g of a k-step) and of the transposing V reads (lane
+  // 4 j + q of group g names key 8 (g ^ 1) + j, dims 4 q of a 16-dim tile).
+  const int koff = (n / RG::KPI) * RG::IB + 16 * (RG::KPI * g + n % RG::KPI);
+  const int voff = ((8 * (g ^ 1)) / RG::KPI) * RG::IB + 16 * RG::KPI * ((n >> 1) & 1) +
+                   16 * (n >> 2) + 8 * (n & 1);
+  auto compute = [&](int base, const char *kst) {
+    (void)kst;
     // Every valid column of the wave sees the whole step: no masks needed.
     bool inside = true;
 #pragma unroll
@@ -317,7 +379,10 @@ __global__ void __launch_bounds__(kThreads)
       }
 #pragma unroll
       for (int h = 0; h < NSUB; ++h) {
-        const u32x4 a = *reinterpret_cast<const u32x4 *>(&sk[16 * h + n][32 * ks + 8 * g]);
+        const u32x4 a =
+            RING ? *reinterpret_cast<const u32x4 *>(kst + koff + h * (16 / RG::KPI) * RG::IB +
+                                                    64 * RG::KPI * ks)
+                 : *reinterpret_cast<const u32x4 *>(&sk[16 * h + n][32 * ks + 8 * g]);
 #pragma unroll
         for (int j = 0; j < NT; ++j) sc[j][h] = mfma_qk(a, qv[j], sc[j][h], QT());
       }
@@ -403,8 +468,16 @@ __global__ void __launch_bounds__(kThreads)
     for (int t = 0; t < NDT; ++t) {
 #pragma unroll
       for (int hf = 0; hf < NHALF; ++hf) {
-        const u32x4 va =
-            *reinterpret_cast<const u32x4 *>(&sv[16 * t + n][32 * hf + 8 * (g ^ 1)]);
+        u32x4 va;
+        if constexpr (RING) {
+          const char *rd =
+              kst + RG::TILE + voff + hf * (32 / RG::KPI) * RG::IB + 32 * RG::KPI * t;
+          const u32x2 lo = lds_read_tr16(rd);
+          const u32x2 hi = lds_read_tr16(rd + (RG::KPI == 4 ? RG::IB : 64));
+          va = u32x4{lo.x, lo.y, hi.x, hi.y};
+        } else {
+          va = *reinterpret_cast<const u32x4 *>(&sv[16 * t + n][32 * hf + 8 * (g ^ 1)]);
+        }
 #pragma unroll
         for (int j = 0; j < NT; ++j) oacc[j][t] = mfma_pv(va, pop[j][hf], oacc[j][t], QT());
       }
@@ -418,7 +491,82 @@ __global__ void __launch_bounds__(kThreads)
   // two-buffer, one-barrier pipeline measured slower: the second buffer
   // cost occupancy.)
   int base = (int)(lo - lo % BS);  // steps start on a block boundary: earlier blocks are never read
-  if constexpr (NT == 1) {
+  if constexpr (RING) {
+    // Three stages, one barrier per step: at step s the loads of s and
+    // s + 1 are in flight; the wave waits for its own loads of s, the
+    // barrier publishes everyone's and frees stage s - 1 (every wave has
+    // consumed its reads of it), the loads of s + 2 go into that stage, and
+    // step s is computed.  The barrier is bracketed by compiler-only
+    // fences: a memory fence would make the compiler wait for every load in
+    // flight, the prefetched stages included.
+    const int n_steps = base < hi ? (int)((hi - base + kPrefillStep - 1) / kPrefillStep) : 0;
+    // Lane l of a load fetches chunk l / KPI of key l % KPI of a 1 KB run of
+    // KPI keys; a wave's IPW loads cover 8 consecutive keys of one block.
+    const int loff = (lane % RG::KPI) * RG::ROWB + 16 * (lane / RG::KPI);
+    const int kb0 = wv * RG::IPW * RG::KPI;
+    auto issue = [&](int sbase, char *st) {
+      int phys = 0;
+      if (sbase + kb0 < nk) {
+        phys = btab[(sbase + kb0) / BS];
+        if (phys < 0 || phys >= p.num_blocks) {
+          poisoned = true;
+          phys = 0;
+        }
+      }
+      const size_t blk = (size_t)phys * blk_stride + head_off + (size_t)(kb0 % BS) * RG::ROWB;
+#pragma unroll
+      for (int ii = 0; ii < RG::IPW; ++ii) {
+        const int i = wv * RG::IPW + ii;
+        const unsigned lds = lds_addr(st) + i * RG::IB;
+        lds_dma16(kcache + blk + 1024 * ii + loff, __builtin_amdgcn_readfirstlane(lds));
+        lds_dma16(vcache + blk + 1024 * ii + loff,
+                  __builtin_amdgcn_readfirstlane(lds + RG::TILE));
+      }
+    };
+    // The stage of step s is s % 3, kept as a byte offset in a scalar.
+    int cur_off = 0;
+    if (n_steps > 0) issue(base, ring);
+    // A use of the query registers here makes the compiler wait for the
+    // query loads (and with them stage 0, needed first anyway) before the
+    // loop, inside which it then has no load of its own to wait for.
+#pragma unroll
+    for (int j = 0; j < NT; ++j)
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) asm volatile("" : "+v"(qop[j][ks]));
+    if (n_steps > 1) issue(base + kPrefillStep, ring + RG::STAGE);
+    for (int s = 0; s < n_steps; ++s) {
+      if (s + 1 < n_steps)
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * RG::IPW));
+      else
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      const int ahead_off = cur_off == 0 ? 2 * RG::STAGE : cur_off - RG::STAGE;
+      if (s + 2 < n_steps) issue(base + kPrefillStep * (s + 2), ring + ahead_off);
+      const int sbase = base + kPrefillStep * s;
+      char *const cur = ring + cur_off;
+      if (sbase + kPrefillStep > nk) {
+        // The step runs past the last key: those rows hold whatever the
+        // cache holds there, and a zero weight times a NaN is NaN, so their
+        // V rows are zeroed before anyone reads the stage.
+        char *vt = cur + RG::TILE;
+        for (int c = threadIdx.x; c < kPrefillStep * (D / 8); c += kThreads) {
+          const int key = c / (D / 8), ch = c % (D / 8);
+          if (sbase + key >= nk)
+            *reinterpret_cast<u32x4 *>(vt + (key / RG::KPI) * RG::IB +
+                                       16 * (RG::KPI * ch + key % RG::KPI)) =
+                u32x4{0u, 0u, 0u, 0u};
+        }
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the stores are done
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+      }
+      compute(sbase, cur);
+      cur_off = cur_off == 2 * RG::STAGE ? 0 : cur_off + RG::STAGE;
+    }
+  } else if constexpr (NT == 1) {
     // With one column tile the registers allow a second stage: loads run
     // two steps ahead (the last step's loads repeat it, so every load is
     // issued and each wait covers only the stage it needs).
@@ -431,13 +579,13 @@ __global__ void __launch_bounds__(kThreads)
       __syncthreads();
       for (int s = 0;; s += 2) {
         sa = load_stage(step_base(s + 2));
-        compute(base + kPrefillStep * s);
+        compute(base + kPrefillStep * s, nullptr);
         __syncthreads();
         if (s + 1 >= n_steps) break;
         store_stage(sb);  // step s + 1
         __syncthreads();
         sb = load_stage(step_base(s + 3));
-        compute(base + kPrefillStep * (s + 1));
+        compute(base + kPrefillStep * (s + 1), nullptr);
         __syncthreads();
         if (s + 2 >= n_steps) break;
         store_stage(sa);  // step s + 2
@@ -452,7 +600,7 @@ __global__ void __launch_bounds__(kThreads)
       for (; base < hi; base += kPrefillStep) {
         const bool more = base + kPrefillStep < hi;
         if (more) st = load_stage(base + kPrefillStep);
-        compute(base);
+        compute(base, nullptr);
         __syncthreads();
         if (more) {
           store_stage(st);
@@ -483,13 +631,19 @@ __global__ void __launch_bounds__(kThreads)
   }
 }
 
+template <typename QT, int D, int BS, bool RING>
+static hipError_t launch_prefill_form(const PrefillParams &p, bool cap, const Launch &l) {
+  if (p.tiles_per_wave == 2)
+    return cap ? launch_kernel(pa_prefill_kernel<QT, D, BS, 2, true, RING>, l, p)
+               : launch_kernel(pa_prefill_kernel<QT, D, BS, 2, false, RING>, l, p);
+  return cap ? launch_kernel(pa_prefill_kernel<QT, D, BS, 1, true, RING>, l, p)
+             : launch_kernel(pa_prefill_kernel<QT, D, BS, 1, false, RING>, l, p);
+}
+
 template <typename QT, int D, int BS>
 static hipError_t launch_prefill_bs(const PrefillParams &p, bool cap, const Launch &l) {
-  if (p.tiles_per_wave == 2)
-    return cap ? launch_kernel(pa_prefill_kernel<QT, D, BS, 2, true>, l, p)
-               : launch_kernel(pa_prefill_kernel<QT, D, BS, 2, false>, l, p);
-  return cap ? launch_kernel(pa_prefill_kernel<QT, D, BS, 1, true>, l, p)
-             : launch_kernel(pa_prefill_kernel<QT, D, BS, 1, false>, l, p);
+  return p.ring ? launch_prefill_form<QT, D, BS, true>(p, cap, l)
+                : launch_prefill_form<QT, D, BS, false>(p, cap, l);
 }
 
 template <typename QT>
