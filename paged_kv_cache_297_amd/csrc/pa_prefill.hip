@@ -54,6 +54,18 @@ __device__ __forceinline__ void prefill_item(int &bx, int &by, int &bz) {
 #endif
 }
 
+// Sum of the two 16-bit values of a packed word, added to c in fp32.
+__device__ __forceinline__ float dot2_sum(unsigned w, float c, __bf16) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w),
+                                         __builtin_bit_cast(bf16x2, 0x3f803f80u), c, false);
+}
+__device__ __forceinline__ float dot2_sum(unsigned w, float c, _Float16) {
+  typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w),
+                                __builtin_bit_cast(f16x2, 0x3c003c00u), c, false);
+}
+
 // Lazy rescaling of the running softmax state: a column keeps its reference
 // max until the running max rises by more than this (log2 units), so its
 // weights exp2(s - m_ref) stay at most 2^8 (exact in the 16-bit P operands
@@ -388,37 +400,76 @@ __global__ void __launch_bounds__(kThreads)
       }
     }
     u32x4 pop[NT][NHALF];
-    float alpha[NT];
-#pragma unroll
-    for (int j = 0; j < NT; ++j) {
-      float psum = 0.0f;
+    // P of column tile j from its logits (x = log2-domain logit, or the raw
+    // dot product when RAW): weights exp2(x - m_run), rounded to the 16-bit
+    // P operand; l_run accumulates the rounded weights (the ones the PV
+    // product uses), two at a time with a dot product against (1, 1).
+    auto make_p = [&](int j, auto raw, const float (&x)[NSUB][4]) {
       u32x2 pk[NSUB];
-      if (!CAP && full) {
-        // Every key visible and no cap: the max of the raw dot products
-        // scaled once, and each weight one fma and one exp2.
-        float bm = -__builtin_inff();
+#pragma unroll
+      for (int h = 0; h < NSUB; ++h) {
+        float pe[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if constexpr (decltype(raw)::value)
+            pe[e] = fast_exp2(fmaf(x[h][e], p.scale_log2, -m_run[j]));
+          else
+            pe[e] = x[h][e] == -__builtin_inff() ? 0.0f : fast_exp2(x[h][e] - m_run[j]);
+        }
+        pk[h] = u32x2{pack2(pe[0], pe[1], QT()), pack2(pe[2], pe[3], QT())};
+        l_run[j] = dot2_sum(pk[h].x, dot2_sum(pk[h].y, l_run[j], QT()), QT());
+      }
+#pragma unroll
+      for (int hf = 0; hf < NHALF; ++hf) pop[j][hf] = regroup_p(pk[2 * hf], pk[2 * hf + 1]);
+    };
+    // Moves column j's reference to bm when bm exceeds it by more than the
+    // lazy margin, rescaling its sum and accumulators (m_run = -inf always
+    // moves for a finite bm: alpha 0, and l_run and oacc are 0).  Returns
+    // whether it moved.
+    auto move_ref = [&](int j, float bm) {
+      const bool move = bm > m_run[j] + kLazyRescale;
+      const float alpha = move ? fast_exp2(m_run[j] - bm) : 1.0f;
+      m_run[j] = move ? bm : m_run[j];
+      l_run[j] *= alpha;
+      return alpha;
+    };
+    float alpha[NT];
+    if (!CAP && full) {
+      // Every key visible and no cap: the logits are the raw dot products
+      // scaled once.  Each lane first checks its own logits of each column
+      // against the column's reference; only when some lane's exceed it by
+      // more than the margin (the first steps, then rarely) does the wave
+      // take the column max across lanes and move references.
+      float lm[NT];
+      bool need = false;
+#pragma unroll
+      for (int j = 0; j < NT; ++j) {
+        float v = -__builtin_inff();
 #pragma unroll
         for (int h = 0; h < NSUB; ++h)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) bm = fmaxf(bm, sc[j][h][e]);
-        bm = xor_max<32>(xor_max<16>(bm)) * p.scale_log2;
-        // Every key is visible, so bm is finite; m_run = -inf always moves
-        // (alpha 0: l_run and oacc are 0).
-        const bool move = bm > m_run[j] + kLazyRescale;
-        const float m_ref = move ? bm : m_run[j];
-        alpha[j] = move ? fast_exp2(m_run[j] - bm) : 1.0f;
-        m_run[j] = m_ref;
+          for (int e = 0; e < 4; ++e) v = fmaxf(v, sc[j][h][e]);
+        lm[j] = v * p.scale_log2;
+        need |= lm[j] > m_run[j] + kLazyRescale;
+      }
 #pragma unroll
-        for (int h = 0; h < NSUB; ++h) {
-          float pe[4];
+      for (int j = 0; j < NT; ++j) alpha[j] = 1.0f;
+      if (__any(need)) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            pe[e] = fast_exp2(fmaf(sc[j][h][e], p.scale_log2, -m_ref));
-            psum += pe[e];
-          }
-          pk[h] = u32x2{pack2(pe[0], pe[1], QT()), pack2(pe[2], pe[3], QT())};
-        }
-      } else {
+        for (int j = 0; j < NT; ++j) alpha[j] = move_ref(j, xor_max<32>(xor_max<16>(lm[j])));
+      }
+#pragma unroll
+      for (int j = 0; j < NT; ++j) {
+        float x[NSUB][4];
+#pragma unroll
+        for (int h = 0; h < NSUB; ++h)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) x[h][e] = sc[j][h][e];
+        make_p(j, std::true_type(), x);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < NT; ++j) {
         float x[NSUB][4];
         float bm = -__builtin_inff();
 #pragma unroll
@@ -430,29 +481,12 @@ __global__ void __launch_bounds__(kThreads)
             x[h][e] = (full || (t >= vlo[j] && t < vhi[j])) ? v : -__builtin_inff();
             bm = fmaxf(bm, x[h][e]);
           }
-        bm = xor_max<32>(xor_max<16>(bm));
-        // bm = -inf (nothing visible yet) never moves the reference; a finite
-        // bm over m_run = -inf always does.
-        const bool move = bm > m_run[j] + kLazyRescale;
-        const float m_ref = move ? bm : m_run[j];
-        alpha[j] = move ? fast_exp2(m_run[j] - bm) : 1.0f;
-        m_run[j] = m_ref;
-#pragma unroll
-        for (int h = 0; h < NSUB; ++h) {
-          float pe[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            pe[e] = x[h][e] == -__builtin_inff() ? 0.0f : fast_exp2(x[h][e] - m_ref);
-            psum += pe[e];
-          }
-          pk[h] = u32x2{pack2(pe[0], pe[1], QT()), pack2(pe[2], pe[3], QT())};
-        }
+        // bm = -inf (nothing visible yet) never moves the reference.
+        alpha[j] = move_ref(j, xor_max<32>(xor_max<16>(bm)));
+        make_p(j, std::false_type(), x);
       }
-      l_run[j] = l_run[j] * alpha[j] + psum;
-#pragma unroll
-      for (int hf = 0; hf < NHALF; ++hf) pop[j][hf] = regroup_p(pk[2 * hf], pk[2 * hf + 1]);
     }
-    // Rescale the accumulators only when some column's max moved.
+    // Rescale the accumulators only when some column's reference moved.
     bool same = true;
 #pragma unroll
     for (int j = 0; j < NT; ++j) same &= alpha[j] == 1.0f;
