@@ -75,6 +75,7 @@ __device__ __forceinline__ float dot2_sum(unsigned w, float c, _Float16) {
 // any reference.
 constexpr float kLazyRescale = 8.0f;
 
+
 // Two-tile form: the query tile lives in LDS (read per step) instead of in
 // registers, which frees the 32 VGPRs that keep it at two waves per SIMD.
 #ifndef PA_PREFILL_Q_LDS
@@ -357,20 +358,35 @@ __global__ void __launch_bounds__(kThreads)
     for (int t = 0; t < NDT; ++t) oacc[j][t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   }
 
-  // Ring form, per lane: base of the QK operand reads (key n % 16 of a
-  // sub-tile, chunk g of a k-step) and of the transposing V reads (lane
-  // 4 j + q of group g names key 8 (g ^ 1) + j, dims 4 q of a 16-dim tile).
+  // Ring form, per lane: base of the QK operand reads (key n of a 16-key
+  // sub-tile, chunk g of a k-step) and of the transposing V reads.  The PV
+  // product pairs contraction index 8 g + 4 r + m of lane group g with key
+  // 16 r + 4 g + m of the 32-key slice: exactly the keys whose weights the
+  // lane holds from the QK product (rows 4 g + m of sub-tile r), so P is
+  // used as computed, with no lane exchange.  In a transposing read, lane
+  // 4 m + x of group g names key 16 r + 4 g + m, dims 4 x of a 16-dim tile.
   const int koff = (n / RG::KPI) * RG::IB + 16 * (RG::KPI * g + n % RG::KPI);
-  const int voff = ((8 * (g ^ 1)) / RG::KPI) * RG::IB + 16 * RG::KPI * ((n >> 1) & 1) +
-                   16 * (n >> 2) + 8 * (n & 1);
+  const int vkey = 4 * g + (n >> 2);
+  const int voff = (vkey / RG::KPI) * RG::IB + 16 * (RG::KPI * ((n >> 1) & 1) + vkey % RG::KPI) +
+                   8 * (n & 1);
+  // The keys every valid column of the wave sees: [full_lo, full_hi)
+  // (wave-uniform; a wave without valid columns sees everything).
+  int full_lo, full_hi;
+  {
+    int a = -1, b = 0x7fffffff;
+#pragma unroll
+    for (int j = 0; j < NT; ++j)
+      if (col_ok[j]) {
+        a = max(a, vlo[j]);
+        b = min(b, vhi[j]);
+      }
+    full_lo = wave_max32(a);
+    full_hi = -wave_max32(-b);
+  }
   auto compute = [&](int base, const char *kst) {
     (void)kst;
     // Every valid column of the wave sees the whole step: no masks needed.
-    bool inside = true;
-#pragma unroll
-    for (int j = 0; j < NT; ++j)
-      inside &= !col_ok[j] || (base >= vlo[j] && base + kPrefillStep <= vhi[j]);
-    const bool full = __all(inside);
+    const bool full = base >= full_lo && base + kPrefillStep <= full_hi;
     // S^T of every column tile; each K fragment read from LDS feeds NT MFMAs.
     f32x4 sc[NT][NSUB];
 #pragma unroll
@@ -420,7 +436,9 @@ __global__ void __launch_bounds__(kThreads)
         l_run[j] = dot2_sum(pk[h].x, dot2_sum(pk[h].y, l_run[j], QT()), QT());
       }
 #pragma unroll
-      for (int hf = 0; hf < NHALF; ++hf) pop[j][hf] = regroup_p(pk[2 * hf], pk[2 * hf + 1]);
+      for (int hf = 0; hf < NHALF; ++hf)
+        pop[j][hf] = RING ? u32x4{pk[2 * hf].x, pk[2 * hf].y, pk[2 * hf + 1].x, pk[2 * hf + 1].y}
+                          : regroup_p(pk[2 * hf], pk[2 * hf + 1]);
     };
     // Moves column j's reference to bm when bm exceeds it by more than the
     // lazy margin, rescaling its sum and accumulators (m_run = -inf always
@@ -507,7 +525,7 @@ __global__ void __launch_bounds__(kThreads)
           const char *rd =
               kst + RG::TILE + voff + hf * (32 / RG::KPI) * RG::IB + 32 * RG::KPI * t;
           const u32x2 lo = lds_read_tr16(rd);
-          const u32x2 hi = lds_read_tr16(rd + (RG::KPI == 4 ? RG::IB : 64));
+          const u32x2 hi = lds_read_tr16(rd + (16 / RG::KPI) * RG::IB);
           va = u32x4{lo.x, lo.y, hi.x, hi.y};
         } else {
           va = *reinterpret_cast<const u32x4 *>(&sv[16 * t + n][32 * hf + 8 * (g ^ 1)]);
