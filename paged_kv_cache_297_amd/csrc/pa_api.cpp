@@ -845,6 +845,10 @@ pa_status paged_prefill(void *out, const void *query, const void *key_cache,
   if (tiles > 0x7fffffffLL) return PA_ERR_BAD_SHAPE;
   p.num_q_tiles = (int)tiles;
   p.causal = o.causal ? 1 : 0;
+  // Tile-major order when the tiles' costs differ widely: causal, with
+  // fewer than twice as many keys as queries (tile t of a prompt sees the
+  // prefix plus t + 1 tiles of keys, so costs span more than 2:1).
+  p.tile_major = (o.causal && (long long)max_seq_k < 2LL * max_seq_q) ? 1 : 0;
   p.window_left = o.window_left;
   p.window_right = o.window_right;
   p.scale_log2 = scale * 1.4426950408889634f;

@@ -26,30 +26,60 @@ namespace pa {
 
 // Workgroups are handed to the 8 XCDs (each with its own L2) round-robin in
 // launch order.  With PA_PREFILL_XCD_MAP the launch index is remapped so that
-// XCD k runs the k-th eighth of the (query tile, KV head, sequence) items in
-// grid order: the query tiles of one (sequence, KV head), which all read the
-// same keys and values, share one L2.
+// each XCD owns a fixed set of (sequence, KV head) pairs, whose query tiles
+// read the same keys and values and then share one L2.  It runs them in one
+// of two orders (p.tile_major, set by the host):
+//   - pair-major: one pair's tiles (heaviest first), then the next pair's,
+//     so that few pairs' keys and values are in flight at once -- for
+//     batches whose tiles cost about the same (chunked prefill: every tile
+//     sees the whole prefix);
+//   - tile-major: the heaviest tiles of all its pairs first -- for causal
+//     batches whose tiles' costs differ widely (a fresh prompt's tile t sees
+//     t + 1 steps), where pair-major leaves the last pair's longest tiles
+//     for the end: a list-scheduling model of 8 pairs x 64 such tiles on 96
+//     slots gives 14% over the ideal makespan pair-major, 2.4% tile-major
+//     (measured on MI355X: 8 fresh 2048-token prompts 0.333 -> 0.317 ms; the
+//     chunked batch, tile-major, 1.05 -> 1.19 ms from L2 misses).
+// With a pair count not divisible by 8, tile-major ignores the XCDs.
 #ifndef PA_PREFILL_XCD_MAP
 #define PA_PREFILL_XCD_MAP 1
 #endif
 constexpr int kXcds = 8;
 
-__device__ __forceinline__ void prefill_item(int &bx, int &by, int &bz) {
+// (bx, by, bz) = (tile rank from the heaviest, KV head, sequence).
+__device__ __forceinline__ void prefill_item(const PrefillParams &p, int &bx, int &by, int &bz) {
   bx = blockIdx.x;
   by = blockIdx.y;
   bz = blockIdx.z;
 #if PA_PREFILL_XCD_MAP
-  // A bijection on [0, whole): launch lin = 8 s + k (XCD k, round s) runs
-  // item k * whole / 8 + s.
   const unsigned long long gx = gridDim.x, gy = gridDim.y;
-  const unsigned long long total = gx * gy * gridDim.z;
+  const unsigned long long pairs = gy * gridDim.z;
+  const unsigned long long total = gx * pairs;
   const unsigned long long lin = bx + gx * (by + gy * bz);
-  const unsigned long long whole = total - total % kXcds;  // the rest keep their place
-  if (lin < whole) {
-    const unsigned long long item = (lin % kXcds) * (whole / kXcds) + lin / kXcds;
-    bx = (int)(item % gx);
-    by = (int)((item / gx) % gy);
-    bz = (int)(item / (gx * gy));
+  if (p.tile_major) {
+    unsigned long long rank, pair;
+    if (pairs % kXcds == 0) {
+      // Launch lin = 8 s + k runs on XCD k as its s-th workgroup.
+      const unsigned long long per = pairs / kXcds, k = lin % kXcds, s = lin / kXcds;
+      rank = s / per;
+      pair = k * per + s % per;
+    } else {
+      rank = lin / pairs;
+      pair = lin % pairs;
+    }
+    bx = (int)rank;
+    by = (int)(pair % gy);
+    bz = (int)(pair / gy);
+  } else {
+    // A bijection on [0, whole): launch lin = 8 s + k (XCD k, round s) runs
+    // item k * whole / 8 + s in (tile, KV head, sequence) order.
+    const unsigned long long whole = total - total % kXcds;  // the rest keep their place
+    if (lin < whole) {
+      const unsigned long long item = (lin % kXcds) * (whole / kXcds) + lin / kXcds;
+      bx = (int)(item % gx);
+      by = (int)((item / gx) % gy);
+      bz = (int)(item / (gx * gy));
+    }
   }
 #endif
 }
@@ -179,7 +209,7 @@ __global__ void __launch_bounds__(kThreads)
   auto qswz = [](int row) { return QCH == 16 ? (row & 15) : ((row >> 1) & 7); };
 
   int bx, by, bz;
-  prefill_item(bx, by, bz);
+  prefill_item(p, bx, by, bz);
   const int tile = p.num_q_tiles - 1 - bx;  // latest (heaviest) tiles first
   const int kvh = by, seq = bz;
   const int q_begin = p.cu_seq_q[seq], q_end = p.cu_seq_q[seq + 1];
