@@ -388,15 +388,27 @@ __global__ void __launch_bounds__(kThreads)
     for (int t = 0; t < NDT; ++t) oacc[j][t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   }
 
-  // Ring form, per lane: base of the QK operand reads (key n of a 16-key
-  // sub-tile, chunk g of a k-step) and of the transposing V reads.  The PV
-  // product pairs contraction index 8 g + 4 r + m of lane group g with key
-  // 16 r + 4 g + m of the 32-key slice: exactly the keys whose weights the
-  // lane holds from the QK product (rows 4 g + m of sub-tile r), so P is
-  // used as computed, with no lane exchange.  In a transposing read, lane
-  // 4 m + x of group g names key 16 r + 4 g + m, dims 4 x of a 16-dim tile.
-  const int koff = (n / RG::KPI) * RG::IB + 16 * (RG::KPI * g + n % RG::KPI);
-  const int vkey = 4 * g + (n >> 2);
+  // Ring form, per lane: base of the QK operand reads and of the
+  // transposing V reads.  Row 4 q + e of a 16-key sub-tile h of the QK
+  // product is key 16 h + 4 tau(q) + e (tau a permutation of the four
+  // 4-key groups), and the PV product pairs contraction index 8 g + 4 r + m
+  // of lane group g with key 16 r + 4 tau(g) + m: exactly the keys whose
+  // weights the lane holds from the QK product (rows 4 g + m of sub-tile r),
+  // so P is used as computed, with no lane exchange.  In a transposing
+  // read, lane 4 m + x of group g names key 16 r + 4 tau(g) + m, dims 4 x
+  // of a 16-dim tile.  A 64-lane transposing read is served 32 lanes at a
+  // time, so lane groups 0 and 1 (and 2 and 3) must fall on disjoint banks:
+  // with 128 dims (successive loads a quarter of the banks apart) tau swaps
+  // the two bits of the group, which puts them half the banks apart; with 64
+  // dims the groups already alternate within a load.  The K reads (16 lanes
+  // at a time) stay conflict free under either.
+  auto ring_tau = [](int q) { return RG::KPI == 4 ? (((q & 1) << 1) | (q >> 1)) : q; };
+  const int krow = 4 * ring_tau(n >> 2) + (n & 3);
+  const int koff = (krow / RG::KPI) * RG::IB + 16 * (RG::KPI * g + krow % RG::KPI);
+  const int vkey = 4 * ring_tau(g) + (n >> 2);
+  // Key of element e of sub-tile h in this lane's QK output: base + 16 h +
+  // kgrp + e.
+  const int kgrp = RING ? 4 * ring_tau(g) : 4 * g;
   const int voff = (vkey / RG::KPI) * RG::IB + 16 * (RG::KPI * ((n >> 1) & 1) + vkey % RG::KPI) +
                    8 * (n & 1);
   // The keys every valid column of the wave sees: [full_lo, full_hi)
@@ -524,7 +536,7 @@ __global__ void __launch_bounds__(kThreads)
         for (int h = 0; h < NSUB; ++h)
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const int t = base + 16 * h + 4 * g + e;
+            const int t = base + 16 * h + kgrp + e;
             const float v = scaled_logit<CAP>(p, sc[j][h][e]);
             x[h][e] = (full || (t >= vlo[j] && t < vhi[j])) ? v : -__builtin_inff();
             bm = fmaxf(bm, x[h][e]);
