@@ -264,7 +264,11 @@ def bench_prefill(args) -> int:
                              wl.scale, wl.block_tables, wl.cu_seq_q, wl.cu_seq_k, wl.max_seq_q,
                              wl.max_seq_k, causal=True, stream=stream)
     lib = B.load_library()
-    for _ in range(args.warmup):
+    # At least 50 warm-up launches: the compute-bound kernel's launch time
+    # falls over its first ~40 launches as the GPU clock ramps up under load
+    # (kernel traces: 390 -> 330 us on the fresh-prompt batch).
+    warmup = max(args.warmup, 50)
+    for _ in range(warmup):
         call()
     torch.cuda.synchronize()
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
@@ -291,7 +295,7 @@ def bench_prefill(args) -> int:
     result = {
         "metric": "paged prefill attention TFLOP/s (causal), 1 MI355X",
         "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "warmup": warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None,
         "dtype": {torch.float16: "f16", torch.bfloat16: "bf16"}[wl.dtype], "data": "synthetic",
         "config": {"workload": (f"{wl.name}: paged prefill, num_seqs={wl.num_seqs}, "
