@@ -51,13 +51,13 @@ PA_HD inline float lse_merge(M m, S s, int k, Exp2 exp2_fn, LoadO load_o) {
 // The arrival of one of the k pieces of an item at the item's counter (zero
 // before its first piece arrives): true for the piece that arrives last,
 // which also resets the counter to zero, so the next call finds it zero.
-// fetch_add(ctr) adds 1 and returns the value before the addition; on the
-// device it is an agent-scope release, so every piece's partial stores are
-// ordered before its increment, and the increments form one release
-// sequence.  acquire(ctr) runs in the last piece only, before it reads
-// anything: an acquire load of the counter (on the device at agent scope),
-// which reads the last increment and so synchronises with every piece's
-// release.  store(ctr, v) writes v.
+// fetch_add(ctr) adds 1 and returns the value before the addition; its
+// caller has made the piece's partial stores visible before calling it.
+// acquire(ctr) runs in the last piece only, before it reads anything.
+// On host threads these are a release fetch-add and an acquire load (the
+// C++ memory model's form of the ordering); the device kernels pass the
+// operations that give the same ordering on gfx950 (pa_partition_common.h,
+// above coherent_store).  store(ctr, v) writes v.
 template <typename FetchAdd, typename Acquire, typename Store>
 PA_HD inline bool arrive_last(int *ctr, int k, FetchAdd fetch_add, Acquire acquire, Store store) {
   const bool last = fetch_add(ctr) == k - 1;

@@ -165,17 +165,24 @@ __device__ __forceinline__ bool begin_work(const Params &p, int block_size, int 
 
 // ---------------------------------------------------------------------------
 // Split mode: the pieces of one (sequence, grid-x slot) exchange their
-// partials through memory and an arrival counter.  Ordering: every wave
-// waits for its partial stores to complete and meets the others at a
-// workgroup barrier (workgroup-scope happens-before); thread 0 then adds 1 to
-// the counter with an agent-scope release atomic, which orders the
-// workgroup's stores before the increment; in the piece that arrives last an
-// agent-scope acquire load of the counter (it reads the last increment),
-// followed by a workgroup barrier, orders the increments of every other
-// piece before the loads of the merge.  The
-// partials themselves are stored and loaded with agent-scope relaxed atomics:
-// they write through and read past the per-XCD L2 caches, so the release
-// finds no dirty lines of them to write back.
+// partials through memory and an arrival counter.  The partials are stored
+// and loaded with agent-scope relaxed atomics, which gfx950 performs at
+// device scope (`global_store` / `global_load` with sc1: written through
+// and read past the per-XCD L2 caches).  Every wave of a piece waits for
+// its partial stores to be performed (s_waitcnt vmcnt(0)) and meets the
+// others at a barrier; then one lane adds 1 to the counter with the
+// device-scope atomic add the compiler emits for an agent-scope fetch-add.
+// The piece that reads k - 1 from it issues the merge's loads only after
+// that value has returned (they depend on it), and they read the device
+// coherence point, so they see every other piece's partials: each of those
+// was performed before that piece's increment was issued.  The HIP memory
+// model would express the same ordering as a release increment and an
+// acquire in the merging piece (PA_ARRIVE_RELEASE_ACQUIRE = 1), which
+// gfx950 lowers to an L2 writeback before every increment and an L2
+// invalidate in every merging piece: nothing for accesses that bypass the
+// L2 anyway, but they measured 2-3% on cut batches (ragged ALiBi split
+// 2134 vs 2074 us, work list 2079 vs 2037 us) and far more where many
+// items are cut, so the default relies on the device-scope accesses above.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ void coherent_store(void *ptr, unsigned v) {
   __hip_atomic_store(reinterpret_cast<unsigned *>(ptr), v, __ATOMIC_RELAXED,
@@ -209,6 +216,24 @@ __device__ __forceinline__ float coherent_load_elem(const QT *ptr) {
   }
 }
 
+// The counter operations of the arrival (the ordering is described with
+// coherent_store above).  PA_ARRIVE_RELEASE_ACQUIRE = 1: agent-scope release
+// increment and acquire load; 0 (default): relaxed increment, no acquire.
+#ifndef PA_ARRIVE_RELEASE_ACQUIRE
+#define PA_ARRIVE_RELEASE_ACQUIRE 0
+#endif
+__device__ __forceinline__ int arrive_add(int *c) {
+  return __hip_atomic_fetch_add(c, 1, PA_ARRIVE_RELEASE_ACQUIRE ? __ATOMIC_RELEASE : __ATOMIC_RELAXED,
+                                __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void arrive_acquire(int *c) {
+  if constexpr (PA_ARRIVE_RELEASE_ACQUIRE)
+    (void)__hip_atomic_load(c, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void arrive_reset(int *c, int v) {
+  __hip_atomic_store(c, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // After a piece's partials are stored (slot = piece): the piece that
 // arrives last at the (sequence, grid-x slot) counter merges the k pieces
 // with the log-sum-exp rescale of the V2 page's Phase 2, writes out, and
@@ -224,13 +249,8 @@ __device__ __forceinline__ void split_merge(const Params &p, const Work &w) {
     int *ctr = p.counters + (size_t)w.seq * p.num_heads + w.xslot;
     sm_last = arrive_last(
         ctr, w.n_part,
-        [](int *c) {
-          return __hip_atomic_fetch_add(c, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-        },
-        [](int *c) { (void)__hip_atomic_load(c, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT); },
-        [](int *c, int v) {
-          __hip_atomic_store(c, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        });
+        [](int *c) { return arrive_add(c); }, [](int *c) { arrive_acquire(c); },
+        [](int *c, int v) { arrive_reset(c, v); });
   }
   __syncthreads();
   if (!sm_last) return;
@@ -521,11 +541,10 @@ __device__ __forceinline__ void piece_stats(const Params &p, const Work &w, int 
 }
 
 // After a wave has stored its piece's partials: its arrival at the item's
-// counter (lane 0; agent-scope release increment, acquire load in the last
-// piece, as split_merge), and in the last piece the Phase 2 merge of the k
-// partials, dims across the wave's lanes.  The wavefront-scope fences order
-// the other lanes' stores before lane 0's release and lane 0's acquire
-// before the other lanes' loads.
+// counter (lane 0, as split_merge), and in the last piece the Phase 2 merge
+// of the k partials, dims across the wave's lanes.  The wavefront-scope
+// fences keep the other lanes' stores before lane 0's increment and lane
+// 0's result before the other lanes' loads.
 template <typename QT, typename TT, int D>
 __device__ __forceinline__ void piece_arrive(const Params &p, const Work &w) {
   const int lane = epi_tid() & 63;
@@ -537,13 +556,8 @@ __device__ __forceinline__ void piece_arrive(const Params &p, const Work &w) {
     int *ctr = p.counters + (size_t)w.seq * p.num_heads + w.xslot;
     last = arrive_last(
         ctr, w.n_part,
-        [](int *c) {
-          return __hip_atomic_fetch_add(c, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-        },
-        [](int *c) { (void)__hip_atomic_load(c, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT); },
-        [](int *c, int v) {
-          __hip_atomic_store(c, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        });
+        [](int *c) { return arrive_add(c); }, [](int *c) { arrive_acquire(c); },
+        [](int *c, int v) { arrive_reset(c, v); });
   }
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
