@@ -159,6 +159,28 @@ def test_prefill_blocks_outside_the_window_are_not_read():
     H.check_close(got[rows], ref, TOL, "window skips stale blocks")
 
 
+@pytest.mark.parametrize("d,bs", [(128, 16), (64, 32)])
+@pytest.mark.parametrize("opts", [dict(causal=True), dict(causal=False),
+                                  dict(causal=False, window_left=20, window_right=3)],
+                         ids=["causal", "full", "window"])
+def test_prefill_unused_slots_hold_nan(d, bs, opts):
+    """The slots of a sequence's last block past its last key hold NaN in K
+    and V (a cache's unwritten tail): the result must equal the oracle's,
+    which never reads them (a zero weight times a NaN value would be NaN)."""
+    qlens, klens = [33, 7, 100, 1, 64], [45, 7, 203, 300, 64 + bs // 2]
+    wl = W.make_prefill_workload(qlens=qlens, klens=klens, H=8, Hkv=2, D=d, bs=bs, seed=9500 + d)
+    tables = wl.block_tables.cpu().numpy()
+    for s, nk in enumerate(klens):
+        if nk % bs:
+            phys = int(tables[s, (nk - 1) // bs])
+            wl.key_cache[phys, :, nk % bs:, :] = float("nan")
+            wl.value_cache[phys, :, nk % bs:, :] = float("nan")
+    got = run(wl, **opts)
+    ref, rows = oracle(wl, **opts)
+    assert np.isfinite(got[rows]).all()
+    H.check_close(got[rows], ref, TOL, f"NaN tails D={d} bs={bs} {opts}")
+
+
 def _random_prefill(case: int) -> dict:
     rng = np.random.default_rng(30000 + case)
     n = int(rng.integers(1, 7))
