@@ -29,7 +29,6 @@ struct Tunables {
   // at 4: 274 vs 305 us); at 1 it loses (ragged batch: 2325 vs 2238 us).
   int rows_mfma_min_group = 3;
   int prefill_tiles = 0;      // prefill column tiles per wave: 0 = by shape, else 1 or 2
-  int prefill_ring = 1;       // prefill K / V staging: 1 direct-to-LDS ring, 0 through registers
   int small_batch_factor = 1; // AUTO: v2 for all if B * Hkv < factor * CUs
   int tile_factor = 2;        // AUTO: v2 iff Hkv * ceil(L/512) > factor * CUs
   int parts_reversed = 1;     // all-v2 launches dispatch the last partition first
@@ -67,7 +66,6 @@ const Tunables &tunables() {
     x.rows_mfma_min_group =
         env_int("PA_ROWS_MFMA_MIN_GROUP", x.rows_mfma_min_group, 1, 1 << 20);
     x.prefill_tiles = env_int("PA_PREFILL_TILES", x.prefill_tiles, 0, 2);
-    x.prefill_ring = env_int("PA_PREFILL_RING", x.prefill_ring, 0, 1);
     x.small_batch_factor = env_int("PA_AUTO_SMALL_BATCH_FACTOR", x.small_batch_factor, 0, 1 << 20);
     x.tile_factor = env_int("PA_AUTO_TILE_FACTOR", x.tile_factor, 0, 1 << 20);
     x.parts_reversed = env_int("PA_PARTS_REVERSED", x.parts_reversed, 0, 1);
@@ -840,7 +838,6 @@ pa_status paged_prefill(void *out, const void *query, const void *key_cache,
   if (tunables().prefill_tiles > 0 && group <= 16 * pa::kWaves)
     p.tiles_per_wave = tunables().prefill_tiles;
   p.q_tile = 16 * p.tiles_per_wave * pa::kWaves / group;
-  p.ring = tunables().prefill_ring;
   const long long tiles = ((long long)max_seq_q + p.q_tile - 1) / p.q_tile;
   if (tiles > 0x7fffffffLL) return PA_ERR_BAD_SHAPE;
   p.num_q_tiles = (int)tiles;

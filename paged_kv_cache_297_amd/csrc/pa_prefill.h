@@ -25,7 +25,6 @@ struct PrefillParams {
   int tiles_per_wave;  // 1 or 2 column tiles per wave
   int q_tile;        // query tokens per workgroup: 16 * tiles_per_wave * waves / group
   int num_q_tiles;   // ceil(max_seq_q / q_tile) = grid.x
-  int ring;          // 1: K / V through the three-stage direct-to-LDS ring
   int tile_major;    // workgroup order: 1 heaviest tiles of all pairs first, 0 pair by pair
   int causal, window_left, window_right;
   float scale_log2;  // scale * log2(e)

@@ -7,17 +7,16 @@
 //
 // A workgroup owns 64 or 128 query columns -- (query token, query head) pairs
 // of one KV head, one or two 16-column MFMA tiles per wave -- and walks the
-// keys its columns can see in steps of 32.  Each step's K and V tiles are loaded once per workgroup (the next
-// step's loads are in flight while the current step is computed) and staged
-// in LDS: K as rows, V transposed, so that both MFMA operands are 16-byte
-// LDS reads, each feeding the wave's column tiles.  Per wave, column
-// tile and step, with v_mfma_f32_16x16x32:
+// keys its columns can see in steps of 32.  Each step's K and V tiles go
+// from the cache straight into LDS with direct-to-LDS loads, through a ring
+// of three stages (one barrier per step), and feed every wave's column
+// tiles.  Per wave, column tile and step, with v_mfma_f32_16x16x32:
 //   S^T = K . Q^T   (A = 16 keys x 32 dims of K, B = 32 dims x 16 columns of
 //                    Q held in registers), two 16-key sub-tiles;
 //   masks, soft cap, online softmax per column (max / sum across the four
 //   lanes of a column);
-//   O^T += V^T . P^T (A = 16 dims x 8 keys of the transposed V, B = P regrouped
-//                    by two permlane swaps, as in the decode kernel).
+//   O^T += V^T . P^T (A = 16 dims x 8 keys of V read with the transposing LDS
+//                    read, B = P as the QK product left it in the lanes).
 #include "pa_launch_kernel.h"
 #include "pa_partition_mfma.h"
 #include "pa_prefill.h"
@@ -106,24 +105,14 @@ __device__ __forceinline__ float dot2_sum(unsigned w, float c, _Float16) {
 constexpr float kLazyRescale = 8.0f;
 
 
-// Two-tile form: the query tile lives in LDS (read per step) instead of in
-// registers, which frees the 32 VGPRs that keep it at two waves per SIMD.
-#ifndef PA_PREFILL_Q_LDS
-#define PA_PREFILL_Q_LDS 1
-#endif
-
-// Waves per SIMD the register allocator must leave room for: three with one
-// column tile per wave; with two, three when the query tile is in LDS (two
-// for head size 128 with 32-token blocks, which would spill at three), else
-// two.
-template <int NT, int D, int BS, bool RING>
+// Waves per SIMD the register allocator must leave room for: three at head
+// size 128 (three 51 KB rings fill a CU's LDS), four at 64.
+template <int D>
 constexpr int prefill_waves_per_eu() {
-  if constexpr (RING) return D == 64 ? 4 : 3;
-  else if constexpr (NT == 1) return 3;
-  else return (PA_PREFILL_Q_LDS && !(D == 128 && BS == 32)) ? 3 : 2;
+  return D == 64 ? 4 : 3;
 }
 
-// Geometry of the ring form: K and V tiles loaded by direct-to-LDS loads
+// Geometry of the ring: K and V tiles loaded by direct-to-LDS loads
 // (global_load_lds_dwordx4: lane l of a wave writes its 16 bytes at
 // M0 + 16 l), three stages deep.  One load moves 1 KB, KPI whole key rows;
 // lane l fetches chunk l / KPI (8 dims) of key l % KPI, so within the load
@@ -175,38 +164,20 @@ __device__ __forceinline__ void lds_dma16(const void *src, unsigned lds) {
                : "memory", "m0");
 }
 
-template <typename QT, int D, int BS, int NT, bool CAP, bool RING>
+template <typename QT, int D, int BS, int NT, bool CAP>
 __global__ void __launch_bounds__(kThreads)
-    __attribute__((amdgpu_waves_per_eu(prefill_waves_per_eu<NT, D, BS, RING>())))
+    __attribute__((amdgpu_waves_per_eu(prefill_waves_per_eu<D>())))
     pa_prefill_kernel(const PrefillParams p) {
   // NT: 16-column MFMA tiles per wave
   constexpr int NKS = D / 32;                  // 32-dim k-steps of QK^T
   constexpr int NDT = D / 16;                  // 16-dim output tiles
-  constexpr int KP = D + 8;                    // padded K row in LDS (elements)
-  constexpr int VP = kPrefillStep + 8;         // padded V^T row in LDS (keys)
-  constexpr int CPR = D / 8;                   // 16-byte chunks per key row
-  constexpr int NLK = kPrefillStep * CPR / kThreads;  // K chunks per thread per step
-  constexpr int VTASKS = (kPrefillStep / 2) * CPR;    // (key pair, chunk) V tasks per step
-  constexpr int NLV = (VTASKS + kThreads - 1) / kThreads;  // V tasks per thread
   constexpr int NSUB = kPrefillStep / 16;      // 16-key sub-tiles per step
   constexpr int NHALF = kPrefillStep / 32;     // 32-key P.V slices per step
-  static_assert(NLK >= 1 && NLK * kThreads == kPrefillStep * CPR, "K tile geometry");
-  static_assert(VTASKS % kThreads == 0 || VTASKS < kThreads, "V tile geometry");
   static_assert(kPrefillStep % BS == 0, "a step covers whole blocks");
 
   using RG = PrefillRing<D>;
-  __shared__ __attribute__((aligned(16))) QT sk[RING ? 1 : kPrefillStep][RING ? 8 : KP];
-  __shared__ __attribute__((aligned(16))) QT sv[RING ? 1 : D][RING ? 8 : VP];
-  __shared__ __attribute__((aligned(1024))) char ring[RING ? RG::BYTES : 16];
+  __shared__ __attribute__((aligned(1024))) char ring[RG::BYTES];
   __shared__ int sm_bad;
-  // Query tile of the two-tile form: row = column of the workgroup, D / 8
-  // 16-byte chunks per row, chunk c stored at c ^ qswz(row) so that the 16
-  // rows one operand read touches fall on distinct bank groups.
-  constexpr bool kQLds = !RING && PA_PREFILL_Q_LDS && NT == 2;
-  constexpr int QCOLS = 16 * NT * kWaves;
-  constexpr int QCH = D / 8;
-  __shared__ __attribute__((aligned(16))) QT sq[kQLds ? QCOLS : 1][kQLds ? D : 8];
-  auto qswz = [](int row) { return QCH == 16 ? (row & 15) : ((row >> 1) & 7); };
 
   int bx, by, bz;
   prefill_item(p, bx, by, bz);
@@ -265,118 +236,25 @@ __global__ void __launch_bounds__(kThreads)
   if (p.window_left >= 0) lo = max(lo, pos0 + t0 - p.window_left);
 
   // B operands of QK^T: 8 query values per lane, column tile and k-step.
-  u32x4 qop[kQLds ? 1 : NT][NKS];
-  if constexpr (kQLds) {
-    // Published by the barrier after the first K / V stage.
-    for (int ci = threadIdx.x; ci < QCOLS * QCH; ci += kThreads) {
-      const int col = ci / QCH, c = ci % QCH;
-      const int tk = t0 + col / p.group, hd = kvh * p.group + col % p.group;
-      const bool ok = col < p.q_tile * p.group && tk < t1;
-      const QT *q = reinterpret_cast<const QT *>(p.query) +
-                    ((size_t)(q_begin + (ok ? tk : t0)) * p.num_heads + hd) * D + 8 * c;
-      *reinterpret_cast<u32x4 *>(&sq[col][(c ^ qswz(col)) * 8]) =
-          ok ? load16(q) : u32x4{0u, 0u, 0u, 0u};
-    }
-  } else {
+  u32x4 qop[NT][NKS];
 #pragma unroll
-    for (int j = 0; j < NT; ++j) {
-      const QT *q = reinterpret_cast<const QT *>(p.query) +
-                    ((size_t)(q_begin + (col_ok[j] ? tok[j] : t0)) * p.num_heads + head[j]) * D;
+  for (int j = 0; j < NT; ++j) {
+    const QT *q = reinterpret_cast<const QT *>(p.query) +
+                  ((size_t)(q_begin + (col_ok[j] ? tok[j] : t0)) * p.num_heads + head[j]) * D;
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks)
-        qop[j][ks] = col_ok[j] ? load16(q + 32 * ks + 8 * g) : u32x4{0u, 0u, 0u, 0u};
-    }
+    for (int ks = 0; ks < NKS; ++ks)
+      qop[j][ks] = col_ok[j] ? load16(q + 32 * ks + 8 * g) : u32x4{0u, 0u, 0u, 0u};
   }
 
   const char *kcache = reinterpret_cast<const char *>(p.key_cache);
   const char *vcache = reinterpret_cast<const char *>(p.value_cache);
   const const_i32_ptr btab =
       as_const_table(p.block_tables + (size_t)seq * p.max_num_blocks_per_seq);
-  // A step covers NB whole blocks (it starts on a block boundary); their
-  // table entries are uniform, read once per step.  An out-of-range entry
-  // reads block 0 and poisons the workgroup's result.
-  constexpr int NB = kPrefillStep / BS;
+  // An out-of-range table entry reads block 0 and poisons the workgroup's
+  // result.
   const size_t head_off = (size_t)kvh * BS * D * sizeof(QT);
   const size_t blk_stride = (size_t)p.num_kv_heads * BS * D * sizeof(QT);
   bool poisoned = false;
-  auto step_blocks = [&](int base, size_t (&boff)[NB]) {
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      int phys = 0;
-      if (base + b * BS < nk) {
-        phys = btab[base / BS + b];
-        if (phys < 0 || phys >= p.num_blocks) {
-          poisoned = true;
-          phys = 0;
-        }
-      }
-      boff[b] = (size_t)phys * blk_stride + head_off;
-    }
-  };
-
-  // One step's tiles in registers: K chunks (row-major) and two keys' chunks
-  // of V; keys at or past nk become zero.  Every load is issued (a block past
-  // the end reads block 0, always addressable), so the stage has no branches
-  // around its loads; the zeroing waits for store_stage, where the data is
-  // consumed (a select right after a load would wait for the load there and
-  // serialise the prefetch).
-  struct Stage {
-    u32x4 k[NLK];
-    u32x4 v[NLV][2];
-    bool kok[NLK], vok[NLV][2];
-  };
-  auto load_stage = [&](int base) {
-    size_t boff[NB];
-    step_blocks(base, boff);
-    Stage st;
-#pragma unroll
-    for (int i = 0; i < NLK; ++i) {
-      const int c = threadIdx.x + kThreads * i, key = c / CPR, ch = c % CPR;
-      const size_t off = boff[key / BS] + ((key % BS) * D + ch * 8) * sizeof(QT);
-      st.k[i] = load16(kcache + off);
-      st.kok[i] = base + key < nk;
-    }
-#pragma unroll
-    for (int i = 0; i < NLV; ++i) {
-      const int c = threadIdx.x + kThreads * i;
-      const int kp = c % (kPrefillStep / 2), ch = c / (kPrefillStep / 2);
-      const int key = 2 * kp;  // keys key, key + 1: one block (block sizes are even)
-      const size_t off = boff[key / BS] + ((key % BS) * D + ch * 8) * sizeof(QT);
-      st.v[i][0] = st.v[i][1] = u32x4{0u, 0u, 0u, 0u};
-      st.vok[i][0] = base + key < nk;
-      st.vok[i][1] = base + key + 1 < nk;
-      if (c < VTASKS) {
-        st.v[i][0] = load16(vcache + off);
-        st.v[i][1] = load16(vcache + off + D * sizeof(QT));
-      }
-    }
-    return st;
-  };
-  auto store_stage = [&](const Stage &st) {
-#pragma unroll
-    for (int i = 0; i < NLK; ++i) {
-      const int c = threadIdx.x + kThreads * i, key = c / CPR, ch = c % CPR;
-      *reinterpret_cast<u32x4 *>(&sk[key][ch * 8]) =
-          st.kok[i] ? st.k[i] : u32x4{0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int i = 0; i < NLV; ++i) {
-      const int c = threadIdx.x + kThreads * i;
-      const int kp = c % (kPrefillStep / 2), ch = c / (kPrefillStep / 2);
-      if (c < VTASKS) {
-        const u32x4 z = {0u, 0u, 0u, 0u};
-        const u32x4 va = st.vok[i][0] ? st.v[i][0] : z, vb = st.vok[i][1] ? st.v[i][1] : z;
-        const unsigned a[4] = {va.x, va.y, va.z, va.w};
-        const unsigned b[4] = {vb.x, vb.y, vb.z, vb.w};
-        // Dim e of the two keys as one dword: the 16-bit halves e % 2 of
-        // word e / 2 of each key (byte permute: bytes 0-3 from a, 4-7 from b).
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          *reinterpret_cast<unsigned *>(&sv[ch * 8 + e][2 * kp]) =
-              __builtin_amdgcn_perm(b[e / 2], a[e / 2], (e % 2) ? 0x07060302u : 0x05040100u);
-      }
-    }
-  };
 
   float m_run[NT], l_run[NT];
   f32x4 oacc[NT][NDT];
@@ -388,7 +266,7 @@ __global__ void __launch_bounds__(kThreads)
     for (int t = 0; t < NDT; ++t) oacc[j][t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   }
 
-  // Ring form, per lane: base of the QK operand reads and of the
+  // Per lane: base of the QK operand reads and of the
   // transposing V reads.  Row 4 q + e of a 16-key sub-tile h of the QK
   // product is key 16 h + 4 tau(q) + e (tau a permutation of the four
   // 4-key groups), and the PV product pairs contraction index 8 g + 4 r + m
@@ -408,7 +286,7 @@ __global__ void __launch_bounds__(kThreads)
   const int vkey = 4 * ring_tau(g) + (n >> 2);
   // Key of element e of sub-tile h in this lane's QK output: base + 16 h +
   // kgrp + e.
-  const int kgrp = RING ? 4 * ring_tau(g) : 4 * g;
+  const int kgrp = 4 * ring_tau(g);
   const int voff = (vkey / RG::KPI) * RG::IB + 16 * (RG::KPI * ((n >> 1) & 1) + vkey % RG::KPI) +
                    8 * (n & 1);
   // The keys every valid column of the wave sees: [full_lo, full_hi)
@@ -426,7 +304,6 @@ __global__ void __launch_bounds__(kThreads)
     full_hi = -wave_max32(-b);
   }
   auto compute = [&](int base, const char *kst) {
-    (void)kst;
     // Every valid column of the wave sees the whole step: no masks needed.
     const bool full = base >= full_lo && base + kPrefillStep <= full_hi;
     // S^T of every column tile; each K fragment read from LDS feeds NT MFMAs.
@@ -437,24 +314,12 @@ __global__ void __launch_bounds__(kThreads)
       for (int j = 0; j < NT; ++j) sc[j][h] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
-      u32x4 qv[NT];
-#pragma unroll
-      for (int j = 0; j < NT; ++j) {
-        if constexpr (kQLds) {
-          const int row = 16 * (NT * wv + j) + n;
-          qv[j] = *reinterpret_cast<const u32x4 *>(&sq[row][((4 * ks + g) ^ qswz(row)) * 8]);
-        } else {
-          qv[j] = qop[j][ks];
-        }
-      }
 #pragma unroll
       for (int h = 0; h < NSUB; ++h) {
-        const u32x4 a =
-            RING ? *reinterpret_cast<const u32x4 *>(kst + koff + h * (16 / RG::KPI) * RG::IB +
-                                                    64 * RG::KPI * ks)
-                 : *reinterpret_cast<const u32x4 *>(&sk[16 * h + n][32 * ks + 8 * g]);
+        const u32x4 a = *reinterpret_cast<const u32x4 *>(kst + koff + h * (16 / RG::KPI) * RG::IB +
+                                                         64 * RG::KPI * ks);
 #pragma unroll
-        for (int j = 0; j < NT; ++j) sc[j][h] = mfma_qk(a, qv[j], sc[j][h], QT());
+        for (int j = 0; j < NT; ++j) sc[j][h] = mfma_qk(a, qop[j][ks], sc[j][h], QT());
       }
     }
     u32x4 pop[NT][NHALF];
@@ -479,8 +344,7 @@ __global__ void __launch_bounds__(kThreads)
       }
 #pragma unroll
       for (int hf = 0; hf < NHALF; ++hf)
-        pop[j][hf] = RING ? u32x4{pk[2 * hf].x, pk[2 * hf].y, pk[2 * hf + 1].x, pk[2 * hf + 1].y}
-                          : regroup_p(pk[2 * hf], pk[2 * hf + 1]);
+        pop[j][hf] = u32x4{pk[2 * hf].x, pk[2 * hf].y, pk[2 * hf + 1].x, pk[2 * hf + 1].y};
     };
     // Moves column j's reference to bm when bm exceeds it by more than the
     // lazy margin, rescaling its sum and accumulators (m_run = -inf always
@@ -562,16 +426,10 @@ __global__ void __launch_bounds__(kThreads)
     for (int t = 0; t < NDT; ++t) {
 #pragma unroll
       for (int hf = 0; hf < NHALF; ++hf) {
-        u32x4 va;
-        if constexpr (RING) {
-          const char *rd =
-              kst + RG::TILE + voff + hf * (32 / RG::KPI) * RG::IB + 32 * RG::KPI * t;
-          const u32x2 lo = lds_read_tr16(rd);
-          const u32x2 hi = lds_read_tr16(rd + (16 / RG::KPI) * RG::IB);
-          va = u32x4{lo.x, lo.y, hi.x, hi.y};
-        } else {
-          va = *reinterpret_cast<const u32x4 *>(&sv[16 * t + n][32 * hf + 8 * (g ^ 1)]);
-        }
+        const char *rd = kst + RG::TILE + voff + hf * (32 / RG::KPI) * RG::IB + 32 * RG::KPI * t;
+        const u32x2 lo = lds_read_tr16(rd);
+        const u32x2 hi = lds_read_tr16(rd + (16 / RG::KPI) * RG::IB);
+        const u32x4 va = u32x4{lo.x, lo.y, hi.x, hi.y};
 #pragma unroll
         for (int j = 0; j < NT; ++j) oacc[j][t] = mfma_pv(va, pop[j][hf], oacc[j][t], QT());
       }
@@ -580,12 +438,8 @@ __global__ void __launch_bounds__(kThreads)
 
   if (threadIdx.x == 0) sm_bad = 0;
   __syncthreads();
-  // One LDS buffer: the next step's tiles load into registers while the
-  // current step is computed, then replace it between two barriers.  (A
-  // two-buffer, one-barrier pipeline measured slower: the second buffer
-  // cost occupancy.)
-  int base = (int)(lo - lo % BS);  // steps start on a block boundary: earlier blocks are never read
-  if constexpr (RING) {
+  const int base = (int)(lo - lo % BS);  // steps start on a block boundary: earlier blocks are never read
+  {
     // Three stages, one barrier per step: at step s the loads of s and
     // s + 1 are in flight; the wave waits for its own loads of s, the
     // barrier publishes everyone's and frees stage s - 1 (every wave has
@@ -660,48 +514,6 @@ __global__ void __launch_bounds__(kThreads)
       compute(sbase, cur);
       cur_off = cur_off == 2 * RG::STAGE ? 0 : cur_off + RG::STAGE;
     }
-  } else if constexpr (NT == 1) {
-    // With one column tile the registers allow a second stage: loads run
-    // two steps ahead (the last step's loads repeat it, so every load is
-    // issued and each wait covers only the stage it needs).
-    const int n_steps = base < hi ? (int)((hi - base + kPrefillStep - 1) / kPrefillStep) : 0;
-    if (n_steps > 0) {
-      auto step_base = [&](int s) { return base + kPrefillStep * min(s, n_steps - 1); };
-      Stage sa = load_stage(step_base(0));
-      Stage sb = load_stage(step_base(1));
-      store_stage(sa);
-      __syncthreads();
-      for (int s = 0;; s += 2) {
-        sa = load_stage(step_base(s + 2));
-        compute(base + kPrefillStep * s, nullptr);
-        __syncthreads();
-        if (s + 1 >= n_steps) break;
-        store_stage(sb);  // step s + 1
-        __syncthreads();
-        sb = load_stage(step_base(s + 3));
-        compute(base + kPrefillStep * (s + 1), nullptr);
-        __syncthreads();
-        if (s + 2 >= n_steps) break;
-        store_stage(sa);  // step s + 2
-        __syncthreads();
-      }
-    }
-  } else {
-    if (base < hi) {
-      Stage st = load_stage(base);
-      store_stage(st);
-      __syncthreads();
-      for (; base < hi; base += kPrefillStep) {
-        const bool more = base + kPrefillStep < hi;
-        if (more) st = load_stage(base + kPrefillStep);
-        compute(base, nullptr);
-        __syncthreads();
-        if (more) {
-          store_stage(st);
-          __syncthreads();
-        }
-      }
-    }
   }
   if (poisoned) sm_bad = 1;
   __syncthreads();
@@ -725,19 +537,13 @@ __global__ void __launch_bounds__(kThreads)
   }
 }
 
-template <typename QT, int D, int BS, bool RING>
-static hipError_t launch_prefill_form(const PrefillParams &p, bool cap, const Launch &l) {
-  if (p.tiles_per_wave == 2)
-    return cap ? launch_kernel(pa_prefill_kernel<QT, D, BS, 2, true, RING>, l, p)
-               : launch_kernel(pa_prefill_kernel<QT, D, BS, 2, false, RING>, l, p);
-  return cap ? launch_kernel(pa_prefill_kernel<QT, D, BS, 1, true, RING>, l, p)
-             : launch_kernel(pa_prefill_kernel<QT, D, BS, 1, false, RING>, l, p);
-}
-
 template <typename QT, int D, int BS>
 static hipError_t launch_prefill_bs(const PrefillParams &p, bool cap, const Launch &l) {
-  return p.ring ? launch_prefill_form<QT, D, BS, true>(p, cap, l)
-                : launch_prefill_form<QT, D, BS, false>(p, cap, l);
+  if (p.tiles_per_wave == 2)
+    return cap ? launch_kernel(pa_prefill_kernel<QT, D, BS, 2, true>, l, p)
+               : launch_kernel(pa_prefill_kernel<QT, D, BS, 2, false>, l, p);
+  return cap ? launch_kernel(pa_prefill_kernel<QT, D, BS, 1, true>, l, p)
+             : launch_kernel(pa_prefill_kernel<QT, D, BS, 1, false>, l, p);
 }
 
 template <typename QT>
