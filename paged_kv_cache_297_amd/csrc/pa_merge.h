@@ -10,25 +10,26 @@
 
 #if defined(__HIPCC__)
 #define PA_HD __host__ __device__
-#define PA_UNROLL4 _Pragma("unroll 4")
+#define PA_UNROLL _Pragma("unroll")
 #else
 #include <math.h>
 #define PA_HD
-#define PA_UNROLL4
+#define PA_UNROLL
 #endif
 
 namespace pa {
 
 constexpr float kMergeLog2e = 1.4426950408889634f;
 
-// One output element of the merge above.  m(c) = m_c, s(c) = S_c, o(c) =
-// O_c (each called for c < k only); exp2_fn(x) = 2^x.  A partial with m_c =
-// -inf (no key in its range) adds nothing and its O_c is not read; a NaN m_c
-// (a piece that met an invalid block-table entry) makes the result NaN.  The
-// partials are taken in index order, so the result does not depend on the
-// order in which they were produced.
-template <typename M, typename S, typename Exp2, typename LoadO>
-PA_HD inline float lse_merge(M m, S s, int k, Exp2 exp2_fn, LoadO load_o) {
+// The merge in two steps, as the kernels run it.
+//
+// lse_rescale, once per head: r_c = exp(m_c - M) S_c for c < k, handed to
+// put_r(c, r_c) (0 for a partial with m_c = -inf, i.e., no key in its
+// range); returns sum_c r_c, or NaN when some m_c is NaN (a piece that met
+// an invalid block-table entry), which makes every output of the head NaN.
+// m(c) = m_c, s(c) = S_c; exp2_fn(x) = 2^x.
+template <typename M, typename S, typename Exp2, typename PutR>
+PA_HD inline float lse_rescale(M m, S s, int k, Exp2 exp2_fn, PutR put_r) {
   const float ninf = -__builtin_inff();
   float big_m = ninf;
   bool nan_seen = false;
@@ -37,15 +38,47 @@ PA_HD inline float lse_merge(M m, S s, int k, Exp2 exp2_fn, LoadO load_o) {
     nan_seen |= mc != mc;
     big_m = fmaxf(big_m, mc);
   }
-  float sum = 0.0f, acc = 0.0f;
-  PA_UNROLL4
+  float sum = 0.0f;
   for (int c = 0; c < k; ++c) {
     const float mc = m(c);
     const float r = mc == ninf ? 0.0f : exp2_fn((mc - big_m) * kMergeLog2e) * s(c);
+    put_r(c, r);
     sum += r;
-    acc = mc == ninf ? acc : fmaf(r, load_o(c), acc);
   }
-  return nan_seen ? __builtin_nanf("") : acc / sum;
+  return nan_seen ? __builtin_nanf("") : sum;
+}
+
+// Pieces whose partial rows a merge requests before it uses any of them.
+constexpr int kMergeBatch = 8;
+
+// lse_combine, per slice of N output values of one head: out[e] = sum_c
+// r_c O_c[e] / sum, from r(c) = r_c and sum of lse_rescale.  load(c)
+// returns piece c's slice in any raw form and unpack(raw, o) turns it into
+// o[0 .. N).  A batch of kMergeBatch loads is issued, unconditionally
+// (indices past k - 1 read slot k - 1 again and are not used), before any
+// of them is unpacked, so their latencies overlap.  A piece with r_c = 0
+// adds nothing and its slice may hold anything (an empty piece writes no
+// row).  The pieces are taken in index order, so the result does not depend
+// on the order in which they were produced.
+template <int N, typename R, typename Load, typename Unpack>
+PA_HD inline void lse_combine(R r, float sum, int k, Load load, Unpack unpack, float (&out)[N]) {
+  using Raw = decltype(load(0));
+  float acc[N];
+  for (int e = 0; e < N; ++e) acc[e] = 0.0f;
+  for (int c0 = 0; c0 < k; c0 += kMergeBatch) {
+    Raw raw[kMergeBatch];
+    PA_UNROLL
+    for (int j = 0; j < kMergeBatch; ++j) raw[j] = load(c0 + j < k ? c0 + j : k - 1);
+    PA_UNROLL
+    for (int j = 0; j < kMergeBatch; ++j)
+      if (c0 + j < k) {
+        float o[N];
+        unpack(raw[j], o);
+        const float rc = r(c0 + j);
+        for (int e = 0; e < N; ++e) acc[e] = rc == 0.0f ? acc[e] : fmaf(rc, o[e], acc[e]);
+      }
+  }
+  for (int e = 0; e < N; ++e) out[e] = acc[e] / sum;
 }
 
 // The arrival of one of the k pieces of an item at the item's counter (zero

@@ -216,6 +216,35 @@ __device__ __forceinline__ float coherent_load_elem(const QT *ptr) {
   }
 }
 
+// Four consecutive values of a partial row (fp32, or the 16-bit type TT),
+// read past the L2 with 8-byte agent-scope loads (ptr 8-byte aligned): the
+// raw bits, then the values.
+struct Raw4 {
+  unsigned long long a, b;
+};
+__device__ __forceinline__ unsigned long long coherent_load8(const void *ptr) {
+  return __hip_atomic_load(reinterpret_cast<const unsigned long long *>(ptr), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename TT>
+__device__ __forceinline__ Raw4 coherent_load4(const TT *ptr) {
+  if constexpr (sizeof(TT) == 4) return Raw4{coherent_load8(ptr), coherent_load8(ptr + 2)};
+  else return Raw4{coherent_load8(ptr), 0ull};
+}
+template <typename TT>
+__device__ __forceinline__ void unpack4(const Raw4 &r, float (&v)[4]) {
+  if constexpr (sizeof(TT) == 4) {
+    v[0] = bits_f((unsigned)r.a);
+    v[1] = bits_f((unsigned)(r.a >> 32));
+    v[2] = bits_f((unsigned)r.b);
+    v[3] = bits_f((unsigned)(r.b >> 32));
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      v[e] = to_f32(__builtin_bit_cast(TT, (unsigned short)(r.a >> (16 * e))));
+  }
+}
+
 // The counter operations of the arrival (the ordering is described with
 // coherent_store above).  PA_ARRIVE_RELEASE_ACQUIRE = 1: agent-scope release
 // increment and acquire load; 0 (default): relaxed increment, no acquire.
@@ -242,6 +271,7 @@ template <typename QT, typename TT, int D>
 __device__ __forceinline__ void split_merge(const Params &p, const Work &w) {
   __shared__ int sm_last;
   __shared__ float sm_pm[16][kSplitMaxPieces], sm_ps[16][kSplitMaxPieces];
+  __shared__ float sm_sum[16];
   const int tid = epi_tid();
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's partial stores are done
   __syncthreads();
@@ -261,19 +291,30 @@ __device__ __forceinline__ void split_merge(const Params &p, const Work &w) {
   for (int idx = tid; idx < w.nh * k; idx += kThreads) {
     const int h = idx / k, c = idx - h * k;
     const size_t r = row0 + (size_t)h * p.max_num_partitions + c;
-    sm_pm[h][c] = bits_f(coherent_load(p.max_logits + r));
-    sm_ps[h][c] = bits_f(coherent_load(p.exp_sums + r));
+    const unsigned m_bits = coherent_load(p.max_logits + r);
+    const unsigned s_bits = coherent_load(p.exp_sums + r);
+    sm_pm[h][c] = bits_f(m_bits);
+    sm_ps[h][c] = bits_f(s_bits);
   }
   __syncthreads();
+  // Per head: the rescaled exp-sums r_c, in place of S_c, and their sum.
+  if (tid < w.nh)
+    sm_sum[tid] = lse_rescale(
+        [&](int c) { return sm_pm[tid][c]; }, [&](int c) { return sm_ps[tid][c]; }, k,
+        [](float x) { return fast_exp2(x); }, [&](int c, float r) { sm_ps[tid][c] = r; });
+  __syncthreads();
+  // Per thread: four consecutive dims of one head, all pieces' slices requested at once.
+  constexpr int G = D / 4;
   const TT *to = reinterpret_cast<const TT *>(p.tmp_out);
-  for (int idx = tid; idx < w.nh * D; idx += kThreads) {
-    const int h = idx / D, d = idx - h * D;
-    const TT *col = to + (row0 + (size_t)h * p.max_num_partitions) * D + d;
-    const float o = lse_merge(
-        [&](int c) { return sm_pm[h][c]; }, [&](int c) { return sm_ps[h][c]; }, k,
-        [](float x) { return fast_exp2(x); },
-        [&](int c) { return coherent_load_elem<TT>(col + (size_t)c * D); });
-    store_out_row<QT, D>(p, w.seq, w.head0 + h, d, o);
+  for (int idx = tid; idx < w.nh * G; idx += kThreads) {
+    const int h = idx / G, d0 = 4 * (idx - h * G);
+    const TT *col = to + (row0 + (size_t)h * p.max_num_partitions) * D + d0;
+    float o[4];
+    lse_combine<4>([&](int c) { return sm_ps[h][c]; }, sm_sum[h], k,
+                   [&](int c) { return coherent_load4<TT>(col + (size_t)c * D); },
+                   [](const Raw4 &r, float(&v)[4]) { unpack4<TT>(r, v); }, o);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) store_out_row<QT, D>(p, w.seq, w.head0 + h, d0 + e, o[e]);
   }
 }
 
@@ -562,20 +603,27 @@ __device__ __forceinline__ void piece_arrive(const Params &p, const Work &w) {
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   if (!__builtin_amdgcn_readfirstlane(last)) return;
-  // Lane c < k holds piece c's statistics; the merge reads them by lane.
+  // Lane c < k holds piece c's statistics, then its rescaled exp-sum r_c;
+  // lanes 0 .. D/4 - 1 each merge four consecutive dims.
   const int k = min(w.n_part, kSplitMaxPieces);
+  constexpr int G = D / 4;
   const TT *to = reinterpret_cast<const TT *>(p.tmp_out);
   for (int h = 0; h < w.nh; ++h) {
     const size_t row0 = ((size_t)w.seq * p.num_heads + w.head0 + h) * p.max_num_partitions;
     const float mc = lane < k ? bits_f(coherent_load(p.max_logits + row0 + lane)) : 0.0f;
     const float sc = lane < k ? bits_f(coherent_load(p.exp_sums + row0 + lane)) : 0.0f;
-    for (int d = lane; d < D; d += 64) {
-      const TT *col = to + row0 * D + d;
-      const float o = lse_merge(
-          [&](int c) { return readlane(mc, c); }, [&](int c) { return readlane(sc, c); }, k,
-          [](float x) { return fast_exp2(x); },
-          [&](int c) { return coherent_load_elem<TT>(col + (size_t)c * D); });
-      store_out_row<QT, D>(p, w.seq, w.head0 + h, d, o);
+    float rl = 0.0f;
+    const float sum = lse_rescale(
+        [&](int c) { return readlane(mc, c); }, [&](int c) { return readlane(sc, c); }, k,
+        [](float x) { return fast_exp2(x); }, [&](int c, float r) { rl = lane == c ? r : rl; });
+    for (int g = lane; g < G; g += 64) {
+      const TT *col = to + row0 * D + 4 * g;
+      float o[4];
+      lse_combine<4>([&](int c) { return readlane(rl, c); }, sum, k,
+                     [&](int c) { return coherent_load4<TT>(col + (size_t)c * D); },
+                     [](const Raw4 &r, float(&v)[4]) { unpack4<TT>(r, v); }, o);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) store_out_row<QT, D>(p, w.seq, w.head0 + h, 4 * g + e, o[e]);
     }
   }
 }

@@ -76,10 +76,17 @@ int main() {
               [](int *p, int v) { __atomic_store_n(p, v, __ATOMIC_RELAXED); });
           if (!last) return;
           ++mergers;
-          for (int j = 0; j < d; ++j)
-            out[j] = pa::lse_merge([&](int cc) { return m[cc]; }, [&](int cc) { return s[cc]; },
-                                   k, [](float x) { return exp2f(x); },
-                                   [&](int cc) { return o[(size_t)cc * d + j]; });
+          std::vector<float> rr(k);
+          const float sum = pa::lse_rescale(
+              [&](int cc) { return m[cc]; }, [&](int cc) { return s[cc]; }, k,
+              [](float x) { return exp2f(x); }, [&](int cc, float v) { rr[cc] = v; });
+          for (int j = 0; j < d; ++j) {
+            float one[1];
+            pa::lse_combine<1>(
+                [&](int cc) { return rr[cc]; }, sum, k, [&](int cc) { return o[(size_t)cc * d + j]; },
+                [](float raw, float(&v)[1]) { v[0] = raw; }, one);
+            out[j] = one[0];
+          }
         });
       }
       for (auto &t : th) t.join();
