@@ -339,6 +339,7 @@ struct ListCursor {
   long long pos;     // line position of the current item
   int seq, x;        // current item
   int L, keys, base; // its length, keys on the line, first key (32-aligned window start)
+  int L_next;        // length of sequence seq + 1 (read one sequence ahead; 0 past the batch)
   long long cost;
   long long start;   // offset at which this worker's piece of the current item starts
 };
@@ -391,6 +392,7 @@ __device__ __forceinline__ void scalarize(ListCursor &c) {
   c.seq = uniform32(c.seq);
   c.x = uniform32(c.x);
   c.L = uniform32(c.L);
+  c.L_next = uniform32(c.L_next);
   c.keys = uniform32(c.keys);
   c.base = uniform32(c.base);
 }
@@ -438,6 +440,7 @@ __device__ __forceinline__ void list_locate(const Params &p, int gx, long long t
       const long long item0 = wave_uniform64(__shfl(run + incl - span, l));  // line position of (seq, 0)
       c.seq = s0 + l;
       c.L = __builtin_amdgcn_readfirstlane(__shfl(L, l));
+      c.L_next = c.seq + 1 < p.num_seqs ? p.seq_lens[c.seq + 1] : 0;
       c.keys = __builtin_amdgcn_readfirstlane(__shfl(keys, l));
       c.base = __builtin_amdgcn_readfirstlane(__shfl(base, l));
       c.cost = wave_uniform64(__shfl(cost, l));
@@ -459,13 +462,107 @@ __device__ __forceinline__ void list_advance(const Params &p, int gx, ListCursor
   if (++c.x < gx) return;
   c.x = 0;
   if (++c.seq >= p.num_seqs) return;
-  c.cost = list_seq_cost(p, c.seq, c.L, c.keys, c.base);
+  c.L = c.L_next;
+  c.keys = list_keys(c.L, p.max_seq_len, p.window_left, &c.base);
+  c.cost = list_cost(c.keys, p.item_cost);
+  c.L_next = c.seq + 1 < p.num_seqs ? p.seq_lens[c.seq + 1] : 0;
+}
+
+// Batches of at most 64 * kListRegChunks sequences: seq_lens is read once,
+// lane l holding sequences 64 i + l, and the worker's range is found from
+// those registers (no further reads); larger batches scan seq_lens in
+// global memory chunk by chunk.
+constexpr int kListRegChunks = 4;
+
+__device__ __forceinline__ bool list_begin_regs(const Params &p, ListCursor &c, int worker,
+                                                int grid_workers) {
+  constexpr int NC = kListRegChunks;
+  const int gx = p.num_kv_heads * p.head_groups;
+  const int lane = threadIdx.x & 63;
+  const int n = p.num_seqs;
+  int L[NC], keys[NC], base[NC];
+  long long cost[NC], incl[NC];  // incl: line position just past sequence 64 i + lane's items
+#pragma unroll
+  for (int i = 0; i < NC; ++i) L[i] = 64 * i + lane < n ? p.seq_lens[64 * i + lane] : 0;
+  long long run = 0;
+  int kmax = 0;
+#pragma unroll
+  for (int i = 0; i < NC; ++i) {
+    const bool in = 64 * i + lane < n;
+    keys[i] = list_keys(L[i], p.max_seq_len, p.window_left, &base[i]);
+    cost[i] = in ? list_cost(keys[i], p.item_cost) : 0;
+    kmax = in ? max(kmax, keys[i]) : kmax;
+    incl[i] = run + wave_inclusive_scan64(cost[i] * gx, lane);
+    run = wave_uniform64(__shfl(incl[i], 63));
+  }
+  c.sh = list_shares(run, uniform32(list_workers(run, grid_workers, wave_max32(kmax))));
+  c.sh.q = wave_uniform64(c.sh.q);
+  c.sh.r = wave_uniform64(c.sh.r);
+  c.w = worker;
+  if (c.w >= c.sh.workers) return false;
+  // The item holding line position target: the first sequence whose items
+  // end after it.
+  auto locate = [&](long long target, long long &offset) {
+    int ci = NC - 1, l = 63;
+    bool found = false;
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+      const unsigned long long hit = __ballot(64 * i + lane < n && target < incl[i]);
+      if (!found && hit) {
+        found = true;
+        ci = i;
+        l = __builtin_ctzll(hit);
+      }
+    }
+    long long end_s = 0, cost_s = 1;
+    int L_s = 0, keys_s = 0, base_s = 0, L_n = 0;
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+      const long long e = __shfl(incl[i], l), cs = __shfl(cost[i], l);
+      const int Ls = __shfl(L[i], l), ks = __shfl(keys[i], l), bs = __shfl(base[i], l);
+      // The next sequence's length: lane l + 1 of this chunk, or lane 0 of the next.
+      const int Ln = l < 63 ? __shfl(L[i], l + 1) : (i + 1 < NC ? __shfl(L[i + 1 < NC ? i + 1 : i], 0) : 0);
+      if (i == ci) {
+        end_s = e;
+        cost_s = cs;
+        L_s = Ls;
+        keys_s = ks;
+        base_s = bs;
+        L_n = Ln;
+      }
+    }
+    c.seq = uniform32(64 * ci + l);
+    c.L = uniform32(L_s);
+    c.L_next = c.seq + 1 < n ? uniform32(L_n) : 0;
+    c.keys = uniform32(keys_s);
+    c.base = uniform32(base_s);
+    c.cost = wave_uniform64(cost_s);
+    const long long item0 = wave_uniform64(end_s) - c.cost * gx;
+    c.x = uniform32((int)list_div(target - item0, c.cost));
+    c.x = c.x < gx ? c.x : gx - 1;
+    c.pos = item0 + (long long)c.x * c.cost;
+    offset = wave_uniform64(target - c.pos);
+  };
+  if (c.w + 1 >= c.sh.workers) {
+    c.end = c.sh.total;
+  } else {
+    long long off = 0;
+    locate(wave_uniform64(list_boundary(c.sh, c.w + 1)), off);
+    c.end = wave_uniform64(c.pos + list_snap(off, c.keys, c.cost));
+  }
+  long long off = 0;
+  locate(wave_uniform64(list_boundary(c.sh, c.w)), off);
+  c.start = list_snap(off, c.keys, c.cost);
+  if (c.start >= c.cost) list_advance(p, gx, c);
+  scalarize(c);
+  return true;
 }
 
 // Sets up worker `worker` of `grid_workers`; false when it has no range (a
 // batch too small for every worker).  Wave-uniform.
 __device__ __forceinline__ bool list_begin(const Params &p, ListCursor &c, int worker,
                                            int grid_workers) {
+  if (p.num_seqs <= 64 * kListRegChunks) return list_begin_regs(p, c, worker, grid_workers);
   const int gx = p.num_kv_heads * p.head_groups;
   const int lane = threadIdx.x & 63;
   long long sum = 0;
@@ -518,7 +615,7 @@ __device__ __forceinline__ bool list_next(const Params &p, int block_size, int g
     w.L = c.L;
     const long long stop = min(c.cost, c.end - c.pos);  // end of the piece (offset)
     const long long start = c.start;
-    const long long item_pos = c.pos;
+    const long long item_pos = c.pos, cost = c.cost;
     const int keys = c.keys, base = c.base;
     list_advance(p, gx, c);
     if (keys == 0) {
@@ -529,8 +626,15 @@ __device__ __forceinline__ bool list_next(const Params &p, int block_size, int g
                              bad ? __builtin_nanf("") : 0.0f);
       continue;
     }
-    list_piece(c.sh, item_pos, keys, c.w, start, &w.n_part, &w.part);
     if (stop <= start) continue;
+    // A piece that spans its whole item is the item (no boundary falls
+    // inside it); only the pieces at the ends of a range need the search.
+    if (start == 0 && stop >= cost) {
+      w.n_part = 1;
+      w.part = 0;
+    } else {
+      list_piece(c.sh, item_pos, keys, c.w, start, &w.n_part, &w.part);
+    }
     w.t_lo = window_first_token(p.window_left, w.L);
     w.v2 = w.n_part > 1;
     w.single = false;

@@ -37,6 +37,7 @@ constexpr int kListMinPiece = 512;   // keys: shortest piece of a cut item
 constexpr int kListStep = 32;        // keys: cuts fall on these steps from the item's base
 constexpr int kListMinRange = 2048;  // keys: shortest range of a worker
 constexpr int kListMaxPieces = 64;   // pieces of one item (the merge keeps their statistics in LDS)
+constexpr int kListMaxWorkers = 65535;  // workers of one launch (keeps list_boundary in 32 bits)
 
 // Keys of a sequence of length L for the list (0 when empty or invalid) and
 // the 32-aligned first key `base` the key offsets count from.
@@ -61,14 +62,17 @@ PA_LHD inline long long list_div(long long a, long long b) {
   return q;
 }
 
-// Workers that get work: at most W, and few enough that each range spans at
-// least max(kListMinRange, max_keys / (kListMaxPieces - 2)) keys, so that no
-// range is empty and no item is cut into more than kListMaxPieces pieces.
+// Workers that get work: at most W (and kListMaxWorkers), and few enough
+// that each range spans at least max(kListMinRange, max_keys /
+// (kListMaxPieces - 2)) keys, so that no range is empty and no item is cut
+// into more than kListMaxPieces pieces.
 PA_LHD inline int list_workers(long long total, int grid_workers, int max_keys) {
   long long r = (max_keys + kListMaxPieces - 3) / (kListMaxPieces - 2);
   r = r > kListMinRange ? r : kListMinRange;
-  const long long w = list_div(total, r);
-  return (int)(w < 1 ? 1 : (w < grid_workers ? w : grid_workers));
+  long long w = list_div(total, r);
+  w = w < grid_workers ? w : grid_workers;
+  w = w < kListMaxWorkers ? w : kListMaxWorkers;
+  return (int)(w < 1 ? 1 : w);
 }
 
 // The line cut into W equal shares: b_w = floor(w * T / W) = w q + floor(w r
@@ -87,8 +91,11 @@ PA_LHD inline ListShares list_shares(long long total, int workers) {
   return sh;
 }
 
+// w r < W^2 < 2^32 (list_workers keeps W below 2^16), so the remainder
+// term is one 32-bit division.
 PA_LHD inline long long list_boundary(const ListShares &sh, int w) {
-  return (long long)w * sh.q + list_div((long long)w * sh.r, sh.workers);
+  return (long long)w * sh.q +
+         (long long)((unsigned)((long long)w * sh.r) / (unsigned)sh.workers);
 }
 
 // A position at key offset o of an item (0 <= o < cost) snapped as described
