@@ -263,42 +263,76 @@ __device__ __forceinline__ void arrive_reset(int *c, int v) {
   __hip_atomic_store(c, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// After a piece's partials are stored (slot = piece): the piece that
-// arrives last at the (sequence, grid-x slot) counter merges the k pieces
-// with the log-sum-exp rescale of the V2 page's Phase 2, writes out, and
-// resets the counter to zero for the next call.
-template <typename QT, typename TT, int D>
-__device__ __forceinline__ void split_merge(const Params &p, const Work &w) {
-  __shared__ int sm_last;
-  __shared__ float sm_pm[16][kSplitMaxPieces], sm_ps[16][kSplitMaxPieces];
-  __shared__ float sm_sum[16];
-  const int tid = epi_tid();
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's partial stores are done
-  __syncthreads();
-  if (tid == 0) {
-    int *ctr = p.counters + (size_t)w.seq * p.num_heads + w.xslot;
-    sm_last = arrive_last(
-        ctr, w.n_part,
-        [](int *c) { return arrive_add(c); }, [](int *c) { arrive_acquire(c); },
-        [](int *c, int v) { arrive_reset(c, v); });
+// Four values in the raw form coherent_load4 returns for a TT row: the
+// values rounded to TT, as a stored partial would hold them.
+template <typename TT>
+__device__ __forceinline__ Raw4 pack4(const float (&v)[4]) {
+  if constexpr (sizeof(TT) == 4) {
+    return Raw4{(unsigned long long)f_bits(v[0]) | ((unsigned long long)f_bits(v[1]) << 32),
+                (unsigned long long)f_bits(v[2]) | ((unsigned long long)f_bits(v[3]) << 32)};
+  } else {
+    unsigned long long a = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      a |= (unsigned long long)__builtin_bit_cast(unsigned short, from_f32<TT>(v[e])) << (16 * e);
+    return Raw4{a, 0ull};
   }
-  __syncthreads();
-  if (!sm_last) return;
-  // At most kSplitMaxPieces pieces by construction (both piece modes); the
+}
+
+__device__ __forceinline__ int *item_counter(const Params &p, int seq, int xslot) {
+  return p.counters + (size_t)seq * p.num_heads + xslot;
+}
+
+// The Phase 2 merge (V2 page, "Phase 2: Reduce across partitions") of the k
+// pieces of item (seq, heads head0 .. head0 + nh - 1) into out, by the whole
+// workgroup.  Piece c's partials are read from its slot c, past the L2,
+// except piece `own` (>= 0), whose normalised rows are own_o[h][d] and
+// statistics own_m[h] (max logit, absolute) / own_s[h] (exp-sum) in LDS;
+// they are rounded to the partial type as a stored partial would be, so the
+// result does not depend on which piece merges.  Ends with the out stores
+// issued.
+// The merge's statistics in LDS: one copy per kernel, whatever the
+// instantiations of merge_pieces it holds.
+struct MergeLds {
+  float pm[16][kSplitMaxPieces], ps[16][kSplitMaxPieces], sum[16];
+};
+__device__ __forceinline__ MergeLds &merge_lds() {
+  __shared__ MergeLds m;
+  return m;
+}
+
+template <typename QT, typename TT, int D, int OSTRIDE>
+__device__ __forceinline__ void merge_pieces(const Params &p, int seq, int head0, int nh, int k,
+                                             int own, const float (*own_o)[OSTRIDE],
+                                             const float *own_m, const float *own_s) {
+  MergeLds &ml = merge_lds();
+  auto &sm_pm = ml.pm;
+  auto &sm_ps = ml.ps;
+  auto &sm_sum = ml.sum;
+  const int tid = epi_tid();
+  // At most kSplitMaxPieces pieces by construction (every piece mode); the
   // bound keeps the LDS statistics in range whatever the caller's sizes.
-  const int k = min(w.n_part, kSplitMaxPieces);
-  const size_t row0 = ((size_t)w.seq * p.num_heads + w.head0) * p.max_num_partitions;
-  for (int idx = tid; idx < w.nh * k; idx += kThreads) {
+  k = min(k, kSplitMaxPieces);
+  const size_t row0 = ((size_t)seq * p.num_heads + head0) * p.max_num_partitions;
+  for (int idx = tid; idx < nh * k; idx += kThreads) {
     const int h = idx / k, c = idx - h * k;
     const size_t r = row0 + (size_t)h * p.max_num_partitions + c;
-    const unsigned m_bits = coherent_load(p.max_logits + r);
-    const unsigned s_bits = coherent_load(p.exp_sums + r);
-    sm_pm[h][c] = bits_f(m_bits);
-    sm_ps[h][c] = bits_f(s_bits);
+    float m, sv;
+    if (c == own) {
+      m = own_m[h];
+      sv = own_s[h];
+    } else {
+      const unsigned m_bits = coherent_load(p.max_logits + r);
+      const unsigned s_bits = coherent_load(p.exp_sums + r);
+      m = bits_f(m_bits);
+      sv = bits_f(s_bits);
+    }
+    sm_pm[h][c] = m;
+    sm_ps[h][c] = sv;
   }
   __syncthreads();
   // Per head: the rescaled exp-sums r_c, in place of S_c, and their sum.
-  if (tid < w.nh)
+  if (tid < nh)
     sm_sum[tid] = lse_rescale(
         [&](int c) { return sm_pm[tid][c]; }, [&](int c) { return sm_ps[tid][c]; }, k,
         [](float x) { return fast_exp2(x); }, [&](int c, float r) { sm_ps[tid][c] = r; });
@@ -306,16 +340,46 @@ __device__ __forceinline__ void split_merge(const Params &p, const Work &w) {
   // Per thread: four consecutive dims of one head, all pieces' slices requested at once.
   constexpr int G = D / 4;
   const TT *to = reinterpret_cast<const TT *>(p.tmp_out);
-  for (int idx = tid; idx < w.nh * G; idx += kThreads) {
+  for (int idx = tid; idx < nh * G; idx += kThreads) {
     const int h = idx / G, d0 = 4 * (idx - h * G);
     const TT *col = to + (row0 + (size_t)h * p.max_num_partitions) * D + d0;
     float o[4];
-    lse_combine<4>([&](int c) { return sm_ps[h][c]; }, sm_sum[h], k,
-                   [&](int c) { return coherent_load4<TT>(col + (size_t)c * D); },
-                   [](const Raw4 &r, float(&v)[4]) { unpack4<TT>(r, v); }, o);
+    lse_combine<4>(
+        [&](int c) { return sm_ps[h][c]; }, sm_sum[h], k,
+        [&](int c) {
+          if (c == own) {
+            float v[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) store_out_row<QT, D>(p, w.seq, w.head0 + h, d0 + e, o[e]);
+            for (int e = 0; e < 4; ++e) v[e] = own_o[h][d0 + e];
+            return pack4<TT>(v);
+          }
+          return coherent_load4<TT>(col + (size_t)c * D);
+        },
+        [](const Raw4 &r, float(&v)[4]) { unpack4<TT>(r, v); }, o);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) store_out_row<QT, D>(p, seq, head0 + h, d0 + e, o[e]);
   }
+}
+
+// After a piece's partials are stored (slot = piece): the piece that
+// arrives last at the (sequence, grid-x slot) counter merges the k pieces
+// with the log-sum-exp rescale of the V2 page's Phase 2, writes out, and
+// resets the counter to zero for the next call.
+template <typename QT, typename TT, int D>
+__device__ __forceinline__ void split_merge(const Params &p, const Work &w) {
+  __shared__ int sm_last;
+  const int tid = epi_tid();
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's partial stores are done
+  __syncthreads();
+  if (tid == 0) {
+    sm_last = arrive_last(
+        item_counter(p, w.seq, w.xslot), w.n_part,
+        [](int *c) { return arrive_add(c); }, [](int *c) { arrive_acquire(c); },
+        [](int *c, int v) { arrive_reset(c, v); });
+  }
+  __syncthreads();
+  if (!sm_last) return;
+  merge_pieces<QT, TT, D, 4>(p, w.seq, w.head0, w.nh, w.n_part, -1, nullptr, nullptr, nullptr);
 }
 
 // ---------------------------------------------------------------------------
@@ -817,6 +881,164 @@ __device__ __forceinline__ void finish_partition(const Params &p, const Work &w,
   if (split && w.v2) {
     if (p.tmp_f32) split_merge<QT, float, D>(p, w);
     else split_merge<QT, QT, D>(p, w);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// List mode, workgroup workers (the MFMA kernel and the VALU kernel's
+// workgroup form): the epilogue of one piece, with the arrivals of cut items
+// kept off the critical path.
+//
+// Every wave of a cut item's piece adds 1 to the item's counter, so an item
+// of k pieces is complete at kWaves * k.  A piece that is not its worker's
+// last stores its partials and is left pending: each of its waves arrives
+// once those stores are known to be performed -- after the wave's second
+// step of the worker's next item (that step's tile was requested after the
+// stores, and a wave's memory operations complete in issue order), or in the
+// next epilogue when it has no such step -- and when one of those arrivals
+// completes the count, the workgroup merges the item in the next epilogue.
+// The worker's last piece, when cut, reads the counter when it starts and,
+// if at most one piece was then missing, again when it ends; once all the
+// other pieces' waves have arrived it is the merger: it merges straight from
+// its own result in LDS (its partials are never stored) and resets the
+// counter.  Otherwise it stores its partials, drains, and thread 0 adds
+// kWaves for the whole piece, the last arriver merging as in the split mode.
+// ---------------------------------------------------------------------------
+struct ListPend {
+  int seq, xslot, head0, nh, n_part;  // the pending piece's item; n_part = 0: none pending
+  bool arrived;                       // this wave has arrived for it
+};
+
+// One wave's arrival for the pending piece (lane 0's counter value before it
+// in old).  Wave-uniform.
+__device__ __forceinline__ void list_pend_arrive(const Params &p, ListPend &pend, int &old) {
+  if (pend.n_part == 0 || pend.arrived) return;
+  if ((threadIdx.x & 63) == 0)
+    old = __hip_atomic_fetch_add(item_counter(p, pend.seq, pend.xslot), 1, __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
+  pend.arrived = true;
+}
+
+// The epilogue.  sm_o / sm_m / sm_l hold the waves' states (written before
+// an LDS barrier); final_cut: this is the worker's last piece and its item
+// is cut; early: thread 0's counter reading at the piece's start; old: lane
+// 0's counter value before its wave's arrival for the pending piece.  Each
+// wave's memory operations up to its last step are complete (vmcnt(0)).
+template <typename QT, int D, int GS, int OSTRIDE>
+__device__ __forceinline__ void finish_list_piece(const Params &p, const Work &w,
+                                                  float (*sm_o)[GS][OSTRIDE],
+                                                  const float (*sm_m)[GS],
+                                                  const float (*sm_l)[GS], ListPend &pend,
+                                                  bool final_cut, int early, int old) {
+  __shared__ int sm_pend_last[kWaves];
+  __shared__ int sm_direct;
+  __shared__ float sm_own_m[16], sm_own_s[16];
+  const int tid = epi_tid(), lane = tid & 63, ew = tid >> 6;
+  const int need = kWaves * w.n_part;
+  // The pending piece: this wave's arrival if it has not arrived yet, and
+  // whether it completed the item.
+  list_pend_arrive(p, pend, old);
+  if (pend.n_part && lane == 0) sm_pend_last[ew] = old == kWaves * pend.n_part - 1;
+  // This piece's result: out, its partials (a pending piece), or, for a cut
+  // last piece, its own rows and statistics in LDS (sm_o[0]: each element is
+  // read and overwritten by the one thread that merges it).
+  for (int idx = tid; idx < w.nh * D; idx += kThreads) {
+    const int h = idx / D, d = idx - h * D;
+    float sum, ml;
+    const float o = wave_merge<GS, OSTRIDE>(p, w, sm_o, sm_m, sm_l, h, d, sum, ml);
+    if (!w.v2) {
+      store_out_row<QT, D>(p, w.seq, w.head0 + h, d, o);
+    } else if (!final_cut) {
+      const size_t row = ((size_t)w.seq * p.num_heads + w.head0 + h) * p.max_num_partitions + w.part;
+      if (p.tmp_f32)
+        coherent_store_elem<float>(reinterpret_cast<float *>(p.tmp_out) + row * D + d, o);
+      else
+        coherent_store_elem<QT>(reinterpret_cast<QT *>(p.tmp_out) + row * D + d, o);
+      if (d == 0) {
+        coherent_store(p.exp_sums + row, f_bits(sum));
+        coherent_store(p.max_logits + row, f_bits(ml));
+      }
+    } else {
+      sm_o[0][h][d] = o;
+      if (d == 0) {
+        sm_own_m[h] = ml;
+        sm_own_s[h] = sum;
+      }
+    }
+  }
+  if (final_cut) {
+    int *ctr = item_counter(p, w.seq, w.xslot);
+    if (tid == 0) {
+      int seen = early;
+      if (seen != need - kWaves && seen >= need - 2 * kWaves) seen = (int)coherent_load(ctr);
+      const bool direct = seen == need - kWaves;
+      if (direct) arrive_reset(ctr, 0);
+      sm_direct = direct;
+    }
+    __syncthreads();
+    if (sm_direct) {
+      if (p.tmp_f32)
+        merge_pieces<QT, float, D, OSTRIDE>(p, w.seq, w.head0, w.nh, w.n_part, w.part, sm_o[0],
+                                            sm_own_m, sm_own_s);
+      else
+        merge_pieces<QT, QT, D, OSTRIDE>(p, w.seq, w.head0, w.nh, w.n_part, w.part, sm_o[0],
+                                         sm_own_m, sm_own_s);
+    } else {
+      // Store the partials, then arrive for all the piece's waves at once.
+      const size_t row0 = ((size_t)w.seq * p.num_heads + w.head0) * p.max_num_partitions + w.part;
+      for (int idx = tid; idx < w.nh * D; idx += kThreads) {
+        const int h = idx / D, d = idx - h * D;
+        const size_t row = row0 + (size_t)h * p.max_num_partitions;
+        if (p.tmp_f32)
+          coherent_store_elem<float>(reinterpret_cast<float *>(p.tmp_out) + row * D + d, sm_o[0][h][d]);
+        else
+          coherent_store_elem<QT>(reinterpret_cast<QT *>(p.tmp_out) + row * D + d, sm_o[0][h][d]);
+        if (d == 0) {
+          coherent_store(p.exp_sums + row, f_bits(sm_own_s[h]));
+          coherent_store(p.max_logits + row, f_bits(sm_own_m[h]));
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's partial stores are done
+      __syncthreads();
+      if (tid == 0) {
+        const bool last = __hip_atomic_fetch_add(ctr, kWaves, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT) == need - kWaves;
+        if (last) arrive_reset(ctr, 0);
+        sm_direct = last;
+      }
+      __syncthreads();
+      if (sm_direct) {
+        if (p.tmp_f32)
+          merge_pieces<QT, float, D, 4>(p, w.seq, w.head0, w.nh, w.n_part, -1, nullptr, nullptr,
+                                        nullptr);
+        else
+          merge_pieces<QT, QT, D, 4>(p, w.seq, w.head0, w.nh, w.n_part, -1, nullptr, nullptr,
+                                     nullptr);
+      }
+    }
+  }
+  // The pending piece's item, when one of its waves' arrivals completed it.
+  if (pend.n_part) {
+    __syncthreads();
+    const bool last = sm_pend_last[0] | sm_pend_last[1] | sm_pend_last[2] | sm_pend_last[3];
+    if (last) {
+      if (tid == 0) arrive_reset(item_counter(p, pend.seq, pend.xslot), 0);
+      if (p.tmp_f32)
+        merge_pieces<QT, float, D, 4>(p, pend.seq, pend.head0, pend.nh, pend.n_part, -1, nullptr,
+                                      nullptr, nullptr);
+      else
+        merge_pieces<QT, QT, D, 4>(p, pend.seq, pend.head0, pend.nh, pend.n_part, -1, nullptr,
+                                   nullptr, nullptr);
+    }
+  }
+  pend.n_part = 0;
+  if (w.v2 && !final_cut) {
+    pend.seq = w.seq;
+    pend.xslot = w.xslot;
+    pend.head0 = w.head0;
+    pend.nh = w.nh;
+    pend.n_part = w.n_part;
+    pend.arrived = false;
   }
 }
 

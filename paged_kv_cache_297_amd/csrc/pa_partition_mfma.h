@@ -89,9 +89,12 @@ __device__ __forceinline__ u32x4 regroup_p(const u32x2 &p0, const u32x2 &p1) {
 // Waves per SIMD the register allocator must leave room for: two, with
 // both ping-pong tiles in registers.  (fp8 tiles are half the size, but three
 // waves make the allocator spill and measured slower than two.)
-template <typename KVT>
+// The persistent list form runs one workgroup per CU, one wave per SIMD:
+// the whole register file is its own.
+template <typename KVT, bool LIST>
 constexpr int mfma_waves_per_eu() {
-  if constexpr (PA_WAVES_PER_EU_MFMA > 0) return PA_WAVES_PER_EU_MFMA;
+  if constexpr (LIST) return 1;
+  else if constexpr (PA_WAVES_PER_EU_MFMA > 0) return PA_WAVES_PER_EU_MFMA;
   else return 2;
 }
 
@@ -115,7 +118,7 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const char *lds_ptr) {
 template <typename QT, typename KVT, int D, int BS, bool CAP, bool WIN, bool ROWS = false,
           bool LIST = false>
 __global__ void __launch_bounds__(kThreads)
-    __attribute__((amdgpu_waves_per_eu(mfma_waves_per_eu<KVT>())))
+    __attribute__((amdgpu_waves_per_eu(mfma_waves_per_eu<KVT, LIST>())))
     pa_partition_mfma(const Params p) {
   constexpr bool kFp8 = std::is_same<KVT, fp8e4m3>::value;
   using PT = typename std::conditional<kFp8, _Float16, KVT>::type;  // P.V operand type
@@ -383,10 +386,14 @@ __global__ void __launch_bounds__(kThreads)
   // still in flight into the back edge).  The scheduling barriers keep each
   // prefetch ahead of the step's compute.  On entry ta is loading the wave's
   // first step.
-  auto run_steps = [&](const Item &it, Tile &ta, Tile &tb, int first, auto stride_c) {
+  // on_second() runs once, after the wave's second step: the first tile
+  // the wave waited for that was requested inside this call.
+  auto run_steps = [&](const Item &it, Tile &ta, Tile &tb, int first, auto stride_c,
+                       auto on_second) {
     constexpr int S = decltype(stride_c)::value;
     int st = first;
     int left = st < it.n_steps ? (it.n_steps - st + S - 1) / S : 0;
+    bool hook = true;
     while (left >= 3) {
       tb = load_tile(it, st + S);
       __builtin_amdgcn_sched_barrier(0);
@@ -394,6 +401,10 @@ __global__ void __launch_bounds__(kThreads)
       ta = load_tile(it, st + 2 * S);
       __builtin_amdgcn_sched_barrier(0);
       process(it, st + S, tb);
+      if (hook) {
+        on_second();
+        hook = false;
+      }
       st += 2 * S;
       left -= 2;
     }
@@ -402,14 +413,16 @@ __global__ void __launch_bounds__(kThreads)
       __builtin_amdgcn_sched_barrier(0);
       process(it, st, ta);
       process(it, st + S, tb);
+      if (hook) on_second();
     } else if (left == 1) {
       process(it, st, ta);
     }
   };
+  auto no_hook = [] {};
 
-  // Cross-wave merge and stores of one item.  Wave totals: the four lanes of
-  // head n hold partial sums over their tokens.
-  auto finish_item = [&](const Item &it) {
+  // The waves' states into LDS (wave totals: the four lanes of head n hold
+  // partial sums over their tokens), then an LDS barrier.
+  auto stage_item = [&] {
     const float l_tot = xor_sum<32>(xor_sum<16>(l_run));
     // Lane indices re-read here (see epi_tid) rather than carried in
     // registers across the list form's item loop.
@@ -423,17 +436,22 @@ __global__ void __launch_bounds__(kThreads)
       sm_l[ew][en] = poisoned ? __builtin_nanf("") : l_tot;
     }
     lds_barrier();
+  };
+  // Cross-wave merge and stores of one item.
+  auto finish_item = [&](const Item &it) {
+    stage_item();
     finish_partition<QT, D, 16, OSTR>(p, it.w, sm_o, sm_m, sm_l);
   };
 
   if constexpr (LIST) {
     // Persistent, one worker per workgroup: the pieces of its share of the
-    // work list in order.  The next piece's query and first tile are
-    // requested before this piece's epilogue (cross-wave merge, stores,
-    // arrival), which then overlaps their latency; the barrier frees the LDS
-    // of one piece's epilogue for the next.  (The GQA groups this kernel
-    // serves make few, large items per worker, where one worker per wave
-    // would cut every item into many pieces.)
+    // work list in order.  The next piece is found while this one streams;
+    // its query and first tile are requested before this piece's epilogue
+    // (cross-wave merge, stores, arrivals), which then overlaps their
+    // latency; the barrier frees the LDS of one piece's epilogue for the
+    // next.  (The GQA groups this kernel serves make few, large items per
+    // worker, where one worker per wave would cut every item into many
+    // pieces.)
     ListCursor cur;
     if (!list_begin(p, cur, (int)blockIdx.x, (int)gridDim.x)) return;
     Work w;
@@ -442,18 +460,30 @@ __global__ void __launch_bounds__(kThreads)
     load_query(w);
     Tile ta, tb;
     if (wv < it.n_steps) ta = load_tile(it, wv);
+    ListPend pend{};
+    int pend_old = 0;
     while (true) {
-      reset_state();
-      run_steps(it, ta, tb, wv, std::integral_constant<int, kWaves>{});
       Work wn;
       const bool more = list_next<QT, D>(p, BS, 16, cur, wn);
+      const bool final_cut = !more && it.w.v2;
+      int early = 0;
+      if (final_cut && threadIdx.x == 0)
+        early = (int)coherent_load(item_counter(p, it.w.seq, it.w.xslot));
+      reset_state();
+      run_steps(it, ta, tb, wv, std::integral_constant<int, kWaves>{},
+                [&] { list_pend_arrive(p, pend, pend_old); });
+      // Nothing is in flight after the wave's last step; this makes its
+      // earlier partial stores performed for the arrivals.
+      __builtin_amdgcn_s_waitcnt(0x0F70);
       Item itn;
       if (more) {
         itn = make_item(wn);
         load_query(wn);
         if (wv < itn.n_steps) ta = load_tile(itn, wv);
       }
-      finish_item(it);
+      stage_item();
+      finish_list_piece<QT, D, 16, OSTR>(p, it.w, sm_o, sm_m, sm_l, pend, final_cut, early,
+                                         pend_old);
       __syncthreads();
       if (!more) break;
       it = itn;
@@ -466,7 +496,7 @@ __global__ void __launch_bounds__(kThreads)
     reset_state();
     Tile ta, tb;
     if (wv < it.n_steps) ta = load_tile(it, wv);
-    run_steps(it, ta, tb, wv, std::integral_constant<int, kWaves>{});
+    run_steps(it, ta, tb, wv, std::integral_constant<int, kWaves>{}, no_hook);
     finish_item(it);
   }
 }
