@@ -87,8 +87,8 @@ def algorithmic_bytes(wl, path: str, cu: int, B, window_left: int = -1,
     table = blocks * 4 + wl.num_seqs * 4
     # Partitions holding a key of the window.
     parts = np.where(lens > 0, (lens + 511) // 512 - t_lo // 512, 0)
-    if path in ("v1", "split", "worklist"):
-        # split / worklist: the pieces' partials are scratch inside one launch,
+    if path in ("v1", "split", "worklist", "auto_ws"):
+        # split / worklist / auto_ws: the pieces' partials are scratch inside one launch,
         # not part of the result; the minimum is that of v1.
         v2 = np.zeros_like(lens, dtype=bool)
     elif path == "v2":
@@ -354,7 +354,7 @@ def prepare(number: int, args, B, W, paths):
                 calls[path].append(lambda out=out, wl=wl, kw=kw: B.paged_attention_v1(
                     out, wl.query, wl.key_cache, wl.value_cache, wl.num_kv_heads, wl.scale,
                     wl.block_tables, wl.seq_lens, wl.block_size, wl.max_seq_len, **kw))
-            elif path in ("split", "worklist"):
+            elif path in ("split", "worklist", "auto_ws"):
                 calls[path].append(B.PreparedCall(
                     path, *common, **kw, counters=B.split_counters(wl.num_seqs, wl.num_heads)))
             else:
@@ -425,7 +425,7 @@ def measure(number: int, args, B, W, cu: int, keep_base: bool = False,
     base, calls, hold = prepare(number, args, B, W, paths)
     ab = algorithmic_bytes(base, args.path, cu, B, args.window, args.partials)
     wall, part_ms, red_ms, step_ms = time_steps(calls[args.path], args.steps, args.warmup, B)
-    if args.path in ("v1", "split", "worklist") or not ab["any_v2"]:
+    if args.path in ("v1", "split", "worklist", "auto_ws") or not ab["any_v2"]:
         # No reduce kernel runs (an all-v1 auto call records its reduce events
         # back to back; their gap is event overhead, not work).
         red_ms = np.zeros(len(part_ms))
@@ -493,7 +493,8 @@ def main() -> int:
     ap.add_argument("--also", default="3,5",
                     help="other workloads timed in the same process, reported inside the line "
                          "(comma list, or 'none')")
-    ap.add_argument("--path", default="auto", choices=["auto", "v2", "v1", "split", "worklist"])
+    ap.add_argument("--path", default="auto",
+                    choices=["auto", "v2", "v1", "split", "worklist", "auto_ws"])
     ap.add_argument("--partials", default="f32", choices=["f32", "out"],
                     help="dtype of tmp_out: float32 (the default contract) or the query dtype")
     ap.add_argument("--copies", type=int, default=4)
@@ -540,7 +541,7 @@ def main() -> int:
     compare = [] if args.compare.strip().lower() in ("", "none") else [
         q.strip() for q in args.compare.split(",")]
     for q in compare:
-        if q not in ("auto", "v2", "v1", "split", "worklist"):
+        if q not in ("auto", "v2", "v1", "split", "worklist", "auto_ws"):
             print(f"unknown path {q!r} in --compare", file=sys.stderr)
             return 2
     head = measure(args.workload, args, B, W, cu, keep_base=not args.no_cpu_baseline,

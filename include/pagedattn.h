@@ -364,6 +364,31 @@ pa_status paged_attention_worklist(
     const float *alibi_slopes, pa_dtype dtype, pa_kv_cache_dtype kv_cache_dtype,
     float k_scale, float v_scale, const pa_decode_options *options, void *stream);
 
+/* The decode of paged_attention_auto_ex for callers that can hand the
+ * library a counters buffer: with it, the call schedules the batch for
+ * balance instead of by the per-sequence v1 / v2 rule -- the work list
+ * (paged_attention_worklist) when the batch's (sequence, KV head group)
+ * items fill the device's compute units at least once, else the balanced
+ * split (paged_attention_split; also for the block-rows layout).  Both run
+ * in one launch and merge cut items with the V2 page's Phase 2 rescale
+ * ("Phase 2: Reduce across partitions") inside it.  The result equals the
+ * v1 / v2 result up to rounding (partials rounded to the options' partial
+ * dtype, fp32 by default).  counters == NULL: exactly
+ * paged_attention_auto_ex (exp_sums, max_logits and tmp_out then as there).
+ * With counters: exp_sums, max_logits and tmp_out are scratch (contents
+ * after the call unspecified), counters as for paged_attention_split (int32
+ * [num_seqs, num_heads], zero before the first call, left zero; calls that
+ * share it must not overlap).  Errors: those of the path taken, checked on
+ * the host before any launch. */
+pa_status paged_attention_auto_ws(
+    void *out, float *exp_sums, float *max_logits, void *tmp_out, int32_t *counters,
+    const void *query, const void *key_cache, const void *value_cache,
+    int num_seqs, int num_heads, int num_kv_heads, int head_size, float scale,
+    const int32_t *block_tables, int max_num_blocks_per_seq, const int32_t *seq_lens,
+    int num_blocks, int block_size, int max_seq_len, int max_num_partitions,
+    const float *alibi_slopes, pa_dtype dtype, pa_kv_cache_dtype kv_cache_dtype,
+    float k_scale, float v_scale, const pa_decode_options *options, void *stream);
+
 /* Bytes of the counters buffer of paged_attention_split (0 for non-positive
  * sizes). */
 size_t pa_split_counters_size(int num_seqs, int num_heads);

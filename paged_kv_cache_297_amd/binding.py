@@ -41,7 +41,7 @@ EXPORTED_SYMBOLS = (
     "paged_attention_partition", "paged_attention_reduce",
     "paged_attention_v1_ex", "paged_attention_v2_ex", "paged_attention_auto_ex",
     "paged_attention_partition_ex", "paged_attention_reduce_ex", "paged_attention_split",
-    "pa_split_counters_size", "paged_attention_split_static", "paged_attention_worklist", "paged_prefill", "pa_partition_size",
+    "pa_split_counters_size", "paged_attention_split_static", "paged_attention_worklist", "paged_attention_auto_ws", "paged_prefill", "pa_partition_size",
     "pa_num_partitions", "pa_should_use_v2", "pa_device_cu_count", "pa_set_timing_events",
     "pa_status_string", "pa_version", "pa_stream_read",
 )
@@ -111,6 +111,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.paged_attention_split.restype = _I
     lib.paged_attention_worklist.argtypes = lib.paged_attention_split.argtypes[:]
     lib.paged_attention_worklist.restype = _I
+    lib.paged_attention_auto_ws.argtypes = lib.paged_attention_split.argtypes[:]
+    lib.paged_attention_auto_ws.restype = _I
     lib.paged_attention_split_static.argtypes = lib.paged_attention_v1.argtypes[:-1] + [_P, _P]
     lib.paged_attention_split_static.restype = _I
     lib.paged_prefill.argtypes = [_P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P, _I, _P, _P, _I, _I,
@@ -322,10 +324,12 @@ def _split_args(out, exp_sums, max_logits, tmp_out, counters, query, *rest, opts
     layout = "block_rows" if opts is not None and opts.kv_layout == 1 else "decode"
     args = _v2_args(out, exp_sums, max_logits, tmp_out, query, *rest, kv_layout=layout)
     b, h = query.shape[0], query.shape[1]
-    if counters.dtype != torch.int32 or not counters.is_contiguous() or counters.numel() < b * h:
+    if counters is not None and (counters.dtype != torch.int32 or not counters.is_contiguous()
+                                 or counters.numel() < b * h):
         raise TypeError("counters must be a contiguous int32 tensor of num_seqs * num_heads")
     ptr = None if opts is None else ctypes.addressof(opts)
-    return args[:4] + [counters.data_ptr()] + args[4:-1] + [ptr, args[-1]]
+    cptr = None if counters is None else counters.data_ptr()
+    return args[:4] + [cptr] + args[4:-1] + [ptr, args[-1]]
 
 
 def paged_attention_worklist(out, exp_sums, max_logits, tmp_out, counters, query, key_cache,
@@ -343,6 +347,23 @@ def paged_attention_worklist(out, exp_sums, max_logits, tmp_out, counters, query
                        max_seq_len, alibi_slopes, kv_cache_dtype, k_scale, v_scale, stream,
                        opts=opts)
     _check(lib.paged_attention_worklist(*args), "paged_attention_worklist")
+
+
+def paged_attention_auto_ws(out, exp_sums, max_logits, tmp_out, counters, query, key_cache,
+                            value_cache, num_kv_heads, scale, block_tables, seq_lens, block_size,
+                            max_seq_len, alibi_slopes=None, kv_cache_dtype="auto", k_scale=1.0,
+                            v_scale=1.0, stream=None, window_left=-1, logits_soft_cap=0.0,
+                            kv_layout="decode") -> None:
+    """Auto decode scheduled for balance when ``counters`` (split_counters) is
+    given: the work list or the balanced split by batch shape, the partial
+    buffers then being scratch; ``counters=None`` is paged_attention_auto."""
+    lib = load_library()
+    opts = _options(window_left, logits_soft_cap, kv_layout, _partial_code(tmp_out, query))
+    args = _split_args(out, exp_sums, max_logits, tmp_out, counters, query, key_cache,
+                       value_cache, num_kv_heads, scale, block_tables, seq_lens, block_size,
+                       max_seq_len, alibi_slopes, kv_cache_dtype, k_scale, v_scale, stream,
+                       opts=opts)
+    _check(lib.paged_attention_auto_ws(*args), "paged_attention_auto_ws")
 
 
 def paged_attention_split(out, exp_sums, max_logits, tmp_out, counters, query, key_cache,
@@ -407,13 +428,13 @@ class PreparedCall:
                  kv_layout="decode"):
         self.lib = load_library()
         self.name = f"paged_attention_{mode}"
-        if mode not in ("v2", "auto", "split", "worklist"):
-            raise ValueError("mode must be 'v2', 'auto', 'split' or 'worklist'")
+        if mode not in ("v2", "auto", "split", "worklist", "auto_ws"):
+            raise ValueError("mode must be 'v2', 'auto', 'split', 'worklist' or 'auto_ws'")
         self.opts = _options(window_left, logits_soft_cap, kv_layout,
                              _partial_code(tmp_out, query))
         self.counters = counters
-        if mode in ("split", "worklist"):
-            if counters is None:
+        if mode in ("split", "worklist", "auto_ws"):
+            if counters is None and mode != "auto_ws":
                 raise ValueError(f"the {mode} mode needs a counters buffer (split_counters)")
             self.args = _split_args(out, exp_sums, max_logits, tmp_out, counters, query,
                                     key_cache, value_cache, num_kv_heads, scale, block_tables,

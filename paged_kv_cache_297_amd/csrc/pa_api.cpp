@@ -716,6 +716,45 @@ pa_status paged_attention_worklist(void *out, float *exp_sums, float *max_logits
   return run_partition(c);
 }
 
+pa_status paged_attention_auto_ws(void *out, float *exp_sums, float *max_logits, void *tmp_out,
+                                  int32_t *counters, const void *query, const void *key_cache,
+                                  const void *value_cache, int num_seqs, int num_heads,
+                                  int num_kv_heads, int head_size, float scale,
+                                  const int32_t *block_tables, int max_num_blocks_per_seq,
+                                  const int32_t *seq_lens, int num_blocks, int block_size,
+                                  int max_seq_len, int max_num_partitions,
+                                  const float *alibi_slopes, pa_dtype dtype,
+                                  pa_kv_cache_dtype kv_cache_dtype, float k_scale, float v_scale,
+                                  const pa_decode_options *options, void *stream) {
+  if (!counters)
+    return paged_attention_auto_ex(out, exp_sums, max_logits, tmp_out, query, key_cache,
+                                   value_cache, num_seqs, num_heads, num_kv_heads, head_size,
+                                   scale, block_tables, max_num_blocks_per_seq, seq_lens,
+                                   num_blocks, block_size, max_seq_len, max_num_partitions,
+                                   alibi_slopes, dtype, kv_cache_dtype, k_scale, v_scale,
+                                   options, stream);
+  Call c = make_call(PA_MODE_V2, out, exp_sums, max_logits, tmp_out, query, key_cache,
+                     value_cache, num_seqs, num_heads, num_kv_heads, head_size, scale,
+                     block_tables, max_num_blocks_per_seq, seq_lens, num_blocks, block_size,
+                     max_seq_len, max_num_partitions, alibi_slopes, dtype, kv_cache_dtype,
+                     k_scale, v_scale, stream);
+  c.split = true;
+  c.counters = counters;
+  pa_status st = apply_options(options, c);
+  if (st != PA_OK) return st;
+  st = validate_common(c, true);
+  if (st != PA_OK || num_seqs == 0) return st;
+  int cu = 0;
+  st = cu_count_current(&cu);
+  if (st != PA_OK) return st;
+  // The work list where the items fill the CUs at least once; the split
+  // for fewer, longer items, and for the block-rows layout, which the list
+  // form does not take.
+  const long long items = (long long)num_seqs * num_kv_heads * make_plan(c).head_groups;
+  c.list = items >= cu && c.kv_layout == PA_KV_LAYOUT_DECODE;
+  return run_partition(c);
+}
+
 pa_status paged_attention_split_static(void *out, const void *query, const void *key_cache,
                                        const void *value_cache, int num_seqs, int num_heads,
                                        int num_kv_heads, int head_size, float scale,

@@ -408,6 +408,13 @@ struct ListCursor {
   long long start;   // offset at which this worker's piece of the current item starts
 };
 
+// Lane l's 64-bit value (l wave-uniform), as a scalar.
+__device__ __forceinline__ long long readlane64(long long v, int l) {
+  const unsigned lo = __builtin_amdgcn_readlane((unsigned)(unsigned long long)v, l);
+  const unsigned hi = __builtin_amdgcn_readlane((unsigned)((unsigned long long)v >> 32), l);
+  return (long long)(((unsigned long long)hi << 32) | lo);
+}
+
 // Wave-uniform 64-bit value (every lane holds the same).
 __device__ __forceinline__ long long wave_uniform64(long long v) {
   const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)(unsigned long long)v);
@@ -556,8 +563,11 @@ __device__ __forceinline__ bool list_begin_regs(const Params &p, ListCursor &c, 
     keys[i] = list_keys(L[i], p.max_seq_len, p.window_left, &base[i]);
     cost[i] = in ? list_cost(keys[i], p.item_cost) : 0;
     kmax = in ? max(kmax, keys[i]) : kmax;
-    incl[i] = run + wave_inclusive_scan64(cost[i] * gx, lane);
-    run = wave_uniform64(__shfl(incl[i], 63));
+    incl[i] = run;
+    if (64 * i < n) {  // chunks past the batch stay at its total
+      incl[i] = run + wave_inclusive_scan64(cost[i] * gx, lane);
+      run = readlane64(incl[i], 63);
+    }
   }
   c.sh = list_shares(run, uniform32(list_workers(run, grid_workers, wave_max32(kmax))));
   c.sh.q = wave_uniform64(c.sh.q);
@@ -578,21 +588,20 @@ __device__ __forceinline__ bool list_begin_regs(const Params &p, ListCursor &c, 
         l = __builtin_ctzll(hit);
       }
     }
+    // Lane l of chunk ci (both wave-uniform): scalar reads of its registers.
     long long end_s = 0, cost_s = 1;
     int L_s = 0, keys_s = 0, base_s = 0, L_n = 0;
 #pragma unroll
     for (int i = 0; i < NC; ++i) {
-      const long long e = __shfl(incl[i], l), cs = __shfl(cost[i], l);
-      const int Ls = __shfl(L[i], l), ks = __shfl(keys[i], l), bs = __shfl(base[i], l);
-      // The next sequence's length: lane l + 1 of this chunk, or lane 0 of the next.
-      const int Ln = l < 63 ? __shfl(L[i], l + 1) : (i + 1 < NC ? __shfl(L[i + 1 < NC ? i + 1 : i], 0) : 0);
       if (i == ci) {
-        end_s = e;
-        cost_s = cs;
-        L_s = Ls;
-        keys_s = ks;
-        base_s = bs;
-        L_n = Ln;
+        end_s = readlane64(incl[i], l);
+        cost_s = readlane64(cost[i], l);
+        L_s = __builtin_amdgcn_readlane(L[i], l);
+        keys_s = __builtin_amdgcn_readlane(keys[i], l);
+        base_s = __builtin_amdgcn_readlane(base[i], l);
+        // The next sequence's length: lane l + 1 of this chunk, or lane 0 of the next.
+        L_n = l < 63 ? __builtin_amdgcn_readlane(L[i], l + 1)
+                     : (i + 1 < NC ? __builtin_amdgcn_readlane(L[i + 1 < NC ? i + 1 : i], 0) : 0);
       }
     }
     c.seq = uniform32(64 * ci + l);

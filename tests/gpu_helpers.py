@@ -25,9 +25,10 @@ def say(msg: str) -> None:
 def run(wl: W.Workload, path: str, poison_outputs: bool = True, window_left: int = -1,
         soft_cap: float = 0.0, block_tables=None, caches=None, kv_layout: str = "decode",
         partials: str = "f32"):
-    """Runs ``path`` ('v1', 'v2', 'auto', 'split', 'worklist') and returns
-    host float64 copies of out, exp_sums, max_logits, tmp_out (the last three
-    None for v1, split and worklist).  ``window_left`` / ``soft_cap``: the decode options (-1 / 0:
+    """Runs ``path`` ('v1', 'v2', 'auto', 'split', 'worklist', 'auto_ws') and
+    returns host float64 copies of out, exp_sums, max_logits, tmp_out (the
+    last three None for v1, split, worklist and auto_ws, whose partial
+    buffers are scratch).  ``window_left`` / ``soft_cap``: the decode options (-1 / 0:
     off); ``block_tables`` replaces the workload's table; ``caches`` = (K, V)
     replaces its caches, which are then in ``kv_layout``; ``partials``: the
     dtype of tmp_out ('f32' or 'out', the query dtype)."""
@@ -44,9 +45,10 @@ def run(wl: W.Workload, path: str, poison_outputs: bool = True, window_left: int
               logits_soft_cap=soft_cap, kv_layout=kv_layout)
     if path == "v1":
         B.paged_attention_v1(out, *args, **kw)
-    elif path in ("split", "worklist"):
+    elif path in ("split", "worklist", "auto_ws"):
         counters = B.split_counters(wl.num_seqs, wl.num_heads, device=out.device)
-        fn = B.paged_attention_split if path == "split" else B.paged_attention_worklist
+        fn = {"split": B.paged_attention_split, "worklist": B.paged_attention_worklist,
+              "auto_ws": B.paged_attention_auto_ws}[path]
         fn(out, es, ml, to, counters, *args, **kw)
         torch.cuda.synchronize()
         assert int(counters.abs().sum().item()) == 0, f"{path} counters not left at zero"
@@ -58,7 +60,7 @@ def run(wl: W.Workload, path: str, poison_outputs: bool = True, window_left: int
         raise ValueError(path)
     torch.cuda.synchronize()
     res = {"out": out.float().cpu().numpy().astype(np.float64)}
-    if path not in ("v1", "split", "worklist"):
+    if path not in ("v1", "split", "worklist", "auto_ws"):
         res["exp_sums"] = es.cpu().numpy().astype(np.float64)
         res["max_logits"] = ml.cpu().numpy().astype(np.float64)
         res["tmp_out"] = to.float().cpu().numpy().astype(np.float64)
@@ -149,8 +151,8 @@ def check_against_oracle(wl: W.Workload, res: dict, ref: dict, seqs, path: str,
         for s, e in zip(seqs, extra):
             check_close(res["out"][s], ref["out_v1"][s], tol, f"{wl.name}/{path} out seq {s}",
                         extra_atol=e)
-    if path in ("v1", "split", "worklist"):
-        return   # no partials (split, worklist: they are scratch)
+    if path in ("v1", "split", "worklist", "auto_ws"):
+        return   # no partials (split, worklist, auto_ws: they are scratch)
     # Partials of sequences on the v2 path.
     v2 = [s for s in seqs if path == "v2" or uses_v2(wl, s, window_left)]
     if not v2:

@@ -44,6 +44,8 @@ def call(lib, fn, B_, H, Hkv, D, bs, L, dtype, kv=0, mode=None, counters=None):
         a = [mode] + a
     elif fn in ("paged_attention_split", "paged_attention_worklist"):
         a = a[:4] + [counters or A] + a[4:-1] + [None, None]
+    elif fn == "paged_attention_auto_ws":
+        a = a[:4] + [counters] + a[4:-1] + [None, None]
     assert getattr(lib, fn)(*a) == B.PA_OK
     return last(lib)
 
@@ -111,3 +113,17 @@ def test_worklist_is_one_persistent_launch(lib):
         ("valu_bf16", (256, 0, 0), (128, 1))
     assert call(lib, "paged_attention_worklist", 64, 28, 4, 128, 16, 8192, BF16) == \
         ("mfma", (256, 0, 0), (BF16, 16))
+
+
+def test_auto_ws_schedules_by_batch_shape(lib):
+    """With counters: the work list when the (sequence, KV head group) items
+    fill the 256 CUs at least once, the balanced split for fewer items; with
+    none, the plain auto launches."""
+    assert call(lib, "paged_attention_auto_ws", 64, 28, 4, 128, 16, 8192, BF16, counters=A) == \
+        ("mfma", (256, 0, 0), (BF16, 16))
+    assert call(lib, "paged_attention_auto_ws", 256, 32, 32, 128, 16, 32768, BF16,
+                counters=A) == ("valu_bf16", (256, 0, 0), (128, 1))
+    assert call(lib, "paged_attention_auto_ws", 4, 32, 8, 128, 16, 100000, F16,
+                counters=A) == ("valu_f16", (8, 4, 8), (128, 4))
+    assert call(lib, "paged_attention_auto_ws", 4, 32, 8, 128, 16, 100000, F16) == \
+        ("reduce", (32, 4, 1), (F16, 128))

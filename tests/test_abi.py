@@ -386,6 +386,25 @@ def test_worklist_counters_options_and_layout():
     assert wl(*split_args(options=layout_opts(rows), dtype=BF16)) == UNSUP
 
 
+@pytest.mark.parametrize("kw,status", CASES)
+def test_auto_ws_validation_follows_v2(kw, status):
+    lib = B.load_library()
+    assert lib.paged_attention_auto_ws(*split_args(**kw)) == status
+
+
+def test_auto_ws_counters_options_and_layout():
+    lib = B.load_library()
+    aw = lib.paged_attention_auto_ws
+    # No counters: the plain auto call (its own argument checks).
+    assert aw(*split_args(counters=None, num_seqs=0)) == OK
+    assert aw(*split_args(counters=None, options=opts(-5, 0.0))) == BADARG
+    assert aw(*split_args(counters=A + 2)) == MISAL
+    assert aw(*split_args(counters=A + 4, num_seqs=0)) == OK
+    assert aw(*split_args(options=opts(-5, 0.0))) == BADARG
+    assert aw(*split_args(options=partial_opts(9))) == BADARG
+    assert aw(*split_args(options=opts(100, 30.0), num_seqs=0)) == OK
+
+
 def test_split_counters_checks():
     lib = B.load_library()
     assert lib.paged_attention_split(*split_args(counters=None)) == NULLP
