@@ -10,9 +10,11 @@ block size 16, lognormal lengths of median 2048 clipped to [16, 32768], about
 The two other long-context workloads (4 x 100000 fp16 tokens; fp8 KV, 32 x
 32768) are timed in the same process and reported inside the line
 (``also_timed``; ``--also none`` skips them), and the other decode paths
-(balanced split, work list) on the headline workload's same inputs
-(``paths_on_this_workload``; ``--compare none`` skips them).  tmp_out is
-float32 by default (``--partials out``: the query dtype).
+(balanced split, work list, and auto_ws -- the auto call given a counters
+buffer, which schedules the batch for balance) on the headline workload's
+same inputs (``paths_on_this_workload``; auto_ws on the other two workloads
+too; ``--compare none`` skips them).  tmp_out is float32 by default
+(``--partials out``: the query dtype).
 
 Inputs are resident in HBM before timing.  By default the step rotates over
 ``--copies`` independent copies of the KV pool (4 x 14 GB for the headline),
@@ -487,7 +489,7 @@ def main() -> int:
     ap.add_argument("--workload", type=int, default=4, choices=[1, 2, 3, 4, 5],
                     help="the headline workload (default 4: ragged MHA ALiBi bf16, the "
                          "largest that fits one GPU)")
-    ap.add_argument("--compare", default="split,worklist",
+    ap.add_argument("--compare", default="split,worklist,auto_ws",
                     help="other decode paths timed on the headline workload, reported inside the "
                          "line (comma list, or 'none')")
     ap.add_argument("--also", default="3,5",
@@ -546,7 +548,8 @@ def main() -> int:
             return 2
     head = measure(args.workload, args, B, W, cu, keep_base=not args.no_cpu_baseline,
                    other_paths=compare)
-    others = [measure(n, args, B, W, cu) for n in also]
+    others = [measure(n, args, B, W, cu, other_paths=[q for q in compare if q == "auto_ws"])
+              for n in also]
 
     if args.calibrate_copy:
         n = args.calibrate_copy * (1 << 20)
@@ -627,6 +630,7 @@ def main() -> int:
             "reduce_avg_ms": round(o["red_avg"], 5),
             "step_frac": round(o["step_achieved"] / HBM_PEAK_GBS, 4),
             "event_step_us_p10_p50_p90": [round(x, 2) for x in o["step_p"]],
+            "paths_on_this_workload": o["other_paths"],
         } for o in others],
     }
     if not args.no_cpu_baseline:
