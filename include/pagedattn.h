@@ -353,8 +353,9 @@ pa_status paged_attention_split(
  *
  * Buffers, counters contract and errors as for paged_attention_split
  * (exp_sums, max_logits and tmp_out are scratch; counters int32 [num_seqs,
- * num_heads], zero before the first call and left zero).  Decode layout only
- * (options->kv_layout = BLOCK_ROWS: PA_ERR_UNSUPPORTED). */
+ * num_heads], zero before the first call and left zero).  On the BLOCK_ROWS
+ * layout only for groups of 3 or more query heads per KV head (the MFMA
+ * form); smaller groups there return PA_ERR_UNSUPPORTED. */
 pa_status paged_attention_worklist(
     void *out, float *exp_sums, float *max_logits, void *tmp_out, int32_t *counters,
     const void *query, const void *key_cache, const void *value_cache,
@@ -369,7 +370,8 @@ pa_status paged_attention_worklist(
  * balance instead of by the per-sequence v1 / v2 rule -- the work list
  * (paged_attention_worklist) when the batch's (sequence, KV head group)
  * items fill the device's compute units at least once, else the balanced
- * split (paged_attention_split; also for the block-rows layout).  Both run
+ * split (paged_attention_split; also on the block-rows layout for groups
+ * of 1 or 2 query heads per KV head, which the work list does not take).  Both run
  * in one launch and merge cut items with the V2 page's Phase 2 rescale
  * ("Phase 2: Reduce across partitions") inside it.  The result equals the
  * v1 / v2 result up to rounding (partials rounded to the options' partial

@@ -243,8 +243,11 @@ pa_status validate_common(const Call &c, bool partition_phase) {
   if (c.kv_cache_dtype != PA_KV_AUTO && c.kv_cache_dtype != PA_KV_FP8_E4M3)
     return PA_ERR_BAD_ARGUMENT;
   if (c.kv_cache_dtype == PA_KV_FP8_E4M3 && c.dtype == PA_DTYPE_F32) return PA_ERR_UNSUPPORTED;
+  // The block-rows layout: 16-bit caches only; the work list only in the
+  // MFMA form (groups of rows_mfma_min_group or more query heads).
   if (c.kv_layout == PA_KV_LAYOUT_BLOCK_ROWS &&
-      (c.dtype == PA_DTYPE_F32 || c.kv_cache_dtype != PA_KV_AUTO || c.list))
+      (c.dtype == PA_DTYPE_F32 || c.kv_cache_dtype != PA_KV_AUTO ||
+       (c.list && c.num_heads / c.num_kv_heads < tunables().rows_mfma_min_group)))
     return PA_ERR_UNSUPPORTED;
   if (c.block_size != 16 && c.block_size != 32) return PA_ERR_UNSUPPORTED;
   if (pa::kPartitionSize % c.block_size != 0) return PA_ERR_UNSUPPORTED;
@@ -748,10 +751,11 @@ pa_status paged_attention_auto_ws(void *out, float *exp_sums, float *max_logits,
   st = cu_count_current(&cu);
   if (st != PA_OK) return st;
   // The work list where the items fill the CUs at least once; the split
-  // for fewer, longer items, and for the block-rows layout, which the list
-  // form does not take.
-  const long long items = (long long)num_seqs * num_kv_heads * make_plan(c).head_groups;
-  c.list = items >= cu && c.kv_layout == PA_KV_LAYOUT_DECODE;
+  // for fewer, longer items, and for the block-rows layout's VALU form,
+  // which has no list form.
+  const Plan pl = make_plan(c);
+  const long long items = (long long)num_seqs * num_kv_heads * pl.head_groups;
+  c.list = items >= cu && (c.kv_layout == PA_KV_LAYOUT_DECODE || pl.mfma);
   return run_partition(c);
 }
 

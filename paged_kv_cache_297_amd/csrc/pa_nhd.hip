@@ -48,14 +48,22 @@ hipError_t launch_partition_nhd(const Params &p, int q_dtype, int head_size, int
   return hipErrorInvalidValue;
 }
 
-template <typename QT, int D, int BS>
-static hipError_t launch_rows_mfma_opts(const Params &p, const Launch &l) {
+// The soft cap, the sliding window and the persistent list form are
+// compile-time variants.
+template <typename QT, int D, int BS, bool LIST>
+static hipError_t launch_rows_mfma_list(const Params &p, const Launch &l) {
   const bool win = p.window_left >= 0;
   if (p.cap_on)
-    return win ? launch_kernel(pa_partition_mfma<QT, QT, D, BS, true, true, true>, l, p)
-               : launch_kernel(pa_partition_mfma<QT, QT, D, BS, true, false, true>, l, p);
-  return win ? launch_kernel(pa_partition_mfma<QT, QT, D, BS, false, true, true>, l, p)
-             : launch_kernel(pa_partition_mfma<QT, QT, D, BS, false, false, true>, l, p);
+    return win ? launch_kernel(pa_partition_mfma<QT, QT, D, BS, true, true, true, LIST>, l, p)
+               : launch_kernel(pa_partition_mfma<QT, QT, D, BS, true, false, true, LIST>, l, p);
+  return win ? launch_kernel(pa_partition_mfma<QT, QT, D, BS, false, true, true, LIST>, l, p)
+             : launch_kernel(pa_partition_mfma<QT, QT, D, BS, false, false, true, LIST>, l, p);
+}
+
+template <typename QT, int D, int BS>
+static hipError_t launch_rows_mfma_opts(const Params &p, const Launch &l) {
+  return p.mode == kModeList ? launch_rows_mfma_list<QT, D, BS, true>(p, l)
+                             : launch_rows_mfma_list<QT, D, BS, false>(p, l);
 }
 
 template <typename QT>

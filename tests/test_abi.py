@@ -381,9 +381,14 @@ def test_worklist_counters_options_and_layout():
     assert wl(*split_args(options=opts(-5, 0.0))) == BADARG
     assert wl(*split_args(options=partial_opts(9))) == BADARG
     assert wl(*split_args(options=opts(100, 30.0), num_seqs=0)) == OK
-    # Decode layout only.
+    # The block-rows layout: only groups of 3+ query heads per KV head (the
+    # MFMA form has a list form; the 1-2 head VALU form has none).
     rows = B.LAYOUT_CODE["block_rows"]
     assert wl(*split_args(options=layout_opts(rows), dtype=BF16)) == UNSUP
+    assert wl(*split_args(options=layout_opts(rows), dtype=BF16, num_heads=8,
+                          num_seqs=0)) == OK
+    assert wl(*split_args(options=layout_opts(rows), dtype=F32, num_heads=8,
+                          num_seqs=0)) == UNSUP
 
 
 @pytest.mark.parametrize("kw,status", CASES)

@@ -1,8 +1,8 @@
 """GPU parity of the work-list path (paged_attention_worklist: one persistent
 launch over a device-built list balanced by memory-load cost): every kernel
 family and the full-size decode workloads against the fp64 oracle, with and
-without the decode options; the counters are left at zero, repeated calls
-are bitwise stable, and the edge cases (empty / invalid lengths, out-of-range
+without the decode options (also on the block-rows layout for MFMA groups);
+the counters are left at zero, repeated calls are bitwise stable, and the edge cases (empty / invalid lengths, out-of-range
 block ids, NaN in unread bytes) behave as for v1 / v2.  It agrees with the
 split path up to rounding of the partials."""
 
@@ -139,3 +139,27 @@ def test_worklist_matches_split_up_to_rounding():
     assert np.allclose(a, b, rtol=2e-2, atol=2e-2)
     rel = np.linalg.norm(a - b) / np.linalg.norm(b)
     assert rel < 5e-3, rel
+
+
+def test_worklist_block_rows_mfma_groups():
+    """The work list on the [num_blocks, Hkv, bs, D] layout (the MFMA form,
+    groups of 3+ query heads per KV head) against the oracle, with and
+    without the decode options, and the full-size GQA batch."""
+    for i, (group, d, bs, dt) in enumerate([(3, 64, 16, torch.bfloat16), (7, 128, 16, torch.float16),
+                                            (8, 128, 32, torch.bfloat16), (16, 64, 32, torch.float16)]):
+        wl = W.make_workload(2, lens=LENS, H=2 * group, Hkv=2, D=d, bs=bs, dtype=dt,
+                             alibi=(i % 2 == 1), seed=9800 + i)
+        caches = W.to_block_rows(wl.key_cache, wl.value_cache)
+        for w_left, cap in OPTIONS[:3]:
+            ref = H.oracle(wl, window_left=w_left, soft_cap=cap)
+            H.say(f"  block rows worklist G={group} D={d} bs={bs} W={w_left} cap={cap}")
+            res = H.run(wl, "worklist", window_left=w_left, soft_cap=cap, caches=caches,
+                        kv_layout="block_rows")
+            H.check_against_oracle(wl, res, ref, range(wl.num_seqs), "worklist",
+                                   window_left=w_left, soft_cap=cap)
+    wl = W.make_workload(2)
+    caches = W.to_block_rows(wl.key_cache, wl.value_cache)
+    ref = H.oracle(wl)
+    for path in ("worklist", "auto_ws"):
+        res = H.run(wl, path, caches=caches, kv_layout="block_rows")
+        H.check_against_oracle(wl, res, ref, range(wl.num_seqs), path)
