@@ -101,6 +101,31 @@ PA_HD inline bool arrive_last(int *ctr, int k, FetchAdd fetch_add, Acquire acqui
   return last;
 }
 
+// The work list's workgroup form: every wave of a piece arrives on its own,
+// so an item of k pieces is complete when the counter reaches waves * k.
+// fetch_add(ctr, n) adds n and returns the value before the addition; each
+// caller has made its piece's partial stores visible before arriving.
+//
+// A wave's arrival: true for the wave whose arrival completes the item.
+template <typename FetchAdd>
+PA_HD inline bool wave_arrive(int *ctr, int k, int waves, FetchAdd fetch_add) {
+  return fetch_add(ctr, 1) == waves * k - 1;
+}
+// A worker's last piece reads the counter (seen) before it arrives: when
+// every other piece's waves have arrived it is the merger, merges straight
+// from its own result and never arrives (its caller resets the counter).
+PA_HD inline bool others_arrived(int seen, int k, int waves) { return seen == waves * (k - 1); }
+// A second read is worth its round trip when at most one piece was missing.
+PA_HD inline bool worth_rereading(int seen, int k, int waves) {
+  return !others_arrived(seen, k, waves) && seen >= waves * (k - 2);
+}
+// Otherwise the last piece stores its partials and arrives for all its
+// waves at once: true when that completes the item.
+template <typename FetchAdd>
+PA_HD inline bool piece_arrive_all(int *ctr, int k, int waves, FetchAdd fetch_add) {
+  return fetch_add(ctr, waves) == waves * (k - 1);
+}
+
 // Keys per piece when a range of len keys is cut into
 // k = ceil(len / target) pieces (1 .. max_pieces) of equal length, rounded up
 // to 32 keys (the MFMA step); the last piece may be shorter.

@@ -943,10 +943,10 @@ __device__ __forceinline__ void finish_list_piece(const Params &p, const Work &w
   __shared__ int sm_direct;
   __shared__ float sm_own_m[16], sm_own_s[16];
   const int tid = epi_tid(), lane = tid & 63, ew = tid >> 6;
-  const int need = kWaves * w.n_part;
   // The pending piece: this wave's arrival if it has not arrived yet, and
   // whether it completed the item.
   list_pend_arrive(p, pend, old);
+  // (the check of wave_arrive in pa_merge.h, on the value the wave's add returned)
   if (pend.n_part && lane == 0) sm_pend_last[ew] = old == kWaves * pend.n_part - 1;
   // This piece's result: out, its partials (a pending piece), or, for a cut
   // last piece, its own rows and statistics in LDS (sm_o[0]: each element is
@@ -979,8 +979,8 @@ __device__ __forceinline__ void finish_list_piece(const Params &p, const Work &w
     int *ctr = item_counter(p, w.seq, w.xslot);
     if (tid == 0) {
       int seen = early;
-      if (seen != need - kWaves && seen >= need - 2 * kWaves) seen = (int)coherent_load(ctr);
-      const bool direct = seen == need - kWaves;
+      if (worth_rereading(seen, w.n_part, kWaves)) seen = (int)coherent_load(ctr);
+      const bool direct = others_arrived(seen, w.n_part, kWaves);
       if (direct) arrive_reset(ctr, 0);
       sm_direct = direct;
     }
@@ -1010,8 +1010,9 @@ __device__ __forceinline__ void finish_list_piece(const Params &p, const Work &w
       __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's partial stores are done
       __syncthreads();
       if (tid == 0) {
-        const bool last = __hip_atomic_fetch_add(ctr, kWaves, __ATOMIC_RELAXED,
-                                                 __HIP_MEMORY_SCOPE_AGENT) == need - kWaves;
+        const bool last = piece_arrive_all(ctr, w.n_part, kWaves, [](int *c, int n) {
+          return __hip_atomic_fetch_add(c, n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        });
         if (last) arrive_reset(ctr, 0);
         sm_direct = last;
       }
