@@ -892,10 +892,15 @@ pa_status paged_prefill(void *out, const void *query, const void *key_cache,
   p.window_left = o.window_left;
   p.window_right = o.window_right;
   p.scale_log2 = scale * 1.4426950408889634f;
-  const bool cap = o.logits_soft_cap > 0.0f;
+  // The uncapped kernel folds the scale into each weight's fma and masks a
+  // key by giving it a raw logit of -inf, which needs scale_log2 > 0.  A
+  // zero scale makes every logit 0, as c tanh(0 / c) = 0 does for any cap
+  // c: it runs the capped kernel with c = 1.
+  const bool cap = o.logits_soft_cap > 0.0f || p.scale_log2 == 0.0f;
   if (cap) {
-    p.cap_in = (float)(2.0 * 1.4426950408889634 * (double)scale / (double)o.logits_soft_cap);
-    p.cap_out = (float)((double)o.logits_soft_cap * 1.4426950408889634);
+    const double c = o.logits_soft_cap > 0.0f ? (double)o.logits_soft_cap : 1.0;
+    p.cap_in = (float)(2.0 * 1.4426950408889634 * (double)scale / c);
+    p.cap_out = (float)(c * 1.4426950408889634);
   }
   const pa::Launch l{dim3((unsigned)tiles, num_kv_heads, num_seqs),
                      reinterpret_cast<hipStream_t>(stream), t_events.partition_start,

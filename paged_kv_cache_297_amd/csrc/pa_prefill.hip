@@ -256,11 +256,20 @@ __global__ void __launch_bounds__(kThreads)
   const size_t blk_stride = (size_t)p.num_kv_heads * BS * D * sizeof(QT);
   bool poisoned = false;
 
-  float m_run[NT], l_run[NT];
+  // The reference starts at the lowest finite float rather than -inf, so
+  // that x - m_run is -inf, and its weight 0, for a masked logit whatever
+  // the column has seen (with -inf it would be NaN before the first move).
+  // Without a cap, m_thr is the raw dot product above which a logit exceeds
+  // the reference by more than the lazy margin, (m_run + margin) /
+  // scale_log2 (scale_log2 >= 0; infinite for a zero scale), so that a step
+  // compares its raw maxima without scaling them.
+  const float inv_scale_log2 = 1.0f / p.scale_log2;
+  float m_run[NT], l_run[NT], m_thr[NT];
   f32x4 oacc[NT][NDT];
 #pragma unroll
   for (int j = 0; j < NT; ++j) {
-    m_run[j] = -__builtin_inff();
+    m_thr[j] = -__builtin_inff();
+    m_run[j] = -__FLT_MAX__;
     l_run[j] = 0.0f;
 #pragma unroll
     for (int t = 0; t < NDT; ++t) oacc[j][t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
@@ -303,7 +312,9 @@ __global__ void __launch_bounds__(kThreads)
     full_lo = wave_max32(a);
     full_hi = -wave_max32(-b);
   }
-  auto compute = [&](int base, const char *kst) {
+  // first: the wave's first step, whose accumulators are still zero (a
+  // rescale of them would change nothing).
+  auto compute = [&](int base, const char *kst, bool first) {
     // Every valid column of the wave sees the whole step: no masks needed.
     const bool full = base >= full_lo && base + kPrefillStep <= full_hi;
     // S^T of every column tile; each K fragment read from LDS feeds NT MFMAs.
@@ -337,7 +348,7 @@ __global__ void __launch_bounds__(kThreads)
           if constexpr (decltype(raw)::value)
             pe[e] = fast_exp2(fmaf(x[h][e], p.scale_log2, -m_run[j]));
           else
-            pe[e] = x[h][e] == -__builtin_inff() ? 0.0f : fast_exp2(x[h][e] - m_run[j]);
+            pe[e] = fast_exp2(x[h][e] - m_run[j]);
         }
         pk[h] = u32x2{pack2(pe[0], pe[1], QT()), pack2(pe[2], pe[3], QT())};
         l_run[j] = dot2_sum(pk[h].x, dot2_sum(pk[h].y, l_run[j], QT()), QT());
@@ -347,23 +358,39 @@ __global__ void __launch_bounds__(kThreads)
         pop[j][hf] = u32x4{pk[2 * hf].x, pk[2 * hf].y, pk[2 * hf + 1].x, pk[2 * hf + 1].y};
     };
     // Moves column j's reference to bm when bm exceeds it by more than the
-    // lazy margin, rescaling its sum and accumulators (m_run = -inf always
-    // moves for a finite bm: alpha 0, and l_run and oacc are 0).  Returns
-    // whether it moved.
+    // lazy margin, rescaling its sum and accumulators (the initial reference
+    // moves for any finite bm above the lowest float: alpha 0, and l_run and
+    // oacc are 0).  Returns the factor.
     auto move_ref = [&](int j, float bm) {
       const bool move = bm > m_run[j] + kLazyRescale;
       const float alpha = move ? fast_exp2(m_run[j] - bm) : 1.0f;
       m_run[j] = move ? bm : m_run[j];
+      if constexpr (!CAP) m_thr[j] = move ? (bm + kLazyRescale) * inv_scale_log2 : m_thr[j];
       l_run[j] *= alpha;
       return alpha;
     };
     float alpha[NT];
-    if (!CAP && full) {
-      // Every key visible and no cap: the logits are the raw dot products
-      // scaled once.  Each lane first checks its own logits of each column
-      // against the column's reference; only when some lane's exceed it by
-      // more than the margin (the first steps, then rarely) does the wave
-      // take the column max across lanes and move references.
+    bool moved;  // some column's reference moved (wave-uniform)
+    if constexpr (!CAP) {
+      // No cap (and scale_log2 > 0: a zero scale runs the capped form): the
+      // logits are the raw dot products scaled once, inside the weights'
+      // fma, and a masked key's raw value becomes -inf, whose weight is 0.
+      // Full and masked steps then share one path, and the softmax state
+      // one set of registers.  Each lane first checks its own raw maxima
+      // against the columns' thresholds; only when some lane's exceed them
+      // (the first steps, then rarely) does the wave take the column maxima
+      // across lanes and move references.
+      if (!full) {
+#pragma unroll
+        for (int j = 0; j < NT; ++j)
+#pragma unroll
+          for (int h = 0; h < NSUB; ++h)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int t = base + 16 * h + kgrp + e;
+              if (t < vlo[j] || t >= vhi[j]) sc[j][h][e] = -__builtin_inff();
+            }
+      }
       float lm[NT];
       bool need = false;
 #pragma unroll
@@ -373,14 +400,16 @@ __global__ void __launch_bounds__(kThreads)
         for (int h = 0; h < NSUB; ++h)
 #pragma unroll
           for (int e = 0; e < 4; ++e) v = fmaxf(v, sc[j][h][e]);
-        lm[j] = v * p.scale_log2;
-        need |= lm[j] > m_run[j] + kLazyRescale;
+        lm[j] = v;
+        need |= v > m_thr[j];
       }
-#pragma unroll
-      for (int j = 0; j < NT; ++j) alpha[j] = 1.0f;
+      moved = false;
       if (__any(need)) {
+        moved = true;
+        // A column with nothing visible yet has max -inf and does not move.
 #pragma unroll
-        for (int j = 0; j < NT; ++j) alpha[j] = move_ref(j, xor_max<32>(xor_max<16>(lm[j])));
+        for (int j = 0; j < NT; ++j)
+          alpha[j] = move_ref(j, xor_max<32>(xor_max<16>(lm[j])) * p.scale_log2);
       }
 #pragma unroll
       for (int j = 0; j < NT; ++j) {
@@ -409,12 +438,13 @@ __global__ void __launch_bounds__(kThreads)
         alpha[j] = move_ref(j, xor_max<32>(xor_max<16>(bm)));
         make_p(j, std::false_type(), x);
       }
+      bool same = true;
+#pragma unroll
+      for (int j = 0; j < NT; ++j) same &= alpha[j] == 1.0f;
+      moved = !__all(same);
     }
     // Rescale the accumulators only when some column's reference moved.
-    bool same = true;
-#pragma unroll
-    for (int j = 0; j < NT; ++j) same &= alpha[j] == 1.0f;
-    if (!__all(same)) {
+    if (moved && !first) {
 #pragma unroll
       for (int j = 0; j < NT; ++j)
 #pragma unroll
@@ -511,7 +541,7 @@ __global__ void __launch_bounds__(kThreads)
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
       }
-      compute(sbase, cur);
+      compute(sbase, cur, s == 0);
       cur_off = cur_off == 2 * RG::STAGE ? 0 : cur_off + RG::STAGE;
     }
   }

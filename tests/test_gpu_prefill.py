@@ -130,6 +130,23 @@ def test_prefill_one_query_matches_decode():
     H.check_close(got, res["out"], TOL, "prefill nq=1 vs decode v1")
 
 
+@pytest.mark.parametrize("scale", [0.0, 1e-30, 2.5])
+@pytest.mark.parametrize("opts", [dict(causal=True), dict(causal=False, window_left=9),
+                                  dict(causal=True, soft_cap=5.0)], ids=["causal", "window", "cap"])
+def test_prefill_scale_extremes(scale, opts):
+    """A zero scale (every logit 0: the mean of the visible values, run by
+    the capped kernel), a tiny one (the raw-logit thresholds overflow to
+    +inf) and a large one, with causal, window and cap masks."""
+    import dataclasses
+    base = W.make_prefill_workload(qlens=[1, 37, 70, 5], klens=[300, 37, 100, 0], H=8, Hkv=2,
+                                   D=128, bs=16, seed=9300)
+    wl = dataclasses.replace(base, scale=scale)
+    H.say(f"  prefill scale {scale} {opts}")
+    got = run(wl, **opts)
+    ref, rows = oracle(wl, **opts)
+    H.check_close(got[rows], ref, TOL, f"prefill scale {scale} {opts}")
+
+
 def test_prefill_repeat_is_bitwise():
     wl = W.make_prefill_workload(qlens=[70, 3, 200], klens=[500, 40, 200], H=16, Hkv=4, D=128,
                                  bs=32, seed=9200)
