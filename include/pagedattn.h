@@ -201,7 +201,20 @@ pa_status paged_attention_v2(
  * sent down the v1 path get out only; their exp_sums / max_logits / tmp_out
  * rows are left as they were.  When the rule sends every sequence to v1
  * (it does at max_seq_len, and it is monotone in the length), the call runs
- * as plain v1: one workgroup per (sequence, KV head), no reduce phase. */
+ * as plain v1: one workgroup per (sequence, KV head), no reduce phase.
+ *
+ * Batches with many (sequence, KV head) items on the narrow-group kernel
+ * (pa_auto_uses_slots: no window, the default layout) run instead as one
+ * persistent launch over equal shares of the batch's memory-load cost (the
+ * PoD page's work estimate), then the reduce phase: piece j of a sequence's
+ * (KV head, head group) item -- every piece of a cut item spans at least
+ * 512 keys, so an item has no more pieces than partitions -- stores its
+ * partials in partition slot j, the slots past the last piece get
+ * max_logits = -inf / exp_sums = 0, and every sequence of two or more
+ * partitions is merged.  out is the same softmax; the partial buffers are
+ * then scratch (not the per-partition partials of v2).  A launch sized by
+ * the longest sequence would otherwise dispatch a workgroup per partition
+ * slot of every sequence. */
 pa_status paged_attention_auto(
     void *out, float *exp_sums, float *max_logits, void *tmp_out,
     const void *query, const void *key_cache, const void *value_cache,
@@ -488,6 +501,19 @@ int pa_num_partitions(int max_seq_len);
  * then leave compute units without a workgroup.  Returns 1 for v2, 0 for v1.
  * Under a sliding window of W >= 0 the auto call passes min(L, W + 1). */
 int pa_should_use_v2(int num_seqs, int num_kv_heads, int seq_len, int cu_count);
+
+/* Whether paged_attention_auto(_ex) and the AUTO phases run a batch of this
+ * shape as the persistent slot form described at paged_attention_auto
+ * (*uses_slots = 1; then its partial buffers are scratch) or by the
+ * per-sequence rule (0).  The shape arguments are those of the call;
+ * options as for the *_ex calls (NULL: none).  Reads the current device's
+ * compute units.  PA_ERR_BAD_ARGUMENT / PA_ERR_BAD_SHAPE / PA_ERR_UNSUPPORTED
+ * for arguments the call itself would refuse, PA_ERR_NULL_POINTER for a NULL
+ * uses_slots; PA_ERR_HIP if the compute units cannot be read. */
+pa_status pa_auto_uses_slots(int num_seqs, int num_heads, int num_kv_heads, int head_size,
+                             int block_size, int max_seq_len, pa_dtype dtype,
+                             pa_kv_cache_dtype kv_cache_dtype,
+                             const pa_decode_options *options, int *uses_slots);
 
 /* Compute units of the current HIP device (cached per device); <= 0 and
  * PA_ERR_HIP if the runtime cannot tell. */

@@ -42,7 +42,8 @@ EXPORTED_SYMBOLS = (
     "paged_attention_v1_ex", "paged_attention_v2_ex", "paged_attention_auto_ex",
     "paged_attention_partition_ex", "paged_attention_reduce_ex", "paged_attention_split",
     "pa_split_counters_size", "paged_attention_split_static", "paged_attention_worklist", "paged_attention_auto_ws", "paged_prefill", "pa_partition_size",
-    "pa_num_partitions", "pa_should_use_v2", "pa_device_cu_count", "pa_set_timing_events",
+    "pa_num_partitions", "pa_should_use_v2", "pa_auto_uses_slots", "pa_device_cu_count",
+    "pa_set_timing_events",
     "pa_status_string", "pa_version", "pa_stream_read",
 )
 
@@ -126,6 +127,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pa_num_partitions.restype = _I
     lib.pa_should_use_v2.argtypes = [_I, _I, _I, _I]
     lib.pa_should_use_v2.restype = _I
+    lib.pa_auto_uses_slots.argtypes = [_I, _I, _I, _I, _I, _I, _I, _I, _P,
+                                       ctypes.POINTER(ctypes.c_int)]
+    lib.pa_auto_uses_slots.restype = _I
     lib.pa_device_cu_count.argtypes = [ctypes.POINTER(ctypes.c_int)]
     lib.pa_device_cu_count.restype = _I
     lib.pa_set_timing_events.argtypes = [_P, _P, _P, _P]
@@ -563,6 +567,22 @@ def num_partitions(max_seq_len: int) -> int:
 
 def should_use_v2(num_seqs: int, num_kv_heads: int, seq_len: int, cu_count: int) -> bool:
     return bool(load_library().pa_should_use_v2(num_seqs, num_kv_heads, seq_len, cu_count))
+
+
+def auto_uses_slots(num_seqs: int, num_heads: int, num_kv_heads: int, head_size: int,
+                    block_size: int, max_seq_len: int, dtype: torch.dtype,
+                    kv_cache_dtype: str = "auto", window_left: int = -1,
+                    logits_soft_cap: float = 0.0, kv_layout: str = "decode") -> bool:
+    """pa_auto_uses_slots: whether the auto call runs this batch shape as the
+    persistent slot form (its partial buffers are then scratch)."""
+    opts = _options(window_left, logits_soft_cap, kv_layout)
+    n = ctypes.c_int(0)
+    _check(load_library().pa_auto_uses_slots(
+        num_seqs, num_heads, num_kv_heads, head_size, block_size, int(max_seq_len),
+        DTYPE_CODE[dtype], _kv_code(kv_cache_dtype),
+        ctypes.addressof(opts) if opts is not None else None, ctypes.byref(n)),
+        "pa_auto_uses_slots")
+    return bool(n.value)
 
 
 def device_cu_count() -> int:

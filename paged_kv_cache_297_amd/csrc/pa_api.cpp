@@ -48,6 +48,7 @@ struct Tunables {
   int list_per_cu = 1;
   int list_lds = 0;           // list: dynamic LDS bytes reserved per worker
   int list_wave = -1;         // list: 1 / 0 = one worker per wave / workgroup; -1: by shape
+  int auto_slots = 1;         // AUTO: large VALU batches as the slot form of the work list
 };
 
 int env_int(const char *name, int fallback, int lo, int hi) {
@@ -75,6 +76,7 @@ const Tunables &tunables() {
     x.list_per_cu = env_int("PA_LIST_PER_CU", x.list_per_cu, 0, 16);
     x.list_lds = env_int("PA_LIST_LDS", x.list_lds, 0, 160 * 1024);
     x.list_wave = env_int("PA_LIST_WAVE", x.list_wave, -1, 1);
+    x.auto_slots = env_int("PA_AUTO_SLOTS", x.auto_slots, 0, 1);
     return x;
   }();
   return t;
@@ -143,6 +145,7 @@ struct Call {
   int32_t *counters;      // paged_attention_split only (mode is then V2 for validation)
   bool split;             // a piece mode: split, or list (the work list)
   bool list;
+  bool list_slots;        // list: the slot form (AUTO without counters; see auto_slots)
   bool static_scratch;    // the partial buffers and counters are the library's own array
   hipStream_t stream;
 };
@@ -330,6 +333,7 @@ Params make_params(const Call &c, int cu, int head_groups) {
     p.list_wave = tunables().list_wave >= 0
                       ? tunables().list_wave
                       : ((long long)c.num_seqs * c.num_kv_heads * head_groups >= 2 * waves ? 1 : 0);
+    if (c.list_slots) p.list_wave = 2;  // the slot form: wave workers
   }
   p.counters = c.counters;
   p.split_target = c.split ? split_target(c, (long long)c.num_kv_heads * head_groups, cu) : 0;
@@ -371,9 +375,40 @@ bool auto_all_v1(const Call &c, int cu) {
   return (long long)c.num_kv_heads * pa_num_partitions(len) <= (long long)t.tile_factor * cu;
 }
 
-pa_status run_partition(const Call &c) {
-  pa_status st = validate_common(c, true);
+// AUTO calls whose grid would be one workgroup per partition slot of the
+// longest sequence for many (sequence, KV head) items -- most of them empty
+// in a ragged batch, and the launch then costs their dispatch -- run as the
+// slot form of the work list: one worker per wave over equal shares of the
+// batch's memory-load cost, piece j of an item stored as the v2 partials of
+// partition slot j (an item has no more pieces than partitions; the slots
+// past its last piece padded) and merged by the reduce kernel for every
+// sequence of two or more partitions.  VALU plans (the MFMA kernel has no
+// wave-worker form), the decode layout, no window, and at least two items
+// per wave worker.  Both phases decide it alike.
+bool auto_slots(const Call &c, int cu) {
+  if (c.mode != PA_MODE_AUTO || c.split || c.list || !tunables().auto_slots) return false;
+  if (c.kv_layout != PA_KV_LAYOUT_DECODE) return false;
+  if (c.window_left >= 0 && c.window_left < c.max_seq_len - 1) return false;
+  if (auto_all_v1(c, cu)) return false;
+  const Plan pl = make_plan(c);
+  if (pl.mfma) return false;
+  const long long items = (long long)c.num_seqs * c.num_kv_heads * pl.head_groups;
+  return items >= 2LL * pa::kWaves * cu;
+}
+
+pa_status run_partition(const Call &c_in) {
+  pa_status st = validate_common(c_in, true);
   if (st != PA_OK) return st;
+  Call c = c_in;
+  if (c.num_seqs > 0 && c.mode == PA_MODE_AUTO && !c.split && !c.list) {
+    int cu_a = 0;
+    st = cu_count_current(&cu_a);
+    if (st != PA_OK) return st;
+    if (auto_slots(c, cu_a)) {
+      c.list = true;
+      c.list_slots = true;
+    }
+  }
   const Plan pl = make_plan(c);
   const long long grid_x = (long long)c.num_kv_heads * pl.head_groups;
   if (grid_x > 0x7fffffffLL || pa_num_partitions(c.max_seq_len) > kMaxGridYZ)
@@ -424,6 +459,17 @@ pa_status run_reduce(const Call &c) {
   if (c.mode == PA_MODE_AUTO) {
     st = cu_count_current(&cu);
     if (st != PA_OK) return st;
+  }
+  if (!c.split && !c.list && auto_slots(c, cu)) {
+    // The slot form of the partition phase: every sequence of two or more
+    // partitions has its slots merged (the v2 rule for all).
+    Call cv = c;
+    cv.mode = PA_MODE_V2;
+    const Params p = make_params(cv, cu, 1);
+    const pa::Launch l{dim3(c.num_heads, c.num_seqs, 1), c.stream, t_events.reduce_start,
+                       t_events.reduce_stop};
+    const hipError_t e = pa::launch_reduce(p, (int)c.dtype, c.head_size, l);
+    return e == hipSuccess ? PA_OK : PA_ERR_HIP;
   }
   if (auto_all_v1(c, cu)) {
     // Nothing to merge.  The profiling events still mark an (empty) phase.
@@ -480,6 +526,7 @@ Call make_call(pa_mode mode, void *out, float *exp_sums, float *max_logits, void
   c.counters = nullptr;
   c.split = false;
   c.list = false;
+  c.list_slots = false;
   c.static_scratch = false;
   c.stream = reinterpret_cast<hipStream_t>(stream);
   return c;
@@ -938,6 +985,34 @@ int pa_should_use_v2(int num_seqs, int num_kv_heads, int seq_len, int cu_count) 
   if ((long long)num_seqs * num_kv_heads < (long long)t.small_batch_factor * cu_count) return 1;
   const long long tiles = (long long)num_kv_heads * (seq_len <= 0 ? 0 : ceil_div(seq_len, pa::kPartitionSize));
   return tiles > (long long)t.tile_factor * cu_count ? 1 : 0;
+}
+
+pa_status pa_auto_uses_slots(int num_seqs, int num_heads, int num_kv_heads, int head_size,
+                             int block_size, int max_seq_len, pa_dtype dtype,
+                             pa_kv_cache_dtype kv_cache_dtype, const pa_decode_options *options,
+                             int *uses_slots) {
+  if (!uses_slots) return PA_ERR_NULL_POINTER;
+  *uses_slots = 0;
+  if (dtype != PA_DTYPE_F32 && dtype != PA_DTYPE_F16 && dtype != PA_DTYPE_BF16)
+    return PA_ERR_BAD_ARGUMENT;
+  if (kv_cache_dtype != PA_KV_AUTO && kv_cache_dtype != PA_KV_FP8_E4M3) return PA_ERR_BAD_ARGUMENT;
+  if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || max_seq_len < 0 ||
+      num_heads % num_kv_heads != 0)
+    return PA_ERR_BAD_SHAPE;
+  if ((head_size != 64 && head_size != 128) || (block_size != 16 && block_size != 32))
+    return PA_ERR_UNSUPPORTED;
+  Call c = make_call(PA_MODE_AUTO, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                     num_seqs, num_heads, num_kv_heads, head_size, 1.0f, nullptr, 0, nullptr, 0,
+                     block_size, max_seq_len, pa_num_partitions(max_seq_len), nullptr, dtype,
+                     kv_cache_dtype, 1.0f, 1.0f, nullptr);
+  const pa_status st = apply_options(options, c);
+  if (st != PA_OK) return st;
+  if (num_seqs == 0) return PA_OK;
+  int cu = 0;
+  const pa_status cs = cu_count_current(&cu);
+  if (cs != PA_OK) return cs;
+  *uses_slots = auto_slots(c, cu) ? 1 : 0;
+  return PA_OK;
 }
 
 pa_status pa_device_cu_count(int *cu_count) {

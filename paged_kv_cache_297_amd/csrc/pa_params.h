@@ -71,7 +71,8 @@ struct Params {
   int *counters;        // split mode: [B, H] arrival counters, zero between calls
   int split_target;     // split mode: keys per piece before equalising (multiple of 512)
   int item_cost;        // list mode: cost of an item beyond its keys (the query row)
-  int list_wave;        // list mode, VALU kernel: one worker per wave (else per workgroup)
+  int list_wave;        // list mode, VALU kernel: 1 = one worker per wave, 2 = the same in
+                        // the slot form (auto without counters), 0 = one per workgroup
 };
 
 // First key position inside the sliding window of a sequence of length

@@ -673,7 +673,10 @@ __device__ __forceinline__ bool list_begin(const Params &p, ListCursor &c, int w
 // The next piece of this worker's range as a Work, or false at the end.
 // Empty and invalid sequences are finished here (out = 0 / NaN, written by
 // the worker's lanes) and skipped.
-template <typename QT, int D>
+// SLOTS: the slot form of the list (auto without counters): piece j of an
+// item goes to partition slot j, and every item of two or more partitions
+// stores partials for the reduce kernel, cut or whole.
+template <typename QT, int D, bool SLOTS = false>
 __device__ __forceinline__ bool list_next(const Params &p, int block_size, int group_slots,
                                           ListCursor &c, Work &w) {
   const int lane = epi_tid() & 63;
@@ -709,7 +712,8 @@ __device__ __forceinline__ bool list_next(const Params &p, int block_size, int g
       list_piece(c.sh, item_pos, keys, c.w, start, &w.n_part, &w.part);
     }
     w.t_lo = window_first_token(p.window_left, w.L);
-    w.v2 = w.n_part > 1;
+    if constexpr (SLOTS) w.v2 = keys > kPartitionSize;
+    else w.v2 = w.n_part > 1;
     w.single = false;
     const int t0 = base + (int)start;
     const int t1 = min(base + (int)min(stop, (long long)keys), w.L);
@@ -727,6 +731,23 @@ __device__ __forceinline__ bool list_next(const Params &p, int block_size, int g
 // ---------------------------------------------------------------------------
 // List mode: the epilogue of one wave's piece, from registers.
 // ---------------------------------------------------------------------------
+
+// The slot form: piece 0 of an item of n_part pieces marks the item's
+// partition slots n_part .. ceil(L / 512) - 1 empty (max logit -inf, exp
+// sum 0: the reduce kernel weighs them 0 and reads no row of them).  Every
+// piece of a cut item spans at least kListMinPiece keys, so an item has no
+// more pieces than partitions.  Lanes of one wave.
+static_assert(kListMinPiece >= kPartitionSize, "pieces must fit the partition slots");
+__device__ __forceinline__ void piece_slot_padding(const Params &p, const Work &w, int lane) {
+  if (w.part != 0) return;
+  const int extra = (w.L + kPartitionSize - 1) / kPartitionSize - w.n_part;
+  for (int idx = lane; idx < w.nh * extra; idx += 64) {
+    const int h = idx / extra, slot = w.n_part + idx % extra;
+    const size_t row = ((size_t)w.seq * p.num_heads + w.head0 + h) * p.max_num_partitions + slot;
+    p.max_logits[row] = -__builtin_inff();
+    p.exp_sums[row] = 0.0f;
+  }
+}
 
 // One element of a piece's normalised output: out directly when the item is
 // whole, else the piece's partial row (slot = piece), written past the L2.

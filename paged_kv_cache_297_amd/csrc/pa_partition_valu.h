@@ -221,7 +221,8 @@ __device__ __forceinline__ float dim_group_sum(float v) {
 #endif
 
 // LIST: 0 = one work item per workgroup (grid decomposition); 1 = persistent
-// list, one worker per workgroup; 2 = persistent list, one worker per wave.
+// list, one worker per workgroup; 2 = persistent list, one worker per wave;
+// 3 = the same as 2 in the slot form (auto without counters).
 template <typename QT, typename KVT, int D, int BS, int GP, bool CAP, bool WIN, int LIST = 0>
 __global__ void __launch_bounds__(kThreads) PA_VALU_OCCUPANCY pa_partition_valu(const Params p) {
   using T = ValuTraits<QT, KVT>;
@@ -479,21 +480,23 @@ __global__ void __launch_bounds__(kThreads) PA_VALU_OCCUPANCY pa_partition_valu(
       if (h < w.nh && w.v2 && el == 0) piece_stats(p, w, h, mh, lsum);
     }
     if (w.v2) {
-      if (p.tmp_f32) piece_arrive<QT, float, D>(p, w);
+      if constexpr (LIST == 3) piece_slot_padding(p, w, el);  // the reduce kernel merges
+      else if (p.tmp_f32) piece_arrive<QT, float, D>(p, w);
       else piece_arrive<QT, QT, D>(p, w);
     }
   };
 
-  if constexpr (LIST == 2) {
+  if constexpr (LIST == 2 || LIST == 3) {
     // Persistent, one worker per wave: every wave walks the pieces of its
     // share of the work list in order, on its own (many small items: a
     // wave's epilogue then overlaps the other waves' streaming).  The next
     // piece's query and first tile are requested before this piece's
-    // epilogue, which then overlaps their latency.
+    // epilogue, which then overlaps their latency.  LIST 3: the slot form
+    // (pieces to partition slots for the reduce kernel, no arrivals).
     ListCursor cur;
     if (!list_begin(p, cur, (int)blockIdx.x * kWaves + wv, (int)gridDim.x * kWaves)) return;
     Work w;
-    if (!list_next<QT, D>(p, BS, GP, cur, w)) return;
+    if (!list_next<QT, D, LIST == 3>(p, BS, GP, cur, w)) return;
     Item it = make_item(w);
     load_query(w);
     Tile ta, tb;
@@ -502,7 +505,7 @@ __global__ void __launch_bounds__(kThreads) PA_VALU_OCCUPANCY pa_partition_valu(
       reset_state();
       run_steps(it, ta, tb, 0, std::integral_constant<int, 1>{});
       Work wn;
-      const bool more = list_next<QT, D>(p, BS, GP, cur, wn);
+      const bool more = list_next<QT, D, LIST == 3>(p, BS, GP, cur, wn);
       Item itn;
       if (more) {
         itn = make_item(wn);

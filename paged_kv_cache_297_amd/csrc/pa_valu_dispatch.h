@@ -24,11 +24,17 @@ hipError_t launch_valu_list(const Params &p, const Launch &l) {
 }
 
 // The soft cap, the sliding window and the persistent list form are
-// compile-time variants.
+// compile-time variants.  The slot form (list_wave == 2) runs without a
+// window only.
 template <typename QT, typename KVT, int D, int BS, int GP>
 hipError_t launch_valu_one(const Params &p, const Launch &l) {
   if constexpr (GP <= valu_max_group(kv_bytes_of<QT, KVT>(), D, BS)) {
     if (p.mode != kModeList) return launch_valu_list<QT, KVT, D, BS, GP, 0>(p, l);
+    if (p.list_wave == 2) {
+      if (p.window_left >= 0) return hipErrorInvalidValue;
+      return p.cap_on ? launch_kernel(pa_partition_valu<QT, KVT, D, BS, GP, true, false, 3>, l, p)
+                      : launch_kernel(pa_partition_valu<QT, KVT, D, BS, GP, false, false, 3>, l, p);
+    }
     return p.list_wave ? launch_valu_list<QT, KVT, D, BS, GP, 2>(p, l)
                        : launch_valu_list<QT, KVT, D, BS, GP, 1>(p, l);
   } else {

@@ -153,6 +153,8 @@ def check_against_oracle(wl: W.Workload, res: dict, ref: dict, seqs, path: str,
                         extra_atol=e)
     if path in ("v1", "split", "worklist", "auto_ws"):
         return   # no partials (split, worklist, auto_ws: they are scratch)
+    if path == "auto" and auto_slots(wl, window_left, soft_cap):
+        return   # auto on the persistent slot form: the partial buffers are scratch
     # Partials of sequences on the v2 path.
     v2 = [s for s in seqs if path == "v2" or uses_v2(wl, s, window_left)]
     if not v2:
@@ -167,6 +169,14 @@ def check_against_oracle(wl: W.Workload, res: dict, ref: dict, seqs, path: str,
         if n:
             check_close(res["tmp_out"][s, :, lo:n], ref["tmp_out"][s, :, lo:n], tol,
                         f"{wl.name}/{path} tmp_out seq {s}")
+
+
+def auto_slots(wl: W.Workload, window_left: int = -1, soft_cap: float = 0.0,
+               kv_layout: str = "decode") -> bool:
+    """Whether the auto call runs this workload as the persistent slot form."""
+    return B.auto_uses_slots(wl.num_seqs, wl.num_heads, wl.num_kv_heads, wl.head_size,
+                             wl.block_size, wl.max_seq_len, wl.dtype, wl.kv_cache_dtype,
+                             window_left, soft_cap, kv_layout)
 
 
 def uses_v2(wl: W.Workload, s: int, window_left: int = -1) -> bool:

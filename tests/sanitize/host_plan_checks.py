@@ -70,10 +70,45 @@ def test_fp8_auto_is_all_v1(lib):
         ("mfma_fp8", (8, 32, 1), (BF16, 16))
 
 
-def test_ragged_alibi_auto_mixes(lib):
+def test_ragged_alibi_auto_runs_the_slot_form(lib):
+    """256 x 32 (sequence, KV head) items on the VALU kernel, at least two per
+    wave worker: the auto partition phase is one persistent launch (256 CUs),
+    not a grid of 32 x 256 x 64 mostly empty slots, and the auto call ends
+    with the reduce over (head, sequence)."""
     kind, grid, args = call(lib, "paged_attention_partition", 256, 32, 32, 128, 16, 32768,
                             BF16, mode=2)
-    assert (kind, grid, args) == ("valu_bf16", (32, 256, 64), (128, 1))
+    assert (kind, grid, args) == ("valu_bf16", (256, 0, 0), (128, 1))
+    assert call(lib, "paged_attention_auto", 256, 32, 32, 128, 16, 32768, BF16) == \
+        ("reduce", (32, 256, 1), (BF16, 128))
+    # v2 keeps its one-slice-per-partition grid.
+    assert call(lib, "paged_attention_partition", 256, 32, 32, 128, 16, 32768, BF16,
+                mode=1) == ("valu_bf16", (32, 256, 64), (128, 1))
+
+
+def test_auto_uses_slots_by_shape(lib):
+    """The slot form: VALU plan, decode layout, no window, at least 2 x 4
+    items per CU (256 CUs here), and not a batch that runs as plain v1."""
+    def q(B_, H, Hkv, L, dtype=BF16, kv=0, window=-1, layout=0, bs=16):
+        n = ctypes.c_int(-1)
+        opts = None
+        if window != -1 or layout != 0:
+            opts = B.DecodeOptions(window, 0.0, layout, 0)
+        assert lib.pa_auto_uses_slots(B_, H, Hkv, 128, bs, L, dtype, kv,
+                                      ctypes.addressof(opts) if opts else None,
+                                      ctypes.byref(n)) == B.PA_OK
+        return n.value
+    assert q(256, 32, 32, 32768) == 1            # ragged ALiBi shape: 8192 items
+    assert q(64, 256, 32, 32768, dtype=F32) == 1  # fp32 runs the VALU kernel at any group
+    assert q(64, 256, 32, 32768) == 0            # bf16 at G = 8: the MFMA kernel
+    assert q(64, 28, 4, 8192) == 0               # GQA: MFMA kernel
+    assert q(4, 32, 8, 100000, dtype=F16) == 0   # 32 items
+    assert q(32, 64, 8, 32768, kv=1) == 0        # fp8 GQA: MFMA
+    assert q(256, 32, 32, 32768, window=4095) == 0
+    assert q(256, 32, 32, 32768, layout=1) == 0
+    assert q(64, 32, 32, 32768) == 1             # 2048 items = 2 per wave worker
+    assert q(63, 32, 32, 32768) == 0
+    assert q(256, 32, 32, 512) == 0              # one partition: plain v1
+    assert q(0, 32, 32, 32768) == 0
 
 
 def test_v1_has_one_slice_and_fp32_valu(lib):
