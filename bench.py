@@ -74,7 +74,7 @@ def kernel_source_hash(prefill: bool = False) -> str:
 
 
 def algorithmic_bytes(wl, path: str, cu: int, B, window_left: int = -1,
-                      partials: str = "f32") -> dict:
+                      partials: str = "f32", kv_layout: str = "decode") -> dict:
     """Bytes each launch must move at minimum (each KV byte inside the window
     once per KV head; partial rows in the partial dtype)."""
     import numpy as np
@@ -99,6 +99,23 @@ def algorithmic_bytes(wl, path: str, cu: int, B, window_left: int = -1,
         v2 = np.array([B.should_use_v2(wl.num_seqs, wl.num_kv_heads, int(n), cu) for n in eff])
     h, d = wl.num_heads, wl.head_size
     esz_t = 4 if partials == "f32" else esz_q
+    if path == "auto" and B.auto_uses_slots(
+            wl.num_seqs, wl.num_heads, wl.num_kv_heads, wl.head_size, wl.block_size,
+            wl.max_seq_len, wl.dtype, wl.kv_cache_dtype, window_left, 0.0, kv_layout):
+        # The slot form: every sequence of two or more partitions goes through
+        # partial rows merged by the reduce -- at least one row per (sequence,
+        # head), a statistics pair per partition slot (pieces and padding).
+        multi = parts > 1
+        rows = int(multi.sum()) * h
+        tmp = rows * d * esz_t
+        stats = int((parts * multi).sum()) * h * 8
+        out_p1 = int((~multi).sum()) * h * d * esz_q
+        out_p2 = int(multi.sum()) * h * d * esz_q
+        reduce_read = rows * d * esz_t + stats
+        return {"kv": kv, "partition": kv + q + table + tmp + stats + out_p1,
+                "reduce": reduce_read + out_p2 + wl.num_seqs * 4,
+                "step": kv + q + table + tmp + stats + out + reduce_read,
+                "any_v2": bool(multi.any())}
     tmp = int((parts * v2).sum()) * h * d * esz_t   # partial outputs
     stats = int((v2 * wl.max_num_partitions).sum()) * h * 8   # values and padding
     multi = v2 & (parts > 1)
@@ -425,7 +442,7 @@ def measure(number: int, args, B, W, cu: int, keep_base: bool = False,
 
     paths = [args.path] + [q for q in other_paths if q != args.path]
     base, calls, hold = prepare(number, args, B, W, paths)
-    ab = algorithmic_bytes(base, args.path, cu, B, args.window, args.partials)
+    ab = algorithmic_bytes(base, args.path, cu, B, args.window, args.partials, args.layout)
     wall, part_ms, red_ms, step_ms = time_steps(calls[args.path], args.steps, args.warmup, B)
     if args.path in ("v1", "split", "worklist", "auto_ws") or not ab["any_v2"]:
         # No reduce kernel runs (an all-v1 auto call records its reduce events
