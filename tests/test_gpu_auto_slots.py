@@ -103,3 +103,58 @@ def test_not_taken_with_window_or_few_items():
     assert not H.auto_slots(wl, window_left=1000)
     small = W.make_workload(4, num_seqs=8, seed=7401)
     assert not H.auto_slots(small)
+
+
+# --------------------------------------------------------------------------
+# Seeded random batches large enough for the slot form: kernel families
+# (dtype, fp8 cache, head group 1 / 2 / 4, head size, block size), ragged
+# lengths with partition-boundary values, empty sequences, ALiBi, a soft cap
+# and NaN-poisoned unused cache slots, against the oracle on every sequence.
+# --------------------------------------------------------------------------
+
+RANDOM_CASES = 8
+RANDOM_KINDS = {"bf16": (torch.bfloat16, "auto"), "f16": (torch.float16, "auto"),
+                "f32": (torch.float32, "auto"), "fp8-bf16": (torch.bfloat16, "fp8_e4m3")}
+
+
+def _draw(case: int) -> dict:
+    rng = np.random.default_rng(40000 + case)
+    kind = str(rng.choice(sorted(RANDOM_KINDS)))
+    group = int(rng.choice([1, 2, 4]))
+    hkv = int(rng.choice([8, 16, 32]))
+    return dict(kind=kind, group=group, hkv=hkv, d=int(rng.choice([64, 128])),
+                bs=int(rng.choice([16, 32])), alibi=bool(rng.random() < 0.4),
+                cap=float(rng.choice([0.0, 0.0, 20.0])), poison=bool(case % 2),
+                seed=int(rng.integers(1 << 30)))
+
+
+def _draw_id(case: int) -> str:
+    c = _draw(case)
+    return f"{case}-{c['kind']}-G{c['group']}x{c['hkv']}-D{c['d']}-bs{c['bs']}"
+
+
+@pytest.mark.parametrize("case", range(RANDOM_CASES), ids=_draw_id)
+def test_slot_form_random(case):
+    c = _draw(case)
+    dtype, kv = RANDOM_KINDS[c["kind"]]
+    cu = B.device_cu_count()
+    rng = np.random.default_rng(c["seed"])
+    n = -(-2 * 4 * cu // c["hkv"])
+    lens = []
+    for _ in range(n):
+        r = rng.random()
+        if r < 0.05:
+            lens.append(0)
+        elif r < 0.3:
+            lens.append(int(512 * rng.integers(1, 8) + rng.integers(-1, 2)))
+        else:
+            lens.append(int(rng.integers(1, 4000)))
+    lens[int(rng.integers(n))] = 512 * (2 * cu // c["hkv"] + 2) + int(rng.integers(0, 512))
+    wl = W.make_workload(2, lens=lens, H=c["hkv"] * c["group"], Hkv=c["hkv"], D=c["d"],
+                         bs=c["bs"], dtype=dtype, kv=kv, alibi=c["alibi"], seed=c["seed"] % 100000,
+                         poison=c["poison"])
+    assert H.auto_slots(wl, soft_cap=c["cap"]), _draw_id(case)
+    H.say(f"  slot form random {_draw_id(case)} B={wl.num_seqs} cap={c['cap']} alibi={c['alibi']}")
+    res = H.run(wl, "auto", soft_cap=c["cap"])
+    ref = H.oracle(wl, soft_cap=c["cap"])
+    H.check_against_oracle(wl, res, ref, range(wl.num_seqs), "auto", soft_cap=c["cap"])
