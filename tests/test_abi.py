@@ -498,3 +498,25 @@ def test_prefill_options_validation():
               popts(cap=1e-45)):
         assert lib.paged_prefill(*prefill_args(options=o)) == BADARG
     assert lib.paged_prefill(*prefill_args(options=popts(0, 5, 9, 30.0), num_seqs=0)) == OK
+
+
+def test_auto_uses_slots_validation():
+    """pa_auto_uses_slots refuses what the auto call itself would refuse,
+    before it reads the device; an empty batch never takes the slot form."""
+    lib = B.load_library()
+    n = ctypes.c_int(-1)
+
+    def q(*a, out=True):
+        return lib.pa_auto_uses_slots(*a, ctypes.byref(n) if out else None)
+
+    assert q(4, 32, 32, 128, 16, 4096, 2, 0, None, out=False) == 1   # PA_ERR_NULL_POINTER
+    assert q(4, 32, 32, 128, 16, 4096, 7, 0, None) == 6              # bad dtype
+    assert q(4, 32, 32, 128, 16, 4096, 2, 5, None) == 6              # bad cache dtype
+    assert q(4, 30, 8, 128, 16, 4096, 2, 0, None) == 2               # heads % kv heads
+    assert q(-1, 32, 32, 128, 16, 4096, 2, 0, None) == 2
+    assert q(4, 32, 32, 96, 16, 4096, 2, 0, None) == 4               # head size
+    assert q(4, 32, 32, 128, 8, 4096, 2, 0, None) == 4               # block size
+    bad = B.DecodeOptions(-2, 0.0, 0, 0)
+    assert q(4, 32, 32, 128, 16, 4096, 2, 0, ctypes.addressof(bad)) == 6
+    n.value = -1
+    assert q(0, 32, 32, 128, 16, 4096, 2, 0, None) == B.PA_OK and n.value == 0
