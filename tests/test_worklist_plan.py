@@ -6,7 +6,8 @@ persistent launch.  For ragged, uniform, windowed and degenerate batches:
 every item's keys are covered exactly once; a cut item's pieces are at
 least 512 keys long, start on 32-key steps, carry consistent piece counts
 and indices 0..k-1 in key order, and number at most 64 and at most the
-item's partitions (ceil(L / 512), the partial slots the caller provides);
+item's partitions (ceil(L / 512), the partial slots the caller provides,
+which auto's slot form fills with piece j in slot j);
 an empty or invalid sequence has exactly one owner; no worker with work in
 the launch is idle; and the workers' memory-load costs (the PoD page's
 qo_len + 2 * page_size * kv_len model) are equal up to one snapping step at
